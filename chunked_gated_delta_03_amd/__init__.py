@@ -1,0 +1,268 @@
+"""MI355X (gfx950) chunked gated-delta-rule forward pass: Python binding.
+
+A thin ctypes layer over ``libgdn.so`` (the C ABI of ``include/gdn.h``): it
+checks tensor shapes/dtypes/devices (the C side only sees pointers), allocates
+outputs and workspace with torch (device memory and streams are torch's
+plumbing), and passes pointers. Every step of the computation runs in the HIP
+kernels. Importing this module fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple, Union
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK = 0
+GDN_ERR_INVALID_ARGUMENT = 1
+GDN_ERR_UNSUPPORTED = 2
+GDN_ERR_HIP = 3
+
+GDN_L2NORM_QK = 1
+GDN_BETA_SIGMOID = 2
+GDN_OUTPUT_FINAL_STATE = 4
+
+CHUNK = 64
+HEAD_DIM = 128
+VEC_ROWS = 8
+
+EXPORTED = (
+    "gdn_last_error", "gdn_num_chunks", "gdn_chunk_fwd_workspace_bytes", "kda_chunk_fwd_workspace_bytes",
+    "gdn_chunk_fwd", "kda_chunk_fwd", "gdn_stage_prepare", "gdn_stage_fwd_h", "gdn_stage_finalize",
+)
+
+
+class GdnError(RuntimeError):
+    """A non-zero status from the library; ``code`` is the GDN_ERR_* value."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__("gdn status %d: %s" % (code, message))
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libgdn.so not found at %s; build it with `python -m chunked_gated_delta_03_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i32, u32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_last_error.argtypes = []
+    lib.gdn_num_chunks.restype = ctypes.c_int
+    lib.gdn_num_chunks.argtypes = [i32, i32, i32, p, ctypes.POINTER(ctypes.c_int64)]
+    for name in ("gdn_chunk_fwd_workspace_bytes", "kda_chunk_fwd_workspace_bytes"):
+        fn = getattr(lib, name)
+        fn.restype = sz
+        fn.argtypes = [i32, i32, i32, i32, i32, i32, p, u32]
+    for name in ("gdn_chunk_fwd", "kda_chunk_fwd"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p, p, sz, p]
+    lib.gdn_stage_prepare.restype = ctypes.c_int
+    lib.gdn_stage_prepare.argtypes = [i32, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p, p, p, p]
+    lib.gdn_stage_fwd_h.restype = ctypes.c_int
+    lib.gdn_stage_fwd_h.argtypes = [i32, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, u32, p, p, p, p]
+    lib.gdn_stage_finalize.restype = ctypes.c_int
+    lib.gdn_stage_finalize.argtypes = [i32, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, p, p]
+    return lib
+
+
+lib = _load()
+
+
+def last_error() -> str:
+    return lib.gdn_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != GDN_OK:
+        raise GdnError(rc, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(device: torch.device, stream=None):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _cu_array(cu_seqlens) -> Optional[np.ndarray]:
+    if cu_seqlens is None:
+        return None
+    if isinstance(cu_seqlens, torch.Tensor):
+        if cu_seqlens.device.type != "cpu":
+            raise ValueError("cu_seqlens must be a host (CPU) tensor or sequence")
+        cu_seqlens = cu_seqlens.numpy()
+    arr = np.asarray(cu_seqlens)
+    if arr.ndim != 1 or not np.issubdtype(arr.dtype, np.integer):
+        raise ValueError("cu_seqlens must be a one-dimensional integer array")
+    if arr.size and (arr.min() < np.iinfo(np.int32).min or arr.max() > np.iinfo(np.int32).max):
+        raise ValueError("cu_seqlens values exceed int32")
+    return np.ascontiguousarray(arr, dtype=np.int32)
+
+
+def _cu_ptr(cu: Optional[np.ndarray]):
+    return None if cu is None else cu.ctypes.data_as(ctypes.c_void_p)
+
+
+def _flags(l2norm_qk: bool, beta_sigmoid: bool, output_final_state: bool) -> int:
+    return ((GDN_L2NORM_QK if l2norm_qk else 0) | (GDN_BETA_SIGMOID if beta_sigmoid else 0)
+            | (GDN_OUTPUT_FINAL_STATE if output_final_state else 0))
+
+
+def num_chunks(B: int, T: int, cu_seqlens=None) -> int:
+    cu = _cu_array(cu_seqlens)
+    n = ctypes.c_int64(0)
+    _check(lib.gdn_num_chunks(B, T, B if cu is None else len(cu) - 1, _cu_ptr(cu), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _check_inputs(q, k, v, g, beta, kda: bool, initial_state, cu):
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16), ("v", v, torch.bfloat16),
+                        ("beta", beta, torch.bfloat16), ("g", g, torch.float32)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch tensor" % name)
+        if t.dtype != dt:
+            raise ValueError("%s must be %s (got %s)" % (name, dt, t.dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if t.device.type != "cuda":
+            raise ValueError("%s must be on the GPU" % name)
+        if t.device != q.device:
+            raise ValueError("%s is on %s, q on %s" % (name, t.device, q.device))
+    if q.dim() != 4:
+        raise ValueError("q must have shape [B,T,H,K]")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if tuple(k.shape) != (B, T, H, K) or tuple(v.shape) != (B, T, H, V) or tuple(beta.shape) != (B, T, H):
+        raise ValueError("shape mismatch: q %s k %s v %s beta %s" % (tuple(q.shape), tuple(k.shape),
+                                                                    tuple(v.shape), tuple(beta.shape)))
+    gshape = (B, T, H, K) if kda else (B, T, H)
+    if tuple(g.shape) != gshape:
+        raise ValueError("g must have shape %s (got %s)" % (gshape, tuple(g.shape)))
+    N = B if cu is None else len(cu) - 1
+    if initial_state is not None:
+        if (initial_state.dtype != torch.float32 or not initial_state.is_contiguous()
+                or tuple(initial_state.shape) != (N, H, K, V) or initial_state.device != q.device):
+            raise ValueError("initial_state must be a contiguous fp32 [N,H,K,V] = %s tensor on %s"
+                             % ((N, H, K, V), q.device))
+    return B, T, H, K, V, N
+
+
+def _chunk_fwd(kda, q, k, v, g, beta, scale, initial_state, cu_seqlens, l2norm_qk, beta_sigmoid,
+               output_final_state, workspace, stream):
+    cu = _cu_array(cu_seqlens)
+    B, T, H, K, V, N = _check_inputs(q, k, v, g, beta, kda, initial_state, cu)
+    scale = K ** -0.5 if scale is None else float(scale)
+    flags = _flags(l2norm_qk, beta_sigmoid, output_final_state)
+    o = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=q.device)
+    fs = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device) if output_final_state else None
+    wsfn = lib.kda_chunk_fwd_workspace_bytes if kda else lib.gdn_chunk_fwd_workspace_bytes
+    need = wsfn(B, T, H, K, V, N, _cu_ptr(cu), flags)
+    if need == 0:
+        workspace = None  # invalid arguments: the call below reports the precise status
+    elif workspace is None:
+        workspace = torch.empty(int(need), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel() * workspace.element_size(), need))
+    fn = lib.kda_chunk_fwd if kda else lib.gdn_chunk_fwd
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _cu_ptr(cu), N,
+              B, T, H, K, V, scale, flags, _ptr(o), _ptr(fs), _ptr(workspace),
+              0 if workspace is None else workspace.numel() * workspace.element_size(),
+              _stream_ptr(q.device, stream)))
+    return o, fs
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, scale: Optional[float] = None, initial_state=None, cu_seqlens=None,
+                  l2norm_qk: bool = False, beta_sigmoid: bool = False, output_final_state: bool = True,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """GDN forward. q,k,v bf16 [B,T,H,128], g fp32 [B,T,H] (natural log),
+    beta bf16 [B,T,H]. Returns (o bf16 [B,T,H,128], final_state fp32 [N,H,128,128] or None)."""
+    return _chunk_fwd(False, q, k, v, g, beta, scale, initial_state, cu_seqlens, l2norm_qk, beta_sigmoid,
+                      output_final_state, workspace, stream)
+
+
+def kda_chunk_fwd(q, k, v, g, beta, scale: Optional[float] = None, initial_state=None, cu_seqlens=None,
+                  l2norm_qk: bool = False, beta_sigmoid: bool = False, output_final_state: bool = True,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """KDA forward: as :func:`gdn_chunk_fwd` with g fp32 [B,T,H,128] in log2 units."""
+    return _chunk_fwd(True, q, k, v, g, beta, scale, initial_state, cu_seqlens, l2norm_qk, beta_sigmoid,
+                      output_final_state, workspace, stream)
+
+
+def workspace_bytes(B, T, H, cu_seqlens=None, kda: bool = False, flags: int = 0) -> int:
+    cu = _cu_array(cu_seqlens)
+    N = B if cu is None else len(cu) - 1
+    fn = lib.kda_chunk_fwd_workspace_bytes if kda else lib.gdn_chunk_fwd_workspace_bytes
+    n = fn(B, T, H, HEAD_DIM, HEAD_DIM, N, _cu_ptr(cu), flags)
+    if n == 0:
+        raise GdnError(GDN_ERR_INVALID_ARGUMENT, last_error())
+    return int(n)
+
+
+# ---- stage entries -------------------------------------------------------------
+
+def gdn_stage_prepare(q, k, g, beta, scale=None, cu_seqlens=None, kda: bool = False, l2norm_qk: bool = False,
+                      beta_sigmoid: bool = False, stream=None):
+    """Returns (tmat fp32 [H,NT,64,64], aqk bf16 [H,NT,64,64], vec fp32 [H,NT,8,64], gk fp32 [H,NT,64,128] or None)."""
+    cu = _cu_array(cu_seqlens)
+    B, T, H, K, V, N = _check_inputs(q, k, q, g, beta, kda, None, cu)
+    NT = num_chunks(B, T, cu)
+    dev = q.device
+    tmat = torch.empty((H, NT, CHUNK, CHUNK), dtype=torch.float32, device=dev)
+    aqk = torch.empty((H, NT, CHUNK, CHUNK), dtype=torch.bfloat16, device=dev)
+    vec = torch.empty((H, NT, VEC_ROWS, CHUNK), dtype=torch.float32, device=dev)
+    gk = torch.empty((H, NT, CHUNK, K), dtype=torch.float32, device=dev) if kda else None
+    scale = K ** -0.5 if scale is None else float(scale)
+    _check(lib.gdn_stage_prepare(int(kda), _ptr(q), _ptr(k), _ptr(g), _ptr(beta), _cu_ptr(cu), N, B, T, H, K, K,
+                                 scale, _flags(l2norm_qk, beta_sigmoid, False), _ptr(tmat), _ptr(aqk), _ptr(vec),
+                                 _ptr(gk), _stream_ptr(dev, stream)))
+    return tmat, aqk, vec, gk
+
+
+def gdn_stage_fwd_h(k, v, tmat, vec, gk=None, initial_state=None, cu_seqlens=None, kda: bool = False,
+                    output_final_state: bool = True, stream=None):
+    """Returns (h fp32 [H,NT,128,128], v_new fp32 [H,NT,64,128], final_state fp32 [N,H,128,128] or None)."""
+    cu = _cu_array(cu_seqlens)
+    B, T, H, K = k.shape
+    V = v.shape[-1]
+    N = B if cu is None else len(cu) - 1
+    NT = num_chunks(B, T, cu)
+    dev = k.device
+    for name, t, shape in (("tmat", tmat, (H, NT, CHUNK, CHUNK)), ("vec", vec, (H, NT, VEC_ROWS, CHUNK))):
+        if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("%s must be contiguous fp32 %s" % (name, shape))
+    if tuple(v.shape) != (B, T, H, V) or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise ValueError("k, v must be bf16 [B,T,H,128]")
+    if initial_state is not None and tuple(initial_state.shape) != (N, H, K, V):
+        raise ValueError("initial_state must be [N,H,K,V]")
+    h = torch.empty((H, NT, K, V), dtype=torch.float32, device=dev)
+    v_new = torch.empty((H, NT, CHUNK, V), dtype=torch.float32, device=dev)
+    fs = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+    _check(lib.gdn_stage_fwd_h(int(kda), _ptr(k), _ptr(v), _ptr(tmat), _ptr(vec), _ptr(gk), _ptr(initial_state),
+                               _cu_ptr(cu), N, B, T, H, K, V, _flags(False, False, output_final_state), _ptr(h),
+                               _ptr(v_new), _ptr(fs), _stream_ptr(dev, stream)))
+    return h, v_new, fs
+
+
+def gdn_stage_finalize(q, aqk, vec, h, v_new, gk=None, cu_seqlens=None, kda: bool = False, stream=None):
+    """Returns o bf16 [B,T,H,128]."""
+    cu = _cu_array(cu_seqlens)
+    B, T, H, K = q.shape
+    N = B if cu is None else len(cu) - 1
+    NT = num_chunks(B, T, cu)
+    for name, t, shape in (("h", h, (H, NT, K, K)), ("v_new", v_new, (H, NT, CHUNK, K)),
+                           ("vec", vec, (H, NT, VEC_ROWS, CHUNK)), ("aqk", aqk, (H, NT, CHUNK, CHUNK))):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError("%s must be contiguous %s" % (name, shape))
+    o = torch.empty((B, T, H, K), dtype=torch.bfloat16, device=q.device)
+    _check(lib.gdn_stage_finalize(int(kda), _ptr(q), _ptr(aqk), _ptr(vec), _ptr(gk), _ptr(h), _ptr(v_new),
+                                  _cu_ptr(cu), N, B, T, H, K, K, _ptr(o), _stream_ptr(q.device, stream)))
+    return o

@@ -1,0 +1,507 @@
+// Host side of the C ABI declared in include/gdn.h: argument validation,
+// chunk tables for packed input, workspace layout and kernel launches.
+//
+// Contract checks follow the pages' adapters (hyper-parallel "Diff Coverage"
+// page of 2026-11-06: _packed_offsets and the Ascend C GDN entry; coverage
+// page of kimi_delta_attention_ascendc.py: _packed_offsets, _packed_metadata,
+// ascendc_chunk_kda): offsets strictly increasing from 0 to T, packed input
+// only with B = 1, chunk size 64, head dimension 128.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/gdn.h"
+#include "gdn_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// Problem description after validation.
+struct Problem {
+  bool kda = false;
+  int B = 0, T = 0, H = 0, N = 0;
+  bool packed = false;
+  int64_t NT = 0;
+  std::vector<int32_t> cu;  // snapshot of the offsets (packed)
+};
+
+constexpr uint32_t kKnownFlags = GDN_L2NORM_QK | GDN_BETA_SIGMOID | GDN_OUTPUT_FINAL_STATE;
+
+int check_shape(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                const int32_t* cu_seqlens, Problem& p) {
+  if (B < 1 || T < 1 || H < 1)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "B, T and H must be >= 1 (got B=%d T=%d H=%d)", B, T, H);
+  if (K != GDN_HEAD_DIM || V != GDN_HEAD_DIM)
+    return fail(GDN_ERR_UNSUPPORTED, "only K = V = %d is supported (got K=%d V=%d)", GDN_HEAD_DIM, K, V);
+  if ((int64_t)B * T > INT32_MAX / 2)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "B*T = %lld tokens exceeds the supported range",
+                (long long)B * T);
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  if (cu_seqlens) {
+    if (B != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "packed input (cu_seqlens) requires B == 1 (got B=%d)", B);
+    if (num_seqs < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "num_seqs must be >= 1 with cu_seqlens");
+    if (cu_seqlens[0] != 0)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens[0] must be 0 (got %d)", cu_seqlens[0]);
+    for (int i = 0; i < num_seqs; ++i)
+      if (cu_seqlens[i + 1] <= cu_seqlens[i])
+        return fail(GDN_ERR_INVALID_ARGUMENT,
+                    "cu_seqlens must be strictly increasing (cu[%d]=%d, cu[%d]=%d)", i, cu_seqlens[i], i + 1,
+                    cu_seqlens[i + 1]);
+    if (cu_seqlens[num_seqs] != T)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens[num_seqs] must equal T (got %d, T=%d)",
+                  cu_seqlens[num_seqs], T);
+    p.packed = true;
+    p.N = num_seqs;
+    p.cu.assign(cu_seqlens, cu_seqlens + num_seqs + 1);
+    p.NT = 0;
+    for (int i = 0; i < num_seqs; ++i) p.NT += (cu_seqlens[i + 1] - cu_seqlens[i] + GDN_CHUNK - 1) / GDN_CHUNK;
+  } else {
+    if (num_seqs != B)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "dense input needs num_seqs == B (got num_seqs=%d B=%d)", num_seqs, B);
+    p.N = B;
+    p.NT = (int64_t)B * ((T + GDN_CHUNK - 1) / GDN_CHUNK);
+  }
+  if ((int64_t)p.N * H > INT32_MAX || p.NT * H > INT32_MAX / 2)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "problem too large");
+  return GDN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Device must be gfx950; result cached per device id.
+int check_device() {
+  static std::mutex mu;
+  static std::vector<int> state;  // 0 unknown, 1 ok, 2 bad
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)state.size() <= dev) state.resize(dev + 1, 0);
+  if (state[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    state[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    if (state[dev] == 2)
+      return fail(GDN_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev,
+                  prop.gcnArchName);
+  }
+  if (state[dev] == 2) return fail(GDN_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return GDN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout: [tables | tmat | aqk | vec | gk(KDA)], each 256-byte aligned.
+struct Layout {
+  size_t tab = 0, tmat = 0, aqk = 0, vec = 0, gk = 0, total = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Layout layout_for(const Problem& p, bool with_intermediates) {
+  Layout L;
+  size_t off = 0;
+  L.tab = off;
+  if (p.packed) off += align256(sizeof(int4) * ((size_t)p.NT + (size_t)p.N));
+  if (with_intermediates) {
+    const size_t cmH = (size_t)p.NT * p.H;
+    L.tmat = off;
+    off += align256(cmH * GDN_CHUNK * GDN_CHUNK * sizeof(float));
+    L.aqk = off;
+    off += align256(cmH * GDN_CHUNK * GDN_CHUNK * sizeof(uint16_t));
+    L.vec = off;
+    off += align256(cmH * GDN_VEC_ROWS * GDN_CHUNK * sizeof(float));
+    if (p.kda) {
+      L.gk = off;
+      off += align256(cmH * GDN_CHUNK * GDN_HEAD_DIM * sizeof(float));
+    }
+  }
+  L.total = off;
+  return L;
+}
+
+// Pinned host staging for chunk tables: a small ring per process; a slot is
+// reused only after the copy that last read it has completed.
+struct StagingSlot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+  bool pending = false;
+  int device = -1;
+};
+
+std::mutex g_stage_mu;
+StagingSlot g_slots[8];
+unsigned g_next_slot = 0;
+
+int upload_tables(const Problem& p, void* dst, hipStream_t stream) {
+  std::vector<int4> tab;
+  tab.reserve((size_t)p.NT + p.N);
+  std::vector<int4> seqs;
+  seqs.reserve(p.N);
+  int c = 0;
+  for (int n = 0; n < p.N; ++n) {
+    const int t0 = p.cu[n], len = p.cu[n + 1] - p.cu[n];
+    const int nch = (len + GDN_CHUNK - 1) / GDN_CHUNK;
+    seqs.push_back(make_int4(t0, len, c, nch));
+    for (int j = 0; j < nch; ++j) {
+      const int rem = len - j * GDN_CHUNK;
+      tab.push_back(make_int4(t0 + j * GDN_CHUNK, rem < GDN_CHUNK ? rem : GDN_CHUNK, n, j));
+    }
+    c += nch;
+  }
+  tab.insert(tab.end(), seqs.begin(), seqs.end());
+  const size_t bytes = tab.size() * sizeof(int4);
+
+  int dev = 0;
+  hipGetDevice(&dev);
+  std::lock_guard<std::mutex> lock(g_stage_mu);
+  StagingSlot& s = g_slots[g_next_slot++ % 8];
+  hipError_t e;
+  if (s.pending) {
+    e = hipEventSynchronize(s.done);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(staging)");
+    s.pending = false;
+  }
+  if (s.device != dev && s.done) {
+    hipEventDestroy(s.done);
+    s.done = nullptr;
+  }
+  if (!s.done) {
+    e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    s.device = dev;
+  }
+  if (s.cap < bytes) {
+    if (s.host) hipHostFree(s.host);
+    s.host = nullptr;
+    s.cap = 0;
+    e = hipHostMalloc(&s.host, bytes, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(staging)");
+    s.cap = bytes;
+  }
+  std::memcpy(s.host, tab.data(), bytes);
+  e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(chunk tables)");
+  e = hipEventRecord(s.done, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(staging)");
+  s.pending = true;
+  return GDN_OK;
+}
+
+gdn::Geometry make_geometry(const Problem& p, void* tab_dev) {
+  gdn::Geometry g;
+  g.T = p.T;
+  g.ncb = (p.T + GDN_CHUNK - 1) / GDN_CHUNK;
+  g.NT = (int)p.NT;
+  g.N = p.N;
+  if (p.packed) {
+    g.ctab = static_cast<const int4*>(tab_dev);
+    g.stab = static_cast<const int4*>(tab_dev) + p.NT;
+  } else {
+    g.ctab = nullptr;
+    g.stab = nullptr;
+  }
+  return g;
+}
+
+// Workspace holder: caller's buffer, or a stream-ordered allocation.
+struct Workspace {
+  char* base = nullptr;
+  bool owned = false;
+  hipStream_t stream = nullptr;
+  ~Workspace() {
+    if (owned && base) hipFreeAsync(base, stream);
+  }
+};
+
+int acquire_workspace(void* ws, size_t ws_bytes, size_t need, hipStream_t stream, Workspace& W) {
+  W.stream = stream;
+  if (need == 0) return GDN_OK;
+  if (ws) {
+    if (ws_bytes < need)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", ws_bytes, need);
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    W.base = static_cast<char*>(ws);
+    return GDN_OK;
+  }
+  void* p = nullptr;
+  hipError_t e = hipMallocAsync(&p, need, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
+  W.base = static_cast<char*>(p);
+  W.owned = true;
+  return GDN_OK;
+}
+
+int check_common(const void* q, const void* k, const void* v, const float* g, const void* beta, float scale,
+                 uint32_t flags) {
+  if (!q || !k || !v || !g || !beta) return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g and beta must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "q, k and v must be 16-byte aligned");
+  if (!(std::isfinite(scale) && scale > 0.0f))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "scale must be finite and > 0 (got %g)", (double)scale);
+  if (flags & ~kKnownFlags) return fail(GDN_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags & ~kKnownFlags);
+  return GDN_OK;
+}
+
+int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float* g, const void* beta,
+              const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+              int32_t H, int32_t K, int32_t V, float scale, uint32_t flags, void* o, float* final_state,
+              void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  g_last_error.clear();
+  Problem p;
+  p.kda = kda;
+  int rc = check_shape(B, T, H, K, V, num_seqs, cu_seqlens, p);
+  if (rc) return rc;
+  rc = check_common(q, k, v, g, beta, scale, flags);
+  if (rc) return rc;
+  if (!o) return fail(GDN_ERR_INVALID_ARGUMENT, "o must be non-NULL");
+  if (!aligned16(o)) return fail(GDN_ERR_INVALID_ARGUMENT, "o must be 16-byte aligned");
+  if ((flags & GDN_OUTPUT_FINAL_STATE) && !final_state)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "GDN_OUTPUT_FINAL_STATE set but final_state is NULL");
+  rc = check_device();
+  if (rc) return rc;
+  if (kda) return fail(GDN_ERR_UNSUPPORTED, "kda_chunk_fwd: per-channel gate path not built yet");
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const Layout L = layout_for(p, true);
+  Workspace W;
+  rc = acquire_workspace(workspace, workspace_bytes, L.total, stream, W);
+  if (rc) return rc;
+  if (p.packed) {
+    rc = upload_tables(p, W.base + L.tab, stream);
+    if (rc) return rc;
+  }
+  const gdn::Geometry geo = make_geometry(p, W.base + L.tab);
+
+  gdn::PrepareArgs pa{};
+  pa.q = static_cast<const uint16_t*>(q);
+  pa.k = static_cast<const uint16_t*>(k);
+  pa.g = g;
+  pa.beta = static_cast<const uint16_t*>(beta);
+  pa.tmat = reinterpret_cast<float*>(W.base + L.tmat);
+  pa.aqk = reinterpret_cast<uint16_t*>(W.base + L.aqk);
+  pa.vec = reinterpret_cast<float*>(W.base + L.vec);
+  pa.gk = kda ? reinterpret_cast<float*>(W.base + L.gk) : nullptr;
+  pa.geo = geo;
+  pa.H = H;
+  pa.scale = scale;
+  pa.flags = flags;
+  hipError_t e = gdn::launch_prepare(kda, pa, stream);
+  if (e != hipSuccess) return hip_fail(e, "prepare launch");
+
+  gdn::FwdArgs fa{};
+  fa.q = pa.q;
+  fa.k = pa.k;
+  fa.v = static_cast<const uint16_t*>(v);
+  fa.tmat = pa.tmat;
+  fa.aqk = pa.aqk;
+  fa.vec = pa.vec;
+  fa.gk = pa.gk;
+  fa.s0 = initial_state;
+  fa.sfinal = (flags & GDN_OUTPUT_FINAL_STATE) ? final_state : nullptr;
+  fa.o = static_cast<uint16_t*>(o);
+  fa.geo = geo;
+  fa.H = H;
+  e = gdn::launch_fwd(kda, false, true, fa, stream);
+  if (e != hipSuccess) return hip_fail(e, "state/output launch");
+  return GDN_OK;
+}
+
+// Shared front half of the stage entries: validation, tables, geometry.
+struct StageCtx {
+  Problem p;
+  Workspace W;
+  gdn::Geometry geo;
+};
+
+int stage_begin(int32_t kda, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+                int32_t K, int32_t V, hipStream_t stream, StageCtx& ctx) {
+  g_last_error.clear();
+  ctx.p.kda = kda != 0;
+  int rc = check_shape(B, T, H, K, V, num_seqs, cu_seqlens, ctx.p);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  if (kda) return fail(GDN_ERR_UNSUPPORTED, "per-channel gate stages not built yet");
+  const Layout L = layout_for(ctx.p, false);
+  rc = acquire_workspace(nullptr, 0, L.total, stream, ctx.W);
+  if (rc) return rc;
+  if (ctx.p.packed) {
+    rc = upload_tables(ctx.p, ctx.W.base + L.tab, stream);
+    if (rc) return rc;
+  }
+  ctx.geo = make_geometry(ctx.p, ctx.W.base + L.tab);
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+int gdn_num_chunks(int32_t B, int32_t T, int32_t num_seqs, const int32_t* cu_seqlens, int64_t* num_chunks) {
+  g_last_error.clear();
+  if (!num_chunks) return fail(GDN_ERR_INVALID_ARGUMENT, "num_chunks must be non-NULL");
+  Problem p;
+  int rc = check_shape(B, T, 1, GDN_HEAD_DIM, GDN_HEAD_DIM, num_seqs, cu_seqlens, p);
+  if (rc) return rc;
+  *num_chunks = p.NT;
+  return GDN_OK;
+}
+
+static size_t workspace_bytes(bool kda, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                              const int32_t* cu_seqlens, uint32_t flags) {
+  g_last_error.clear();
+  Problem p;
+  p.kda = kda;
+  if (check_shape(B, T, H, K, V, num_seqs, cu_seqlens, p)) return 0;
+  if (flags & ~kKnownFlags) {
+    fail(GDN_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags & ~kKnownFlags);
+    return 0;
+  }
+  return layout_for(p, true).total;
+}
+
+size_t gdn_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                     const int32_t* cu_seqlens, uint32_t flags) {
+  return workspace_bytes(false, B, T, H, K, V, num_seqs, cu_seqlens, flags);
+}
+
+size_t kda_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                     const int32_t* cu_seqlens, uint32_t flags) {
+  return workspace_bytes(true, B, T, H, K, V, num_seqs, cu_seqlens, flags);
+}
+
+int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                  int32_t H, int32_t K, int32_t V, float scale, uint32_t flags, void* o, float* final_state,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_fwd(false, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, scale, flags, o,
+                   final_state, workspace, workspace_bytes, stream);
+}
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                  int32_t H, int32_t K, int32_t V, float scale, uint32_t flags, void* o, float* final_state,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_fwd(true, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, scale, flags, o,
+                   final_state, workspace, workspace_bytes, stream);
+}
+
+int gdn_stage_prepare(int32_t kda, const void* q, const void* k, const float* g, const void* beta,
+                      const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+                      int32_t V, float scale, uint32_t flags, float* tmat, void* aqk, float* vec, float* gk,
+                      void* stream_ptr) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  g_last_error.clear();
+  int rc = check_common(q, k, q, g, beta, scale, flags);
+  if (rc) return rc;
+  if (!tmat || !aqk || !vec || (kda && !gk))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "tmat, aqk, vec (and gk for KDA) must be non-NULL");
+  StageCtx ctx;
+  rc = stage_begin(kda, cu_seqlens, num_seqs, B, T, H, K, V, stream, ctx);
+  if (rc) return rc;
+  gdn::PrepareArgs pa{};
+  pa.q = static_cast<const uint16_t*>(q);
+  pa.k = static_cast<const uint16_t*>(k);
+  pa.g = g;
+  pa.beta = static_cast<const uint16_t*>(beta);
+  pa.tmat = tmat;
+  pa.aqk = static_cast<uint16_t*>(aqk);
+  pa.vec = vec;
+  pa.gk = gk;
+  pa.geo = ctx.geo;
+  pa.H = H;
+  pa.scale = scale;
+  pa.flags = flags;
+  hipError_t e = gdn::launch_prepare(kda != 0, pa, stream);
+  if (e != hipSuccess) return hip_fail(e, "prepare launch");
+  return GDN_OK;
+}
+
+int gdn_stage_fwd_h(int32_t kda, const void* k, const void* v, const float* tmat, const float* vec, const float* gk,
+                    const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                    int32_t H, int32_t K, int32_t V, uint32_t flags, float* h, float* v_new, float* final_state,
+                    void* stream_ptr) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  g_last_error.clear();
+  if (!k || !v || !tmat || !vec || !h || !v_new || (kda && !gk))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "k, v, tmat, vec, h, v_new (and gk for KDA) must be non-NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(GDN_ERR_INVALID_ARGUMENT, "k and v must be 16-byte aligned");
+  if (flags & ~kKnownFlags) return fail(GDN_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags & ~kKnownFlags);
+  if ((flags & GDN_OUTPUT_FINAL_STATE) && !final_state)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "GDN_OUTPUT_FINAL_STATE set but final_state is NULL");
+  StageCtx ctx;
+  int rc = stage_begin(kda, cu_seqlens, num_seqs, B, T, H, K, V, stream, ctx);
+  if (rc) return rc;
+  gdn::FwdArgs fa{};
+  fa.k = static_cast<const uint16_t*>(k);
+  fa.v = static_cast<const uint16_t*>(v);
+  fa.tmat = tmat;
+  fa.vec = vec;
+  fa.gk = gk;
+  fa.s0 = initial_state;
+  fa.sfinal = (flags & GDN_OUTPUT_FINAL_STATE) ? final_state : nullptr;
+  fa.h_out = h;
+  fa.vnew_out = v_new;
+  fa.geo = ctx.geo;
+  fa.H = H;
+  hipError_t e = gdn::launch_fwd(kda != 0, true, false, fa, stream);
+  if (e != hipSuccess) return hip_fail(e, "chunk_fwd_h launch");
+  return GDN_OK;
+}
+
+int gdn_stage_finalize(int32_t kda, const void* q, const void* aqk, const float* vec, const float* gk, const float* h,
+                       const float* v_new, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                       int32_t H, int32_t K, int32_t V, void* o, void* stream_ptr) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  g_last_error.clear();
+  if (!q || !aqk || !vec || !h || !v_new || !o || (kda && !gk))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "q, aqk, vec, h, v_new, o (and gk for KDA) must be non-NULL");
+  if (!aligned16(q) || !aligned16(o)) return fail(GDN_ERR_INVALID_ARGUMENT, "q and o must be 16-byte aligned");
+  StageCtx ctx;
+  int rc = stage_begin(kda, cu_seqlens, num_seqs, B, T, H, K, V, stream, ctx);
+  if (rc) return rc;
+  gdn::FinArgs fa{};
+  fa.q = static_cast<const uint16_t*>(q);
+  fa.aqk = static_cast<const uint16_t*>(aqk);
+  fa.vec = vec;
+  fa.gk = gk;
+  fa.h = h;
+  fa.vnew = v_new;
+  fa.o = static_cast<uint16_t*>(o);
+  fa.geo = ctx.geo;
+  fa.H = H;
+  hipError_t e = gdn::launch_finalize(kda != 0, fa, stream);
+  if (e != hipSuccess) return hip_fail(e, "finalize launch");
+  return GDN_OK;
+}
+
+}  // extern "C"

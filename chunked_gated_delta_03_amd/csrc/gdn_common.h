@@ -1,0 +1,101 @@
+// Device-side helpers shared by the gfx950 kernels of the chunked
+// gated-delta-rule forward pass: bf16 packing, MFMA wrappers, chunk geometry.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kChunk = 64;   // tokens per chunk
+constexpr int kDim = 128;    // K == V
+constexpr int kVecRows = 8;  // per-chunk vectors written by prepare
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint16_t u16x4;
+typedef __attribute__((ext_vector_type(8))) uint16_t u16x8;
+
+// ---- bf16 <-> fp32 -------------------------------------------------------
+__device__ __forceinline__ float bf2f(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+// Round to nearest even. Inputs here are finite.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+// hi = bf16(x), lo = bf16(x - hi): hi + lo carries ~16 significant bits.
+__device__ __forceinline__ void split_bf(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f2bf(x);
+  lo = f2bf(x - bf2f(hi));
+}
+
+// ---- MFMA ------------------------------------------------------------------
+// v_mfma_f32_16x16x32_bf16, wave64. Lane l: A row (l % 16), B column (l % 16),
+// both holding contraction slots 8*(l/16) .. 8*(l/16)+7; D column (l % 16),
+// rows 4*(l/16) .. 4*(l/16)+3. Only the pairing of slots between A and B
+// matters, so callers may map slots to any contraction indices as long as A
+// and B agree.
+__device__ __forceinline__ f32x4 mfma16(const u16x8& a, const u16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u16x8 cat4(const u16x4& a, const u16x4& b) {
+  return u16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// ---- chunk geometry ----------------------------------------------------------
+// A chunk is at most 64 consecutive tokens of one sequence. Dense input:
+// sequence n is batch row n and chunk j of it starts at token n*T + 64*j.
+// Packed input: tables built on the host from cu_seqlens.
+struct ChunkInfo {
+  int tok0;  // first token (flat index into the [B*T] token axis)
+  int len;   // valid rows, 1..64
+  int seq;   // sequence index n
+  int j;     // chunk index inside the sequence
+};
+struct SeqInfo {
+  int tok0;
+  int len;
+  int c0;    // global index of the sequence's first chunk
+  int nch;   // chunks in the sequence
+};
+
+struct Geometry {
+  const int4* ctab;  // [NT] {tok0, len, seq, j} or nullptr (dense)
+  const int4* stab;  // [N]  {tok0, len, c0, nch} or nullptr (dense)
+  int T;             // dense sequence length
+  int ncb;           // dense chunks per sequence = ceil(T/64)
+  int NT;            // total chunks
+  int N;             // sequences
+
+  __device__ __forceinline__ ChunkInfo chunk(int c) const {
+    ChunkInfo ci;
+    if (ctab) {
+      int4 e = ctab[c];
+      ci.tok0 = e.x; ci.len = e.y; ci.seq = e.z; ci.j = e.w;
+    } else {
+      int n = c / ncb, j = c - n * ncb;
+      ci.seq = n; ci.j = j;
+      ci.tok0 = n * T + j * kChunk;
+      int rem = T - j * kChunk;
+      ci.len = rem < kChunk ? rem : kChunk;
+    }
+    return ci;
+  }
+  __device__ __forceinline__ SeqInfo seq(int n) const {
+    SeqInfo si;
+    if (stab) {
+      int4 e = stab[n];
+      si.tok0 = e.x; si.len = e.y; si.c0 = e.z; si.nch = e.w;
+    } else {
+      si.tok0 = n * T; si.len = T; si.c0 = n * ncb; si.nch = ncb;
+    }
+    return si;
+  }
+};
+
+}  // namespace gdn

@@ -1,0 +1,162 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) chunked gated-delta-rule forward pass.
+ *
+ * The operation (Gated DeltaNet, and Kimi Delta Attention with a per-channel
+ * gate) is the recurrence, per sequence and head, with the state S kept as a
+ * K x V matrix:
+ *
+ *     S_t = Decay_t(S_{t-1});  S_t += beta_t k_t (v_t - S_t^T k_t)^T;
+ *     o_t = scale * S_t^T q_t
+ *
+ * with Decay_t(S) = exp(g_t) S for GDN (g natural-log, one scalar per token
+ * and head) and Decay_t(S)[d,:] = 2^(g_t[d]) S[d,:] for KDA (g in log2 units,
+ * one value per token, head and key channel). q/k may be L2-normalised in
+ * the kernel (x / sqrt(sum x^2 + 1e-6)) and beta may be passed as logits
+ * (sigmoid in the kernel). Sources, by page title and function:
+ *   - the eager chunk algorithm, the L2-norm helper and the K x V state
+ *     orientation: hyper-parallel "Diff Coverage" page, gate build
+ *     2026-09-10 (torch_chunk_gated_delta_rule, _l2norm,
+ *     _prepare_gdn_chunks_for_summary, _run_prepared_gdn_chunks);
+ *   - the native fused-forward flags (q/k L2-norm, sigmoid(beta), layout,
+ *     cu_seqlens) and the contract checks: "Diff Coverage" page, gate build
+ *     2026-11-06 (_load_ops, _packed_offsets, the Ascend C GDN adapter);
+ *   - the prepare / chunk_fwd_h / finalize stage split, the host chunk table,
+ *     packed B=1 rule and chunk size 64: the coverage page of
+ *     kimi_delta_attention_ascendc.py (_packed_metadata, ascendc_chunk_kda,
+ *     _AscendCKDAStages.forward).
+ *
+ * Contract shared by every entry point
+ * ------------------------------------
+ *   Sizes: K == V == 128, chunk size 64 (GDN_ERR_UNSUPPORTED otherwise).
+ *   B >= 1, T >= 1, H >= 1, scale finite and > 0.
+ *   q, k   bf16 [B,T,H,K], v bf16 [B,T,H,V], beta bf16 [B,T,H], o bf16
+ *          [B,T,H,V]: contiguous, token-major; device pointers.
+ *   g      fp32 device pointer, [B,T,H] (GDN) or [B,T,H,K] (KDA).
+ *   Packed input: cu_seqlens != NULL is a HOST int32 array of num_seqs+1
+ *          offsets, strictly increasing from 0 to T (so no empty document);
+ *          B must be 1. The library copies it before returning, so the caller
+ *          may free it at once. Documents need not be multiples of 64: the
+ *          last chunk of each document is partial. Chunks never span
+ *          documents. Dense input: cu_seqlens == NULL and num_seqs == B.
+ *   States: initial_state fp32 [N,H,K,V] device pointer or NULL (= zeros);
+ *          final_state fp32 [N,H,K,V], written when non-NULL and flags has
+ *          GDN_OUTPUT_FINAL_STATE. N = num_seqs.
+ *   Ownership: the caller allocates every buffer. The library reads the
+ *          inputs, writes only the outputs and the workspace, and keeps no
+ *          pointer after it returns.
+ *   Stream: `stream` is a hipStream_t (NULL = the null stream). All work is
+ *          enqueued on it; nothing is synchronised. The device is the one
+ *          current on the calling thread.
+ *   Workspace: device memory of at least the size the matching
+ *          *_workspace_bytes call returns. NULL means the library allocates
+ *          it stream-ordered (hipMallocAsync) and frees it on the same stream.
+ *   Errors: a non-zero status means nothing was launched and nothing was
+ *          written (except for GDN_ERR_HIP raised by a launch, after which the
+ *          outputs are undefined). gdn_last_error() gives the message of the
+ *          calling thread's last failure.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_OK 0
+#define GDN_ERR_INVALID_ARGUMENT 1 /* shape, pointer, offsets, scale, flags */
+#define GDN_ERR_UNSUPPORTED 2      /* K/V != 128, device not gfx950 */
+#define GDN_ERR_HIP 3              /* HIP runtime or launch failure */
+
+#define GDN_L2NORM_QK 1u          /* normalise q and k rows in the kernel */
+#define GDN_BETA_SIGMOID 2u       /* beta holds logits: beta = 1/(1+exp(-x)) */
+#define GDN_OUTPUT_FINAL_STATE 4u /* write final_state */
+
+#define GDN_CHUNK 64
+#define GDN_HEAD_DIM 128
+#define GDN_VEC_ROWS 8 /* per-chunk vectors in the prepare output, see below */
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* gdn_last_error(void);
+
+/* Number of 64-token chunks over all sequences: sum over documents of
+ * ceil(len/64) (dense: B * ceil(T/64)). Returns a status; *num_chunks is set
+ * on success. Follows the chunk table of _packed_metadata on the coverage
+ * page of kimi_delta_attention_ascendc.py. */
+int gdn_num_chunks(int32_t B, int32_t T, int32_t num_seqs, const int32_t* cu_seqlens, int64_t* num_chunks);
+
+/* Workspace bytes for gdn_chunk_fwd / kda_chunk_fwd (0 on invalid arguments;
+ * gdn_last_error() then says why). */
+size_t gdn_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                     int32_t num_seqs, const int32_t* cu_seqlens, uint32_t flags);
+size_t kda_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                     int32_t num_seqs, const int32_t* cu_seqlens, uint32_t flags);
+
+/* Whole forward pass, GDN (scalar natural-log gate g [B,T,H]). Computes o
+ * and, with GDN_OUTPUT_FINAL_STATE, final_state, exactly as the recurrence
+ * above (the chunked algorithm of torch_chunk_gated_delta_rule on the
+ * 2026-09-10 "Diff Coverage" page is the method). */
+int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                  int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, float scale, uint32_t flags,
+                  void* o, float* final_state, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Whole forward pass, KDA (per-key-channel log2 gate g [B,T,H,K]; the
+ * chunk-local cumulative log2 decay slot gk of the KDA prepare stage on the
+ * kimi_delta_attention_ascendc.py coverage page). Same arguments otherwise. */
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                  int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, float scale, uint32_t flags,
+                  void* o, float* final_state, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stage entry points (the prepare / chunk_fwd_h / finalize split of
+ * _AscendCKDAStages.forward on the kimi_delta_attention_ascendc.py coverage
+ * page). The whole-pass entries above run the same prepare kernel followed by
+ * a kernel that fuses chunk_fwd_h and finalize; these entries expose the
+ * chunk-form intermediates for parity checks. NT is gdn_num_chunks(); chunk
+ * c is global (documents in order, chunks in order inside a document).
+ * Every intermediate is head-major with 64 rows per chunk; rows of a partial
+ * chunk past the end of its document are zero.
+ *
+ *   tmat [H,NT,64,64] fp32  T = (I + strictLower(diag(beta) Kn Kn^T * Gamma))^-1,
+ *                          the forward-substitution result plus identity
+ *                          (GDN: Gamma[i,j] = exp(G_i - G_j); KDA: per channel
+ *                          inside the sum), Kn the normalised keys.
+ *   aqk  [H,NT,64,64] bf16 scale * (Qn Kn^T * Gamma), lower triangle with the
+ *                          diagonal, zero above.
+ *   vec  [H,NT,8,64]  fp32 per-row vectors of the chunk, row r:
+ *                          0 beta (after the sigmoid when flagged)
+ *                          1 GDN: beta*rk*exp(G)      KDA: beta
+ *                          2 GDN: rk*exp(G_last - G)  KDA: rk
+ *                          3 GDN: scale*rq*exp(G)     KDA: scale*rq
+ *                          4 GDN: G (natural log)     KDA: 0
+ *                          5 rq   6 rk   (1/sqrt(sum x^2 + 1e-6), or 1)
+ *                          7 entry 0: GDN exp(G_last), KDA 0; others 0
+ *                          with G the chunk-local cumulative sum of g.
+ *   gk   [H,NT,64,128] fp32 (KDA only, else NULL) chunk-local cumulative
+ *                          log2 gate per key channel.
+ *   h    [H,NT,128,128] fp32 state entering each chunk (K x V).
+ *   v_new [H,NT,64,128] fp32 U - W S for each chunk.
+ */
+int gdn_stage_prepare(int32_t kda, const void* q, const void* k, const float* g, const void* beta,
+                      const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+                      int32_t K, int32_t V, float scale, uint32_t flags,
+                      float* tmat, void* aqk, float* vec, float* gk, void* stream);
+
+int gdn_stage_fwd_h(int32_t kda, const void* k, const void* v, const float* tmat, const float* vec,
+                    const float* gk, const float* initial_state, const int32_t* cu_seqlens,
+                    int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                    uint32_t flags, float* h, float* v_new, float* final_state, void* stream);
+
+int gdn_stage_finalize(int32_t kda, const void* q, const void* aqk, const float* vec, const float* gk,
+                       const float* h, const float* v_new, const int32_t* cu_seqlens, int32_t num_seqs,
+                       int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, void* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -143,6 +143,19 @@ def _chunk_one(q, k, v, beta, g, scale, s0, C, kda, keep):
     return o, S, inter
 
 
+def _row_vectors(beta, rq, rk, C):
+    """Per-row beta (after the optional sigmoid) and the normalisation factors
+    1/sqrt(sum x^2 + 1e-6) (1 without normalisation), chunked [B,H,NC,C] with
+    zero padding."""
+    B, H, T = beta.shape
+    pad = (C - T % C) % C
+    out = {}
+    for name, x in (("beta", beta), ("rq", rq), ("rk", rk)):
+        x = np.concatenate([x, np.zeros((B, H, pad))], axis=2) if pad else x
+        out[name] = x.reshape(B, H, -1, C)
+    return out
+
+
 def chunk(inp, chunk_size: int = 64, flags: Optional[int] = None, keep: bool = False):
     """Chunked fp64 forward on a :class:`gdn_inputs.GdnInputs` problem.
 
@@ -157,7 +170,11 @@ def chunk(inp, chunk_size: int = 64, flags: Optional[int] = None, keep: bool = F
     v = decode_bf16(inp.v)
     beta = decode_bf16(inp.beta)
     g = np.asarray(inp.g, dtype=np.float64)
+    rq = np.ones(q.shape[:3])
+    rk = np.ones(k.shape[:3])
     if flags & 1:
+        rq = 1.0 / np.sqrt((q * q).sum(-1) + 1e-6)
+        rk = 1.0 / np.sqrt((k * k).sum(-1) + 1e-6)
         q = l2norm(q)
         k = l2norm(k)
     if flags & 2:
@@ -175,6 +192,8 @@ def chunk(inp, chunk_size: int = 64, flags: Optional[int] = None, keep: bool = F
         o, S, inter = _chunk_one(hm(q), hm(k), hm(v), hm(beta), hm(g), inp.scale, s0, chunk_size, inp.kda, keep)
         o_all[:] = np.moveaxis(o, 1, 2)
         fs[:] = S
+        if keep:
+            inter.update(_row_vectors(hm(beta), hm(rq), hm(rk), chunk_size))
         inters.append(inter)
     else:
         cu = [int(x) for x in inp.cu_seqlens]
@@ -185,5 +204,7 @@ def chunk(inp, chunk_size: int = 64, flags: Optional[int] = None, keep: bool = F
                                      chunk_size, inp.kda, keep)
             o_all[:, a:b] = np.moveaxis(o, 1, 2)
             fs[n] = S[0]
+            if keep:
+                inter.update(_row_vectors(sl(beta), sl(rq), sl(rk), chunk_size))
             inters.append(inter)
     return o_all, fs, (inters if keep else None)

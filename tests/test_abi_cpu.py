@@ -1,0 +1,119 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/gdn.h declares, and rejects invalid arguments before any HIP call
+(status code + message, nothing launched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import chunked_gated_delta_03_amd as m
+    return m
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    for must in ("gdn_chunk_fwd", "kda_chunk_fwd", "gdn_last_error", "gdn_chunk_fwd_workspace_bytes",
+                 "gdn_stage_prepare", "gdn_stage_fwd_h", "gdn_stage_finalize", "gdn_num_chunks"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(gdn):
+    lib = ctypes.CDLL(gdn.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert set(gdn.EXPORTED) <= set(_declared_functions())
+
+
+FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced by the validation paths
+
+
+def _call_fwd(gdn, B=1, T=64, H=2, K=128, V=128, cu=None, num_seqs=None, scale=0.1, flags=4, q=FAKE, o=FAKE,
+              fs=FAKE, kda=False):
+    cu_arr = None if cu is None else np.asarray(cu, dtype=np.int32)
+    n = (B if cu is None else len(cu) - 1) if num_seqs is None else num_seqs
+    fn = gdn.lib.kda_chunk_fwd if kda else gdn.lib.gdn_chunk_fwd
+    return fn(q, FAKE, FAKE, FAKE, FAKE, None, None if cu_arr is None else cu_arr.ctypes.data_as(ctypes.c_void_p),
+              n, B, T, H, K, V, scale, flags, o, fs, None, 0, None)
+
+
+@pytest.mark.parametrize("kda", [False, True])
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(B=0), 1, "B, T and H"),
+    (dict(T=0), 1, "B, T and H"),
+    (dict(H=0), 1, "B, T and H"),
+    (dict(K=64), 2, "K = V = 128"),
+    (dict(V=256), 2, "K = V = 128"),
+    (dict(scale=0.0), 1, "scale"),
+    (dict(scale=float("nan")), 1, "scale"),
+    (dict(scale=-1.0), 1, "scale"),
+    (dict(flags=8), 1, "unknown flag"),
+    (dict(q=None), 1, "non-NULL"),
+    (dict(q=ctypes.c_void_p(0x100002)), 1, "aligned"),
+    (dict(o=None), 1, "o must be non-NULL"),
+    (dict(fs=None), 1, "final_state is NULL"),
+    (dict(B=2, num_seqs=3), 1, "num_seqs == B"),
+    (dict(B=2, T=10, cu=[0, 4, 10]), 1, "B == 1"),
+    (dict(T=10, cu=[1, 4, 10]), 1, "cu_seqlens[0]"),
+    (dict(T=10, cu=[0, 4, 4, 10]), 1, "strictly increasing"),
+    (dict(T=10, cu=[0, 6, 4, 10]), 1, "strictly increasing"),
+    (dict(T=10, cu=[0, 4, 9]), 1, "must equal T"),
+    (dict(T=10, cu=[0, 4, 10], num_seqs=0), 1, "num_seqs"),
+])
+def test_invalid_arguments_rejected(gdn, kw, code, msg, kda):
+    rc = _call_fwd(gdn, kda=kda, **kw)
+    assert rc == code
+    assert msg in gdn.last_error()
+
+
+def test_num_chunks(gdn):
+    assert gdn.num_chunks(1, 1) == 1
+    assert gdn.num_chunks(3, 64) == 3
+    assert gdn.num_chunks(3, 65) == 6
+    assert gdn.num_chunks(1, 150, [0, 1, 18, 82, 150]) == 1 + 1 + 1 + 2
+    with pytest.raises(gdn.GdnError):
+        gdn.num_chunks(1, 150, [0, 100, 90, 150])
+
+
+def test_workspace_bytes(gdn):
+    a = gdn.workspace_bytes(4, 4096, 16)
+    nt = 4 * 64
+    per = 64 * 64 * 4 + 64 * 64 * 2 + 8 * 64 * 4
+    assert a >= 16 * nt * per
+    assert a % 256 == 0
+    b = gdn.workspace_bytes(1, 150, 16, cu_seqlens=[0, 1, 18, 82, 150])
+    assert b >= 16 * 5 * per + 16 * (5 + 4)
+    k = gdn.workspace_bytes(2, 8192, 32, kda=True)
+    assert k >= 32 * 2 * 128 * (per + 64 * 128 * 4)
+    with pytest.raises(gdn.GdnError):
+        gdn.workspace_bytes(1, 10, 4, cu_seqlens=[0, 11])
+
+
+def test_stage_entries_validate_before_device(gdn):
+    rc = gdn.lib.gdn_stage_prepare(0, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 2, 128, 128, 0.1, 0,
+                                   None, FAKE, FAKE, None, None)
+    assert rc == gdn.GDN_ERR_INVALID_ARGUMENT
+    rc = gdn.lib.gdn_stage_fwd_h(0, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, 1, 64, 2, 128, 128, 4,
+                                 FAKE, FAKE, None, None)
+    assert rc == gdn.GDN_ERR_INVALID_ARGUMENT and "final_state" in gdn.last_error()
+    rc = gdn.lib.gdn_stage_finalize(0, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 1, 1, 64, 2, 64, 64, FAKE, None)
+    assert rc == gdn.GDN_ERR_UNSUPPORTED
+
+
+def test_python_wrapper_checks_shapes(gdn):
+    import torch
+    q = torch.zeros((1, 8, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        gdn.gdn_chunk_fwd(q, q, q, torch.zeros((1, 8, 2)), torch.zeros((1, 8, 2), dtype=torch.bfloat16))

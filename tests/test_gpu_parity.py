@@ -1,0 +1,217 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Stage tests compare each kernel's output with the chunk-form intermediates of
+``oracle.chunk``; end-to-end tests compare o and the final state with the
+token recurrence ``oracle.recur`` (max |o - o_ref| <= 2e-2, max |S - S_ref| /
+max |S_ref| <= 1e-3). Full-size workloads are checked on (sequence, head)
+units sampled from the same launch the benchmark times.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import gdn_inputs as gi
+import oracle
+from gpu_util import O_ATOL, S_RTOL, hm_chunks, o_err, run_gpu, s_err, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import chunked_gated_delta_03_amd as m
+    return m
+
+
+def _problems_reduced():
+    rng = np.random.default_rng(77)
+    out = [
+        ("tiny", gi.make_inputs("tiny")),
+        ("gdn_B2_T300_H3", gi.make_inputs("gdn", B=2, T=300, H=3)),
+        ("gdn_T1", gi.make_inputs("gdn", B=3, T=1, H=2)),
+        ("gdn_T63", gi.make_inputs("gdn", B=1, T=63, H=2)),
+        ("gdn_T64", gi.make_inputs("gdn", B=2, T=64, H=2)),
+        ("gdn_T65", gi.make_inputs("gdn", B=1, T=65, H=2)),
+        ("gdn_T127", gi.make_inputs("gdn", B=1, T=127, H=3)),
+        ("varlen_docs", gi.make_inputs("varlen", H=3, doc_lengths=[1, 17, 63, 64, 65, 130, 200])),
+        ("varlen_one_doc", gi.make_inputs("varlen", H=2, doc_lengths=[333])),
+        ("long_T2048_H2", gi.make_inputs("long", T=2048, H=2)),
+        ("mild_gate_init", gi.random_problem(rng, 2, 250, 2, 128, 128, gate_scale=0.01, with_initial_state=True)),
+        ("host_normalised_B2_T300_H3", gi.make_inputs("tiny", B=2, T=300, H=3)),
+    ]
+    return out
+
+
+REDUCED = _problems_reduced()
+
+
+@pytest.mark.parametrize("name,inp", REDUCED, ids=[n for n, _ in REDUCED])
+def test_end_to_end_reduced(gdn, name, inp):
+    _say("case", name, "B,T,H =", inp.B, inp.T, inp.H, "docs", None if inp.cu_seqlens is None else len(inp.cu_seqlens) - 1)
+    o_ref, s_ref = oracle.recur(inp)
+    o, fs = run_gpu(inp)
+    assert np.isfinite(o).all()
+    eo = o_err(o, o_ref)
+    es = s_err(fs, s_ref)
+    _say("  o max-abs err %.3e   final-state rel err %.3e" % (eo, es))
+    assert eo <= O_ATOL
+    assert es <= S_RTOL
+
+
+def test_stage_parity(gdn):
+    """Each stage against the chunk-form intermediates of the oracle."""
+    for name, inp in [("tiny", gi.make_inputs("tiny")),
+                      ("gdn_B2_T200_H2", gi.make_inputs("gdn", B=2, T=200, H=2)),
+                      ("varlen", gi.make_inputs("varlen", H=2, doc_lengths=[17, 64, 100]))]:
+        _say("stage case", name)
+        d = to_device(inp)
+        l2, sig = bool(inp.flags & 1), bool(inp.flags & 2)
+        tmat, aqk, vec, _ = gdn.gdn_stage_prepare(d["q"], d["k"], d["g"], d["beta"], scale=inp.scale,
+                                                  cu_seqlens=inp.cu_seqlens, l2norm_qk=l2, beta_sigmoid=sig)
+        torch.cuda.synchronize()
+        _, _, inters = oracle.chunk(inp, keep=True)
+        dense = inp.cu_seqlens is None
+        T_ref = hm_chunks([it["T"] for it in inters], dense)
+        A_ref = hm_chunks([it["Aqk"] for it in inters], dense)
+        G_ref = hm_chunks([it["G"] for it in inters], dense)
+        b_ref = hm_chunks([it["beta"] for it in inters], dense)
+        rq_ref = hm_chunks([it["rq"] for it in inters], dense)
+        rk_ref = hm_chunks([it["rk"] for it in inters], dense)
+        tm = tmat.cpu().numpy().astype(np.float64)
+        assert np.abs(tm - T_ref).max() <= 1e-4 * max(1.0, np.abs(T_ref).max())
+        aq = aqk.float().cpu().numpy().astype(np.float64)
+        assert np.abs(aq - A_ref).max() <= 1e-2 * max(1e-3, np.abs(A_ref).max())
+        vc = vec.cpu().numpy().astype(np.float64)
+        np.testing.assert_allclose(vc[:, :, 4], G_ref, rtol=1e-5, atol=1e-4)
+        np.testing.assert_allclose(vc[:, :, 0], b_ref, rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(vc[:, :, 5], rq_ref, rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(vc[:, :, 6], rk_ref, rtol=1e-5, atol=1e-6)
+
+        s0 = d["initial_state"]
+        h, v_new, fs = gdn.gdn_stage_fwd_h(d["k"], d["v"], tmat, vec, initial_state=s0, cu_seqlens=inp.cu_seqlens)
+        torch.cuda.synchronize()
+        h_ref = hm_chunks([it["h"] for it in inters], dense)
+        vn_ref = hm_chunks([it["v_new"] for it in inters], dense)
+        hh = h.cpu().numpy().astype(np.float64)
+        vn = v_new.cpu().numpy().astype(np.float64)
+        eh = np.abs(hh - h_ref).max() / max(np.abs(h_ref).max(), 1e-30)
+        ev = np.abs(vn - vn_ref).max() / max(np.abs(vn_ref).max(), 1e-30)
+        _say("  h rel err %.3e  v_new rel err %.3e" % (eh, ev))
+        assert eh <= 1e-3 and ev <= 1e-3
+        _, s_ref = oracle.recur(inp)
+        assert s_err(fs.cpu().numpy().astype(np.float64), s_ref) <= S_RTOL
+
+        # finalize alone, fed the oracle's h and v_new
+        o = gdn.gdn_stage_finalize(d["q"], aqk, vec, torch.from_numpy(h_ref.astype(np.float32)).cuda(),
+                                   torch.from_numpy(vn_ref.astype(np.float32)).cuda(), cu_seqlens=inp.cu_seqlens)
+        torch.cuda.synchronize()
+        o_ref, _ = oracle.recur(inp)
+        assert o_err(o.float().cpu().numpy().astype(np.float64), o_ref) <= O_ATOL
+
+
+def test_fused_matches_stage_path(gdn):
+    inp = gi.make_inputs("gdn", B=2, T=500, H=4)
+    d = to_device(inp)
+    tmat, aqk, vec, _ = gdn.gdn_stage_prepare(d["q"], d["k"], d["g"], d["beta"], scale=inp.scale,
+                                              l2norm_qk=True, beta_sigmoid=True)
+    h, v_new, fs1 = gdn.gdn_stage_fwd_h(d["k"], d["v"], tmat, vec)
+    o1 = gdn.gdn_stage_finalize(d["q"], aqk, vec, h, v_new)
+    o2, fs2 = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=inp.scale, l2norm_qk=True,
+                                beta_sigmoid=True)
+    torch.cuda.synchronize()
+    assert torch.equal(fs1, fs2)
+    assert (o1.float() - o2.float()).abs().max().item() <= 1e-2
+
+
+def test_deterministic(gdn):
+    inp = gi.make_inputs("varlen", H=4, doc_lengths=[100, 1, 300, 64])
+    a = run_gpu(inp)
+    b = run_gpu(inp)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_no_final_state_flag(gdn):
+    inp = gi.make_inputs("gdn", B=1, T=130, H=2)
+    inp.flags &= ~gi.FLAG_OUTPUT_FINAL_STATE
+    o, fs = run_gpu(inp)
+    assert fs is None
+    o_ref, _ = oracle.recur(inp)
+    assert o_err(o, o_ref) <= O_ATOL
+
+
+def test_caller_workspace_and_errors(gdn):
+    inp = gi.make_inputs("gdn", B=1, T=100, H=2)
+    need = gdn.workspace_bytes(1, 100, 2)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o, fs = run_gpu(inp, workspace=ws)
+    o_ref, s_ref = oracle.recur(inp)
+    assert o_err(o, o_ref) <= O_ATOL and s_err(fs, s_ref) <= S_RTOL
+    d = to_device(inp)
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=-1.0)
+    assert e.value.code == gdn.GDN_ERR_INVALID_ARGUMENT
+    q64 = torch.zeros((1, 8, 2, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.gdn_chunk_fwd(q64, q64, q64, torch.zeros((1, 8, 2), device="cuda"),
+                          torch.zeros((1, 8, 2), dtype=torch.bfloat16, device="cuda"))
+    assert e.value.code == gdn.GDN_ERR_UNSUPPORTED
+
+
+def _sampled(inp, units):
+    o_ref, s_ref = oracle.recur(inp, units=units)
+    return o_ref, s_ref
+
+
+def _check_units(inp, o, fs, o_ref, s_ref, units):
+    cu = inp.cu_seqlens
+    for n, h in units:
+        if cu is None:
+            eo = np.abs(o[n, :, h] - o_ref[n, :, h]).max()
+        else:
+            a, b = int(cu[n]), int(cu[n + 1])
+            eo = np.abs(o[0, a:b, h] - o_ref[0, a:b, h]).max()
+        es = np.abs(fs[n, h] - s_ref[n, h]).max() / max(np.abs(s_ref[n, h]).max(), 1e-30)
+        _say("  unit (%d,%d): o err %.3e  S rel err %.3e" % (n, h, eo, es))
+        assert eo <= O_ATOL and es <= S_RTOL
+
+
+def test_full_size_gdn_sampled(gdn):
+    """B=4 T=4096 H=16, the benchmarked launch; 6 sampled (sequence, head) units."""
+    inp = gi.make_inputs("gdn")
+    _say("full-size gdn: generating done")
+    o, fs = run_gpu(inp)
+    assert np.isfinite(o).all() and np.isfinite(fs).all()
+    units = [(0, 0), (1, 5), (2, 9), (3, 15), (0, 15), (3, 0)]
+    o_ref, s_ref = _sampled(inp, units)
+    _check_units(inp, o, fs, o_ref, s_ref, units)
+
+
+def test_full_size_varlen_sampled(gdn):
+    """Packed T=32768 H=16, documents ~U[17,8192]; every document, 2 heads each."""
+    inp = gi.make_inputs("varlen")
+    N = inp.num_seqs
+    _say("full-size varlen: %d documents" % N)
+    o, fs = run_gpu(inp)
+    units = [(n, (3 * n) % inp.H) for n in range(N)] + [(n, (3 * n + 7) % inp.H) for n in range(N)]
+    o_ref, s_ref = _sampled(inp, units)
+    _check_units(inp, o, fs, o_ref, s_ref, units)
+
+
+def test_full_size_long_sampled(gdn):
+    """B=1 T=131072 H=32 (2048 sequential chunks); 2 sampled heads."""
+    inp = gi.make_inputs("long")
+    _say("full-size long: inputs ready")
+    o, fs = run_gpu(inp)
+    units = [(0, 0), (0, 31)]
+    o_ref, s_ref = _sampled(inp, units)
+    _check_units(inp, o, fs, o_ref, s_ref, units)
