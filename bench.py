@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked gated-delta-rule forward pass on one MI355X.
+
+One step = one call of gdn_chunk_fwd (kda_chunk_fwd for the KDA workload) over
+the whole synthetic batch: the prepare kernel and the fused state/output
+kernel, inputs resident in HBM, workspace preallocated. Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload gdn|varlen|long|kda|tiny]
+                    [--no-cpu-baseline]
+
+The default workload is B=4 T=4096 H=16 K=V=128 (GDN, in-kernel L2-norm and
+sigmoid(beta), final state on), the configuration the headline metric is
+quoted on. Only one GPU is used: --gpus above 1 is refused.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd tokens/s, GDN H=16 K=V=128 T=4096 B=4; % bf16 MFMA peak"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+# Algorithmic work per token-head (q, k, v bf16 + gate + beta + o bf16), and
+# its split between the two kernels by first touch of the algorithm's inputs
+# and outputs: prepare reads q, k, g, beta; the state/output kernel reads v
+# and writes o and the states.
+GDN_PREP_BYTES = 256 + 256 + 4 + 2
+KDA_PREP_BYTES = 256 + 256 + 512 + 2
+STATE_BYTES = 256 + 256
+STATE_BYTES_PER_UNIT = 128 * 128 * 4  # one fp32 state per (sequence, head), each of initial/final
+ALG_FLOPS_PER_TH = 140629             # conservative (triangle-exploiting) count
+
+
+KERNEL_SOURCES = ("gdn_common.h", "gdn_kernels.h", "gdn_prepare.hip", "gdn_fwd.hip")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources; HBM counters recorded for other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "chunked_gated_delta_03_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, kernel_name_part: str):
+    """Scaled HBM bytes per launch of a kernel from the committed counter
+    summary of this workload, or None if absent or taken on other sources."""
+    import glob
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*_hbm_counters.json")):
+        with open(path) as f:
+            d = json.load(f)
+        if d.get("workload") != workload or d.get("kernel_source_hash") != kernel_source_hash():
+            continue
+        for name, rec in d["kernels"].items():
+            if kernel_name_part in name:
+                return rec["hbm_bytes_scaled"]
+    return None
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gdn", choices=["gdn", "varlen", "long", "kda", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run plain device-to-device copies of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def calibrate_copy(mib: int, reps: int = 5) -> None:
+    """Plain copies of a known size: the FETCH_SIZE / WRITE_SIZE counters of
+    this copy kernel give the scale factor between counter and true bytes."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the forward pass is benchmarked on a single MI355X "
+              "(--gpus %d / WORLD_SIZE %d refused)." % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import chunked_gated_delta_03_amd as gdn
+    import gdn_inputs as gi
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = gi.make_inputs(args.workload)
+    B, T, H, K, V = inp.B, inp.T, inp.H, inp.K, inp.V
+    N = inp.num_seqs
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(dev)
+    q, k, v, beta = bf(inp.q), bf(inp.k), bf(inp.v), bf(inp.beta)
+    g = torch.from_numpy(inp.g).to(dev)
+    s0 = None if inp.initial_state is None else torch.from_numpy(inp.initial_state).to(dev)
+    o = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
+    fs = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    ws_bytes = gdn.workspace_bytes(B, T, H, cu_seqlens=inp.cu_seqlens, kda=inp.kda, flags=inp.flags)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    cu = None if inp.cu_seqlens is None else np.ascontiguousarray(inp.cu_seqlens, dtype=np.int32)
+    cu_p = None if cu is None else cu.ctypes.data_as(ctypes.c_void_p)
+    stream = torch.cuda.current_stream(dev)
+    fn = gdn.lib.kda_chunk_fwd if inp.kda else gdn.lib.gdn_chunk_fwd
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    call_args = (P(q), P(k), P(v), P(g), P(beta), P(s0), cu_p, N, B, T, H, K, V, float(inp.scale), int(inp.flags),
+                 P(o), P(fs), P(ws), ws_bytes, ctypes.c_void_p(stream.cuda_stream))
+
+    def step():
+        rc = fn(*call_args)
+        if rc != 0:
+            raise RuntimeError("gdn call failed: %s" % gdn.last_error())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    gdn.timing_enable(True)
+    gdn.timing_read()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gdn.timing_enable(False)
+    prep_ms, state_ms, calls = gdn.timing_read()
+    assert calls == args.steps
+
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    wall_ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tokens = B * T
+    value = tokens / (ms_per_step * 1e-3)
+    th = tokens * H
+    prep_us = prep_ms * 1e3 / calls
+    state_us = state_ms * 1e3 / calls
+
+    n_states = (1 if inp.flags & gi.FLAG_OUTPUT_FINAL_STATE else 0) + (0 if s0 is None else 1)
+    prep_bytes = th * (KDA_PREP_BYTES if inp.kda else GDN_PREP_BYTES)
+    state_bytes = th * STATE_BYTES + n_states * N * H * STATE_BYTES_PER_UNIT
+    path_bytes = prep_bytes + state_bytes
+    kernels = {
+        "prepare": {"avg_us": prep_us, "alg_bytes": prep_bytes, "symbol": "prepare_kernel"},
+        "state_output": {"avg_us": state_us, "alg_bytes": state_bytes, "symbol": "fwd_kernel"},
+    }
+    dom_name = max(kernels, key=lambda n: kernels[n]["avg_us"])
+    dom = kernels[dom_name]
+    achieved = dom["alg_bytes"] / (dom["avg_us"] * 1e-6) / 1e9
+    roofline = {
+        "kernel": dom_name,
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": recorded_traffic(args.workload, dom["symbol"]),
+    }
+    path_gbps = path_bytes / (ms_per_step * 1e-3) / 1e9
+    mfma_frac = th * ALG_FLOPS_PER_TH / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        units = [(n, h) for n in range(N) for h in range(H)]
+        sample_desc = "whole workload"
+        budget_units = len(units)
+        if args.workload in ("long", "kda"):
+            budget_units = 8 if args.workload == "long" else 16
+            units = units[:budget_units]
+            sample_desc = "%d of %d (sequence, head) units" % (budget_units, N * H)
+        tok_units = sum((int(inp.cu_seqlens[n + 1] - inp.cu_seqlens[n]) if inp.cu_seqlens is not None else T)
+                        for n, _ in units)
+        # repeat the sample until about 10 s of CPU time has been measured
+        reps = 0
+        c0 = time.perf_counter()
+        while True:
+            oracle.recur(inp, units=units)
+            reps += 1
+            if time.perf_counter() - c0 >= 10.0 or reps >= 50:
+                break
+        c1 = time.perf_counter()
+        per = (c1 - c0) / reps
+        cpu = {
+            "value": round(tok_units / H / per, 1),
+            "unit": "tokens/s",
+            "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "fp64 token recurrence (C, OpenMP over units) on %s: %d token-heads, %.3f s per pass, "
+                      "%d passes; tokens/s = token-heads / H / s" % (sample_desc, tok_units, per, reps),
+        }
+
+    wl = {
+        "gdn": "GDN B=4 T=4096 H=16 K=V=128 chunk 64, in-kernel L2-norm + sigmoid(beta), final state",
+        "varlen": "packed GDN B=1 T=32768 H=16 docs~U[17,8192], per-doc initial/final state",
+        "long": "GDN B=1 T=131072 H=32 K=V=128 chunk 64",
+        "kda": "KDA B=2 T=8192 H=32 K=V=128 per-channel log2 gate",
+        "tiny": "GDN B=1 T=256 H=2",
+    }[args.workload]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl, "global_batch": B, "seq_len": T, "heads": H, "head_dim": K,
+                   "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "mfma_bf16_frac": round(mfma_frac, 4),
+        "path_alg_hbm_frac": round(path_gbps / HBM_PEAK_GBPS, 4),
+        "kernels_us": {"prepare": round(prep_us, 2), "state_output": round(state_us, 2)},
+        "wall_ms_per_step": round(wall_ms_per_step, 5),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -34,6 +34,7 @@ VEC_ROWS = 8
 EXPORTED = (
     "gdn_last_error", "gdn_num_chunks", "gdn_chunk_fwd_workspace_bytes", "kda_chunk_fwd_workspace_bytes",
     "gdn_chunk_fwd", "kda_chunk_fwd", "gdn_stage_prepare", "gdn_stage_fwd_h", "gdn_stage_finalize",
+    "gdn_timing_enable", "gdn_timing_read",
 )
 
 
@@ -63,6 +64,11 @@ def _load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p, p, sz, p]
+    lib.gdn_timing_enable.restype = ctypes.c_int
+    lib.gdn_timing_enable.argtypes = [i32]
+    lib.gdn_timing_read.restype = ctypes.c_int
+    lib.gdn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_int64)]
     lib.gdn_stage_prepare.restype = ctypes.c_int
     lib.gdn_stage_prepare.argtypes = [i32, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p, p, p, p]
     lib.gdn_stage_fwd_h.restype = ctypes.c_int
@@ -266,3 +272,15 @@ def gdn_stage_finalize(q, aqk, vec, h, v_new, gk=None, cu_seqlens=None, kda: boo
     _check(lib.gdn_stage_finalize(int(kda), _ptr(q), _ptr(aqk), _ptr(vec), _ptr(gk), _ptr(h), _ptr(v_new),
                                   _cu_ptr(cu), N, B, T, H, K, K, _ptr(o), _stream_ptr(q.device, stream)))
     return o
+
+
+def timing_enable(enable: bool = True) -> None:
+    """Record per-kernel HIP events in every whole-pass call of this thread."""
+    _check(lib.gdn_timing_enable(1 if enable else 0))
+
+
+def timing_read() -> Tuple[float, float, int]:
+    """(prepare ms summed, state/output ms summed, calls) since the last read."""
+    a, b, n = ctypes.c_double(0), ctypes.c_double(0), ctypes.c_int64(0)
+    _check(lib.gdn_timing_read(ctypes.byref(a), ctypes.byref(b), ctypes.byref(n)))
+    return a.value, b.value, int(n.value)

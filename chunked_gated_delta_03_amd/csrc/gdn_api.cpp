@@ -258,6 +258,35 @@ int acquire_workspace(void* ws, size_t ws_bytes, size_t need, hipStream_t stream
   return GDN_OK;
 }
 
+// Optional per-kernel timing of the whole-pass entries (benchmarks): while
+// enabled on the calling thread, each call records three events on its
+// stream (before prepare, between the kernels, after the state kernel).
+struct TimingRec {
+  hipEvent_t ev[3];
+};
+thread_local bool g_timing = false;
+thread_local std::vector<TimingRec> g_timing_recs;
+thread_local std::vector<TimingRec> g_timing_pool;
+
+int timing_mark(std::vector<TimingRec>& recs, int which, hipStream_t stream) {
+  if (which == 0) {
+    TimingRec r;
+    if (!g_timing_pool.empty()) {
+      r = g_timing_pool.back();
+      g_timing_pool.pop_back();
+    } else {
+      for (int i = 0; i < 3; ++i) {
+        hipError_t e = hipEventCreate(&r.ev[i]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate(timing)");
+      }
+    }
+    recs.push_back(r);
+  }
+  hipError_t e = hipEventRecord(recs.back().ev[which], stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(timing)");
+  return GDN_OK;
+}
+
 int check_common(const void* q, const void* k, const void* v, const float* g, const void* beta, float scale,
                  uint32_t flags) {
   if (!q || !k || !v || !g || !beta) return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g and beta must be non-NULL");
@@ -298,6 +327,7 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
     if (rc) return rc;
   }
   const gdn::Geometry geo = make_geometry(p, W.base + L.tab);
+  if (g_timing && (rc = timing_mark(g_timing_recs, 0, stream))) return rc;
 
   gdn::PrepareArgs pa{};
   pa.q = static_cast<const uint16_t*>(q);
@@ -314,6 +344,7 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
   pa.flags = flags;
   hipError_t e = gdn::launch_prepare(kda, pa, stream);
   if (e != hipSuccess) return hip_fail(e, "prepare launch");
+  if (g_timing && (rc = timing_mark(g_timing_recs, 1, stream))) return rc;
 
   gdn::FwdArgs fa{};
   fa.q = pa.q;
@@ -330,6 +361,7 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
   fa.H = H;
   e = gdn::launch_fwd(kda, false, true, fa, stream);
   if (e != hipSuccess) return hip_fail(e, "state/output launch");
+  if (g_timing && (rc = timing_mark(g_timing_recs, 2, stream))) return rc;
   return GDN_OK;
 }
 
@@ -413,6 +445,35 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   void* workspace, size_t workspace_bytes, void* stream) {
   return chunk_fwd(true, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, scale, flags, o,
                    final_state, workspace, workspace_bytes, stream);
+}
+
+int gdn_timing_enable(int32_t enable) {
+  g_last_error.clear();
+  g_timing = enable != 0;
+  return GDN_OK;
+}
+
+int gdn_timing_read(double* prepare_ms, double* state_ms, int64_t* calls) {
+  g_last_error.clear();
+  if (!prepare_ms || !state_ms || !calls) return fail(GDN_ERR_INVALID_ARGUMENT, "NULL output pointer");
+  double a = 0.0, b = 0.0;
+  for (TimingRec& r : g_timing_recs) {
+    hipError_t e = hipEventSynchronize(r.ev[2]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(timing)");
+    float t0 = 0.f, t1 = 0.f;
+    e = hipEventElapsedTime(&t0, r.ev[0], r.ev[1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    e = hipEventElapsedTime(&t1, r.ev[1], r.ev[2]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    a += t0;
+    b += t1;
+  }
+  *prepare_ms = a;
+  *state_ms = b;
+  *calls = (int64_t)g_timing_recs.size();
+  g_timing_pool.insert(g_timing_pool.end(), g_timing_recs.begin(), g_timing_recs.end());
+  g_timing_recs.clear();
+  return GDN_OK;
 }
 
 int gdn_stage_prepare(int32_t kda, const void* q, const void* k, const float* g, const void* beta,

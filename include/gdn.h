@@ -111,6 +111,16 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, float scale, uint32_t flags,
                   void* o, float* final_state, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Per-kernel timing of gdn_chunk_fwd / kda_chunk_fwd, for benchmarks. While
+ * enabled (per calling thread), every whole-pass call records three HIP
+ * events on its stream: before the prepare kernel, between the prepare and
+ * the state/output kernel, and after it. gdn_timing_read() waits for the
+ * recorded events, returns the summed milliseconds of each kernel and the
+ * number of calls, and clears the record. Events are created by the library
+ * and reused; they are never destroyed before the process ends. */
+int gdn_timing_enable(int32_t enable);
+int gdn_timing_read(double* prepare_ms, double* state_ms, int64_t* calls);
+
 /*
  * Stage entry points (the prepare / chunk_fwd_h / finalize split of
  * _AscendCKDAStages.forward on the kimi_delta_attention_ascendc.py coverage
