@@ -315,7 +315,6 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
     return fail(GDN_ERR_INVALID_ARGUMENT, "GDN_OUTPUT_FINAL_STATE set but final_state is NULL");
   rc = check_device();
   if (rc) return rc;
-  if (kda) return fail(GDN_ERR_UNSUPPORTED, "kda_chunk_fwd: per-channel gate path not built yet");
 
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const Layout L = layout_for(p, true);
@@ -380,7 +379,6 @@ int stage_begin(int32_t kda, const int32_t* cu_seqlens, int32_t num_seqs, int32_
   if (rc) return rc;
   rc = check_device();
   if (rc) return rc;
-  if (kda) return fail(GDN_ERR_UNSUPPORTED, "per-channel gate stages not built yet");
   const Layout L = layout_for(ctx.p, false);
   rc = acquire_workspace(nullptr, 0, L.total, stream, ctx.W);
   if (rc) return rc;

@@ -426,7 +426,7 @@ __global__ __launch_bounds__(256) void gdn_finalize_kernel(FinArgs a) {
 constexpr int kFwdWaves = 4;
 
 hipError_t launch_fwd(bool kda, bool store_h, bool compute_o, const FwdArgs& a, hipStream_t stream) {
-  if (kda) return hipErrorNotSupported;
+  if (kda) return launch_kda_fwd(store_h, compute_o, a, stream);
   dim3 grid(a.geo.N * a.H, kDim / (16 * kFwdWaves));
   dim3 block(64 * kFwdWaves);
   if (store_h && !compute_o)
@@ -439,7 +439,7 @@ hipError_t launch_fwd(bool kda, bool store_h, bool compute_o, const FwdArgs& a, 
 }
 
 hipError_t launch_finalize(bool kda, const FinArgs& a, hipStream_t stream) {
-  if (kda) return hipErrorNotSupported;
+  if (kda) return launch_kda_finalize(a, stream);
   dim3 grid(a.geo.NT, a.H);
   hipLaunchKernelGGL(gdn_finalize_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError();

@@ -1,5 +1,5 @@
-// Prepare kernel: everything of one (chunk, head) that does not depend on the
-// carried state. One workgroup of 4 waves per (chunk, head).
+// Prepare kernels: everything of one (chunk, head) that does not depend on
+// the carried state. One workgroup of 4 waves per (chunk, head).
 //
 // Steps of the eager chunk algorithm on the hyper-parallel "Diff Coverage"
 // page (gate build 2026-09-10; _prepare_gdn_chunks_for_summary), done here:
@@ -18,6 +18,16 @@
 // The WY products U = T v_beta and W = T (k_beta e^G) are not formed here:
 // the state kernel applies T to (beta v - c * (k S)) directly, which needs T
 // and the per-row vectors only.
+//
+// Kimi Delta Attention (per-key-channel gate in log2 units; the chunk-local
+// cumulative log2 decay gk of the KDA prepare stage on the coverage page of
+// kimi_delta_attention_ascendc.py): Gamma carries a channel index inside the
+// contraction, sum_d k_id k_jd 2^(G_id - G_jd). Between 16-row tiles I > J
+// it is an MFMA product of rows scaled against the reference row r = 16 I:
+// (k_i 2^(G_i - G_r)) . (k_j 2^(G_r - G_j)), both exponents <= 0 because
+// r lies between j and i. Inside a diagonal tile no such reference is safe for
+// an unbounded gate, so those pairs are summed elementwise with the mask
+// applied before the power.
 #include "gdn_kernels.h"
 
 namespace gdn {
@@ -25,7 +35,7 @@ namespace gdn {
 constexpr int kLdRow = kDim + 8;    // bf16 row stride of a 64 x 128 tile in LDS
 constexpr int kLdF = kChunk + 1;    // fp32 row stride of a 64 x 64 matrix in LDS
 constexpr int kLdQ = kChunk + 8;    // bf16 row stride of a 64 x 64 matrix in LDS
-
+constexpr int kLdG = kDim + 4;      // fp32 row stride of the 64 x 128 KDA gate
 
 __device__ __forceinline__ float sumsq8(const uint4& v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -40,29 +50,10 @@ __device__ __forceinline__ float sumsq8(const uint4& v) {
   return s;
 }
 
-__global__ __launch_bounds__(256) void gdn_prepare_kernel(PrepareArgs a) {
-  const int c = blockIdx.x;
-  const int h = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int g4 = lane >> 4;
-  const int l16 = lane & 15;
-  const ChunkInfo ci = a.geo.chunk(c);
-  const int H = a.H;
-
-  __shared__ uint16_t sk[kChunk * kLdRow];
-  __shared__ uint16_t sq[kChunk * kLdRow];
-  __shared__ float sA[kChunk * kLdF];
-  __shared__ float sT[kChunk * kLdF];
-  __shared__ float sP[4][16 * 17];
-  __shared__ uint16_t sAqk[kChunk * kLdQ];
-  __shared__ float sG[kChunk], sBeta[kChunk], sRq[kChunk], sRk[kChunk];
-
+// q, k rows of the chunk into LDS (zero past the end), normalisation factors.
+__device__ __forceinline__ void load_qk_norms(const PrepareArgs& a, const ChunkInfo& ci, int h, int tid,
+                                              uint16_t* sk, uint16_t* sq, float* sRk, float* sRq) {
   const bool l2 = (a.flags & 1u) != 0;
-  const bool sig = (a.flags & 2u) != 0;
-
-  // ---- 1. q, k rows into LDS; per-row normalisation factors ---------------
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int idx = pass * 256 + tid;
@@ -70,7 +61,7 @@ __global__ __launch_bounds__(256) void gdn_prepare_kernel(PrepareArgs a) {
     const int cc = (idx & 15) * 8;
     uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
     if (r < ci.len) {
-      const size_t off = ((size_t)(ci.tok0 + r) * H + h) * kDim + cc;
+      const size_t off = ((size_t)(ci.tok0 + r) * a.H + h) * kDim + cc;
       kv = *reinterpret_cast<const uint4*>(a.k + off);
       qv = *reinterpret_cast<const uint4*>(a.q + off);
     }
@@ -88,25 +79,137 @@ __global__ __launch_bounds__(256) void gdn_prepare_kernel(PrepareArgs a) {
       sRq[r] = valid ? (l2 ? 1.0f / sqrtf(ssq + 1e-6f) : 1.0f) : 0.0f;
     }
   }
+}
 
-  // ---- 2. gate cumsum and beta (wave 0) -------------------------------------
+// beta (with the optional sigmoid) by wave 0; zero past the end.
+__device__ __forceinline__ void load_beta(const PrepareArgs& a, const ChunkInfo& ci, int h, int lane,
+                                          float* sBeta) {
+  const bool valid = lane < ci.len;
+  float b = valid ? bf2f(a.beta[(size_t)(ci.tok0 + lane) * a.H + h]) : 0.0f;
+  if ((a.flags & 2u) && valid) b = 1.0f / (1.0f + expf(-b));
+  sBeta[lane] = b;
+}
+
+// T = (I - A)^-1 for strictly lower A (fp32, LDS), blockwise. All 256
+// threads call it; it ends with a barrier.
+__device__ __forceinline__ void invert_unit_lower(const float* sA, float* sT, float (*sP)[16 * 17], int wave,
+                                                  int lane) {
+  const int g4 = lane >> 4;
+  const int l16 = lane & 15;
+  // diagonal 16x16 blocks by forward substitution, one block per wave
+  if (lane < 16) {
+    const int base = 16 * wave;
+    float t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float val = (i == lane) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) val = fmaf(sA[(base + i) * kLdF + base + m], t[m], val);
+      t[i] = val;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sT[(base + i) * kLdF + base + lane] = t[i];
+  }
+  __syncthreads();
+  // off-diagonal blocks, one block row at a time:
+  // T_ij = T_ii * sum_{m=j}^{i-1} A_im T_mj ; lane holds (row l16, cols 4*g4..+3)
+  for (int I = 1; I < 4; ++I) {
+    const int J = wave;
+    if (J < I) {
+      float p[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int M = J; M < I; ++M) {
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const float av = sA[(16 * I + l16) * kLdF + 16 * M + x];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[e] = fmaf(av, sT[(16 * M + x) * kLdF + 16 * J + 4 * g4 + e], p[e]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sP[wave][l16 * 17 + 4 * g4 + e] = p[e];
+    }
+    __syncthreads();
+    if (J < I) {
+      float r[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const float tv = sT[(16 * I + l16) * kLdF + 16 * I + x];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = fmaf(tv, sP[wave][x * 17 + 4 * g4 + e], r[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sT[(16 * I + l16) * kLdF + 16 * J + 4 * g4 + e] = r[e];
+    }
+    __syncthreads();
+  }
+}
+
+// T (fp32) and Aqk (bf16) to global, zero above the diagonal blocks.
+__device__ __forceinline__ void store_t_aqk(const PrepareArgs& a, size_t cm, int tid, const float* sT,
+                                            const uint16_t* sAqk) {
+  float* tdst = a.tmat + cm * (kChunk * kChunk);
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int idx = pass * 256 + tid;
+    const int r = idx >> 4;
+    const int c4 = (idx & 15) * 4;
+    float4 val;
+    const bool upper = (c4 >> 4) > (r >> 4);
+    val.x = upper ? 0.f : sT[r * kLdF + c4 + 0];
+    val.y = upper ? 0.f : sT[r * kLdF + c4 + 1];
+    val.z = upper ? 0.f : sT[r * kLdF + c4 + 2];
+    val.w = upper ? 0.f : sT[r * kLdF + c4 + 3];
+    *reinterpret_cast<float4*>(tdst + r * kChunk + c4) = val;
+  }
+  uint16_t* qdst = a.aqk + cm * (kChunk * kChunk);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int idx = pass * 256 + tid;
+    const int r = idx >> 3;
+    const int c8 = (idx & 7) * 8;
+    u16x8 val;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) val[e] = ((c8 >> 4) > (r >> 4)) ? (uint16_t)0 : sAqk[r * kLdQ + c8 + e];
+    *reinterpret_cast<u16x8*>(qdst + r * kChunk + c8) = val;
+  }
+}
+
+// ===========================================================================
+// GDN: scalar natural-log gate per (token, head)
+// ===========================================================================
+__global__ __launch_bounds__(256) void gdn_prepare_kernel(PrepareArgs a) {
+  const int c = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g4 = lane >> 4;
+  const int l16 = lane & 15;
+  const ChunkInfo ci = a.geo.chunk(c);
+
+  __shared__ uint16_t sk[kChunk * kLdRow];
+  __shared__ uint16_t sq[kChunk * kLdRow];
+  __shared__ float sA[kChunk * kLdF];
+  __shared__ float sT[kChunk * kLdF];
+  __shared__ float sP[4][16 * 17];
+  __shared__ uint16_t sAqk[kChunk * kLdQ];
+  __shared__ float sG[kChunk], sBeta[kChunk], sRq[kChunk], sRk[kChunk];
+
+  load_qk_norms(a, ci, h, tid, sk, sq, sRk, sRq);
   if (wave == 0) {
     const bool valid = lane < ci.len;
-    const size_t th = (size_t)(ci.tok0 + lane) * H + h;
-    float x = valid ? a.g[th] : 0.0f;
+    float x = valid ? a.g[(size_t)(ci.tok0 + lane) * a.H + h] : 0.0f;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float y = __shfl_up(x, o);
       if (lane >= o) x += y;
     }
     sG[lane] = x;
-    float b = valid ? bf2f(a.beta[th]) : 0.0f;
-    if (sig && valid) b = 1.0f / (1.0f + expf(-b));
-    sBeta[lane] = b;
+    load_beta(a, ci, h, lane, sBeta);
   }
   __syncthreads();
 
-  // ---- 3. Gram tiles on MFMA: k k^T (strictly lower) and q k^T (lower) ------
+  // Gram tiles on MFMA: k k^T (strictly lower) and q k^T (lower).
   // 10 lower 16x16 tiles each; job = kind*10 + tile, wave takes every 4th.
   for (int job = wave; job < 20; job += 4) {
     const int kind = job / 10;  // 0: k k^T, 1: q k^T
@@ -138,81 +241,10 @@ __global__ __launch_bounds__(256) void gdn_prepare_kernel(PrepareArgs a) {
   }
   __syncthreads();
 
-  // ---- 4a. diagonal 16x16 blocks of T by forward substitution --------------
-  if (lane < 16) {
-    const int base = 16 * wave;
-    float t[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float val = (i == lane) ? 1.0f : 0.0f;
-#pragma unroll
-      for (int m = 0; m < i; ++m) val = fmaf(sA[(base + i) * kLdF + base + m], t[m], val);
-      t[i] = val;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sT[(base + i) * kLdF + base + lane] = t[i];
-  }
-  __syncthreads();
+  invert_unit_lower(sA, sT, sP, wave, lane);
 
-  // ---- 4b. off-diagonal blocks, one block row at a time --------------------
-  // T_ij = T_ii * sum_{m=j}^{i-1} A_im T_mj ; lane holds (row l16, cols 4*g4..+3)
-  for (int I = 1; I < 4; ++I) {
-    const int J = wave;
-    if (J < I) {
-      float p[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int M = J; M < I; ++M) {
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const float av = sA[(16 * I + l16) * kLdF + 16 * M + x];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) p[e] = fmaf(av, sT[(16 * M + x) * kLdF + 16 * J + 4 * g4 + e], p[e]);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sP[wave][l16 * 17 + 4 * g4 + e] = p[e];
-    }
-    __syncthreads();
-    if (J < I) {
-      float r[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const float tv = sT[(16 * I + l16) * kLdF + 16 * I + x];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = fmaf(tv, sP[wave][x * 17 + 4 * g4 + e], r[e]);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sT[(16 * I + l16) * kLdF + 16 * J + 4 * g4 + e] = r[e];
-    }
-    __syncthreads();
-  }
-
-  // ---- 5. outputs ------------------------------------------------------------
   const size_t cm = (size_t)h * a.geo.NT + c;
-  float* tdst = a.tmat + cm * (kChunk * kChunk);
-#pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    const int idx = pass * 256 + tid;
-    const int r = idx >> 4;
-    const int c4 = (idx & 15) * 4;
-    float4 val;
-    const bool upper = (c4 >> 4) > (r >> 4);
-    val.x = upper ? 0.f : sT[r * kLdF + c4 + 0];
-    val.y = upper ? 0.f : sT[r * kLdF + c4 + 1];
-    val.z = upper ? 0.f : sT[r * kLdF + c4 + 2];
-    val.w = upper ? 0.f : sT[r * kLdF + c4 + 3];
-    *reinterpret_cast<float4*>(tdst + r * kChunk + c4) = val;
-  }
-  uint16_t* qdst = a.aqk + cm * (kChunk * kChunk);
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int idx = pass * 256 + tid;
-    const int r = idx >> 3;
-    const int c8 = (idx & 7) * 8;
-    u16x8 val;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) val[e] = ((c8 >> 4) > (r >> 4)) ? (uint16_t)0 : sAqk[r * kLdQ + c8 + e];
-    *reinterpret_cast<u16x8*>(qdst + r * kChunk + c8) = val;
-  }
+  store_t_aqk(a, cm, tid, sT, sAqk);
   if (tid < 64) {
     const int i = tid;
     const bool valid = i < ci.len;
@@ -232,10 +264,165 @@ __global__ __launch_bounds__(256) void gdn_prepare_kernel(PrepareArgs a) {
   }
 }
 
+// ===========================================================================
+// KDA: per-key-channel log2 gate per (token, head, channel)
+// ===========================================================================
+__global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
+  const int c = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g4 = lane >> 4;
+  const int l16 = lane & 15;
+  const ChunkInfo ci = a.geo.chunk(c);
+  const size_t cm = (size_t)h * a.geo.NT + c;
+
+  __shared__ uint16_t sk[kChunk * kLdRow];
+  __shared__ uint16_t sq[kChunk * kLdRow];
+  __shared__ float sG[kChunk * kLdG];
+  __shared__ float sA[kChunk * kLdF];
+  __shared__ float sT[kChunk * kLdF];
+  __shared__ float sP[4][16 * 17];
+  __shared__ uint16_t sAqk[kChunk * kLdQ];
+  __shared__ float sBeta[kChunk], sRq[kChunk], sRk[kChunk];
+
+  load_qk_norms(a, ci, h, tid, sk, sq, sRk, sRq);
+  if (wave == 0) load_beta(a, ci, h, lane, sBeta);
+
+  // per-channel cumulative gate: thread (d, half) scans 32 rows
+  {
+    const int d = tid & 127;
+    const int half = tid >> 7;
+    float run = 0.0f;
+    for (int r = 32 * half; r < 32 * half + 32; ++r) {
+      const float gv = r < ci.len ? a.g[((size_t)(ci.tok0 + r) * a.H + h) * kDim + d] : 0.0f;
+      run += gv;
+      sG[r * kLdG + d] = run;
+    }
+  }
+  __syncthreads();
+  {
+    const int d = tid & 127;
+    const int half = tid >> 7;
+    if (half == 1) {
+      const float base = sG[31 * kLdG + d];
+      for (int r = 32; r < 64; ++r) sG[r * kLdG + d] += base;
+    }
+  }
+  __syncthreads();
+  {
+    float* gdst = a.gk + cm * (kChunk * kDim);
+    for (int idx = tid; idx < kChunk * kDim / 4; idx += 256) {
+      const int r = idx >> 5, c4 = (idx & 31) * 4;
+      *reinterpret_cast<float4*>(gdst + r * kDim + c4) =
+          make_float4(sG[r * kLdG + c4], sG[r * kLdG + c4 + 1], sG[r * kLdG + c4 + 2], sG[r * kLdG + c4 + 3]);
+    }
+  }
+
+  // off-diagonal tiles I > J on MFMA, rows scaled against r = 16 I; the
+  // k k^T product carries hi + lo operands (it feeds the inverse), the
+  // q k^T product single bf16 operands.
+  for (int job = wave; job < 6; job += 4) {
+    int t = job, I = 1;
+    while (t >= I) { t -= I; ++I; }
+    const int J = t;
+    const int r = 16 * I;
+    const int i = 16 * I + l16;   // A-operand row
+    const int j = 16 * J + l16;   // B-operand row (column of the product)
+    f32x4 accA = {0.f, 0.f, 0.f, 0.f};
+    f32x4 accQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u16x8 lk_hi, lk_lo, lq, rr_hi, rr_lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 32 * s + 8 * g4 + e;
+        const float gr = sG[r * kLdG + d];
+        const float fi = exp2f(sG[i * kLdG + d] - gr);
+        const float fj = exp2f(gr - sG[j * kLdG + d]);
+        uint16_t hh, ll;
+        split_bf(bf2f(sk[i * kLdRow + d]) * fi, hh, ll);
+        lk_hi[e] = hh; lk_lo[e] = ll;
+        lq[e] = f2bf(bf2f(sq[i * kLdRow + d]) * fi);
+        split_bf(bf2f(sk[j * kLdRow + d]) * fj, hh, ll);
+        rr_hi[e] = hh; rr_lo[e] = ll;
+      }
+      accA = mfma16(lk_hi, rr_hi, accA);
+      accA = mfma16(lk_hi, rr_lo, accA);
+      accA = mfma16(lk_lo, rr_hi, accA);
+      accQ = mfma16(lq, rr_hi, accQ);
+    }
+    const int jc = 16 * J + l16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ii = 16 * I + 4 * g4 + e;
+      sA[ii * kLdF + jc] = -sBeta[ii] * sRk[ii] * sRk[jc] * accA[e];
+      sAqk[ii * kLdQ + jc] = f2bf(a.scale * sRq[ii] * sRk[jc] * accQ[e]);
+    }
+  }
+
+  // diagonal tiles: pairs i >= j of each 16-row block, elementwise; the
+  // entries above the diagonal inside these tiles are zero
+  for (int idx = tid; idx < 4 * 256; idx += 256) {
+    const int I = idx >> 8, il = (idx >> 4) & 15, jl = idx & 15;
+    if (il < jl) sAqk[(16 * I + il) * kLdQ + 16 * I + jl] = 0;
+  }
+  for (int p = tid; p < 4 * 136; p += 256) {
+    const int I = p / 136;
+    int rem = p - I * 136, il = 0;
+    while (rem > il) { rem -= il + 1; ++il; }
+    const int i = 16 * I + il, j = 16 * I + rem;
+    float skk = 0.f, sqk = 0.f;
+    for (int d = 0; d < kDim; d += 4) {
+      const float4 gi = *reinterpret_cast<const float4*>(sG + i * kLdG + d);
+      const float4 gj = *reinterpret_cast<const float4*>(sG + j * kLdG + d);
+      const u16x4 ki = *reinterpret_cast<const u16x4*>(sk + i * kLdRow + d);
+      const u16x4 kj = *reinterpret_cast<const u16x4*>(sk + j * kLdRow + d);
+      const u16x4 qi = *reinterpret_cast<const u16x4*>(sq + i * kLdRow + d);
+      const float e0 = exp2f(gi.x - gj.x), e1 = exp2f(gi.y - gj.y);
+      const float e2 = exp2f(gi.z - gj.z), e3 = exp2f(gi.w - gj.w);
+      const float w0 = bf2f(kj[0]) * e0, w1 = bf2f(kj[1]) * e1, w2 = bf2f(kj[2]) * e2, w3 = bf2f(kj[3]) * e3;
+      skk = fmaf(bf2f(ki[0]), w0, skk);
+      skk = fmaf(bf2f(ki[1]), w1, skk);
+      skk = fmaf(bf2f(ki[2]), w2, skk);
+      skk = fmaf(bf2f(ki[3]), w3, skk);
+      sqk = fmaf(bf2f(qi[0]), w0, sqk);
+      sqk = fmaf(bf2f(qi[1]), w1, sqk);
+      sqk = fmaf(bf2f(qi[2]), w2, sqk);
+      sqk = fmaf(bf2f(qi[3]), w3, sqk);
+    }
+    sA[i * kLdF + j] = (i > j) ? -sBeta[i] * sRk[i] * sRk[j] * skk : 0.0f;
+    sAqk[i * kLdQ + j] = f2bf(a.scale * sRq[i] * sRk[j] * sqk);
+  }
+  __syncthreads();
+
+  invert_unit_lower(sA, sT, sP, wave, lane);
+
+  store_t_aqk(a, cm, tid, sT, sAqk);
+  if (tid < 64) {
+    const int i = tid;
+    const bool valid = i < ci.len;
+    const float b = valid ? sBeta[i] : 0.f;
+    const float rk = sRk[i], rq = sRq[i];
+    float* vd = a.vec + cm * (kVecRows * kChunk);
+    vd[0 * 64 + i] = b;
+    vd[1 * 64 + i] = valid ? b * rk : 0.f;
+    vd[2 * 64 + i] = valid ? rk : 0.f;
+    vd[3 * 64 + i] = valid ? a.scale * rq : 0.f;
+    vd[4 * 64 + i] = 0.f;
+    vd[5 * 64 + i] = rq;
+    vd[6 * 64 + i] = rk;
+    vd[7 * 64 + i] = 0.f;
+  }
+}
+
 hipError_t launch_prepare(bool kda, const PrepareArgs& a, hipStream_t stream) {
-  if (kda) return hipErrorNotSupported;
   dim3 grid(a.geo.NT, a.H);
-  hipLaunchKernelGGL(gdn_prepare_kernel, grid, dim3(256), 0, stream, a);
+  if (kda)
+    hipLaunchKernelGGL(kda_prepare_kernel, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(gdn_prepare_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

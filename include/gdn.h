@@ -139,7 +139,7 @@ int gdn_timing_read(double* prepare_ms, double* state_ms, int64_t* calls);
  *                          diagonal, zero above.
  *   vec  [H,NT,8,64]  fp32 per-row vectors of the chunk, row r:
  *                          0 beta (after the sigmoid when flagged)
- *                          1 GDN: beta*rk*exp(G)      KDA: beta
+ *                          1 GDN: beta*rk*exp(G)      KDA: beta*rk
  *                          2 GDN: rk*exp(G_last - G)  KDA: rk
  *                          3 GDN: scale*rq*exp(G)     KDA: scale*rq
  *                          4 GDN: G (natural log)     KDA: 0

@@ -167,6 +167,85 @@ def test_caller_workspace_and_errors(gdn):
     assert e.value.code == gdn.GDN_ERR_UNSUPPORTED
 
 
+def _kda_problems():
+    rng = np.random.default_rng(91)
+    return [
+        ("kda_B1_T300_H2", gi.make_inputs("kda", B=1, T=300, H=2)),
+        ("kda_B2_T64_H3", gi.make_inputs("kda", B=2, T=64, H=3)),
+        ("kda_T1", gi.make_inputs("kda", B=2, T=1, H=2)),
+        ("kda_T65", gi.make_inputs("kda", B=1, T=65, H=2)),
+        ("kda_mild_init", gi.random_problem(rng, 2, 200, 2, 128, 128, kda=True, gate_scale=0.02,
+                                            with_initial_state=True)),
+        ("kda_packed", gi.random_problem(rng, 1, 317, 2, 128, 128, kda=True, with_initial_state=True,
+                                         cu_seqlens=[0, 1, 18, 82, 147, 317])),
+    ]
+
+
+KDA = _kda_problems()
+
+
+@pytest.mark.parametrize("name,inp", KDA, ids=[n for n, _ in KDA])
+def test_kda_end_to_end_reduced(gdn, name, inp):
+    _say("kda case", name, "B,T,H =", inp.B, inp.T, inp.H)
+    o_ref, s_ref = oracle.recur(inp)
+    o, fs = run_gpu(inp)
+    assert np.isfinite(o).all()
+    eo, es = o_err(o, o_ref), s_err(fs, s_ref)
+    _say("  o max-abs err %.3e   final-state rel err %.3e" % (eo, es))
+    assert eo <= O_ATOL and es <= S_RTOL
+
+
+def test_kda_stage_parity(gdn):
+    for name, inp in [("kda_B1_T200_H2", gi.make_inputs("kda", B=1, T=200, H=2)),
+                      ("kda_packed", gi.random_problem(np.random.default_rng(5), 1, 150, 2, 128, 128, kda=True,
+                                                       with_initial_state=True, cu_seqlens=[0, 17, 81, 150]))]:
+        _say("kda stage case", name)
+        d = to_device(inp)
+        tmat, aqk, vec, gk = gdn.gdn_stage_prepare(d["q"], d["k"], d["g"], d["beta"], scale=inp.scale,
+                                                   cu_seqlens=inp.cu_seqlens, kda=True, l2norm_qk=True,
+                                                   beta_sigmoid=True)
+        torch.cuda.synchronize()
+        _, _, inters = oracle.chunk(inp, keep=True)
+        dense = inp.cu_seqlens is None
+        T_ref = hm_chunks([it["T"] for it in inters], dense)
+        A_ref = hm_chunks([it["Aqk"] for it in inters], dense)
+        G_ref = hm_chunks([it["G"] for it in inters], dense)
+        tm = tmat.cpu().numpy().astype(np.float64)
+        et = np.abs(tm - T_ref).max() / max(1.0, np.abs(T_ref).max())
+        aq = aqk.float().cpu().numpy().astype(np.float64)
+        ea = np.abs(aq - A_ref).max() / max(1e-3, np.abs(A_ref).max())
+        gg = gk.cpu().numpy().astype(np.float64)
+        eg = np.abs(gg - G_ref).max() / max(1.0, np.abs(G_ref).max())
+        _say("  T err %.3e  Aqk err %.3e  G err %.3e" % (et, ea, eg))
+        assert et <= 1e-4 and ea <= 1e-2 and eg <= 1e-5
+        h, v_new, fs = gdn.gdn_stage_fwd_h(d["k"], d["v"], tmat, vec, gk=gk, initial_state=d["initial_state"],
+                                           cu_seqlens=inp.cu_seqlens, kda=True)
+        torch.cuda.synchronize()
+        h_ref = hm_chunks([it["h"] for it in inters], dense)
+        vn_ref = hm_chunks([it["v_new"] for it in inters], dense)
+        eh = np.abs(h.cpu().numpy() - h_ref).max() / max(np.abs(h_ref).max(), 1e-30)
+        ev = np.abs(v_new.cpu().numpy() - vn_ref).max() / max(np.abs(vn_ref).max(), 1e-30)
+        _say("  h rel err %.3e  v_new rel err %.3e" % (eh, ev))
+        assert eh <= 1e-3 and ev <= 1e-3
+        o = gdn.gdn_stage_finalize(d["q"], aqk, vec, torch.from_numpy(h_ref.astype(np.float32)).cuda(),
+                                   torch.from_numpy(vn_ref.astype(np.float32)).cuda(), gk=gk,
+                                   cu_seqlens=inp.cu_seqlens, kda=True)
+        torch.cuda.synchronize()
+        o_ref, _ = oracle.recur(inp)
+        assert o_err(o.float().cpu().numpy().astype(np.float64), o_ref) <= O_ATOL
+
+
+def test_full_size_kda_sampled(gdn):
+    """B=2 T=8192 H=32 per-channel gate; 4 sampled (sequence, head) units."""
+    inp = gi.make_inputs("kda")
+    _say("full-size kda: inputs ready")
+    o, fs = run_gpu(inp)
+    assert np.isfinite(o).all() and np.isfinite(fs).all()
+    units = [(0, 0), (1, 31), (0, 17), (1, 8)]
+    o_ref, s_ref = _sampled(inp, units)
+    _check_units(inp, o, fs, o_ref, s_ref, units)
+
+
 def _sampled(inp, units):
     o_ref, s_ref = oracle.recur(inp, units=units)
     return o_ref, s_ref
