@@ -56,6 +56,7 @@ struct FinArgs {
 hipError_t launch_prepare(bool kda, const PrepareArgs& a, hipStream_t stream);
 hipError_t launch_fwd(bool kda, bool store_h, bool compute_o, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_finalize(bool kda, const FinArgs& a, hipStream_t stream);
+hipError_t launch_gdn_state(bool store_h, bool compute_o, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_kda_fwd(bool store_h, bool compute_o, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_kda_finalize(const FinArgs& a, hipStream_t stream);
 
