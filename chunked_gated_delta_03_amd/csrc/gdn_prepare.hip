@@ -91,12 +91,15 @@ __device__ __forceinline__ void load_beta(const PrepareArgs& a, const ChunkInfo&
 }
 
 // T = (I - A)^-1 for strictly lower A (fp32, LDS), blockwise. All 256
-// threads call it; it ends with a barrier.
-__device__ __forceinline__ void invert_unit_lower(const float* sA, float* sT, float (*sP)[16 * 17], int wave,
-                                                  int lane) {
+// threads call it; it ends with a barrier. The diagonal 16x16 blocks are
+// inverted by forward substitution (one block per wave); the off-diagonal
+// blocks follow one block row at a time, T_ij = T_ii * (sum_m A_im T_mj),
+// as 16x16x16 fp32 MFMA products. In the second product the contraction
+// slot of lane group g at step ks is 4g + ks, so the first product's
+// accumulator feeds it as the B operand without leaving registers.
+__device__ __forceinline__ void invert_unit_lower(const float* sA, float* sT, int wave, int lane) {
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
-  // diagonal 16x16 blocks by forward substitution, one block per wave
   if (lane < 16) {
     const int base = 16 * wave;
     float t[16];
@@ -111,34 +114,26 @@ __device__ __forceinline__ void invert_unit_lower(const float* sA, float* sT, fl
     for (int i = 0; i < 16; ++i) sT[(base + i) * kLdF + base + lane] = t[i];
   }
   __syncthreads();
-  // off-diagonal blocks, one block row at a time:
-  // T_ij = T_ii * sum_{m=j}^{i-1} A_im T_mj ; lane holds (row l16, cols 4*g4..+3)
   for (int I = 1; I < 4; ++I) {
     const int J = wave;
     if (J < I) {
-      float p[4] = {0.f, 0.f, 0.f, 0.f};
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
       for (int M = J; M < I; ++M) {
 #pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const float av = sA[(16 * I + l16) * kLdF + 16 * M + x];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) p[e] = fmaf(av, sT[(16 * M + x) * kLdF + 16 * J + 4 * g4 + e], p[e]);
+        for (int ks = 0; ks < 4; ++ks) {
+          const float av = sA[(16 * I + l16) * kLdF + 16 * M + 4 * ks + g4];
+          const float bv = sT[(16 * M + 4 * ks + g4) * kLdF + 16 * J + l16];
+          p = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, p, 0, 0, 0);
         }
       }
+      f32x4 r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sP[wave][l16 * 17 + 4 * g4 + e] = p[e];
-    }
-    __syncthreads();
-    if (J < I) {
-      float r[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const float tv = sT[(16 * I + l16) * kLdF + 16 * I + x];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = fmaf(tv, sP[wave][x * 17 + 4 * g4 + e], r[e]);
+      for (int ks = 0; ks < 4; ++ks) {
+        const float av = sT[(16 * I + l16) * kLdF + 16 * I + 4 * g4 + ks];
+        r = __builtin_amdgcn_mfma_f32_16x16x4f32(av, p[ks], r, 0, 0, 0);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sT[(16 * I + l16) * kLdF + 16 * J + 4 * g4 + e] = r[e];
+      for (int e = 0; e < 4; ++e) sT[(16 * I + 4 * g4 + e) * kLdF + 16 * J + l16] = r[e];
     }
     __syncthreads();
   }
@@ -187,15 +182,22 @@ __global__ __launch_bounds__(256) void gdn_prepare_kernel(PrepareArgs a) {
   const int l16 = lane & 15;
   const ChunkInfo ci = a.geo.chunk(c);
 
-  __shared__ uint16_t sk[kChunk * kLdRow];
-  __shared__ uint16_t sq[kChunk * kLdRow];
-  __shared__ float sA[kChunk * kLdF];
-  __shared__ float sT[kChunk * kLdF];
-  __shared__ float sP[4][16 * 17];
-  __shared__ uint16_t sAqk[kChunk * kLdQ];
+  // q, k rows live only until the Gram tiles are in registers; A, T and Aqk
+  // reuse their space afterwards.
+  __shared__ union alignas(16) {
+    struct {
+      uint16_t k[kChunk * kLdRow];
+      uint16_t q[kChunk * kLdRow];
+    } in;
+    struct {
+      float A[kChunk * kLdF];
+      float T[kChunk * kLdF];
+      uint16_t aqk[kChunk * kLdQ];
+    } mat;
+  } u;
   __shared__ float sG[kChunk], sBeta[kChunk], sRq[kChunk], sRk[kChunk];
 
-  load_qk_norms(a, ci, h, tid, sk, sq, sRk, sRq);
+  load_qk_norms(a, ci, h, tid, u.in.k, u.in.q, sRk, sRq);
   if (wave == 0) {
     const bool valid = lane < ci.len;
     float x = valid ? a.g[(size_t)(ci.tok0 + lane) * a.H + h] : 0.0f;
@@ -209,42 +211,55 @@ __global__ __launch_bounds__(256) void gdn_prepare_kernel(PrepareArgs a) {
   }
   __syncthreads();
 
-  // Gram tiles on MFMA: k k^T (strictly lower) and q k^T (lower).
-  // 10 lower 16x16 tiles each; job = kind*10 + tile, wave takes every 4th.
-  for (int job = wave; job < 20; job += 4) {
-    const int kind = job / 10;  // 0: k k^T, 1: q k^T
+  // Gram tiles on MFMA: k k^T (strictly lower) and q k^T (lower), 10 lower
+  // 16x16 tiles each; job = kind*10 + tile, wave w takes jobs w, w+4, ...
+  f32x4 acc[5];
+#pragma unroll
+  for (int jj = 0; jj < 5; ++jj) {
+    const int job = wave + 4 * jj;
+    const int kind = job / 10;
     int t = job % 10, I = 0;
     while (t > I) { t -= I + 1; ++I; }
     const int J = t;
-    const uint16_t* left = kind == 0 ? sk : sq;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint16_t* left = kind == 0 ? u.in.k : u.in.q;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const u16x8 av = *reinterpret_cast<const u16x8*>(left + (16 * I + l16) * kLdRow + 32 * s + 8 * g4);
-      const u16x8 bv = *reinterpret_cast<const u16x8*>(sk + (16 * J + l16) * kLdRow + 32 * s + 8 * g4);
-      acc = mfma16(av, bv, acc);
+      const u16x8 bv = *reinterpret_cast<const u16x8*>(u.in.k + (16 * J + l16) * kLdRow + 32 * s + 8 * g4);
+      x = mfma16(av, bv, x);
     }
+    acc[jj] = x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int jj = 0; jj < 5; ++jj) {
+    const int job = wave + 4 * jj;
+    const int kind = job / 10;
+    int t = job % 10, I = 0;
+    while (t > I) { t -= I + 1; ++I; }
+    const int J = t;
     const int jc = 16 * J + l16;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * I + 4 * g4 + e;
       if (kind == 0) {
         float val = 0.0f;
-        if (i > jc) val = -sBeta[i] * sRk[i] * sRk[jc] * acc[e] * expf(sG[i] - sG[jc]);
-        sA[i * kLdF + jc] = val;
+        if (i > jc) val = -sBeta[i] * sRk[i] * sRk[jc] * acc[jj][e] * expf(sG[i] - sG[jc]);
+        u.mat.A[i * kLdF + jc] = val;
       } else {
         float val = 0.0f;
-        if (i >= jc) val = a.scale * sRq[i] * sRk[jc] * acc[e] * expf(sG[i] - sG[jc]);
-        sAqk[i * kLdQ + jc] = f2bf(val);
+        if (i >= jc) val = a.scale * sRq[i] * sRk[jc] * acc[jj][e] * expf(sG[i] - sG[jc]);
+        u.mat.aqk[i * kLdQ + jc] = f2bf(val);
       }
     }
   }
   __syncthreads();
 
-  invert_unit_lower(sA, sT, sP, wave, lane);
+  invert_unit_lower(u.mat.A, u.mat.T, wave, lane);
 
   const size_t cm = (size_t)h * a.geo.NT + c;
-  store_t_aqk(a, cm, tid, sT, sAqk);
+  store_t_aqk(a, cm, tid, u.mat.T, u.mat.aqk);
   if (tid < 64) {
     const int i = tid;
     const bool valid = i < ci.len;
@@ -278,14 +293,22 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
   const ChunkInfo ci = a.geo.chunk(c);
   const size_t cm = (size_t)h * a.geo.NT + c;
 
-  __shared__ uint16_t sk[kChunk * kLdRow];
-  __shared__ uint16_t sq[kChunk * kLdRow];
-  __shared__ float sG[kChunk * kLdG];
-  __shared__ float sA[kChunk * kLdF];
-  __shared__ float sT[kChunk * kLdF];
-  __shared__ float sP[4][16 * 17];
-  __shared__ uint16_t sAqk[kChunk * kLdQ];
+  __shared__ union alignas(16) {
+    struct {
+      uint16_t k[kChunk * kLdRow];
+      uint16_t q[kChunk * kLdRow];
+      float G[kChunk * kLdG];
+    } in;
+    struct {
+      float A[kChunk * kLdF];
+      float T[kChunk * kLdF];
+      uint16_t aqk[kChunk * kLdQ];
+    } mat;
+  } u;
   __shared__ float sBeta[kChunk], sRq[kChunk], sRk[kChunk];
+  uint16_t* sk = u.in.k;
+  uint16_t* sq = u.in.q;
+  float* sG = u.in.G;
 
   load_qk_norms(a, ci, h, tid, sk, sq, sRk, sRq);
   if (wave == 0) load_beta(a, ci, h, lane, sBeta);
@@ -322,16 +345,20 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
 
   // off-diagonal tiles I > J on MFMA, rows scaled against r = 16 I; the
   // k k^T product carries hi + lo operands (it feeds the inverse), the
-  // q k^T product single bf16 operands.
-  for (int job = wave; job < 6; job += 4) {
+  // q k^T product single bf16 operands. Wave w: jobs w and w + 4.
+  f32x4 accA[2], accQ[2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int job = wave + 4 * jj;
+    accA[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accQ[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (job >= 6) continue;
     int t = job, I = 1;
     while (t >= I) { t -= I; ++I; }
     const int J = t;
     const int r = 16 * I;
     const int i = 16 * I + l16;   // A-operand row
     const int j = 16 * J + l16;   // B-operand row (column of the product)
-    f32x4 accA = {0.f, 0.f, 0.f, 0.f};
-    f32x4 accQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u16x8 lk_hi, lk_lo, lq, rr_hi, rr_lo;
@@ -348,27 +375,21 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
         split_bf(bf2f(sk[j * kLdRow + d]) * fj, hh, ll);
         rr_hi[e] = hh; rr_lo[e] = ll;
       }
-      accA = mfma16(lk_hi, rr_hi, accA);
-      accA = mfma16(lk_hi, rr_lo, accA);
-      accA = mfma16(lk_lo, rr_hi, accA);
-      accQ = mfma16(lq, rr_hi, accQ);
-    }
-    const int jc = 16 * J + l16;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int ii = 16 * I + 4 * g4 + e;
-      sA[ii * kLdF + jc] = -sBeta[ii] * sRk[ii] * sRk[jc] * accA[e];
-      sAqk[ii * kLdQ + jc] = f2bf(a.scale * sRq[ii] * sRk[jc] * accQ[e]);
+      accA[jj] = mfma16(lk_hi, rr_hi, accA[jj]);
+      accA[jj] = mfma16(lk_hi, rr_lo, accA[jj]);
+      accA[jj] = mfma16(lk_lo, rr_hi, accA[jj]);
+      accQ[jj] = mfma16(lq, rr_hi, accQ[jj]);
     }
   }
 
-  // diagonal tiles: pairs i >= j of each 16-row block, elementwise; the
-  // entries above the diagonal inside these tiles are zero
-  for (int idx = tid; idx < 4 * 256; idx += 256) {
-    const int I = idx >> 8, il = (idx >> 4) & 15, jl = idx & 15;
-    if (il < jl) sAqk[(16 * I + il) * kLdQ + 16 * I + jl] = 0;
-  }
-  for (int p = tid; p < 4 * 136; p += 256) {
+  // diagonal tiles: pairs i >= j of each 16-row block, elementwise
+  float dkk[3], dqk[3];
+#pragma unroll
+  for (int pp = 0; pp < 3; ++pp) {
+    const int p = tid + 256 * pp;
+    dkk[pp] = 0.f;
+    dqk[pp] = 0.f;
+    if (p >= 4 * 136) continue;
     const int I = p / 136;
     int rem = p - I * 136, il = 0;
     while (rem > il) { rem -= il + 1; ++il; }
@@ -392,14 +413,47 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
       sqk = fmaf(bf2f(qi[2]), w2, sqk);
       sqk = fmaf(bf2f(qi[3]), w3, sqk);
     }
-    sA[i * kLdF + j] = (i > j) ? -sBeta[i] * sRk[i] * sRk[j] * skk : 0.0f;
-    sAqk[i * kLdQ + j] = f2bf(a.scale * sRq[i] * sRk[j] * sqk);
+    dkk[pp] = skk;
+    dqk[pp] = sqk;
   }
   __syncthreads();
 
-  invert_unit_lower(sA, sT, sP, wave, lane);
+  // results into the reused LDS
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int job = wave + 4 * jj;
+    if (job >= 6) continue;
+    int t = job, I = 1;
+    while (t >= I) { t -= I; ++I; }
+    const int J = t;
+    const int jc = 16 * J + l16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ii = 16 * I + 4 * g4 + e;
+      u.mat.A[ii * kLdF + jc] = -sBeta[ii] * sRk[ii] * sRk[jc] * accA[jj][e];
+      u.mat.aqk[ii * kLdQ + jc] = f2bf(a.scale * sRq[ii] * sRk[jc] * accQ[jj][e]);
+    }
+  }
+  for (int idx = tid; idx < 4 * 256; idx += 256) {
+    const int I = idx >> 8, il = (idx >> 4) & 15, jl = idx & 15;
+    if (il < jl) u.mat.aqk[(16 * I + il) * kLdQ + 16 * I + jl] = 0;
+  }
+#pragma unroll
+  for (int pp = 0; pp < 3; ++pp) {
+    const int p = tid + 256 * pp;
+    if (p >= 4 * 136) continue;
+    const int I = p / 136;
+    int rem = p - I * 136, il = 0;
+    while (rem > il) { rem -= il + 1; ++il; }
+    const int i = 16 * I + il, j = 16 * I + rem;
+    u.mat.A[i * kLdF + j] = (i > j) ? -sBeta[i] * sRk[i] * sRk[j] * dkk[pp] : 0.0f;
+    u.mat.aqk[i * kLdQ + j] = f2bf(a.scale * sRq[i] * sRk[j] * dqk[pp]);
+  }
+  __syncthreads();
 
-  store_t_aqk(a, cm, tid, sT, sAqk);
+  invert_unit_lower(u.mat.A, u.mat.T, wave, lane);
+
+  store_t_aqk(a, cm, tid, u.mat.T, u.mat.aqk);
   if (tid < 64) {
     const int i = tid;
     const bool valid = i < ci.len;
