@@ -51,23 +51,32 @@ __device__ __forceinline__ float sumsq8(const uint4& v) {
 }
 
 // q, k rows of the chunk into LDS (zero past the end), normalisation factors.
+// All global loads are issued before the first LDS write.
 __device__ __forceinline__ void load_qk_norms(const PrepareArgs& a, const ChunkInfo& ci, int h, int tid,
                                               uint16_t* sk, uint16_t* sq, float* sRk, float* sRq) {
   const bool l2 = (a.flags & 1u) != 0;
+  uint4 kv[4], qv[4];
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int idx = pass * 256 + tid;
     const int r = idx >> 4;
     const int cc = (idx & 15) * 8;
-    uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
+    kv[pass] = make_uint4(0, 0, 0, 0);
+    qv[pass] = make_uint4(0, 0, 0, 0);
     if (r < ci.len) {
       const size_t off = ((size_t)(ci.tok0 + r) * a.H + h) * kDim + cc;
-      kv = *reinterpret_cast<const uint4*>(a.k + off);
-      qv = *reinterpret_cast<const uint4*>(a.q + off);
+      kv[pass] = *reinterpret_cast<const uint4*>(a.k + off);
+      qv[pass] = *reinterpret_cast<const uint4*>(a.q + off);
     }
-    *reinterpret_cast<uint4*>(sk + r * kLdRow + cc) = kv;
-    *reinterpret_cast<uint4*>(sq + r * kLdRow + cc) = qv;
-    float ssk = sumsq8(kv), ssq = sumsq8(qv);
+  }
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int idx = pass * 256 + tid;
+    const int r = idx >> 4;
+    const int cc = (idx & 15) * 8;
+    *reinterpret_cast<uint4*>(sk + r * kLdRow + cc) = kv[pass];
+    *reinterpret_cast<uint4*>(sq + r * kLdRow + cc) = qv[pass];
+    float ssk = sumsq8(kv[pass]), ssq = sumsq8(qv[pass]);
 #pragma unroll
     for (int m = 8; m >= 1; m >>= 1) {
       ssk += __shfl_xor(ssk, m);
@@ -195,18 +204,18 @@ __global__ __launch_bounds__(256) void gdn_prepare_kernel(PrepareArgs a) {
       uint16_t aqk[kChunk * kLdQ];
     } mat;
   } u;
-  __shared__ float sG[kChunk], sBeta[kChunk], sRq[kChunk], sRk[kChunk];
+  __shared__ __attribute__((aligned(16))) float sG[kChunk], sBeta[kChunk], sRq[kChunk], sRk[kChunk];
 
+  float gx = 0.0f;
+  if (wave == 0 && lane < ci.len) gx = a.g[(size_t)(ci.tok0 + lane) * a.H + h];
   load_qk_norms(a, ci, h, tid, u.in.k, u.in.q, sRk, sRq);
   if (wave == 0) {
-    const bool valid = lane < ci.len;
-    float x = valid ? a.g[(size_t)(ci.tok0 + lane) * a.H + h] : 0.0f;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const float y = __shfl_up(x, o);
-      if (lane >= o) x += y;
+      const float y = __shfl_up(gx, o);
+      if (lane >= o) gx += y;
     }
-    sG[lane] = x;
+    sG[lane] = gx;
     load_beta(a, ci, h, lane, sBeta);
   }
   __syncthreads();
@@ -223,12 +232,14 @@ __global__ __launch_bounds__(256) void gdn_prepare_kernel(PrepareArgs a) {
     const int J = t;
     const uint16_t* left = kind == 0 ? u.in.k : u.in.q;
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    u16x8 av[4], bv[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const u16x8 av = *reinterpret_cast<const u16x8*>(left + (16 * I + l16) * kLdRow + 32 * s + 8 * g4);
-      const u16x8 bv = *reinterpret_cast<const u16x8*>(u.in.k + (16 * J + l16) * kLdRow + 32 * s + 8 * g4);
-      x = mfma16(av, bv, x);
+      av[s] = *reinterpret_cast<const u16x8*>(left + (16 * I + l16) * kLdRow + 32 * s + 8 * g4);
+      bv[s] = *reinterpret_cast<const u16x8*>(u.in.k + (16 * J + l16) * kLdRow + 32 * s + 8 * g4);
     }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) x = mfma16(av[s], bv[s], x);
     acc[jj] = x;
   }
   __syncthreads();
@@ -240,16 +251,24 @@ __global__ __launch_bounds__(256) void gdn_prepare_kernel(PrepareArgs a) {
     while (t > I) { t -= I + 1; ++I; }
     const int J = t;
     const int jc = 16 * J + l16;
+    const int i0 = 16 * I + 4 * g4;
+    const float4 gi = *reinterpret_cast<const float4*>(sG + i0);
+    const float4 ri = *reinterpret_cast<const float4*>((kind == 0 ? sRk : sRq) + i0);
+    const float4 bi = *reinterpret_cast<const float4*>(sBeta + i0);
+    const float gj = sG[jc], rj = sRk[jc];
+    const float gia[4] = {gi.x, gi.y, gi.z, gi.w};
+    const float ria[4] = {ri.x, ri.y, ri.z, ri.w};
+    const float bia[4] = {bi.x, bi.y, bi.z, bi.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 16 * I + 4 * g4 + e;
+      const int i = i0 + e;
       if (kind == 0) {
         float val = 0.0f;
-        if (i > jc) val = -sBeta[i] * sRk[i] * sRk[jc] * acc[jj][e] * expf(sG[i] - sG[jc]);
+        if (i > jc) val = -bia[e] * ria[e] * rj * acc[jj][e] * __expf(gia[e] - gj);
         u.mat.A[i * kLdF + jc] = val;
       } else {
         float val = 0.0f;
-        if (i >= jc) val = a.scale * sRq[i] * sRk[jc] * acc[jj][e] * expf(sG[i] - sG[jc]);
+        if (i >= jc) val = a.scale * ria[e] * rj * acc[jj][e] * __expf(gia[e] - gj);
         u.mat.aqk[i * kLdQ + jc] = f2bf(val);
       }
     }

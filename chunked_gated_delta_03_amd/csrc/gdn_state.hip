@@ -60,6 +60,33 @@ __device__ __forceinline__ void split_hw(float x, uint16_t& hi, uint16_t& lo) {
   lo = __builtin_bit_cast(uint16_t, (__bf16)(x - (float)h));
 }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// Two floats to packed bf16 hi and lo words: hi = bf16(x), lo = bf16(x - hi).
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t hp = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+  const float h0 = __uint_as_float(hp << 16);
+  const float h1 = __uint_as_float(hp & 0xFFFF0000u);
+  hi = hp;
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, bf16x2));
+}
+__device__ __forceinline__ uint32_t pack2(float x0, float x1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+}
+// B operand (8 contraction slots) from two accumulator tiles: slots 0..3 are
+// rows 4g..4g+3 of tile a, slots 4..7 the same rows of tile b.
+__device__ __forceinline__ void split_tiles(const f32x4& a, const f32x4& b, u16x8& hi, u16x8& lo) {
+  uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+  split2(a[0], a[1], h0, l0);
+  split2(a[2], a[3], h1, l1);
+  split2(b[0], b[1], h2, l2);
+  split2(b[2], b[3], h3, l3);
+  hi = __builtin_bit_cast(u16x8, u32x4{h0, h1, h2, h3});
+  lo = __builtin_bit_cast(u16x8, u32x4{l0, l1, l2, l3});
+}
+
 template <int NWC>
 struct alignas(16) Smem {
   static constexpr int BV = 16 * NWC;
@@ -234,17 +261,6 @@ __global__ __launch_bounds__((NWC + kLoaders) * 64) void gdn_state_kernel(FwdArg
       const int c = si.c0 + jc;
       const size_t cm = (size_t)h * a.geo.NT + c;
 
-      u16x8 Shi[4], Slo[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint16_t hh, ll;
-          split_hw(S[2 * s][e], hh, ll);
-          Shi[s][e] = hh; Slo[s][e] = ll;
-          split_hw(S[2 * s + 1][e], hh, ll);
-          Shi[s][4 + e] = hh; Slo[s][4 + e] = ll;
-        }
       if constexpr (STORE_H) {
         float* hd = a.h_out + cm * (kDim * kDim);
 #pragma unroll
@@ -253,58 +269,101 @@ __global__ __launch_bounds__((NWC + kLoaders) * 64) void gdn_state_kernel(FwdArg
           for (int e = 0; e < 4; ++e) hd[(size_t)(16 * t + 4 * g4 + e) * kDim + colw + l16] = S[t][e];
       }
 
-      // X = k S
+      // X = k S: contraction step s uses state tiles 2s, 2s+1 (split just
+      // before use); four independent accumulators per step
+      u16x8 Shi[4], Slo[4];
       f32x4 X[4];
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        u16x8 fk[4];
+      for (int it = 0; it < 4; ++it) X[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      {
+        u16x8 fk[2][4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          fk[s] = *reinterpret_cast<const u16x8*>(B.k + (16 * it + l16) * kLdK + 32 * s + 8 * g4);
-        X[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int it = 0; it < 4; ++it)
+          fk[0][it] = *reinterpret_cast<const u16x8*>(B.k + (16 * it + l16) * kLdK + 8 * g4);
+        split_tiles(S[0], S[1], Shi[0], Slo[0]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          X[it] = mfma16(fk[s], Shi[s], X[it]);
-          X[it] = mfma16(fk[s], Slo[s], X[it]);
+          if (s + 1 < 4) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+              fk[(s + 1) & 1][it] =
+                  *reinterpret_cast<const u16x8*>(B.k + (16 * it + l16) * kLdK + 32 * (s + 1) + 8 * g4);
+          }
+#pragma unroll
+          for (int it = 0; it < 4; ++it) X[it] = mfma16(fk[s & 1][it], Shi[s], X[it]);
+          if (s + 1 < 4) split_tiles(S[2 * s + 2], S[2 * s + 3], Shi[s + 1], Slo[s + 1]);
+#pragma unroll
+          for (int it = 0; it < 4; ++it) X[it] = mfma16(fk[s & 1][it], Slo[s], X[it]);
         }
       }
 
-      // Y = beta v - c X
-      u16x8 Yhi[2], Ylo[2];
+      // first half of the output, o_inter = q S_hi (independent of v_new)
+      f32x4 O[4];
+      if constexpr (COMPUTE_O) {
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const u16x4 vv = *reinterpret_cast<const u16x4*>(B.vt + (16 * w + l16) * kLdVT + 16 * it + 4 * g4);
-        const float4 bt = *reinterpret_cast<const float4*>(B.vec + 16 * it + 4 * g4);
-        const float4 cc = *reinterpret_cast<const float4*>(B.vec + kChunk + 16 * it + 4 * g4);
-        const float bta[4] = {bt.x, bt.y, bt.z, bt.w};
-        const float cca[4] = {cc.x, cc.y, cc.z, cc.w};
+        for (int it = 0; it < 4; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+        u16x8 fq[2][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float y = bta[e] * bf2f(vv[e]) - cca[e] * X[it][e];
-          uint16_t hh, ll;
-          split_hw(y, hh, ll);
-          Yhi[it >> 1][(it & 1) * 4 + e] = hh;
-          Ylo[it >> 1][(it & 1) * 4 + e] = ll;
+        for (int it = 0; it < 4; ++it)
+          fq[0][it] = *reinterpret_cast<const u16x8*>(B.q + (16 * it + l16) * kLdK + 8 * g4);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if (s + 1 < 4) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+              fq[(s + 1) & 1][it] =
+                  *reinterpret_cast<const u16x8*>(B.q + (16 * it + l16) * kLdK + 32 * (s + 1) + 8 * g4);
+          }
+#pragma unroll
+          for (int it = 0; it < 4; ++it) O[it] = mfma16(fq[s & 1][it], Shi[s], O[it]);
         }
       }
 
-      // v_new = T Y
+      // Y = beta v - c X for tiles 2h, 2h+1 -> B operand of contraction step h
+      auto make_y = [&](int hh, u16x8& yhi, u16x8& ylo) {
+        f32x4 y2[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int it = 2 * hh + k2;
+          const u16x4 vv = *reinterpret_cast<const u16x4*>(B.vt + (16 * w + l16) * kLdVT + 16 * it + 4 * g4);
+          const float4 bt = *reinterpret_cast<const float4*>(B.vec + 16 * it + 4 * g4);
+          const float4 cc = *reinterpret_cast<const float4*>(B.vec + kChunk + 16 * it + 4 * g4);
+          y2[k2][0] = bt.x * bf2f(vv[0]) - cc.x * X[it][0];
+          y2[k2][1] = bt.y * bf2f(vv[1]) - cc.y * X[it][1];
+          y2[k2][2] = bt.z * bf2f(vv[2]) - cc.z * X[it][2];
+          y2[k2][3] = bt.w * bf2f(vv[3]) - cc.w * X[it][3];
+        }
+        split_tiles(y2[0], y2[1], yhi, ylo);
+      };
+
+      // v_new = T Y, three split products, four independent accumulators
       f32x4 VN[4];
+      {
+        u16x8 th[4][2], tl[4][2];
 #pragma unroll
-      for (int io = 0; io < 4; ++io) {
-        const uint16_t* row = B.t + (16 * io + l16) * kLdT2 + 8 * g4;
-        const u16x8 th0 = *reinterpret_cast<const u16x8*>(row);
-        const u16x8 th1 = *reinterpret_cast<const u16x8*>(row + 32);
-        const u16x8 tl0 = *reinterpret_cast<const u16x8*>(row + kChunk);
-        const u16x8 tl1 = *reinterpret_cast<const u16x8*>(row + kChunk + 32);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma16(th0, Yhi[0], acc);
-        acc = mfma16(th0, Ylo[0], acc);
-        acc = mfma16(tl0, Yhi[0], acc);
-        acc = mfma16(th1, Yhi[1], acc);
-        acc = mfma16(th1, Ylo[1], acc);
-        acc = mfma16(tl1, Yhi[1], acc);
-        VN[io] = acc;
+        for (int io = 0; io < 4; ++io) {
+          const uint16_t* row = B.t + (16 * io + l16) * kLdT2 + 8 * g4;
+          th[io][0] = *reinterpret_cast<const u16x8*>(row);
+          th[io][1] = *reinterpret_cast<const u16x8*>(row + 32);
+          tl[io][0] = *reinterpret_cast<const u16x8*>(row + kChunk);
+          tl[io][1] = *reinterpret_cast<const u16x8*>(row + kChunk + 32);
+          VN[io] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        u16x8 Yhi[2], Ylo[2];
+        make_y(0, Yhi[0], Ylo[0]);
+#pragma unroll
+        for (int io = 0; io < 4; ++io) VN[io] = mfma16(th[io][0], Yhi[0], VN[io]);
+        make_y(1, Yhi[1], Ylo[1]);
+#pragma unroll
+        for (int io = 0; io < 4; ++io) VN[io] = mfma16(th[io][0], Ylo[0], VN[io]);
+#pragma unroll
+        for (int io = 0; io < 4; ++io) VN[io] = mfma16(tl[io][0], Yhi[0], VN[io]);
+#pragma unroll
+        for (int io = 0; io < 4; ++io) VN[io] = mfma16(th[io][1], Yhi[1], VN[io]);
+#pragma unroll
+        for (int io = 0; io < 4; ++io) VN[io] = mfma16(th[io][1], Ylo[1], VN[io]);
+#pragma unroll
+        for (int io = 0; io < 4; ++io) VN[io] = mfma16(tl[io][1], Yhi[1], VN[io]);
       }
       if constexpr (STORE_H) {
         float* vd = a.vnew_out + cm * (kChunk * kDim);
@@ -314,66 +373,75 @@ __global__ __launch_bounds__((NWC + kLoaders) * 64) void gdn_state_kernel(FwdArg
           for (int e = 0; e < 4; ++e) vd[(size_t)(16 * io + 4 * g4 + e) * kDim + colw + l16] = VN[io][e];
       }
 
-      // state update: S <- exp(G_last) S + k^T (d * v_new)
-      u16x8 Zhi[2], Zlo[2];
+      // state update: S <- exp(G_last) S + k^T (d * v_new), eight accumulators;
+      // contraction step s uses v_new tiles 2s, 2s+1
+      auto make_z = [&](int hh, u16x8& zhi, u16x8& zlo) {
+        f32x4 z2[2];
 #pragma unroll
-      for (int io = 0; io < 4; ++io) {
-        const float4 dd = *reinterpret_cast<const float4*>(B.vec + 2 * kChunk + 16 * io + 4 * g4);
-        const float dda[4] = {dd.x, dd.y, dd.z, dd.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint16_t hh, ll;
-          split_hw(dda[e] * VN[io][e], hh, ll);
-          Zhi[io >> 1][(io & 1) * 4 + e] = hh;
-          Zlo[io >> 1][(io & 1) * 4 + e] = ll;
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int io = 2 * hh + k2;
+          const float4 dd = *reinterpret_cast<const float4*>(B.vec + 2 * kChunk + 16 * io + 4 * g4);
+          z2[k2][0] = dd.x * VN[io][0];
+          z2[k2][1] = dd.y * VN[io][1];
+          z2[k2][2] = dd.z * VN[io][2];
+          z2[k2][3] = dd.w * VN[io][3];
         }
-      }
-      const float dec = B.dec[0];
+        split_tiles(z2[0], z2[1], zhi, zlo);
+      };
+      {
+        u16x8 ak[2][8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint16_t* col = B.k + perm_col(16 * t + 4 * trQ);
-        u16x8 ak[2];
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const u16x4 r0 = tr_read(col + (32 * s + 4 * trG + trJ) * kLdK);
-          const u16x4 r1 = tr_read(col + (32 * s + 16 + 4 * trG + trJ) * kLdK);
-          ak[s] = cat4(r0, r1);
-        }
-        f32x4 acc = S[t] * dec;
+          for (int t = 0; t < 8; ++t) {
+            const uint16_t* col = B.k + perm_col(16 * t + 4 * trQ);
+            const u16x4 r0 = tr_read(col + (32 * s + 4 * trG + trJ) * kLdK);
+            const u16x4 r1 = tr_read(col + (32 * s + 16 + 4 * trG + trJ) * kLdK);
+            ak[s][t] = cat4(r0, r1);
+          }
+        const float dec = B.dec[0];
+        u16x8 Zhi[2], Zlo[2];
+        make_z(0, Zhi[0], Zlo[0]);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          acc = mfma16(ak[s], Zhi[s], acc);
-          acc = mfma16(ak[s], Zlo[s], acc);
-        }
-        S[t] = acc;
+        for (int t = 0; t < 8; ++t) S[t] = mfma16(ak[0][t], Zhi[0], S[t] * dec);
+        make_z(1, Zhi[1], Zlo[1]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) S[t] = mfma16(ak[0][t], Zlo[0], S[t]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) S[t] = mfma16(ak[1][t], Zhi[1], S[t]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) S[t] = mfma16(ak[1][t], Zlo[1], S[t]);
       }
 
-      // output: o = r * (q S_hi) + Aqk bf16(v_new)
+      // second half of the output: o = r * o_inter + Aqk bf16(v_new)
       if constexpr (COMPUTE_O) {
         u16x8 VNb[2];
 #pragma unroll
-        for (int io = 0; io < 4; ++io)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) VNb[io >> 1][(io & 1) * 4 + e] = bfr(VN[io][e]);
+        for (int hh = 0; hh < 2; ++hh) {
+          u32x4 p;
+          p[0] = pack2(VN[2 * hh][0], VN[2 * hh][1]);
+          p[1] = pack2(VN[2 * hh][2], VN[2 * hh][3]);
+          p[2] = pack2(VN[2 * hh + 1][0], VN[2 * hh + 1][1]);
+          p[3] = pack2(VN[2 * hh + 1][2], VN[2 * hh + 1][3]);
+          VNb[hh] = __builtin_bit_cast(u16x8, p);
+        }
+        u16x8 fa[4][2];
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-          u16x8 fq[4];
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            fq[s] = *reinterpret_cast<const u16x8*>(B.q + (16 * it + l16) * kLdK + 32 * s + 8 * g4);
           const uint16_t* arow = B.aqk + (16 * it + l16) * kLdA + 8 * g4;
-          const u16x8 fa0 = *reinterpret_cast<const u16x8*>(arow);
-          const u16x8 fa1 = *reinterpret_cast<const u16x8*>(arow + 32);
-          f32x4 O = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < 4; ++s) O = mfma16(fq[s], Shi[s], O);
+          fa[it][0] = *reinterpret_cast<const u16x8*>(arow);
+          fa[it][1] = *reinterpret_cast<const u16x8*>(arow + 32);
           const float4 rr = *reinterpret_cast<const float4*>(B.vec + 3 * kChunk + 16 * it + 4 * g4);
-          O[0] *= rr.x; O[1] *= rr.y; O[2] *= rr.z; O[3] *= rr.w;
-          O = mfma16(fa0, VNb[0], O);
-          O = mfma16(fa1, VNb[1], O);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sm.o[b][(16 * it + 4 * g4 + e) * kLdO + w * 16 + l16] = bfr(O[e]);
+          O[it][0] *= rr.x; O[it][1] *= rr.y; O[it][2] *= rr.z; O[it][3] *= rr.w;
         }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int it = 0; it < 4; ++it) O[it] = mfma16(fa[it][s], VNb[s], O[it]);
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sm.o[b][(16 * it + 4 * g4 + e) * kLdO + w * 16 + l16] = bfr(O[it][e]);
       }
     } else {
       if constexpr (COMPUTE_O) {
