@@ -41,7 +41,7 @@ STATE_BYTES_PER_UNIT = 128 * 128 * 4  # one fp32 state per (sequence, head), eac
 ALG_FLOPS_PER_TH = 140629             # conservative (triangle-exploiting) count
 
 
-KERNEL_SOURCES = ("gdn_common.h", "gdn_kernels.h", "gdn_prepare.hip", "gdn_fwd.hip", "gdn_state.hip", "kda_fwd.hip")
+KERNEL_SOURCES = ("gdn_common.h", "gdn_kernels.h", "gdn_prepare.hip", "gdn_fwd.hip", "gdn_state.hip", "gdn_state_common.h", "kda_fwd.hip")
 
 
 def kernel_source_hash() -> str:
@@ -170,7 +170,7 @@ def main():
     path_bytes = prep_bytes + state_bytes
     kernels = {
         "prepare": {"avg_us": prep_us, "alg_bytes": prep_bytes, "symbol": "prepare_kernel"},
-        "state_output": {"avg_us": state_us, "alg_bytes": state_bytes, "symbol": "kda_fwd_kernel" if inp.kda else "gdn_state_kernel"},
+        "state_output": {"avg_us": state_us, "alg_bytes": state_bytes, "symbol": "kda_state_kernel" if inp.kda else "gdn_state_kernel"},
     }
     dom_name = max(kernels, key=lambda n: kernels[n]["avg_us"])
     dom = kernels[dom_name]

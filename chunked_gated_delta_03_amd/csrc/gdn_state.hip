@@ -27,65 +27,18 @@
 //   column 32s + 16h + 4g + e  ->  position 32s + 8g + 4h + e.
 // k^T for the state update is read from the same row-major k with the
 // transposing LDS read (ds_read_b64_tr_b16).
-#include "gdn_kernels.h"
+#include "gdn_state_common.h"
 
 namespace gdn {
 
 namespace {
+using namespace st;
 
 constexpr int kLoaders = 4;              // loader waves per workgroup
 constexpr int kLdK = kDim + 8;           // k, q rows (permuted columns), bf16
 constexpr int kLdT2 = 2 * kChunk + 8;    // T rows: hi | lo (permuted), bf16
 constexpr int kLdA = kChunk + 8;         // Aqk rows (permuted), bf16
 constexpr int kLdVT = kChunk + 8;        // v^T rows (chunk rows in order), bf16
-
-typedef __attribute__((address_space(3))) u16x4 lds_u16x4;
-
-__device__ __forceinline__ int perm_col(int c) {
-  return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3);
-}
-
-__device__ __forceinline__ u16x4 tr_read(const uint16_t* p) {
-  typedef __attribute__((ext_vector_type(4))) short s4;
-  s4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(p));
-  return __builtin_bit_cast(u16x4, r);
-}
-
-__device__ __forceinline__ uint16_t bfr(float x) {
-  return __builtin_bit_cast(uint16_t, (__bf16)x);
-}
-__device__ __forceinline__ void split_hw(float x, uint16_t& hi, uint16_t& lo) {
-  const __bf16 h = (__bf16)x;
-  hi = __builtin_bit_cast(uint16_t, h);
-  lo = __builtin_bit_cast(uint16_t, (__bf16)(x - (float)h));
-}
-
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-
-// Two floats to packed bf16 hi and lo words: hi = bf16(x), lo = bf16(x - hi).
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const uint32_t hp = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
-  const float h0 = __uint_as_float(hp << 16);
-  const float h1 = __uint_as_float(hp & 0xFFFF0000u);
-  hi = hp;
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, bf16x2));
-}
-__device__ __forceinline__ uint32_t pack2(float x0, float x1) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
-}
-// B operand (8 contraction slots) from two accumulator tiles: slots 0..3 are
-// rows 4g..4g+3 of tile a, slots 4..7 the same rows of tile b.
-__device__ __forceinline__ void split_tiles(const f32x4& a, const f32x4& b, u16x8& hi, u16x8& lo) {
-  uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-  split2(a[0], a[1], h0, l0);
-  split2(a[2], a[3], h1, l1);
-  split2(b[0], b[1], h2, l2);
-  split2(b[2], b[3], h3, l3);
-  hi = __builtin_bit_cast(u16x8, u32x4{h0, h1, h2, h3});
-  lo = __builtin_bit_cast(u16x8, u32x4{l0, l1, l2, l3});
-}
 
 template <int NWC>
 struct alignas(16) Smem {
@@ -191,17 +144,11 @@ __global__ __launch_bounds__((NWC + kLoaders) * 64) void gdn_state_kernel(FwdArg
     for (int p = 0; p < 1024 / NL; ++p) {
       const int idx = p * NL + ltid;
       const int r = idx >> 4, c4 = (idx & 15) * 4;
-      const float tv[4] = {tr[p].x, tr[p].y, tr[p].z, tr[p].w};
-      u16x4 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint16_t x0, x1;
-        split_hw(tv[e], x0, x1);
-        hi[e] = x0;
-        lo[e] = x1;
-      }
-      *reinterpret_cast<u16x4*>(B.t + r * kLdT2 + perm_col(c4)) = hi;
-      *reinterpret_cast<u16x4*>(B.t + r * kLdT2 + kChunk + perm_col(c4)) = lo;
+      uint32_t h0, h1, l0, l1;
+      split2(tr[p].x, tr[p].y, h0, l0);
+      split2(tr[p].z, tr[p].w, h1, l1);
+      *reinterpret_cast<uint2*>(B.t + r * kLdT2 + perm_col(c4)) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(B.t + r * kLdT2 + kChunk + perm_col(c4)) = make_uint2(l0, l1);
     }
     if constexpr (COMPUTE_O) {
 #pragma unroll

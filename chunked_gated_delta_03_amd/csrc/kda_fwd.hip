@@ -1,6 +1,9 @@
 // Kimi Delta Attention state kernel (per-key-channel log2 gate): the
-// sequential chunk pass, optionally fused with the output. One workgroup
-// (4 waves) per (sequence, head, 64-column V-block), each wave 16 columns.
+// sequential chunk pass, optionally fused with the output. One workgroup per
+// (sequence, head, V-block of 16*NWC columns): NWC compute waves hold the
+// K x V state (each 128 x 16, MFMA accumulators) and run the recurrence;
+// kLoaders loader waves build the operands of chunk c+1 in registers while
+// chunk c is computed, then write them into LDS between two barriers.
 //
 // Per chunk, with S (K x V) the state entering it, G the chunk-local
 // cumulative log2 gate per channel (written by the prepare kernel) and
@@ -10,29 +13,45 @@
 //   v_new = T (beta v - (beta rk) * (kd S))
 //   o     = (scale rq) * (qd S) + Aqk v_new
 //   S    <- diag(2^G_last) S + kg^T (rk * v_new)
-// kd, kg and the right-hand sides that carry the state are bf16 hi + lo
-// pairs (three products each), as in the GDN kernel.
-#include "gdn_kernels.h"
+// kd, kg (bf16 hi + lo), S and the right-hand sides that carry the state
+// use split products as in the GDN kernel.
+#include "gdn_state_common.h"
 
 namespace gdn {
 
 namespace {
-constexpr int kLdRow = kDim + 8;   // bf16 row stride, 64 x 128 tiles
-constexpr int kLdT = kChunk + 8;   // bf16 row stride, 128 x 64 and 64 x 64 tiles
-constexpr int kNW = 4;             // waves per workgroup
-constexpr int kBV = 16 * kNW;      // V columns per workgroup
-constexpr int kLdV = kBV + 8;
+using namespace st;
+constexpr int kLdRow = kDim + 8;   // bf16 row stride, 64 x 128 tiles (permuted columns)
+constexpr int kLdT = kChunk + 8;   // bf16 row stride, 64 x 64 tiles
+constexpr int kLdT2 = 2 * kChunk + 8;
+constexpr int kLoadersK = 4;
+
+template <int NWC>
+struct alignas(16) KdaSmem {
+  static constexpr int BV = 16 * NWC;
+  static constexpr int kLdO = BV + 8;
+  uint16_t kdh[kChunk * kLdRow];
+  uint16_t kdl[kChunk * kLdRow];
+  uint16_t kgh[kChunk * kLdRow];
+  uint16_t kgl[kChunk * kLdRow];
+  uint16_t qd[kChunk * kLdRow];
+  uint16_t t[kChunk * kLdT2];
+  uint16_t aqk[kChunk * kLdT];
+  uint16_t vt[BV * kLdT];
+  float vec[4 * kChunk];
+  float dec[kDim];
+  uint16_t o[2][kChunk * kLdO];
+};
 }  // namespace
 
-__device__ __forceinline__ u16x8 frag8(const uint16_t* row, int s, int g4) {
-  // contraction slots of K-step s for lane group g4: indices 32s+4g4+(0..3)
-  // and 32s+16+4g4+(0..3), matching the accumulator rows of the B operand.
-  return cat4(*reinterpret_cast<const u16x4*>(row + 32 * s + 4 * g4),
-              *reinterpret_cast<const u16x4*>(row + 32 * s + 16 + 4 * g4));
-}
+template <int NWC, bool STORE_H, bool COMPUTE_O>
+__global__ __launch_bounds__((NWC + kLoadersK) * 64) void kda_state_kernel(FwdArgs a) {
+  using SM = KdaSmem<NWC>;
+  constexpr int BV = SM::BV;
+  constexpr int kLdO = SM::kLdO;
+  constexpr int NL = 64 * kLoadersK;
+  __shared__ SM sm;
 
-template <bool STORE_H, bool COMPUTE_O>
-__global__ __launch_bounds__(kNW * 64) void kda_fwd_kernel(FwdArgs a) {
   const int unit = blockIdx.x;
   const int n = unit / a.H;
   const int h = unit - n * a.H;
@@ -40,271 +59,347 @@ __global__ __launch_bounds__(kNW * 64) void kda_fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int g4 = lane >> 4;
-  const int l16 = lane & 15;
   const int H = a.H;
-  const int colw = vb * kBV + w * 16;
   const SeqInfo si = a.geo.seq(n);
+  const bool compute = w < NWC;
+  const int ltid = tid - NWC * 64;
 
-  __shared__ uint16_t skd_hi[kChunk * kLdRow];
-  __shared__ uint16_t skd_lo[kChunk * kLdRow];
-  __shared__ uint16_t skgT_hi[kDim * kLdT];
-  __shared__ uint16_t skgT_lo[kDim * kLdT];
-  __shared__ uint16_t sTh[kChunk * kLdT];
-  __shared__ uint16_t sTl[kChunk * kLdT];
-  __shared__ uint16_t sv[kChunk * kLdV];
-  __shared__ float sVec[4 * kChunk];
-  __shared__ float sDec[kDim];
-  __shared__ uint16_t sqd[COMPUTE_O ? kChunk * kLdRow : 1];
-  __shared__ uint16_t sAqk[COMPUTE_O ? kChunk * kLdT : 1];
-  __shared__ uint16_t sO[COMPUTE_O ? kChunk * kLdV : 1];
+  // ---------------------------------------------------------------- loaders
+  // thread block of the elementwise k/q/G work: rows m0..m0+3, channels d0..d0+7
+  const int m0 = 4 * (ltid & 15), d0 = 8 * (ltid >> 4);
+  uint32_t rkdh[4][4], rkdl[4][4], rkgh[4][4], rkgl[4][4], rqd[4][4];
+  float4 rt[1024 / NL];
+  uint4 ra[512 / NL];
+  u16x4 rv[4];
+  float4 rvec;
+  float rdec;
+  const int vm0 = 4 * (ltid & 15), vc0 = 4 * (ltid >> 4);
+  constexpr int NVB = 16 * (BV / 4);
 
-  f32x4 S[8];
-  const size_t sbase = ((size_t)n * H + h) * kDim * kDim;
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      S[t][e] = a.s0 ? a.s0[sbase + (size_t)(16 * t + 4 * g4 + e) * kDim + colw + l16] : 0.0f;
-
-  const float* sBeta = sVec;
-  const float* sC = sVec + kChunk;
-  const float* sD = sVec + 2 * kChunk;
-  const float* sR = sVec + 3 * kChunk;
-
-  for (int jc = 0; jc < si.nch; ++jc) {
+  auto build = [&](int jc) {
     const int c = si.c0 + jc;
     const int tok0 = si.tok0 + jc * kChunk;
     const int rem = si.len - jc * kChunk;
     const int len = rem < kChunk ? rem : kChunk;
     const size_t cm = (size_t)h * a.geo.NT + c;
     const float* gk = a.gk + cm * (kChunk * kDim);
-
-    // ---- stage the chunk: each thread a 4-row x 8-channel block -----------
+    float glast[8];
     {
-      const int m0 = 4 * (tid & 15);
-      const int d0 = 8 * (tid >> 4);
-      float glast[8];
-      {
-        const float4 x0 = *reinterpret_cast<const float4*>(gk + 63 * kDim + d0);
-        const float4 x1 = *reinterpret_cast<const float4*>(gk + 63 * kDim + d0 + 4);
-        glast[0] = x0.x; glast[1] = x0.y; glast[2] = x0.z; glast[3] = x0.w;
-        glast[4] = x1.x; glast[5] = x1.y; glast[6] = x1.z; glast[7] = x1.w;
-      }
-      uint16_t kgh[8][4], kgl[8][4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int m = m0 + rr;
-        uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
-        if (m < len) {
-          const size_t off = ((size_t)(tok0 + m) * H + h) * kDim + d0;
-          kv = *reinterpret_cast<const uint4*>(a.k + off);
-          if constexpr (COMPUTE_O) qv = *reinterpret_cast<const uint4*>(a.q + off);
-        }
-        const float4 ga = *reinterpret_cast<const float4*>(gk + m * kDim + d0);
-        const float4 gb = *reinterpret_cast<const float4*>(gk + m * kDim + d0 + 4);
-        const float gv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
-        const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
-        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-        u16x8 kdh, kdl, qdv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float kx = bf2f((uint16_t)((e & 1) ? (kw[e >> 1] >> 16) : (kw[e >> 1] & 0xFFFFu)));
-          const float qx = bf2f((uint16_t)((e & 1) ? (qw[e >> 1] >> 16) : (qw[e >> 1] & 0xFFFFu)));
-          const float fd = exp2f(gv[e]);
-          const float fg = exp2f(glast[e] - gv[e]);
-          uint16_t hh, ll;
-          split_bf(kx * fd, hh, ll);
-          kdh[e] = hh; kdl[e] = ll;
-          split_bf(kx * fg, hh, ll);
-          kgh[e][rr] = hh; kgl[e][rr] = ll;
-          qdv[e] = f2bf(qx * fd);
-        }
-        *reinterpret_cast<u16x8*>(skd_hi + m * kLdRow + d0) = kdh;
-        *reinterpret_cast<u16x8*>(skd_lo + m * kLdRow + d0) = kdl;
-        if constexpr (COMPUTE_O) *reinterpret_cast<u16x8*>(sqd + m * kLdRow + d0) = qdv;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        *reinterpret_cast<u16x4*>(skgT_hi + (d0 + e) * kLdT + m0) = u16x4{kgh[e][0], kgh[e][1], kgh[e][2], kgh[e][3]};
-        *reinterpret_cast<u16x4*>(skgT_lo + (d0 + e) * kLdT + m0) = u16x4{kgl[e][0], kgl[e][1], kgl[e][2], kgl[e][3]};
-      }
-      if (tid < kDim) sDec[tid] = exp2f(gk[63 * kDim + tid]);
+      const float4 x0 = *reinterpret_cast<const float4*>(gk + 63 * kDim + d0);
+      const float4 x1 = *reinterpret_cast<const float4*>(gk + 63 * kDim + d0 + 4);
+      glast[0] = x0.x; glast[1] = x0.y; glast[2] = x0.z; glast[3] = x0.w;
+      glast[4] = x1.x; glast[5] = x1.y; glast[6] = x1.z; glast[7] = x1.w;
     }
-    {
-      const float* tsrc = a.tmat + cm * (kChunk * kChunk);
-      for (int idx = tid; idx < 1024; idx += kNW * 64) {
-        const int r = idx >> 4, c4 = (idx & 15) * 4;
-        const float4 tv4 = reinterpret_cast<const float4*>(tsrc)[idx];
-        const float tv[4] = {tv4.x, tv4.y, tv4.z, tv4.w};
-        u16x4 hi, lo;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint16_t a0, a1;
-          split_bf(tv[e], a0, a1);
-          hi[e] = a0; lo[e] = a1;
-        }
-        *reinterpret_cast<u16x4*>(sTh + r * kLdT + c4) = hi;
-        *reinterpret_cast<u16x4*>(sTl + r * kLdT + c4) = lo;
+    for (int rr = 0; rr < 4; ++rr) {
+      const int m = m0 + rr;
+      uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
+      if (m < len) {
+        const size_t off = ((size_t)(tok0 + m) * H + h) * kDim + d0;
+        kv = *reinterpret_cast<const uint4*>(a.k + off);
+        if constexpr (COMPUTE_O) qv = *reinterpret_cast<const uint4*>(a.q + off);
       }
+      const float4 ga = *reinterpret_cast<const float4*>(gk + m * kDim + d0);
+      const float4 gb = *reinterpret_cast<const float4*>(gk + m * kDim + d0 + 4);
+      const float gv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+      const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+      const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) {
+        const float k0 = __uint_as_float(kw[pr] << 16), k1 = __uint_as_float(kw[pr] & 0xFFFF0000u);
+        const float q0 = __uint_as_float(qw[pr] << 16), q1 = __uint_as_float(qw[pr] & 0xFFFF0000u);
+        const float fd0 = exp2f(gv[2 * pr]), fd1 = exp2f(gv[2 * pr + 1]);
+        const float fg0 = exp2f(glast[2 * pr] - gv[2 * pr]), fg1 = exp2f(glast[2 * pr + 1] - gv[2 * pr + 1]);
+        split2(k0 * fd0, k1 * fd1, rkdh[rr][pr], rkdl[rr][pr]);
+        split2(k0 * fg0, k1 * fg1, rkgh[rr][pr], rkgl[rr][pr]);
+        rqd[rr][pr] = pack2(q0 * fd0, q1 * fd1);
+      }
+    }
+    const float* tsrc = a.tmat + cm * (kChunk * kChunk);
+#pragma unroll
+    for (int p = 0; p < 1024 / NL; ++p) rt[p] = reinterpret_cast<const float4*>(tsrc)[p * NL + ltid];
+    if constexpr (COMPUTE_O) {
+      const uint16_t* asrc = a.aqk + cm * (kChunk * kChunk);
+#pragma unroll
+      for (int p = 0; p < 512 / NL; ++p) ra[p] = reinterpret_cast<const uint4*>(asrc)[p * NL + ltid];
+    }
+    if (ltid < NVB) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = vm0 + e;
+        rv[e] = r < len ? *reinterpret_cast<const u16x4*>(a.v + ((size_t)(tok0 + r) * H + h) * kDim + vb * BV + vc0)
+                        : u16x4{0, 0, 0, 0};
+      }
+    }
+    const float* vsrc = a.vec + cm * (kVecRows * kChunk);
+    if (ltid < 64) rvec = reinterpret_cast<const float4*>(vsrc)[ltid];
+    if (ltid < kDim) rdec = exp2f(gk[63 * kDim + ltid]);
+  };
+
+  auto write = [&]() {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int off = (m0 + rr) * kLdRow;
+      const int p0 = perm_col(d0), p1 = perm_col(d0 + 4);
+      *reinterpret_cast<uint2*>(sm.kdh + off + p0) = make_uint2(rkdh[rr][0], rkdh[rr][1]);
+      *reinterpret_cast<uint2*>(sm.kdh + off + p1) = make_uint2(rkdh[rr][2], rkdh[rr][3]);
+      *reinterpret_cast<uint2*>(sm.kdl + off + p0) = make_uint2(rkdl[rr][0], rkdl[rr][1]);
+      *reinterpret_cast<uint2*>(sm.kdl + off + p1) = make_uint2(rkdl[rr][2], rkdl[rr][3]);
+      *reinterpret_cast<uint2*>(sm.kgh + off + p0) = make_uint2(rkgh[rr][0], rkgh[rr][1]);
+      *reinterpret_cast<uint2*>(sm.kgh + off + p1) = make_uint2(rkgh[rr][2], rkgh[rr][3]);
+      *reinterpret_cast<uint2*>(sm.kgl + off + p0) = make_uint2(rkgl[rr][0], rkgl[rr][1]);
+      *reinterpret_cast<uint2*>(sm.kgl + off + p1) = make_uint2(rkgl[rr][2], rkgl[rr][3]);
       if constexpr (COMPUTE_O) {
-        const uint16_t* asrc = a.aqk + cm * (kChunk * kChunk);
-        for (int idx = tid; idx < 512; idx += kNW * 64) {
-          const int r = idx >> 3, c8 = (idx & 7) * 8;
-          *reinterpret_cast<uint4*>(sAqk + r * kLdT + c8) = reinterpret_cast<const uint4*>(asrc)[idx];
-        }
-      }
-      for (int idx = tid; idx < 64 * kBV / 8; idx += kNW * 64) {
-        const int r = idx / (kBV / 8), cu = idx - r * (kBV / 8);
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (r < len)
-          val = *reinterpret_cast<const uint4*>(a.v + ((size_t)(tok0 + r) * H + h) * kDim + vb * kBV + cu * 8);
-        *reinterpret_cast<uint4*>(sv + r * kLdV + cu * 8) = val;
-      }
-      const float* vsrc = a.vec + cm * (kVecRows * kChunk);
-      if (tid < 64) reinterpret_cast<float4*>(sVec)[tid] = reinterpret_cast<const float4*>(vsrc)[tid];
-    }
-    __syncthreads();
-
-    u16x8 Shi[4], Slo[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint16_t hh, ll;
-        split_bf(S[2 * s][e], hh, ll);
-        Shi[s][e] = hh; Slo[s][e] = ll;
-        split_bf(S[2 * s + 1][e], hh, ll);
-        Shi[s][4 + e] = hh; Slo[s][4 + e] = ll;
-      }
-
-    if constexpr (STORE_H) {
-      float* hd = a.h_out + cm * (kDim * kDim);
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hd[(size_t)(16 * t + 4 * g4 + e) * kDim + colw + l16] = S[t][e];
-    }
-
-    // X = kd S, three split products
-    f32x4 X[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      X[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* rh = skd_hi + (16 * it + l16) * kLdRow;
-      const uint16_t* rl = skd_lo + (16 * it + l16) * kLdRow;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const u16x8 ah = frag8(rh, s, g4);
-        const u16x8 al = frag8(rl, s, g4);
-        X[it] = mfma16(ah, Shi[s], X[it]);
-        X[it] = mfma16(ah, Slo[s], X[it]);
-        X[it] = mfma16(al, Shi[s], X[it]);
+        *reinterpret_cast<uint2*>(sm.qd + off + p0) = make_uint2(rqd[rr][0], rqd[rr][1]);
+        *reinterpret_cast<uint2*>(sm.qd + off + p1) = make_uint2(rqd[rr][2], rqd[rr][3]);
       }
     }
-
-    u16x8 Yhi[2], Ylo[2];
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = 16 * it + 4 * g4 + e;
-        const float vv = bf2f(sv[m * kLdV + w * 16 + l16]);
-        const float y = sBeta[m] * vv - sC[m] * X[it][e];
-        uint16_t hh, ll;
-        split_bf(y, hh, ll);
-        Yhi[it >> 1][(it & 1) * 4 + e] = hh;
-        Ylo[it >> 1][(it & 1) * 4 + e] = ll;
-      }
-
-    f32x4 VN[4];
-#pragma unroll
-    for (int io = 0; io < 4; ++io) {
-      VN[io] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* rh = sTh + (16 * io + l16) * kLdT;
-      const uint16_t* rl = sTl + (16 * io + l16) * kLdT;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const u16x8 ah = frag8(rh, s, g4);
-        const u16x8 al = frag8(rl, s, g4);
-        VN[io] = mfma16(ah, Yhi[s], VN[io]);
-        VN[io] = mfma16(ah, Ylo[s], VN[io]);
-        VN[io] = mfma16(al, Yhi[s], VN[io]);
-      }
+    for (int p = 0; p < 1024 / NL; ++p) {
+      const int idx = p * NL + ltid;
+      const int r = idx >> 4, c4 = (idx & 15) * 4;
+      uint32_t h0, h1, l0, l1;
+      split2(rt[p].x, rt[p].y, h0, l0);
+      split2(rt[p].z, rt[p].w, h1, l1);
+      *reinterpret_cast<uint2*>(sm.t + r * kLdT2 + perm_col(c4)) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(sm.t + r * kLdT2 + kChunk + perm_col(c4)) = make_uint2(l0, l1);
     }
-
-    if constexpr (STORE_H) {
-      float* vd = a.vnew_out + cm * (kChunk * kDim);
-#pragma unroll
-      for (int io = 0; io < 4; ++io)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vd[(size_t)(16 * io + 4 * g4 + e) * kDim + colw + l16] = VN[io][e];
-    }
-
     if constexpr (COMPUTE_O) {
-      u16x8 VNb[2];
 #pragma unroll
-      for (int io = 0; io < 4; ++io)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) VNb[io >> 1][(io & 1) * 4 + e] = f2bf(VN[io][e]);
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        f32x4 O = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t* row = sqd + (16 * it + l16) * kLdRow;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) O = mfma16(frag8(row, s, g4), Shi[s], O);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) O[e] *= sR[16 * it + 4 * g4 + e];
-        const uint16_t* arow = sAqk + (16 * it + l16) * kLdT;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) O = mfma16(frag8(arow, s, g4), VNb[s], O);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sO[(16 * it + 4 * g4 + e) * kLdV + w * 16 + l16] = f2bf(O[e]);
+      for (int p = 0; p < 512 / NL; ++p) {
+        const int idx = p * NL + ltid;
+        const int r = idx >> 3, c8 = (idx & 7) * 8;
+        const u16x8 av = __builtin_bit_cast(u16x8, ra[p]);
+        *reinterpret_cast<u16x4*>(sm.aqk + r * kLdT + perm_col(c8)) = u16x4{av[0], av[1], av[2], av[3]};
+        *reinterpret_cast<u16x4*>(sm.aqk + r * kLdT + perm_col(c8 + 4)) = u16x4{av[4], av[5], av[6], av[7]};
       }
     }
+    if (ltid < NVB) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<u16x4*>(sm.vt + (vc0 + j) * kLdT + vm0) = u16x4{rv[0][j], rv[1][j], rv[2][j], rv[3][j]};
+    }
+    if (ltid < 64) reinterpret_cast<float4*>(sm.vec)[ltid] = rvec;
+    if (ltid < kDim) sm.dec[ltid] = rdec;
+  };
 
-    // S <- diag(2^G_last) S + kg^T (rk * v_new)
-    {
-      u16x8 Zhi[2], Zlo[2];
-#pragma unroll
-      for (int io = 0; io < 4; ++io)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float z = sD[16 * io + 4 * g4 + e] * VN[io][e];
-          uint16_t hh, ll;
-          split_bf(z, hh, ll);
-          Zhi[io >> 1][(io & 1) * 4 + e] = hh;
-          Zlo[io >> 1][(io & 1) * 4 + e] = ll;
-        }
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        f32x4 acc;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = S[t][e] * sDec[16 * t + 4 * g4 + e];
-        const uint16_t* rh = skgT_hi + (16 * t + l16) * kLdT;
-        const uint16_t* rl = skgT_lo + (16 * t + l16) * kLdT;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const u16x8 ah = frag8(rh, s, g4);
-          const u16x8 al = frag8(rl, s, g4);
-          acc = mfma16(ah, Zhi[s], acc);
-          acc = mfma16(ah, Zlo[s], acc);
-          acc = mfma16(al, Zhi[s], acc);
-        }
-        S[t] = acc;
-      }
+  auto store_o = [&](int jc, int b) {
+    const int tok0 = si.tok0 + jc * kChunk;
+    const int rem = si.len - jc * kChunk;
+    const int len = rem < kChunk ? rem : kChunk;
+    constexpr int NOU = 64 * BV / 8;
+    for (int idx = ltid; idx < NOU; idx += NL) {
+      const int r = idx / (BV / 8), cu = idx - r * (BV / 8);
+      if (r < len)
+        *reinterpret_cast<uint4*>(a.o + ((size_t)(tok0 + r) * H + h) * kDim + vb * BV + cu * 8) =
+            *reinterpret_cast<const uint4*>(sm.o[b] + r * kLdO + cu * 8);
     }
+  };
+
+  // ---------------------------------------------------------------- compute
+  const int g4 = lane >> 4;
+  const int l16 = lane & 15;
+  const int colw = vb * BV + w * 16;
+  const size_t sbase = ((size_t)n * H + h) * kDim * kDim;
+  const int trG = lane >> 4, trJ = (lane >> 2) & 3, trQ = lane & 3;
+  // The two roles run separate loops with the same barrier sequence (two
+  // barriers per chunk), so their loop-carried registers never overlap.
+  if (!compute) {
+    build(0);
+    write();
     __syncthreads();
-
-    if constexpr (COMPUTE_O) {
-      for (int idx = tid; idx < 64 * kBV / 8; idx += kNW * 64) {
-        const int r = idx / (kBV / 8), cu = idx - r * (kBV / 8);
-        if (r < len)
-          *reinterpret_cast<uint4*>(a.o + ((size_t)(tok0 + r) * H + h) * kDim + vb * kBV + cu * 8) =
-              *reinterpret_cast<const uint4*>(sO + r * kLdV + cu * 8);
+    for (int jc = 0; jc < si.nch; ++jc) {
+      if constexpr (COMPUTE_O) {
+        if (jc >= 1) store_o(jc - 1, (jc - 1) & 1);
       }
+      if (jc + 1 < si.nch) build(jc + 1);
+      __syncthreads();
+      if (jc + 1 < si.nch) write();
       __syncthreads();
     }
+    if constexpr (COMPUTE_O) {
+      if (si.nch >= 1) store_o(si.nch - 1, (si.nch - 1) & 1);
+    }
+    return;
+  }
+
+  f32x4 S[8];
+  u16x8 Shi[4], Slo[4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      S[t][e] = a.s0 ? a.s0[sbase + (size_t)(16 * t + 4 * g4 + e) * kDim + colw + l16] : 0.0f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) split_tiles(S[2 * s], S[2 * s + 1], Shi[s], Slo[s]);
+  __syncthreads();
+
+  for (int jc = 0; jc < si.nch; ++jc) {
+    const int b = jc & 1;
+    {
+      const int c = si.c0 + jc;
+      const size_t cm = (size_t)h * a.geo.NT + c;
+      if constexpr (STORE_H) {
+        float* hd = a.h_out + cm * (kDim * kDim);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hd[(size_t)(16 * t + 4 * g4 + e) * kDim + colw + l16] = S[t][e];
+      }
+
+      // X = kd S (three split products), four accumulators
+      f32x4 X[4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) X[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u16x8 fh[4], fl[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          fh[it] = *reinterpret_cast<const u16x8*>(sm.kdh + (16 * it + l16) * kLdRow + 32 * s + 8 * g4);
+          fl[it] = *reinterpret_cast<const u16x8*>(sm.kdl + (16 * it + l16) * kLdRow + 32 * s + 8 * g4);
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) X[it] = mfma16(fh[it], Shi[s], X[it]);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) X[it] = mfma16(fh[it], Slo[s], X[it]);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) X[it] = mfma16(fl[it], Shi[s], X[it]);
+      }
+
+      // o_inter = qd S_hi
+      f32x4 O[4];
+      if constexpr (COMPUTE_O) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          u16x8 fq[4];
+#pragma unroll
+          for (int it = 0; it < 4; ++it)
+            fq[it] = *reinterpret_cast<const u16x8*>(sm.qd + (16 * it + l16) * kLdRow + 32 * s + 8 * g4);
+#pragma unroll
+          for (int it = 0; it < 4; ++it) O[it] = mfma16(fq[it], Shi[s], O[it]);
+        }
+      }
+
+      // Y = beta v - (beta rk) X, then v_new = T Y
+      auto make_y = [&](int hh, u16x8& yhi, u16x8& ylo) {
+        f32x4 y2[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int it = 2 * hh + k2;
+          const u16x4 vv = *reinterpret_cast<const u16x4*>(sm.vt + (16 * w + l16) * kLdT + 16 * it + 4 * g4);
+          const float4 bt = *reinterpret_cast<const float4*>(sm.vec + 16 * it + 4 * g4);
+          const float4 cc = *reinterpret_cast<const float4*>(sm.vec + kChunk + 16 * it + 4 * g4);
+          y2[k2][0] = bt.x * bf2f(vv[0]) - cc.x * X[it][0];
+          y2[k2][1] = bt.y * bf2f(vv[1]) - cc.y * X[it][1];
+          y2[k2][2] = bt.z * bf2f(vv[2]) - cc.z * X[it][2];
+          y2[k2][3] = bt.w * bf2f(vv[3]) - cc.w * X[it][3];
+        }
+        split_tiles(y2[0], y2[1], yhi, ylo);
+      };
+      f32x4 VN[4];
+      {
+        u16x8 th[4][2], tl[4][2];
+#pragma unroll
+        for (int io = 0; io < 4; ++io) {
+          const uint16_t* row = sm.t + (16 * io + l16) * kLdT2 + 8 * g4;
+          th[io][0] = *reinterpret_cast<const u16x8*>(row);
+          th[io][1] = *reinterpret_cast<const u16x8*>(row + 32);
+          tl[io][0] = *reinterpret_cast<const u16x8*>(row + kChunk);
+          tl[io][1] = *reinterpret_cast<const u16x8*>(row + kChunk + 32);
+          VN[io] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        u16x8 Yhi[2], Ylo[2];
+        make_y(0, Yhi[0], Ylo[0]);
+#pragma unroll
+        for (int io = 0; io < 4; ++io) VN[io] = mfma16(th[io][0], Yhi[0], VN[io]);
+        make_y(1, Yhi[1], Ylo[1]);
+#pragma unroll
+        for (int io = 0; io < 4; ++io) VN[io] = mfma16(th[io][0], Ylo[0], VN[io]);
+#pragma unroll
+        for (int io = 0; io < 4; ++io) VN[io] = mfma16(tl[io][0], Yhi[0], VN[io]);
+#pragma unroll
+        for (int io = 0; io < 4; ++io) VN[io] = mfma16(th[io][1], Yhi[1], VN[io]);
+#pragma unroll
+        for (int io = 0; io < 4; ++io) VN[io] = mfma16(th[io][1], Ylo[1], VN[io]);
+#pragma unroll
+        for (int io = 0; io < 4; ++io) VN[io] = mfma16(tl[io][1], Yhi[1], VN[io]);
+      }
+      if constexpr (STORE_H) {
+        float* vd = a.vnew_out + cm * (kChunk * kDim);
+#pragma unroll
+        for (int io = 0; io < 4; ++io)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vd[(size_t)(16 * io + 4 * g4 + e) * kDim + colw + l16] = VN[io][e];
+      }
+
+      // output second half first (it only needs v_new): o = r o_inter + Aqk v_new
+      if constexpr (COMPUTE_O) {
+        const u16x8 vnb0 = pack_tiles(VN[0], VN[1]);
+        const u16x8 vnb1 = pack_tiles(VN[2], VN[3]);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const uint16_t* arow = sm.aqk + (16 * it + l16) * kLdT + 8 * g4;
+          const float4 rr = *reinterpret_cast<const float4*>(sm.vec + 3 * kChunk + 16 * it + 4 * g4);
+          O[it][0] *= rr.x; O[it][1] *= rr.y; O[it][2] *= rr.z; O[it][3] *= rr.w;
+          O[it] = mfma16(*reinterpret_cast<const u16x8*>(arow), vnb0, O[it]);
+          O[it] = mfma16(*reinterpret_cast<const u16x8*>(arow + 32), vnb1, O[it]);
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sm.o[b][(16 * it + 4 * g4 + e) * kLdO + w * 16 + l16] = bfr(O[it][e]);
+      }
+
+      // S <- diag(2^G_last) S + kg^T (rk * v_new), three split products
+      {
+        u16x8 Zhi[2], Zlo[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          f32x4 z2[2];
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const int io = 2 * hh + k2;
+            const float4 dd = *reinterpret_cast<const float4*>(sm.vec + 2 * kChunk + 16 * io + 4 * g4);
+            z2[k2][0] = dd.x * VN[io][0];
+            z2[k2][1] = dd.y * VN[io][1];
+            z2[k2][2] = dd.z * VN[io][2];
+            z2[k2][3] = dd.w * VN[io][3];
+          }
+          split_tiles(z2[0], z2[1], Zhi[hh], Zlo[hh]);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float4 dv = *reinterpret_cast<const float4*>(sm.dec + 16 * t + 4 * g4);
+          S[t][0] *= dv.x; S[t][1] *= dv.y; S[t][2] *= dv.z; S[t][3] *= dv.w;
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          u16x8 gh[8], gl[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int pc = perm_col(16 * t + 4 * trQ);
+            const int r0 = (32 * s + 4 * trG + trJ) * kLdRow + pc;
+            const int r1 = (32 * s + 16 + 4 * trG + trJ) * kLdRow + pc;
+            gh[t] = cat4(tr_read(sm.kgh + r0), tr_read(sm.kgh + r1));
+            gl[t] = cat4(tr_read(sm.kgl + r0), tr_read(sm.kgl + r1));
+          }
+#pragma unroll
+          for (int t = 0; t < 8; ++t) S[t] = mfma16(gh[t], Zhi[s], S[t]);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) S[t] = mfma16(gh[t], Zlo[s], S[t]);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) S[t] = mfma16(gl[t], Zhi[s], S[t]);
+        }
+      }
+    }
+    __syncthreads();
+    // split the new state for the next chunk while the loaders write LDS
+#pragma unroll
+    for (int s = 0; s < 4; ++s) split_tiles(S[2 * s], S[2 * s + 1], Shi[s], Slo[s]);
+    __syncthreads();
   }
 
   if (a.sfinal) {
@@ -393,13 +488,16 @@ __global__ __launch_bounds__(256) void kda_finalize_kernel(FinArgs a) {
   }
 }
 
+constexpr int kKdaComputeWaves = 2;
+
 hipError_t launch_kda_fwd(bool store_h, bool compute_o, const FwdArgs& a, hipStream_t stream) {
-  dim3 grid(a.geo.N * a.H, kDim / kBV);
-  dim3 block(64 * kNW);
+  constexpr int NWC = kKdaComputeWaves;
+  dim3 grid(a.geo.N * a.H, kDim / (16 * NWC));
+  dim3 block(64 * (NWC + kLoadersK));
   if (store_h && !compute_o)
-    hipLaunchKernelGGL((kda_fwd_kernel<true, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((kda_state_kernel<NWC, true, false>), grid, block, 0, stream, a);
   else if (!store_h && compute_o)
-    hipLaunchKernelGGL((kda_fwd_kernel<false, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((kda_state_kernel<NWC, false, true>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
