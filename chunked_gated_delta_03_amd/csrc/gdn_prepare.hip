@@ -37,6 +37,10 @@ constexpr int kLdF = kChunk + 1;    // fp32 row stride of a 64 x 64 matrix in LD
 constexpr int kLdQ = kChunk + 8;    // bf16 row stride of a 64 x 64 matrix in LDS
 constexpr int kLdG = kDim + 4;      // fp32 row stride of the 64 x 128 KDA gate
 
+// the 10 lower 16x16 tiles (I >= J) of a 64 x 64 matrix
+__constant__ int kTileI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+__constant__ int kTileJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+
 __device__ __forceinline__ float sumsq8(const uint4& v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   float s = 0.f;
@@ -220,56 +224,59 @@ __global__ __launch_bounds__(256) void gdn_prepare_kernel(PrepareArgs a) {
   }
   __syncthreads();
 
-  // Gram tiles on MFMA: k k^T (strictly lower) and q k^T (lower), 10 lower
-  // 16x16 tiles each; job = kind*10 + tile, wave w takes jobs w, w+4, ...
+  // Gram tiles on MFMA: k k^T (strictly lower) by waves 0-1, q k^T (lower) by
+  // waves 2-3; each wave takes 5 of the 10 lower 16x16 tiles.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int kind = wv >> 1;
+  const uint16_t* left = kind == 0 ? u.in.k : u.in.q;
   f32x4 acc[5];
 #pragma unroll
   for (int jj = 0; jj < 5; ++jj) {
-    const int job = wave + 4 * jj;
-    const int kind = job / 10;
-    int t = job % 10, I = 0;
-    while (t > I) { t -= I + 1; ++I; }
-    const int J = t;
-    const uint16_t* left = kind == 0 ? u.in.k : u.in.q;
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    const int t = (wv & 1) + 2 * jj;
+    const int I = kTileI[t], J = kTileJ[t];
     u16x8 av[4], bv[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       av[s] = *reinterpret_cast<const u16x8*>(left + (16 * I + l16) * kLdRow + 32 * s + 8 * g4);
       bv[s] = *reinterpret_cast<const u16x8*>(u.in.k + (16 * J + l16) * kLdRow + 32 * s + 8 * g4);
     }
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) x = mfma16(av[s], bv[s], x);
     acc[jj] = x;
   }
   __syncthreads();
+  // scale into A (fp32) or Aqk (bf16); the causal mask is applied to the
+  // exponent before the exponential (masked entries use a large negative one)
+  {
+    const float* rrow = kind == 0 ? sRk : sRq;
+    const float sgn = kind == 0 ? -1.0f : a.scale;
 #pragma unroll
-  for (int jj = 0; jj < 5; ++jj) {
-    const int job = wave + 4 * jj;
-    const int kind = job / 10;
-    int t = job % 10, I = 0;
-    while (t > I) { t -= I + 1; ++I; }
-    const int J = t;
-    const int jc = 16 * J + l16;
-    const int i0 = 16 * I + 4 * g4;
-    const float4 gi = *reinterpret_cast<const float4*>(sG + i0);
-    const float4 ri = *reinterpret_cast<const float4*>((kind == 0 ? sRk : sRq) + i0);
-    const float4 bi = *reinterpret_cast<const float4*>(sBeta + i0);
-    const float gj = sG[jc], rj = sRk[jc];
-    const float gia[4] = {gi.x, gi.y, gi.z, gi.w};
-    const float ria[4] = {ri.x, ri.y, ri.z, ri.w};
-    const float bia[4] = {bi.x, bi.y, bi.z, bi.w};
+    for (int jj = 0; jj < 5; ++jj) {
+      const int t = (wv & 1) + 2 * jj;
+      const int I = kTileI[t], J = kTileJ[t];
+      const int jc = 16 * J + l16;
+      const int i0 = 16 * I + 4 * g4;
+      const float4 gi = *reinterpret_cast<const float4*>(sG + i0);
+      const float4 ri = *reinterpret_cast<const float4*>(rrow + i0);
+      const float4 bi = kind == 0 ? *reinterpret_cast<const float4*>(sBeta + i0) : make_float4(1.f, 1.f, 1.f, 1.f);
+      const float gj = sG[jc], rj = sRk[jc] * sgn;
+      const float gia[4] = {gi.x, gi.y, gi.z, gi.w};
+      const float ria[4] = {ri.x, ri.y, ri.z, ri.w};
+      const float bia[4] = {bi.x, bi.y, bi.z, bi.w};
+      float val[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = i0 + e;
+      for (int e = 0; e < 4; ++e) {
+        const float m = (i0 + e + kind > jc) ? 1.0f : 0.0f;  // i > j (k k^T) or i >= j (q k^T)
+        const float ex = __expf((gia[e] - gj) * m);
+        val[e] = m * bia[e] * ria[e] * rj * acc[jj][e] * ex;
+      }
       if (kind == 0) {
-        float val = 0.0f;
-        if (i > jc) val = -bia[e] * ria[e] * rj * acc[jj][e] * __expf(gia[e] - gj);
-        u.mat.A[i * kLdF + jc] = val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u.mat.A[(i0 + e) * kLdF + jc] = val[e];
       } else {
-        float val = 0.0f;
-        if (i >= jc) val = a.scale * ria[e] * rj * acc[jj][e] * __expf(gia[e] - gj);
-        u.mat.aqk[i * kLdQ + jc] = f2bf(val);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u.mat.aqk[(i0 + e) * kLdQ + jc] = __builtin_bit_cast(uint16_t, (__bf16)val[e]);
       }
     }
   }
@@ -332,14 +339,31 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
   load_qk_norms(a, ci, h, tid, sk, sq, sRk, sRq);
   if (wave == 0) load_beta(a, ci, h, lane, sBeta);
 
-  // per-channel cumulative gate: thread (d, half) scans 32 rows
+  // per-channel cumulative gate: the 64 x 128 block is loaded with all its
+  // vector loads in flight, then thread (d, half) scans 32 rows in LDS
+  {
+    float4 gv[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int idx = p * 256 + tid;
+      const int r = idx >> 5, c4 = (idx & 31) * 4;
+      gv[p] = r < ci.len ? *reinterpret_cast<const float4*>(a.g + ((size_t)(ci.tok0 + r) * a.H + h) * kDim + c4)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int idx = p * 256 + tid;
+      const int r = idx >> 5, c4 = (idx & 31) * 4;
+      *reinterpret_cast<float4*>(sG + r * kLdG + c4) = gv[p];
+    }
+  }
+  __syncthreads();
   {
     const int d = tid & 127;
     const int half = tid >> 7;
     float run = 0.0f;
     for (int r = 32 * half; r < 32 * half + 32; ++r) {
-      const float gv = r < ci.len ? a.g[((size_t)(ci.tok0 + r) * a.H + h) * kDim + d] : 0.0f;
-      run += gv;
+      run += sG[r * kLdG + d];
       sG[r * kLdG + d] = run;
     }
   }
