@@ -217,12 +217,15 @@ def workspace_bytes(B, T, H, cu_seqlens=None, kda: bool = False, flags: int = 0)
 
 def gdn_stage_prepare(q, k, g, beta, scale=None, cu_seqlens=None, kda: bool = False, l2norm_qk: bool = False,
                       beta_sigmoid: bool = False, stream=None):
-    """Returns (tmat fp32 [H,NT,64,64], aqk bf16 [H,NT,64,64], vec fp32 [H,NT,8,64], gk fp32 [H,NT,64,128] or None)."""
+    """Returns (tmat bf16 [H,NT,64,128], aqk bf16 [H,NT,64,64], vec fp32 [H,NT,8,64], gk fp32 [H,NT,64,128] or None).
+
+    tmat rows hold T as bf16 hi (64) then lo (64); tmat and aqk store their
+    columns permuted (column 32s+16h+4g+e at position 32s+8g+4h+e)."""
     cu = _cu_array(cu_seqlens)
     B, T, H, K, V, N = _check_inputs(q, k, q, g, beta, kda, None, cu)
     NT = num_chunks(B, T, cu)
     dev = q.device
-    tmat = torch.empty((H, NT, CHUNK, CHUNK), dtype=torch.float32, device=dev)
+    tmat = torch.empty((H, NT, CHUNK, 2 * CHUNK), dtype=torch.bfloat16, device=dev)
     aqk = torch.empty((H, NT, CHUNK, CHUNK), dtype=torch.bfloat16, device=dev)
     vec = torch.empty((H, NT, VEC_ROWS, CHUNK), dtype=torch.float32, device=dev)
     gk = torch.empty((H, NT, CHUNK, K), dtype=torch.float32, device=dev) if kda else None
@@ -242,9 +245,10 @@ def gdn_stage_fwd_h(k, v, tmat, vec, gk=None, initial_state=None, cu_seqlens=Non
     N = B if cu is None else len(cu) - 1
     NT = num_chunks(B, T, cu)
     dev = k.device
-    for name, t, shape in (("tmat", tmat, (H, NT, CHUNK, CHUNK)), ("vec", vec, (H, NT, VEC_ROWS, CHUNK))):
-        if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError("%s must be contiguous fp32 %s" % (name, shape))
+    for name, t, shape, dt in (("tmat", tmat, (H, NT, CHUNK, 2 * CHUNK), torch.bfloat16),
+                               ("vec", vec, (H, NT, VEC_ROWS, CHUNK), torch.float32)):
+        if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous():
+            raise ValueError("%s must be contiguous %s %s" % (name, dt, shape))
     if tuple(v.shape) != (B, T, H, V) or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
         raise ValueError("k, v must be bf16 [B,T,H,128]")
     if initial_state is not None and tuple(initial_state.shape) != (N, H, K, V):

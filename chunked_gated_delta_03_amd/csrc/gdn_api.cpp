@@ -130,7 +130,7 @@ Layout layout_for(const Problem& p, bool with_intermediates) {
   if (with_intermediates) {
     const size_t cmH = (size_t)p.NT * p.H;
     L.tmat = off;
-    off += align256(cmH * GDN_CHUNK * GDN_CHUNK * sizeof(float));
+    off += align256(cmH * GDN_CHUNK * 2 * GDN_CHUNK * sizeof(uint16_t));  // T as bf16 hi | lo
     L.aqk = off;
     off += align256(cmH * GDN_CHUNK * GDN_CHUNK * sizeof(uint16_t));
     L.vec = off;
@@ -178,17 +178,17 @@ int upload_tables(const Problem& p, void* dst, hipStream_t stream) {
   const size_t bytes = tab.size() * sizeof(int4);
 
   int dev = 0;
-  hipGetDevice(&dev);
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   std::lock_guard<std::mutex> lock(g_stage_mu);
   StagingSlot& s = g_slots[g_next_slot++ % 8];
-  hipError_t e;
   if (s.pending) {
     e = hipEventSynchronize(s.done);
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(staging)");
     s.pending = false;
   }
   if (s.device != dev && s.done) {
-    hipEventDestroy(s.done);
+    (void)hipEventDestroy(s.done);
     s.done = nullptr;
   }
   if (!s.done) {
@@ -197,7 +197,7 @@ int upload_tables(const Problem& p, void* dst, hipStream_t stream) {
     s.device = dev;
   }
   if (s.cap < bytes) {
-    if (s.host) hipHostFree(s.host);
+    if (s.host) (void)hipHostFree(s.host);
     s.host = nullptr;
     s.cap = 0;
     e = hipHostMalloc(&s.host, bytes, hipHostMallocDefault);
@@ -235,7 +235,7 @@ struct Workspace {
   bool owned = false;
   hipStream_t stream = nullptr;
   ~Workspace() {
-    if (owned && base) hipFreeAsync(base, stream);
+    if (owned && base) (void)hipFreeAsync(base, stream);
   }
 };
 
@@ -333,7 +333,7 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
   pa.k = static_cast<const uint16_t*>(k);
   pa.g = g;
   pa.beta = static_cast<const uint16_t*>(beta);
-  pa.tmat = reinterpret_cast<float*>(W.base + L.tmat);
+  pa.tmat = reinterpret_cast<uint16_t*>(W.base + L.tmat);
   pa.aqk = reinterpret_cast<uint16_t*>(W.base + L.aqk);
   pa.vec = reinterpret_cast<float*>(W.base + L.vec);
   pa.gk = kda ? reinterpret_cast<float*>(W.base + L.gk) : nullptr;
@@ -476,7 +476,7 @@ int gdn_timing_read(double* prepare_ms, double* state_ms, int64_t* calls) {
 
 int gdn_stage_prepare(int32_t kda, const void* q, const void* k, const float* g, const void* beta,
                       const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
-                      int32_t V, float scale, uint32_t flags, float* tmat, void* aqk, float* vec, float* gk,
+                      int32_t V, float scale, uint32_t flags, void* tmat, void* aqk, float* vec, float* gk,
                       void* stream_ptr) {
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   g_last_error.clear();
@@ -492,7 +492,7 @@ int gdn_stage_prepare(int32_t kda, const void* q, const void* k, const float* g,
   pa.k = static_cast<const uint16_t*>(k);
   pa.g = g;
   pa.beta = static_cast<const uint16_t*>(beta);
-  pa.tmat = tmat;
+  pa.tmat = static_cast<uint16_t*>(tmat);
   pa.aqk = static_cast<uint16_t*>(aqk);
   pa.vec = vec;
   pa.gk = gk;
@@ -505,7 +505,7 @@ int gdn_stage_prepare(int32_t kda, const void* q, const void* k, const float* g,
   return GDN_OK;
 }
 
-int gdn_stage_fwd_h(int32_t kda, const void* k, const void* v, const float* tmat, const float* vec, const float* gk,
+int gdn_stage_fwd_h(int32_t kda, const void* k, const void* v, const void* tmat, const float* vec, const float* gk,
                     const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
                     int32_t H, int32_t K, int32_t V, uint32_t flags, float* h, float* v_new, float* final_state,
                     void* stream_ptr) {
@@ -523,7 +523,7 @@ int gdn_stage_fwd_h(int32_t kda, const void* k, const void* v, const float* tmat
   gdn::FwdArgs fa{};
   fa.k = static_cast<const uint16_t*>(k);
   fa.v = static_cast<const uint16_t*>(v);
-  fa.tmat = tmat;
+  fa.tmat = static_cast<const uint16_t*>(tmat);
   fa.vec = vec;
   fa.gk = gk;
   fa.s0 = initial_state;

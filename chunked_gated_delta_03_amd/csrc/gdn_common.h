@@ -32,6 +32,39 @@ __device__ __forceinline__ void split_bf(float x, uint16_t& hi, uint16_t& lo) {
   lo = f2bf(x - bf2f(hi));
 }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// Two floats to one packed pair of bf16 (round to nearest even).
+__device__ __forceinline__ uint32_t pack2(float x0, float x1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+}
+
+// Two floats to packed bf16 hi and lo words: hi = bf16(x), lo = bf16(x - hi).
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t hp = pack2(x0, x1);
+  const float h0 = __uint_as_float(hp << 16);
+  const float h1 = __uint_as_float(hp & 0xFFFF0000u);
+  hi = hp;
+  lo = pack2(x0 - h0, x1 - h1);
+}
+
+// ---- permuted contraction columns ---------------------------------------------
+// An MFMA 16x16x32 contraction step s takes, in lane group g (= lane / 16),
+// contraction indices 32s + 4g + (0..3) and 32s + 16 + 4g + (0..3): the
+// accumulator rows that a B operand built from two accumulator tiles holds.
+// Matrices used as A operands against such B operands store their columns
+// permuted so that these eight indices are adjacent (one 16-byte read):
+//   column 32s + 16h + 4g + e  ->  position 32s + 8g + 4h + e.
+__device__ __forceinline__ int perm_col(int c) {
+  return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3);
+}
+// inverse: the column stored at position p
+__device__ __forceinline__ int unperm_col(int p) {
+  return (p & ~31) | ((p & 4) << 2) | ((p & 24) >> 1) | (p & 3);
+}
+
 // ---- MFMA ------------------------------------------------------------------
 // v_mfma_f32_16x16x32_bf16, wave64. Lane l: A row (l % 16), B column (l % 16),
 // both holding contraction slots 8*(l/16) .. 8*(l/16)+7; D column (l % 16),

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void gdn_finalize_kernel(FinArgs a) {
   }
   for (int idx = tid; idx < 64 * 64; idx += 256) {
     const int r = idx >> 6, cc = idx & 63;
-    sAqk[r * kLdT + cc] = a.aqk[cm * 4096 + idx];
+    sAqk[r * kLdT + unperm_col(cc)] = a.aqk[cm * 4096 + idx];
   }
   for (int idx = tid; idx < kDim * kDim; idx += 256) {
     const int r = idx >> 7, cc = idx & 127;

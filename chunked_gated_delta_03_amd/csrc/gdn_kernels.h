@@ -13,8 +13,8 @@ struct PrepareArgs {
   const uint16_t* k;
   const float* g;
   const uint16_t* beta;
-  float* tmat;     // [H,NT,64,64]
-  uint16_t* aqk;   // [H,NT,64,64]
+  uint16_t* tmat;  // [H,NT,64,128] bf16 hi | lo, permuted columns
+  uint16_t* aqk;   // [H,NT,64,64] bf16, permuted columns
   float* vec;      // [H,NT,8,64]
   float* gk;       // [H,NT,64,128], KDA only
   Geometry geo;
@@ -27,8 +27,8 @@ struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  const float* tmat;
-  const uint16_t* aqk;
+  const uint16_t* tmat;  // [H,NT,64,128] bf16 hi | lo, permuted columns
+  const uint16_t* aqk;   // [H,NT,64,64] bf16, permuted columns
   const float* vec;
   const float* gk;       // KDA only
   const float* s0;       // [N,H,K,V] or nullptr
@@ -42,7 +42,7 @@ struct FwdArgs {
 
 struct FinArgs {
   const uint16_t* q;
-  const uint16_t* aqk;
+  const uint16_t* aqk;   // permuted columns
   const float* vec;
   const float* gk;       // KDA only
   const float* h;

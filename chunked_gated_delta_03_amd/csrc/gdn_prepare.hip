@@ -153,32 +153,36 @@ __device__ __forceinline__ void invert_unit_lower(const float* sA, float* sT, in
 }
 
 // T (fp32) and Aqk (bf16) to global, zero above the diagonal blocks.
+// T and Aqk to HBM in the layout the state kernel stages without arithmetic:
+// T as a bf16 hi | lo pair per element (row r: 64 hi then 64 lo), Aqk as
+// bf16, both with their columns permuted by perm_col. Thread item (r, m)
+// forms output positions 8m .. 8m+7 of row r; blocks above the diagonal are
+// zero.
 __device__ __forceinline__ void store_t_aqk(const PrepareArgs& a, size_t cm, int tid, const float* sT,
                                             const uint16_t* sAqk) {
-  float* tdst = a.tmat + cm * (kChunk * kChunk);
-#pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    const int idx = pass * 256 + tid;
-    const int r = idx >> 4;
-    const int c4 = (idx & 15) * 4;
-    float4 val;
-    const bool upper = (c4 >> 4) > (r >> 4);
-    val.x = upper ? 0.f : sT[r * kLdF + c4 + 0];
-    val.y = upper ? 0.f : sT[r * kLdF + c4 + 1];
-    val.z = upper ? 0.f : sT[r * kLdF + c4 + 2];
-    val.w = upper ? 0.f : sT[r * kLdF + c4 + 3];
-    *reinterpret_cast<float4*>(tdst + r * kChunk + c4) = val;
-  }
+  uint16_t* tdst = a.tmat + cm * (kChunk * 2 * kChunk);
   uint16_t* qdst = a.aqk + cm * (kChunk * kChunk);
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int idx = pass * 256 + tid;
-    const int r = idx >> 3;
-    const int c8 = (idx & 7) * 8;
-    u16x8 val;
+    const int r = idx >> 3, m = idx & 7;
+    const int c0 = 32 * (m >> 2) + 4 * (m & 3);  // columns c0 + e and c0 + 16 + e
+    const bool up0 = (c0 >> 4) > (r >> 4);
+    const bool up1 = ((c0 + 16) >> 4) > (r >> 4);
+    float x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) val[e] = ((c8 >> 4) > (r >> 4)) ? (uint16_t)0 : sAqk[r * kLdQ + c8 + e];
-    *reinterpret_cast<u16x8*>(qdst + r * kChunk + c8) = val;
+    for (int e = 0; e < 4; ++e) {
+      x[e] = up0 ? 0.f : sT[r * kLdF + c0 + e];
+      x[4 + e] = up1 ? 0.f : sT[r * kLdF + c0 + 16 + e];
+    }
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) split2(x[2 * p], x[2 * p + 1], hi[p], lo[p]);
+    *reinterpret_cast<uint4*>(tdst + r * (2 * kChunk) + 8 * m) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *reinterpret_cast<uint4*>(tdst + r * (2 * kChunk) + kChunk + 8 * m) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    const u16x4 q0 = up0 ? u16x4{0, 0, 0, 0} : *reinterpret_cast<const u16x4*>(sAqk + r * kLdQ + c0);
+    const u16x4 q1 = up1 ? u16x4{0, 0, 0, 0} : *reinterpret_cast<const u16x4*>(sAqk + r * kLdQ + c0 + 16);
+    *reinterpret_cast<u16x8*>(qdst + r * kChunk + 8 * m) = cat4(q0, q1);
   }
 }
 

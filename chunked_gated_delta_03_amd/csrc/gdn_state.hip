@@ -1,13 +1,15 @@
 // State kernel (GDN): the sequential chunk pass (chunk_fwd_h), fused with the
 // output (finalize) for the whole-pass entry. One workgroup per (sequence,
-// head, V-block of 16*NWC columns) with two kinds of waves:
-//   - NWC compute waves, each holding a 128 x 16 block of the fp32 K x V state
-//     in MFMA accumulators and running the chunk recurrence;
-//   - kLoaders loader waves that, while the compute waves work on chunk c out
-//     of one LDS buffer, stage chunk c+1 into the other (q, k rows, T split
-//     into bf16 hi/lo, Aqk, v transposed, per-row vectors) and write the
-//     output rows of chunk c-1 to HBM.
-// One workgroup barrier per chunk.
+// head, V-block of 16*NCB columns) with two kinds of waves:
+//   - 2*NCB compute waves. Each 16-column slice of the fp32 K x V state is
+//     held by a pair of waves, one per half of the K rows (64 x 16 each, in
+//     MFMA accumulators), so a wave carries half of every K-contraction. A
+//     compute wave also stores its output rows of chunk c-1 during chunk c;
+//   - kLoaders loader waves that write chunk c+1 (loaded into registers
+//     during chunk c-1) into the other LDS buffer at the start of chunk c
+//     and issue the loads of chunk c+2.
+// Two workgroup barriers per chunk: one after the pairs have posted their
+// partial sums, one when the chunk's buffers change hands.
 //
 // Per chunk, with S the state entering it (hyper-parallel "Diff Coverage"
 // page, gate build 2026-09-10, _run_prepared_gdn_chunks and the state update
@@ -15,18 +17,29 @@
 //   v_new = U - W S = T (beta v - c * (k S)),     c = beta * rk * exp(G)
 //   o     = (q * r) S + Aqk v_new,                r = scale * rq * exp(G)
 //   S    <- exp(G_last) S + k^T (d * v_new),      d = rk * exp(G_last - G)
-// k, q and v enter the MFMAs as the exact bf16 inputs; the operands that
-// carry the state (S in k S, T and the right-hand side in T(...), d * v_new
-// in the update) are bf16 hi + lo pairs with fp32 accumulation.
+// In a pair, each wave forms k S and q S over its K half; the halves are
+// summed through LDS. Both waves then form the whole v_new (T times the
+// right-hand side), update their own K half of S, and finish 32 of the 64
+// output rows. k, q and v enter the MFMAs as the exact bf16 inputs; the
+// operands that carry the state (S in k S, T and the right-hand side in T(...),
+// d * v_new in the update) are bf16 hi + lo pairs with fp32 accumulation.
 //
-// LDS layouts. An MFMA 16x16x32 contraction step s takes, in lane group g4,
-// the contraction indices 32s + 4 g4 + (0..3) and 32s + 16 + 4 g4 + (0..3):
-// those are the accumulator rows the B operand (S, Y or Z) already holds in
-// registers. Matrices read as A operands store their columns permuted so that
-// these eight indices are adjacent (one 16-byte read):
-//   column 32s + 16h + 4g + e  ->  position 32s + 8g + 4h + e.
-// k^T for the state update is read from the same row-major k with the
-// transposing LDS read (ds_read_b64_tr_b16).
+// Layouts. Row i of state tile t (16 K rows) holds K index perm_col(16 t + i):
+// then the B operand of contraction step s built from tiles 2s, 2s+1 covers
+// K indices 32s + 8g .. 32s + 8g + 7 in lane group g, which an A-operand
+// fragment of a k or q row reads as one 16-byte piece in natural column
+// order. k, q and T rows (256 bytes) are stored as 16-byte pieces with piece p
+// of row r at slot p ^ (r & 15), Aqk rows (128 bytes) with p ^ (r & 7), so
+// that the 16 rows of a fragment read fall on distinct banks; T (hi | lo) and
+// Aqk come from the prepare kernel with permuted columns. k^T for the update
+// and the v columns are read with the transposing LDS read (ds_read_b64_tr_b16).
+//
+// Register arrays are indexed with compile-time indices only (the compute
+// loop is specialised per K half): an index that depends on the wave becomes
+// an indexed register move, whose read of an MFMA result is not ordered
+// after the MFMA, or a private-memory array.
+#include <type_traits>
+
 #include "gdn_state_common.h"
 
 namespace gdn {
@@ -35,35 +48,34 @@ namespace {
 using namespace st;
 
 constexpr int kLoaders = 4;              // loader waves per workgroup
-constexpr int kLdK = kDim + 8;           // k, q rows (permuted columns), bf16
-constexpr int kLdT2 = 2 * kChunk + 8;    // T rows: hi | lo (permuted), bf16
-constexpr int kLdA = kChunk + 8;         // Aqk rows (permuted), bf16
-constexpr int kLdVT = kChunk + 8;        // v^T rows (chunk rows in order), bf16
 
-template <int NWC>
+template <int NCB>
 struct alignas(16) Smem {
-  static constexpr int BV = 16 * NWC;
-  static constexpr int kLdO = BV + 8;
+  static constexpr int BV = 16 * NCB;
+  static constexpr int NCW = 2 * NCB;    // compute waves
   struct alignas(16) Buf {
-    uint16_t k[kChunk * kLdK];
-    uint16_t q[kChunk * kLdK];
-    uint16_t t[kChunk * kLdT2];
-    uint16_t aqk[kChunk * kLdA];
-    uint16_t vt[BV * kLdVT];
-    float vec[4 * kChunk];
-    float dec[4];
+    uint16_t k[kChunk * kDim];           // swizzled 16-byte pieces
+    uint16_t q[kChunk * kDim];
+    uint16_t t[kChunk * 2 * kChunk];     // hi | lo, swizzled pieces
+    uint16_t aqk[kChunk * kChunk];       // swizzled pieces (8 per row)
+    uint16_t v[kChunk * BV];             // v rows of this V-block
+    float vec[kVecRows * kChunk];
   };
   Buf buf[2];
-  uint16_t o[2][kChunk * kLdO];
+  // per wave: its partial k S (4 tiles) and the partner's two tiles of its
+  // partial q S; lane-major 16-byte slots
+  f32x4 xch[NCW][6][64];
+  // per wave: its 32 output rows x 16 columns (bf16) of the last chunk
+  uint16_t o[NCW][32 * 16];
 };
 
 }  // namespace
 
-template <int NWC, bool STORE_H, bool COMPUTE_O>
-__global__ __launch_bounds__((NWC + kLoaders) * 64) void gdn_state_kernel(FwdArgs a) {
-  using SM = Smem<NWC>;
+template <int NCB, bool STORE_H, bool COMPUTE_O>
+__global__ __launch_bounds__((2 * NCB + kLoaders) * 64) void gdn_state_kernel(FwdArgs a) {
+  using SM = Smem<NCB>;
   constexpr int BV = SM::BV;
-  constexpr int kLdO = SM::kLdO;
+  constexpr int NCW = SM::NCW;
   __shared__ SM sm;
 
   const int unit = blockIdx.x;
@@ -72,207 +84,203 @@ __global__ __launch_bounds__((NWC + kLoaders) * 64) void gdn_state_kernel(FwdArg
   const int vb = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H;
   const SeqInfo si = a.geo.seq(n);
-  const bool compute = w < NWC;
+  const int last = si.nch - 1;
 
-  // ------------------------------------------------------------------ loaders
-  const int ltid = tid - NWC * 64;  // 0 .. 64*kLoaders-1 on loader waves
-  auto stage = [&](int jc, int b) {
-    typename SM::Buf& B = sm.buf[b];
-    const int c = si.c0 + jc;
-    const int tok0 = si.tok0 + jc * kChunk;
-    const int rem = si.len - jc * kChunk;
-    const int len = rem < kChunk ? rem : kChunk;
-    const size_t cm = (size_t)h * a.geo.NT + c;
+  // ------------------------------------------------------------- loaders
+  if (w >= NCW) {
+    // Chunk jc's operands as 16-byte pieces: loader lane ltid takes pieces
+    // ltid + NL*p of each array, loads them into registers one chunk ahead
+    // and writes them to their (swizzled) LDS slots. Rows of k, q, v past the
+    // end of the sequence are zero.
     constexpr int NL = 64 * kLoaders;
-    // k (and q): 16-byte pieces of rows, written as two permuted halves
-    uint4 kr[1024 / NL], qr[1024 / NL];
+    constexpr int PPR = BV / 8;              // v pieces per row
+    const int ltid = tid - NCW * 64;
+    u32x4 kr[1024 / NL], qr[1024 / NL], tr[1024 / NL], ar[512 / NL], vr, er;
+    auto fetch = [&](int jc) {
+      const int tok0 = si.tok0 + jc * kChunk;
+      const int rem = si.len - jc * kChunk;
+      const int len = rem < kChunk ? rem : kChunk;
+      const size_t cm = (size_t)h * a.geo.NT + si.c0 + jc;
 #pragma unroll
-    for (int p = 0; p < 1024 / NL; ++p) {
-      const int idx = p * NL + ltid;
-      const int r = idx >> 4, cc = (idx & 15) * 8;
-      const size_t off = ((size_t)(tok0 + r) * H + h) * kDim + cc;
-      kr[p] = r < len ? *reinterpret_cast<const uint4*>(a.k + off) : make_uint4(0, 0, 0, 0);
-      if constexpr (COMPUTE_O) qr[p] = r < len ? *reinterpret_cast<const uint4*>(a.q + off) : make_uint4(0, 0, 0, 0);
-    }
-    float4 tr[1024 / NL];
-    const float* tsrc = a.tmat + cm * (kChunk * kChunk);
-#pragma unroll
-    for (int p = 0; p < 1024 / NL; ++p) tr[p] = reinterpret_cast<const float4*>(tsrc)[p * NL + ltid];
-    uint4 ar[512 / NL];
-    if constexpr (COMPUTE_O) {
-      const uint16_t* asrc = a.aqk + cm * (kChunk * kChunk);
-#pragma unroll
-      for (int p = 0; p < 512 / NL; ++p) ar[p] = reinterpret_cast<const uint4*>(asrc)[p * NL + ltid];
-    }
-    // v block as 4 rows x 4 columns per thread
-    constexpr int NVB = 16 * (BV / 4);  // blocks
-    u16x4 vr[4];
-    const int vbk = ltid;
-    const int vm0 = 4 * (vbk & 15), vc0 = 4 * (vbk >> 4);
-    if (vbk < NVB) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = vm0 + e;
-        vr[e] = r < len ? *reinterpret_cast<const u16x4*>(a.v + ((size_t)(tok0 + r) * H + h) * kDim + vb * BV + vc0)
-                        : u16x4{0, 0, 0, 0};
+      for (int p = 0; p < 1024 / NL; ++p) {
+        const int idx = p * NL + ltid, r = idx >> 4;
+        const size_t off = ((size_t)(tok0 + r) * H + h) * kDim + 8 * (idx & 15);
+        kr[p] = r < len ? *reinterpret_cast<const u32x4*>(a.k + off) : u32x4{0, 0, 0, 0};
+        if constexpr (COMPUTE_O) qr[p] = r < len ? *reinterpret_cast<const u32x4*>(a.q + off) : u32x4{0, 0, 0, 0};
+        tr[p] = reinterpret_cast<const u32x4*>(a.tmat + cm * (kChunk * 2 * kChunk))[idx];
       }
-    }
-    const float* vsrc = a.vec + cm * (kVecRows * kChunk);
-    float4 vecr = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (ltid < 64) vecr = reinterpret_cast<const float4*>(vsrc)[ltid];
-    float decr = 0.f;
-    if (ltid == 64) decr = vsrc[7 * kChunk];
-
-    // ---- LDS writes
-#pragma unroll
-    for (int p = 0; p < 1024 / NL; ++p) {
-      const int idx = p * NL + ltid;
-      const int r = idx >> 4, cc = (idx & 15) * 8;
-      const u16x8 kv = __builtin_bit_cast(u16x8, kr[p]);
-      *reinterpret_cast<u16x4*>(B.k + r * kLdK + perm_col(cc)) = u16x4{kv[0], kv[1], kv[2], kv[3]};
-      *reinterpret_cast<u16x4*>(B.k + r * kLdK + perm_col(cc + 4)) = u16x4{kv[4], kv[5], kv[6], kv[7]};
       if constexpr (COMPUTE_O) {
-        const u16x8 qv = __builtin_bit_cast(u16x8, qr[p]);
-        *reinterpret_cast<u16x4*>(B.q + r * kLdK + perm_col(cc)) = u16x4{qv[0], qv[1], qv[2], qv[3]};
-        *reinterpret_cast<u16x4*>(B.q + r * kLdK + perm_col(cc + 4)) = u16x4{qv[4], qv[5], qv[6], qv[7]};
+#pragma unroll
+        for (int p = 0; p < 512 / NL; ++p) ar[p] = reinterpret_cast<const u32x4*>(a.aqk + cm * (kChunk * kChunk))[p * NL + ltid];
       }
-    }
-#pragma unroll
-    for (int p = 0; p < 1024 / NL; ++p) {
-      const int idx = p * NL + ltid;
-      const int r = idx >> 4, c4 = (idx & 15) * 4;
-      uint32_t h0, h1, l0, l1;
-      split2(tr[p].x, tr[p].y, h0, l0);
-      split2(tr[p].z, tr[p].w, h1, l1);
-      *reinterpret_cast<uint2*>(B.t + r * kLdT2 + perm_col(c4)) = make_uint2(h0, h1);
-      *reinterpret_cast<uint2*>(B.t + r * kLdT2 + kChunk + perm_col(c4)) = make_uint2(l0, l1);
-    }
-    if constexpr (COMPUTE_O) {
-#pragma unroll
-      for (int p = 0; p < 512 / NL; ++p) {
-        const int idx = p * NL + ltid;
-        const int r = idx >> 3, c8 = (idx & 7) * 8;
-        const u16x8 av = __builtin_bit_cast(u16x8, ar[p]);
-        *reinterpret_cast<u16x4*>(B.aqk + r * kLdA + perm_col(c8)) = u16x4{av[0], av[1], av[2], av[3]};
-        *reinterpret_cast<u16x4*>(B.aqk + r * kLdA + perm_col(c8 + 4)) = u16x4{av[4], av[5], av[6], av[7]};
+      if (ltid < 64 * PPR) {
+        const int r = ltid / PPR;
+        vr = r < len ? *reinterpret_cast<const u32x4*>(a.v + ((size_t)(tok0 + r) * H + h) * kDim + vb * BV + 8 * (ltid % PPR))
+                     : u32x4{0, 0, 0, 0};
       }
-    }
-    if (vbk < NVB) {
+      if (ltid < kVecRows * kChunk / 4) er = reinterpret_cast<const u32x4*>(a.vec + cm * (kVecRows * kChunk))[ltid];
+    };
+    // part 0: k, q; part 1: T, Aqk, v, row vectors
+    auto put = [&](int b, int part) {
+      typename SM::Buf& B = sm.buf[b];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<u16x4*>(B.vt + (vc0 + j) * kLdVT + vm0) = u16x4{vr[0][j], vr[1][j], vr[2][j], vr[3][j]};
-    }
-    if (ltid < 64) reinterpret_cast<float4*>(B.vec)[ltid] = vecr;
-    if (ltid == 64) B.dec[0] = decr;
-  };
-
-  auto store_o = [&](int jc, int b) {
-    const int tok0 = si.tok0 + jc * kChunk;
-    const int rem = si.len - jc * kChunk;
-    const int len = rem < kChunk ? rem : kChunk;
-    constexpr int NOU = 64 * BV / 8;
-    for (int idx = ltid; idx < NOU; idx += 64 * kLoaders) {
-      const int r = idx / (BV / 8), cu = idx - r * (BV / 8);
-      if (r < len)
-        *reinterpret_cast<uint4*>(a.o + ((size_t)(tok0 + r) * H + h) * kDim + vb * BV + cu * 8) =
-            *reinterpret_cast<const uint4*>(sm.o[b] + r * kLdO + cu * 8);
-    }
-  };
-
-  // ------------------------------------------------------------------ compute
-  const int g4 = lane >> 4;
-  const int l16 = lane & 15;
-  const int colw = vb * BV + w * 16;
-  const size_t sbase = ((size_t)n * H + h) * kDim * kDim;
-  f32x4 S[8];
-  if (compute) {
+      for (int p = 0; p < 1024 / NL; ++p) {
+        const int idx = p * NL + ltid, r = idx >> 4;
+        const int slot = 8 * ((idx & 15) ^ (r & 15));
+        if (part == 0) {
+          *reinterpret_cast<u32x4*>(B.k + r * kDim + slot) = kr[p];
+          if constexpr (COMPUTE_O) *reinterpret_cast<u32x4*>(B.q + r * kDim + slot) = qr[p];
+        } else {
+          *reinterpret_cast<u32x4*>(B.t + r * (2 * kChunk) + slot) = tr[p];
+        }
+      }
+      if (part == 0) return;
+      if constexpr (COMPUTE_O) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        S[t][e] = a.s0 ? a.s0[sbase + (size_t)(16 * t + 4 * g4 + e) * kDim + colw + l16] : 0.0f;
+        for (int p = 0; p < 512 / NL; ++p) {
+          const int idx = p * NL + ltid, r = idx >> 3;
+          *reinterpret_cast<u32x4*>(B.aqk + r * kChunk + 8 * ((idx & 7) ^ (r & 7))) = ar[p];
+        }
+      }
+      if (ltid < 64 * PPR) *reinterpret_cast<u32x4*>(B.v + 8 * ltid) = vr;
+      if (ltid < kVecRows * kChunk / 4) *reinterpret_cast<u32x4*>(B.vec + 4 * ltid) = er;
+    };
+    // Same barrier sequence as the compute waves: one before the loop, two
+    // per chunk. During chunk jc, chunk jc+1 goes into the buffer chunk jc-1
+    // released (k and q before the first barrier, the rest after it) and the
+    // loads of chunk jc+2 are issued. Both run unconditionally (past the end
+    // the last chunk is repeated, harmlessly), so no load waits for another.
+    if (si.nch > 0) {
+      fetch(0);
+      put(0, 0);
+      put(0, 1);
+      fetch(min(1, last));
+    }
+    __syncthreads();
+    for (int jc = 0; jc < si.nch; ++jc) {
+      const int bn = (jc & 1) ^ 1;
+      put(bn, 0);
+      __syncthreads();
+      put(bn, 1);
+      fetch(min(jc + 2, last));
+      __syncthreads();
+    }
+    return;
   }
-  // transposing-read lane roles: group G = lane/16, row offset j, column quad qd
-  const int trG = lane >> 4, trJ = (lane >> 2) & 3, trQ = lane & 3;
 
-  if (!compute) stage(0, 0);
-  __syncthreads();
+  // ------------------------------------------------------------- compute
+  // The K half is a compile-time constant of each specialisation below, so
+  // every register-array index is static.
+  const int cb = w >> 1;         // 16-column slice of the V-block
+  auto compute = [&](auto kh_c) {
+    constexpr int kh = decltype(kh_c)::value;  // half of the K rows held by this wave
+    const int g4 = lane >> 4;
+    const int l16 = lane & 15;
+    const int colw = vb * BV + cb * 16;
+    const size_t sbase = ((size_t)n * H + h) * kDim * kDim;
+    // S[t]: rows perm_col(64 kh + 16 t + 4 g4 + e), column colw + l16
+    auto srow = [&](int t, int e) { return perm_col(64 * kh + 16 * t + 4 * g4 + e); };
+    f32x4 S[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[t][e] = a.s0 ? a.s0[sbase + (size_t)srow(t, e) * kDim + colw + l16] : 0.0f;
+    // transposing-read lane roles: group G = lane/16, row offset j, column quad
+    const int trG = lane >> 4, trJ = (lane >> 2) & 3, trQ = lane & 3;
+    f32x4* xmine = &sm.xch[w][0][0];
+    const f32x4* xpart = &sm.xch[w ^ 1][0][0];
+    uint16_t* ostage = sm.o[w];
 
-  for (int jc = 0; jc < si.nch; ++jc) {
-    const int b = jc & 1;
-    if (compute) {
+    // output rows 32 kh .. 32 kh + 31 of chunk jc, staged in ostage, to HBM
+    auto store_o = [&](int jc) {
+      const int tok0 = si.tok0 + jc * kChunk;
+      const int rem = si.len - jc * kChunk;
+      const int len = rem < kChunk ? rem : kChunk;
+      const int r = 32 * kh + (lane >> 1);
+      const u32x4 val = *reinterpret_cast<const u32x4*>(ostage + 8 * lane);
+      if (r < len) *reinterpret_cast<u32x4*>(a.o + ((size_t)(tok0 + r) * H + h) * kDim + colw + 8 * (lane & 1)) = val;
+    };
+
+    __syncthreads();
+
+    for (int jc = 0; jc < si.nch; ++jc) {
+      const int b = jc & 1;
       const typename SM::Buf& B = sm.buf[b];
       const int c = si.c0 + jc;
       const size_t cm = (size_t)h * a.geo.NT + c;
 
+      // output rows of chunk jc-1
+      if constexpr (COMPUTE_O) {
+        if (jc >= 1) store_o(jc - 1);
+      }
+
       if constexpr (STORE_H) {
         float* hd = a.h_out + cm * (kDim * kDim);
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) hd[(size_t)(16 * t + 4 * g4 + e) * kDim + colw + l16] = S[t][e];
+          for (int e = 0; e < 4; ++e) hd[(size_t)srow(t, e) * kDim + colw + l16] = S[t][e];
       }
 
-      // X = k S: contraction step s uses state tiles 2s, 2s+1 (split just
-      // before use); four independent accumulators per step
-      u16x8 Shi[4], Slo[4];
-      f32x4 X[4];
+      // partial X = k S and o_inter = q S_hi over this wave's K half
+      // (contraction steps 2 kh, 2 kh + 1)
+      u16x8 Shi[2], Slo[2];
+      split_tiles(S[0], S[1], Shi[0], Slo[0]);
+      split_tiles(S[2], S[3], Shi[1], Slo[1]);
+      f32x4 X[4], OI[4];
 #pragma unroll
-      for (int it = 0; it < 4; ++it) X[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-      {
-        u16x8 fk[2][4];
+      for (int it = 0; it < 4; ++it) {
+        X[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+        OI[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
-          fk[0][it] = *reinterpret_cast<const u16x8*>(B.k + (16 * it + l16) * kLdK + 8 * g4);
-        split_tiles(S[0], S[1], Shi[0], Slo[0]);
+      for (int sp = 0; sp < 2; ++sp) {
+        const int s = 2 * kh + sp;
+        const int slot = 8 * ((4 * s + g4) ^ l16);
+        u16x8 fk[4], fq[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if (s + 1 < 4) {
-#pragma unroll
-            for (int it = 0; it < 4; ++it)
-              fk[(s + 1) & 1][it] =
-                  *reinterpret_cast<const u16x8*>(B.k + (16 * it + l16) * kLdK + 32 * (s + 1) + 8 * g4);
-          }
-#pragma unroll
-          for (int it = 0; it < 4; ++it) X[it] = mfma16(fk[s & 1][it], Shi[s], X[it]);
-          if (s + 1 < 4) split_tiles(S[2 * s + 2], S[2 * s + 3], Shi[s + 1], Slo[s + 1]);
-#pragma unroll
-          for (int it = 0; it < 4; ++it) X[it] = mfma16(fk[s & 1][it], Slo[s], X[it]);
+        for (int it = 0; it < 4; ++it) {
+          fk[it] = *reinterpret_cast<const u16x8*>(B.k + (16 * it + l16) * kDim + slot);
+          if constexpr (COMPUTE_O) fq[it] = *reinterpret_cast<const u16x8*>(B.q + (16 * it + l16) * kDim + slot);
         }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) X[it] = mfma16(fk[it], Shi[sp], X[it]);
+        if constexpr (COMPUTE_O) {
+#pragma unroll
+          for (int it = 0; it < 4; ++it) OI[it] = mfma16(fq[it], Shi[sp], OI[it]);
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) X[it] = mfma16(fk[it], Slo[sp], X[it]);
       }
 
-      // first half of the output, o_inter = q S_hi (independent of v_new)
-      f32x4 O[4];
+      // post the partial sums, then add the partner's
+#pragma unroll
+      for (int it = 0; it < 4; ++it) xmine[it * 64 + lane] = X[it];
       if constexpr (COMPUTE_O) {
 #pragma unroll
-        for (int it = 0; it < 4; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-        u16x8 fq[2][4];
+        for (int i = 0; i < 2; ++i) xmine[(4 + i) * 64 + lane] = OI[2 * (1 - kh) + i];
+      }
+      __syncthreads();
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
-          fq[0][it] = *reinterpret_cast<const u16x8*>(B.q + (16 * it + l16) * kLdK + 8 * g4);
+      for (int it = 0; it < 4; ++it) X[it] += xpart[it * 64 + lane];
+      f32x4 O[2];
+      if constexpr (COMPUTE_O) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if (s + 1 < 4) {
-#pragma unroll
-            for (int it = 0; it < 4; ++it)
-              fq[(s + 1) & 1][it] =
-                  *reinterpret_cast<const u16x8*>(B.q + (16 * it + l16) * kLdK + 32 * (s + 1) + 8 * g4);
-          }
-#pragma unroll
-          for (int it = 0; it < 4; ++it) O[it] = mfma16(fq[s & 1][it], Shi[s], O[it]);
-        }
+        for (int i = 0; i < 2; ++i) O[i] = OI[2 * kh + i] + xpart[(4 + i) * 64 + lane];
       }
 
-      // Y = beta v - c X for tiles 2h, 2h+1 -> B operand of contraction step h
+      // Y = beta v - c X for tiles 2h, 2h+1 -> B operand of contraction step h.
+      // The v values of rows 16 it + 4 g4 + j, column 16 cb + l16 come from
+      // a transposing read of the v rows.
       auto make_y = [&](int hh, u16x8& yhi, u16x8& ylo) {
         f32x4 y2[2];
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
           const int it = 2 * hh + k2;
-          const u16x4 vv = *reinterpret_cast<const u16x4*>(B.vt + (16 * w + l16) * kLdVT + 16 * it + 4 * g4);
+          const u16x4 vv = tr_read(B.v + (16 * it + 4 * g4 + trJ) * BV + 16 * cb + 4 * trQ);
           const float4 bt = *reinterpret_cast<const float4*>(B.vec + 16 * it + 4 * g4);
           const float4 cc = *reinterpret_cast<const float4*>(B.vec + kChunk + 16 * it + 4 * g4);
           y2[k2][0] = bt.x * bf2f(vv[0]) - cc.x * X[it][0];
@@ -283,17 +291,20 @@ __global__ __launch_bounds__((NWC + kLoaders) * 64) void gdn_state_kernel(FwdArg
         split_tiles(y2[0], y2[1], yhi, ylo);
       };
 
-      // v_new = T Y, three split products, four independent accumulators
+      // v_new = T Y (all 64 rows), three split products, four accumulators.
+      // T is lower triangular: rows 0..31 have no terms in contraction step 1.
       f32x4 VN[4];
       {
         u16x8 th[4][2], tl[4][2];
 #pragma unroll
         for (int io = 0; io < 4; ++io) {
-          const uint16_t* row = B.t + (16 * io + l16) * kLdT2 + 8 * g4;
-          th[io][0] = *reinterpret_cast<const u16x8*>(row);
-          th[io][1] = *reinterpret_cast<const u16x8*>(row + 32);
-          tl[io][0] = *reinterpret_cast<const u16x8*>(row + kChunk);
-          tl[io][1] = *reinterpret_cast<const u16x8*>(row + kChunk + 32);
+          const uint16_t* row = B.t + (16 * io + l16) * (2 * kChunk);
+          th[io][0] = *reinterpret_cast<const u16x8*>(row + 8 * (g4 ^ l16));
+          tl[io][0] = *reinterpret_cast<const u16x8*>(row + 8 * ((8 + g4) ^ l16));
+          if (io >= 2) {
+            th[io][1] = *reinterpret_cast<const u16x8*>(row + 8 * ((4 + g4) ^ l16));
+            tl[io][1] = *reinterpret_cast<const u16x8*>(row + 8 * ((12 + g4) ^ l16));
+          }
           VN[io] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         u16x8 Yhi[2], Ylo[2];
@@ -306,21 +317,23 @@ __global__ __launch_bounds__((NWC + kLoaders) * 64) void gdn_state_kernel(FwdArg
 #pragma unroll
         for (int io = 0; io < 4; ++io) VN[io] = mfma16(tl[io][0], Yhi[0], VN[io]);
 #pragma unroll
-        for (int io = 0; io < 4; ++io) VN[io] = mfma16(th[io][1], Yhi[1], VN[io]);
+        for (int io = 2; io < 4; ++io) VN[io] = mfma16(th[io][1], Yhi[1], VN[io]);
 #pragma unroll
-        for (int io = 0; io < 4; ++io) VN[io] = mfma16(th[io][1], Ylo[1], VN[io]);
+        for (int io = 2; io < 4; ++io) VN[io] = mfma16(th[io][1], Ylo[1], VN[io]);
 #pragma unroll
-        for (int io = 0; io < 4; ++io) VN[io] = mfma16(tl[io][1], Yhi[1], VN[io]);
+        for (int io = 2; io < 4; ++io) VN[io] = mfma16(tl[io][1], Yhi[1], VN[io]);
       }
       if constexpr (STORE_H) {
         float* vd = a.vnew_out + cm * (kChunk * kDim);
 #pragma unroll
-        for (int io = 0; io < 4; ++io)
+        for (int i = 0; i < 2; ++i) {
+          const f32x4 vt = VN[2 * kh + i];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vd[(size_t)(16 * io + 4 * g4 + e) * kDim + colw + l16] = VN[io][e];
+          for (int e = 0; e < 4; ++e) vd[(size_t)(16 * (2 * kh + i) + 4 * g4 + e) * kDim + colw + l16] = vt[e];
+        }
       }
 
-      // state update: S <- exp(G_last) S + k^T (d * v_new), eight accumulators;
+      // state update of this K half: S <- exp(G_last) S + k^T (d * v_new);
       // contraction step s uses v_new tiles 2s, 2s+1
       auto make_z = [&](int hh, u16x8& zhi, u16x8& zlo) {
         f32x4 z2[2];
@@ -336,95 +349,87 @@ __global__ __launch_bounds__((NWC + kLoaders) * 64) void gdn_state_kernel(FwdArg
         split_tiles(z2[0], z2[1], zhi, zlo);
       };
       {
-        u16x8 ak[2][8];
+        // A operand of tile t: row i is K index perm_col(64 kh + 16 t + i);
+        // lane (trG, 4 trJ + trQ) reads the 4 columns starting at
+        // perm_col(64 kh + 16 t + 4 trQ) of token row 32 s + 4 trG + trJ (+16)
+        u16x8 ak[2][4];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const uint16_t* col = B.k + perm_col(16 * t + 4 * trQ);
-            const u16x4 r0 = tr_read(col + (32 * s + 4 * trG + trJ) * kLdK);
-            const u16x4 r1 = tr_read(col + (32 * s + 16 + 4 * trG + trJ) * kLdK);
-            ak[s][t] = cat4(r0, r1);
+          for (int t = 0; t < 4; ++t) {
+            const int c0 = perm_col(64 * kh + 16 * t + 4 * trQ);
+            const int r0 = 32 * s + 4 * trG + trJ, r1 = r0 + 16;
+            const u16x4 x0 = tr_read(B.k + r0 * kDim + 8 * ((c0 >> 3) ^ (r0 & 15)) + (c0 & 7));
+            const u16x4 x1 = tr_read(B.k + r1 * kDim + 8 * ((c0 >> 3) ^ (r1 & 15)) + (c0 & 7));
+            ak[s][t] = cat4(x0, x1);
           }
-        const float dec = B.dec[0];
+        const float dec = B.vec[7 * kChunk];
         u16x8 Zhi[2], Zlo[2];
         make_z(0, Zhi[0], Zlo[0]);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) S[t] = mfma16(ak[0][t], Zhi[0], S[t] * dec);
+        for (int t = 0; t < 4; ++t) S[t] = mfma16(ak[0][t], Zhi[0], S[t] * dec);
         make_z(1, Zhi[1], Zlo[1]);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) S[t] = mfma16(ak[0][t], Zlo[0], S[t]);
+        for (int t = 0; t < 4; ++t) S[t] = mfma16(ak[0][t], Zlo[0], S[t]);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) S[t] = mfma16(ak[1][t], Zhi[1], S[t]);
+        for (int t = 0; t < 4; ++t) S[t] = mfma16(ak[1][t], Zhi[1], S[t]);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) S[t] = mfma16(ak[1][t], Zlo[1], S[t]);
+        for (int t = 0; t < 4; ++t) S[t] = mfma16(ak[1][t], Zlo[1], S[t]);
       }
 
-      // second half of the output: o = r * o_inter + Aqk bf16(v_new)
+      // output rows of this wave: o = r * o_inter + Aqk bf16(v_new), staged
+      // for the store at the start of the next chunk
       if constexpr (COMPUTE_O) {
-        u16x8 VNb[2];
+        const u16x8 VNb0 = pack_tiles(VN[0], VN[1]);
+        const u16x8 VNb1 = kh == 1 ? pack_tiles(VN[2], VN[3]) : VNb0;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          u32x4 p;
-          p[0] = pack2(VN[2 * hh][0], VN[2 * hh][1]);
-          p[1] = pack2(VN[2 * hh][2], VN[2 * hh][3]);
-          p[2] = pack2(VN[2 * hh + 1][0], VN[2 * hh + 1][1]);
-          p[3] = pack2(VN[2 * hh + 1][2], VN[2 * hh + 1][3]);
-          VNb[hh] = __builtin_bit_cast(u16x8, p);
-        }
-        u16x8 fa[4][2];
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const uint16_t* arow = B.aqk + (16 * it + l16) * kLdA + 8 * g4;
-          fa[it][0] = *reinterpret_cast<const u16x8*>(arow);
-          fa[it][1] = *reinterpret_cast<const u16x8*>(arow + 32);
+        for (int i = 0; i < 2; ++i) {
+          const int it = 2 * kh + i;
+          const int r = 16 * it + l16;
           const float4 rr = *reinterpret_cast<const float4*>(B.vec + 3 * kChunk + 16 * it + 4 * g4);
-          O[it][0] *= rr.x; O[it][1] *= rr.y; O[it][2] *= rr.z; O[it][3] *= rr.w;
+          O[i][0] *= rr.x; O[i][1] *= rr.y; O[i][2] *= rr.z; O[i][3] *= rr.w;
+          O[i] = mfma16(*reinterpret_cast<const u16x8*>(B.aqk + r * kChunk + 8 * (g4 ^ (r & 7))), VNb0, O[i]);
+          if (kh == 1)  // Aqk is lower triangular
+            O[i] = mfma16(*reinterpret_cast<const u16x8*>(B.aqk + r * kChunk + 8 * ((4 + g4) ^ (r & 7))), VNb1, O[i]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ostage[(16 * i + 4 * g4 + e) * 16 + l16] = bfr(O[i][e]);
         }
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int it = 0; it < 4; ++it) O[it] = mfma16(fa[it][s], VNb[s], O[it]);
-#pragma unroll
-        for (int it = 0; it < 4; ++it)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sm.o[b][(16 * it + 4 * g4 + e) * kLdO + w * 16 + l16] = bfr(O[it][e]);
       }
-    } else {
-      if constexpr (COMPUTE_O) {
-        if (jc >= 1) store_o(jc - 1, b ^ 1);
-      }
-      if (jc + 1 < si.nch) stage(jc + 1, b ^ 1);
+      __syncthreads();
     }
-    __syncthreads();
-  }
 
-  if (compute) {
+    if constexpr (COMPUTE_O) {
+      if (si.nch >= 1) store_o(last);
+    }
     if (a.sfinal) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a.sfinal[sbase + (size_t)(16 * t + 4 * g4 + e) * kDim + colw + l16] = S[t][e];
+        for (int e = 0; e < 4; ++e) a.sfinal[sbase + (size_t)srow(t, e) * kDim + colw + l16] = S[t][e];
     }
-  } else {
-    if constexpr (COMPUTE_O) {
-      if (si.nch >= 1) store_o(si.nch - 1, (si.nch - 1) & 1);
-    }
-  }
+  };
+  if (w & 1)
+    compute(std::integral_constant<int, 1>{});
+  else
+    compute(std::integral_constant<int, 0>{});
 }
 
-constexpr int kStateComputeWaves = 2;
-
+// Column slices per workgroup: 2 (four waves) when the (sequence, head)
+// units times four V-blocks fill the chip, else 1.
 hipError_t launch_gdn_state(bool store_h, bool compute_o, const FwdArgs& a, hipStream_t stream) {
-  constexpr int NWC = kStateComputeWaves;
-  dim3 grid(a.geo.N * a.H, kDim / (16 * NWC));
-  dim3 block(64 * (NWC + kLoaders));
-  if (store_h && !compute_o)
-    hipLaunchKernelGGL((gdn_state_kernel<NWC, true, false>), grid, block, 0, stream, a);
-  else if (!store_h && compute_o)
-    hipLaunchKernelGGL((gdn_state_kernel<NWC, false, true>), grid, block, 0, stream, a);
-  else
+  const long units = (long)a.geo.N * a.H;
+  const bool narrow = units * (kDim / 32) < 256;
+  const dim3 grid1(a.geo.N * a.H, kDim / 16), grid2(a.geo.N * a.H, kDim / 32);
+  const dim3 block1(64 * (2 + kLoaders)), block2(64 * (4 + kLoaders));
+  if (store_h && !compute_o) {
+    if (narrow) hipLaunchKernelGGL((gdn_state_kernel<1, true, false>), grid1, block1, 0, stream, a);
+    else hipLaunchKernelGGL((gdn_state_kernel<2, true, false>), grid2, block2, 0, stream, a);
+  } else if (!store_h && compute_o) {
+    if (narrow) hipLaunchKernelGGL((gdn_state_kernel<1, false, true>), grid1, block1, 0, stream, a);
+    else hipLaunchKernelGGL((gdn_state_kernel<2, false, true>), grid2, block2, 0, stream, a);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

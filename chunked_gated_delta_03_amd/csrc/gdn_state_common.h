@@ -1,20 +1,11 @@
-// Helpers shared by the state kernels: LDS column permutation for MFMA A
-// operands, the transposing LDS read and packed bf16 hi/lo splits.
+// Helpers shared by the state kernels: the transposing LDS read and bf16
+// hi/lo splits of accumulator tiles.
 #pragma once
 
 #include "gdn_kernels.h"
 
 namespace gdn {
 namespace st {
-
-// An MFMA 16x16x32 contraction step s takes, in lane group g4, contraction
-// indices 32s + 4 g4 + (0..3) and 32s + 16 + 4 g4 + (0..3): the accumulator
-// rows that the B operand (state, Y or Z tiles) already holds in registers.
-// A-operand matrices store their columns permuted so these eight indices are
-// adjacent (one 16-byte LDS read):  32s + 16h + 4g + e -> 32s + 8g + 4h + e.
-__device__ __forceinline__ int perm_col(int c) {
-  return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3);
-}
 
 // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element (i % 4)
 // of the 8-byte chunks read by lanes 4j + i/4, j = 0..3 (measured on gfx950).
@@ -24,24 +15,8 @@ __device__ __forceinline__ u16x4 tr_read(const uint16_t* p) {
   return __builtin_bit_cast(u16x4, r);
 }
 
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 __device__ __forceinline__ uint16_t bfr(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
-
-__device__ __forceinline__ uint32_t pack2(float x0, float x1) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
-}
-
-// Two floats to packed bf16 hi and lo words: hi = bf16(x), lo = bf16(x - hi).
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const uint32_t hp = pack2(x0, x1);
-  const float h0 = __uint_as_float(hp << 16);
-  const float h1 = __uint_as_float(hp & 0xFFFF0000u);
-  hi = hp;
-  lo = pack2(x0 - h0, x1 - h1);
-}
 
 // B operand (8 contraction slots) from two accumulator tiles: slots 0..3 are
 // rows 4g..4g+3 of tile a, slots 4..7 the same rows of tile b.

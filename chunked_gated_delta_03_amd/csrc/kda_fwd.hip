@@ -68,7 +68,7 @@ __global__ __launch_bounds__((NWC + kLoadersK) * 64) void kda_state_kernel(FwdAr
   // thread block of the elementwise k/q/G work: rows m0..m0+3, channels d0..d0+7
   const int m0 = 4 * (ltid & 15), d0 = 8 * (ltid >> 4);
   uint32_t rkdh[4][4], rkdl[4][4], rkgh[4][4], rkgl[4][4], rqd[4][4];
-  float4 rt[1024 / NL];
+  uint4 rt[1024 / NL];
   uint4 ra[512 / NL];
   u16x4 rv[4];
   float4 rvec;
@@ -115,9 +115,9 @@ __global__ __launch_bounds__((NWC + kLoadersK) * 64) void kda_state_kernel(FwdAr
         rqd[rr][pr] = pack2(q0 * fd0, q1 * fd1);
       }
     }
-    const float* tsrc = a.tmat + cm * (kChunk * kChunk);
+    const uint16_t* tsrc = a.tmat + cm * (kChunk * 2 * kChunk);
 #pragma unroll
-    for (int p = 0; p < 1024 / NL; ++p) rt[p] = reinterpret_cast<const float4*>(tsrc)[p * NL + ltid];
+    for (int p = 0; p < 1024 / NL; ++p) rt[p] = reinterpret_cast<const uint4*>(tsrc)[p * NL + ltid];
     if constexpr (COMPUTE_O) {
       const uint16_t* asrc = a.aqk + cm * (kChunk * kChunk);
 #pragma unroll
@@ -154,24 +154,17 @@ __global__ __launch_bounds__((NWC + kLoadersK) * 64) void kda_state_kernel(FwdAr
         *reinterpret_cast<uint2*>(sm.qd + off + p1) = make_uint2(rqd[rr][2], rqd[rr][3]);
       }
     }
+    // T (hi | lo) and Aqk arrive with permuted columns: plain row copies
 #pragma unroll
     for (int p = 0; p < 1024 / NL; ++p) {
       const int idx = p * NL + ltid;
-      const int r = idx >> 4, c4 = (idx & 15) * 4;
-      uint32_t h0, h1, l0, l1;
-      split2(rt[p].x, rt[p].y, h0, l0);
-      split2(rt[p].z, rt[p].w, h1, l1);
-      *reinterpret_cast<uint2*>(sm.t + r * kLdT2 + perm_col(c4)) = make_uint2(h0, h1);
-      *reinterpret_cast<uint2*>(sm.t + r * kLdT2 + kChunk + perm_col(c4)) = make_uint2(l0, l1);
+      *reinterpret_cast<uint4*>(sm.t + (idx >> 4) * kLdT2 + 8 * (idx & 15)) = rt[p];
     }
     if constexpr (COMPUTE_O) {
 #pragma unroll
       for (int p = 0; p < 512 / NL; ++p) {
         const int idx = p * NL + ltid;
-        const int r = idx >> 3, c8 = (idx & 7) * 8;
-        const u16x8 av = __builtin_bit_cast(u16x8, ra[p]);
-        *reinterpret_cast<u16x4*>(sm.aqk + r * kLdT + perm_col(c8)) = u16x4{av[0], av[1], av[2], av[3]};
-        *reinterpret_cast<u16x4*>(sm.aqk + r * kLdT + perm_col(c8 + 4)) = u16x4{av[4], av[5], av[6], av[7]};
+        *reinterpret_cast<uint4*>(sm.aqk + (idx >> 3) * kLdT + 8 * (idx & 7)) = ra[p];
       }
     }
     if (ltid < NVB) {
@@ -438,7 +431,7 @@ __global__ __launch_bounds__(256) void kda_finalize_kernel(FinArgs a) {
   }
   for (int idx = tid; idx < 64 * 64; idx += 256) {
     const int r = idx >> 6, cc = idx & 63;
-    sAqk[r * kLdT + cc] = a.aqk[cm * 4096 + idx];
+    sAqk[r * kLdT + unperm_col(cc)] = a.aqk[cm * 4096 + idx];
   }
   for (int idx = tid; idx < kDim * kDim; idx += 256) {
     const int r = idx >> 7, cc = idx & 127;

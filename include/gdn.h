@@ -131,12 +131,17 @@ int gdn_timing_read(double* prepare_ms, double* state_ms, int64_t* calls);
  * Every intermediate is head-major with 64 rows per chunk; rows of a partial
  * chunk past the end of its document are zero.
  *
- *   tmat [H,NT,64,64] fp32  T = (I + strictLower(diag(beta) Kn Kn^T * Gamma))^-1,
+ *   tmat [H,NT,64,128] bf16 T = (I + strictLower(diag(beta) Kn Kn^T * Gamma))^-1,
  *                          the forward-substitution result plus identity
  *                          (GDN: Gamma[i,j] = exp(G_i - G_j); KDA: per channel
- *                          inside the sum), Kn the normalised keys.
+ *                          inside the sum), Kn the normalised keys. Row i
+ *                          holds hi[64] then lo[64] with hi = bf16(T_ij) and
+ *                          lo = bf16(T_ij - hi), both with permuted columns:
+ *                          column 32s + 16h + 4g + e (s, h in {0,1},
+ *                          g, e in 0..3) is stored at position
+ *                          32s + 8g + 4h + e.
  *   aqk  [H,NT,64,64] bf16 scale * (Qn Kn^T * Gamma), lower triangle with the
- *                          diagonal, zero above.
+ *                          diagonal, zero above; columns permuted as tmat's.
  *   vec  [H,NT,8,64]  fp32 per-row vectors of the chunk, row r:
  *                          0 beta (after the sigmoid when flagged)
  *                          1 GDN: beta*rk*exp(G)      KDA: beta*rk
@@ -154,9 +159,9 @@ int gdn_timing_read(double* prepare_ms, double* state_ms, int64_t* calls);
 int gdn_stage_prepare(int32_t kda, const void* q, const void* k, const float* g, const void* beta,
                       const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
                       int32_t K, int32_t V, float scale, uint32_t flags,
-                      float* tmat, void* aqk, float* vec, float* gk, void* stream);
+                      void* tmat, void* aqk, float* vec, float* gk, void* stream);
 
-int gdn_stage_fwd_h(int32_t kda, const void* k, const void* v, const float* tmat, const float* vec,
+int gdn_stage_fwd_h(int32_t kda, const void* k, const void* v, const void* tmat, const float* vec,
                     const float* gk, const float* initial_state, const int32_t* cu_seqlens,
                     int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
                     uint32_t flags, float* h, float* v_new, float* final_state, void* stream);

@@ -48,3 +48,26 @@ def hm_chunks(arr_list, dense: bool):
         B, H, NC = a.shape[:3]
         parts.append(np.moveaxis(a, 1, 0).reshape(H, B * NC, *a.shape[3:]))
     return np.concatenate(parts, axis=1)
+
+
+# Column order of the stage outputs tmat and aqk: column 32s + 16h + 4g + e is
+# stored at position 32s + 8g + 4h + e (the layout the stage entry documents).
+_POS = np.arange(64)
+_COL_AT_POS = (_POS & ~31) | ((_POS & 4) << 2) | ((_POS & 24) >> 1) | (_POS & 3)
+
+
+def unpermute_cols(x):
+    out = np.empty_like(x)
+    out[..., _COL_AT_POS] = x
+    return out
+
+
+def decode_tmat(tmat):
+    """Stage tmat (bf16 [H,NT,64,128], hi | lo, permuted) -> fp64 T [H,NT,64,64]."""
+    t = tmat.float().cpu().numpy().astype(np.float64)
+    return unpermute_cols(t[..., :64]) + unpermute_cols(t[..., 64:])
+
+
+def decode_aqk(aqk):
+    """Stage aqk (bf16 [H,NT,64,64], permuted columns) -> fp64 [H,NT,64,64]."""
+    return unpermute_cols(aqk.float().cpu().numpy().astype(np.float64))

@@ -117,3 +117,17 @@ def test_python_wrapper_checks_shapes(gdn):
     q = torch.zeros((1, 8, 2, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         gdn.gdn_chunk_fwd(q, q, q, torch.zeros((1, 8, 2)), torch.zeros((1, 8, 2), dtype=torch.bfloat16))
+
+
+def test_stage_column_order_decoder():
+    """The test-side decoder of the stage outputs' column order follows the
+    documented mapping 32s+16h+4g+e -> 32s+8g+4h+e and is a permutation."""
+    import numpy as np
+    from gpu_util import unpermute_cols
+    stored = np.zeros(64)
+    for s in range(2):
+        for h in range(2):
+            for g in range(4):
+                for e in range(4):
+                    stored[32 * s + 8 * g + 4 * h + e] = 32 * s + 16 * h + 4 * g + e
+    np.testing.assert_array_equal(unpermute_cols(stored), np.arange(64))

@@ -13,7 +13,7 @@ import pytest
 
 import gdn_inputs as gi
 import oracle
-from gpu_util import O_ATOL, S_RTOL, hm_chunks, o_err, run_gpu, s_err, to_device
+from gpu_util import O_ATOL, S_RTOL, decode_aqk, decode_tmat, hm_chunks, o_err, run_gpu, s_err, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +48,9 @@ def _problems_reduced():
         ("long_T2048_H2", gi.make_inputs("long", T=2048, H=2)),
         ("mild_gate_init", gi.random_problem(rng, 2, 250, 2, 128, 128, gate_scale=0.01, with_initial_state=True)),
         ("host_normalised_B2_T300_H3", gi.make_inputs("tiny", B=2, T=300, H=3)),
+        # 64+ (sequence, head) units: the state kernel's four-compute-wave form
+        ("wide_B4_T200_H16", gi.make_inputs("gdn", B=4, T=200, H=16)),
+        ("wide_varlen_H16", gi.make_inputs("varlen", H=16, doc_lengths=[1, 64, 65, 130, 7])),
     ]
     return out
 
@@ -87,9 +90,9 @@ def test_stage_parity(gdn):
         b_ref = hm_chunks([it["beta"] for it in inters], dense)
         rq_ref = hm_chunks([it["rq"] for it in inters], dense)
         rk_ref = hm_chunks([it["rk"] for it in inters], dense)
-        tm = tmat.cpu().numpy().astype(np.float64)
+        tm = decode_tmat(tmat)
         assert np.abs(tm - T_ref).max() <= 1e-4 * max(1.0, np.abs(T_ref).max())
-        aq = aqk.float().cpu().numpy().astype(np.float64)
+        aq = decode_aqk(aqk)
         assert np.abs(aq - A_ref).max() <= 1e-2 * max(1e-3, np.abs(A_ref).max())
         vc = vec.cpu().numpy().astype(np.float64)
         np.testing.assert_allclose(vc[:, :, 4], G_ref, rtol=1e-5, atol=1e-4)
@@ -210,9 +213,9 @@ def test_kda_stage_parity(gdn):
         T_ref = hm_chunks([it["T"] for it in inters], dense)
         A_ref = hm_chunks([it["Aqk"] for it in inters], dense)
         G_ref = hm_chunks([it["G"] for it in inters], dense)
-        tm = tmat.cpu().numpy().astype(np.float64)
+        tm = decode_tmat(tmat)
         et = np.abs(tm - T_ref).max() / max(1.0, np.abs(T_ref).max())
-        aq = aqk.float().cpu().numpy().astype(np.float64)
+        aq = decode_aqk(aqk)
         ea = np.abs(aq - A_ref).max() / max(1e-3, np.abs(A_ref).max())
         gg = gk.cpu().numpy().astype(np.float64)
         eg = np.abs(gg - G_ref).max() / max(1.0, np.abs(G_ref).max())
