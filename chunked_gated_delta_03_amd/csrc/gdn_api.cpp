@@ -92,25 +92,31 @@ int check_shape(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t n
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Device must be gfx950; result cached per device id.
-int check_device() {
+// Device must be gfx950; result and compute-unit count cached per device id.
+int check_device(int* cus) {
   static std::mutex mu;
   static std::vector<int> state;  // 0 unknown, 1 ok, 2 bad
+  static std::vector<int> ncu;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   std::lock_guard<std::mutex> lock(mu);
-  if ((int)state.size() <= dev) state.resize(dev + 1, 0);
+  if ((int)state.size() <= dev) {
+    state.resize(dev + 1, 0);
+    ncu.resize(dev + 1, 0);
+  }
   if (state[dev] == 0) {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
     state[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    ncu[dev] = prop.multiProcessorCount;
     if (state[dev] == 2)
       return fail(GDN_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev,
                   prop.gcnArchName);
   }
   if (state[dev] == 2) return fail(GDN_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  if (cus) *cus = ncu[dev];
   return GDN_OK;
 }
 
@@ -313,7 +319,8 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
   if (!aligned16(o)) return fail(GDN_ERR_INVALID_ARGUMENT, "o must be 16-byte aligned");
   if ((flags & GDN_OUTPUT_FINAL_STATE) && !final_state)
     return fail(GDN_ERR_INVALID_ARGUMENT, "GDN_OUTPUT_FINAL_STATE set but final_state is NULL");
-  rc = check_device();
+  int cus = 0;
+  rc = check_device(&cus);
   if (rc) return rc;
 
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
@@ -341,6 +348,7 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
   pa.H = H;
   pa.scale = scale;
   pa.flags = flags;
+  pa.cus = cus;
   hipError_t e = gdn::launch_prepare(kda, pa, stream);
   if (e != hipSuccess) return hip_fail(e, "prepare launch");
   if (g_timing && (rc = timing_mark(g_timing_recs, 1, stream))) return rc;
@@ -369,6 +377,7 @@ struct StageCtx {
   Problem p;
   Workspace W;
   gdn::Geometry geo;
+  int cus = 0;
 };
 
 int stage_begin(int32_t kda, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
@@ -377,7 +386,7 @@ int stage_begin(int32_t kda, const int32_t* cu_seqlens, int32_t num_seqs, int32_
   ctx.p.kda = kda != 0;
   int rc = check_shape(B, T, H, K, V, num_seqs, cu_seqlens, ctx.p);
   if (rc) return rc;
-  rc = check_device();
+  rc = check_device(&ctx.cus);
   if (rc) return rc;
   const Layout L = layout_for(ctx.p, false);
   rc = acquire_workspace(nullptr, 0, L.total, stream, ctx.W);
@@ -497,6 +506,7 @@ int gdn_stage_prepare(int32_t kda, const void* q, const void* k, const float* g,
   pa.vec = vec;
   pa.gk = gk;
   pa.geo = ctx.geo;
+  pa.cus = ctx.cus;
   pa.H = H;
   pa.scale = scale;
   pa.flags = flags;

@@ -105,11 +105,14 @@ struct Geometry {
   int NT;            // total chunks
   int N;             // sequences
 
+  // The tables are read-only for a kernel's lifetime: they are read through
+  // the constant address space (scalar loads when the index is uniform, which
+  // do not count against the vector-memory counter).
   __device__ __forceinline__ ChunkInfo chunk(int c) const {
     ChunkInfo ci;
     if (ctab) {
-      int4 e = ctab[c];
-      ci.tok0 = e.x; ci.len = e.y; ci.seq = e.z; ci.j = e.w;
+      const __attribute__((address_space(4))) int* e = (const __attribute__((address_space(4))) int*)ctab + 4 * c;
+      ci.tok0 = e[0]; ci.len = e[1]; ci.seq = e[2]; ci.j = e[3];
     } else {
       int n = c / ncb, j = c - n * ncb;
       ci.seq = n; ci.j = j;
@@ -122,8 +125,8 @@ struct Geometry {
   __device__ __forceinline__ SeqInfo seq(int n) const {
     SeqInfo si;
     if (stab) {
-      int4 e = stab[n];
-      si.tok0 = e.x; si.len = e.y; si.c0 = e.z; si.nch = e.w;
+      const __attribute__((address_space(4))) int* e = (const __attribute__((address_space(4))) int*)stab + 4 * n;
+      si.tok0 = e[0]; si.len = e[1]; si.c0 = e[2]; si.nch = e[3];
     } else {
       si.tok0 = n * T; si.len = T; si.c0 = n * ncb; si.nch = ncb;
     }

@@ -21,6 +21,7 @@ struct PrepareArgs {
   int H;
   float scale;
   uint32_t flags;
+  int cus;         // compute units of the device (grid size of persistent launches)
 };
 
 struct FwdArgs {

@@ -54,33 +54,37 @@ __device__ __forceinline__ float sumsq8(const uint4& v) {
   return s;
 }
 
-// q, k rows of the chunk into LDS (zero past the end), normalisation factors.
-// All global loads are issued before the first LDS write.
-__device__ __forceinline__ void load_qk_norms(const PrepareArgs& a, const ChunkInfo& ci, int h, int tid,
-                                              uint16_t* sk, uint16_t* sq, float* sRk, float* sRq) {
-  const bool l2 = (a.flags & 1u) != 0;
-  uint4 kv[4], qv[4];
+// The q, k rows of one (chunk, head) in registers, zero past the end.
+struct QKRegs {
+  u32x4 k[4], q[4];
+};
+
+__device__ __forceinline__ void fetch_qk(const PrepareArgs& a, const ChunkInfo& ci, int h, int tid, QKRegs& x) {
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int idx = pass * 256 + tid;
     const int r = idx >> 4;
     const int cc = (idx & 15) * 8;
-    kv[pass] = make_uint4(0, 0, 0, 0);
-    qv[pass] = make_uint4(0, 0, 0, 0);
-    if (r < ci.len) {
-      const size_t off = ((size_t)(ci.tok0 + r) * a.H + h) * kDim + cc;
-      kv[pass] = *reinterpret_cast<const uint4*>(a.k + off);
-      qv[pass] = *reinterpret_cast<const uint4*>(a.q + off);
-    }
+    const size_t off = ((size_t)(ci.tok0 + r) * a.H + h) * kDim + cc;
+    x.k[pass] = r < ci.len ? *reinterpret_cast<const u32x4*>(a.k + off) : u32x4{0, 0, 0, 0};
+    x.q[pass] = r < ci.len ? *reinterpret_cast<const u32x4*>(a.q + off) : u32x4{0, 0, 0, 0};
   }
+}
+
+// q, k rows into LDS and their normalisation factors.
+__device__ __forceinline__ void put_qk_norms(const PrepareArgs& a, const ChunkInfo& ci, int tid, const QKRegs& x,
+                                             uint16_t* sk, uint16_t* sq, float* sRk, float* sRq) {
+  const bool l2 = (a.flags & 1u) != 0;
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int idx = pass * 256 + tid;
     const int r = idx >> 4;
     const int cc = (idx & 15) * 8;
-    *reinterpret_cast<uint4*>(sk + r * kLdRow + cc) = kv[pass];
-    *reinterpret_cast<uint4*>(sq + r * kLdRow + cc) = qv[pass];
-    float ssk = sumsq8(kv[pass]), ssq = sumsq8(qv[pass]);
+    const uint4 kv = __builtin_bit_cast(uint4, x.k[pass]);
+    const uint4 qv = __builtin_bit_cast(uint4, x.q[pass]);
+    *reinterpret_cast<uint4*>(sk + r * kLdRow + cc) = kv;
+    *reinterpret_cast<uint4*>(sq + r * kLdRow + cc) = qv;
+    float ssk = sumsq8(kv), ssq = sumsq8(qv);
 #pragma unroll
     for (int m = 8; m >= 1; m >>= 1) {
       ssk += __shfl_xor(ssk, m);
@@ -92,6 +96,15 @@ __device__ __forceinline__ void load_qk_norms(const PrepareArgs& a, const ChunkI
       sRq[r] = valid ? (l2 ? 1.0f / sqrtf(ssq + 1e-6f) : 1.0f) : 0.0f;
     }
   }
+}
+
+// q, k rows of the chunk into LDS (zero past the end), normalisation factors.
+// All global loads are issued before the first LDS write.
+__device__ __forceinline__ void load_qk_norms(const PrepareArgs& a, const ChunkInfo& ci, int h, int tid,
+                                              uint16_t* sk, uint16_t* sq, float* sRk, float* sRq) {
+  QKRegs x;
+  fetch_qk(a, ci, h, tid, x);
+  put_qk_norms(a, ci, tid, x, sk, sq, sRk, sRq);
 }
 
 // beta (with the optional sigmoid) by wave 0; zero past the end.
@@ -189,15 +202,17 @@ __device__ __forceinline__ void store_t_aqk(const PrepareArgs& a, size_t cm, int
 // ===========================================================================
 // GDN: scalar natural-log gate per (token, head)
 // ===========================================================================
-__global__ __launch_bounds__(256) void gdn_prepare_kernel(PrepareArgs a) {
-  const int c = blockIdx.x;
-  const int h = blockIdx.y;
+// One workgroup per compute-unit slot, looping over the (chunk, head) items
+// (chunk-major, so neighbouring workgroups read neighbouring rows); the q, k,
+// g and beta of the next item are loaded into registers while the current
+// one is computed.
+__global__ __launch_bounds__(256, 3) void gdn_prepare_kernel(PrepareArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
-  const ChunkInfo ci = a.geo.chunk(c);
+  const int n_items = a.geo.NT * a.H;
 
   // q, k rows live only until the Gram tiles are in registers; A, T and Aqk
   // reuse their space afterwards.
@@ -214,98 +229,125 @@ __global__ __launch_bounds__(256) void gdn_prepare_kernel(PrepareArgs a) {
   } u;
   __shared__ __attribute__((aligned(16))) float sG[kChunk], sBeta[kChunk], sRq[kChunk], sRk[kChunk];
 
-  float gx = 0.0f;
-  if (wave == 0 && lane < ci.len) gx = a.g[(size_t)(ci.tok0 + lane) * a.H + h];
-  load_qk_norms(a, ci, h, tid, u.in.k, u.in.q, sRk, sRq);
-  if (wave == 0) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float y = __shfl_up(gx, o);
-      if (lane >= o) gx += y;
+  // registers of the next item: q, k rows (all threads), raw g and beta
+  // (wave 0; masked when they are written to LDS, so nothing waits on them)
+  QKRegs nx;
+  float ngx = 0.0f;
+  uint16_t nbx = 0;
+  auto fetch = [&](int it) {
+    const int c = it / a.H, h = it - (it / a.H) * a.H;
+    const ChunkInfo ci = a.geo.chunk(c);
+    fetch_qk(a, ci, h, tid, nx);
+    if (wave == 0) {
+      const size_t off = (size_t)(ci.tok0 + (lane < ci.len ? lane : 0)) * a.H + h;
+      ngx = a.g[off];
+      nbx = a.beta[off];
     }
-    sG[lane] = gx;
-    load_beta(a, ci, h, lane, sBeta);
-  }
-  __syncthreads();
+  };
+  if ((int)blockIdx.x < n_items) fetch(blockIdx.x);
 
-  // Gram tiles on MFMA: k k^T (strictly lower) by waves 0-1, q k^T (lower) by
-  // waves 2-3; each wave takes 5 of the 10 lower 16x16 tiles.
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int kind = wv >> 1;
-  const uint16_t* left = kind == 0 ? u.in.k : u.in.q;
-  f32x4 acc[5];
+  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int c = it / a.H;
+    const int h = it - c * a.H;
+    const ChunkInfo ci = a.geo.chunk(c);
+
+    put_qk_norms(a, ci, tid, nx, u.in.k, u.in.q, sRk, sRq);
+    if (wave == 0) {
+      const bool valid = lane < ci.len;
+      float gx = valid ? ngx : 0.0f;
 #pragma unroll
-  for (int jj = 0; jj < 5; ++jj) {
-    const int t = (wv & 1) + 2 * jj;
-    const int I = kTileI[t], J = kTileJ[t];
-    u16x8 av[4], bv[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      av[s] = *reinterpret_cast<const u16x8*>(left + (16 * I + l16) * kLdRow + 32 * s + 8 * g4);
-      bv[s] = *reinterpret_cast<const u16x8*>(u.in.k + (16 * J + l16) * kLdRow + 32 * s + 8 * g4);
+      for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(gx, o);
+        if (lane >= o) gx += y;
+      }
+      sG[lane] = gx;
+      const float b = valid ? bf2f(nbx) : 0.0f;
+      sBeta[lane] = ((a.flags & 2u) && valid) ? 1.0f / (1.0f + expf(-b)) : b;
     }
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) x = mfma16(av[s], bv[s], x);
-    acc[jj] = x;
-  }
-  __syncthreads();
-  // scale into A (fp32) or Aqk (bf16); the causal mask is applied to the
-  // exponent before the exponential (masked entries use a large negative one)
-  {
-    const float* rrow = kind == 0 ? sRk : sRq;
-    const float sgn = kind == 0 ? -1.0f : a.scale;
+    // the next item's loads (the last item's again past the end, harmlessly)
+    fetch(min(it + (int)gridDim.x, n_items - 1));
+    __syncthreads();
+
+    // Gram tiles on MFMA: k k^T (strictly lower) by waves 0-1, q k^T (lower) by
+    // waves 2-3; each wave takes 5 of the 10 lower 16x16 tiles.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int kind = wv >> 1;
+    const uint16_t* left = kind == 0 ? u.in.k : u.in.q;
+    f32x4 acc[5];
 #pragma unroll
     for (int jj = 0; jj < 5; ++jj) {
       const int t = (wv & 1) + 2 * jj;
       const int I = kTileI[t], J = kTileJ[t];
-      const int jc = 16 * J + l16;
-      const int i0 = 16 * I + 4 * g4;
-      const float4 gi = *reinterpret_cast<const float4*>(sG + i0);
-      const float4 ri = *reinterpret_cast<const float4*>(rrow + i0);
-      const float4 bi = kind == 0 ? *reinterpret_cast<const float4*>(sBeta + i0) : make_float4(1.f, 1.f, 1.f, 1.f);
-      const float gj = sG[jc], rj = sRk[jc] * sgn;
-      const float gia[4] = {gi.x, gi.y, gi.z, gi.w};
-      const float ria[4] = {ri.x, ri.y, ri.z, ri.w};
-      const float bia[4] = {bi.x, bi.y, bi.z, bi.w};
-      float val[4];
+      u16x8 av[4], bv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float m = (i0 + e + kind > jc) ? 1.0f : 0.0f;  // i > j (k k^T) or i >= j (q k^T)
-        const float ex = __expf((gia[e] - gj) * m);
-        val[e] = m * bia[e] * ria[e] * rj * acc[jj][e] * ex;
+      for (int s = 0; s < 4; ++s) {
+        av[s] = *reinterpret_cast<const u16x8*>(left + (16 * I + l16) * kLdRow + 32 * s + 8 * g4);
+        bv[s] = *reinterpret_cast<const u16x8*>(u.in.k + (16 * J + l16) * kLdRow + 32 * s + 8 * g4);
       }
-      if (kind == 0) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) u.mat.A[(i0 + e) * kLdF + jc] = val[e];
-      } else {
+      for (int s = 0; s < 4; ++s) x = mfma16(av[s], bv[s], x);
+      acc[jj] = x;
+    }
+    __syncthreads();
+    // scale into A (fp32) or Aqk (bf16); the causal mask is applied to the
+    // exponent before the exponential (masked entries use a large negative one)
+    {
+      const float* rrow = kind == 0 ? sRk : sRq;
+      const float sgn = kind == 0 ? -1.0f : a.scale;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) u.mat.aqk[(i0 + e) * kLdQ + jc] = __builtin_bit_cast(uint16_t, (__bf16)val[e]);
+      for (int jj = 0; jj < 5; ++jj) {
+        const int t = (wv & 1) + 2 * jj;
+        const int I = kTileI[t], J = kTileJ[t];
+        const int jc = 16 * J + l16;
+        const int i0 = 16 * I + 4 * g4;
+        const float4 gi = *reinterpret_cast<const float4*>(sG + i0);
+        const float4 ri = *reinterpret_cast<const float4*>(rrow + i0);
+        const float4 bi = kind == 0 ? *reinterpret_cast<const float4*>(sBeta + i0) : make_float4(1.f, 1.f, 1.f, 1.f);
+        const float gj = sG[jc], rj = sRk[jc] * sgn;
+        const float gia[4] = {gi.x, gi.y, gi.z, gi.w};
+        const float ria[4] = {ri.x, ri.y, ri.z, ri.w};
+        const float bia[4] = {bi.x, bi.y, bi.z, bi.w};
+        float val[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float m = (i0 + e + kind > jc) ? 1.0f : 0.0f;  // i > j (k k^T) or i >= j (q k^T)
+          const float ex = __expf((gia[e] - gj) * m);
+          val[e] = m * bia[e] * ria[e] * rj * acc[jj][e] * ex;
+        }
+        if (kind == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) u.mat.A[(i0 + e) * kLdF + jc] = val[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) u.mat.aqk[(i0 + e) * kLdQ + jc] = __builtin_bit_cast(uint16_t, (__bf16)val[e]);
+        }
       }
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  invert_unit_lower(u.mat.A, u.mat.T, wave, lane);
+    invert_unit_lower(u.mat.A, u.mat.T, wave, lane);
 
-  const size_t cm = (size_t)h * a.geo.NT + c;
-  store_t_aqk(a, cm, tid, u.mat.T, u.mat.aqk);
-  if (tid < 64) {
-    const int i = tid;
-    const bool valid = i < ci.len;
-    const float G = sG[i];
-    const float Glast = sG[63];
-    const float b = valid ? sBeta[i] : 0.f;
-    const float rk = sRk[i], rq = sRq[i];
-    float* vd = a.vec + cm * (kVecRows * kChunk);
-    vd[0 * 64 + i] = b;
-    vd[1 * 64 + i] = valid ? b * rk * expf(G) : 0.f;
-    vd[2 * 64 + i] = valid ? rk * expf(Glast - G) : 0.f;
-    vd[3 * 64 + i] = valid ? a.scale * rq * expf(G) : 0.f;
-    vd[4 * 64 + i] = G;
-    vd[5 * 64 + i] = rq;
-    vd[6 * 64 + i] = rk;
-    vd[7 * 64 + i] = (i == 0) ? expf(Glast) : 0.f;
+    const size_t cm = (size_t)h * a.geo.NT + c;
+    store_t_aqk(a, cm, tid, u.mat.T, u.mat.aqk);
+    if (tid < 64) {
+      const int i = tid;
+      const bool valid = i < ci.len;
+      const float G = sG[i];
+      const float Glast = sG[63];
+      const float b = valid ? sBeta[i] : 0.f;
+      const float rk = sRk[i], rq = sRq[i];
+      float* vd = a.vec + cm * (kVecRows * kChunk);
+      vd[0 * 64 + i] = b;
+      vd[1 * 64 + i] = valid ? b * rk * expf(G) : 0.f;
+      vd[2 * 64 + i] = valid ? rk * expf(Glast - G) : 0.f;
+      vd[3 * 64 + i] = valid ? a.scale * rq * expf(G) : 0.f;
+      vd[4 * 64 + i] = G;
+      vd[5 * 64 + i] = rq;
+      vd[6 * 64 + i] = rk;
+      vd[7 * 64 + i] = (i == 0) ? expf(Glast) : 0.f;
+    }
+    __syncthreads();  // LDS is rewritten by the next item
   }
 }
 
@@ -519,11 +561,14 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
 }
 
 hipError_t launch_prepare(bool kda, const PrepareArgs& a, hipStream_t stream) {
-  dim3 grid(a.geo.NT, a.H);
-  if (kda)
-    hipLaunchKernelGGL(kda_prepare_kernel, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(gdn_prepare_kernel, grid, dim3(256), 0, stream, a);
+  if (kda) {
+    hipLaunchKernelGGL(kda_prepare_kernel, dim3(a.geo.NT, a.H), dim3(256), 0, stream, a);
+  } else {
+    // three workgroups fit a compute unit (43.5 KiB of LDS each)
+    const long items = (long)a.geo.NT * a.H;
+    const long slots = 3L * (a.cus > 0 ? a.cus : 256);
+    hipLaunchKernelGGL(gdn_prepare_kernel, dim3((unsigned)(items < slots ? items : slots)), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
