@@ -50,7 +50,7 @@ STATE_BYTES_PER_UNIT = 128 * 128 * 4  # one fp32 state per (sequence, head), eac
 ALG_FLOPS_PER_TH = 140629             # conservative (triangle-exploiting) count
 
 
-KERNEL_SOURCES = ("gdn_common.h", "gdn_kernels.h", "gdn_prepare.hip", "gdn_fwd.hip", "gdn_state.hip", "gdn_state_common.h", "kda_fwd.hip")
+KERNEL_SOURCES = ("gdn_common.h", "gdn_kernels.h", "gdn_prepare.hip", "gdn_fwd.hip", "gdn_state.hip", "gdn_state_common.h", "kda_fwd.hip", "kda_state.hip")
 
 
 def kernel_source_hash() -> str:

@@ -181,6 +181,8 @@ def _kda_problems():
                                             with_initial_state=True)),
         ("kda_packed", gi.random_problem(rng, 1, 317, 2, 128, 128, kda=True, with_initial_state=True,
                                          cu_seqlens=[0, 1, 18, 82, 147, 317])),
+        # 64+ (sequence, head) units: the four-compute-wave form of the state kernel
+        ("kda_wide_B2_T130_H32", gi.make_inputs("kda", B=2, T=130, H=32)),
     ]
 
 
