@@ -40,6 +40,11 @@ constexpr int kLdG = kDim + 4;      // fp32 row stride of the 64 x 128 KDA gate
 // the 10 lower 16x16 tiles (I >= J) of a 64 x 64 matrix
 __constant__ int kTileI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
 __constant__ int kTileJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+// the 6 tiles below the diagonal (I > J), and the 6 pairs i > j of a 4 x 4 block
+__constant__ int kOffI[6] = {1, 2, 2, 3, 3, 3};
+__constant__ int kOffJ[6] = {0, 0, 1, 0, 1, 2};
+__constant__ int kInI[6] = {1, 2, 2, 3, 3, 3};
+__constant__ int kInJ[6] = {0, 0, 1, 0, 1, 2};
 
 __device__ __forceinline__ float sumsq8(const uint4& v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -378,63 +383,86 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
     } mat;
   } u;
   __shared__ float sBeta[kChunk], sRq[kChunk], sRk[kChunk];
+  __shared__ __attribute__((aligned(16))) float sSeg[8 * kDim];  // gate segment totals
   uint16_t* sk = u.in.k;
   uint16_t* sq = u.in.q;
   float* sG = u.in.G;
 
-  load_qk_norms(a, ci, h, tid, sk, sq, sRk, sRq);
-  if (wave == 0) load_beta(a, ci, h, lane, sBeta);
+  // all global loads (q, k rows, the gate block, beta) in flight together;
+  // thread (channel quad cq, segment sg) holds rows 8 sg .. 8 sg + 7 of
+  // channels 4 cq .. 4 cq + 3 of the gate
+  const int cq = tid & 31, sg = tid >> 5;
+  float4 gv[8];
+  {
+    QKRegs x;
+    fetch_qk(a, ci, h, tid, x);
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const int r = 8 * sg + rr;
+      gv[rr] = r < ci.len ? *reinterpret_cast<const float4*>(a.g + ((size_t)(ci.tok0 + r) * a.H + h) * kDim + 4 * cq)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (wave == 0) load_beta(a, ci, h, lane, sBeta);
+    put_qk_norms(a, ci, tid, x, sk, sq, sRk, sRq);
+  }
 
-  // per-channel cumulative gate: the 64 x 128 block is loaded with all its
-  // vector loads in flight, then thread (d, half) scans 32 rows in LDS
+  // per-channel cumulative gate: each thread scans its 8 rows in registers;
+  // the segment totals go through LDS
   {
-    float4 gv[8];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int idx = p * 256 + tid;
-      const int r = idx >> 5, c4 = (idx & 31) * 4;
-      gv[p] = r < ci.len ? *reinterpret_cast<const float4*>(a.g + ((size_t)(ci.tok0 + r) * a.H + h) * kDim + c4)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int rr = 1; rr < 8; ++rr) {
+      gv[rr].x += gv[rr - 1].x; gv[rr].y += gv[rr - 1].y; gv[rr].z += gv[rr - 1].z; gv[rr].w += gv[rr - 1].w;
     }
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int idx = p * 256 + tid;
-      const int r = idx >> 5, c4 = (idx & 31) * 4;
-      *reinterpret_cast<float4*>(sG + r * kLdG + c4) = gv[p];
+    reinterpret_cast<float4*>(sSeg)[sg * 32 + cq] = gv[7];
+    __syncthreads();
+    float4 base = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s2 = 0; s2 < sg; ++s2) {
+      const float4 t = reinterpret_cast<const float4*>(sSeg)[s2 * 32 + cq];
+      base.x += t.x; base.y += t.y; base.z += t.z; base.w += t.w;
     }
-  }
-  __syncthreads();
-  {
-    const int d = tid & 127;
-    const int half = tid >> 7;
-    float run = 0.0f;
-    for (int r = 32 * half; r < 32 * half + 32; ++r) {
-      run += sG[r * kLdG + d];
-      sG[r * kLdG + d] = run;
-    }
-  }
-  __syncthreads();
-  {
-    const int d = tid & 127;
-    const int half = tid >> 7;
-    if (half == 1) {
-      const float base = sG[31 * kLdG + d];
-      for (int r = 32; r < 64; ++r) sG[r * kLdG + d] += base;
-    }
-  }
-  __syncthreads();
-  {
     float* gdst = a.gk + cm * (kChunk * kDim);
-    for (int idx = tid; idx < kChunk * kDim / 4; idx += 256) {
-      const int r = idx >> 5, c4 = (idx & 31) * 4;
-      *reinterpret_cast<float4*>(gdst + r * kDim + c4) =
-          make_float4(sG[r * kLdG + c4], sG[r * kLdG + c4 + 1], sG[r * kLdG + c4 + 2], sG[r * kLdG + c4 + 3]);
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const int r = 8 * sg + rr;
+      const float4 G = make_float4(gv[rr].x + base.x, gv[rr].y + base.y, gv[rr].z + base.z, gv[rr].w + base.w);
+      *reinterpret_cast<float4*>(sG + r * kLdG + 4 * cq) = G;
+      *reinterpret_cast<float4*>(gdst + r * kDim + 4 * cq) = G;
     }
   }
+  __syncthreads();
 
-  // off-diagonal tiles I > J on MFMA, rows scaled against r = 16 I; the
-  // k k^T product carries hi + lo operands (it feeds the inverse), the
-  // q k^T product single bf16 operands. Wave w: jobs w and w + 4.
+  // Gram tiles. Lane (l16, g4) of an MFMA step s covers channels
+  // 32 s + 8 g4 .. + 7 of operand row/column l16. Products of rows scaled
+  // against a reference row r with j < r <= i have both exponents <= 0.
+  auto g8 = [&](int row, int d0, float (&x)[8]) {
+    const float4 x0 = *reinterpret_cast<const float4*>(sG + row * kLdG + d0);
+    const float4 x1 = *reinterpret_cast<const float4*>(sG + row * kLdG + d0 + 4);
+    x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+  };
+  auto scale_split = [&](const u16x8& v, const float (&f)[8], u16x8& hi, u16x8& lo) {
+    u32x4 hh, ll;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t x, y;
+      split2(bf2f(v[2 * p]) * f[2 * p], bf2f(v[2 * p + 1]) * f[2 * p + 1], x, y);
+      hh[p] = x;
+      ll[p] = y;
+    }
+    hi = __builtin_bit_cast(u16x8, hh);
+    lo = __builtin_bit_cast(u16x8, ll);
+  };
+  auto scale_pack = [&](const u16x8& v, const float (&f)[8]) {
+    u32x4 pp;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) pp[p] = pack2(bf2f(v[2 * p]) * f[2 * p], bf2f(v[2 * p + 1]) * f[2 * p + 1]);
+    return __builtin_bit_cast(u16x8, pp);
+  };
+  auto row8 = [&](const uint16_t* base, int row, int d0) {
+    return *reinterpret_cast<const u16x8*>(base + row * kLdRow + d0);
+  };
+
+  // off-diagonal tiles I > J (reference r = 16 I; k k^T with hi + lo
+  // operands, q k^T with single bf16 operands). Wave w: jobs w and w + 4.
   f32x4 accA[2], accQ[2];
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj) {
@@ -442,79 +470,109 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
     accA[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     accQ[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (job >= 6) continue;
-    int t = job, I = 1;
-    while (t >= I) { t -= I; ++I; }
-    const int J = t;
-    const int r = 16 * I;
-    const int i = 16 * I + l16;   // A-operand row
-    const int j = 16 * J + l16;   // B-operand row (column of the product)
+    const int I = kOffI[job], J = kOffJ[job];
+    const int i = 16 * I + l16, j = 16 * J + l16, r = 16 * I;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u16x8 lk_hi, lk_lo, lq, rr_hi, rr_lo;
+      const int d0 = 32 * s + 8 * g4;
+      float gi[8], gr[8], gj[8], fi[8], fj[8];
+      g8(i, d0, gi);
+      g8(r, d0, gr);
+      g8(j, d0, gj);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int d = 32 * s + 8 * g4 + e;
-        const float gr = sG[r * kLdG + d];
-        const float fi = exp2f(sG[i * kLdG + d] - gr);
-        const float fj = exp2f(gr - sG[j * kLdG + d]);
-        uint16_t hh, ll;
-        split_bf(bf2f(sk[i * kLdRow + d]) * fi, hh, ll);
-        lk_hi[e] = hh; lk_lo[e] = ll;
-        lq[e] = f2bf(bf2f(sq[i * kLdRow + d]) * fi);
-        split_bf(bf2f(sk[j * kLdRow + d]) * fj, hh, ll);
-        rr_hi[e] = hh; rr_lo[e] = ll;
+        fi[e] = exp2f(gi[e] - gr[e]);
+        fj[e] = exp2f(gr[e] - gj[e]);
       }
-      accA[jj] = mfma16(lk_hi, rr_hi, accA[jj]);
-      accA[jj] = mfma16(lk_hi, rr_lo, accA[jj]);
-      accA[jj] = mfma16(lk_lo, rr_hi, accA[jj]);
-      accQ[jj] = mfma16(lq, rr_hi, accQ[jj]);
+      u16x8 ah, al, bh, bl;
+      scale_split(row8(sk, i, d0), fi, ah, al);
+      const u16x8 aq = scale_pack(row8(sq, i, d0), fi);
+      scale_split(row8(sk, j, d0), fj, bh, bl);
+      accA[jj] = mfma16(ah, bh, accA[jj]);
+      accA[jj] = mfma16(ah, bl, accA[jj]);
+      accA[jj] = mfma16(al, bh, accA[jj]);
+      accQ[jj] = mfma16(aq, bh, accQ[jj]);
     }
   }
 
-  // diagonal tiles: pairs i >= j of each 16-row block, elementwise
-  float dkk[3], dqk[3];
+  // diagonal tile I = wave (rows/columns t0 .. t0+15), split into 4 x 4
+  // sub-blocks p = l16 / 4. Pass P (reference t0 + 4P) takes A rows of
+  // sub-block P and B columns of sub-blocks below P; together the passes
+  // cover every pair of different sub-blocks exactly once. q k^T without
+  // decay gives the diagonal of the output matrix.
+  const int t0 = 16 * wave;
+  const int psub = l16 >> 2;
+  f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dQ = {0.f, 0.f, 0.f, 0.f}, dQ0 = {0.f, 0.f, 0.f, 0.f};
+  {
+    const int i = t0 + l16;  // A row and B column of this lane
+    const u16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-  for (int pp = 0; pp < 3; ++pp) {
-    const int p = tid + 256 * pp;
-    dkk[pp] = 0.f;
-    dqk[pp] = 0.f;
-    if (p >= 4 * 136) continue;
-    const int I = p / 136;
-    int rem = p - I * 136, il = 0;
-    while (rem > il) { rem -= il + 1; ++il; }
-    const int i = 16 * I + il, j = 16 * I + rem;
-    float skk = 0.f, sqk = 0.f;
-    for (int d = 0; d < kDim; d += 4) {
-      const float4 gi = *reinterpret_cast<const float4*>(sG + i * kLdG + d);
-      const float4 gj = *reinterpret_cast<const float4*>(sG + j * kLdG + d);
-      const u16x4 ki = *reinterpret_cast<const u16x4*>(sk + i * kLdRow + d);
-      const u16x4 kj = *reinterpret_cast<const u16x4*>(sk + j * kLdRow + d);
-      const u16x4 qi = *reinterpret_cast<const u16x4*>(sq + i * kLdRow + d);
-      const float e0 = exp2f(gi.x - gj.x), e1 = exp2f(gi.y - gj.y);
-      const float e2 = exp2f(gi.z - gj.z), e3 = exp2f(gi.w - gj.w);
-      const float w0 = bf2f(kj[0]) * e0, w1 = bf2f(kj[1]) * e1, w2 = bf2f(kj[2]) * e2, w3 = bf2f(kj[3]) * e3;
-      skk = fmaf(bf2f(ki[0]), w0, skk);
-      skk = fmaf(bf2f(ki[1]), w1, skk);
-      skk = fmaf(bf2f(ki[2]), w2, skk);
-      skk = fmaf(bf2f(ki[3]), w3, skk);
-      sqk = fmaf(bf2f(qi[0]), w0, sqk);
-      sqk = fmaf(bf2f(qi[1]), w1, sqk);
-      sqk = fmaf(bf2f(qi[2]), w2, sqk);
-      sqk = fmaf(bf2f(qi[3]), w3, sqk);
+    for (int s = 0; s < 4; ++s) {
+      const int d0 = 32 * s + 8 * g4;
+      float gi[8], gp[8], fa[8];
+      g8(i, d0, gi);
+      g8(t0 + 4 * psub, d0, gp);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fa[e] = exp2f(gi[e] - gp[e]);
+      const u16x8 ki = row8(sk, i, d0), qi = row8(sq, i, d0);
+      u16x8 ah, al;
+      scale_split(ki, fa, ah, al);
+      const u16x8 aq = scale_pack(qi, fa);
+      dQ0 = mfma16(qi, ki, dQ0);
+#pragma unroll
+      for (int P = 1; P < 4; ++P) {
+        float gr[8], fb[8];
+        g8(t0 + 4 * P, d0, gr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fb[e] = exp2f(psub < P ? gr[e] - gi[e] : -1000.0f);
+        u16x8 bh, bl;
+        scale_split(ki, fb, bh, bl);
+        const bool rowP = psub == P;
+        const u16x8 aph = rowP ? ah : zero8, apl = rowP ? al : zero8, apq = rowP ? aq : zero8;
+        dA = mfma16(aph, bh, dA);
+        dA = mfma16(aph, bl, dA);
+        dA = mfma16(apl, bh, dA);
+        dQ = mfma16(apq, bh, dQ);
+      }
     }
-    dkk[pp] = skk;
-    dqk[pp] = sqk;
   }
+  // pairs inside a 4 x 4 sub-block (i > j), elementwise with the mask
+  // before the power: lane < 48 takes pair lane / 2 and half the channels
+  float ekk = 0.f, eqk = 0.f;
+  int ei = 0, ej = 0;
+  if (lane < 48) {
+    const int pp = lane >> 1, half = lane & 1;
+    const int sb = pp / 6, w6 = pp - 6 * (pp / 6);
+    const int il = kInI[w6], jl = kInJ[w6];
+    ei = t0 + 4 * sb + il;
+    ej = t0 + 4 * sb + jl;
+    for (int d = 64 * half; d < 64 * half + 64; d += 4) {
+      const float4 gi = *reinterpret_cast<const float4*>(sG + ei * kLdG + d);
+      const float4 gj = *reinterpret_cast<const float4*>(sG + ej * kLdG + d);
+      const u16x4 ki = *reinterpret_cast<const u16x4*>(sk + ei * kLdRow + d);
+      const u16x4 kj = *reinterpret_cast<const u16x4*>(sk + ej * kLdRow + d);
+      const u16x4 qi = *reinterpret_cast<const u16x4*>(sq + ei * kLdRow + d);
+      const float w0 = bf2f(kj[0]) * exp2f(gi.x - gj.x), w1 = bf2f(kj[1]) * exp2f(gi.y - gj.y);
+      const float w2 = bf2f(kj[2]) * exp2f(gi.z - gj.z), w3 = bf2f(kj[3]) * exp2f(gi.w - gj.w);
+      ekk = fmaf(bf2f(ki[0]), w0, ekk); ekk = fmaf(bf2f(ki[1]), w1, ekk);
+      ekk = fmaf(bf2f(ki[2]), w2, ekk); ekk = fmaf(bf2f(ki[3]), w3, ekk);
+      eqk = fmaf(bf2f(qi[0]), w0, eqk); eqk = fmaf(bf2f(qi[1]), w1, eqk);
+      eqk = fmaf(bf2f(qi[2]), w2, eqk); eqk = fmaf(bf2f(qi[3]), w3, eqk);
+    }
+  }
+  ekk += __shfl_xor(ekk, 1);
+  eqk += __shfl_xor(eqk, 1);
   __syncthreads();
 
-  // results into the reused LDS
+  // results into the reused LDS: A = -beta_i rk_i rk_j (k k^T)_ij (i > j),
+  // Aqk = scale rq_i rk_j (q k^T)_ij (i >= j), zero above the diagonal
+  // inside the diagonal tiles (the inverse and the stores ignore the blocks
+  // above them)
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj) {
     const int job = wave + 4 * jj;
     if (job >= 6) continue;
-    int t = job, I = 1;
-    while (t >= I) { t -= I; ++I; }
-    const int J = t;
+    const int I = kOffI[job], J = kOffJ[job];
     const int jc = 16 * J + l16;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -523,20 +581,21 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
       u.mat.aqk[ii * kLdQ + jc] = f2bf(a.scale * sRq[ii] * sRk[jc] * accQ[jj][e]);
     }
   }
-  for (int idx = tid; idx < 4 * 256; idx += 256) {
-    const int I = idx >> 8, il = (idx >> 4) & 15, jl = idx & 15;
-    if (il < jl) u.mat.aqk[(16 * I + il) * kLdQ + 16 * I + jl] = 0;
-  }
+  {
+    const int jc = t0 + l16;
 #pragma unroll
-  for (int pp = 0; pp < 3; ++pp) {
-    const int p = tid + 256 * pp;
-    if (p >= 4 * 136) continue;
-    const int I = p / 136;
-    int rem = p - I * 136, il = 0;
-    while (rem > il) { rem -= il + 1; ++il; }
-    const int i = 16 * I + il, j = 16 * I + rem;
-    u.mat.A[i * kLdF + j] = (i > j) ? -sBeta[i] * sRk[i] * sRk[j] * dkk[pp] : 0.0f;
-    u.mat.aqk[i * kLdQ + j] = f2bf(a.scale * sRq[i] * sRk[j] * dqk[pp]);
+    for (int e = 0; e < 4; ++e) {
+      const int il = 4 * g4 + e, ii = t0 + il;
+      if ((il >> 2) == psub && il > l16) continue;  // inside a sub-block: elementwise lanes
+      const bool lower = il > l16;
+      u.mat.A[ii * kLdF + jc] = lower ? -sBeta[ii] * sRk[ii] * sRk[jc] * dA[e] : 0.0f;
+      const float qv = il == l16 ? dQ0[e] : dQ[e];
+      u.mat.aqk[ii * kLdQ + jc] = il >= l16 ? f2bf(a.scale * sRq[ii] * sRk[jc] * qv) : (uint16_t)0;
+    }
+  }
+  if (lane < 48 && (lane & 1) == 0) {
+    u.mat.A[ei * kLdF + ej] = -sBeta[ei] * sRk[ei] * sRk[ej] * ekk;
+    u.mat.aqk[ei * kLdQ + ej] = f2bf(a.scale * sRq[ei] * sRk[ej] * eqk);
   }
   __syncthreads();
 
@@ -561,12 +620,13 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
 }
 
 hipError_t launch_prepare(bool kda, const PrepareArgs& a, hipStream_t stream) {
+  const long items = (long)a.geo.NT * a.H;
+  const int cus = a.cus > 0 ? a.cus : 256;
   if (kda) {
     hipLaunchKernelGGL(kda_prepare_kernel, dim3(a.geo.NT, a.H), dim3(256), 0, stream, a);
   } else {
     // three workgroups fit a compute unit (43.5 KiB of LDS each)
-    const long items = (long)a.geo.NT * a.H;
-    const long slots = 3L * (a.cus > 0 ? a.cus : 256);
+    const long slots = 3L * cus;
     hipLaunchKernelGGL(gdn_prepare_kernel, dim3((unsigned)(items < slots ? items : slots)), dim3(256), 0, stream, a);
   }
   return hipGetLastError();
