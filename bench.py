@@ -6,12 +6,15 @@ the whole synthetic batch: the prepare kernel and the fused state/output
 kernel, inputs resident in HBM, workspace preallocated. Prints one JSON line.
 
 Timing: each of the K timed calls is bracketed by its own HIP events on the
-call's stream, with a 1 GiB buffer written before it so that the inputs come
-from HBM rather than the 256 MB last-level cache; the headline is the median
-(p10 and p90 reported beside it). A second scrubbed pass of K calls, with the
-library recording HIP events around each kernel on the launch stream, gives
-the per-kernel durations (kept out of the headline pass, whose calls they
-would lengthen). The same K calls are also timed back to back without the
+call's stream, with a 1 GiB buffer read before it, so that the inputs come
+from HBM rather than the 256 MB last-level cache and the caches hold only
+clean lines; the headline is the median (p10 and p90 reported beside it). A
+second scrubbed pass of K calls, with the library recording HIP events around
+each kernel on the launch stream, gives the per-kernel durations (kept out of
+the headline pass, whose calls they would lengthen). Two more passes are
+reported beside the headline: the K calls with the 1 GiB buffer written
+instead of read before each (the caches then hold dirty lines of other data,
+whose write-back the call pays for), and the K calls back to back with no
 scrub ("warm").
 
     python bench.py [--steps K] [--warmup W] [--workload gdn|varlen|long|kda|tiny]
@@ -85,7 +88,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gdn", choices=["gdn", "varlen", "long", "kda", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--scrub-mib", type=int, default=1024, help="bytes written between timed calls (0: none)")
+    ap.add_argument("--scrub-mib", type=int, default=1024, help="MiB read between timed calls (0: none)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run plain device-to-device copies of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -150,30 +153,40 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # scrubbed: one event pair per call, a 1 GiB write before each
-    scrub = torch.empty(max(args.scrub_mib, 1) * (1 << 20) // 4, dtype=torch.float32, device=dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # scrubbed: one event pair per call, a 1 GiB read before each
+    scrub = torch.full((max(args.scrub_mib, 1) * (1 << 20) // 4,), 1.0, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
-    for i in range(args.steps):
+
+    def scrub_read():
         if args.scrub_mib:
-            scrub.fill_(float(i))
-        evs[i][0].record(stream)
-        step()
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    per_call = np.array([a.elapsed_time(b) for a, b in evs])
+            scrub.sum()
+
+    def timed_calls(before):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            before(i)
+            evs[i][0].record(stream)
+            step()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])
+
+    per_call = timed_calls(lambda i: scrub_read())
 
     # scrubbed again, with per-kernel events recorded by the library
     gdn.timing_enable(True)
     gdn.timing_read()
     for i in range(args.steps):
-        if args.scrub_mib:
-            scrub.fill_(float(i))
+        scrub_read()
         step()
     torch.cuda.synchronize()
     gdn.timing_enable(False)
     prep_ms, state_ms, calls = gdn.timing_read()
     assert calls == args.steps
+
+    # the buffer written instead of read before each call
+    per_call_dirty = timed_calls(lambda i: scrub.fill_(float(i)) if args.scrub_mib else None)
     del scrub
 
     # warm: the same number of calls back to back
@@ -280,9 +293,10 @@ def main():
         "mfma_bf16_frac": round(mfma_frac, 4),
         "path_alg_hbm_frac": round(path_gbps / HBM_PEAK_GBPS, 4),
         "kernels_us": {"prepare": round(prep_us, 2), "state_output": round(state_us, 2)},
-        "timing": {"per_call": "median of %d calls, %d MiB written before each" % (args.steps, args.scrub_mib),
+        "timing": {"per_call": "median of %d calls, %d MiB read before each" % (args.steps, args.scrub_mib),
                    "p10_ms": round(float(np.percentile(per_call, 10)), 5),
                    "p90_ms": round(float(np.percentile(per_call, 90)), 5),
+                   "written_scrub_ms": round(float(np.median(per_call_dirty)), 5),
                    "warm_ms_per_step": round(warm_ms_per_step, 5),
                    "warm_tokens_per_s": round(tokens / (warm_ms_per_step * 1e-3), 1)},
         "wall_ms_per_step": round(wall_ms_per_step, 5),

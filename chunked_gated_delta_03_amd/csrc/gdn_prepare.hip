@@ -207,152 +207,374 @@ __device__ __forceinline__ void store_t_aqk(const PrepareArgs& a, size_t cm, int
 // ===========================================================================
 // GDN: scalar natural-log gate per (token, head)
 // ===========================================================================
-// One workgroup per compute-unit slot, looping over the (chunk, head) items
-// (chunk-major, so neighbouring workgroups read neighbouring rows); the q, k,
-// g and beta of the next item are loaded into registers while the current
-// one is computed.
-__global__ __launch_bounds__(256, 3) void gdn_prepare_kernel(PrepareArgs a) {
+constexpr int kLdP = kChunk + 4;  // fp32 row stride (16-byte aligned rows) of A and T
+
+// 16x16 fp32 product X Y on v_mfma_f32_16x16x4f32, both factors in the
+// accumulator layout (lane (g, l) holds rows 4g..4g+3 of column l): xt holds
+// X^T, y holds Y. The contraction slot of lane group g at step ks is 4g + ks,
+// which is register ks of both operands.
+__device__ __forceinline__ f32x4 mm16(const f32x4& xt, const f32x4& y, f32x4 acc) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[ks], y[ks], acc, 0, 0, 0);
+  return acc;
+}
+
+// acc += A_IM T_MJ, both 16x16 blocks read from LDS (stride kLdP); the
+// contraction slot of lane group g at step ks is 4g + ks, so the A fragment
+// is one 16-byte read.
+__device__ __forceinline__ f32x4 mm_lds(const float* sA, const float* sT, int I, int M, int J, int g, int l,
+                                        f32x4 acc) {
+  const float4 av = *reinterpret_cast<const float4*>(sA + (16 * I + l) * kLdP + 16 * M + 4 * g);
+  const float ava[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ava[ks], sT[(16 * M + 4 * g + ks) * kLdP + 16 * J + l], acc, 0, 0, 0);
+  return acc;
+}
+
+// inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then the
+// row broadcasts of lanes 15 and 31)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+  x += dpp_or_zero<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_or_zero<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_or_zero<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_or_zero<0x118, 0xF>(x);  // row_shr:8
+  x += dpp_or_zero<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_or_zero<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+// Gram tiles per wave. Wave W loads the 16 rows of block W of k and q (MFMA
+// operand order) and shares its k block with the other waves through LDS. It
+// forms the q k^T tiles of block row W (its own q rows against k_J), the
+// diagonal k k^T tile (W, W) and some of the six k k^T tiles below the
+// diagonal:
+//   wave 0: (2,0) (3,0) (3,1)    wave 1: (1,0) (2,1)    wave 2: (3,2)    wave 3: none
+// Each wave then owns row block W: the norms of its rows, the inverse of its
+// diagonal block and block row W of T.
+
+struct PrepSmem {
+  union {
+    float A[kChunk * kLdP];   // off-diagonal blocks of A
+    u16x8 kst[4][4][64];      // the k blocks in operand order, [block][step][lane]
+  } u;
+  float T[kChunk * kLdP];     // lower blocks of T
+  uint16_t aqk[kChunk * kLdQ];
+  float G[kChunk], beta[kChunk], rq[kChunk], rk[kChunk];
+};
+
+// One 16x128 block of q or k rows in MFMA operand order: lane (g, l) holds
+// row 16R + l, columns 32s + 8g .. +7 in element s. Rows past the chunk end
+// read the last valid row (finite data; their norm factors are zero).
+__device__ __forceinline__ void fetch_block(const uint16_t* base, const PrepareArgs& a, const ChunkInfo& ci, int h,
+                                            int R, int g, int l, u16x8 (&blk)[4]) {
+  const int r = min(16 * R + l, ci.len - 1);
+  const uint16_t* p = base + ((size_t)(ci.tok0 + r) * a.H + h) * kDim + 8 * g;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) blk[s] = *reinterpret_cast<const u16x8*>(p + 32 * s);
+}
+
+__device__ __forceinline__ float sumsq_blk(const u16x8 (&blk)[4]) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    s += sumsq8(__builtin_bit_cast(uint4, blk[i]));
+  return s;
+}
+
+__device__ __forceinline__ f32x4 gram_tile(const u16x8 (&x)[4], const u16x8 (&y)[4]) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = mfma16(x[s], y[s], acc);
+  return acc;
+}
+
+// T (stride kLdP) and Aqk of one item to HBM, as store_t_aqk.
+__device__ __forceinline__ void store_t_aqk_p(const PrepareArgs& a, size_t cm, int tid, const float* sT,
+                                              const uint16_t* sAqk) {
+  uint16_t* tdst = a.tmat + cm * (kChunk * 2 * kChunk);
+  uint16_t* qdst = a.aqk + cm * (kChunk * kChunk);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int idx = pass * 256 + tid;
+    const int r = idx >> 3, m = idx & 7;
+    const int c0 = 32 * (m >> 2) + 4 * (m & 3);  // columns c0 + e and c0 + 16 + e
+    const bool up0 = (c0 >> 4) > (r >> 4);
+    const bool up1 = ((c0 + 16) >> 4) > (r >> 4);
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 x0 = up0 ? z : *reinterpret_cast<const float4*>(sT + r * kLdP + c0);
+    const float4 x1 = up1 ? z : *reinterpret_cast<const float4*>(sT + r * kLdP + c0 + 16);
+    uint32_t hi[4], lo[4];
+    split2(x0.x, x0.y, hi[0], lo[0]);
+    split2(x0.z, x0.w, hi[1], lo[1]);
+    split2(x1.x, x1.y, hi[2], lo[2]);
+    split2(x1.z, x1.w, hi[3], lo[3]);
+    *reinterpret_cast<uint4*>(tdst + r * (2 * kChunk) + 8 * m) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *reinterpret_cast<uint4*>(tdst + r * (2 * kChunk) + kChunk + 8 * m) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    const u16x4 q0 = up0 ? u16x4{0, 0, 0, 0} : *reinterpret_cast<const u16x4*>(sAqk + r * kLdQ + c0);
+    const u16x4 q1 = up1 ? u16x4{0, 0, 0, 0} : *reinterpret_cast<const u16x4*>(sAqk + r * kLdQ + c0 + 16);
+    *reinterpret_cast<u16x8*>(qdst + r * kChunk + 8 * m) = cat4(q0, q1);
+  }
+}
+
+// The work of wave W over all items of the workgroup (persistent, items
+// chunk-major). Per item: its k block to LDS, the Gram tiles that need only
+// its own rows, the norms, gate scan and beta; after a barrier the tiles that
+// need other k blocks, the previous item's T, Aqk and row vectors to HBM and
+// the next item's loads; after a second barrier the scaling into A / Aqk, the
+// diagonal block inverse in registers and the off-diagonal blocks of T, one
+// block diagonal per barrier.
+template <int W>
+__device__ __forceinline__ void gdn_prepare_wave(const PrepareArgs& a, PrepSmem& sm) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int g4 = lane >> 4;
-  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int l = lane & 15;
   const int n_items = a.geo.NT * a.H;
+  const bool l2 = (a.flags & 1u) != 0;
 
-  // q, k rows live only until the Gram tiles are in registers; A, T and Aqk
-  // reuse their space afterwards.
-  __shared__ union alignas(16) {
-    struct {
-      uint16_t k[kChunk * kLdRow];
-      uint16_t q[kChunk * kLdRow];
-    } in;
-    struct {
-      float A[kChunk * kLdF];
-      float T[kChunk * kLdF];
-      uint16_t aqk[kChunk * kLdQ];
-    } mat;
-  } u;
-  __shared__ __attribute__((aligned(16))) float sG[kChunk], sBeta[kChunk], sRq[kChunk], sRk[kChunk];
-
-  // registers of the next item: q, k rows (all threads), raw g and beta
-  // (wave 0; masked when they are written to LDS, so nothing waits on them)
-  QKRegs nx;
-  float ngx = 0.0f;
-  uint16_t nbx = 0;
+  // own rows of the item in flight, with the gate and beta (wave 0)
+  u16x8 kw[4], qw[4];
+  float graw = 0.f;
+  uint16_t braw = 0;
   auto fetch = [&](int it) {
     const int c = it / a.H, h = it - (it / a.H) * a.H;
     const ChunkInfo ci = a.geo.chunk(c);
-    fetch_qk(a, ci, h, tid, nx);
-    if (wave == 0) {
-      const size_t off = (size_t)(ci.tok0 + (lane < ci.len ? lane : 0)) * a.H + h;
-      ngx = a.g[off];
-      nbx = a.beta[off];
+    fetch_block(a.k, a, ci, h, W, g, l, kw);
+    fetch_block(a.q, a, ci, h, W, g, l, qw);
+    if constexpr (W == 0) {
+      const size_t off = (size_t)(ci.tok0 + min(lane, ci.len - 1)) * a.H + h;
+      graw = a.g[off];
+      braw = a.beta[off];
     }
   };
-  if ((int)blockIdx.x < n_items) fetch(blockIdx.x);
+  auto kblk = [&](int J, u16x8 (&x)[4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) x[s] = sm.u.kst[J][s][lane];
+  };
 
+  int prev = -1;  // item whose T and Aqk are still in LDS
+  float vrow0 = 0.f, vrow1 = 0.f;  // its row vectors W and W + 4
+  auto store_prev = [&]() {
+    const int c = prev / a.H, h = prev - (prev / a.H) * a.H;
+    const size_t cm = (size_t)h * a.geo.NT + c;
+    store_t_aqk_p(a, cm, tid, sm.T, sm.aqk);
+    float* vd = a.vec + cm * (kVecRows * kChunk);
+    vd[W * 64 + lane] = vrow0;
+    vd[(W + 4) * 64 + lane] = vrow1;
+  };
+
+  if ((int)blockIdx.x < n_items) fetch(blockIdx.x);
   for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
     const int c = it / a.H;
-    const int h = it - c * a.H;
     const ChunkInfo ci = a.geo.chunk(c);
 
-    put_qk_norms(a, ci, tid, nx, u.in.k, u.in.q, sRk, sRq);
-    if (wave == 0) {
-      const bool valid = lane < ci.len;
-      float gx = valid ? ngx : 0.0f;
+    // own k block to LDS (the A area is free since the previous item's last
+    // barrier); the tiles of own rows only
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float y = __shfl_up(gx, o);
-        if (lane >= o) gx += y;
-      }
-      sG[lane] = gx;
-      const float b = valid ? bf2f(nbx) : 0.0f;
-      sBeta[lane] = ((a.flags & 2u) && valid) ? 1.0f / (1.0f + expf(-b)) : b;
-    }
-    // the next item's loads (the last item's again past the end, harmlessly)
-    fetch(min(it + (int)gridDim.x, n_items - 1));
-    __syncthreads();
-
-    // Gram tiles on MFMA: k k^T (strictly lower) by waves 0-1, q k^T (lower) by
-    // waves 2-3; each wave takes 5 of the 10 lower 16x16 tiles.
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const int kind = wv >> 1;
-    const uint16_t* left = kind == 0 ? u.in.k : u.in.q;
-    f32x4 acc[5];
-#pragma unroll
-    for (int jj = 0; jj < 5; ++jj) {
-      const int t = (wv & 1) + 2 * jj;
-      const int I = kTileI[t], J = kTileJ[t];
-      u16x8 av[4], bv[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        av[s] = *reinterpret_cast<const u16x8*>(left + (16 * I + l16) * kLdRow + 32 * s + 8 * g4);
-        bv[s] = *reinterpret_cast<const u16x8*>(u.in.k + (16 * J + l16) * kLdRow + 32 * s + 8 * g4);
-      }
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) x = mfma16(av[s], bv[s], x);
-      acc[jj] = x;
-    }
-    __syncthreads();
-    // scale into A (fp32) or Aqk (bf16); the causal mask is applied to the
-    // exponent before the exponential (masked entries use a large negative one)
+    for (int s = 0; s < 4; ++s) sm.u.kst[W][s][lane] = kw[s];
+    const f32x4 kkD = gram_tile(kw, kw);
+    const f32x4 qkD = gram_tile(qw, kw);
+    // norms of this wave's 16 rows; lanes l, l+16, l+32, l+48 share a row
     {
-      const float* rrow = kind == 0 ? sRk : sRq;
-      const float sgn = kind == 0 ? -1.0f : a.scale;
-#pragma unroll
-      for (int jj = 0; jj < 5; ++jj) {
-        const int t = (wv & 1) + 2 * jj;
-        const int I = kTileI[t], J = kTileJ[t];
-        const int jc = 16 * J + l16;
-        const int i0 = 16 * I + 4 * g4;
-        const float4 gi = *reinterpret_cast<const float4*>(sG + i0);
-        const float4 ri = *reinterpret_cast<const float4*>(rrow + i0);
-        const float4 bi = kind == 0 ? *reinterpret_cast<const float4*>(sBeta + i0) : make_float4(1.f, 1.f, 1.f, 1.f);
-        const float gj = sG[jc], rj = sRk[jc] * sgn;
-        const float gia[4] = {gi.x, gi.y, gi.z, gi.w};
-        const float ria[4] = {ri.x, ri.y, ri.z, ri.w};
-        const float bia[4] = {bi.x, bi.y, bi.z, bi.w};
-        float val[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float m = (i0 + e + kind > jc) ? 1.0f : 0.0f;  // i > j (k k^T) or i >= j (q k^T)
-          const float ex = __expf((gia[e] - gj) * m);
-          val[e] = m * bia[e] * ria[e] * rj * acc[jj][e] * ex;
-        }
-        if (kind == 0) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) u.mat.A[(i0 + e) * kLdF + jc] = val[e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) u.mat.aqk[(i0 + e) * kLdQ + jc] = __builtin_bit_cast(uint16_t, (__bf16)val[e]);
-        }
+      float sk = sumsq_blk(kw), sq = sumsq_blk(qw);
+      sk += __shfl_xor(sk, 16);
+      sq += __shfl_xor(sq, 16);
+      sk += __shfl_xor(sk, 32);
+      sq += __shfl_xor(sq, 32);
+      if (g == 0) {
+        const int r = 16 * W + l;
+        const bool valid = r < ci.len;
+        sm.rk[r] = valid ? (l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f) : 0.0f;
+        sm.rq[r] = valid ? (l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f) : 0.0f;
       }
+    }
+    if constexpr (W == 0) {
+      const bool valid = lane < ci.len;
+      sm.G[lane] = wave_inclusive_sum(valid ? graw : 0.0f);
+      const float b = valid ? bf2f(braw) : 0.0f;
+      sm.beta[lane] = ((a.flags & 2u) && valid) ? 1.0f / (1.0f + expf(-b)) : b;
     }
     __syncthreads();
 
-    invert_unit_lower(u.mat.A, u.mat.T, wave, lane);
-
-    const size_t cm = (size_t)h * a.geo.NT + c;
-    store_t_aqk(a, cm, tid, u.mat.T, u.mat.aqk);
-    if (tid < 64) {
-      const int i = tid;
-      const bool valid = i < ci.len;
-      const float G = sG[i];
-      const float Glast = sG[63];
-      const float b = valid ? sBeta[i] : 0.f;
-      const float rk = sRk[i], rq = sRq[i];
-      float* vd = a.vec + cm * (kVecRows * kChunk);
-      vd[0 * 64 + i] = b;
-      vd[1 * 64 + i] = valid ? b * rk * expf(G) : 0.f;
-      vd[2 * 64 + i] = valid ? rk * expf(Glast - G) : 0.f;
-      vd[3 * 64 + i] = valid ? a.scale * rq * expf(G) : 0.f;
-      vd[4 * 64 + i] = G;
-      vd[5 * 64 + i] = rq;
-      vd[6 * 64 + i] = rk;
-      vd[7 * 64 + i] = (i == 0) ? expf(Glast) : 0.f;
+    // tiles with other k blocks: kk* = k k^T (I, J), qk* = q_W k_J^T
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 kk0 = z, kk1 = z, kk2 = z, qk0 = z, qk1 = z, qk2 = z;
+    {
+      u16x8 b0[4], b1[4], b2[4];
+      if constexpr (W == 0) {
+        kblk(2, b0); kblk(3, b1); kblk(1, b2);
+        kk0 = gram_tile(b0, kw);  // (2,0)
+        kk1 = gram_tile(b1, kw);  // (3,0)
+        kk2 = gram_tile(b1, b2);  // (3,1)
+      } else if constexpr (W == 1) {
+        kblk(0, b0); kblk(2, b1);
+        kk0 = gram_tile(kw, b0);  // (1,0)
+        kk1 = gram_tile(b1, kw);  // (2,1)
+        qk0 = gram_tile(qw, b0);  // q (1,0)
+      } else if constexpr (W == 2) {
+        kblk(0, b0); kblk(1, b1); kblk(3, b2);
+        kk0 = gram_tile(b2, kw);  // (3,2)
+        qk0 = gram_tile(qw, b0);  // q (2,0)
+        qk1 = gram_tile(qw, b1);  // q (2,1)
+      } else {
+        kblk(0, b0); kblk(1, b1); kblk(2, b2);
+        qk0 = gram_tile(qw, b0);  // q (3,0)
+        qk1 = gram_tile(qw, b1);  // q (3,1)
+        qk2 = gram_tile(qw, b2);  // q (3,2)
+      }
     }
-    __syncthreads();  // LDS is rewritten by the next item
+    const int next = min(it + (int)gridDim.x, n_items - 1);
+    if (prev >= 0) store_prev();
+    prev = it;
+    fetch(next);
+    __syncthreads();
+
+    // scaling: A_ij = -beta_i rk_i rk_j e^(G_i - G_j) (k_i . k_j), i > j;
+    // Aqk_ij = scale rq_i rk_j e^(G_i - G_j) (q_i . k_j), i >= j. Off-diagonal
+    // tiles need no mask; on the diagonal the mask zeroes the exponent first.
+    auto put_kk = [&](int I, int J, const f32x4& kk) {
+      const int i0 = 16 * I + 4 * g, j = 16 * J + l;
+      const float4 gi = *reinterpret_cast<const float4*>(sm.G + i0);
+      const float4 bi = *reinterpret_cast<const float4*>(sm.beta + i0);
+      const float4 ki = *reinterpret_cast<const float4*>(sm.rk + i0);
+      const float gj = sm.G[j], rj = sm.rk[j];
+      const float gia[4] = {gi.x, gi.y, gi.z, gi.w}, bia[4] = {bi.x, bi.y, bi.z, bi.w};
+      const float kia[4] = {ki.x, ki.y, ki.z, ki.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.u.A[(i0 + e) * kLdP + j] = -bia[e] * kia[e] * rj * __expf(gia[e] - gj) * kk[e];
+    };
+    auto put_qk = [&](int J, const f32x4& qk) {  // block row W
+      const int i0 = 16 * W + 4 * g, j = 16 * J + l;
+      const float4 gi = *reinterpret_cast<const float4*>(sm.G + i0);
+      const float4 qi = *reinterpret_cast<const float4*>(sm.rq + i0);
+      const float gj = sm.G[j], rj = sm.rk[j] * a.scale;
+      const float gia[4] = {gi.x, gi.y, gi.z, gi.w}, qia[4] = {qi.x, qi.y, qi.z, qi.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float m = (J < W || 4 * g + e >= l) ? 1.0f : 0.0f;
+        sm.aqk[(i0 + e) * kLdQ + j] =
+            __builtin_bit_cast(uint16_t, (__bf16)(m * qia[e] * rj * __expf((gia[e] - gj) * m) * qk[e]));
+      }
+    };
+    put_qk(W, qkD);
+    if constexpr (W == 0) {
+      put_kk(2, 0, kk0);
+      put_kk(3, 0, kk1);
+      put_kk(3, 1, kk2);
+    } else if constexpr (W == 1) {
+      put_kk(1, 0, kk0);
+      put_kk(2, 1, kk1);
+      put_qk(0, qk0);
+    } else if constexpr (W == 2) {
+      put_kk(3, 2, kk0);
+      put_qk(0, qk0);
+      put_qk(1, qk1);
+    } else {
+      put_qk(0, qk0);
+      put_qk(1, qk1);
+      put_qk(2, qk2);
+    }
+
+    // diagonal block W: N (strictly lower part of A's block) and N^T in the
+    // accumulator layout from the symmetric k k^T tile
+    f32x4 N, Nt, Y;
+    {
+      const int r0 = 16 * W + 4 * g, cc = 16 * W + l;
+      const float4 gi = *reinterpret_cast<const float4*>(sm.G + r0);
+      const float4 bi = *reinterpret_cast<const float4*>(sm.beta + r0);
+      const float4 ki = *reinterpret_cast<const float4*>(sm.rk + r0);
+      const float gc = sm.G[cc], bc = sm.beta[cc], kc = sm.rk[cc];
+      const float gia[4] = {gi.x, gi.y, gi.z, gi.w}, bia[4] = {bi.x, bi.y, bi.z, bi.w};
+      const float kia[4] = {ki.x, ki.y, ki.z, ki.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;  // row inside the block; column l
+        const float lower = r > l ? 1.0f : 0.0f, upper = r < l ? 1.0f : 0.0f;
+        const float kk = kkD[e] * kia[e] * kc;
+        N[e] = lower * -bia[e] * kk * __expf((gia[e] - gc) * lower);
+        Nt[e] = upper * -bc * kk * __expf((gc - gia[e]) * upper);
+        Y[e] = Nt[e] + (r == l ? 1.0f : 0.0f);
+      }
+    }
+    // (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8) for the nilpotent N;
+    // Y carries the transposed partial product, finally T_WW^T.
+    {
+      const f32x4 N2 = mm16(Nt, N, z), N2t = mm16(N, Nt, z);
+      Y = mm16(N2, Y, Y);
+      const f32x4 N4 = mm16(N2t, N2, z), N4t = mm16(N2, N2t, z);
+      Y = mm16(N4, Y, Y);
+      const f32x4 N8 = mm16(N4t, N4, z);
+      Y = mm16(N8, Y, Y);
+    }
+    // lane (g, l) holds T_WW[l][4g + e]
+    *reinterpret_cast<float4*>(sm.T + (16 * W + l) * kLdP + 16 * W + 4 * g) = make_float4(Y[0], Y[1], Y[2], Y[3]);
+    __syncthreads();
+
+    // off-diagonal blocks of block row W: T_WJ = T_WW sum_{J <= M < W} A_WM T_MJ,
+    // partial sums formed as soon as their T blocks exist
+    auto put_t = [&](int J, const f32x4& t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.T[(16 * W + 4 * g + e) * kLdP + 16 * J + l] = t[e];
+    };
+    f32x4 p0 = z, p1 = z;
+    if constexpr (W == 1) {
+      put_t(0, mm16(Y, mm_lds(sm.u.A, sm.T, 1, 0, 0, g, l, z), z));
+    } else if constexpr (W == 2) {
+      put_t(1, mm16(Y, mm_lds(sm.u.A, sm.T, 2, 1, 1, g, l, z), z));
+      p0 = mm_lds(sm.u.A, sm.T, 2, 0, 0, g, l, z);
+    } else if constexpr (W == 3) {
+      put_t(2, mm16(Y, mm_lds(sm.u.A, sm.T, 3, 2, 2, g, l, z), z));
+      p1 = mm_lds(sm.u.A, sm.T, 3, 1, 1, g, l, z);
+      p0 = mm_lds(sm.u.A, sm.T, 3, 0, 0, g, l, z);
+    }
+    __syncthreads();
+    if constexpr (W == 2) {
+      put_t(0, mm16(Y, mm_lds(sm.u.A, sm.T, 2, 1, 0, g, l, p0), z));
+    } else if constexpr (W == 3) {
+      put_t(1, mm16(Y, mm_lds(sm.u.A, sm.T, 3, 2, 1, g, l, p1), z));
+      p0 = mm_lds(sm.u.A, sm.T, 3, 1, 0, g, l, p0);
+    }
+    __syncthreads();
+    if constexpr (W == 3) put_t(0, mm16(Y, mm_lds(sm.u.A, sm.T, 3, 2, 0, g, l, p0), z));
+
+    // row vectors W and W + 4 of this item (beta, c, d, r, G, rq, rk, e^G_last)
+    {
+      const int i = lane;
+      const bool valid = i < ci.len;
+      const float G = sm.G[i];
+      if constexpr (W == 0) {
+        vrow0 = valid ? sm.beta[i] : 0.f;
+        vrow1 = G;
+      } else if constexpr (W == 1) {
+        vrow0 = valid ? sm.beta[i] * sm.rk[i] * expf(G) : 0.f;
+        vrow1 = sm.rq[i];
+      } else if constexpr (W == 2) {
+        vrow0 = valid ? sm.rk[i] * expf(sm.G[63] - G) : 0.f;
+        vrow1 = sm.rk[i];
+      } else {
+        vrow0 = valid ? a.scale * sm.rq[i] * expf(G) : 0.f;
+        vrow1 = (i == 0) ? expf(sm.G[63]) : 0.f;
+      }
+    }
+    __syncthreads();  // T complete; A, the k blocks and the vectors are rewritten by the next item
+  }
+  if (prev >= 0) store_prev();
+}
+
+// One workgroup (4 waves) per compute-unit slot (three fit), looping over
+// the (chunk, head) items.
+__global__ __launch_bounds__(256, 3) void gdn_prepare_kernel(PrepareArgs a) {
+  __shared__ __attribute__((aligned(16))) PrepSmem sm;
+  switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+    case 0: gdn_prepare_wave<0>(a, sm); break;
+    case 1: gdn_prepare_wave<1>(a, sm); break;
+    case 2: gdn_prepare_wave<2>(a, sm); break;
+    default: gdn_prepare_wave<3>(a, sm); break;
   }
 }
 
