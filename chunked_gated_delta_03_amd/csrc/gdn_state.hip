@@ -149,10 +149,11 @@ __global__ __launch_bounds__((2 * NCB + kLoaders) * 64) void gdn_state_kernel(Fw
       if (ltid < kVecRows * kChunk / 4) *reinterpret_cast<u32x4*>(B.vec + 4 * ltid) = er;
     };
     // Same barrier sequence as the compute waves: one before the loop, two
-    // per chunk. During chunk jc, chunk jc+1 goes into the buffer chunk jc-1
-    // released (k and q before the first barrier, the rest after it) and the
-    // loads of chunk jc+2 are issued. Both run unconditionally (past the end
-    // the last chunk is repeated, harmlessly), so no load waits for another.
+    // per chunk. During chunk jc, after the pair barrier (so that the LDS
+    // writes do not compete with the compute waves' reads before it), chunk
+    // jc+1 goes into the buffer chunk jc-1 released and the loads of chunk
+    // jc+2 are issued. Both run unconditionally (past the end the last chunk
+    // is repeated, harmlessly), so no load waits for another.
     if (si.nch > 0) {
       fetch(0);
       put(0, 0);
@@ -162,8 +163,8 @@ __global__ __launch_bounds__((2 * NCB + kLoaders) * 64) void gdn_state_kernel(Fw
     __syncthreads();
     for (int jc = 0; jc < si.nch; ++jc) {
       const int bn = (jc & 1) ^ 1;
-      put(bn, 0);
       __syncthreads();
+      put(bn, 0);
       put(bn, 1);
       fetch(min(jc + 2, last));
       __syncthreads();
