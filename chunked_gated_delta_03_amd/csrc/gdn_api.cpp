@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -122,6 +123,8 @@ int check_device(int* cus) {
 
 // ---------------------------------------------------------------------------
 // Workspace layout: [tables | tmat | aqk | vec | gk(KDA)], each 256-byte aligned.
+// Packed tables: chunk table [NT] int4, sequence table [N] int4, sequence
+// launch order [N] int (padded to whole int4).
 struct Layout {
   size_t tab = 0, tmat = 0, aqk = 0, vec = 0, gk = 0, total = 0;
 };
@@ -132,7 +135,7 @@ Layout layout_for(const Problem& p, bool with_intermediates) {
   Layout L;
   size_t off = 0;
   L.tab = off;
-  if (p.packed) off += align256(sizeof(int4) * ((size_t)p.NT + (size_t)p.N));
+  if (p.packed) off += align256(sizeof(int4) * ((size_t)p.NT + (size_t)p.N + ((size_t)p.N + 3) / 4));
   if (with_intermediates) {
     const size_t cmH = (size_t)p.NT * p.H;
     L.tmat = off;
@@ -181,6 +184,19 @@ int upload_tables(const Problem& p, void* dst, hipStream_t stream) {
     c += nch;
   }
   tab.insert(tab.end(), seqs.begin(), seqs.end());
+  // launch order of the sequential state pass: longest sequences first
+  // (ties in sequence order)
+  std::vector<int> order(p.N);
+  for (int n = 0; n < p.N; ++n) order[n] = n;
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return seqs[x].w > seqs[y].w; });
+  for (int n = 0; n < p.N; n += 4) {
+    int4 e = make_int4(0, 0, 0, 0);
+    e.x = order[n];
+    if (n + 1 < p.N) e.y = order[n + 1];
+    if (n + 2 < p.N) e.z = order[n + 2];
+    if (n + 3 < p.N) e.w = order[n + 3];
+    tab.push_back(e);
+  }
   const size_t bytes = tab.size() * sizeof(int4);
 
   int dev = 0;
@@ -228,9 +244,11 @@ gdn::Geometry make_geometry(const Problem& p, void* tab_dev) {
   if (p.packed) {
     g.ctab = static_cast<const int4*>(tab_dev);
     g.stab = static_cast<const int4*>(tab_dev) + p.NT;
+    g.sorder = reinterpret_cast<const int*>(static_cast<const int4*>(tab_dev) + p.NT + p.N);
   } else {
     g.ctab = nullptr;
     g.stab = nullptr;
+    g.sorder = nullptr;
   }
   return g;
 }

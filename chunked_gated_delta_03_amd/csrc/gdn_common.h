@@ -100,6 +100,7 @@ struct SeqInfo {
 struct Geometry {
   const int4* ctab;  // [NT] {tok0, len, seq, j} or nullptr (dense)
   const int4* stab;  // [N]  {tok0, len, c0, nch} or nullptr (dense)
+  const int* sorder; // [N]  sequences by decreasing chunk count, or nullptr (dense: in order)
   int T;             // dense sequence length
   int ncb;           // dense chunks per sequence = ceil(T/64)
   int NT;            // total chunks
@@ -132,6 +133,30 @@ struct Geometry {
     }
     return si;
   }
+  // sequence of rank r in the launch order
+  __device__ __forceinline__ int seq_of_rank(int r) const {
+    return sorder ? ((const __attribute__((address_space(4))) int*)sorder)[r] : r;
+  }
 };
+
+// Workgroup -> (sequence, head, V-block) of the sequential state kernels,
+// for a 1-D grid of ceil(N H / 8) * 8 * VB workgroups. Units (sequence,
+// head) are taken in the order of geo.sorder (longest sequences first, so
+// that the long ones start in the first dispatch round); the VB blocks of a
+// unit get workgroup ids i, i + 8, i + 16, ..., which the dispatcher places
+// on the same XCD (ids go round-robin over the 8 XCDs), so they share that
+// XCD's L2 for the unit's k, q, T, Aqk rows. Returns false for the padding
+// workgroups past the last unit.
+__device__ __forceinline__ bool state_unit(const Geometry& geo, int H, int VB, int& n, int& h, int& vb) {
+  const int i = blockIdx.x;
+  const int uidx = (i / (8 * VB)) * 8 + (i & 7);
+  vb = (i >> 3) % VB;
+  if (uidx >= geo.N * H) return false;
+  const int r = uidx / H;
+  h = uidx - r * H;
+  n = geo.seq_of_rank(r);
+  return true;
+}
+__host__ inline unsigned state_grid(int N, int H, int VB) { return (unsigned)(((N * H + 7) / 8) * 8 * VB); }
 
 }  // namespace gdn

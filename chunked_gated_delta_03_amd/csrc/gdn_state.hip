@@ -78,10 +78,8 @@ __global__ __launch_bounds__((2 * NCB + kLoaders) * 64) void gdn_state_kernel(Fw
   constexpr int NCW = SM::NCW;
   __shared__ SM sm;
 
-  const int unit = blockIdx.x;
-  const int n = unit / a.H;
-  const int h = unit - n * a.H;
-  const int vb = blockIdx.y;
+  int n, h, vb;
+  if (!state_unit(a.geo, a.H, kDim / (16 * NCB), n, h, vb)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -420,7 +418,7 @@ __global__ __launch_bounds__((2 * NCB + kLoaders) * 64) void gdn_state_kernel(Fw
 hipError_t launch_gdn_state(bool store_h, bool compute_o, const FwdArgs& a, hipStream_t stream) {
   const long units = (long)a.geo.N * a.H;
   const bool narrow = units * (kDim / 32) < 256;
-  const dim3 grid1(a.geo.N * a.H, kDim / 16), grid2(a.geo.N * a.H, kDim / 32);
+  const dim3 grid1(state_grid(a.geo.N, a.H, kDim / 16)), grid2(state_grid(a.geo.N, a.H, kDim / 32));
   const dim3 block1(64 * (2 + kLoaders)), block2(64 * (4 + kLoaders));
   if (store_h && !compute_o) {
     if (narrow) hipLaunchKernelGGL((gdn_state_kernel<1, true, false>), grid1, block1, 0, stream, a);

@@ -65,10 +65,8 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
   constexpr int NCW = SM::NCW;
   __shared__ SM sm;
 
-  const int unit = blockIdx.x;
-  const int n = unit / a.H;
-  const int h = unit - n * a.H;
-  const int vb = blockIdx.y;
+  int n, h, vb;
+  if (!state_unit(a.geo, a.H, kDim / (16 * NCB), n, h, vb)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -442,7 +440,7 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
 hipError_t launch_kda_fwd(bool store_h, bool compute_o, const FwdArgs& a, hipStream_t stream) {
   const long units = (long)a.geo.N * a.H;
   const bool narrow = units * (kDim / 32) < 256;
-  const dim3 grid1(a.geo.N * a.H, kDim / 16), grid2(a.geo.N * a.H, kDim / 32);
+  const dim3 grid1(state_grid(a.geo.N, a.H, kDim / 16)), grid2(state_grid(a.geo.N, a.H, kDim / 32));
   const dim3 block1(64 * (2 + kLoadersK)), block2(64 * (4 + kLoadersK));
   if (store_h && !compute_o) {
     if (narrow) hipLaunchKernelGGL((kda_state_kernel<1, true, false>), grid1, block1, 0, stream, a);
