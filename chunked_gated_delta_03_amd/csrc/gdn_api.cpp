@@ -122,11 +122,11 @@ int check_device(int* cus) {
 }
 
 // ---------------------------------------------------------------------------
-// Workspace layout: [tables | tmat | aqk | vec | gk(KDA)], each 256-byte aligned.
+// Workspace layout: [tables | tmat | aqk | vec | kdec(KDA)], each 256-byte aligned.
 // Packed tables: chunk table [NT] int4, sequence table [N] int4, sequence
 // launch order [N] int (padded to whole int4).
 struct Layout {
-  size_t tab = 0, tmat = 0, aqk = 0, vec = 0, gk = 0, total = 0;
+  size_t tab = 0, tmat = 0, aqk = 0, vec = 0, kdec = 0, total = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -145,8 +145,8 @@ Layout layout_for(const Problem& p, bool with_intermediates) {
     L.vec = off;
     off += align256(cmH * GDN_VEC_ROWS * GDN_CHUNK * sizeof(float));
     if (p.kda) {
-      L.gk = off;
-      off += align256(cmH * GDN_CHUNK * GDN_HEAD_DIM * sizeof(float));
+      L.kdec = off;
+      off += align256(cmH * gdn::kKdecElems * sizeof(uint16_t));
     }
   }
   L.total = off;
@@ -361,7 +361,8 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
   pa.tmat = reinterpret_cast<uint16_t*>(W.base + L.tmat);
   pa.aqk = reinterpret_cast<uint16_t*>(W.base + L.aqk);
   pa.vec = reinterpret_cast<float*>(W.base + L.vec);
-  pa.gk = kda ? reinterpret_cast<float*>(W.base + L.gk) : nullptr;
+  pa.gk = nullptr;
+  pa.kdec = kda ? reinterpret_cast<uint16_t*>(W.base + L.kdec) : nullptr;
   pa.geo = geo;
   pa.H = H;
   pa.scale = scale;
@@ -378,7 +379,8 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
   fa.tmat = pa.tmat;
   fa.aqk = pa.aqk;
   fa.vec = pa.vec;
-  fa.gk = pa.gk;
+  fa.gk = nullptr;
+  fa.kdec = pa.kdec;
   fa.s0 = initial_state;
   fa.sfinal = (flags & GDN_OUTPUT_FINAL_STATE) ? final_state : nullptr;
   fa.o = static_cast<uint16_t*>(o);

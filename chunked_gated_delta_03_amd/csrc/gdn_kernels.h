@@ -16,13 +16,25 @@ struct PrepareArgs {
   uint16_t* tmat;  // [H,NT,64,128] bf16 hi | lo, permuted columns
   uint16_t* aqk;   // [H,NT,64,64] bf16, permuted columns
   float* vec;      // [H,NT,8,64]
-  float* gk;       // [H,NT,64,128], KDA only
+  float* gk;       // [H,NT,64,128], KDA stage entry only
+  uint16_t* kdec;  // [H,NT] blocks of kKdecElems, KDA whole pass only (see kda_kdec_*)
   Geometry geo;
   int H;
   float scale;
   uint32_t flags;
   int cus;         // compute units of the device (grid size of persistent launches)
 };
+
+// KDA whole pass: the decayed operands of one (chunk, head), written by the
+// prepare kernel and copied by the state kernel's loaders. bf16 arrays of
+// 64 x 128 in natural column order, then 2^G_last per channel (fp32).
+constexpr int kKdecKdh = 0;                       // k 2^G, hi
+constexpr int kKdecKdl = 1 * kChunk * kDim;       // k 2^G, lo
+constexpr int kKdecKgh = 2 * kChunk * kDim;       // k 2^(G_last - G), hi
+constexpr int kKdecKgl = 3 * kChunk * kDim;       // k 2^(G_last - G), lo
+constexpr int kKdecQd = 4 * kChunk * kDim;        // q 2^G
+constexpr int kKdecDec = 5 * kChunk * kDim;       // 2^G_last, 128 fp32 (256 uint16 slots)
+constexpr int kKdecElems = 5 * kChunk * kDim + 2 * kDim;
 
 struct FwdArgs {
   const uint16_t* q;
@@ -31,7 +43,8 @@ struct FwdArgs {
   const uint16_t* tmat;  // [H,NT,64,128] bf16 hi | lo, permuted columns
   const uint16_t* aqk;   // [H,NT,64,64] bf16, permuted columns
   const float* vec;
-  const float* gk;       // KDA only
+  const float* gk;       // KDA stage entry only
+  const uint16_t* kdec;  // KDA whole pass only
   const float* s0;       // [N,H,K,V] or nullptr
   float* sfinal;         // [N,H,K,V] or nullptr
   uint16_t* o;           // [B*T,H,V]

@@ -642,16 +642,57 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
       const float4 t = reinterpret_cast<const float4*>(sSeg)[s2 * 32 + cq];
       base.x += t.x; base.y += t.y; base.z += t.z; base.w += t.w;
     }
-    float* gdst = a.gk + cm * (kChunk * kDim);
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
       const int r = 8 * sg + rr;
       const float4 G = make_float4(gv[rr].x + base.x, gv[rr].y + base.y, gv[rr].z + base.z, gv[rr].w + base.w);
       *reinterpret_cast<float4*>(sG + r * kLdG + 4 * cq) = G;
-      *reinterpret_cast<float4*>(gdst + r * kDim + 4 * cq) = G;
+      if (a.gk) *reinterpret_cast<float4*>(a.gk + cm * (kChunk * kDim) + r * kDim + 4 * cq) = G;
     }
   }
   __syncthreads();
+
+  // whole pass: the state kernel's decayed operands k 2^G and
+  // k 2^(G_last - G) (bf16 hi + lo), q 2^G (bf16) and 2^G_last per channel.
+  // Thread item (row r, 8 channels from 8 p) per pass, as the q, k loads.
+  if (a.kdec) {
+    uint16_t* kd = a.kdec + cm * kKdecElems;
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int idx = pass * 256 + tid, r = idx >> 4, c0 = (idx & 15) * 8;
+      const uint4 kv = *reinterpret_cast<const uint4*>(sk + r * kLdRow + c0);
+      const uint4 qv = *reinterpret_cast<const uint4*>(sq + r * kLdRow + c0);
+      const float4 g0 = *reinterpret_cast<const float4*>(sG + r * kLdG + c0);
+      const float4 g1 = *reinterpret_cast<const float4*>(sG + r * kLdG + c0 + 4);
+      const float4 l0 = *reinterpret_cast<const float4*>(sG + 63 * kLdG + c0);
+      const float4 l1 = *reinterpret_cast<const float4*>(sG + 63 * kLdG + c0 + 4);
+      const float ga[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const float la[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+      const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, qw[4] = {qv.x, qv.y, qv.z, qv.w};
+      uint32_t dh[4], dl[4], gh[4], gl[4], qq[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float k0 = __uint_as_float(kw[e] << 16), k1 = __uint_as_float(kw[e] & 0xFFFF0000u);
+        const float q0 = __uint_as_float(qw[e] << 16), q1 = __uint_as_float(qw[e] & 0xFFFF0000u);
+        const float f0 = exp2f(ga[2 * e]), f1 = exp2f(ga[2 * e + 1]);
+        const float d0 = exp2f(la[2 * e] - ga[2 * e]), d1 = exp2f(la[2 * e + 1] - ga[2 * e + 1]);
+        split2(k0 * f0, k1 * f1, dh[e], dl[e]);
+        split2(k0 * d0, k1 * d1, gh[e], gl[e]);
+        qq[e] = pack2(q0 * f0, q1 * f1);
+      }
+      const int off = r * kDim + c0;
+      *reinterpret_cast<uint4*>(kd + kKdecKdh + off) = make_uint4(dh[0], dh[1], dh[2], dh[3]);
+      *reinterpret_cast<uint4*>(kd + kKdecKdl + off) = make_uint4(dl[0], dl[1], dl[2], dl[3]);
+      *reinterpret_cast<uint4*>(kd + kKdecKgh + off) = make_uint4(gh[0], gh[1], gh[2], gh[3]);
+      *reinterpret_cast<uint4*>(kd + kKdecKgl + off) = make_uint4(gl[0], gl[1], gl[2], gl[3]);
+      *reinterpret_cast<uint4*>(kd + kKdecQd + off) = make_uint4(qq[0], qq[1], qq[2], qq[3]);
+    }
+    if (tid < 32) {
+      const float4 l = *reinterpret_cast<const float4*>(sG + 63 * kLdG + 4 * tid);
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(kd + kKdecDec) + 4 * tid) =
+          make_float4(exp2f(l.x), exp2f(l.y), exp2f(l.z), exp2f(l.w));
+    }
+  }
 
   // Gram tiles. Lane (l16, g4) of an MFMA step s covers channels
   // 32 s + 8 g4 .. + 7 of operand row/column l16. Products of rows scaled

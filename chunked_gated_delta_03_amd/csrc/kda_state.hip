@@ -5,7 +5,9 @@
 //     held by a pair of waves, one per half of the K rows (64 x 16 each, in
 //     MFMA accumulators); the pair exchanges its partial K-contractions
 //     through LDS, as in the GDN state kernel;
-//   - kLoaders loader waves that form the chunk's decayed operands.
+//   - kLoaders loader waves that stage the chunk's decayed operands: in the
+//     whole pass they copy them from the prepare kernel's output; in the
+//     stage entry they form them from k, q and the cumulative gate.
 //
 // Per chunk, with S (K x V) the state entering it, G the chunk-local
 // cumulative log2 gate per channel (written by the prepare kernel) and
@@ -75,7 +77,90 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
   const int last = si.nch - 1;
 
   // ------------------------------------------------------------- loaders
+  if constexpr (COMPUTE_O) {
+    if (w >= NCW) {
+      // Whole pass: the decayed operands come from the prepare kernel; the
+      // loaders copy them (16-byte pieces, loaded one chunk ahead) into the
+      // same windows as below.
+      constexpr int NL = 64 * kLoadersK;
+      constexpr int PPR = BV / 8;
+      const int ltid = tid - NCW * 64;
+      const int pc = ltid & 15;
+      u32x4 dh[1024 / NL], dl[1024 / NL], qq[1024 / NL], gh[1024 / NL], gl[1024 / NL], tr[1024 / NL];
+      u32x4 ar[512 / NL], vr, er, dr;
+      auto fetch = [&](int jc) {
+        const int tok0 = si.tok0 + jc * kChunk;
+        const int rem = si.len - jc * kChunk;
+        const int len = rem < kChunk ? rem : kChunk;
+        const size_t cm = (size_t)h * a.geo.NT + si.c0 + jc;
+        const uint16_t* kd = a.kdec + cm * kKdecElems;
+#pragma unroll
+        for (int p = 0; p < 1024 / NL; ++p) {
+          const int idx = p * NL + ltid;
+          dh[p] = reinterpret_cast<const u32x4*>(kd + kKdecKdh)[idx];
+          dl[p] = reinterpret_cast<const u32x4*>(kd + kKdecKdl)[idx];
+          qq[p] = reinterpret_cast<const u32x4*>(kd + kKdecQd)[idx];
+          gh[p] = reinterpret_cast<const u32x4*>(kd + kKdecKgh)[idx];
+          gl[p] = reinterpret_cast<const u32x4*>(kd + kKdecKgl)[idx];
+          tr[p] = reinterpret_cast<const u32x4*>(a.tmat + cm * (kChunk * 2 * kChunk))[idx];
+        }
+#pragma unroll
+        for (int p = 0; p < 512 / NL; ++p) ar[p] = reinterpret_cast<const u32x4*>(a.aqk + cm * (kChunk * kChunk))[p * NL + ltid];
+        if (ltid < 64 * PPR) {
+          const int r = ltid / PPR;
+          vr = r < len ? *reinterpret_cast<const u32x4*>(a.v + ((size_t)(tok0 + r) * H + h) * kDim + vb * BV + 8 * (ltid % PPR))
+                       : u32x4{0, 0, 0, 0};
+        }
+        if (ltid < kVecRows * kChunk / 4) er = reinterpret_cast<const u32x4*>(a.vec + cm * (kVecRows * kChunk))[ltid];
+        if (ltid < kDim / 4) dr = reinterpret_cast<const u32x4*>(kd + kKdecDec)[ltid];
+      };
+      auto put_early = [&]() {  // kd, qd of the fetched chunk
+#pragma unroll
+        for (int p = 0; p < 1024 / NL; ++p) {
+          const int idx = p * NL + ltid, r = idx >> 4;
+          const int slot = 8 * (pc ^ (r & 15));
+          *reinterpret_cast<u32x4*>(sm.kdh + r * kDim + slot) = dh[p];
+          *reinterpret_cast<u32x4*>(sm.kdl + r * kDim + slot) = dl[p];
+          *reinterpret_cast<u32x4*>(sm.qd + r * kDim + slot) = qq[p];
+        }
+      };
+      auto put_late = [&]() {  // kg, T, Aqk, v, row vectors, channel decays
+#pragma unroll
+        for (int p = 0; p < 1024 / NL; ++p) {
+          const int idx = p * NL + ltid, r = idx >> 4;
+          const int slot = 8 * (pc ^ (r & 15));
+          *reinterpret_cast<u32x4*>(sm.kgh + r * kDim + slot) = gh[p];
+          *reinterpret_cast<u32x4*>(sm.kgl + r * kDim + slot) = gl[p];
+          *reinterpret_cast<u32x4*>(sm.t + r * (2 * kChunk) + slot) = tr[p];
+        }
+#pragma unroll
+        for (int p = 0; p < 512 / NL; ++p) {
+          const int idx = p * NL + ltid, r = idx >> 3;
+          *reinterpret_cast<u32x4*>(sm.aqk + r * kChunk + 8 * ((idx & 7) ^ (r & 7))) = ar[p];
+        }
+        if (ltid < 64 * PPR) *reinterpret_cast<u32x4*>(sm.v + 8 * ltid) = vr;
+        if (ltid < kVecRows * kChunk / 4) *reinterpret_cast<u32x4*>(sm.vec + 4 * ltid) = er;
+        if (ltid < kDim / 4) *reinterpret_cast<u32x4*>(sm.dec + 4 * ltid) = dr;
+      };
+      // same barrier sequence and windows as the stage loaders below
+      if (si.nch > 0) {
+        fetch(0);
+        put_early();
+      }
+      __syncthreads();
+      for (int jc = 0; jc < si.nch; ++jc) {
+        put_late();
+        fetch(min(jc + 1, last));
+        __syncthreads();
+        put_early();
+        __syncthreads();
+      }
+      return;
+    }
+  }
   if (w >= NCW) {
+    // Stage entry: the loaders form the decayed operands from k, q and the
+    // cumulative gate.
     constexpr int NL = 64 * kLoadersK;
     constexpr int PPR = BV / 8;              // v pieces per row
     const int ltid = tid - NCW * 64;
