@@ -101,6 +101,6 @@ def recur(inp, units: Optional[Sequence[tuple]] = None, flags: Optional[int] = N
     return o, fs
 
 
-from .chunk import chunk, decode_bf16, l2norm  # noqa: E402  (pure numpy, no C)
+from .chunk import apply_state_summary, chunk, decode_bf16, l2norm, state_summary  # noqa: E402  (pure numpy, no C)
 
 __all__ = ["build", "recur", "chunk", "decode_bf16", "l2norm", "num_threads", "L2NORM", "BETA_SIGMOID"]

@@ -208,3 +208,51 @@ def chunk(inp, chunk_size: int = 64, flags: Optional[int] = None, keep: bool = F
                 inter.update(_row_vectors(sl(beta), sl(rq), sl(rk), chunk_size))
             inters.append(inter)
     return o_all, fs, (inters if keep else None)
+
+
+def state_summary(inp, chunk_size: int = 64, flags: Optional[int] = None):
+    """Affine state summary ``state_out = M state_in + S`` of every sequence.
+
+    Follows ``_compute_gdn_state_summary_from_prepared`` (2026-09-10 page):
+    starting from ``S = 0`` and ``M = I``, for each chunk in order,
+    ``transition = decay I - (k * e^{G_last - G})^T W`` and
+    ``S <- transition S + (k * e^{G_last - G})^T U``, ``M <- transition M``,
+    with W, U the chunk form's WY terms. For KDA the decay is
+    ``diag(2^{G_last})`` and the key decay per channel (the reading of the
+    chunk form above). The initial state of ``inp`` is ignored.
+
+    Returns ``(M, S)``: fp64 [N,H,K,K] and [N,H,K,V].
+    """
+    zero = type(inp)(**{**inp.__dict__, "initial_state": None})
+    _, _, inters = chunk(zero, chunk_size=chunk_size, flags=flags, keep=True)
+    Ms, Ss = [], []
+    for it in inters:
+        G, W, U, kk = it["G"], it["W"], it["U"], it["k"]
+        Bn, H, NC = G.shape[:3]
+        K = kk.shape[-1]
+        V = U.shape[-1]
+        M = np.broadcast_to(np.eye(K), (Bn, H, K, K)).copy()
+        S = np.zeros((Bn, H, K, V))
+        for c in range(NC):
+            Gc = G[:, :, c]
+            if inp.kda:
+                kd = kk[:, :, c] * np.exp2(Gc[:, :, -1:, :] - Gc)
+                decay = np.eye(K) * np.exp2(Gc[:, :, -1, :])[..., None, :]
+            else:
+                kd = kk[:, :, c] * np.exp(Gc[..., -1:] - Gc)[..., None]
+                decay = np.exp(Gc[..., -1])[..., None, None] * np.eye(K)
+            kdt = np.swapaxes(kd, -1, -2)
+            trans = decay - kdt @ W[:, :, c]
+            S = trans @ S + kdt @ U[:, :, c]
+            M = trans @ M
+        Ms.append(M)
+        Ss.append(S)
+    return np.concatenate(Ms, axis=0), np.concatenate(Ss, axis=0)
+
+
+def apply_state_summary(M: np.ndarray, S: np.ndarray, state_in: Optional[np.ndarray]) -> np.ndarray:
+    """``state_out = M state_in + S`` (``_apply_gdn_state_summary``, 2026-09-10
+    page); ``state_in`` None means zero."""
+    if state_in is None:
+        return np.asarray(S, dtype=np.float64).copy()
+    return np.asarray(M, dtype=np.float64) @ np.asarray(state_in, dtype=np.float64) + S

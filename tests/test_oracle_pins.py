@@ -278,3 +278,48 @@ def test_unit_subset_matches_full_run(oracle_lib):
         np.testing.assert_array_equal(ou[n, :, h], o[n, :, h])
         np.testing.assert_array_equal(su[n, h], s[n, h])
     assert np.abs(ou[1]).max() == 0.0
+
+
+def _segment(inp, a, b):
+    """Tokens a..b-1 of a dense single-sequence problem, no initial state."""
+    sl = lambda x: np.ascontiguousarray(x[:, a:b])
+    return gi.GdnInputs(**{**inp.__dict__, "T": b - a, "q": sl(inp.q), "k": sl(inp.k), "v": sl(inp.v),
+                           "g": sl(inp.g), "beta": sl(inp.beta), "initial_state": None})
+
+
+@pytest.mark.parametrize("kda", [False, True])
+@pytest.mark.parametrize("packed", [False, True])
+def test_state_summary_against_recurrence(oracle_lib, kda, packed):
+    """oracle.state_summary (``_compute_gdn_state_summary_from_prepared``): S
+    equals the token recurrence's final state from a zero state, and
+    M S0 + S its final state from S0 (so M is the exact transition); the apply
+    step reproduces the latter. A wrong transition term (decay, key decay, W)
+    or a wrong chunk order fails one of them."""
+    rng = np.random.default_rng(31 + kda + 2 * packed)
+    H, K, V, C = 2, 16, 8, 16
+    cu = np.asarray([0, 7, 40, 100], dtype=np.int32) if packed else None
+    inp = gi.random_problem(rng, 1, 100, H, K, V, kda=kda, with_initial_state=True, gate_scale=0.05,
+                            cu_seqlens=cu)
+    M, S = oracle.state_summary(inp, chunk_size=C)
+    zero = gi.GdnInputs(**{**inp.__dict__, "initial_state": None})
+    _, s_zero = oracle.recur(zero)
+    _, s_with = oracle.recur(inp)
+    assert _rel(S, s_zero) < 1e-10
+    assert _rel(M @ inp.initial_state.astype(np.float64) + S, s_with) < 1e-10
+    assert _rel(oracle.apply_state_summary(M, S, inp.initial_state), s_with) < 1e-10
+    assert np.abs(M - np.eye(K)).max() > 1e-2      # not trivially the identity
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_state_summary_composes_over_segments(oracle_lib, kda):
+    """Sequence-parallel use of the summary: the final state of a sequence
+    equals the second segment's summary applied to the first segment's final
+    state (segments split at a chunk boundary and mid-chunk)."""
+    rng = np.random.default_rng(41 + kda)
+    H, K, V, C = 2, 16, 8, 16
+    inp = gi.random_problem(rng, 1, 90, H, K, V, kda=kda, gate_scale=0.05)
+    _, s_full = oracle.recur(inp)
+    for t0 in (32, 45):
+        _, s_a = oracle.recur(_segment(inp, 0, t0))
+        M, S = oracle.state_summary(_segment(inp, t0, 90), chunk_size=C)
+        assert _rel(oracle.apply_state_summary(M, S, s_a), s_full) < 1e-10
