@@ -88,6 +88,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gdn", choices=["gdn", "varlen", "long", "kda", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", default="fwd", choices=["fwd", "summary"],
+                    help="fwd: the forward pass (default); summary: the affine state summary and its apply step")
     ap.add_argument("--scrub-mib", type=int, default=1024, help="MiB read between timed calls (0: none)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run plain device-to-device copies of this many MiB (counter calibration)")
@@ -105,6 +107,62 @@ def calibrate_copy(mib: int, reps: int = 5) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps}), flush=True)
+
+
+def bench_summary(args, gdn, gi, inp, q, k, v, g, beta, dev):
+    """Times gdn_state_summary / kda_state_summary on the workload (prepare and
+    the two state-only passes) and the apply step over its (sequence, head)
+    pairs, each call after a 1 GiB read; prints one JSON line."""
+    import torch
+    B, T, H, K, V = inp.B, inp.T, inp.H, inp.K, inp.V
+    N = inp.num_seqs
+    kw = dict(q=q, cu_seqlens=inp.cu_seqlens, kda=inp.kda, l2norm_qk=bool(inp.flags & gi.FLAG_L2NORM_QK),
+              beta_sigmoid=bool(inp.flags & gi.FLAG_BETA_SIGMOID))
+    M, S = gdn.state_summary(k, v, g, beta, **kw)
+    need = gdn.lib.gdn_state_summary_workspace_bytes(int(inp.kda), B, T, H, K, V, N, None if inp.cu_seqlens is None
+                                                     else np.ascontiguousarray(inp.cu_seqlens, dtype=np.int32)
+                                                     .ctypes.data_as(ctypes.c_void_p))
+    ws = torch.empty(int(need), dtype=torch.uint8, device=dev)
+    s_in = torch.randn((N, H, K, V), device=dev) * 0.02
+    out = torch.empty_like(S)
+    scrub = torch.full((max(args.scrub_mib, 1) * (1 << 20) // 4,), 1.0, dtype=torch.float32, device=dev)
+
+    def timed(fn, n):
+        ts = []
+        for _ in range(n):
+            if args.scrub_mib:
+                scrub.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
+
+    summ = lambda: gdn.state_summary(k, v, g, beta, workspace=ws, **kw)
+    app = lambda: gdn.state_summary_apply(M, S, s_in, out=out)
+    for _ in range(args.warmup):
+        summ()
+        app()
+    torch.cuda.synchronize()
+    ms, p10, p90 = timed(summ, args.steps)
+    ams, _, _ = timed(app, args.steps)
+    tokens = B * T
+    kind = "KDA" if inp.kda else "GDN"
+    line = {
+        "metric": "state summary tokens/s",
+        "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "%s state summary (M, S) B=%d T=%d H=%d, %d sequences" % (kind, B, T, H, N),
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": K, "parallelism": "single-gpu"},
+        "timing": {"per_call": "median of %d calls, %d MiB read before each" % (args.steps, args.scrub_mib),
+                   "p10_ms": round(p10, 5), "p90_ms": round(p90, 5)},
+        "apply_us": round(ams * 1e3, 2),
+        "apply_pairs": N * H,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def main():
@@ -138,6 +196,9 @@ def main():
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     cu = None if inp.cu_seqlens is None else np.ascontiguousarray(inp.cu_seqlens, dtype=np.int32)
     cu_p = None if cu is None else cu.ctypes.data_as(ctypes.c_void_p)
+    if args.op == "summary":
+        bench_summary(args, gdn, gi, inp, q, k, v, g, beta, dev)
+        return
     stream = torch.cuda.current_stream(dev)
     fn = gdn.lib.kda_chunk_fwd if inp.kda else gdn.lib.gdn_chunk_fwd
     P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())

@@ -34,7 +34,8 @@ VEC_ROWS = 8
 EXPORTED = (
     "gdn_last_error", "gdn_num_chunks", "gdn_chunk_fwd_workspace_bytes", "kda_chunk_fwd_workspace_bytes",
     "gdn_chunk_fwd", "kda_chunk_fwd", "gdn_stage_prepare", "gdn_stage_fwd_h", "gdn_stage_finalize",
-    "gdn_timing_enable", "gdn_timing_read",
+    "gdn_timing_enable", "gdn_timing_read", "gdn_state_summary", "kda_state_summary",
+    "gdn_state_summary_workspace_bytes", "gdn_state_summary_apply",
 )
 
 
@@ -69,6 +70,14 @@ def _load() -> ctypes.CDLL:
     lib.gdn_timing_read.restype = ctypes.c_int
     lib.gdn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_int64)]
+    for name in ("gdn_state_summary", "kda_state_summary"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, u32, p, p, p, sz, p]
+    lib.gdn_state_summary_workspace_bytes.restype = sz
+    lib.gdn_state_summary_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, p]
+    lib.gdn_state_summary_apply.restype = ctypes.c_int
+    lib.gdn_state_summary_apply.argtypes = [p, p, p, p, i32, i32, i32, i32, p]
     lib.gdn_stage_prepare.restype = ctypes.c_int
     lib.gdn_stage_prepare.argtypes = [i32, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p, p, p, p]
     lib.gdn_stage_fwd_h.restype = ctypes.c_int
@@ -201,6 +210,50 @@ def kda_chunk_fwd(q, k, v, g, beta, scale: Optional[float] = None, initial_state
     """KDA forward: as :func:`gdn_chunk_fwd` with g fp32 [B,T,H,128] in log2 units."""
     return _chunk_fwd(True, q, k, v, g, beta, scale, initial_state, cu_seqlens, l2norm_qk, beta_sigmoid,
                       output_final_state, workspace, stream)
+
+
+def state_summary(k, v, g, beta, q=None, cu_seqlens=None, kda: bool = False, l2norm_qk: bool = False,
+                  beta_sigmoid: bool = False, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Affine state summary of every (sequence, head): final = M @ initial + S.
+    Inputs as :func:`gdn_chunk_fwd` / :func:`kda_chunk_fwd` (q optional, unused).
+    Returns (M fp32 [N,H,128,128], S fp32 [N,H,128,128])."""
+    cu = _cu_array(cu_seqlens)
+    B, T, H, K, V, N = _check_inputs(k if q is None else q, k, v, g, beta, kda, None, cu)
+    flags = _flags(l2norm_qk, beta_sigmoid, False)
+    M = torch.empty((N, H, K, K), dtype=torch.float32, device=k.device)
+    S = torch.empty((N, H, K, V), dtype=torch.float32, device=k.device)
+    need = lib.gdn_state_summary_workspace_bytes(int(kda), B, T, H, K, V, N, _cu_ptr(cu))
+    if need == 0:
+        workspace = None
+    elif workspace is None:
+        workspace = torch.empty(int(need), dtype=torch.uint8, device=k.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel() * workspace.element_size(), need))
+    fn = lib.kda_state_summary if kda else lib.gdn_state_summary
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _cu_ptr(cu), N, B, T, H, K, V, flags,
+              _ptr(M), _ptr(S), _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+              _stream_ptr(k.device, stream)))
+    return M, S
+
+
+def state_summary_apply(M: torch.Tensor, S: torch.Tensor, state_in: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """state_out = M @ state_in + S per (sequence, head); fp32 [N,H,128,128] device tensors."""
+    for name, t in (("M", M), ("S", S), ("state_in", state_in), ("out", out)):
+        if t is None:
+            continue
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 4 or t.device.type != "cuda":
+            raise ValueError("%s must be a contiguous fp32 [N,H,128,128] tensor on the GPU" % name)
+        if tuple(t.shape) != tuple(S.shape) or t.device != S.device:
+            raise ValueError("%s has shape %s on %s; S has %s on %s" % (name, tuple(t.shape), t.device,
+                                                                        tuple(S.shape), S.device))
+    N, H, K, V = S.shape
+    if out is None:
+        out = torch.empty_like(S)
+    _check(lib.gdn_state_summary_apply(_ptr(M), _ptr(S), _ptr(state_in), _ptr(out), N, H, K, V,
+                                       _stream_ptr(S.device, stream)))
+    return out
 
 
 def workspace_bytes(B, T, H, cu_seqlens=None, kda: bool = False, flags: int = 0) -> int:

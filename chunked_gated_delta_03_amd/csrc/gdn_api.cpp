@@ -131,7 +131,9 @@ struct Layout {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Layout layout_for(const Problem& p, bool with_intermediates) {
+// kda_gate: a KDA pass whose state kernel forms the decayed operands from the
+// cumulative gate (state summary) instead of reading them from prepare.
+Layout layout_for(const Problem& p, bool with_intermediates, bool kda_gate = false) {
   Layout L;
   size_t off = 0;
   L.tab = off;
@@ -146,7 +148,8 @@ Layout layout_for(const Problem& p, bool with_intermediates) {
     off += align256(cmH * GDN_VEC_ROWS * GDN_CHUNK * sizeof(float));
     if (p.kda) {
       L.kdec = off;
-      off += align256(cmH * gdn::kKdecElems * sizeof(uint16_t));
+      off += align256(kda_gate ? cmH * GDN_CHUNK * GDN_HEAD_DIM * sizeof(float)
+                               : cmH * gdn::kKdecElems * sizeof(uint16_t));
     }
   }
   L.total = off;
@@ -392,6 +395,74 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
   return GDN_OK;
 }
 
+// State summary of every (sequence, head): prepare, then the state-only
+// pass twice: from S0 = 0 with v (S), and from S0 = I with v = 0 (M).
+int state_summary(bool kda, const void* q, const void* k, const void* v, const float* g, const void* beta,
+                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+                  int32_t V, uint32_t flags, float* transition, float* state_ext, void* workspace,
+                  size_t workspace_bytes, void* stream_ptr) {
+  g_last_error.clear();
+  Problem p;
+  p.kda = kda;
+  int rc = check_shape(B, T, H, K, V, num_seqs, cu_seqlens, p);
+  if (rc) return rc;
+  rc = check_common(q ? q : k, k, v, g, beta, 1.0f, flags);
+  if (rc) return rc;
+  if (!transition || !state_ext) return fail(GDN_ERR_INVALID_ARGUMENT, "transition and state_ext must be non-NULL");
+  int cus = 0;
+  rc = check_device(&cus);
+  if (rc) return rc;
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const Layout L = layout_for(p, true, true);
+  Workspace W;
+  rc = acquire_workspace(workspace, workspace_bytes, L.total, stream, W);
+  if (rc) return rc;
+  if (p.packed) {
+    rc = upload_tables(p, W.base + L.tab, stream);
+    if (rc) return rc;
+  }
+  const gdn::Geometry geo = make_geometry(p, W.base + L.tab);
+
+  gdn::PrepareArgs pa{};
+  pa.q = static_cast<const uint16_t*>(q ? q : k);  // only the unused Aqk depends on q
+  pa.k = static_cast<const uint16_t*>(k);
+  pa.g = g;
+  pa.beta = static_cast<const uint16_t*>(beta);
+  pa.tmat = reinterpret_cast<uint16_t*>(W.base + L.tmat);
+  pa.aqk = reinterpret_cast<uint16_t*>(W.base + L.aqk);
+  pa.vec = reinterpret_cast<float*>(W.base + L.vec);
+  pa.gk = kda ? reinterpret_cast<float*>(W.base + L.kdec) : nullptr;
+  pa.kdec = nullptr;
+  pa.geo = geo;
+  pa.H = H;
+  pa.scale = 1.0f;
+  pa.flags = flags & ~(uint32_t)GDN_OUTPUT_FINAL_STATE;
+  pa.cus = cus;
+  hipError_t e = gdn::launch_prepare(kda, pa, stream);
+  if (e != hipSuccess) return hip_fail(e, "prepare launch");
+
+  gdn::FwdArgs fa{};
+  fa.k = pa.k;
+  fa.v = static_cast<const uint16_t*>(v);
+  fa.tmat = pa.tmat;
+  fa.aqk = pa.aqk;
+  fa.vec = pa.vec;
+  fa.gk = pa.gk;
+  fa.s0 = nullptr;
+  fa.sfinal = state_ext;
+  fa.geo = geo;
+  fa.H = H;
+  fa.s_identity = 0;
+  e = gdn::launch_fwd(kda, false, false, fa, stream);
+  if (e != hipSuccess) return hip_fail(e, "state pass launch");
+  fa.sfinal = transition;
+  fa.s_identity = 1;
+  e = gdn::launch_fwd(kda, false, false, fa, stream);
+  if (e != hipSuccess) return hip_fail(e, "transition pass launch");
+  return GDN_OK;
+}
+
 // Shared front half of the stage entries: validation, tables, geometry.
 struct StageCtx {
   Problem p;
@@ -472,6 +543,51 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   void* workspace, size_t workspace_bytes, void* stream) {
   return chunk_fwd(true, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, scale, flags, o,
                    final_state, workspace, workspace_bytes, stream);
+}
+
+int gdn_state_summary(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                      const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+                      int32_t V, uint32_t flags, float* transition, float* state_ext, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return state_summary(false, q, k, v, g, beta, cu_seqlens, num_seqs, B, T, H, K, V, flags, transition, state_ext,
+                       workspace, workspace_bytes, stream);
+}
+
+int kda_state_summary(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                      const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+                      int32_t V, uint32_t flags, float* transition, float* state_ext, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return state_summary(true, q, k, v, g, beta, cu_seqlens, num_seqs, B, T, H, K, V, flags, transition, state_ext,
+                       workspace, workspace_bytes, stream);
+}
+
+size_t gdn_state_summary_workspace_bytes(int32_t kda, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                         int32_t num_seqs, const int32_t* cu_seqlens) {
+  g_last_error.clear();
+  Problem p;
+  p.kda = kda != 0;
+  if (check_shape(B, T, H, K, V, num_seqs, cu_seqlens, p)) return 0;
+  return layout_for(p, true, true).total;
+}
+
+int gdn_state_summary_apply(const float* transition, const float* state_ext, const float* state_in,
+                            float* state_out, int32_t N, int32_t H, int32_t K, int32_t V, void* stream) {
+  g_last_error.clear();
+  if (!transition || !state_ext || !state_out)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "transition, state_ext and state_out must be non-NULL");
+  if (N <= 0 || H <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "N and H must be positive (got %d, %d)", N, H);
+  if (K != GDN_HEAD_DIM || V != GDN_HEAD_DIM)
+    return fail(GDN_ERR_UNSUPPORTED, "K and V must be %d (got %d, %d)", GDN_HEAD_DIM, K, V);
+  if (!aligned16(transition) || !aligned16(state_ext) || !aligned16(state_out) || (state_in && !aligned16(state_in)))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "state arrays must be 16-byte aligned");
+  if (state_out == transition || state_out == state_in)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "state_out must not alias transition or state_in");
+  int rc = check_device(nullptr);
+  if (rc) return rc;
+  hipError_t e = gdn::launch_summary_apply(transition, state_ext, state_in, state_out, (long)N * H,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "summary apply launch");
+  return GDN_OK;
 }
 
 int gdn_timing_enable(int32_t enable) {

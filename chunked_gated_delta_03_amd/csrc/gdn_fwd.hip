@@ -91,6 +91,49 @@ __global__ __launch_bounds__(256) void gdn_finalize_kernel(FinArgs a) {
   }
 }
 
+// State summary apply, state_out = M state_in + S per (sequence, head)
+// (_apply_gdn_state_summary on the 2026-09-10 coverage page), fp32. One WG
+// per (unit, 16 rows of the output): the 16 rows of M are staged in LDS,
+// thread (column c, row parity) accumulates 8 rows over the 128 contraction
+// indices in order; state_in nullptr means zero.
+__global__ __launch_bounds__(256) void summary_apply_kernel(const float* M, const float* S, const float* sin,
+                                                            float* sout) {
+  __shared__ __attribute__((aligned(16))) float sM[16 * kDim];
+  const size_t u = blockIdx.x;
+  const int r0 = 16 * blockIdx.y;
+  const int tid = threadIdx.x;
+  const float* Mu = M + u * kDim * kDim;
+  const float* Su = S + u * kDim * kDim;
+  float* Ou = sout + u * kDim * kDim;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int idx = p * 256 + tid;  // float4 index inside the 16 x 128 block
+    reinterpret_cast<float4*>(sM)[idx] = reinterpret_cast<const float4*>(Mu + (size_t)r0 * kDim)[idx];
+  }
+  __syncthreads();
+  const int c = tid & 127, rs = tid >> 7;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (sin) {
+    const float* Iu = sin + u * kDim * kDim;
+    for (int kk = 0; kk < kDim; ++kk) {
+      const float x = Iu[(size_t)kk * kDim + c];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(sM[(rs + 2 * i) * kDim + kk], x, acc[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const size_t off = (size_t)(r0 + rs + 2 * i) * kDim + c;
+    Ou[off] = acc[i] + Su[off];
+  }
+}
+
+hipError_t launch_summary_apply(const float* M, const float* S, const float* sin, float* sout, long units,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(summary_apply_kernel, dim3((unsigned)units, kDim / 16), dim3(256), 0, stream, M, S, sin, sout);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd(bool kda, bool store_h, bool compute_o, const FwdArgs& a, hipStream_t stream) {
   if (kda) return launch_kda_fwd(store_h, compute_o, a, stream);
   return launch_gdn_state(store_h, compute_o, a, stream);

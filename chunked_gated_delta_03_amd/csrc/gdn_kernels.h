@@ -52,6 +52,7 @@ struct FwdArgs {
   float* vnew_out;       // [H,NT,64,V]  (stage mode)
   Geometry geo;
   int H;
+  int s_identity;        // state summary transition: S0 = I and v taken as 0 (s0 ignored)
 };
 
 struct FinArgs {
@@ -73,5 +74,7 @@ hipError_t launch_finalize(bool kda, const FinArgs& a, hipStream_t stream);
 hipError_t launch_gdn_state(bool store_h, bool compute_o, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_kda_fwd(bool store_h, bool compute_o, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_kda_finalize(const FinArgs& a, hipStream_t stream);
+hipError_t launch_summary_apply(const float* M, const float* S, const float* sin, float* sout, long units,
+                                hipStream_t stream);
 
 }  // namespace gdn

@@ -108,7 +108,7 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
         for (int p = 0; p < 512 / NL; ++p) ar[p] = reinterpret_cast<const u32x4*>(a.aqk + cm * (kChunk * kChunk))[p * NL + ltid];
         if (ltid < 64 * PPR) {
           const int r = ltid / PPR;
-          vr = r < len ? *reinterpret_cast<const u32x4*>(a.v + ((size_t)(tok0 + r) * H + h) * kDim + vb * BV + 8 * (ltid % PPR))
+          vr = (r < len && !a.s_identity) ? *reinterpret_cast<const u32x4*>(a.v + ((size_t)(tok0 + r) * H + h) * kDim + vb * BV + 8 * (ltid % PPR))
                        : u32x4{0, 0, 0, 0};
         }
         if (ltid < kVecRows * kChunk / 4) er = reinterpret_cast<const u32x4*>(a.vec + cm * (kVecRows * kChunk))[ltid];
@@ -196,7 +196,7 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
       }
       if (ltid < 64 * PPR) {
         const int r = ltid / PPR;
-        vr = r < len ? *reinterpret_cast<const u32x4*>(a.v + ((size_t)(tok0 + r) * H + h) * kDim + vb * BV + 8 * (ltid % PPR))
+        vr = (r < len && !a.s_identity) ? *reinterpret_cast<const u32x4*>(a.v + ((size_t)(tok0 + r) * H + h) * kDim + vb * BV + 8 * (ltid % PPR))
                      : u32x4{0, 0, 0, 0};
       }
       if (ltid < kVecRows * kChunk / 4) er = reinterpret_cast<const u32x4*>(a.vec + cm * (kVecRows * kChunk))[ltid];
@@ -299,7 +299,9 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[t][e] = a.s0 ? a.s0[sbase + (size_t)srow(t, e) * kDim + colw + l16] : 0.0f;
+      for (int e = 0; e < 4; ++e)
+        S[t][e] = a.s_identity ? (srow(t, e) == colw + l16 ? 1.0f : 0.0f)
+                               : (a.s0 ? a.s0[sbase + (size_t)srow(t, e) * kDim + colw + l16] : 0.0f);
     const int trG = lane >> 4, trJ = (lane >> 2) & 3, trQ = lane & 3;
     f32x4* xmine = &sm.xch[w][0][0];
     const f32x4* xpart = &sm.xch[w ^ 1][0][0];
@@ -533,6 +535,9 @@ hipError_t launch_kda_fwd(bool store_h, bool compute_o, const FwdArgs& a, hipStr
   } else if (!store_h && compute_o) {
     if (narrow) hipLaunchKernelGGL((kda_state_kernel<1, false, true>), grid1, block1, 0, stream, a);
     else hipLaunchKernelGGL((kda_state_kernel<2, false, true>), grid2, block2, 0, stream, a);
+  } else if (!store_h && !compute_o) {  // state only (state summary)
+    if (narrow) hipLaunchKernelGGL((kda_state_kernel<1, false, false>), grid1, block1, 0, stream, a);
+    else hipLaunchKernelGGL((kda_state_kernel<2, false, false>), grid2, block2, 0, stream, a);
   } else {
     return hipErrorInvalidValue;
   }

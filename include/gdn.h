@@ -170,6 +170,47 @@ int gdn_stage_finalize(int32_t kda, const void* q, const void* aqk, const float*
                        const float* h, const float* v_new, const int32_t* cu_seqlens, int32_t num_seqs,
                        int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, void* o, void* stream);
 
+/*
+ * Affine state summary (_compute_gdn_state_summary_from_prepared and
+ * _apply_gdn_state_summary on the 2026-09-10 "Diff Coverage" page): for every
+ * sequence n and head h, the final state is affine in the initial one,
+ *   S_final = M S_initial + S,
+ * with M [K,K] the product over the chunks, in order, of the chunk
+ * transitions decay*I - (k * decay_to_end)^T W (KDA: diag(2^G_last) and the
+ * per-channel key decay), and S [K,V] the final state from a zero initial
+ * state. Segments of one long sequence can then be processed independently
+ * and chained by the apply step (the single-GPU half of sequence-parallel
+ * processing).
+ *
+ * gdn_state_summary / kda_state_summary: inputs as gdn_chunk_fwd /
+ *   kda_chunk_fwd (q may be NULL: no output is formed, so q and the scale
+ *   are not used). flags: GDN_L2NORM_QK and GDN_BETA_SIGMOID as there;
+ *   GDN_OUTPUT_FINAL_STATE is ignored. Outputs (device, fp32, caller-owned):
+ *     transition [N,H,K,K]  M, row-major (M[i][j] multiplies S_initial[j][:]);
+ *     state_ext  [N,H,K,V]  S.
+ *   Runs the prepare kernel, then the state-only pass twice (from a zero
+ *   state with v, and from the identity with v taken as zero). workspace as
+ *   for gdn_chunk_fwd, sized by gdn_state_summary_workspace_bytes (0 on a
+ *   contract error). Errors as gdn_chunk_fwd; nothing is launched on error.
+ *
+ * gdn_state_summary_apply: state_out = transition @ state_in + state_ext for
+ *   N*H (sequence, head) pairs, fp32 (device arrays, 16-byte aligned,
+ *   caller-owned; state_in NULL means zero; state_out may be state_ext but
+ *   not transition or state_in). K = V = 128.
+ */
+int gdn_state_summary(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                      const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+                      int32_t V, uint32_t flags, float* transition, float* state_ext, void* workspace,
+                      size_t workspace_bytes, void* stream);
+int kda_state_summary(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                      const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+                      int32_t V, uint32_t flags, float* transition, float* state_ext, void* workspace,
+                      size_t workspace_bytes, void* stream);
+size_t gdn_state_summary_workspace_bytes(int32_t kda, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                         int32_t num_seqs, const int32_t* cu_seqlens);
+int gdn_state_summary_apply(const float* transition, const float* state_ext, const float* state_in,
+                            float* state_out, int32_t N, int32_t H, int32_t K, int32_t V, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

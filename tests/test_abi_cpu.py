@@ -26,7 +26,9 @@ def _declared_functions():
 def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for must in ("gdn_chunk_fwd", "kda_chunk_fwd", "gdn_last_error", "gdn_chunk_fwd_workspace_bytes",
-                 "gdn_stage_prepare", "gdn_stage_fwd_h", "gdn_stage_finalize", "gdn_num_chunks"):
+                 "gdn_stage_prepare", "gdn_stage_fwd_h", "gdn_stage_finalize", "gdn_num_chunks",
+                 "gdn_state_summary", "kda_state_summary", "gdn_state_summary_workspace_bytes",
+                 "gdn_state_summary_apply"):
         assert must in names
 
 
@@ -131,3 +133,41 @@ def test_stage_column_order_decoder():
                 for e in range(4):
                     stored[32 * s + 8 * g + 4 * h + e] = 32 * s + 16 * h + 4 * g + e
     np.testing.assert_array_equal(unpermute_cols(stored), np.arange(64))
+
+
+@pytest.mark.parametrize("kda", [False, True])
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(K=64), 2, "K = V = 128"),
+    (dict(B=0), 1, "B, T and H"),
+    (dict(flags=8), 1, "unknown flag"),
+    (dict(k=None), 1, "non-NULL"),
+    (dict(M=None), 1, "transition and state_ext"),
+    (dict(S=None), 1, "transition and state_ext"),
+    (dict(T=10, cu=[0, 4, 9]), 1, "must equal T"),
+])
+def test_state_summary_validates_before_device(gdn, kw, code, msg, kda):
+    a = dict(B=1, T=64, H=2, K=128, V=128, flags=3, k=FAKE, M=FAKE, S=FAKE, cu=None)
+    a.update(kw)
+    cu = None if a["cu"] is None else np.asarray(a["cu"], dtype=np.int32)
+    n = a["B"] if cu is None else len(cu) - 1
+    fn = gdn.lib.kda_state_summary if kda else gdn.lib.gdn_state_summary
+    rc = fn(None, a["k"], FAKE, FAKE, FAKE, None if cu is None else cu.ctypes.data_as(ctypes.c_void_p), n,
+            a["B"], a["T"], a["H"], a["K"], a["V"], a["flags"], a["M"], a["S"], None, 0, None)
+    assert rc == code
+    assert msg in gdn.last_error()
+
+
+def test_state_summary_workspace_and_apply_validation(gdn):
+    ws = gdn.lib.gdn_state_summary_workspace_bytes
+    a = ws(0, 1, 8192, 32, 128, 128, 1, None)
+    k = ws(1, 1, 8192, 32, 128, 128, 1, None)
+    per = 64 * 64 * 4 + 64 * 64 * 2 + 8 * 64 * 4
+    assert a >= 32 * 128 * per and a % 256 == 0
+    assert k >= a + 32 * 128 * 64 * 128 * 4     # KDA keeps the cumulative gate
+    assert ws(0, 1, 10, 4, 64, 128, 1, None) == 0
+    ap = gdn.lib.gdn_state_summary_apply
+    assert ap(None, FAKE, FAKE, FAKE, 1, 2, 128, 128, None) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert ap(FAKE, FAKE, FAKE, ctypes.c_void_p(0x200000), 1, 2, 64, 128, None) == gdn.GDN_ERR_UNSUPPORTED
+    assert ap(FAKE, FAKE, ctypes.c_void_p(0x200000), ctypes.c_void_p(0x200000), 1, 2, 128, 128, None) \
+        == gdn.GDN_ERR_INVALID_ARGUMENT and "alias" in gdn.last_error()
+    assert ap(FAKE, FAKE, FAKE, ctypes.c_void_p(0x200008), 1, 2, 128, 128, None) == gdn.GDN_ERR_INVALID_ARGUMENT
