@@ -27,6 +27,11 @@ Workloads (natural-log gate for GDN, log2 gate for KDA):
 
 Every workload can be drawn at reduced B/T/H with the same recipe, which is
 how the parity tests obtain sizes the oracle finishes in seconds.
+
+``make_conv_inputs`` draws the input of the causal depthwise Conv1d + SiLU
+that forms q, k, v: projections x ~ N(0,1) in bf16 of D = 3 * H * 128
+channels for the GDN layer shape (q, k, v of H heads), weights and bias with
+a depthwise Conv1d's default initialisation U(-1/sqrt(W), 1/sqrt(W)), W = 4.
 """
 from __future__ import annotations
 
@@ -227,3 +232,45 @@ def random_problem(
         g=g, beta=f32_to_bf16_bits(beta), initial_state=s0,
         cu_seqlens=None if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int32),
     )
+
+
+# ---------------------------------------------------------------------------
+# Causal depthwise Conv1d (+ SiLU) that forms q, k, v from the projections
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class ConvInputs:
+    """x bf16 bits [B,T,D] (token-major), weight fp32 [D,W] (a depthwise
+    Conv1d's [D,1,W] weight), bias fp32 [D] or None, halo bf16 bits
+    [B,(W-1)*dilation,D] or None (rows preceding each sequence; packed input:
+    preceding the first document), cu_seqlens int32 or None (then B = 1)."""
+    B: int
+    T: int
+    D: int
+    W: int
+    dilation: int
+    silu: bool
+    x: np.ndarray
+    weight: np.ndarray
+    bias: Optional[np.ndarray]
+    halo: Optional[np.ndarray]
+    cu_seqlens: Optional[np.ndarray]
+
+
+def make_conv_inputs(B: int, T: int, D: int, W: int = 4, dilation: int = 1, seed: int = 2001, silu: bool = True,
+                     bias: bool = False, halo: bool = False, doc_lengths: Optional[list] = None) -> ConvInputs:
+    """x ~ N(0,1) in bf16; weight and bias ~ U(-1/sqrt(W), 1/sqrt(W)) (the
+    default initialisation of a depthwise Conv1d, fan-in W); halo ~ N(0,1).
+    With doc_lengths, B must be 1 and T is their sum."""
+    rng = np.random.default_rng(seed)
+    cu = None
+    if doc_lengths is not None:
+        assert B == 1
+        cu = np.concatenate([[0], np.cumsum(np.asarray(doc_lengths, dtype=np.int64))]).astype(np.int32)
+        T = int(cu[-1])
+    bound = np.float32(1.0 / math.sqrt(W))
+    x = f32_to_bf16_bits(rng.standard_normal((B, T, D), dtype=np.float32))
+    w = rng.uniform(-bound, bound, size=(D, W)).astype(np.float32)
+    b = rng.uniform(-bound, bound, size=(D,)).astype(np.float32) if bias else None
+    hw = (W - 1) * dilation
+    h = f32_to_bf16_bits(rng.standard_normal((B, hw, D), dtype=np.float32)) if (halo and hw > 0) else None
+    return ConvInputs(B=B, T=T, D=D, W=W, dilation=dilation, silu=silu, x=x, weight=w, bias=b, halo=h, cu_seqlens=cu)

@@ -14,8 +14,12 @@ Two independent fp64 definitions of the same result:
   / ``_run_prepared_gdn_chunks``), exporting its intermediates for stage
   parity.
 
-Every function is pinned by ``tests/test_oracle_pins.py`` against facts fixed
-by the mathematics (closed forms, invariants, hand-derived fixtures); see the
+Besides these, :func:`state_summary` / :func:`apply_state_summary` (the
+affine summary of a sequence) and :func:`short_conv` (module ``oracle.conv``,
+the causal depthwise Conv1d + SiLU that forms q, k, v).
+
+Every function is pinned by ``tests/test_oracle_pins.py`` (and
+``tests/test_conv_pins.py``) against facts fixed by the mathematics (closed forms, invariants, hand-derived fixtures); see the
 header of each function for what pins it.
 """
 from __future__ import annotations
@@ -102,5 +106,6 @@ def recur(inp, units: Optional[Sequence[tuple]] = None, flags: Optional[int] = N
 
 
 from .chunk import apply_state_summary, chunk, decode_bf16, l2norm, state_summary  # noqa: E402  (pure numpy, no C)
+from .conv import short_conv  # noqa: E402  (pure numpy, no C)
 
 __all__ = ["build", "recur", "chunk", "decode_bf16", "l2norm", "num_threads", "L2NORM", "BETA_SIGMOID"]
