@@ -88,8 +88,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gdn", choices=["gdn", "varlen", "long", "kda", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="fwd", choices=["fwd", "summary"],
-                    help="fwd: the forward pass (default); summary: the affine state summary and its apply step")
+    ap.add_argument("--op", default="fwd", choices=["fwd", "summary", "conv"],
+                    help="fwd: the forward pass (default); summary: the affine state summary and its apply step; "
+                         "conv: the causal depthwise Conv1d + SiLU forming q, k, v (D = 3*H*128, W = 4)")
     ap.add_argument("--scrub-mib", type=int, default=1024, help="MiB read between timed calls (0: none)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run plain device-to-device copies of this many MiB (counter calibration)")
@@ -165,6 +166,48 @@ def bench_summary(args, gdn, gi, inp, q, k, v, g, beta, dev):
     print(json.dumps(line), flush=True)
 
 
+def bench_conv(args, gdn, gi, dev):
+    """Times gdn_short_conv on the projections of the workload's GDN layer:
+    D = 3 * H * 128 channels (q, k, v), W = 4, SiLU, each call after a 1 GiB
+    read; HBM-bound, so reported against the HBM roofline (algorithmic bytes:
+    x read once, y written once)."""
+    import torch
+    B, T, H = gi.WORKLOADS[args.workload][:3]
+    D = 3 * H * 128
+    inp = gi.make_conv_inputs(B, T, D, W=4, seed=2001)
+    x = torch.from_numpy(inp.x).view(torch.bfloat16).to(dev)
+    w = torch.from_numpy(inp.weight).to(dev)
+    y = torch.empty_like(x)
+    scrub = torch.full((max(args.scrub_mib, 1) * (1 << 20) // 4,), 1.0, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        gdn.short_conv(x, w, out=y)
+    ts = []
+    for _ in range(args.steps):
+        if args.scrub_mib:
+            scrub.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gdn.short_conv(x, w, out=y)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    alg = 2.0 * B * T * D * 2
+    gbps = alg / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "short conv tokens/s", "value": round(B * T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "causal depthwise Conv1d + SiLU, B=%d T=%d D=%d W=4" % (B, T, D), "global_batch": B,
+                   "seq_len": T, "channels": D, "parallelism": "single-gpu"},
+        "roofline": {"kernel": "short_conv", "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "timing": {"per_call": "median of %d calls, %d MiB read before each" % (args.steps, args.scrub_mib),
+                   "p10_ms": round(float(np.percentile(ts, 10)), 5), "p90_ms": round(float(np.percentile(ts, 90)), 5)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy_mib:
@@ -183,6 +226,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.op == "conv":
+        bench_conv(args, gdn, gi, dev)
+        return
     inp = gi.make_inputs(args.workload)
     B, T, H, K, V = inp.B, inp.T, inp.H, inp.K, inp.V
     N = inp.num_seqs

@@ -35,7 +35,8 @@ EXPORTED = (
     "gdn_last_error", "gdn_num_chunks", "gdn_chunk_fwd_workspace_bytes", "kda_chunk_fwd_workspace_bytes",
     "gdn_chunk_fwd", "kda_chunk_fwd", "gdn_stage_prepare", "gdn_stage_fwd_h", "gdn_stage_finalize",
     "gdn_timing_enable", "gdn_timing_read", "gdn_state_summary", "kda_state_summary",
-    "gdn_state_summary_workspace_bytes", "gdn_state_summary_apply",
+    "gdn_state_summary_workspace_bytes", "gdn_state_summary_apply", "gdn_short_conv",
+    "gdn_short_conv_workspace_bytes",
 )
 
 
@@ -78,6 +79,10 @@ def _load() -> ctypes.CDLL:
     lib.gdn_state_summary_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, p]
     lib.gdn_state_summary_apply.restype = ctypes.c_int
     lib.gdn_state_summary_apply.argtypes = [p, p, p, p, i32, i32, i32, i32, p]
+    lib.gdn_short_conv_workspace_bytes.restype = sz
+    lib.gdn_short_conv_workspace_bytes.argtypes = [i32, p]
+    lib.gdn_short_conv.restype = ctypes.c_int
+    lib.gdn_short_conv.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, p, p, sz, p]
     lib.gdn_stage_prepare.restype = ctypes.c_int
     lib.gdn_stage_prepare.argtypes = [i32, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p, p, p, p]
     lib.gdn_stage_fwd_h.restype = ctypes.c_int
@@ -253,6 +258,38 @@ def state_summary_apply(M: torch.Tensor, S: torch.Tensor, state_in: Optional[tor
         out = torch.empty_like(S)
     _check(lib.gdn_state_summary_apply(_ptr(M), _ptr(S), _ptr(state_in), _ptr(out), N, H, K, V,
                                        _stream_ptr(S.device, stream)))
+    return out
+
+
+def short_conv(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+               halo: Optional[torch.Tensor] = None, cu_seqlens=None, dilation: int = 1, silu: bool = True,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Causal depthwise Conv1d (+ SiLU): x bf16 [B,T,D], weight fp32 [D,W] or
+    [D,1,W], bias fp32 [D], halo bf16 [B or 1,(W-1)*dilation,D]. Returns y bf16 [B,T,D]."""
+    cu = _cu_array(cu_seqlens)
+    if x.dtype != torch.bfloat16 or x.dim() != 3 or not x.is_contiguous() or x.device.type != "cuda":
+        raise ValueError("x must be a contiguous bf16 [B,T,D] tensor on the GPU")
+    B, T, D = x.shape
+    w = weight.reshape(weight.shape[0], -1)
+    if w.dtype != torch.float32 or not w.is_contiguous() or w.shape[0] != D or w.device != x.device:
+        raise ValueError("weight must be a contiguous fp32 [D,W] (or [D,1,W]) tensor on %s" % x.device)
+    W = w.shape[1]
+    if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (D,) or bias.device != x.device):
+        raise ValueError("bias must be fp32 [D] on %s" % x.device)
+    if halo is not None:
+        rows = 1 if cu is not None else B
+        if (halo.dtype != torch.bfloat16 or not halo.is_contiguous() or halo.device != x.device
+                or tuple(halo.shape) != (rows, (W - 1) * dilation, D)):
+            raise ValueError("halo must be a contiguous bf16 %s tensor on %s" % ((rows, (W - 1) * dilation, D),
+                                                                                    x.device))
+    if out is None:
+        out = torch.empty_like(x)
+    N = B if cu is None else len(cu) - 1
+    need = lib.gdn_short_conv_workspace_bytes(N, _cu_ptr(cu))
+    ws = torch.empty(int(need), dtype=torch.uint8, device=x.device) if need else None
+    _check(lib.gdn_short_conv(_ptr(x), _ptr(w), _ptr(bias), _ptr(halo), _cu_ptr(cu), N, B, T, D, W, dilation,
+                              int(silu), _ptr(out), _ptr(ws), 0 if ws is None else int(need),
+                              _stream_ptr(x.device, stream)))
     return out
 
 

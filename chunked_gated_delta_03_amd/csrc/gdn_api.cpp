@@ -170,6 +170,8 @@ std::mutex g_stage_mu;
 StagingSlot g_slots[8];
 unsigned g_next_slot = 0;
 
+int stage_upload(const void* src, size_t bytes, void* dst, hipStream_t stream);
+
 int upload_tables(const Problem& p, void* dst, hipStream_t stream) {
   std::vector<int4> tab;
   tab.reserve((size_t)p.NT + p.N);
@@ -200,8 +202,12 @@ int upload_tables(const Problem& p, void* dst, hipStream_t stream) {
     if (n + 3 < p.N) e.w = order[n + 3];
     tab.push_back(e);
   }
-  const size_t bytes = tab.size() * sizeof(int4);
+  return stage_upload(tab.data(), tab.size() * sizeof(int4), dst, stream);
+}
 
+// Host data to device memory on `stream` through the pinned staging ring;
+// the host buffer may be reused by the caller immediately.
+int stage_upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -229,9 +235,9 @@ int upload_tables(const Problem& p, void* dst, hipStream_t stream) {
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(staging)");
     s.cap = bytes;
   }
-  std::memcpy(s.host, tab.data(), bytes);
+  std::memcpy(s.host, src, bytes);
   e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(chunk tables)");
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(tables)");
   e = hipEventRecord(s.done, stream);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord(staging)");
   s.pending = true;
@@ -587,6 +593,57 @@ int gdn_state_summary_apply(const float* transition, const float* state_ext, con
   hipError_t e = gdn::launch_summary_apply(transition, state_ext, state_in, state_out, (long)N * H,
                                            static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "summary apply launch");
+  return GDN_OK;
+}
+
+size_t gdn_short_conv_workspace_bytes(int32_t num_seqs, const int32_t* cu_seqlens) {
+  g_last_error.clear();
+  return cu_seqlens ? align256(sizeof(int32_t) * ((size_t)num_seqs + 1)) : 0;
+}
+
+int gdn_short_conv(const void* x, const float* weight, const float* bias, const void* halo,
+                   const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t D, int32_t W,
+                   int32_t dilation, int32_t silu, void* y, void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  g_last_error.clear();
+  Problem p;
+  int rc = check_shape(B, T, 1, GDN_HEAD_DIM, GDN_HEAD_DIM, num_seqs, cu_seqlens, p);
+  if (rc) return rc;
+  if (!x || !weight || !y) return fail(GDN_ERR_INVALID_ARGUMENT, "x, weight and y must be non-NULL");
+  if (D < 8 || D % 8 != 0) return fail(GDN_ERR_UNSUPPORTED, "D must be a positive multiple of 8 (got %d)", D);
+  if (W < 1 || W > 8) return fail(GDN_ERR_UNSUPPORTED, "kernel size W must be 1..8 (got %d)", W);
+  if (dilation < 1 || (int64_t)(W - 1) * dilation > 4096)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "dilation must be >= 1 with (W-1)*dilation <= 4096 (got %d)", dilation);
+  if ((int64_t)B * T * D > INT64_MAX / 4) return fail(GDN_ERR_INVALID_ARGUMENT, "problem too large");
+  if (!aligned16(x) || !aligned16(y) || (halo && !aligned16(halo)))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "x, y and halo must be 16-byte aligned");
+  if (x == y) return fail(GDN_ERR_INVALID_ARGUMENT, "y must not alias x");
+  rc = check_device(nullptr);
+  if (rc) return rc;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  Workspace Wk;
+  const size_t need = gdn_short_conv_workspace_bytes(num_seqs, cu_seqlens);
+  rc = acquire_workspace(workspace, workspace_bytes, need, stream, Wk);
+  if (rc) return rc;
+  if (cu_seqlens) {
+    rc = stage_upload(cu_seqlens, sizeof(int32_t) * ((size_t)num_seqs + 1), Wk.base, stream);
+    if (rc) return rc;
+  }
+  gdn::ConvArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.w = weight;
+  a.bias = bias;
+  a.halo = static_cast<const uint16_t*>(halo);
+  a.cu = cu_seqlens ? reinterpret_cast<const int*>(Wk.base) : nullptr;
+  a.y = static_cast<uint16_t*>(y);
+  a.B = B;
+  a.T = T;
+  a.D = D;
+  a.W = W;
+  a.dilation = dilation;
+  a.N = p.N;
+  a.silu = silu != 0;
+  hipError_t e = gdn::launch_short_conv(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "short conv launch");
   return GDN_OK;
 }
 

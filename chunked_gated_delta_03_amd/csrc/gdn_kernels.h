@@ -74,6 +74,19 @@ hipError_t launch_finalize(bool kda, const FinArgs& a, hipStream_t stream);
 hipError_t launch_gdn_state(bool store_h, bool compute_o, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_kda_fwd(bool store_h, bool compute_o, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_kda_finalize(const FinArgs& a, hipStream_t stream);
+// Causal depthwise Conv1d + SiLU over token-major rows of D channels.
+struct ConvArgs {
+  const uint16_t* x;     // [B*T, D] bf16
+  const float* w;        // [D, W]
+  const float* bias;     // [D] or nullptr
+  const uint16_t* halo;  // [B or 1, (W-1)*dilation, D] bf16 or nullptr
+  const int* cu;         // device offsets [N+1] (packed) or nullptr
+  uint16_t* y;           // [B*T, D] bf16
+  int B, T, D, W, dilation, N;
+  int silu;
+};
+hipError_t launch_short_conv(const ConvArgs& a, hipStream_t stream);
+
 hipError_t launch_summary_apply(const float* M, const float* S, const float* sin, float* sout, long units,
                                 hipStream_t stream);
 

@@ -211,6 +211,33 @@ size_t gdn_state_summary_workspace_bytes(int32_t kda, int32_t B, int32_t T, int3
 int gdn_state_summary_apply(const float* transition, const float* state_ext, const float* state_in,
                             float* state_out, int32_t N, int32_t H, int32_t K, int32_t V, void* stream);
 
+/*
+ * Causal depthwise Conv1d + SiLU (the ShortConv forming q, k, v from the
+ * projections; _causal_conv1d_with_cp_halo on the 2026-09-10 "Diff Coverage"
+ * page): per channel c and token t,
+ *   y[t,c] = act(bias[c] + sum_{j<W} weight[c,j] * x[t - (W-1-j)*dilation, c]),
+ * act = SiLU (z / (1 + e^-z)) if silu != 0, else identity; rows before the
+ * start of a sequence come from the halo, else zero.
+ *   x     [B,T,D] bf16, token-major, 16-byte aligned; D a multiple of 8.
+ *   weight [D,W] fp32 (a depthwise Conv1d's [D,1,W] weight), W in 1..8.
+ *   bias  [D] fp32 or NULL.
+ *   halo  bf16 or NULL: [B,(W-1)*dilation,D] rows preceding each sequence
+ *         (dense), or [1,(W-1)*dilation,D] preceding the first document
+ *         (packed); the preceding rank's last rows in a sequence split.
+ *   cu_seqlens host int32 [num_seqs+1] or NULL, as gdn_chunk_fwd (B = 1):
+ *         every document is its own sequence.
+ *   y     [B,T,D] bf16 output (round to nearest even), must not alias x.
+ * fp32 accumulation. workspace: gdn_short_conv_workspace_bytes (the device
+ * copy of the offsets; 0 for dense input), or NULL for a stream-ordered
+ * allocation. Errors as gdn_chunk_fwd (D not a multiple of 8 or W outside
+ * 1..8: GDN_ERR_UNSUPPORTED); nothing is launched on error. Asynchronous on
+ * `stream`; buffers are caller-owned.
+ */
+size_t gdn_short_conv_workspace_bytes(int32_t num_seqs, const int32_t* cu_seqlens);
+int gdn_short_conv(const void* x, const float* weight, const float* bias, const void* halo,
+                   const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t D, int32_t W,
+                   int32_t dilation, int32_t silu, void* y, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

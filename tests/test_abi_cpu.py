@@ -28,7 +28,7 @@ def test_header_declares_expected_entry_points():
     for must in ("gdn_chunk_fwd", "kda_chunk_fwd", "gdn_last_error", "gdn_chunk_fwd_workspace_bytes",
                  "gdn_stage_prepare", "gdn_stage_fwd_h", "gdn_stage_finalize", "gdn_num_chunks",
                  "gdn_state_summary", "kda_state_summary", "gdn_state_summary_workspace_bytes",
-                 "gdn_state_summary_apply"):
+                 "gdn_state_summary_apply", "gdn_short_conv", "gdn_short_conv_workspace_bytes"):
         assert must in names
 
 
@@ -171,3 +171,29 @@ def test_state_summary_workspace_and_apply_validation(gdn):
     assert ap(FAKE, FAKE, ctypes.c_void_p(0x200000), ctypes.c_void_p(0x200000), 1, 2, 128, 128, None) \
         == gdn.GDN_ERR_INVALID_ARGUMENT and "alias" in gdn.last_error()
     assert ap(FAKE, FAKE, FAKE, ctypes.c_void_p(0x200008), 1, 2, 128, 128, None) == gdn.GDN_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(D=12), 2, "multiple of 8"),
+    (dict(W=9), 2, "1..8"),
+    (dict(W=0), 2, "1..8"),
+    (dict(dil=0), 1, "dilation"),
+    (dict(x=None), 1, "non-NULL"),
+    (dict(y=None), 1, "non-NULL"),
+    (dict(y=FAKE), 1, "alias"),
+    (dict(halo=ctypes.c_void_p(0x100008)), 1, "aligned"),
+    (dict(B=2, cu=[0, 4, 10], T=10), 1, "B == 1"),
+    (dict(T=10, cu=[0, 4, 9]), 1, "must equal T"),
+])
+def test_short_conv_validates_before_device(gdn, kw, code, msg):
+    a = dict(B=1, T=64, D=64, W=4, dil=1, x=FAKE, y=ctypes.c_void_p(0x200000), halo=None, cu=None)
+    a.update(kw)
+    cu = None if a["cu"] is None else np.asarray(a["cu"], dtype=np.int32)
+    n = a["B"] if cu is None else len(cu) - 1
+    rc = gdn.lib.gdn_short_conv(a["x"], FAKE, None, a["halo"], None if cu is None else cu.ctypes.data_as(ctypes.c_void_p),
+                                n, a["B"], a["T"], a["D"], a["W"], a["dil"], 1, a["y"], None, 0, None)
+    assert rc == code
+    assert msg in gdn.last_error()
+    cu2 = np.asarray([0, 5, 9], dtype=np.int32)
+    assert gdn.lib.gdn_short_conv_workspace_bytes(2, cu2.ctypes.data_as(ctypes.c_void_p)) == 256
+    assert gdn.lib.gdn_short_conv_workspace_bytes(2, None) == 0
