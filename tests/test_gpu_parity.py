@@ -299,3 +299,42 @@ def test_full_size_long_sampled(gdn):
     units = [(0, 0), (0, 31)]
     o_ref, s_ref = _sampled(inp, units)
     _check_units(inp, o, fs, o_ref, s_ref, units)
+
+
+def _degenerate_cases():
+    """The method's degenerate inputs, on both gate kinds: a gate of -1000 at
+    one token (the carried state and earlier tokens are forgotten: every decay
+    path underflows to exactly 0), beta = 0 (the state only decays), k = 0
+    (no writes), and a run whose gate is -1000 at every token."""
+    out = []
+    for kda in (False, True):
+        tag = "kda" if kda else "gdn"
+        rng = np.random.default_rng(300 + kda)
+        base = gi.random_problem(rng, 2, 200, 2, 128, 128, kda=kda, gate_scale=0.05, with_initial_state=True)
+        g = base.g.copy()
+        g[:, 77] = -1000.0
+        out.append((tag + "_reset_at_77", gi.GdnInputs(**{**base.__dict__, "g": g})))
+        beta0 = gi.f32_to_bf16_bits(np.zeros(base.beta.shape, dtype=np.float32))
+        out.append((tag + "_beta_zero", gi.GdnInputs(**{**base.__dict__, "beta": beta0,
+                                                         "flags": gi.FLAG_L2NORM_QK | gi.FLAG_OUTPUT_FINAL_STATE})))
+        k0 = gi.f32_to_bf16_bits(np.zeros(gi.bf16_bits_to_f32(base.k).shape, dtype=np.float32))
+        out.append((tag + "_k_zero", gi.GdnInputs(**{**base.__dict__, "k": k0,
+                                                      "flags": gi.FLAG_BETA_SIGMOID | gi.FLAG_OUTPUT_FINAL_STATE})))
+        out.append((tag + "_gate_all_reset", gi.GdnInputs(**{**base.__dict__, "g": np.full_like(base.g, -1000.0)})))
+    return out
+
+
+DEGENERATE = _degenerate_cases()
+
+
+@pytest.mark.parametrize("name,inp", DEGENERATE, ids=[n for n, _ in DEGENERATE])
+def test_degenerate_inputs(gdn, name, inp):
+    _say("degenerate case", name)
+    o_ref, s_ref = oracle.recur(inp)
+    o, fs = run_gpu(inp)
+    assert np.isfinite(o).all() and np.isfinite(fs).all()
+    eo = o_err(o, o_ref)
+    es = float(np.abs(fs - s_ref).max() / max(np.abs(s_ref).max(), 1e-3))
+    _say("  o max-abs err %.3e   final-state err %.3e (max |S_ref| %.2e)" % (eo, es, np.abs(s_ref).max()))
+    assert eo <= O_ATOL
+    assert es <= S_RTOL
