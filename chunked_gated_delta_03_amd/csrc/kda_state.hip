@@ -20,13 +20,15 @@
 // kd, kg (bf16 hi + lo), S and the right-hand sides that carry the state
 // use split products as in the GDN kernel; qd is a single bf16 operand.
 //
-// LDS holds one chunk of every operand (the decayed operands alone are 80 KiB,
-// too much to double-buffer). Each array is rewritten for the next chunk only
-// while the compute waves do not read it: kd and qd are read before the pair
-// barrier, so the loaders write the next chunk's after it; T, Aqk, v, the row
-// vectors, the channel decays and kg are read after the pair barrier, so the
-// loaders write the next chunk's between the end of a chunk and the next pair
-// barrier. Layouts and the state-row permutation are those of the GDN state
+// LDS holds one chunk of most operands (the decayed operands alone are 80 KiB,
+// too much to double-buffer). Each such array is rewritten for the next chunk
+// only while the compute waves do not read it: kd and qd are read before the
+// pair barrier, so the loaders write the next chunk's after it; Aqk, v and kg
+// are read after the pair barrier, so the loaders write the next chunk's
+// between the end of a chunk and the next pair barrier. T, the row vectors
+// and the channel decays (read after the pair barrier) have two buffers in
+// the whole pass and are written after the pair barrier with kd and qd: LDS
+// writes before that barrier compete with the compute waves' reads there. Layouts and the state-row permutation are those of the GDN state
 // kernel: 16-byte pieces of 256-byte rows at slot p ^ (r & 15) (Aqk rows:
 // p ^ (r & 7)), row i of state tile t is K index perm_col(16 t + i).
 #include <type_traits>
@@ -49,11 +51,14 @@ struct alignas(16) KSmem {
   uint16_t qd[kChunk * kDim];            // q 2^G
   uint16_t kgh[kChunk * kDim];           // k 2^(G_last - G), hi and lo
   uint16_t kgl[kChunk * kDim];
-  uint16_t t[kChunk * 2 * kChunk];       // T hi | lo (permuted columns)
+  // T, the row vectors and the channel decays have two buffers (chunk
+  // parity) in the whole pass, so the loaders write the next chunk's after
+  // the pair barrier; the stage entry uses buffer 0 only
+  uint16_t t[2][kChunk * 2 * kChunk];    // T hi | lo (permuted columns)
   uint16_t aqk[kChunk * kChunk];         // permuted columns
   uint16_t v[kChunk * BV];               // v rows of this V-block
-  float vec[kVecRows * kChunk];
-  float dec[kDim];                       // 2^G_last per channel
+  float vec[2][kVecRows * kChunk];
+  float dec[2][kDim];                    // 2^G_last per channel
   f32x4 xch[NCW][6][64];
   uint16_t o[NCW][32 * 16];
 };
@@ -86,13 +91,21 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
       constexpr int PPR = BV / 8;
       const int ltid = tid - NCW * 64;
       const int pc = ltid & 15;
-      u32x4 dh[1024 / NL], dl[1024 / NL], qq[1024 / NL], gh[1024 / NL], gl[1024 / NL], tr[1024 / NL];
-      u32x4 ar[512 / NL], vr, er, dr;
-      auto fetch = [&](int jc) {
-        const int tok0 = si.tok0 + jc * kChunk;
+      // two register sets: the arrays written before the pair barrier (kg,
+      // Aqk, v) and those written after it (kd, qd, T, row vectors, decays),
+      // each loaded one chunk ahead in the window in which it is written
+      u32x4 dh[1024 / NL], dl[1024 / NL], qq[1024 / NL], tr[1024 / NL], er, dr;  // after the barrier
+      u32x4 gh[1024 / NL], gl[1024 / NL], ar[512 / NL], vr;                       // before it
+      auto chunk_at = [&](int jc, int& tok0, int& len, size_t& cm) {
+        tok0 = si.tok0 + jc * kChunk;
         const int rem = si.len - jc * kChunk;
-        const int len = rem < kChunk ? rem : kChunk;
-        const size_t cm = (size_t)h * a.geo.NT + si.c0 + jc;
+        len = rem < kChunk ? rem : kChunk;
+        cm = (size_t)h * a.geo.NT + si.c0 + jc;
+      };
+      auto fetch_early = [&](int jc) {
+        int tok0, len;
+        size_t cm;
+        chunk_at(jc, tok0, len, cm);
         const uint16_t* kd = a.kdec + cm * kKdecElems;
 #pragma unroll
         for (int p = 0; p < 1024 / NL; ++p) {
@@ -100,21 +113,31 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
           dh[p] = reinterpret_cast<const u32x4*>(kd + kKdecKdh)[idx];
           dl[p] = reinterpret_cast<const u32x4*>(kd + kKdecKdl)[idx];
           qq[p] = reinterpret_cast<const u32x4*>(kd + kKdecQd)[idx];
+          tr[p] = reinterpret_cast<const u32x4*>(a.tmat + cm * (kChunk * 2 * kChunk))[idx];
+        }
+        if (ltid < kVecRows * kChunk / 4) er = reinterpret_cast<const u32x4*>(a.vec + cm * (kVecRows * kChunk))[ltid];
+        if (ltid < kDim / 4) dr = reinterpret_cast<const u32x4*>(kd + kKdecDec)[ltid];
+      };
+      auto fetch_late = [&](int jc) {
+        int tok0, len;
+        size_t cm;
+        chunk_at(jc, tok0, len, cm);
+        const uint16_t* kd = a.kdec + cm * kKdecElems;
+#pragma unroll
+        for (int p = 0; p < 1024 / NL; ++p) {
+          const int idx = p * NL + ltid;
           gh[p] = reinterpret_cast<const u32x4*>(kd + kKdecKgh)[idx];
           gl[p] = reinterpret_cast<const u32x4*>(kd + kKdecKgl)[idx];
-          tr[p] = reinterpret_cast<const u32x4*>(a.tmat + cm * (kChunk * 2 * kChunk))[idx];
         }
 #pragma unroll
         for (int p = 0; p < 512 / NL; ++p) ar[p] = reinterpret_cast<const u32x4*>(a.aqk + cm * (kChunk * kChunk))[p * NL + ltid];
         if (ltid < 64 * PPR) {
           const int r = ltid / PPR;
           vr = (r < len && !a.s_identity) ? *reinterpret_cast<const u32x4*>(a.v + ((size_t)(tok0 + r) * H + h) * kDim + vb * BV + 8 * (ltid % PPR))
-                       : u32x4{0, 0, 0, 0};
+                                          : u32x4{0, 0, 0, 0};
         }
-        if (ltid < kVecRows * kChunk / 4) er = reinterpret_cast<const u32x4*>(a.vec + cm * (kVecRows * kChunk))[ltid];
-        if (ltid < kDim / 4) dr = reinterpret_cast<const u32x4*>(kd + kKdecDec)[ltid];
       };
-      auto put_early = [&]() {  // kd, qd of the fetched chunk
+      auto put_early = [&](int tb) {  // kd, qd, T, row vectors, decays of the fetched chunk
 #pragma unroll
         for (int p = 0; p < 1024 / NL; ++p) {
           const int idx = p * NL + ltid, r = idx >> 4;
@@ -122,16 +145,18 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
           *reinterpret_cast<u32x4*>(sm.kdh + r * kDim + slot) = dh[p];
           *reinterpret_cast<u32x4*>(sm.kdl + r * kDim + slot) = dl[p];
           *reinterpret_cast<u32x4*>(sm.qd + r * kDim + slot) = qq[p];
+          *reinterpret_cast<u32x4*>(sm.t[tb] + r * (2 * kChunk) + slot) = tr[p];
         }
+        if (ltid < kVecRows * kChunk / 4) *reinterpret_cast<u32x4*>(sm.vec[tb] + 4 * ltid) = er;
+        if (ltid < kDim / 4) *reinterpret_cast<u32x4*>(sm.dec[tb] + 4 * ltid) = dr;
       };
-      auto put_late = [&]() {  // kg, T, Aqk, v, row vectors, channel decays
+      auto put_late = [&]() {  // kg, Aqk, v of the chunk about to start
 #pragma unroll
         for (int p = 0; p < 1024 / NL; ++p) {
           const int idx = p * NL + ltid, r = idx >> 4;
           const int slot = 8 * (pc ^ (r & 15));
           *reinterpret_cast<u32x4*>(sm.kgh + r * kDim + slot) = gh[p];
           *reinterpret_cast<u32x4*>(sm.kgl + r * kDim + slot) = gl[p];
-          *reinterpret_cast<u32x4*>(sm.t + r * (2 * kChunk) + slot) = tr[p];
         }
 #pragma unroll
         for (int p = 0; p < 512 / NL; ++p) {
@@ -139,20 +164,25 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
           *reinterpret_cast<u32x4*>(sm.aqk + r * kChunk + 8 * ((idx & 7) ^ (r & 7))) = ar[p];
         }
         if (ltid < 64 * PPR) *reinterpret_cast<u32x4*>(sm.v + 8 * ltid) = vr;
-        if (ltid < kVecRows * kChunk / 4) *reinterpret_cast<u32x4*>(sm.vec + 4 * ltid) = er;
-        if (ltid < kDim / 4) *reinterpret_cast<u32x4*>(sm.dec + 4 * ltid) = dr;
       };
-      // same barrier sequence and windows as the stage loaders below
+      // same barrier sequence as the stage loaders below. During chunk jc:
+      // before the pair barrier, chunk jc's kg, Aqk, v go in and chunk
+      // jc+1's are loaded; after it, chunk jc+1's kd, qd, T, row vectors and
+      // decays go in and chunk jc+2's are loaded (past the end the last chunk
+      // is repeated, harmlessly)
       if (si.nch > 0) {
-        fetch(0);
-        put_early();
+        fetch_early(0);
+        fetch_late(0);
+        put_early(0);
+        fetch_early(min(1, last));
       }
       __syncthreads();
       for (int jc = 0; jc < si.nch; ++jc) {
         put_late();
-        fetch(min(jc + 1, last));
+        fetch_late(min(jc + 1, last));
         __syncthreads();
-        put_early();
+        put_early((jc + 1) & 1);
+        fetch_early(min(jc + 2, last));
         __syncthreads();
       }
       return;
@@ -249,7 +279,7 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
         const int slot = 8 * (pc ^ (r & 15));
         *reinterpret_cast<u32x4*>(sm.kgh + r * kDim + slot) = kgh[p];
         *reinterpret_cast<u32x4*>(sm.kgl + r * kDim + slot) = kgl[p];
-        *reinterpret_cast<u32x4*>(sm.t + r * (2 * kChunk) + slot) = tr[p];
+        *reinterpret_cast<u32x4*>(sm.t[0] + r * (2 * kChunk) + slot) = tr[p];
       }
       if constexpr (COMPUTE_O) {
 #pragma unroll
@@ -259,10 +289,10 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
         }
       }
       if (ltid < 64 * PPR) *reinterpret_cast<u32x4*>(sm.v + 8 * ltid) = vr;
-      if (ltid < kVecRows * kChunk / 4) *reinterpret_cast<u32x4*>(sm.vec + 4 * ltid) = er;
+      if (ltid < kVecRows * kChunk / 4) *reinterpret_cast<u32x4*>(sm.vec[0] + 4 * ltid) = er;
       if (ltid < 16) {
-        *reinterpret_cast<float4*>(sm.dec + 8 * ltid) = dec0;
-        *reinterpret_cast<float4*>(sm.dec + 8 * ltid + 4) = dec1;
+        *reinterpret_cast<float4*>(sm.dec[0] + 8 * ltid) = dec0;
+        *reinterpret_cast<float4*>(sm.dec[0] + 8 * ltid + 4) = dec1;
       }
     };
 
@@ -321,6 +351,7 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
     for (int jc = 0; jc < si.nch; ++jc) {
       const int c = si.c0 + jc;
       const size_t cm = (size_t)h * a.geo.NT + c;
+      const int tb = COMPUTE_O ? (jc & 1) : 0;  // buffer of T, row vectors, decays
 
       if constexpr (COMPUTE_O) {
         if (jc >= 1) store_o(jc - 1);
@@ -390,8 +421,8 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
         for (int k2 = 0; k2 < 2; ++k2) {
           const int it = 2 * hh + k2;
           const u16x4 vv = tr_read(sm.v + (16 * it + 4 * g4 + trJ) * BV + 16 * cb + 4 * trQ);
-          const float4 bt = *reinterpret_cast<const float4*>(sm.vec + 16 * it + 4 * g4);
-          const float4 cc = *reinterpret_cast<const float4*>(sm.vec + kChunk + 16 * it + 4 * g4);
+          const float4 bt = *reinterpret_cast<const float4*>(sm.vec[tb] + 16 * it + 4 * g4);
+          const float4 cc = *reinterpret_cast<const float4*>(sm.vec[tb] + kChunk + 16 * it + 4 * g4);
           y2[k2][0] = bt.x * bf2f(vv[0]) - cc.x * X[it][0];
           y2[k2][1] = bt.y * bf2f(vv[1]) - cc.y * X[it][1];
           y2[k2][2] = bt.z * bf2f(vv[2]) - cc.z * X[it][2];
@@ -404,7 +435,7 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
         u16x8 th[4][2], tl[4][2];
 #pragma unroll
         for (int io = 0; io < 4; ++io) {
-          const uint16_t* row = sm.t + (16 * io + l16) * (2 * kChunk);
+          const uint16_t* row = sm.t[tb] + (16 * io + l16) * (2 * kChunk);
           th[io][0] = *reinterpret_cast<const u16x8*>(row + 8 * (g4 ^ l16));
           tl[io][0] = *reinterpret_cast<const u16x8*>(row + 8 * ((8 + g4) ^ l16));
           if (io >= 2) {  // T is lower triangular
@@ -445,7 +476,7 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
           const int io = 2 * hh + k2;
-          const float4 dd = *reinterpret_cast<const float4*>(sm.vec + 2 * kChunk + 16 * io + 4 * g4);
+          const float4 dd = *reinterpret_cast<const float4*>(sm.vec[tb] + 2 * kChunk + 16 * io + 4 * g4);
           z2[k2][0] = dd.x * VN[io][0];
           z2[k2][1] = dd.y * VN[io][1];
           z2[k2][2] = dd.z * VN[io][2];
@@ -469,7 +500,7 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           // the 4 rows of tile t in lane group g4 are 4 consecutive channels
-          const float4 dv = *reinterpret_cast<const float4*>(sm.dec + perm_col(64 * kh + 16 * t + 4 * g4));
+          const float4 dv = *reinterpret_cast<const float4*>(sm.dec[tb] + perm_col(64 * kh + 16 * t + 4 * g4));
           S[t][0] *= dv.x; S[t][1] *= dv.y; S[t][2] *= dv.z; S[t][3] *= dv.w;
         }
         u16x8 Zhi[2], Zlo[2];
@@ -494,7 +525,7 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
         for (int i = 0; i < 2; ++i) {
           const int it = 2 * kh + i;
           const int r = 16 * it + l16;
-          const float4 rr = *reinterpret_cast<const float4*>(sm.vec + 3 * kChunk + 16 * it + 4 * g4);
+          const float4 rr = *reinterpret_cast<const float4*>(sm.vec[tb] + 3 * kChunk + 16 * it + 4 * g4);
           O[i][0] *= rr.x; O[i][1] *= rr.y; O[i][2] *= rr.z; O[i][3] *= rr.w;
           O[i] = mfma16(*reinterpret_cast<const u16x8*>(sm.aqk + r * kChunk + 8 * (g4 ^ (r & 7))), VNb0, O[i]);
           if (kh == 1)  // Aqk is lower triangular
