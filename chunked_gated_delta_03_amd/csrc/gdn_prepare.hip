@@ -11,8 +11,10 @@
 //   - A = -(beta k k^T * Gamma), strictly lower, Gamma[i,j] = exp(G_i - G_j)
 //     with the mask applied before the exponential;
 //   - T = (I - A)^-1 (the page's row-by-row forward substitution plus the
-//     identity), computed blockwise: 16x16 diagonal blocks by substitution,
-//     then the off-diagonal blocks T_ij = T_ii * sum_m A_im T_mj;
+//     identity), computed blockwise: each 16x16 diagonal block as the
+//     product (I + N)(I + N^2)(I + N^4)(I + N^8) of its strictly lower part N
+//     (equal to the substitution result for a nilpotent N), then the
+//     off-diagonal blocks T_ij = T_ii * sum_m A_im T_mj;
 //   - the intra-chunk output matrix scale * (q k^T * Gamma), lower with the
 //     diagonal (_run_prepared_gdn_chunks).
 // The WY products U = T v_beta and W = T (k_beta e^G) are not formed here:
@@ -119,55 +121,6 @@ __device__ __forceinline__ void load_beta(const PrepareArgs& a, const ChunkInfo&
   float b = valid ? bf2f(a.beta[(size_t)(ci.tok0 + lane) * a.H + h]) : 0.0f;
   if ((a.flags & 2u) && valid) b = 1.0f / (1.0f + expf(-b));
   sBeta[lane] = b;
-}
-
-// T = (I - A)^-1 for strictly lower A (fp32, LDS), blockwise. All 256
-// threads call it; it ends with a barrier. The diagonal 16x16 blocks are
-// inverted by forward substitution (one block per wave); the off-diagonal
-// blocks follow one block row at a time, T_ij = T_ii * (sum_m A_im T_mj),
-// as 16x16x16 fp32 MFMA products. In the second product the contraction
-// slot of lane group g at step ks is 4g + ks, so the first product's
-// accumulator feeds it as the B operand without leaving registers.
-__device__ __forceinline__ void invert_unit_lower(const float* sA, float* sT, int wave, int lane) {
-  const int g4 = lane >> 4;
-  const int l16 = lane & 15;
-  if (lane < 16) {
-    const int base = 16 * wave;
-    float t[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float val = (i == lane) ? 1.0f : 0.0f;
-#pragma unroll
-      for (int m = 0; m < i; ++m) val = fmaf(sA[(base + i) * kLdF + base + m], t[m], val);
-      t[i] = val;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sT[(base + i) * kLdF + base + lane] = t[i];
-  }
-  __syncthreads();
-  for (int I = 1; I < 4; ++I) {
-    const int J = wave;
-    if (J < I) {
-      f32x4 p = {0.f, 0.f, 0.f, 0.f};
-      for (int M = J; M < I; ++M) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const float av = sA[(16 * I + l16) * kLdF + 16 * M + 4 * ks + g4];
-          const float bv = sT[(16 * M + 4 * ks + g4) * kLdF + 16 * J + l16];
-          p = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, p, 0, 0, 0);
-        }
-      }
-      f32x4 r = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const float av = sT[(16 * I + l16) * kLdF + 16 * I + 4 * g4 + ks];
-        r = __builtin_amdgcn_mfma_f32_16x16x4f32(av, p[ks], r, 0, 0, 0);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sT[(16 * I + 4 * g4 + e) * kLdF + 16 * J + l16] = r[e];
-    }
-    __syncthreads();
-  }
 }
 
 // T (fp32) and Aqk (bf16) to global, zero above the diagonal blocks.
@@ -578,6 +531,73 @@ __global__ __launch_bounds__(256, 3) void gdn_prepare_kernel(PrepareArgs a) {
   }
 }
 
+// T = (I - A)^-1 for strictly lower A (fp32 in LDS, row stride LD; only the
+// strictly lower part of A is read), as in the GDN prepare: wave W inverts
+// diagonal block W in registers by the nilpotent product formula on fp32
+// MFMA, then forms block row W of T, T_WJ = T_WW sum_{J<=M<W} A_WM T_MJ, one
+// block diagonal per barrier with the partial sums formed as soon as their
+// T blocks exist. All 256 threads call it; it ends with a barrier. The wave
+// index only selects straight-line branches (no register array is indexed
+// by it).
+template <int LD>
+__device__ __forceinline__ void invert_unit_lower(const float* sA, float* sT, int wave, int lane) {
+  const int W = __builtin_amdgcn_readfirstlane(wave);
+  const int g = lane >> 4, l = lane & 15;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  f32x4 N, Nt, Y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 4 * g + e;  // row inside the block; column l
+    N[e] = r > l ? sA[(16 * W + r) * LD + 16 * W + l] : 0.0f;
+    Nt[e] = l > r ? sA[(16 * W + l) * LD + 16 * W + r] : 0.0f;
+    Y[e] = Nt[e] + (r == l ? 1.0f : 0.0f);
+  }
+  {
+    const f32x4 N2 = mm16(Nt, N, z), N2t = mm16(N, Nt, z);
+    Y = mm16(N2, Y, Y);
+    const f32x4 N4 = mm16(N2t, N2, z), N4t = mm16(N2, N2t, z);
+    Y = mm16(N4, Y, Y);
+    const f32x4 N8 = mm16(N4t, N4, z);
+    Y = mm16(N8, Y, Y);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) sT[(16 * W + l) * LD + 16 * W + 4 * g + e] = Y[e];  // T_WW[l][4g+e]
+  __syncthreads();
+  // A_IM T_MJ + acc from LDS, contraction slot 4g + ks
+  auto mml = [&](int I, int M, int J, f32x4 acc) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * I + l) * LD + 16 * M + 4 * g + ks],
+                                                 sT[(16 * M + 4 * g + ks) * LD + 16 * J + l], acc, 0, 0, 0);
+    return acc;
+  };
+  auto put_t = [&](int J, const f32x4& t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sT[(16 * W + 4 * g + e) * LD + 16 * J + l] = t[e];
+  };
+  f32x4 p0 = z, p1 = z;
+  if (W == 1) {
+    put_t(0, mm16(Y, mml(1, 0, 0, z), z));
+  } else if (W == 2) {
+    put_t(1, mm16(Y, mml(2, 1, 1, z), z));
+    p0 = mml(2, 0, 0, z);
+  } else if (W == 3) {
+    put_t(2, mm16(Y, mml(3, 2, 2, z), z));
+    p1 = mml(3, 1, 1, z);
+    p0 = mml(3, 0, 0, z);
+  }
+  __syncthreads();
+  if (W == 2) {
+    put_t(0, mm16(Y, mml(2, 1, 0, p0), z));
+  } else if (W == 3) {
+    put_t(1, mm16(Y, mml(3, 2, 1, p1), z));
+    p0 = mml(3, 1, 0, p0);
+  }
+  __syncthreads();
+  if (W == 3) put_t(0, mm16(Y, mml(3, 2, 0, p0), z));
+  __syncthreads();
+}
+
 // ===========================================================================
 // KDA: per-key-channel log2 gate per (token, head, channel)
 // ===========================================================================
@@ -862,7 +882,7 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
   }
   __syncthreads();
 
-  invert_unit_lower(u.mat.A, u.mat.T, wave, lane);
+  invert_unit_lower<kLdF>(u.mat.A, u.mat.T, wave, lane);
 
   store_t_aqk(a, cm, tid, u.mat.T, u.mat.aqk);
   if (tid < 64) {
