@@ -1,5 +1,7 @@
 // Prepare kernels: everything of one (chunk, head) that does not depend on
-// the carried state. One workgroup of 4 waves per (chunk, head).
+// the carried state. GDN: persistent workgroups of 4 waves (three per compute
+// unit) looping over the (chunk, head) items; KDA: one workgroup of 4 waves
+// per (chunk, head).
 //
 // Steps of the eager chunk algorithm on the hyper-parallel "Diff Coverage"
 // page (gate build 2026-09-10; _prepare_gdn_chunks_for_summary), done here:
@@ -39,9 +41,6 @@ constexpr int kLdF = kChunk + 1;    // fp32 row stride of a 64 x 64 matrix in LD
 constexpr int kLdQ = kChunk + 8;    // bf16 row stride of a 64 x 64 matrix in LDS
 constexpr int kLdG = kDim + 4;      // fp32 row stride of the 64 x 128 KDA gate
 
-// the 10 lower 16x16 tiles (I >= J) of a 64 x 64 matrix
-__constant__ int kTileI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ int kTileJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 // the 6 tiles below the diagonal (I > J), and the 6 pairs i > j of a 4 x 4 block
 __constant__ int kOffI[6] = {1, 2, 2, 3, 3, 3};
 __constant__ int kOffJ[6] = {0, 0, 1, 0, 1, 2};
@@ -103,15 +102,6 @@ __device__ __forceinline__ void put_qk_norms(const PrepareArgs& a, const ChunkIn
       sRq[r] = valid ? (l2 ? 1.0f / sqrtf(ssq + 1e-6f) : 1.0f) : 0.0f;
     }
   }
-}
-
-// q, k rows of the chunk into LDS (zero past the end), normalisation factors.
-// All global loads are issued before the first LDS write.
-__device__ __forceinline__ void load_qk_norms(const PrepareArgs& a, const ChunkInfo& ci, int h, int tid,
-                                              uint16_t* sk, uint16_t* sq, float* sRk, float* sRq) {
-  QKRegs x;
-  fetch_qk(a, ci, h, tid, x);
-  put_qk_norms(a, ci, tid, x, sk, sq, sRk, sRq);
 }
 
 // beta (with the optional sigmoid) by wave 0; zero past the end.
