@@ -90,3 +90,27 @@ def test_short_conv_halo_continuation(gdn):
     tail = gi.ConvInputs(**{**inp.__dict__, "T": 200 - t0, "x": np.ascontiguousarray(inp.x[:, t0:]),
                             "halo": np.ascontiguousarray(inp.x[:, t0 - hw:t0])})
     assert np.array_equal(_run(gdn, tail), full[:, t0:])
+
+
+def test_conv_feeds_gdn_forward(gdn):
+    """The layer order of the pages: the mixed projections go through the
+    ShortConv + SiLU, are split into q, k, v (16 heads each) and run through
+    the GDN forward; against the conv oracle followed by the token recurrence
+    on the same bf16 q, k, v."""
+    B, T, H = 1, 300, 4
+    D = 3 * H * 128
+    cin = gi.make_conv_inputs(B, T, D, W=4, seed=23)
+    y = _run(gdn, cin)                                   # fp64 view of the bf16 GPU output
+    y_ref = oracle.short_conv(cin)
+    assert not (np.abs(y - y_ref) > RTOL * np.abs(y_ref) + ATOL).any()
+    bits = gi.f32_to_bf16_bits(y.astype(np.float32))     # exactly the GPU's bf16 values
+    q, k, v = (np.ascontiguousarray(bits[:, :, i * H * 128:(i + 1) * H * 128]).reshape(B, T, H, 128)
+               for i in range(3))
+    base = gi.make_inputs("gdn", B=B, T=T, H=H)
+    inp = gi.GdnInputs(**{**base.__dict__, "q": q, "k": k, "v": v})
+    from gpu_util import O_ATOL, S_RTOL, o_err, run_gpu, s_err
+    o, fs = run_gpu(inp)
+    o_ref, s_ref = oracle.recur(inp)
+    eo, es = o_err(o, o_ref), s_err(fs, s_ref)
+    _say("  conv -> GDN: o err %.3e  S rel err %.3e" % (eo, es))
+    assert eo <= O_ATOL and es <= S_RTOL
