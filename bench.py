@@ -88,9 +88,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gdn", choices=["gdn", "varlen", "long", "kda", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="fwd", choices=["fwd", "summary", "conv"],
+    ap.add_argument("--op", default="fwd", choices=["fwd", "summary", "conv", "bwd"],
                     help="fwd: the forward pass (default); summary: the affine state summary and its apply step; "
-                         "conv: the causal depthwise Conv1d + SiLU forming q, k, v (D = 3*H*128, W = 4)")
+                         "conv: the causal depthwise Conv1d + SiLU forming q, k, v (D = 3*H*128, W = 4); "
+                         "bwd: the GDN backward pass")
     ap.add_argument("--scrub-mib", type=int, default=1024, help="MiB read between timed calls (0: none)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run plain device-to-device copies of this many MiB (counter calibration)")
@@ -162,6 +163,59 @@ def bench_summary(args, gdn, gi, inp, q, k, v, g, beta, dev):
                    "p10_ms": round(p10, 5), "p90_ms": round(p90, 5)},
         "apply_us": round(ams * 1e3, 2),
         "apply_pairs": N * H,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_bwd(args, gdn, gi, inp, q, k, v, g, beta, dev):
+    """Times gdn_chunk_bwd on the workload (forward recompute: prepare and the
+    state pass storing h and v_new; then the reverse state pass, the state
+    products and the per-chunk gradients), each call after a 1 GiB read;
+    prints one JSON line. The cotangents are seeded N(0,1) (dO, bf16) and
+    0.1 N(0,1) (dS_final)."""
+    import torch
+    if inp.kda:
+        raise SystemExit("the backward pass is built for the GDN (scalar) gate only")
+    B, T, H, K, V = inp.B, inp.T, inp.H, inp.K, inp.V
+    N = inp.num_seqs
+    gen = torch.Generator(device=dev).manual_seed(7)
+    do = torch.randn((B, T, H, V), device=dev, generator=gen).to(torch.bfloat16)
+    dsf = torch.randn((N, H, K, V), device=dev, generator=gen) * 0.1
+    s0 = None if inp.initial_state is None else torch.from_numpy(inp.initial_state).to(dev)
+    cu = None if inp.cu_seqlens is None else np.ascontiguousarray(inp.cu_seqlens, dtype=np.int32)
+    need = gdn.lib.gdn_chunk_bwd_workspace_bytes(B, T, H, K, V, N, None if cu is None else
+                                                 cu.ctypes.data_as(ctypes.c_void_p), inp.flags & 3)
+    ws = torch.empty(int(need), dtype=torch.uint8, device=dev)
+    kw = dict(scale=inp.scale, initial_state=s0, d_final_state=dsf, cu_seqlens=inp.cu_seqlens,
+              l2norm_qk=bool(inp.flags & gi.FLAG_L2NORM_QK), beta_sigmoid=bool(inp.flags & gi.FLAG_BETA_SIGMOID),
+              workspace=ws)
+    call = lambda: gdn.gdn_chunk_bwd(q, k, v, g, beta, do, **kw)
+    scrub = torch.full((max(args.scrub_mib, 1) * (1 << 20) // 4,), 1.0, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(args.steps):
+        if args.scrub_mib:
+            scrub.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    tokens = B * T
+    line = {
+        "metric": "bwd tokens/s (GDN gradients dq dk dv dg dbeta dS0)",
+        "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": "GDN backward B=%d T=%d H=%d, %d sequences, flags %d" % (B, T, H, N, inp.flags & 3),
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": K, "parallelism": "single-gpu"},
+        "timing": {"per_call": "median of %d calls, %d MiB read before each" % (args.steps, args.scrub_mib),
+                   "p10_ms": round(float(np.percentile(ts, 10)), 5),
+                   "p90_ms": round(float(np.percentile(ts, 90)), 5)},
     }
     print(json.dumps(line), flush=True)
 
@@ -244,6 +298,9 @@ def main():
     cu_p = None if cu is None else cu.ctypes.data_as(ctypes.c_void_p)
     if args.op == "summary":
         bench_summary(args, gdn, gi, inp, q, k, v, g, beta, dev)
+        return
+    if args.op == "bwd":
+        bench_bwd(args, gdn, gi, inp, q, k, v, g, beta, dev)
         return
     stream = torch.cuda.current_stream(dev)
     fn = gdn.lib.kda_chunk_fwd if inp.kda else gdn.lib.gdn_chunk_fwd

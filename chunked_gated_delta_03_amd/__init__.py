@@ -36,7 +36,7 @@ EXPORTED = (
     "gdn_chunk_fwd", "kda_chunk_fwd", "gdn_stage_prepare", "gdn_stage_fwd_h", "gdn_stage_finalize",
     "gdn_timing_enable", "gdn_timing_read", "gdn_state_summary", "kda_state_summary",
     "gdn_state_summary_workspace_bytes", "gdn_state_summary_apply", "gdn_short_conv",
-    "gdn_short_conv_workspace_bytes",
+    "gdn_short_conv_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes",
 )
 
 
@@ -83,6 +83,11 @@ def _load() -> ctypes.CDLL:
     lib.gdn_short_conv_workspace_bytes.argtypes = [i32, p]
     lib.gdn_short_conv.restype = ctypes.c_int
     lib.gdn_short_conv.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, p, p, sz, p]
+    lib.gdn_chunk_bwd_workspace_bytes.restype = sz
+    lib.gdn_chunk_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, p, u32]
+    lib.gdn_chunk_bwd.restype = ctypes.c_int
+    lib.gdn_chunk_bwd.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p,
+                                  p, p, p, p, p, p, p, sz, p]
     lib.gdn_stage_prepare.restype = ctypes.c_int
     lib.gdn_stage_prepare.argtypes = [i32, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p, p, p, p]
     lib.gdn_stage_fwd_h.restype = ctypes.c_int
@@ -215,6 +220,44 @@ def kda_chunk_fwd(q, k, v, g, beta, scale: Optional[float] = None, initial_state
     """KDA forward: as :func:`gdn_chunk_fwd` with g fp32 [B,T,H,128] in log2 units."""
     return _chunk_fwd(True, q, k, v, g, beta, scale, initial_state, cu_seqlens, l2norm_qk, beta_sigmoid,
                       output_final_state, workspace, stream)
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, do, scale: Optional[float] = None, initial_state=None, d_final_state=None,
+                  cu_seqlens=None, l2norm_qk: bool = False, beta_sigmoid: bool = False,
+                  workspace: Optional[torch.Tensor] = None, stream=None):
+    """GDN backward: gradients of <do, o> + <d_final_state, final_state> for the
+    forward of :func:`gdn_chunk_fwd` with the same arguments. do bf16
+    [B,T,H,128]; d_final_state fp32 [N,H,128,128] or None (zero).
+    Returns fp32 (dq, dk, dv [B,T,H,128], dg [B,T,H] w.r.t. the raw gate,
+    dbeta [B,T,H] w.r.t. beta as passed, d_initial_state [N,H,128,128])."""
+    cu = _cu_array(cu_seqlens)
+    B, T, H, K, V, N = _check_inputs(q, k, v, g, beta, False, initial_state, cu)
+    if (not isinstance(do, torch.Tensor) or do.dtype != torch.bfloat16 or not do.is_contiguous()
+            or tuple(do.shape) != (B, T, H, V) or do.device != q.device):
+        raise ValueError("do must be a contiguous bf16 [B,T,H,V] tensor on %s" % q.device)
+    if d_final_state is not None and (d_final_state.dtype != torch.float32 or not d_final_state.is_contiguous()
+                                      or tuple(d_final_state.shape) != (N, H, K, V)
+                                      or d_final_state.device != q.device):
+        raise ValueError("d_final_state must be a contiguous fp32 [N,H,K,V] tensor on %s" % q.device)
+    scale = K ** -0.5 if scale is None else float(scale)
+    flags = _flags(l2norm_qk, beta_sigmoid, False)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq, dk, dv = (torch.empty((B, T, H, K), **f32) for _ in range(3))
+    dg, dbeta = torch.empty((B, T, H), **f32), torch.empty((B, T, H), **f32)
+    ds0 = torch.empty((N, H, K, V), **f32)
+    need = lib.gdn_chunk_bwd_workspace_bytes(B, T, H, K, V, N, _cu_ptr(cu), flags)
+    if need == 0:
+        workspace = None
+    elif workspace is None:
+        workspace = torch.empty(int(need), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel() * workspace.element_size(), need))
+    _check(lib.gdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _cu_ptr(cu), N,
+                             B, T, H, K, V, scale, flags, _ptr(do), _ptr(d_final_state), _ptr(dq), _ptr(dk),
+                             _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(ds0), _ptr(workspace),
+                             0 if workspace is None else workspace.numel() * workspace.element_size(),
+                             _stream_ptr(q.device, stream)))
+    return dq, dk, dv, dg, dbeta, ds0
 
 
 def state_summary(k, v, g, beta, q=None, cu_seqlens=None, kda: bool = False, l2norm_qk: bool = False,

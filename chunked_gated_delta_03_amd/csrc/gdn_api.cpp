@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "../../include/gdn.h"
+#include "gdn_bwd.h"
 #include "gdn_kernels.h"
 
 namespace {
@@ -469,6 +470,130 @@ int state_summary(bool kda, const void* q, const void* k, const void* v, const f
   return GDN_OK;
 }
 
+// Backward pass (GDN): workspace = forward layout | h | v_new | dS_next |
+// dv_new | E, F, D | <dS_next, S>, each 256-byte aligned.
+struct BwdLayout {
+  Layout fwd;
+  size_t h = 0, vnew = 0, dhn = 0, dvn = 0, efd = 0, sdot = 0, total = 0;
+};
+
+BwdLayout bwd_layout_for(const Problem& p) {
+  BwdLayout L;
+  L.fwd = layout_for(p, true);
+  size_t off = L.fwd.total;
+  const size_t cmH = (size_t)p.NT * p.H;
+  const size_t state = cmH * GDN_HEAD_DIM * GDN_HEAD_DIM * sizeof(float);
+  const size_t rows = cmH * GDN_CHUNK * GDN_HEAD_DIM * sizeof(float);
+  L.h = off;
+  off += align256(state);
+  L.vnew = off;
+  off += align256(rows);
+  L.dhn = off;
+  off += align256(state);
+  L.dvn = off;
+  off += align256(rows);
+  L.efd = off;
+  off += align256(3 * rows);
+  L.sdot = off;
+  off += align256(cmH * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+// Recompute the forward intermediates (prepare; state pass storing the
+// state entering every chunk and v_new), then the three backward kernels.
+int chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
+              const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+              int32_t H, int32_t K, int32_t V, float scale, uint32_t flags, const void* d_o,
+              const float* d_final_state, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+              float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  g_last_error.clear();
+  Problem p;
+  p.kda = false;
+  int rc = check_shape(B, T, H, K, V, num_seqs, cu_seqlens, p);
+  if (rc) return rc;
+  rc = check_common(q, k, v, g, beta, scale, flags);
+  if (rc) return rc;
+  if (!d_o || !dq || !dk || !dv || !dg || !dbeta)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "d_o, dq, dk, dv, dg and dbeta must be non-NULL");
+  if (!aligned16(d_o) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "d_o, dq, dk and dv must be 16-byte aligned");
+  int cus = 0;
+  rc = check_device(&cus);
+  if (rc) return rc;
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const BwdLayout L = bwd_layout_for(p);
+  Workspace W;
+  rc = acquire_workspace(workspace, workspace_bytes, L.total, stream, W);
+  if (rc) return rc;
+  if (p.packed) {
+    rc = upload_tables(p, W.base + L.fwd.tab, stream);
+    if (rc) return rc;
+  }
+  const gdn::Geometry geo = make_geometry(p, W.base + L.fwd.tab);
+
+  gdn::PrepareArgs pa{};
+  pa.q = static_cast<const uint16_t*>(q);
+  pa.k = static_cast<const uint16_t*>(k);
+  pa.g = g;
+  pa.beta = static_cast<const uint16_t*>(beta);
+  pa.tmat = reinterpret_cast<uint16_t*>(W.base + L.fwd.tmat);
+  pa.aqk = reinterpret_cast<uint16_t*>(W.base + L.fwd.aqk);
+  pa.vec = reinterpret_cast<float*>(W.base + L.fwd.vec);
+  pa.geo = geo;
+  pa.H = H;
+  pa.scale = scale;
+  pa.flags = flags & ~(uint32_t)GDN_OUTPUT_FINAL_STATE;
+  pa.cus = cus;
+  hipError_t e = gdn::launch_prepare(false, pa, stream);
+  if (e != hipSuccess) return hip_fail(e, "prepare launch");
+
+  gdn::FwdArgs fa{};
+  fa.k = pa.k;
+  fa.v = static_cast<const uint16_t*>(v);
+  fa.tmat = pa.tmat;
+  fa.aqk = pa.aqk;
+  fa.vec = pa.vec;
+  fa.s0 = initial_state;
+  fa.sfinal = nullptr;
+  fa.h_out = reinterpret_cast<float*>(W.base + L.h);
+  fa.vnew_out = reinterpret_cast<float*>(W.base + L.vnew);
+  fa.geo = geo;
+  fa.H = H;
+  e = gdn::launch_fwd(false, true, false, fa, stream);
+  if (e != hipSuccess) return hip_fail(e, "forward recompute launch");
+
+  gdn::BwdArgs ba{};
+  ba.q = pa.q;
+  ba.k = pa.k;
+  ba.v = fa.v;
+  ba.dout = static_cast<const uint16_t*>(d_o);
+  ba.tmat = pa.tmat;
+  ba.aqk = pa.aqk;
+  ba.vec = pa.vec;
+  ba.h = fa.h_out;
+  ba.vnew = fa.vnew_out;
+  ba.dsfinal = d_final_state;
+  ba.dhn = reinterpret_cast<float*>(W.base + L.dhn);
+  ba.dvn = reinterpret_cast<float*>(W.base + L.dvn);
+  ba.efd = reinterpret_cast<float*>(W.base + L.efd);
+  ba.sdot = reinterpret_cast<float*>(W.base + L.sdot);
+  ba.ds0 = d_initial_state;
+  ba.dq = dq;
+  ba.dk = dk;
+  ba.dv = dv;
+  ba.dg = dg;
+  ba.dbeta = dbeta;
+  ba.geo = geo;
+  ba.H = H;
+  ba.scale = scale;
+  ba.flags = flags;
+  e = gdn::launch_gdn_bwd(ba, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return GDN_OK;
+}
+
 // Shared front half of the stage entries: validation, tables, geometry.
 struct StageCtx {
   Problem p;
@@ -549,6 +674,27 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   void* workspace, size_t workspace_bytes, void* stream) {
   return chunk_fwd(true, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, scale, flags, o,
                    final_state, workspace, workspace_bytes, stream);
+}
+
+size_t gdn_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                     const int32_t* cu_seqlens, uint32_t flags) {
+  g_last_error.clear();
+  Problem p;
+  if (check_shape(B, T, H, K, V, num_seqs, cu_seqlens, p)) return 0;
+  if (flags & ~kKnownFlags) {
+    fail(GDN_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags & ~kKnownFlags);
+    return 0;
+  }
+  return bwd_layout_for(p).total;
+}
+
+int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                  int32_t H, int32_t K, int32_t V, float scale, uint32_t flags, const void* d_o,
+                  const float* d_final_state, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                  float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_bwd(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, scale, flags, d_o,
+                   d_final_state, dq, dk, dv, dg, dbeta, d_initial_state, workspace, workspace_bytes, stream);
 }
 
 int gdn_state_summary(const void* q, const void* k, const void* v, const float* g, const void* beta,

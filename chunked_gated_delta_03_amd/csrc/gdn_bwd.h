@@ -1,0 +1,37 @@
+// Argument block and launcher of the backward-pass kernels (host + device).
+#pragma once
+
+#include "gdn_kernels.h"
+
+namespace gdn {
+
+// Backward pass (GDN scalar gate): gradients of <dO, o> + <dS_final, S_final>.
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;      // [B*T,H,V] bf16
+  const uint16_t* tmat;      // prepare outputs, as FwdArgs
+  const uint16_t* aqk;
+  const float* vec;
+  const float* h;            // [H,NT,K,V] state entering each chunk (forward stage)
+  const float* vnew;         // [H,NT,64,V] U - W S (forward stage)
+  const float* dsfinal;      // [N,H,K,V] or nullptr (zero)
+  float* dhn;                // [H,NT,K,V] gradient w.r.t. the state leaving each chunk
+  float* dvn;                // [H,NT,64,V] gradient w.r.t. v_new
+  float* efd;                // [3][H,NT,64,K]: dO S^T, dv_new S^T, v_new dS_next^T
+  float* sdot;               // [H,NT] <dS_next, S>
+  float* ds0;                // [N,H,K,V] or nullptr
+  float* dq;                 // [B*T,H,K] fp32
+  float* dk;
+  float* dv;
+  float* dg;                 // [B*T,H] fp32
+  float* dbeta;              // [B*T,H] fp32
+  Geometry geo;
+  int H;
+  float scale;
+  uint32_t flags;
+};
+hipError_t launch_gdn_bwd(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace gdn

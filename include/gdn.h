@@ -171,6 +171,43 @@ int gdn_stage_finalize(int32_t kda, const void* q, const void* aqk, const float*
                        int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, void* o, void* stream);
 
 /*
+ * Backward pass, GDN scalar gate (the three stages bwd_prepare_saved,
+ * bwd_state_saved and bwd_finish_saved of _GDNStateP2PTritonFunction.backward
+ * on the hyper-parallel "Diff Coverage" page of 2026-09-10; as the native
+ * backward of the 2026-11-06 gate build, the gate gradient is the one of the
+ * raw per-token gate). For the forward of gdn_chunk_fwd with the same
+ * arguments, the gradients of
+ *   L = <d_o, o> + <d_final_state, final_state>
+ * with respect to the raw inputs:
+ *   d_o            [B,T,H,V] bf16, the output cotangent (required);
+ *   d_final_state  [N,H,K,V] fp32 or NULL (zero);
+ *   dq, dk         [B,T,H,K] fp32 w.r.t. q, k as passed (through the
+ *                  in-kernel L2-norm when GDN_L2NORM_QK is set);
+ *   dv             [B,T,H,V] fp32;
+ *   dg             [B,T,H]   fp32 w.r.t. the raw gate g (natural log);
+ *   dbeta          [B,T,H]   fp32 w.r.t. beta as passed (through the sigmoid
+ *                  when GDN_BETA_SIGMOID is set);
+ *   d_initial_state [N,H,K,V] fp32 or NULL (not written); the gradient
+ *                  w.r.t. initial_state (NULL initial_state meaning zero).
+ * All other arguments as gdn_chunk_fwd (GDN_OUTPUT_FINAL_STATE is ignored).
+ * Outputs are device arrays owned by the caller; dq, dk, dv and d_o 16-byte
+ * aligned. The call recomputes the forward intermediates (prepare kernel,
+ * then the state pass storing the state entering every chunk and v_new),
+ * then runs the reverse state pass and the per-chunk gradient kernels, all
+ * on `stream`. workspace: as gdn_chunk_fwd, sized by
+ * gdn_chunk_bwd_workspace_bytes (0 on a contract error; about
+ * NT*H*(192 KiB) plus the forward's). Errors as gdn_chunk_fwd; nothing is
+ * launched on error.
+ */
+size_t gdn_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                     const int32_t* cu_seqlens, uint32_t flags);
+int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                  int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, float scale, uint32_t flags,
+                  const void* d_o, const float* d_final_state, float* dq, float* dk, float* dv, float* dg,
+                  float* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Affine state summary (_compute_gdn_state_summary_from_prepared and
  * _apply_gdn_state_summary on the 2026-09-10 "Diff Coverage" page): for every
  * sequence n and head h, the final state is affine in the initial one,

@@ -28,7 +28,8 @@ def test_header_declares_expected_entry_points():
     for must in ("gdn_chunk_fwd", "kda_chunk_fwd", "gdn_last_error", "gdn_chunk_fwd_workspace_bytes",
                  "gdn_stage_prepare", "gdn_stage_fwd_h", "gdn_stage_finalize", "gdn_num_chunks",
                  "gdn_state_summary", "kda_state_summary", "gdn_state_summary_workspace_bytes",
-                 "gdn_state_summary_apply", "gdn_short_conv", "gdn_short_conv_workspace_bytes"):
+                 "gdn_state_summary_apply", "gdn_short_conv", "gdn_short_conv_workspace_bytes",
+                 "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes"):
         assert must in names
 
 
@@ -197,3 +198,38 @@ def test_short_conv_validates_before_device(gdn, kw, code, msg):
     cu2 = np.asarray([0, 5, 9], dtype=np.int32)
     assert gdn.lib.gdn_short_conv_workspace_bytes(2, cu2.ctypes.data_as(ctypes.c_void_p)) == 256
     assert gdn.lib.gdn_short_conv_workspace_bytes(2, None) == 0
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(K=64), 2, "K = V = 128"),
+    (dict(B=0), 1, "B, T and H"),
+    (dict(flags=8), 1, "unknown flag"),
+    (dict(scale=0.0), 1, "scale"),
+    (dict(q=None), 1, "non-NULL"),
+    (dict(do=None), 1, "d_o, dq"),
+    (dict(dg=None), 1, "d_o, dq"),
+    (dict(dq=ctypes.c_void_p(0x100008)), 1, "aligned"),
+    (dict(B=2, cu=[0, 4, 10], T=10), 1, "B == 1"),
+    (dict(T=10, cu=[0, 4, 9]), 1, "must equal T"),
+])
+def test_chunk_bwd_validates_before_device(gdn, kw, code, msg):
+    a = dict(B=1, T=64, H=2, K=128, V=128, flags=3, scale=0.1, q=FAKE, do=FAKE, dq=FAKE, dg=FAKE, cu=None)
+    a.update(kw)
+    cu = None if a["cu"] is None else np.asarray(a["cu"], dtype=np.int32)
+    n = a["B"] if cu is None else len(cu) - 1
+    rc = gdn.lib.gdn_chunk_bwd(a["q"], FAKE, FAKE, FAKE, FAKE, None,
+                               None if cu is None else cu.ctypes.data_as(ctypes.c_void_p), n, a["B"], a["T"], a["H"],
+                               a["K"], a["V"], a["scale"], a["flags"], a["do"], None, a["dq"], FAKE, FAKE, a["dg"],
+                               FAKE, None, None, 0, None)
+    assert rc == code
+    assert msg in gdn.last_error()
+
+
+def test_chunk_bwd_workspace_bytes(gdn):
+    ws = gdn.lib.gdn_chunk_bwd_workspace_bytes
+    fwd = gdn.lib.gdn_chunk_fwd_workspace_bytes(4, 4096, 16, 128, 128, 4, None, 3)
+    b = ws(4, 4096, 16, 128, 128, 4, None, 3)
+    cmh = 4 * 64 * 16
+    assert b >= fwd + cmh * (2 * 128 * 128 * 4 + 5 * 64 * 128 * 4 + 4) and b % 256 == 0
+    assert ws(4, 4096, 16, 64, 128, 4, None, 3) == 0
+    assert ws(4, 4096, 16, 128, 128, 4, None, 8) == 0
