@@ -43,25 +43,46 @@ constexpr int kL32 = 36;    // fp32, 32 wide
 constexpr int kLb = 136;    // bf16, 128 wide
 constexpr int kVecStride = kVecRows * kChunk;
 
-__device__ __forceinline__ float ldv(const float* p) { return *p; }
-__device__ __forceinline__ float ldv(const uint16_t* p) { return bf2f(*p); }
+// Four consecutive contraction slots k .. k+3 of row (or column) rc of an
+// operand stored at p[rc * SR + k * SK] (LDS): one 16-byte (fp32) or 8-byte
+// (bf16) read when the contraction index is the contiguous one.
+template <int SR, int SK>
+__device__ __forceinline__ void fetch4(const float* p, int rc, int k, float (&v)[4]) {
+  if constexpr (SK == 1) {
+    const float4 t = *reinterpret_cast<const float4*>(p + rc * SR + k);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = p[rc * SR + (k + j) * SK];
+  }
+}
+template <int SR, int SK>
+__device__ __forceinline__ void fetch4(const uint16_t* p, int rc, int k, float (&v)[4]) {
+  if constexpr (SK == 1) {
+    const uint2 t = *reinterpret_cast<const uint2*>(p + rc * SR + k);
+    v[0] = __uint_as_float(t.x << 16); v[1] = __uint_as_float(t.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(t.y << 16); v[3] = __uint_as_float(t.y & 0xFFFF0000u);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = bf2f(p[rc * SR + (k + j) * SK]);
+  }
+}
 
 // One 16x16 output tile of C = op(A) op(B) on v_mfma_f32_16x16x4f32:
 // acc (lane (g, l) holds C[r0 + 4g + e][c0 + l]) += sum_k A(r, k) B(k, c),
-// k over [0, kd), kd a multiple of 16. A(r, k) is a[r * sar + k * sak] and
-// B(k, c) is b[k * sbk + c * sbc] (LDS, fp32 or bf16), so transposed
-// operands are a matter of strides. Contraction slot g at step ks is
-// k0 + 4g + ks for both operands.
-template <class TA, class TB>
-__device__ __forceinline__ f32x4 tile_mm(const TA* a, int sar, int sak, const TB* b, int sbk, int sbc, int r0,
-                                         int c0, int kd, int lane, f32x4 acc) {
+// k over [0, kd), kd a multiple of 16. A(r, k) is a[r * SAR + k * SAK] and
+// B(k, c) is b[k * SBK + c * SBC] (LDS, fp32 or bf16), so transposed
+// operands are a matter of strides. Lane group g takes the contraction slots
+// k0 + 4g .. k0 + 4g + 3 (one per MFMA step) of both operands.
+template <int SAR, int SAK, int SBK, int SBC, class TA, class TB>
+__device__ __forceinline__ f32x4 tile_mm(const TA* a, const TB* b, int r0, int c0, int kd, int lane, f32x4 acc) {
   const int l = lane & 15, g = lane >> 4;
-  const TA* ap = a + (r0 + l) * sar + 4 * g * sak;
-  const TB* bp = b + (c0 + l) * sbc + 4 * g * sbk;
   for (int k0 = 0; k0 < kd; k0 += 16) {
+    float av[4], bv[4];
+    fetch4<SAR, SAK>(a, r0 + l, k0 + 4 * g, av);
+    fetch4<SBC, SBK>(b, c0 + l, k0 + 4 * g, bv);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ldv(ap + (k0 + ks) * sak), ldv(bp + (k0 + ks) * sbk), acc, 0, 0, 0);
+    for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks], bv[ks], acc, 0, 0, 0);
   }
   return acc;
 }
@@ -77,30 +98,109 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
-// T (fp32, natural column order, stride kL64) from the prepare kernel's
-// bf16 hi | lo rows with permuted columns
-__device__ __forceinline__ void load_t(float* sT, const uint16_t* tm, int tid) {
-  for (int idx = tid; idx < kChunk * kChunk; idx += 256) {
-    const int r = idx >> 6, p = idx & 63;
-    sT[r * kL64 + unperm_col(p)] = bf2f(tm[r * 128 + p]) + bf2f(tm[r * 128 + 64 + p]);
-  }
-}
-
 // ===========================================================================
 // Kernel 1: reverse state pass. One workgroup per (sequence, head, 32 value
 // columns); the state gradient block (128 x 32) lives in registers, wave w
-// holding rows 32w .. 32w+31.
+// holding rows 32w .. 32w+31. Every operand sits in LDS with its contraction
+// index contiguous (transposed copies where a product contracts over the
+// chunk rows), and the next chunk's inputs are fetched into registers while
+// the current chunk computes.
 // ===========================================================================
-struct DhSmem {
-  float k[kChunk * kL128];   // raw k
-  float qg[kChunk * kL128];  // q scaled by scale rq e^G
-  float aqk[kChunk * kL64];  // scale Qn Kn^T * Gamma (lower, with diagonal)
-  float t[kChunk * kL64];
-  float dO[kChunk * kL32];
-  float dS[kDim * kL32];
-  float z[kChunk * kL32];    // dV', then diag(b rk e^G) T^T dV'
+constexpr int kLt = 72;  // bf16 row stride of 128 x 64 transposed matrices
+
+struct alignas(16) DhSmem {
+  uint16_t k[kChunk * kLb];   // k [i][kk]
+  uint16_t kT[kDim * kLt];    // k^T [kk][i]
+  float qgT[kDim * kL64];     // (q * scale rq e^G)^T [kk][i]
+  float aqkT[kChunk * kL64];  // Aqk^T [i][j]
+  float tT[kChunk * kL64];    // T^T [j][i]
+  float dST[32 * kL128];      // dS^T [c][kk]
+  float dOT[32 * kL64];       // dO^T [c][i]
+  float zT[32 * kL64];        // dV'^T, then Z^T [c][i]
   float kgs[kChunk], xs[kChunk];
 };
+
+// one chunk's inputs in flight, per thread
+struct DhRegs {
+  u16x8 k[4], q[4];
+  float qs[4];
+  u16x8 a[2];
+  u16x8 th[2], tl[2];
+  u16x8 o;
+  float kgs, xs;
+};
+
+__device__ __forceinline__ void dh_fetch(const BwdArgs& a, int h, int c, int v0, int tid, DhRegs& R) {
+  const ChunkInfo ci = a.geo.chunk(c);
+  const size_t cm = (size_t)h * a.geo.NT + c;
+  const float* vec = a.vec + cm * kVecStride;
+  const u16x8 z8 = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int idx = tid + 256 * m, r = idx >> 4, cc = (idx & 15) * 8;
+    R.k[m] = z8;
+    R.q[m] = z8;
+    R.qs[m] = 0.0f;
+    if (r < ci.len) {
+      const size_t off = ((size_t)(ci.tok0 + r) * a.H + h) * kDim + cc;
+      R.k[m] = *reinterpret_cast<const u16x8*>(a.k + off);
+      R.q[m] = *reinterpret_cast<const u16x8*>(a.q + off);
+      R.qs[m] = vec[3 * kChunk + r];
+    }
+  }
+  const uint16_t* aq = a.aqk + cm * 4096;
+  const uint16_t* tm = a.tmat + cm * (kChunk * 128);
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int idx = tid + 256 * m, r = idx >> 3, p8 = (idx & 7) * 8;
+    R.a[m] = *reinterpret_cast<const u16x8*>(aq + r * 64 + p8);
+    R.th[m] = *reinterpret_cast<const u16x8*>(tm + r * 128 + p8);
+    R.tl[m] = *reinterpret_cast<const u16x8*>(tm + r * 128 + 64 + p8);
+  }
+  {
+    const int r = tid >> 2, cc = (tid & 3) * 8;
+    R.o = z8;
+    if (r < ci.len) R.o = *reinterpret_cast<const u16x8*>(a.dout + ((size_t)(ci.tok0 + r) * a.H + h) * kDim + v0 + cc);
+  }
+  R.kgs = 0.0f;
+  R.xs = 0.0f;
+  if (tid < kChunk && tid < ci.len) {
+    R.kgs = vec[2 * kChunk + tid];
+    R.xs = vec[1 * kChunk + tid];
+  }
+}
+
+__device__ __forceinline__ void dh_put(DhSmem& sm, const DhRegs& R, int tid) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int idx = tid + 256 * m, r = idx >> 4, cc = (idx & 15) * 8;
+    *reinterpret_cast<u16x8*>(sm.k + r * kLb + cc) = R.k[m];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sm.kT[(cc + e) * kLt + r] = R.k[m][e];
+      sm.qgT[(cc + e) * kL64 + r] = bf2f(R.q[m][e]) * R.qs[m];
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int idx = tid + 256 * m, r = idx >> 3, p8 = (idx & 7) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int col = unperm_col(p8 + e);
+      sm.aqkT[col * kL64 + r] = bf2f(R.a[m][e]);
+      sm.tT[col * kL64 + r] = bf2f(R.th[m][e]) + bf2f(R.tl[m][e]);
+    }
+  }
+  {
+    const int r = tid >> 2, cc = (tid & 3) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm.dOT[(cc + e) * kL64 + r] = bf2f(R.o[e]);
+  }
+  if (tid < kChunk) {
+    sm.kgs[tid] = R.kgs;
+    sm.xs[tid] = R.xs;
+  }
+}
 
 __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
   int n, h, vb;
@@ -124,86 +224,53 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
         ds[rt][ct][e] = a.dsfinal ? a.dsfinal[(unit * kDim + row) * kDim + col] : 0.0f;
       }
 
+  DhRegs R;
+  dh_fetch(a, h, si.c0 + si.nch - 1, v0, tid, R);
   for (int jc = si.nch - 1; jc >= 0; --jc) {
     const int c = si.c0 + jc;
-    const ChunkInfo ci = a.geo.chunk(c);
     const size_t cm = (size_t)h * a.geo.NT + c;
-    const float* vec = a.vec + cm * kVecStride;
-    // gradient w.r.t. the state leaving chunk c
+    dh_put(sm, R, tid);
+    // gradient w.r.t. the state leaving chunk c: to memory and to LDS (dS^T)
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < 2; ++ct) {
+        const int row0 = 32 * w + 16 * rt + 4 * g, col = 16 * ct + l;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 32 * w + 16 * rt + 4 * g + e, col = 16 * ct + l;
-          a.dhn[cm * (kDim * kDim) + row * kDim + v0 + col] = ds[rt][ct][e];
-          sm.dS[row * kL32 + col] = ds[rt][ct][e];
-        }
-    for (int idx = tid; idx < kChunk * 16; idx += 256) {
-      const int r = idx >> 4, cc = (idx & 15) * 8;
-      u16x8 kv = u16x8{0, 0, 0, 0, 0, 0, 0, 0}, qv = kv;
-      float qs = 0.0f;
-      if (r < ci.len) {
-        const size_t off = ((size_t)(ci.tok0 + r) * H + h) * kDim + cc;
-        kv = *reinterpret_cast<const u16x8*>(a.k + off);
-        qv = *reinterpret_cast<const u16x8*>(a.q + off);
-        qs = vec[3 * kChunk + r];
+        for (int e = 0; e < 4; ++e) a.dhn[cm * (kDim * kDim) + (row0 + e) * kDim + v0 + col] = ds[rt][ct][e];
+        *reinterpret_cast<float4*>(sm.dST + col * kL128 + row0) =
+            make_float4(ds[rt][ct][0], ds[rt][ct][1], ds[rt][ct][2], ds[rt][ct][3]);
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sm.k[r * kL128 + cc + e] = bf2f(kv[e]);
-        sm.qg[r * kL128 + cc + e] = bf2f(qv[e]) * qs;
-      }
-    }
-    for (int idx = tid; idx < kChunk * kChunk; idx += 256) {
-      const int r = idx >> 6, p = idx & 63;
-      sm.aqk[r * kL64 + unperm_col(p)] = bf2f(a.aqk[cm * 4096 + idx]);
-    }
-    load_t(sm.t, a.tmat + cm * (kChunk * 128), tid);
-    {
-      const int r = tid >> 2, cc = (tid & 3) * 8;
-      u16x8 dv = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (r < ci.len) dv = *reinterpret_cast<const u16x8*>(a.dout + ((size_t)(ci.tok0 + r) * H + h) * kDim + v0 + cc);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm.dO[r * kL32 + cc + e] = bf2f(dv[e]);
-    }
-    if (tid < kChunk) {
-      const bool ok = tid < ci.len;
-      sm.kgs[tid] = ok ? vec[2 * kChunk + tid] : 0.0f;
-      sm.xs[tid] = ok ? vec[1 * kChunk + tid] : 0.0f;
-    }
-    const float eL = vec[7 * kChunk];
+    const float eL = a.vec[cm * kVecStride + 7 * kChunk];
     __syncthreads();
+    if (jc > 0) dh_fetch(a, h, c - 1, v0, tid, R);
 
     // dV' = diag(rk e^(G_L - G)) k dS + Aqk^T dO   (rows 16w .. 16w+15)
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      f32x4 acc = tile_mm(sm.k, kL128, 1, sm.dS, kL32, 1, 16 * w, 16 * ct, kDim, lane, zero4());
+      f32x4 acc = tile_mm<kLb, 1, 1, kL128>(sm.k, sm.dST, 16 * w, 16 * ct, kDim, lane, zero4());
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] *= sm.kgs[16 * w + 4 * g + e];
-      acc = tile_mm(sm.aqk, 1, kL64, sm.dO, kL32, 1, 16 * w, 16 * ct, kChunk, lane, acc);
+      acc = tile_mm<kL64, 1, 1, kL64>(sm.aqkT, sm.dOT, 16 * w, 16 * ct, kChunk, lane, acc);
+      const int row0 = 16 * w + 4 * g, col = 16 * ct + l;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * w + 4 * g + e, col = 16 * ct + l;
-        a.dvn[cm * (kChunk * kDim) + row * kDim + v0 + col] = acc[e];
-        sm.z[row * kL32 + col] = acc[e];
-      }
+      for (int e = 0; e < 4; ++e) a.dvn[cm * (kChunk * kDim) + (row0 + e) * kDim + v0 + col] = acc[e];
+      *reinterpret_cast<float4*>(sm.zT + col * kL64 + row0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
     __syncthreads();
     // Z = diag(b rk e^G) T^T dV'
     f32x4 zz[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      zz[ct] = tile_mm(sm.t, 1, kL64, sm.z, kL32, 1, 16 * w, 16 * ct, kChunk, lane, zero4());
+      zz[ct] = tile_mm<kL64, 1, 1, kL64>(sm.tT, sm.zT, 16 * w, 16 * ct, kChunk, lane, zero4());
 #pragma unroll
       for (int e = 0; e < 4; ++e) zz[ct][e] *= sm.xs[16 * w + 4 * g + e];
     }
     __syncthreads();
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sm.z[(16 * w + 4 * g + e) * kL32 + 16 * ct + l] = zz[ct][e];
+      *reinterpret_cast<float4*>(sm.zT + (16 * ct + l) * kL64 + 16 * w + 4 * g) =
+          make_float4(zz[ct][0], zz[ct][1], zz[ct][2], zz[ct][3]);
     __syncthreads();
     // dS = e^(G_L) dS + qg^T dO - k^T Z   (W^T dV' = k^T Z)
 #pragma unroll
@@ -212,8 +279,8 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
       for (int ct = 0; ct < 2; ++ct) {
         const int r0 = 32 * w + 16 * rt;
         f32x4 acc = ds[rt][ct] * eL;
-        acc = tile_mm(sm.qg, 1, kL128, sm.dO, kL32, 1, r0, 16 * ct, kChunk, lane, acc);
-        const f32x4 t = tile_mm(sm.k, 1, kL128, sm.z, kL32, 1, r0, 16 * ct, kChunk, lane, zero4());
+        acc = tile_mm<kL64, 1, 1, kL64>(sm.qgT, sm.dOT, r0, 16 * ct, kChunk, lane, acc);
+        const f32x4 t = tile_mm<kLt, 1, 1, kL64>(sm.kT, sm.zT, r0, 16 * ct, kChunk, lane, zero4());
         ds[rt][ct] = acc - t;
       }
     __syncthreads();
@@ -233,20 +300,24 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
 
 // ===========================================================================
 // Kernel 2: products with the chunk's state and state gradient, one
-// workgroup per (chunk, head): E = dO S^T, F = dV' S^T, D = V' dS_next^T
-// (64 x 128 each) and <dS_next, S>. Wave w computes rows 16w .. 16w+15.
+// workgroup of 8 waves per (chunk, head): E = dO S^T, F = dV' S^T,
+// D = V' dS_next^T (64 x 128 each) and <dS_next, S>. Wave w computes rows
+// 16 (w % 4) .. +15, columns 64 (w / 4) .. +63. Both operands of every
+// product are contiguous along the contraction (S is [kk][v], contracted
+// over v).
 // ===========================================================================
-struct SpSmem {
+struct alignas(16) SpSmem {
   float s[kDim * kL128];     // S, then dS_next
   float x[kChunk * kL128];   // dO, then V'
   float y[kChunk * kL128];   // dV'
-  float red[4];
+  float red[8];
 };
 
-__global__ __launch_bounds__(256, 1) void gdn_bwd_sprod_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void gdn_bwd_sprod_kernel(BwdArgs a) {
   __shared__ SpSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l = lane & 15, g = lane >> 4;
+  const int rt = w & 3, ch = w >> 2;
   const int NT = a.geo.NT;
   const size_t cm = blockIdx.x;
   const int h = (int)(cm / NT), c = (int)(cm % NT);
@@ -255,21 +326,45 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_sprod_kernel(BwdArgs a) {
   const size_t plane = (size_t)a.H * NT * kChunk * kDim;
 
   const float* S = a.h + cm * (kDim * kDim);
-  for (int idx = tid; idx < kDim * kDim / 4; idx += 256) {
-    const int r = idx >> 5, cc = (idx & 31) * 4;
-    *reinterpret_cast<float4*>(sm.s + r * kL128 + cc) = *reinterpret_cast<const float4*>(S + r * kDim + cc);
-  }
-  for (int idx = tid; idx < kChunk * 16; idx += 256) {
-    const int r = idx >> 4, cc = (idx & 15) * 8;
-    u16x8 dv = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    if (r < ci.len) dv = *reinterpret_cast<const u16x8*>(a.dout + ((size_t)(ci.tok0 + r) * H + h) * kDim + cc);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sm.x[r * kL128 + cc + e] = bf2f(dv[e]);
-  }
   const float* dvn = a.dvn + cm * (kChunk * kDim);
-  for (int idx = tid; idx < kChunk * kDim / 4; idx += 256) {
-    const int r = idx >> 5, cc = (idx & 31) * 4;
-    *reinterpret_cast<float4*>(sm.y + r * kL128 + cc) = *reinterpret_cast<const float4*>(dvn + r * kDim + cc);
+  {
+    float4 sv[8], yv[4];
+    u16x8 dv[2];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
+      sv[m] = *reinterpret_cast<const float4*>(S + r * kDim + cc);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
+      yv[m] = *reinterpret_cast<const float4*>(dvn + r * kDim + cc);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int idx = tid + 512 * m, r = idx >> 4, cc = (idx & 15) * 8;
+      dv[m] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (r < ci.len) dv[m] = *reinterpret_cast<const u16x8*>(a.dout + ((size_t)(ci.tok0 + r) * H + h) * kDim + cc);
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
+      *reinterpret_cast<float4*>(sm.s + r * kL128 + cc) = sv[m];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
+      *reinterpret_cast<float4*>(sm.y + r * kL128 + cc) = yv[m];
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int idx = tid + 512 * m, r = idx >> 4, cc = (idx & 15) * 8;
+      float4 lo, hi;
+      lo.x = bf2f(dv[m][0]); lo.y = bf2f(dv[m][1]); lo.z = bf2f(dv[m][2]); lo.w = bf2f(dv[m][3]);
+      hi.x = bf2f(dv[m][4]); hi.y = bf2f(dv[m][5]); hi.z = bf2f(dv[m][6]); hi.w = bf2f(dv[m][7]);
+      *reinterpret_cast<float4*>(sm.x + r * kL128 + cc) = lo;
+      *reinterpret_cast<float4*>(sm.x + r * kL128 + cc + 4) = hi;
+    }
   }
   __syncthreads();
 
@@ -277,13 +372,14 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_sprod_kernel(BwdArgs a) {
   float* F = E + plane;
   float* D = F + plane;
 #pragma unroll 2
-  for (int ct = 0; ct < 8; ++ct) {
+  for (int j = 0; j < 4; ++j) {
+    const int ct = 4 * ch + j;
     // B(v, kk) = S[kk][v]
-    const f32x4 e4 = tile_mm(sm.x, kL128, 1, sm.s, 1, kL128, 16 * w, 16 * ct, kDim, lane, zero4());
-    const f32x4 f4 = tile_mm(sm.y, kL128, 1, sm.s, 1, kL128, 16 * w, 16 * ct, kDim, lane, zero4());
+    const f32x4 e4 = tile_mm<kL128, 1, 1, kL128>(sm.x, sm.s, 16 * rt, 16 * ct, kDim, lane, zero4());
+    const f32x4 f4 = tile_mm<kL128, 1, 1, kL128>(sm.y, sm.s, 16 * rt, 16 * ct, kDim, lane, zero4());
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = 16 * w + 4 * g + e, col = 16 * ct + l;
+      const int row = 16 * rt + 4 * g + e, col = 16 * ct + l;
       E[row * kDim + col] = e4[e];
       F[row * kDim + col] = f4[e];
     }
@@ -291,31 +387,48 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_sprod_kernel(BwdArgs a) {
   __syncthreads();
 
   const float* dSn = a.dhn + cm * (kDim * kDim);
-  float part = 0.0f;
-  for (int idx = tid; idx < kDim * kDim / 4; idx += 256) {
-    const int r = idx >> 5, cc = (idx & 31) * 4;
-    const float4 nv = *reinterpret_cast<const float4*>(dSn + r * kDim + cc);
-    float4* dst = reinterpret_cast<float4*>(sm.s + r * kL128 + cc);
-    const float4 ov = *dst;
-    part += ov.x * nv.x + ov.y * nv.y + ov.z * nv.z + ov.w * nv.w;
-    *dst = nv;
-  }
   const float* vn = a.vnew + cm * (kChunk * kDim);
-  for (int idx = tid; idx < kChunk * kDim / 4; idx += 256) {
-    const int r = idx >> 5, cc = (idx & 31) * 4;
-    *reinterpret_cast<float4*>(sm.x + r * kL128 + cc) = *reinterpret_cast<const float4*>(vn + r * kDim + cc);
+  float part = 0.0f;
+  {
+    float4 nv[8], xv[4];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
+      nv[m] = *reinterpret_cast<const float4*>(dSn + r * kDim + cc);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
+      xv[m] = *reinterpret_cast<const float4*>(vn + r * kDim + cc);
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
+      float4* dst = reinterpret_cast<float4*>(sm.s + r * kL128 + cc);
+      const float4 ov = *dst;
+      part += ov.x * nv[m].x + ov.y * nv[m].y + ov.z * nv[m].z + ov.w * nv[m].w;
+      *dst = nv[m];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
+      *reinterpret_cast<float4*>(sm.x + r * kL128 + cc) = xv[m];
+    }
   }
   part += __shfl_xor(part, 16);
   part += __shfl_xor(part, 32);
   part = sum16(part);
   if (lane == 0) sm.red[w] = part;
   __syncthreads();
-  if (tid == 0) a.sdot[cm] = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
+  if (tid == 0)
+    a.sdot[cm] = ((sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3])) +
+                 ((sm.red[4] + sm.red[5]) + (sm.red[6] + sm.red[7]));
 #pragma unroll 2
-  for (int ct = 0; ct < 8; ++ct) {
-    const f32x4 d4 = tile_mm(sm.x, kL128, 1, sm.s, 1, kL128, 16 * w, 16 * ct, kDim, lane, zero4());
+  for (int j = 0; j < 4; ++j) {
+    const int ct = 4 * ch + j;
+    const f32x4 d4 = tile_mm<kL128, 1, 1, kL128>(sm.x, sm.s, 16 * rt, 16 * ct, kDim, lane, zero4());
 #pragma unroll
-    for (int e = 0; e < 4; ++e) D[(16 * w + 4 * g + e) * kDim + 16 * ct + l] = d4[e];
+    for (int e = 0; e < 4; ++e) D[(16 * rt + 4 * g + e) * kDim + 16 * ct + l] = d4[e];
   }
 }
 
@@ -324,9 +437,12 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_sprod_kernel(BwdArgs a) {
 // 16w .. 16w+15 of every 64-row result; per-row sums (d beta, dG) are kept
 // per lane and reduced at the end, column sums through LDS partials.
 // ===========================================================================
-struct InSmem {
-  uint16_t q[kChunk * kLb], k[kChunk * kLb], v[kChunk * kLb], dO[kChunk * kLb];
-  float t[kChunk * kL64];
+constexpr int kLk = 68;  // bf16 row stride of k^T [kk][i] (kept in dO's place)
+
+struct alignas(16) InSmem {
+  uint16_t q[kChunk * kLb], k[kChunk * kLb], v[kChunk * kLb];
+  uint16_t dO[kChunk * kLb];  // dO [i][v]; after the o-term products, k^T [kk][i] (stride kLk)
+  float tT[kChunk * kL64];    // T^T [j][i]
   float m1[kChunk * kL64];
   float m2[kChunk * kL64];
   float x[kChunk * kL128];  // V', then F, then dV'
@@ -336,10 +452,36 @@ struct InSmem {
   float red[4];
 };
 
+// T^T (fp32, stride kL64) from the prepare kernel's bf16 hi | lo rows with
+// permuted columns; 16-byte loads, all issued before the first store
+__device__ __forceinline__ void load_tT(float* sT, const uint16_t* tm, int tid) {
+  u16x8 th[2], tl[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int idx = tid + 256 * m, r = idx >> 3, p8 = (idx & 7) * 8;
+    th[m] = *reinterpret_cast<const u16x8*>(tm + r * 128 + p8);
+    tl[m] = *reinterpret_cast<const u16x8*>(tm + r * 128 + 64 + p8);
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int idx = tid + 256 * m, r = idx >> 3, p8 = (idx & 7) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sT[unperm_col(p8 + e) * kL64 + r] = bf2f(th[m][e]) + bf2f(tl[m][e]);
+  }
+}
+
+// 64 x 128 fp32 rows into LDS (stride kL128), 256 threads, loads issued together
 __device__ __forceinline__ void load_f32_rows(float* dst, const float* src, int tid) {
-  for (int idx = tid; idx < kChunk * kDim / 4; idx += 256) {
-    const int r = idx >> 5, cc = (idx & 31) * 4;
-    *reinterpret_cast<float4*>(dst + r * kL128 + cc) = *reinterpret_cast<const float4*>(src + r * kDim + cc);
+  float4 v[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int idx = tid + 256 * m, r = idx >> 5, cc = (idx & 31) * 4;
+    v[m] = *reinterpret_cast<const float4*>(src + r * kDim + cc);
+  }
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int idx = tid + 256 * m, r = idx >> 5, cc = (idx & 31) * 4;
+    *reinterpret_cast<float4*>(dst + r * kL128 + cc) = v[m];
   }
 }
 
@@ -357,8 +499,9 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
   const size_t plane = (size_t)a.H * NT * kChunk * kDim;
   const float* vec = a.vec + cm * kVecStride;
 
-  for (int idx = tid; idx < kChunk * 16; idx += 256) {
-    const int r = idx >> 4, cc = (idx & 15) * 8;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int idx = tid + 256 * m, r = idx >> 4, cc = (idx & 15) * 8;
     uint4 qv = make_uint4(0, 0, 0, 0), kv = qv, vv = qv, ov = qv;
     if (r < L) {
       const size_t off = ((size_t)(ci.tok0 + r) * H + h) * kDim + cc;
@@ -372,7 +515,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
     *reinterpret_cast<uint4*>(sm.v + r * kLb + cc) = vv;
     *reinterpret_cast<uint4*>(sm.dO + r * kLb + cc) = ov;
   }
-  load_t(sm.t, a.tmat + cm * (kChunk * 128), tid);
+  load_tT(sm.tT, a.tmat + cm * (kChunk * 128), tid);
   load_f32_rows(sm.x, a.vnew + cm * (kChunk * kDim), tid);
   if (tid < kChunk) {
     const bool ok = tid < L;
@@ -406,8 +549,8 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
   for (int ct = 0; ct < 4; ++ct) {
     f32x4 m1v = zero4(), m2v = zero4();
     if (ct <= w) {
-      const f32x4 p1 = tile_mm(sm.dO, kLb, 1, sm.x, 1, kL128, 16 * w, 16 * ct, kDim, lane, zero4());
-      const f32x4 mq = tile_mm(sm.q, kLb, 1, sm.k, 1, kLb, 16 * w, 16 * ct, kDim, lane, zero4());
+      const f32x4 p1 = tile_mm<kLb, 1, 1, kL128>(sm.dO, sm.x, 16 * w, 16 * ct, kDim, lane, zero4());
+      const f32x4 mq = tile_mm<kLb, 1, 1, kLb>(sm.q, sm.k, 16 * w, 16 * ct, kDim, lane, zero4());
       const int j = 16 * ct + l;
       const float Gj = sm.G[j], rkj = sm.rk[j];
 #pragma unroll
@@ -424,26 +567,31 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
       }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sm.m1[(16 * w + 4 * g + e) * kL64 + 16 * ct + l] = m1v[e];
-      sm.m2[(16 * w + 4 * g + e) * kL64 + 16 * ct + l] = m2v[e];
-    }
+    for (int e = 0; e < 4; ++e) sm.m1[(16 * w + 4 * g + e) * kL64 + 16 * ct + l] = m1v[e];
+    *reinterpret_cast<float4*>(sm.m2 + (16 * ct + l) * kL64 + 16 * w + 4 * g) = make_float4(m2v[0], m2v[1], m2v[2], m2v[3]);
   }
   __syncthreads();
   load_f32_rows(sm.x, a.efd + plane + cm * (kChunk * kDim), tid);  // F
+  for (int idx = tid; idx < kChunk * 16; idx += 256) {           // k^T into dO's place
+    const int r = idx >> 4, cc = (idx & 15) * 8;
+    const u16x8 kv = *reinterpret_cast<const u16x8*>(sm.k + r * kLb + cc);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm.dO[(cc + e) * kLk + r] = kv[e];
+  }
+  __syncthreads();
 
   f32x4 dq[8], dk[8];
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
-    dq[ct] = tile_mm(sm.m1, kL64, 1, sm.k, kLb, 1, 16 * w, 16 * ct, kChunk, lane, zero4());
-    dk[ct] = tile_mm(sm.m2, 1, kL64, sm.q, kLb, 1, 16 * w, 16 * ct, kChunk, lane, zero4());
+    dq[ct] = tile_mm<kL64, 1, 1, kLk>(sm.m1, sm.dO, 16 * w, 16 * ct, kChunk, lane, zero4());
+    dk[ct] = tile_mm<kL64, 1, kLb, 1>(sm.m2, sm.q, 16 * w, 16 * ct, kChunk, lane, zero4());
   }
   __syncthreads();
 
   // ---- F: dX = -T^T F, and -F X^T into dT -------------------------------
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
-    const f32x4 t = tile_mm(sm.t, 1, kL64, sm.x, kL128, 1, 16 * w, 16 * ct, kChunk, lane, zero4());
+    const f32x4 t = tile_mm<kL64, 1, kL128, 1>(sm.tT, sm.x, 16 * w, 16 * ct, kChunk, lane, zero4());
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * w + 4 * g + e;
@@ -457,7 +605,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
   f32x4 dT[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    const f32x4 t = tile_mm(sm.x, kL128, 1, sm.k, 1, kLb, 16 * w, 16 * ct, kDim, lane, zero4());
+    const f32x4 t = tile_mm<kL128, 1, 1, kLb>(sm.x, sm.k, 16 * w, 16 * ct, kDim, lane, zero4());
     const int j = 16 * ct + l;
     const float xs = j < L ? sm.b[j] * sm.rk[j] * __expf(sm.G[j]) : 0.0f;
 #pragma unroll
@@ -470,7 +618,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
   // ---- dV': dY = T^T dV', dv = b dY, and dV' Y^T into dT -----------------
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
-    const f32x4 t = tile_mm(sm.t, 1, kL64, sm.x, kL128, 1, 16 * w, 16 * ct, kChunk, lane, zero4());
+    const f32x4 t = tile_mm<kL64, 1, kL128, 1>(sm.tT, sm.x, 16 * w, 16 * ct, kChunk, lane, zero4());
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * w + 4 * g + e, col = 16 * ct + l;
@@ -480,20 +628,19 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    const f32x4 t = tile_mm(sm.x, kL128, 1, sm.v, 1, kLb, 16 * w, 16 * ct, kDim, lane, zero4());
+    const f32x4 t = tile_mm<kL128, 1, 1, kLb>(sm.x, sm.v, 16 * w, 16 * ct, kDim, lane, zero4());
     const float bj = sm.b[16 * ct + l];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      dT[ct][e] += t[e] * bj;
-      sm.m1[(16 * w + 4 * g + e) * kL64 + 16 * ct + l] = dT[ct][e];
-    }
+    for (int e = 0; e < 4; ++e) dT[ct][e] += t[e] * bj;
+    *reinterpret_cast<float4*>(sm.m1 + (16 * ct + l) * kL64 + 16 * w + 4 * g) =
+        make_float4(dT[ct][0], dT[ct][1], dT[ct][2], dT[ct][3]);  // dT^T
   }
   __syncthreads();
 
   // ---- dA = strictLower(T^T dT T^T) ---------------------------------------
   f32x4 q1[4];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) q1[ct] = tile_mm(sm.t, 1, kL64, sm.m1, kL64, 1, 16 * w, 16 * ct, kChunk, lane, zero4());
+  for (int ct = 0; ct < 4; ++ct) q1[ct] = tile_mm<kL64, 1, 1, kL64>(sm.tT, sm.m1, 16 * w, 16 * ct, kChunk, lane, zero4());
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -505,8 +652,8 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
     pa[ct] = zero4();
     pb[ct] = zero4();
     if (ct <= w) {
-      const f32x4 dA = tile_mm(sm.m2, kL64, 1, sm.t, 1, kL64, 16 * w, 16 * ct, kChunk, lane, zero4());
-      const f32x4 mk = tile_mm(sm.k, kLb, 1, sm.k, 1, kLb, 16 * w, 16 * ct, kDim, lane, zero4());
+      const f32x4 dA = tile_mm<kL64, 1, kL64, 1>(sm.m2, sm.tT, 16 * w, 16 * ct, kChunk, lane, zero4());
+      const f32x4 mk = tile_mm<kLb, 1, 1, kLb>(sm.k, sm.k, 16 * w, 16 * ct, kDim, lane, zero4());
       const int j = 16 * ct + l;
       const float Gj = sm.G[j], rkj = sm.rk[j];
 #pragma unroll
@@ -529,38 +676,46 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
   }
   __syncthreads();
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
+  for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sm.m1[(16 * w + 4 * g + e) * kL64 + 16 * ct + l] = pa[ct][e];
-      sm.m2[(16 * w + 4 * g + e) * kL64 + 16 * ct + l] = pb[ct][e];
-    }
+    for (int e = 0; e < 4; ++e) sm.m1[(16 * w + 4 * g + e) * kL64 + 16 * ct + l] = pa[ct][e];
+    *reinterpret_cast<float4*>(sm.m2 + (16 * ct + l) * kL64 + 16 * w + 4 * g) =
+        make_float4(pb[ct][0], pb[ct][1], pb[ct][2], pb[ct][3]);  // Pb^T
+  }
   __syncthreads();
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
-    dk[ct] = tile_mm(sm.m1, kL64, 1, sm.k, kLb, 1, 16 * w, 16 * ct, kChunk, lane, dk[ct]);
-    dk[ct] = tile_mm(sm.m2, 1, kL64, sm.k, kLb, 1, 16 * w, 16 * ct, kChunk, lane, dk[ct]);
+    dk[ct] = tile_mm<kL64, 1, 1, kLk>(sm.m1, sm.dO, 16 * w, 16 * ct, kChunk, lane, dk[ct]);
+    dk[ct] = tile_mm<kL64, 1, 1, kLk>(sm.m2, sm.dO, 16 * w, 16 * ct, kChunk, lane, dk[ct]);
   }
 
   // ---- E = dO S^T and D = V' dS_next^T -----------------------------------
   const float* E = a.efd + cm * (kChunk * kDim);
   const float* D = E + 2 * plane;
+  // (all 64 rows of E and D exist, zero past the end: the loads need no guard
+  // and are issued together)
   float cl = 0.0f;
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct)
+  for (int ct = 0; ct < 8; ++ct) {
+    float Ev[4], Dv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * w + 4 * g + e, col = 16 * ct + l;
-      if (okr[e]) {
-        const float Ev = E[i * kDim + col], Dv = D[i * kDim + col];
-        dq[ct][e] += scale * eG[e] * Ev;
-        accG[e] += scale * eG[e] * rq_[e] * Ev * bf2f(sm.q[i * kLb + col]);
-        dk[ct][e] += er[e] * Dv;
-        const float cc = er[e] * rk_[e] * Dv * bf2f(sm.k[i * kLb + col]);
-        accG[e] -= cc;
-        cl += cc;
-      }
+      Ev[e] = E[i * kDim + col];
+      Dv[e] = D[i * kDim + col];
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * w + 4 * g + e, col = 16 * ct + l;
+      const float sE = okr[e] ? scale * eG[e] : 0.0f;   // eG, er are 0 past the end
+      dq[ct][e] += sE * Ev[e];
+      accG[e] += sE * rq_[e] * Ev[e] * bf2f(sm.q[i * kLb + col]);
+      dk[ct][e] += er[e] * Dv[e];
+      const float cc = er[e] * rk_[e] * Dv[e] * bf2f(sm.k[i * kLb + col]);
+      accG[e] -= cc;
+      cl += cc;
+    }
+  }
 
   // ---- L2-norm backward, outputs dq, dk ------------------------------------
   const bool l2 = (a.flags & 1u) != 0;
@@ -656,7 +811,7 @@ hipError_t launch_gdn_bwd(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned cms = (unsigned)((size_t)a.H * a.geo.NT);
-  hipLaunchKernelGGL(gdn_bwd_sprod_kernel, dim3(cms), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(gdn_bwd_sprod_kernel, dim3(cms), dim3(512), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(gdn_bwd_intra_kernel, dim3(cms), dim3(256), 0, stream, a);
