@@ -137,7 +137,7 @@ __device__ __forceinline__ void dh_fetch(const BwdArgs& a, int h, int c, int v0,
   const u16x8 z8 = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const int idx = tid + 256 * m, r = idx >> 4, cc = (idx & 15) * 8;
+    const int idx = tid + 256 * m, r = idx & 63, cc = (idx >> 6) * 8;
     R.k[m] = z8;
     R.q[m] = z8;
     R.qs[m] = 0.0f;
@@ -152,13 +152,13 @@ __device__ __forceinline__ void dh_fetch(const BwdArgs& a, int h, int c, int v0,
   const uint16_t* tm = a.tmat + cm * (kChunk * 128);
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const int idx = tid + 256 * m, r = idx >> 3, p8 = (idx & 7) * 8;
+    const int idx = tid + 256 * m, r = idx & 63, p8 = (idx >> 6) * 8;
     R.a[m] = *reinterpret_cast<const u16x8*>(aq + r * 64 + p8);
     R.th[m] = *reinterpret_cast<const u16x8*>(tm + r * 128 + p8);
     R.tl[m] = *reinterpret_cast<const u16x8*>(tm + r * 128 + 64 + p8);
   }
   {
-    const int r = tid >> 2, cc = (tid & 3) * 8;
+    const int r = tid & 63, cc = (tid >> 6) * 8;
     R.o = z8;
     if (r < ci.len) R.o = *reinterpret_cast<const u16x8*>(a.dout + ((size_t)(ci.tok0 + r) * a.H + h) * kDim + v0 + cc);
   }
@@ -173,7 +173,7 @@ __device__ __forceinline__ void dh_fetch(const BwdArgs& a, int h, int c, int v0,
 __device__ __forceinline__ void dh_put(DhSmem& sm, const DhRegs& R, int tid) {
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const int idx = tid + 256 * m, r = idx >> 4, cc = (idx & 15) * 8;
+    const int idx = tid + 256 * m, r = idx & 63, cc = (idx >> 6) * 8;
     *reinterpret_cast<u16x8*>(sm.k + r * kLb + cc) = R.k[m];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -183,7 +183,7 @@ __device__ __forceinline__ void dh_put(DhSmem& sm, const DhRegs& R, int tid) {
   }
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const int idx = tid + 256 * m, r = idx >> 3, p8 = (idx & 7) * 8;
+    const int idx = tid + 256 * m, r = idx & 63, p8 = (idx >> 6) * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int col = unperm_col(p8 + e);
@@ -192,7 +192,7 @@ __device__ __forceinline__ void dh_put(DhSmem& sm, const DhRegs& R, int tid) {
     }
   }
   {
-    const int r = tid >> 2, cc = (tid & 3) * 8;
+    const int r = tid & 63, cc = (tid >> 6) * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) sm.dOT[(cc + e) * kL64 + r] = bf2f(R.o[e]);
   }
@@ -458,13 +458,13 @@ __device__ __forceinline__ void load_tT(float* sT, const uint16_t* tm, int tid) 
   u16x8 th[2], tl[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const int idx = tid + 256 * m, r = idx >> 3, p8 = (idx & 7) * 8;
+    const int idx = tid + 256 * m, r = idx & 63, p8 = (idx >> 6) * 8;
     th[m] = *reinterpret_cast<const u16x8*>(tm + r * 128 + p8);
     tl[m] = *reinterpret_cast<const u16x8*>(tm + r * 128 + 64 + p8);
   }
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const int idx = tid + 256 * m, r = idx >> 3, p8 = (idx & 7) * 8;
+    const int idx = tid + 256 * m, r = idx & 63, p8 = (idx >> 6) * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) sT[unperm_col(p8 + e) * kL64 + r] = bf2f(th[m][e]) + bf2f(tl[m][e]);
   }
@@ -572,8 +572,9 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
   }
   __syncthreads();
   load_f32_rows(sm.x, a.efd + plane + cm * (kChunk * kDim), tid);  // F
-  for (int idx = tid; idx < kChunk * 16; idx += 256) {           // k^T into dO's place
-    const int r = idx >> 4, cc = (idx & 15) * 8;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {                                   // k^T into dO's place
+    const int idx = tid + 256 * m, r = idx & 63, cc = (idx >> 6) * 8;
     const u16x8 kv = *reinterpret_cast<const u16x8*>(sm.k + r * kLb + cc);
 #pragma unroll
     for (int e = 0; e < 8; ++e) sm.dO[(cc + e) * kLk + r] = kv[e];
