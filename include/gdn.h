@@ -195,9 +195,9 @@ int gdn_stage_finalize(int32_t kda, const void* q, const void* aqk, const float*
  * then the state pass storing the state entering every chunk and v_new),
  * then runs the reverse state pass and the per-chunk gradient kernels, all
  * on `stream`. workspace: as gdn_chunk_fwd, sized by
- * gdn_chunk_bwd_workspace_bytes (0 on a contract error; about
- * NT*H*(192 KiB) plus the forward's). Errors as gdn_chunk_fwd; nothing is
- * launched on error.
+ * gdn_chunk_bwd_workspace_bytes (0 on a contract error; the forward's
+ * plus NT*H*288 KiB). Errors as gdn_chunk_fwd; nothing is launched on
+ * error.
  */
 size_t gdn_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
                                      const int32_t* cu_seqlens, uint32_t flags);
