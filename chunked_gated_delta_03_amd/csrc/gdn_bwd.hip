@@ -101,33 +101,38 @@ __device__ __forceinline__ float sum16(float x) {
 // ===========================================================================
 // Kernel 1: reverse state pass. One workgroup per (sequence, head, 32 value
 // columns); the state gradient block (128 x 32) lives in registers, wave w
-// holding rows 32w .. 32w+31. Every operand sits in LDS with its contraction
-// index contiguous (transposed copies where a product contracts over the
-// chunk rows), and the next chunk's inputs are fetched into registers while
-// the current chunk computes.
+// holding rows 32w .. 32w+31. Products on v_mfma_f32_16x16x32_bf16: the
+// inputs k, q, dO and the stored Aqk are exact in bf16; T comes as the
+// prepare kernel's bf16 hi + lo pair; fp32 operands (dS, dV', Z, dO scaled
+// by scale rq e^G) are split into hi + lo in LDS and both halves multiplied
+// (hi*hi + hi*lo + lo*hi where both sides are split). Every operand sits in
+// LDS with its contraction index contiguous (transposed where a product
+// contracts over the chunk rows), so each MFMA operand is one 16-byte read.
+// The next chunk's inputs are fetched into registers while the current one
+// computes.
 // ===========================================================================
-constexpr int kLt = 72;  // bf16 row stride of 128 x 64 transposed matrices
+constexpr int kLh = 72;  // bf16 row stride of 64-wide operands
 
 struct alignas(16) DhSmem {
-  uint16_t k[kChunk * kLb];   // k [i][kk]
-  uint16_t kT[kDim * kLt];    // k^T [kk][i]
-  float qgT[kDim * kL64];     // (q * scale rq e^G)^T [kk][i]
-  float aqkT[kChunk * kL64];  // Aqk^T [i][j]
-  float tT[kChunk * kL64];    // T^T [j][i]
-  float dST[32 * kL128];      // dS^T [c][kk]
-  float dOT[32 * kL64];       // dO^T [c][i]
-  float zT[32 * kL64];        // dV'^T, then Z^T [c][i]
+  uint16_t k[kChunk * kLb];                       // k [i][kk]
+  uint16_t kT[kDim * kLh];                        // k^T [kk][i]
+  uint16_t qT[kDim * kLh];                        // q^T [kk][i]
+  uint16_t aqkT[kChunk * kLh];                    // Aqk^T [i][j]
+  uint16_t tTh[kChunk * kLh], tTl[kChunk * kLh];  // T^T [j][i], hi and lo
+  uint16_t dSTh[32 * kLb], dSTl[32 * kLb];        // dS^T [c][kk]
+  uint16_t dOT[32 * kLh];                         // dO^T [c][i]
+  uint16_t dOsTh[32 * kLh], dOsTl[32 * kLh];      // (diag(scale rq e^G) dO)^T
+  uint16_t zTh[32 * kLh], zTl[32 * kLh];          // dV'^T, then Z^T
   float kgs[kChunk], xs[kChunk];
 };
 
 // one chunk's inputs in flight, per thread
 struct DhRegs {
   u16x8 k[4], q[4];
-  float qs[4];
   u16x8 a[2];
   u16x8 th[2], tl[2];
   u16x8 o;
-  float kgs, xs;
+  float qgs, kgs, xs;
 };
 
 __device__ __forceinline__ void dh_fetch(const BwdArgs& a, int h, int c, int v0, int tid, DhRegs& R) {
@@ -140,12 +145,10 @@ __device__ __forceinline__ void dh_fetch(const BwdArgs& a, int h, int c, int v0,
     const int idx = tid + 256 * m, r = idx & 63, cc = (idx >> 6) * 8;
     R.k[m] = z8;
     R.q[m] = z8;
-    R.qs[m] = 0.0f;
     if (r < ci.len) {
       const size_t off = ((size_t)(ci.tok0 + r) * a.H + h) * kDim + cc;
       R.k[m] = *reinterpret_cast<const u16x8*>(a.k + off);
       R.q[m] = *reinterpret_cast<const u16x8*>(a.q + off);
-      R.qs[m] = vec[3 * kChunk + r];
     }
   }
   const uint16_t* aq = a.aqk + cm * 4096;
@@ -160,7 +163,11 @@ __device__ __forceinline__ void dh_fetch(const BwdArgs& a, int h, int c, int v0,
   {
     const int r = tid & 63, cc = (tid >> 6) * 8;
     R.o = z8;
-    if (r < ci.len) R.o = *reinterpret_cast<const u16x8*>(a.dout + ((size_t)(ci.tok0 + r) * a.H + h) * kDim + v0 + cc);
+    R.qgs = 0.0f;
+    if (r < ci.len) {
+      R.o = *reinterpret_cast<const u16x8*>(a.dout + ((size_t)(ci.tok0 + r) * a.H + h) * kDim + v0 + cc);
+      R.qgs = vec[3 * kChunk + r];
+    }
   }
   R.kgs = 0.0f;
   R.xs = 0.0f;
@@ -177,8 +184,8 @@ __device__ __forceinline__ void dh_put(DhSmem& sm, const DhRegs& R, int tid) {
     *reinterpret_cast<u16x8*>(sm.k + r * kLb + cc) = R.k[m];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      sm.kT[(cc + e) * kLt + r] = R.k[m][e];
-      sm.qgT[(cc + e) * kL64 + r] = bf2f(R.q[m][e]) * R.qs[m];
+      sm.kT[(cc + e) * kLh + r] = R.k[m][e];
+      sm.qT[(cc + e) * kLh + r] = R.q[m][e];
     }
   }
 #pragma unroll
@@ -187,19 +194,43 @@ __device__ __forceinline__ void dh_put(DhSmem& sm, const DhRegs& R, int tid) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int col = unperm_col(p8 + e);
-      sm.aqkT[col * kL64 + r] = bf2f(R.a[m][e]);
-      sm.tT[col * kL64 + r] = bf2f(R.th[m][e]) + bf2f(R.tl[m][e]);
+      sm.aqkT[col * kLh + r] = R.a[m][e];
+      sm.tTh[col * kLh + r] = R.th[m][e];
+      sm.tTl[col * kLh + r] = R.tl[m][e];
     }
   }
   {
     const int r = tid & 63, cc = (tid >> 6) * 8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sm.dOT[(cc + e) * kL64 + r] = bf2f(R.o[e]);
+    for (int e = 0; e < 8; ++e) {
+      sm.dOT[(cc + e) * kLh + r] = R.o[e];
+      uint16_t hi, lo;
+      split_bf(bf2f(R.o[e]) * R.qgs, hi, lo);
+      sm.dOsTh[(cc + e) * kLh + r] = hi;
+      sm.dOsTl[(cc + e) * kLh + r] = lo;
+    }
   }
   if (tid < kChunk) {
     sm.kgs[tid] = R.kgs;
     sm.xs[tid] = R.xs;
   }
+}
+
+__device__ __forceinline__ u16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const u16x8*>(p); }
+
+// four consecutive values of column c (rows r0 .. r0+3 of a C tile) into a
+// transposed hi | lo pair: dst[c * ld + r0 ..]
+__device__ __forceinline__ void put_split4(uint16_t* dh, uint16_t* dl, int off, const f32x4& v) {
+  u16x4 h4, l4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint16_t hi, lo;
+    split_bf(v[e], hi, lo);
+    h4[e] = hi;
+    l4[e] = lo;
+  }
+  *reinterpret_cast<u16x4*>(dh + off) = h4;
+  *reinterpret_cast<u16x4*>(dl + off) = l4;
 }
 
 __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
@@ -230,7 +261,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
     const int c = si.c0 + jc;
     const size_t cm = (size_t)h * a.geo.NT + c;
     dh_put(sm, R, tid);
-    // gradient w.r.t. the state leaving chunk c: to memory and to LDS (dS^T)
+    // gradient w.r.t. the state leaving chunk c: to memory, and to LDS as dS^T
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -238,8 +269,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
         const int row0 = 32 * w + 16 * rt + 4 * g, col = 16 * ct + l;
 #pragma unroll
         for (int e = 0; e < 4; ++e) a.dhn[cm * (kDim * kDim) + (row0 + e) * kDim + v0 + col] = ds[rt][ct][e];
-        *reinterpret_cast<float4*>(sm.dST + col * kL128 + row0) =
-            make_float4(ds[rt][ct][0], ds[rt][ct][1], ds[rt][ct][2], ds[rt][ct][3]);
+        put_split4(sm.dSTh, sm.dSTl, col * kLb + row0, ds[rt][ct]);
       }
     const float eL = a.vec[cm * kVecStride + 7 * kChunk];
     __syncthreads();
@@ -248,39 +278,64 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
     // dV' = diag(rk e^(G_L - G)) k dS + Aqk^T dO   (rows 16w .. 16w+15)
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      f32x4 acc = tile_mm<kLb, 1, 1, kL128>(sm.k, sm.dST, 16 * w, 16 * ct, kDim, lane, zero4());
+      f32x4 acc = zero4();
+      const uint16_t* ap = sm.k + (16 * w + l) * kLb + 8 * g;
+      const int bo = (16 * ct + l) * kLb + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u16x8 av = ld8(ap + 32 * ks);
+        acc = mfma16(av, ld8(sm.dSTh + bo + 32 * ks), acc);
+        acc = mfma16(av, ld8(sm.dSTl + bo + 32 * ks), acc);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] *= sm.kgs[16 * w + 4 * g + e];
-      acc = tile_mm<kL64, 1, 1, kL64>(sm.aqkT, sm.dOT, 16 * w, 16 * ct, kChunk, lane, acc);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        acc = mfma16(ld8(sm.aqkT + (16 * w + l) * kLh + 32 * ks + 8 * g),
+                     ld8(sm.dOT + (16 * ct + l) * kLh + 32 * ks + 8 * g), acc);
       const int row0 = 16 * w + 4 * g, col = 16 * ct + l;
 #pragma unroll
       for (int e = 0; e < 4; ++e) a.dvn[cm * (kChunk * kDim) + (row0 + e) * kDim + v0 + col] = acc[e];
-      *reinterpret_cast<float4*>(sm.zT + col * kL64 + row0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      put_split4(sm.zTh, sm.zTl, col * kLh + row0, acc);
     }
     __syncthreads();
     // Z = diag(b rk e^G) T^T dV'
     f32x4 zz[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      zz[ct] = tile_mm<kL64, 1, 1, kL64>(sm.tT, sm.zT, 16 * w, 16 * ct, kChunk, lane, zero4());
+      f32x4 acc = zero4();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) zz[ct][e] *= sm.xs[16 * w + 4 * g + e];
+      for (int ks = 0; ks < 2; ++ks) {
+        const int ao = (16 * w + l) * kLh + 32 * ks + 8 * g, bo = (16 * ct + l) * kLh + 32 * ks + 8 * g;
+        const u16x8 ah = ld8(sm.tTh + ao), bh = ld8(sm.zTh + bo);
+        acc = mfma16(ah, bh, acc);
+        acc = mfma16(ah, ld8(sm.zTl + bo), acc);
+        acc = mfma16(ld8(sm.tTl + ao), bh, acc);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] *= sm.xs[16 * w + 4 * g + e];
+      zz[ct] = acc;
     }
     __syncthreads();
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-      *reinterpret_cast<float4*>(sm.zT + (16 * ct + l) * kL64 + 16 * w + 4 * g) =
-          make_float4(zz[ct][0], zz[ct][1], zz[ct][2], zz[ct][3]);
+    for (int ct = 0; ct < 2; ++ct) put_split4(sm.zTh, sm.zTl, (16 * ct + l) * kLh + 16 * w + 4 * g, zz[ct]);
     __syncthreads();
-    // dS = e^(G_L) dS + qg^T dO - k^T Z   (W^T dV' = k^T Z)
+    // dS = e^(G_L) dS + q^T diag(scale rq e^G) dO - k^T Z   (W^T dV' = k^T Z)
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const int r0 = 32 * w + 16 * rt;
+        const int ar = (32 * w + 16 * rt + l) * kLh + 8 * g, bc = (16 * ct + l) * kLh + 8 * g;
         f32x4 acc = ds[rt][ct] * eL;
-        acc = tile_mm<kL64, 1, 1, kL64>(sm.qgT, sm.dOT, r0, 16 * ct, kChunk, lane, acc);
-        const f32x4 t = tile_mm<kLt, 1, 1, kL64>(sm.kT, sm.zT, r0, 16 * ct, kChunk, lane, zero4());
+        f32x4 t = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const u16x8 aq = ld8(sm.qT + ar + 32 * ks), ak = ld8(sm.kT + ar + 32 * ks);
+          acc = mfma16(aq, ld8(sm.dOsTh + bc + 32 * ks), acc);
+          acc = mfma16(aq, ld8(sm.dOsTl + bc + 32 * ks), acc);
+          t = mfma16(ak, ld8(sm.zTh + bc + 32 * ks), t);
+          t = mfma16(ak, ld8(sm.zTl + bc + 32 * ks), t);
+        }
         ds[rt][ct] = acc - t;
       }
     __syncthreads();
