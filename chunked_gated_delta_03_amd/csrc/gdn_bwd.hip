@@ -488,9 +488,11 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_sprod_kernel(BwdArgs a) {
 }
 
 // ===========================================================================
-// Kernel 3: input gradients of one (chunk, head). Wave w owns rows
-// 16w .. 16w+15 of every 64-row result; per-row sums (d beta, dG) are kept
-// per lane and reduced at the end, column sums through LDS partials.
+// Kernel 3: input gradients of one (chunk, head), 8 waves. Wave w owns rows
+// 16 (w % 4) .. +15 of every 64-row result and half of its column tiles
+// (h = w / 4); per-row sums (d beta, dG, the L2-norm dots) are kept per lane,
+// reduced over the 16 lanes of a row group and combined over the two halves
+// through LDS; column sums go through LDS partials.
 // ===========================================================================
 constexpr int kLk = 68;  // bf16 row stride of k^T [kk][i] (kept in dO's place)
 
@@ -503,47 +505,40 @@ struct alignas(16) InSmem {
   float x[kChunk * kL128];  // V', then F, then dV'
   float b[kChunk], G[kChunk], rq[kChunk], rk[kChunk];
   float colg[4][kChunk];
-  float rowg[kChunk], rowb[kChunk];
-  float red[4];
+  float rowg[2][kChunk], rowb[2][kChunk], dotq[2][kChunk], dotk[2][kChunk];
+  float red[8];
 };
 
 // T^T (fp32, stride kL64) from the prepare kernel's bf16 hi | lo rows with
-// permuted columns; 16-byte loads, all issued before the first store
+// permuted columns; 16-byte loads (512 threads, one row piece each)
 __device__ __forceinline__ void load_tT(float* sT, const uint16_t* tm, int tid) {
-  u16x8 th[2], tl[2];
+  const int r = tid & 63, p8 = (tid >> 6) * 8;
+  const u16x8 th = *reinterpret_cast<const u16x8*>(tm + r * 128 + p8);
+  const u16x8 tl = *reinterpret_cast<const u16x8*>(tm + r * 128 + 64 + p8);
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int idx = tid + 256 * m, r = idx & 63, p8 = (idx >> 6) * 8;
-    th[m] = *reinterpret_cast<const u16x8*>(tm + r * 128 + p8);
-    tl[m] = *reinterpret_cast<const u16x8*>(tm + r * 128 + 64 + p8);
-  }
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int idx = tid + 256 * m, r = idx & 63, p8 = (idx >> 6) * 8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sT[unperm_col(p8 + e) * kL64 + r] = bf2f(th[m][e]) + bf2f(tl[m][e]);
-  }
+  for (int e = 0; e < 8; ++e) sT[unperm_col(p8 + e) * kL64 + r] = bf2f(th[e]) + bf2f(tl[e]);
 }
 
-// 64 x 128 fp32 rows into LDS (stride kL128), 256 threads, loads issued together
+// 64 x 128 fp32 rows into LDS (stride kL128), 512 threads, loads issued together
 __device__ __forceinline__ void load_f32_rows(float* dst, const float* src, int tid) {
-  float4 v[8];
+  float4 v[4];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int idx = tid + 256 * m, r = idx >> 5, cc = (idx & 31) * 4;
+  for (int m = 0; m < 4; ++m) {
+    const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
     v[m] = *reinterpret_cast<const float4*>(src + r * kDim + cc);
   }
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int idx = tid + 256 * m, r = idx >> 5, cc = (idx & 31) * 4;
+  for (int m = 0; m < 4; ++m) {
+    const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
     *reinterpret_cast<float4*>(dst + r * kL128 + cc) = v[m];
   }
 }
 
-__global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
   __shared__ InSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l = lane & 15, g = lane >> 4;
+  const int rt = w & 3, hf = w >> 2;  // row tile, column half
   const int NT = a.geo.NT;
   const size_t cm = blockIdx.x;
   const int h = (int)(cm / NT), c = (int)(cm % NT);
@@ -555,8 +550,8 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
   const float* vec = a.vec + cm * kVecStride;
 
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int idx = tid + 256 * m, r = idx >> 4, cc = (idx & 15) * 8;
+  for (int m = 0; m < 2; ++m) {
+    const int idx = tid + 512 * m, r = idx >> 4, cc = (idx & 15) * 8;
     uint4 qv = make_uint4(0, 0, 0, 0), kv = qv, vv = qv, ov = qv;
     if (r < L) {
       const size_t off = ((size_t)(ci.tok0 + r) * H + h) * kDim + cc;
@@ -581,13 +576,14 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
   }
   __syncthreads();
 
-  // this lane's rows i = 16w + 4g + e
+  // this lane's rows i = 16 rt + 4g + e
+  const int r0 = 16 * rt;
   float rb_[4], rG[4], rq_[4], rk_[4], eG[4], er[4];
   bool okr[4];
   const float GL = sm.G[L - 1];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int i = 16 * w + 4 * g + e;
+    const int i = r0 + 4 * g + e;
     okr[e] = i < L;
     rb_[e] = sm.b[i];
     rG[e] = sm.G[i];
@@ -597,75 +593,79 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
     er[e] = okr[e] ? __expf(GL - rG[e]) : 0.0f;
   }
   float accG[4] = {0.f, 0.f, 0.f, 0.f}, accB[4] = {0.f, 0.f, 0.f, 0.f};
-  float colG[4] = {0.f, 0.f, 0.f, 0.f};
+  float colG[2] = {0.f, 0.f};
 
   // ---- dO V'^T and Qn Kn^T on the lower tiles: the o-term gradients -----
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
+  for (int jt = 0; jt < 2; ++jt) {
+    const int ct = 2 * hf + jt;
     f32x4 m1v = zero4(), m2v = zero4();
-    if (ct <= w) {
-      const f32x4 p1 = tile_mm<kLb, 1, 1, kL128>(sm.dO, sm.x, 16 * w, 16 * ct, kDim, lane, zero4());
-      const f32x4 mq = tile_mm<kLb, 1, 1, kLb>(sm.q, sm.k, 16 * w, 16 * ct, kDim, lane, zero4());
+    if (ct <= rt) {
+      const f32x4 p1 = tile_mm<kLb, 1, 1, kL128>(sm.dO, sm.x, r0, 16 * ct, kDim, lane, zero4());
+      const f32x4 mq = tile_mm<kLb, 1, 1, kLb>(sm.q, sm.k, r0, 16 * ct, kDim, lane, zero4());
       const int j = 16 * ct + l;
       const float Gj = sm.G[j], rkj = sm.rk[j];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * w + 4 * g + e;
+        const int i = r0 + 4 * g + e;
         if (j <= i && okr[e]) {
           const float sp = scale * p1[e] * __expf(rG[e] - Gj);
           const float z = sp * rq_[e] * rkj * mq[e];
           accG[e] += z;
-          colG[ct] -= z;
+          colG[jt] -= z;
           m1v[e] = sp * rkj;
           m2v[e] = sp * rq_[e];
         }
       }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm.m1[(16 * w + 4 * g + e) * kL64 + 16 * ct + l] = m1v[e];
-    *reinterpret_cast<float4*>(sm.m2 + (16 * ct + l) * kL64 + 16 * w + 4 * g) = make_float4(m2v[0], m2v[1], m2v[2], m2v[3]);
+    for (int e = 0; e < 4; ++e) sm.m1[(r0 + 4 * g + e) * kL64 + 16 * ct + l] = m1v[e];
+    *reinterpret_cast<float4*>(sm.m2 + (16 * ct + l) * kL64 + r0 + 4 * g) = make_float4(m2v[0], m2v[1], m2v[2], m2v[3]);
   }
   __syncthreads();
   load_f32_rows(sm.x, a.efd + plane + cm * (kChunk * kDim), tid);  // F
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {                                   // k^T into dO's place
-    const int idx = tid + 256 * m, r = idx & 63, cc = (idx >> 6) * 8;
+  for (int m = 0; m < 2; ++m) {                                   // k^T into dO's place
+    const int idx = tid + 512 * m, r = idx & 63, cc = (idx >> 6) * 8;
     const u16x8 kv = *reinterpret_cast<const u16x8*>(sm.k + r * kLb + cc);
 #pragma unroll
     for (int e = 0; e < 8; ++e) sm.dO[(cc + e) * kLk + r] = kv[e];
   }
   __syncthreads();
 
-  f32x4 dq[8], dk[8];
+  // columns of this wave's 64 x 128 tiles: 16 (4 hf + j) + l
+  f32x4 dq[4], dk[4];
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    dq[ct] = tile_mm<kL64, 1, 1, kLk>(sm.m1, sm.dO, 16 * w, 16 * ct, kChunk, lane, zero4());
-    dk[ct] = tile_mm<kL64, 1, kLb, 1>(sm.m2, sm.q, 16 * w, 16 * ct, kChunk, lane, zero4());
+  for (int j = 0; j < 4; ++j) {
+    const int ct = 4 * hf + j;
+    dq[j] = tile_mm<kL64, 1, 1, kLk>(sm.m1, sm.dO, r0, 16 * ct, kChunk, lane, zero4());
+    dk[j] = tile_mm<kL64, 1, kLb, 1>(sm.m2, sm.q, r0, 16 * ct, kChunk, lane, zero4());
   }
-  __syncthreads();
 
   // ---- F: dX = -T^T F, and -F X^T into dT -------------------------------
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    const f32x4 t = tile_mm<kL64, 1, kL128, 1>(sm.tT, sm.x, 16 * w, 16 * ct, kChunk, lane, zero4());
+  for (int j = 0; j < 4; ++j) {
+    const int ct = 4 * hf + j;
+    const f32x4 t = tile_mm<kL64, 1, kL128, 1>(sm.tT, sm.x, r0, 16 * ct, kChunk, lane, zero4());
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 16 * w + 4 * g + e;
+      const int i = r0 + 4 * g + e;
       const float kv = bf2f(sm.k[i * kLb + 16 * ct + l]);
-      dk[ct][e] -= rb_[e] * eG[e] * t[e];
+      dk[j][e] -= rb_[e] * eG[e] * t[e];
       const float tk = -rk_[e] * eG[e] * t[e] * kv;  // e^G dX_i . kn_i, one column
       accB[e] += tk;
       accG[e] += rb_[e] * tk;
     }
   }
-  f32x4 dT[4];
+  f32x4 dT[2];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const f32x4 t = tile_mm<kL128, 1, 1, kLb>(sm.x, sm.k, 16 * w, 16 * ct, kDim, lane, zero4());
+  for (int jt = 0; jt < 2; ++jt) {
+    const int ct = 2 * hf + jt;
+    const f32x4 t = tile_mm<kL128, 1, 1, kLb>(sm.x, sm.k, r0, 16 * ct, kDim, lane, zero4());
     const int j = 16 * ct + l;
     const float xs = j < L ? sm.b[j] * sm.rk[j] * __expf(sm.G[j]) : 0.0f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dT[ct][e] = -t[e] * xs;
+    for (int e = 0; e < 4; ++e) dT[jt][e] = -t[e] * xs;
   }
   __syncthreads();
   load_f32_rows(sm.x, a.dvn + cm * (kChunk * kDim), tid);  // dV'
@@ -673,76 +673,81 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
 
   // ---- dV': dY = T^T dV', dv = b dY, and dV' Y^T into dT -----------------
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    const f32x4 t = tile_mm<kL64, 1, kL128, 1>(sm.tT, sm.x, 16 * w, 16 * ct, kChunk, lane, zero4());
+  for (int j = 0; j < 4; ++j) {
+    const int ct = 4 * hf + j;
+    const f32x4 t = tile_mm<kL64, 1, kL128, 1>(sm.tT, sm.x, r0, 16 * ct, kChunk, lane, zero4());
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 16 * w + 4 * g + e, col = 16 * ct + l;
+      const int i = r0 + 4 * g + e, col = 16 * ct + l;
       accB[e] += t[e] * bf2f(sm.v[i * kLb + col]);
       if (okr[e]) a.dv[((size_t)(ci.tok0 + i) * H + h) * kDim + col] = rb_[e] * t[e];
     }
   }
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const f32x4 t = tile_mm<kL128, 1, 1, kLb>(sm.x, sm.v, 16 * w, 16 * ct, kDim, lane, zero4());
+  for (int jt = 0; jt < 2; ++jt) {
+    const int ct = 2 * hf + jt;
+    const f32x4 t = tile_mm<kL128, 1, 1, kLb>(sm.x, sm.v, r0, 16 * ct, kDim, lane, zero4());
     const float bj = sm.b[16 * ct + l];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dT[ct][e] += t[e] * bj;
-    *reinterpret_cast<float4*>(sm.m1 + (16 * ct + l) * kL64 + 16 * w + 4 * g) =
-        make_float4(dT[ct][0], dT[ct][1], dT[ct][2], dT[ct][3]);  // dT^T
+    for (int e = 0; e < 4; ++e) dT[jt][e] += t[e] * bj;
+    *reinterpret_cast<float4*>(sm.m1 + (16 * ct + l) * kL64 + r0 + 4 * g) =
+        make_float4(dT[jt][0], dT[jt][1], dT[jt][2], dT[jt][3]);  // dT^T
   }
   __syncthreads();
 
   // ---- dA = strictLower(T^T dT T^T) ---------------------------------------
-  f32x4 q1[4];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) q1[ct] = tile_mm<kL64, 1, 1, kL64>(sm.tT, sm.m1, 16 * w, 16 * ct, kChunk, lane, zero4());
+  for (int jt = 0; jt < 2; ++jt) {
+    const int ct = 2 * hf + jt;
+    const f32x4 q1 = tile_mm<kL64, 1, 1, kL64>(sm.tT, sm.m1, r0, 16 * ct, kChunk, lane, zero4());
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.m2[(16 * w + 4 * g + e) * kL64 + 16 * ct + l] = q1[ct][e];
+    for (int e = 0; e < 4; ++e) sm.m2[(r0 + 4 * g + e) * kL64 + 16 * ct + l] = q1[e];
+  }
   __syncthreads();
-  f32x4 pa[4], pb[4];
+  f32x4 pa[2], pb[2];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    pa[ct] = zero4();
-    pb[ct] = zero4();
-    if (ct <= w) {
-      const f32x4 dA = tile_mm<kL64, 1, kL64, 1>(sm.m2, sm.tT, 16 * w, 16 * ct, kChunk, lane, zero4());
-      const f32x4 mk = tile_mm<kLb, 1, 1, kLb>(sm.k, sm.k, 16 * w, 16 * ct, kDim, lane, zero4());
+  for (int jt = 0; jt < 2; ++jt) {
+    const int ct = 2 * hf + jt;
+    pa[jt] = zero4();
+    pb[jt] = zero4();
+    if (ct <= rt) {
+      const f32x4 dA = tile_mm<kL64, 1, kL64, 1>(sm.m2, sm.tT, r0, 16 * ct, kChunk, lane, zero4());
+      const f32x4 mk = tile_mm<kLb, 1, 1, kLb>(sm.k, sm.k, r0, 16 * ct, kDim, lane, zero4());
       const int j = 16 * ct + l;
       const float Gj = sm.G[j], rkj = sm.rk[j];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * w + 4 * g + e;
+        const int i = r0 + 4 * g + e;
         if (j < i && okr[e]) {
           const float gam = __expf(rG[e] - Gj);
           const float mkk = rk_[e] * rkj * mk[e];
           const float Aij = -rb_[e] * mkk * gam;
           const float z = dA[e] * Aij;
           accG[e] += z;
-          colG[ct] -= z;
+          colG[jt] -= z;
           const float P = dA[e] * gam;
           accB[e] -= P * mkk;
-          pa[ct][e] = -rb_[e] * P * rkj;
-          pb[ct][e] = -P * rb_[e] * rk_[e];
+          pa[jt][e] = -rb_[e] * P * rkj;
+          pb[jt][e] = -P * rb_[e] * rk_[e];
         }
       }
     }
   }
   __syncthreads();
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
+  for (int jt = 0; jt < 2; ++jt) {
+    const int ct = 2 * hf + jt;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm.m1[(16 * w + 4 * g + e) * kL64 + 16 * ct + l] = pa[ct][e];
-    *reinterpret_cast<float4*>(sm.m2 + (16 * ct + l) * kL64 + 16 * w + 4 * g) =
-        make_float4(pb[ct][0], pb[ct][1], pb[ct][2], pb[ct][3]);  // Pb^T
+    for (int e = 0; e < 4; ++e) sm.m1[(r0 + 4 * g + e) * kL64 + 16 * ct + l] = pa[jt][e];
+    *reinterpret_cast<float4*>(sm.m2 + (16 * ct + l) * kL64 + r0 + 4 * g) =
+        make_float4(pb[jt][0], pb[jt][1], pb[jt][2], pb[jt][3]);  // Pb^T
   }
   __syncthreads();
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    dk[ct] = tile_mm<kL64, 1, 1, kLk>(sm.m1, sm.dO, 16 * w, 16 * ct, kChunk, lane, dk[ct]);
-    dk[ct] = tile_mm<kL64, 1, 1, kLk>(sm.m2, sm.dO, 16 * w, 16 * ct, kChunk, lane, dk[ct]);
+  for (int j = 0; j < 4; ++j) {
+    const int ct = 4 * hf + j;
+    dk[j] = tile_mm<kL64, 1, 1, kLk>(sm.m1, sm.dO, r0, 16 * ct, kChunk, lane, dk[j]);
+    dk[j] = tile_mm<kL64, 1, 1, kLk>(sm.m2, sm.dO, r0, 16 * ct, kChunk, lane, dk[j]);
   }
 
   // ---- E = dO S^T and D = V' dS_next^T -----------------------------------
@@ -752,50 +757,83 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
   // and are issued together)
   float cl = 0.0f;
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
+  for (int j = 0; j < 4; ++j) {
+    const int ct = 4 * hf + j;
     float Ev[4], Dv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 16 * w + 4 * g + e, col = 16 * ct + l;
+      const int i = r0 + 4 * g + e, col = 16 * ct + l;
       Ev[e] = E[i * kDim + col];
       Dv[e] = D[i * kDim + col];
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 16 * w + 4 * g + e, col = 16 * ct + l;
+      const int i = r0 + 4 * g + e, col = 16 * ct + l;
       const float sE = okr[e] ? scale * eG[e] : 0.0f;   // eG, er are 0 past the end
-      dq[ct][e] += sE * Ev[e];
+      dq[j][e] += sE * Ev[e];
       accG[e] += sE * rq_[e] * Ev[e] * bf2f(sm.q[i * kLb + col]);
-      dk[ct][e] += er[e] * Dv[e];
+      dk[j][e] += er[e] * Dv[e];
       const float cc = er[e] * rk_[e] * Dv[e] * bf2f(sm.k[i * kLb + col]);
       accG[e] -= cc;
       cl += cc;
     }
   }
 
-  // ---- L2-norm backward, outputs dq, dk ------------------------------------
-  const bool l2 = (a.flags & 1u) != 0;
+  // ---- row dots of the L2-norm backward, combined over the two halves -----
   float sq[4] = {0.f, 0.f, 0.f, 0.f}, sk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 16 * w + 4 * g + e, col = 16 * ct + l;
-      sq[e] += bf2f(sm.q[i * kLb + col]) * dq[ct][e];
-      sk[e] += bf2f(sm.k[i * kLb + col]) * dk[ct][e];
+      const int i = r0 + 4 * g + e, col = 16 * (4 * hf + j) + l;
+      sq[e] += bf2f(sm.q[i * kLb + col]) * dq[j][e];
+      sk[e] += bf2f(sm.k[i * kLb + col]) * dk[j][e];
     }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     sq[e] = sum16(sq[e]);
     sk[e] = sum16(sk[e]);
+    accG[e] = sum16(accG[e]);
+    accB[e] = sum16(accB[e]);
   }
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct)
+  if (l == 0) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 16 * w + 4 * g + e, col = 16 * ct + l;
+      const int i = r0 + 4 * g + e;
+      sm.dotq[hf][i] = sq[e];
+      sm.dotk[hf][i] = sk[e];
+      sm.rowg[hf][i] = accG[e];
+      sm.rowb[hf][i] = accB[e];
+    }
+  }
+#pragma unroll
+  for (int jt = 0; jt < 2; ++jt) {
+    float x = colG[jt];
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    if (g == 0) sm.colg[rt][16 * (2 * hf + jt) + l] = x;
+  }
+  cl += __shfl_xor(cl, 16);
+  cl += __shfl_xor(cl, 32);
+  cl = sum16(cl);
+  if (lane == 0) sm.red[w] = cl;
+  __syncthreads();
+
+  // ---- L2-norm backward, outputs dq, dk ------------------------------------
+  const bool l2 = (a.flags & 1u) != 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = r0 + 4 * g + e;
+    sq[e] = sm.dotq[0][i] + sm.dotq[1][i];
+    sk[e] = sm.dotk[0][i] + sm.dotk[1][i];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = r0 + 4 * g + e, col = 16 * (4 * hf + j) + l;
       if (!okr[e]) continue;
-      float gq = dq[ct][e], gk = dk[ct][e];
+      float gq = dq[j][e], gk = dk[j][e];
       if (l2) {
         // d x = r (d xn - xn (xn . d xn)), xn = r x
         gq = rq_[e] * (gq - rq_[e] * rq_[e] * bf2f(sm.q[i * kLb + col]) * sq[e]);
@@ -806,41 +844,20 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
       a.dk[off] = gk;
     }
 
-  // ---- row and column sums: d beta and dG, then dg ------------------------
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    accG[e] = sum16(accG[e]);
-    accB[e] = sum16(accB[e]);
-  }
-  if (l == 0) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sm.rowg[16 * w + 4 * g + e] = accG[e];
-      sm.rowb[16 * w + 4 * g + e] = accB[e];
-    }
-  }
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    float x = colG[ct];
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    if (g == 0) sm.colg[w][16 * ct + l] = x;
-  }
-  cl += __shfl_xor(cl, 16);
-  cl += __shfl_xor(cl, 32);
-  cl = sum16(cl);
-  if (lane == 0) sm.red[w] = cl;
-  __syncthreads();
+  // ---- d beta and dG, then dg ----------------------------------------------
   if (w == 0) {
     // lane r holds chunk row 63 - r, so the inclusive scan over lanes is the
     // reverse cumulative sum over rows
     const int i = 63 - lane;
     float dG = 0.0f;
     if (i < L) {
-      dG = sm.rowg[i] + ((sm.colg[0][i] + sm.colg[1][i]) + (sm.colg[2][i] + sm.colg[3][i]));
+      dG = (sm.rowg[0][i] + sm.rowg[1][i]) + ((sm.colg[0][i] + sm.colg[1][i]) + (sm.colg[2][i] + sm.colg[3][i]));
       if (i == L - 1) {
         const float eL = vec[7 * kChunk];
-        dG += eL * a.sdot[cm] + ((sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]));
+        float cls = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < 8; ++ww) cls += sm.red[ww];
+        dG += eL * a.sdot[cm] + cls;
       }
     }
     float x = dG;
@@ -853,7 +870,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
       const size_t tok = (size_t)(ci.tok0 + i) * H + h;
       a.dg[tok] = x;
       const float bi = sm.b[i];
-      const float db = sm.rowb[i];
+      const float db = sm.rowb[0][i] + sm.rowb[1][i];
       a.dbeta[tok] = (a.flags & 2u) ? db * bi * (1.0f - bi) : db;
     }
   }
@@ -870,7 +887,7 @@ hipError_t launch_gdn_bwd(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(gdn_bwd_sprod_kernel, dim3(cms), dim3(512), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gdn_bwd_intra_kernel, dim3(cms), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(gdn_bwd_intra_kernel, dim3(cms), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
