@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fwd tokens/s, GDN H=16 K=V=128 T=4096 B=4; % bf16 MFMA peak"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MFMA_FP32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
 
 # Algorithmic work per token-head (q, k, v bf16 + gate + beta + o bf16), and
 # its split between the two kernels by first touch of the algorithm's inputs
@@ -53,7 +54,8 @@ STATE_BYTES_PER_UNIT = 128 * 128 * 4  # one fp32 state per (sequence, head), eac
 ALG_FLOPS_PER_TH = 140629             # conservative (triangle-exploiting) count
 
 
-KERNEL_SOURCES = ("gdn_common.h", "gdn_kernels.h", "gdn_prepare.hip", "gdn_fwd.hip", "gdn_state.hip", "gdn_state_common.h", "kda_fwd.hip", "kda_state.hip")
+KERNEL_SOURCES = ("gdn_common.h", "gdn_kernels.h", "gdn_prepare.hip", "gdn_fwd.hip", "gdn_state.hip",
+                  "gdn_state_common.h", "kda_fwd.hip", "kda_state.hip", "gdn_bwd.h", "gdn_bwd.hip", "short_conv.hip")
 
 
 def kernel_source_hash() -> str:
@@ -205,6 +207,40 @@ def bench_bwd(args, gdn, gi, inp, q, k, v, g, beta, dev):
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
     ms = float(np.median(ts))
+    # per-kernel durations from the library's events (a second pass, same protocol)
+    gdn.timing_enable(True)
+    for _ in range(args.steps):
+        if args.scrub_mib:
+            scrub.sum()
+        call()
+    torch.cuda.synchronize()
+    kms, ncalls = gdn.bwd_timing_read()
+    gdn.timing_enable(False)
+    names = ("prepare", "fwd_state", "bwd_dh", "bwd_sprod", "bwd_intra")
+    kus = {n: 1e3 * t / max(ncalls, 1) for n, t in zip(names, kms)}
+    # algorithmic work per chunk-head of each backward kernel (64 rows)
+    cmh = gdn.num_chunks(B, T, inp.cu_seqlens) * H
+    work = {
+        # bf16 MFMA products of the reverse pass: k dS, Aqk^T dO, T^T dV', q^T dO, k^T Z
+        "bwd_dh": ("mfma", 2 * (64 * 128 * 128 + 2 * 64 * 64 * 128 + 2 * 128 * 64 * 128), MFMA_BF16_PEAK_TFLOPS,
+                   "gdn_bwd_dh_kernel"),
+        # S, dS_next (64 KiB each), dV', V' (32 KiB each), dO (16 KiB) read; E, F, D (96 KiB) written
+        "bwd_sprod": ("hbm", 2 * 65536 + 2 * 32768 + 16384 + 98304, HBM_PEAK_GBPS, "gdn_bwd_sprod_kernel"),
+        # fp32 MFMA products of the per-chunk gradients (lower tiles only where triangular)
+        "bwd_intra": ("mfma", 11206656, MFMA_FP32_PEAK_TFLOPS, "gdn_bwd_intra_kernel"),
+    }
+    dom = max(work, key=lambda n: kus[n])
+    bound, per_cmh, peak, sym = work[dom]
+    per_launch = per_cmh * cmh
+    if bound == "hbm":
+        achieved = per_launch / (kus[dom] * 1e-6) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s",
+                "frac": round(achieved / peak, 4)}
+    else:
+        achieved = per_launch / (kus[dom] * 1e-6) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    roof["traffic"] = recorded_traffic("bwd_" + args.workload, sym)
     tokens = B * T
     line = {
         "metric": "bwd tokens/s (GDN gradients dq dk dv dg dbeta dS0)",
@@ -213,6 +249,8 @@ def bench_bwd(args, gdn, gi, inp, q, k, v, g, beta, dev):
         "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
         "config": {"workload": "GDN backward B=%d T=%d H=%d, %d sequences, flags %d" % (B, T, H, N, inp.flags & 3),
                    "global_batch": B, "seq_len": T, "heads": H, "head_dim": K, "parallelism": "single-gpu"},
+        "roofline": roof,
+        "kernels_us": {n: round(v, 2) for n, v in kus.items()},
         "timing": {"per_call": "median of %d calls, %d MiB read before each" % (args.steps, args.scrub_mib),
                    "p10_ms": round(float(np.percentile(ts, 10)), 5),
                    "p90_ms": round(float(np.percentile(ts, 90)), 5)},

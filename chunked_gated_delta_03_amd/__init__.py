@@ -37,6 +37,7 @@ EXPORTED = (
     "gdn_timing_enable", "gdn_timing_read", "gdn_state_summary", "kda_state_summary",
     "gdn_state_summary_workspace_bytes", "gdn_state_summary_apply", "gdn_short_conv",
     "gdn_short_conv_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes",
+    "gdn_bwd_timing_read",
 )
 
 
@@ -83,6 +84,8 @@ def _load() -> ctypes.CDLL:
     lib.gdn_short_conv_workspace_bytes.argtypes = [i32, p]
     lib.gdn_short_conv.restype = ctypes.c_int
     lib.gdn_short_conv.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, p, p, sz, p]
+    lib.gdn_bwd_timing_read.restype = ctypes.c_int
+    lib.gdn_bwd_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     lib.gdn_chunk_bwd_workspace_bytes.restype = sz
     lib.gdn_chunk_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, p, u32]
     lib.gdn_chunk_bwd.restype = ctypes.c_int
@@ -414,6 +417,16 @@ def gdn_stage_finalize(q, aqk, vec, h, v_new, gk=None, cu_seqlens=None, kda: boo
 def timing_enable(enable: bool = True) -> None:
     """Record per-kernel HIP events in every whole-pass call of this thread."""
     _check(lib.gdn_timing_enable(1 if enable else 0))
+
+
+def bwd_timing_read() -> Tuple[Tuple[float, ...], int]:
+    """Summed ms of the backward's five kernels (prepare, forward state pass,
+    reverse state pass, state products, per-chunk gradients) over the calls
+    made while timing was enabled, and the number of calls."""
+    ms = (ctypes.c_double * 5)()
+    n = ctypes.c_int64(0)
+    _check(lib.gdn_bwd_timing_read(ms, ctypes.byref(n)))
+    return tuple(float(x) for x in ms), int(n.value)
 
 
 def timing_read() -> Tuple[float, float, int]:

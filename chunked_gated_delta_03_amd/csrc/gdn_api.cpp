@@ -321,6 +321,34 @@ int timing_mark(std::vector<TimingRec>& recs, int which, hipStream_t stream) {
   return GDN_OK;
 }
 
+// The backward entry's marks: before prepare, after prepare, after the
+// forward state pass, after each of the three backward kernels.
+constexpr int kBwdMarks = 6;
+struct BwdTimingRec {
+  hipEvent_t ev[kBwdMarks];
+};
+thread_local std::vector<BwdTimingRec> g_bwd_recs;
+thread_local std::vector<BwdTimingRec> g_bwd_pool;
+
+int bwd_timing_mark(int which, hipStream_t stream) {
+  if (which == 0) {
+    BwdTimingRec r;
+    if (!g_bwd_pool.empty()) {
+      r = g_bwd_pool.back();
+      g_bwd_pool.pop_back();
+    } else {
+      for (int i = 0; i < kBwdMarks; ++i) {
+        hipError_t e = hipEventCreate(&r.ev[i]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate(timing)");
+      }
+    }
+    g_bwd_recs.push_back(r);
+  }
+  hipError_t e = hipEventRecord(g_bwd_recs.back().ev[which], stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(timing)");
+  return GDN_OK;
+}
+
 int check_common(const void* q, const void* k, const void* v, const float* g, const void* beta, float scale,
                  uint32_t flags) {
   if (!q || !k || !v || !g || !beta) return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g and beta must be non-NULL");
@@ -532,6 +560,7 @@ int chunk_bwd(const void* q, const void* k, const void* v, const float* g, const
     if (rc) return rc;
   }
   const gdn::Geometry geo = make_geometry(p, W.base + L.fwd.tab);
+  if (g_timing && (rc = bwd_timing_mark(0, stream))) return rc;
 
   gdn::PrepareArgs pa{};
   pa.q = static_cast<const uint16_t*>(q);
@@ -561,8 +590,10 @@ int chunk_bwd(const void* q, const void* k, const void* v, const float* g, const
   fa.vnew_out = reinterpret_cast<float*>(W.base + L.vnew);
   fa.geo = geo;
   fa.H = H;
+  if (g_timing && (rc = bwd_timing_mark(1, stream))) return rc;
   e = gdn::launch_fwd(false, true, false, fa, stream);
   if (e != hipSuccess) return hip_fail(e, "forward recompute launch");
+  if (g_timing && (rc = bwd_timing_mark(2, stream))) return rc;
 
   gdn::BwdArgs ba{};
   ba.q = pa.q;
@@ -589,8 +620,11 @@ int chunk_bwd(const void* q, const void* k, const void* v, const float* g, const
   ba.H = H;
   ba.scale = scale;
   ba.flags = flags;
-  e = gdn::launch_gdn_bwd(ba, stream);
-  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  for (int stage = 0; stage < 3; ++stage) {
+    e = gdn::launch_gdn_bwd(ba, stage, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    if (g_timing && (rc = bwd_timing_mark(3 + stage, stream))) return rc;
+  }
   return GDN_OK;
 }
 
@@ -819,6 +853,27 @@ int gdn_timing_read(double* prepare_ms, double* state_ms, int64_t* calls) {
   *calls = (int64_t)g_timing_recs.size();
   g_timing_pool.insert(g_timing_pool.end(), g_timing_recs.begin(), g_timing_recs.end());
   g_timing_recs.clear();
+  return GDN_OK;
+}
+
+int gdn_bwd_timing_read(double* ms, int64_t* calls) {
+  g_last_error.clear();
+  if (!ms || !calls) return fail(GDN_ERR_INVALID_ARGUMENT, "NULL output pointer");
+  double acc[kBwdMarks - 1] = {0.0, 0.0, 0.0, 0.0, 0.0};
+  for (BwdTimingRec& r : g_bwd_recs) {
+    hipError_t e = hipEventSynchronize(r.ev[kBwdMarks - 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(timing)");
+    for (int i = 0; i + 1 < kBwdMarks; ++i) {
+      float t = 0.f;
+      e = hipEventElapsedTime(&t, r.ev[i], r.ev[i + 1]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+      acc[i] += t;
+    }
+  }
+  for (int i = 0; i + 1 < kBwdMarks; ++i) ms[i] = acc[i];
+  *calls = (int64_t)g_bwd_recs.size();
+  g_bwd_pool.insert(g_bwd_pool.end(), g_bwd_recs.begin(), g_bwd_recs.end());
+  g_bwd_recs.clear();
   return GDN_OK;
 }
 

@@ -32,6 +32,7 @@ struct BwdArgs {
   float scale;
   uint32_t flags;
 };
-hipError_t launch_gdn_bwd(const BwdArgs& a, hipStream_t stream);
+// stage 0: reverse state pass, 1: state products, 2: per-chunk gradients
+hipError_t launch_gdn_bwd(const BwdArgs& a, int stage, hipStream_t stream);
 
 }  // namespace gdn

@@ -878,16 +878,14 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_gdn_bwd(const BwdArgs& a, hipStream_t stream) {
-  const unsigned units = state_grid(a.geo.N, a.H, 4);
-  hipLaunchKernelGGL(gdn_bwd_dh_kernel, dim3(units), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t launch_gdn_bwd(const BwdArgs& a, int stage, hipStream_t stream) {
   const unsigned cms = (unsigned)((size_t)a.H * a.geo.NT);
-  hipLaunchKernelGGL(gdn_bwd_sprod_kernel, dim3(cms), dim3(512), 0, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gdn_bwd_intra_kernel, dim3(cms), dim3(512), 0, stream, a);
+  if (stage == 0)
+    hipLaunchKernelGGL(gdn_bwd_dh_kernel, dim3(state_grid(a.geo.N, a.H, 4)), dim3(256), 0, stream, a);
+  else if (stage == 1)
+    hipLaunchKernelGGL(gdn_bwd_sprod_kernel, dim3(cms), dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL(gdn_bwd_intra_kernel, dim3(cms), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -121,6 +121,15 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
 int gdn_timing_enable(int32_t enable);
 int gdn_timing_read(double* prepare_ms, double* state_ms, int64_t* calls);
 
+/* The same for gdn_chunk_bwd: while timing is enabled, every backward call
+ * records six events on its stream (before the prepare kernel, after it,
+ * after the forward state pass, after each of the three backward kernels).
+ * gdn_bwd_timing_read() waits for them and returns, in ms[0..4], the summed
+ * milliseconds of prepare, forward state pass, reverse state pass, state
+ * products and per-chunk gradients, and the number of calls; it clears the
+ * record. */
+int gdn_bwd_timing_read(double* ms, int64_t* calls);
+
 /*
  * Stage entry points (the prepare / chunk_fwd_h / finalize split of
  * _AscendCKDAStages.forward on the kimi_delta_attention_ascendc.py coverage
