@@ -126,11 +126,14 @@ struct alignas(16) DhSmem {
   float kgs[kChunk], xs[kChunk];
 };
 
-// one chunk's inputs in flight, per thread
+// one chunk's inputs in flight, per thread. k and q: rows 4j .. 4j+3 at
+// columns 8c .. 8c+7 (j = tid % 16, c = tid / 16), so that the transposed
+// copies take one 8-byte store per column. Aqk and T: rows 2j, 2j+1 at
+// positions 8c .. 8c+7 (j = tid % 32, c = tid / 32). dO: row tid % 64, value
+// columns 8 (tid / 64) .. +7.
 struct DhRegs {
   u16x8 k[4], q[4];
-  u16x8 a[2];
-  u16x8 th[2], tl[2];
+  u16x8 a[2], th[2], tl[2];
   u16x8 o;
   float qgs, kgs, xs;
 };
@@ -140,25 +143,31 @@ __device__ __forceinline__ void dh_fetch(const BwdArgs& a, int h, int c, int v0,
   const size_t cm = (size_t)h * a.geo.NT + c;
   const float* vec = a.vec + cm * kVecStride;
   const u16x8 z8 = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  {
+    const int r0 = 4 * (tid & 15), cc = 8 * (tid >> 4);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int idx = tid + 256 * m, r = idx & 63, cc = (idx >> 6) * 8;
-    R.k[m] = z8;
-    R.q[m] = z8;
-    if (r < ci.len) {
-      const size_t off = ((size_t)(ci.tok0 + r) * a.H + h) * kDim + cc;
-      R.k[m] = *reinterpret_cast<const u16x8*>(a.k + off);
-      R.q[m] = *reinterpret_cast<const u16x8*>(a.q + off);
+    for (int m = 0; m < 4; ++m) {
+      const int r = r0 + m;
+      R.k[m] = z8;
+      R.q[m] = z8;
+      if (r < ci.len) {
+        const size_t off = ((size_t)(ci.tok0 + r) * a.H + h) * kDim + cc;
+        R.k[m] = *reinterpret_cast<const u16x8*>(a.k + off);
+        R.q[m] = *reinterpret_cast<const u16x8*>(a.q + off);
+      }
     }
   }
   const uint16_t* aq = a.aqk + cm * 4096;
   const uint16_t* tm = a.tmat + cm * (kChunk * 128);
+  {
+    const int r0 = 2 * (tid & 31), p8 = 8 * (tid >> 5);
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int idx = tid + 256 * m, r = idx & 63, p8 = (idx >> 6) * 8;
-    R.a[m] = *reinterpret_cast<const u16x8*>(aq + r * 64 + p8);
-    R.th[m] = *reinterpret_cast<const u16x8*>(tm + r * 128 + p8);
-    R.tl[m] = *reinterpret_cast<const u16x8*>(tm + r * 128 + 64 + p8);
+    for (int m = 0; m < 2; ++m) {
+      const int r = r0 + m;
+      R.a[m] = *reinterpret_cast<const u16x8*>(aq + r * 64 + p8);
+      R.th[m] = *reinterpret_cast<const u16x8*>(tm + r * 128 + p8);
+      R.tl[m] = *reinterpret_cast<const u16x8*>(tm + r * 128 + 64 + p8);
+    }
   }
   {
     const int r = tid & 63, cc = (tid >> 6) * 8;
@@ -178,25 +187,24 @@ __device__ __forceinline__ void dh_fetch(const BwdArgs& a, int h, int c, int v0,
 }
 
 __device__ __forceinline__ void dh_put(DhSmem& sm, const DhRegs& R, int tid) {
+  {
+    const int r0 = 4 * (tid & 15), cc = 8 * (tid >> 4);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int idx = tid + 256 * m, r = idx & 63, cc = (idx >> 6) * 8;
-    *reinterpret_cast<u16x8*>(sm.k + r * kLb + cc) = R.k[m];
+    for (int m = 0; m < 4; ++m) *reinterpret_cast<u16x8*>(sm.k + (r0 + m) * kLb + cc) = R.k[m];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      sm.kT[(cc + e) * kLh + r] = R.k[m][e];
-      sm.qT[(cc + e) * kLh + r] = R.q[m][e];
+      *reinterpret_cast<u16x4*>(sm.kT + (cc + e) * kLh + r0) = u16x4{R.k[0][e], R.k[1][e], R.k[2][e], R.k[3][e]};
+      *reinterpret_cast<u16x4*>(sm.qT + (cc + e) * kLh + r0) = u16x4{R.q[0][e], R.q[1][e], R.q[2][e], R.q[3][e]};
     }
   }
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int idx = tid + 256 * m, r = idx & 63, p8 = (idx >> 6) * 8;
+  {
+    const int r0 = 2 * (tid & 31), p8 = 8 * (tid >> 5);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int col = unperm_col(p8 + e);
-      sm.aqkT[col * kLh + r] = R.a[m][e];
-      sm.tTh[col * kLh + r] = R.th[m][e];
-      sm.tTl[col * kLh + r] = R.tl[m][e];
+      const int off = unperm_col(p8 + e) * kLh + r0;
+      *reinterpret_cast<uint32_t*>(sm.aqkT + off) = (uint32_t)R.a[0][e] | ((uint32_t)R.a[1][e] << 16);
+      *reinterpret_cast<uint32_t*>(sm.tTh + off) = (uint32_t)R.th[0][e] | ((uint32_t)R.th[1][e] << 16);
+      *reinterpret_cast<uint32_t*>(sm.tTl + off) = (uint32_t)R.tl[0][e] | ((uint32_t)R.tl[1][e] << 16);
     }
   }
   {
