@@ -101,6 +101,10 @@ CASES = [
     ("workload_gates_no_dsf", lambda: gi.make_inputs("gdn", B=1, T=200, H=2), False),
     ("reset_at_77", _reset_problem, True),
     ("host_normalised_no_flags", _noflag_problem, True),
+    ("l2norm_only", lambda: gi.random_problem(np.random.default_rng(35), 1, 100, 2, 128, 128, gate_scale=0.3,
+                                              with_initial_state=True,
+                                              flags=gi.FLAG_L2NORM_QK | gi.FLAG_OUTPUT_FINAL_STATE), True),
+    ("long_T2048_H2", lambda: gi.make_inputs("long", T=2048, H=2), True),
 ]
 
 
@@ -133,3 +137,58 @@ def test_gdn_bwd_full_size_sampled(gdn):
         sub = {n: (got[n][b:b + 1, h:h + 1] if n == "ds0" else got[n][b:b + 1, :, h:h + 1]) for n in NAMES}
         _say("  slice b=%d h=%d" % (b, h))
         _compare(sub, ref)
+
+
+def test_gdn_bwd_sigmoid_only(gdn):
+    """beta through the in-kernel sigmoid, q and k normalised on the host."""
+    base = _noflag_problem()
+    rng = np.random.default_rng(44)
+    logits = gi.f32_to_bf16_bits(rng.standard_normal((base.B, base.T, base.H)).astype(np.float32))
+    inp = gi.GdnInputs(**{**base.__dict__, "beta": logits,
+                          "flags": gi.FLAG_BETA_SIGMOID | gi.FLAG_OUTPUT_FINAL_STATE})
+    do_bits, dsf = _cotangents(inp, 9)
+    got = _run_bwd(gdn, inp, do_bits, dsf)
+    ref = og.grads(inp, gi.bf16_bits_to_f32(do_bits).astype(np.float64), dsf.astype(np.float64))
+    _compare(got, ref)
+
+
+def test_gdn_bwd_packed_full_size_sampled(gdn):
+    """The packed workload (T=32768, H=16, documents of 17..8192 tokens, initial
+    states): the whole backward on the GPU, then the shortest document and one
+    head against the oracle run on that slice alone."""
+    inp = gi.make_inputs("varlen")
+    cu = [int(x) for x in inp.cu_seqlens]
+    n = int(np.argmin(np.diff(cu)))
+    a, e, h = cu[n], cu[n + 1], 5
+    _say("bwd packed full size: %d documents, checking document %d (%d tokens), head %d" % (len(cu) - 1, n, e - a, h))
+    do_bits, dsf = _cotangents(inp, 10)
+    got = _run_bwd(gdn, inp, do_bits, dsf)
+    sl = lambda x: np.ascontiguousarray(x[:, a:e, h:h + 1])
+    one = gi.GdnInputs(**{**inp.__dict__, "T": e - a, "H": 1, "q": sl(inp.q), "k": sl(inp.k), "v": sl(inp.v),
+                          "g": sl(inp.g), "beta": sl(inp.beta), "cu_seqlens": None,
+                          "initial_state": np.ascontiguousarray(inp.initial_state[n:n + 1, h:h + 1])})
+    ref = og.grads(one, gi.bf16_bits_to_f32(sl(do_bits)).astype(np.float64),
+                   dsf[n:n + 1, h:h + 1].astype(np.float64))
+    sub = {k: (got[k][n:n + 1, h:h + 1] if k == "ds0" else got[k][:, a:e, h:h + 1]) for k in NAMES}
+    _compare(sub, ref)
+
+
+def test_gdn_bwd_deterministic_with_caller_workspace(gdn):
+    """No atomics: two calls, the second with a caller-provided workspace,
+    give bitwise-equal gradients."""
+    inp = gi.random_problem(np.random.default_rng(36), 1, 300, 3, 128, 128, gate_scale=0.3,
+                            with_initial_state=True, cu_seqlens=np.array([0, 10, 300]))
+    do_bits, dsf = _cotangents(inp, 11)
+    first = _run_bwd(gdn, inp, do_bits, dsf)
+    need = gdn.lib.gdn_chunk_bwd_workspace_bytes(1, 300, 3, 128, 128, 2,
+                                                 np.ascontiguousarray(inp.cu_seqlens, dtype=np.int32)
+                                                 .ctypes.data_as(__import__("ctypes").c_void_p), 3)
+    ws = torch.empty(int(need), dtype=torch.uint8, device="cuda")
+    d = to_device(inp)
+    do = torch.from_numpy(np.ascontiguousarray(do_bits)).view(torch.bfloat16).cuda()
+    out = gdn.gdn_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do, scale=inp.scale,
+                            initial_state=d["initial_state"], d_final_state=torch.from_numpy(dsf).cuda(),
+                            cu_seqlens=inp.cu_seqlens, l2norm_qk=True, beta_sigmoid=True, workspace=ws)
+    torch.cuda.synchronize()
+    for name, t in zip(NAMES, out):
+        assert np.array_equal(t.cpu().numpy().astype(np.float64), first[name]), name
