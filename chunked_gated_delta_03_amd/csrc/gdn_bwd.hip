@@ -68,14 +68,28 @@ __device__ __forceinline__ void fetch4(const uint16_t* p, int rc, int k, float (
   }
 }
 
+// An fp32 operand kept in LDS as a bf16 hi | lo pair (value = hi + lo).
+struct HL {
+  const uint16_t* h;
+  const uint16_t* l;
+};
+template <int SR, int SK>
+__device__ __forceinline__ void fetch4(const HL& p, int rc, int k, float (&v)[4]) {
+  float a[4], b[4];
+  fetch4<SR, SK>(p.h, rc, k, a);
+  fetch4<SR, SK>(p.l, rc, k, b);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = a[j] + b[j];
+}
+
 // One 16x16 output tile of C = op(A) op(B) on v_mfma_f32_16x16x4f32:
 // acc (lane (g, l) holds C[r0 + 4g + e][c0 + l]) += sum_k A(r, k) B(k, c),
 // k over [0, kd), kd a multiple of 16. A(r, k) is a[r * SAR + k * SAK] and
 // B(k, c) is b[k * SBK + c * SBC] (LDS, fp32 or bf16), so transposed
 // operands are a matter of strides. Lane group g takes the contraction slots
 // k0 + 4g .. k0 + 4g + 3 (one per MFMA step) of both operands.
-template <int SAR, int SAK, int SBK, int SBC, class TA, class TB>
-__device__ __forceinline__ f32x4 tile_mm(const TA* a, const TB* b, int r0, int c0, int kd, int lane, f32x4 acc) {
+template <int SAR, int SAK, int SBK, int SBC, class PA, class PB>
+__device__ __forceinline__ f32x4 tile_mm(PA a, PB b, int r0, int c0, int kd, int lane, f32x4 acc) {
   const int l = lane & 15, g = lane >> 4;
   for (int k0 = 0; k0 < kd; k0 += 16) {
     float av[4], bv[4];
@@ -501,20 +515,31 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_sprod_kernel(BwdArgs a) {
 // (h = w / 4); per-row sums (d beta, dG, the L2-norm dots) are kept per lane,
 // reduced over the 16 lanes of a row group and combined over the two halves
 // through LDS; column sums go through LDS partials.
+//
+// fp32 intermediates (V', F, dV', the o-term and dA-derived matrices, dT, Q1)
+// sit in LDS as bf16 hi | lo pairs. A product with one exact bf16 operand
+// (q, k, v, dO) whose contraction index is contiguous on both sides runs on
+// v_mfma_f32_16x16x32_bf16 (hi and lo each against the exact operand); the
+// others (contractions over the chunk rows of F, dV', dT, and those with T)
+// run on v_mfma_f32_16x16x4f32 with hi + lo summed on read.
 // ===========================================================================
-constexpr int kLk = 68;  // bf16 row stride of k^T [kk][i] (kept in dO's place)
+constexpr int kLp = 72;  // bf16 row stride of 64-wide matrices and of k^T [kk][i]
 
 struct alignas(16) InSmem {
   uint16_t q[kChunk * kLb], k[kChunk * kLb], v[kChunk * kLb];
-  uint16_t dO[kChunk * kLb];  // dO [i][v]; after the o-term products, k^T [kk][i] (stride kLk)
-  float tT[kChunk * kL64];    // T^T [j][i]
-  float m1[kChunk * kL64];
-  float m2[kChunk * kL64];
-  float x[kChunk * kL128];  // V', then F, then dV'
+  uint16_t okT[kDim * kLp];                      // dO [i][v] (stride kLb), then k^T [kk][i] (stride kLp)
+  uint16_t xh[kChunk * kLb], xl[kChunk * kLb];  // V', then F, then dV' [i][*]
+  uint16_t m1h[kChunk * kLp], m1l[kChunk * kLp];
+  uint16_t m2h[kChunk * kLp], m2l[kChunk * kLp];
+  union {
+    float tT[kChunk * kL64];  // T^T [j][i], until the dA products
+    struct {
+      float colg[4][kChunk];
+      float rowg[2][kChunk], rowb[2][kChunk], dotq[2][kChunk], dotk[2][kChunk];
+      float red[8];
+    } r;
+  } u;
   float b[kChunk], G[kChunk], rq[kChunk], rk[kChunk];
-  float colg[4][kChunk];
-  float rowg[2][kChunk], rowb[2][kChunk], dotq[2][kChunk], dotk[2][kChunk];
-  float red[8];
 };
 
 // T^T (fp32, stride kL64) from the prepare kernel's bf16 hi | lo rows with
@@ -527,8 +552,9 @@ __device__ __forceinline__ void load_tT(float* sT, const uint16_t* tm, int tid) 
   for (int e = 0; e < 8; ++e) sT[unperm_col(p8 + e) * kL64 + r] = bf2f(th[e]) + bf2f(tl[e]);
 }
 
-// 64 x 128 fp32 rows into LDS (stride kL128), 512 threads, loads issued together
-__device__ __forceinline__ void load_f32_rows(float* dst, const float* src, int tid) {
+// 64 x 128 fp32 rows into LDS as a bf16 hi | lo pair (stride kLb), 512
+// threads, loads issued together
+__device__ __forceinline__ void load_split_rows(uint16_t* dh, uint16_t* dl, const float* src, int tid) {
   float4 v[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -538,8 +564,58 @@ __device__ __forceinline__ void load_f32_rows(float* dst, const float* src, int 
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
-    *reinterpret_cast<float4*>(dst + r * kL128 + cc) = v[m];
+    put_split4(dh, dl, r * kLb + cc, f32x4{v[m].x, v[m].y, v[m].z, v[m].w});
   }
+}
+
+// a C tile (rows r0 + 4g + e, column c) into a row-major hi | lo pair
+__device__ __forceinline__ void put_split_rows(uint16_t* dh, uint16_t* dl, int off, int ld, const f32x4& v) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint16_t hi, lo;
+    split_bf(v[e], hi, lo);
+    dh[off + e * ld] = hi;
+    dl[off + e * ld] = lo;
+  }
+}
+
+// 16x16 tiles on v_mfma_f32_16x16x32_bf16, contraction kd (a multiple of 32)
+// contiguous in both operands: row r of A at a + r * SA, column c of B at
+// b + c * SB. x = exact bf16 operand, p = hi | lo pair.
+template <int SA, int SB>
+__device__ __forceinline__ f32x4 bmm_xx(const uint16_t* a, const uint16_t* b, int r0, int c0, int kd, int lane,
+                                        f32x4 acc) {
+  const int l = lane & 15, g = lane >> 4;
+  const uint16_t* ap = a + (r0 + l) * SA + 8 * g;
+  const uint16_t* bp = b + (c0 + l) * SB + 8 * g;
+  for (int k0 = 0; k0 < kd; k0 += 32) acc = mfma16(ld8(ap + k0), ld8(bp + k0), acc);
+  return acc;
+}
+template <int SA, int SB>
+__device__ __forceinline__ f32x4 bmm_px(const uint16_t* ah, const uint16_t* al, const uint16_t* b, int r0, int c0,
+                                        int kd, int lane, f32x4 acc) {
+  const int l = lane & 15, g = lane >> 4;
+  const int ao = (r0 + l) * SA + 8 * g;
+  const uint16_t* bp = b + (c0 + l) * SB + 8 * g;
+  for (int k0 = 0; k0 < kd; k0 += 32) {
+    const u16x8 bv = ld8(bp + k0);
+    acc = mfma16(ld8(ah + ao + k0), bv, acc);
+    acc = mfma16(ld8(al + ao + k0), bv, acc);
+  }
+  return acc;
+}
+template <int SA, int SB>
+__device__ __forceinline__ f32x4 bmm_xp(const uint16_t* a, const uint16_t* bh, const uint16_t* bl, int r0, int c0,
+                                        int kd, int lane, f32x4 acc) {
+  const int l = lane & 15, g = lane >> 4;
+  const uint16_t* ap = a + (r0 + l) * SA + 8 * g;
+  const int bo = (c0 + l) * SB + 8 * g;
+  for (int k0 = 0; k0 < kd; k0 += 32) {
+    const u16x8 av = ld8(ap + k0);
+    acc = mfma16(av, ld8(bh + bo + k0), acc);
+    acc = mfma16(av, ld8(bl + bo + k0), acc);
+  }
+  return acc;
 }
 
 __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
@@ -556,6 +632,8 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
   const float scale = a.scale;
   const size_t plane = (size_t)a.H * NT * kChunk * kDim;
   const float* vec = a.vec + cm * kVecStride;
+  uint16_t* const sdO = sm.okT;  // dO, stride kLb
+  uint16_t* const skT = sm.okT;  // k^T, stride kLp (after the o-term products)
 
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
@@ -571,10 +649,10 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
     *reinterpret_cast<uint4*>(sm.q + r * kLb + cc) = qv;
     *reinterpret_cast<uint4*>(sm.k + r * kLb + cc) = kv;
     *reinterpret_cast<uint4*>(sm.v + r * kLb + cc) = vv;
-    *reinterpret_cast<uint4*>(sm.dO + r * kLb + cc) = ov;
+    *reinterpret_cast<uint4*>(sdO + r * kLb + cc) = ov;
   }
-  load_tT(sm.tT, a.tmat + cm * (kChunk * 128), tid);
-  load_f32_rows(sm.x, a.vnew + cm * (kChunk * kDim), tid);
+  load_tT(sm.u.tT, a.tmat + cm * (kChunk * 128), tid);
+  load_split_rows(sm.xh, sm.xl, a.vnew + cm * (kChunk * kDim), tid);  // V'
   if (tid < kChunk) {
     const bool ok = tid < L;
     sm.b[tid] = ok ? vec[0 * kChunk + tid] : 0.0f;
@@ -609,8 +687,8 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
     const int ct = 2 * hf + jt;
     f32x4 m1v = zero4(), m2v = zero4();
     if (ct <= rt) {
-      const f32x4 p1 = tile_mm<kLb, 1, 1, kL128>(sm.dO, sm.x, r0, 16 * ct, kDim, lane, zero4());
-      const f32x4 mq = tile_mm<kLb, 1, 1, kLb>(sm.q, sm.k, r0, 16 * ct, kDim, lane, zero4());
+      const f32x4 p1 = bmm_xp<kLb, kLb>(sdO, sm.xh, sm.xl, r0, 16 * ct, kDim, lane, zero4());
+      const f32x4 mq = bmm_xx<kLb, kLb>(sm.q, sm.k, r0, 16 * ct, kDim, lane, zero4());
       const int j = 16 * ct + l;
       const float Gj = sm.G[j], rkj = sm.rk[j];
 #pragma unroll
@@ -626,18 +704,22 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
         }
       }
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.m1[(r0 + 4 * g + e) * kL64 + 16 * ct + l] = m1v[e];
-    *reinterpret_cast<float4*>(sm.m2 + (16 * ct + l) * kL64 + r0 + 4 * g) = make_float4(m2v[0], m2v[1], m2v[2], m2v[3]);
+    put_split_rows(sm.m1h, sm.m1l, (r0 + 4 * g) * kLp + 16 * ct + l, kLp, m1v);  // M1a [i][j]
+    put_split4(sm.m2h, sm.m2l, (16 * ct + l) * kLp + r0 + 4 * g, m2v);            // M1b^T [j][i]
   }
   __syncthreads();
-  load_f32_rows(sm.x, a.efd + plane + cm * (kChunk * kDim), tid);  // F
+  load_split_rows(sm.xh, sm.xl, a.efd + plane + cm * (kChunk * kDim), tid);  // F
+  {
+    // k^T into dO's place: rows 4j .. 4j+3 at columns 8c .. 8c+7 per thread
+    const int rr = 4 * (tid & 15), cc = 8 * ((tid >> 4) & 15);
+    if (tid < 256) {
+      u16x8 kv[4];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {                                   // k^T into dO's place
-    const int idx = tid + 512 * m, r = idx & 63, cc = (idx >> 6) * 8;
-    const u16x8 kv = *reinterpret_cast<const u16x8*>(sm.k + r * kLb + cc);
+      for (int m = 0; m < 4; ++m) kv[m] = ld8(sm.k + (rr + m) * kLb + cc);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sm.dO[(cc + e) * kLk + r] = kv[e];
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<u16x4*>(skT + (cc + e) * kLp + rr) = u16x4{kv[0][e], kv[1][e], kv[2][e], kv[3][e]};
+    }
   }
   __syncthreads();
 
@@ -646,15 +728,15 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int ct = 4 * hf + j;
-    dq[j] = tile_mm<kL64, 1, 1, kLk>(sm.m1, sm.dO, r0, 16 * ct, kChunk, lane, zero4());
-    dk[j] = tile_mm<kL64, 1, kLb, 1>(sm.m2, sm.q, r0, 16 * ct, kChunk, lane, zero4());
+    dq[j] = bmm_px<kLp, kLp>(sm.m1h, sm.m1l, skT, r0, 16 * ct, kChunk, lane, zero4());
+    dk[j] = tile_mm<kLp, 1, kLb, 1>(HL{sm.m2h, sm.m2l}, sm.q, r0, 16 * ct, kChunk, lane, zero4());
   }
 
   // ---- F: dX = -T^T F, and -F X^T into dT -------------------------------
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int ct = 4 * hf + j;
-    const f32x4 t = tile_mm<kL64, 1, kL128, 1>(sm.tT, sm.x, r0, 16 * ct, kChunk, lane, zero4());
+    const f32x4 t = tile_mm<kL64, 1, kLb, 1>(sm.u.tT, HL{sm.xh, sm.xl}, r0, 16 * ct, kChunk, lane, zero4());
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = r0 + 4 * g + e;
@@ -669,21 +751,21 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
 #pragma unroll
   for (int jt = 0; jt < 2; ++jt) {
     const int ct = 2 * hf + jt;
-    const f32x4 t = tile_mm<kL128, 1, 1, kLb>(sm.x, sm.k, r0, 16 * ct, kDim, lane, zero4());
+    const f32x4 t = bmm_px<kLb, kLb>(sm.xh, sm.xl, sm.k, r0, 16 * ct, kDim, lane, zero4());
     const int j = 16 * ct + l;
     const float xs = j < L ? sm.b[j] * sm.rk[j] * __expf(sm.G[j]) : 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) dT[jt][e] = -t[e] * xs;
   }
   __syncthreads();
-  load_f32_rows(sm.x, a.dvn + cm * (kChunk * kDim), tid);  // dV'
+  load_split_rows(sm.xh, sm.xl, a.dvn + cm * (kChunk * kDim), tid);  // dV'
   __syncthreads();
 
   // ---- dV': dY = T^T dV', dv = b dY, and dV' Y^T into dT -----------------
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int ct = 4 * hf + j;
-    const f32x4 t = tile_mm<kL64, 1, kL128, 1>(sm.tT, sm.x, r0, 16 * ct, kChunk, lane, zero4());
+    const f32x4 t = tile_mm<kL64, 1, kLb, 1>(sm.u.tT, HL{sm.xh, sm.xl}, r0, 16 * ct, kChunk, lane, zero4());
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = r0 + 4 * g + e, col = 16 * ct + l;
@@ -694,12 +776,11 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
 #pragma unroll
   for (int jt = 0; jt < 2; ++jt) {
     const int ct = 2 * hf + jt;
-    const f32x4 t = tile_mm<kL128, 1, 1, kLb>(sm.x, sm.v, r0, 16 * ct, kDim, lane, zero4());
+    const f32x4 t = bmm_px<kLb, kLb>(sm.xh, sm.xl, sm.v, r0, 16 * ct, kDim, lane, zero4());
     const float bj = sm.b[16 * ct + l];
 #pragma unroll
     for (int e = 0; e < 4; ++e) dT[jt][e] += t[e] * bj;
-    *reinterpret_cast<float4*>(sm.m1 + (16 * ct + l) * kL64 + r0 + 4 * g) =
-        make_float4(dT[jt][0], dT[jt][1], dT[jt][2], dT[jt][3]);  // dT^T
+    put_split4(sm.m1h, sm.m1l, (16 * ct + l) * kLp + r0 + 4 * g, dT[jt]);  // dT^T [j][m]
   }
   __syncthreads();
 
@@ -707,9 +788,8 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
 #pragma unroll
   for (int jt = 0; jt < 2; ++jt) {
     const int ct = 2 * hf + jt;
-    const f32x4 q1 = tile_mm<kL64, 1, 1, kL64>(sm.tT, sm.m1, r0, 16 * ct, kChunk, lane, zero4());
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.m2[(r0 + 4 * g + e) * kL64 + 16 * ct + l] = q1[e];
+    const f32x4 q1 = tile_mm<kL64, 1, 1, kLp>(sm.u.tT, HL{sm.m1h, sm.m1l}, r0, 16 * ct, kChunk, lane, zero4());
+    put_split_rows(sm.m2h, sm.m2l, (r0 + 4 * g) * kLp + 16 * ct + l, kLp, q1);  // Q1 [i][m]
   }
   __syncthreads();
   f32x4 pa[2], pb[2];
@@ -719,8 +799,8 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
     pa[jt] = zero4();
     pb[jt] = zero4();
     if (ct <= rt) {
-      const f32x4 dA = tile_mm<kL64, 1, kL64, 1>(sm.m2, sm.tT, r0, 16 * ct, kChunk, lane, zero4());
-      const f32x4 mk = tile_mm<kLb, 1, 1, kLb>(sm.k, sm.k, r0, 16 * ct, kDim, lane, zero4());
+      const f32x4 dA = tile_mm<kLp, 1, kL64, 1>(HL{sm.m2h, sm.m2l}, sm.u.tT, r0, 16 * ct, kChunk, lane, zero4());
+      const f32x4 mk = bmm_xx<kLb, kLb>(sm.k, sm.k, r0, 16 * ct, kDim, lane, zero4());
       const int j = 16 * ct + l;
       const float Gj = sm.G[j], rkj = sm.rk[j];
 #pragma unroll
@@ -745,17 +825,15 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
 #pragma unroll
   for (int jt = 0; jt < 2; ++jt) {
     const int ct = 2 * hf + jt;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.m1[(r0 + 4 * g + e) * kL64 + 16 * ct + l] = pa[jt][e];
-    *reinterpret_cast<float4*>(sm.m2 + (16 * ct + l) * kL64 + r0 + 4 * g) =
-        make_float4(pb[jt][0], pb[jt][1], pb[jt][2], pb[jt][3]);  // Pb^T
+    put_split_rows(sm.m1h, sm.m1l, (r0 + 4 * g) * kLp + 16 * ct + l, kLp, pa[jt]);  // Pa [i][j]
+    put_split4(sm.m2h, sm.m2l, (16 * ct + l) * kLp + r0 + 4 * g, pb[jt]);           // Pb^T [j][i]
   }
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int ct = 4 * hf + j;
-    dk[j] = tile_mm<kL64, 1, 1, kLk>(sm.m1, sm.dO, r0, 16 * ct, kChunk, lane, dk[j]);
-    dk[j] = tile_mm<kL64, 1, 1, kLk>(sm.m2, sm.dO, r0, 16 * ct, kChunk, lane, dk[j]);
+    dk[j] = bmm_px<kLp, kLp>(sm.m1h, sm.m1l, skT, r0, 16 * ct, kChunk, lane, dk[j]);
+    dk[j] = bmm_px<kLp, kLp>(sm.m2h, sm.m2l, skT, r0, 16 * ct, kChunk, lane, dk[j]);
   }
 
   // ---- E = dO S^T and D = V' dS_next^T -----------------------------------
@@ -788,6 +866,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
   }
 
   // ---- row dots of the L2-norm backward, combined over the two halves -----
+  // (T^T is dead since the dA products: its LDS holds the reduction arrays)
   float sq[4] = {0.f, 0.f, 0.f, 0.f}, sk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -808,10 +887,10 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = r0 + 4 * g + e;
-      sm.dotq[hf][i] = sq[e];
-      sm.dotk[hf][i] = sk[e];
-      sm.rowg[hf][i] = accG[e];
-      sm.rowb[hf][i] = accB[e];
+      sm.u.r.dotq[hf][i] = sq[e];
+      sm.u.r.dotk[hf][i] = sk[e];
+      sm.u.r.rowg[hf][i] = accG[e];
+      sm.u.r.rowb[hf][i] = accB[e];
     }
   }
 #pragma unroll
@@ -819,12 +898,12 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
     float x = colG[jt];
     x += __shfl_xor(x, 16);
     x += __shfl_xor(x, 32);
-    if (g == 0) sm.colg[rt][16 * (2 * hf + jt) + l] = x;
+    if (g == 0) sm.u.r.colg[rt][16 * (2 * hf + jt) + l] = x;
   }
   cl += __shfl_xor(cl, 16);
   cl += __shfl_xor(cl, 32);
   cl = sum16(cl);
-  if (lane == 0) sm.red[w] = cl;
+  if (lane == 0) sm.u.r.red[w] = cl;
   __syncthreads();
 
   // ---- L2-norm backward, outputs dq, dk ------------------------------------
@@ -832,8 +911,8 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int i = r0 + 4 * g + e;
-    sq[e] = sm.dotq[0][i] + sm.dotq[1][i];
-    sk[e] = sm.dotk[0][i] + sm.dotk[1][i];
+    sq[e] = sm.u.r.dotq[0][i] + sm.u.r.dotq[1][i];
+    sk[e] = sm.u.r.dotk[0][i] + sm.u.r.dotk[1][i];
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -859,12 +938,13 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
     const int i = 63 - lane;
     float dG = 0.0f;
     if (i < L) {
-      dG = (sm.rowg[0][i] + sm.rowg[1][i]) + ((sm.colg[0][i] + sm.colg[1][i]) + (sm.colg[2][i] + sm.colg[3][i]));
+      dG = (sm.u.r.rowg[0][i] + sm.u.r.rowg[1][i]) +
+           ((sm.u.r.colg[0][i] + sm.u.r.colg[1][i]) + (sm.u.r.colg[2][i] + sm.u.r.colg[3][i]));
       if (i == L - 1) {
         const float eL = vec[7 * kChunk];
         float cls = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < 8; ++ww) cls += sm.red[ww];
+        for (int ww = 0; ww < 8; ++ww) cls += sm.u.r.red[ww];
         dG += eL * a.sdot[cm] + cls;
       }
     }
@@ -878,7 +958,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
       const size_t tok = (size_t)(ci.tok0 + i) * H + h;
       a.dg[tok] = x;
       const float bi = sm.b[i];
-      const float db = sm.rowb[0][i] + sm.rowb[1][i];
+      const float db = sm.u.r.rowb[0][i] + sm.u.r.rowb[1][i];
       a.dbeta[tok] = (a.flags & 2u) ? db * bi * (1.0f - bi) : db;
     }
   }
