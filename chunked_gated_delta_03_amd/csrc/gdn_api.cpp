@@ -620,6 +620,7 @@ int chunk_bwd(const void* q, const void* k, const void* v, const float* g, const
   ba.H = H;
   ba.scale = scale;
   ba.flags = flags;
+  ba.cus = cus;
   for (int stage = 0; stage < 3; ++stage) {
     e = gdn::launch_gdn_bwd(ba, stage, stream);
     if (e != hipSuccess) return hip_fail(e, "backward launch");

@@ -31,6 +31,7 @@ struct BwdArgs {
   int H;
   float scale;
   uint32_t flags;
+  int cus;                   // compute units of the device (launch shape of the reverse pass)
 };
 // stage 0: reverse state pass, 1: state products, 2: per-chunk gradients
 hipError_t launch_gdn_bwd(const BwdArgs& a, int stage, hipStream_t stream);

@@ -127,16 +127,17 @@ __device__ __forceinline__ float sum16(float x) {
 // ===========================================================================
 constexpr int kLh = 72;  // bf16 row stride of 64-wide operands
 
+template <int NCT>  // 16-column tiles of the value block: 2 (32 columns) or 1 (16)
 struct alignas(16) DhSmem {
   uint16_t k[kChunk * kLb];                       // k [i][kk]
   uint16_t kT[kDim * kLh];                        // k^T [kk][i]
   uint16_t qT[kDim * kLh];                        // q^T [kk][i]
   uint16_t aqkT[kChunk * kLh];                    // Aqk^T [i][j]
   uint16_t tTh[kChunk * kLh], tTl[kChunk * kLh];  // T^T [j][i], hi and lo
-  uint16_t dSTh[32 * kLb], dSTl[32 * kLb];        // dS^T [c][kk]
-  uint16_t dOT[32 * kLh];                         // dO^T [c][i]
-  uint16_t dOsTh[32 * kLh], dOsTl[32 * kLh];      // (diag(scale rq e^G) dO)^T
-  uint16_t zTh[32 * kLh], zTl[32 * kLh];          // dV'^T, then Z^T
+  uint16_t dSTh[16 * NCT * kLb], dSTl[16 * NCT * kLb];    // dS^T [c][kk]
+  uint16_t dOT[16 * NCT * kLh];                           // dO^T [c][i]
+  uint16_t dOsTh[16 * NCT * kLh], dOsTl[16 * NCT * kLh];  // (diag(scale rq e^G) dO)^T
+  uint16_t zTh[16 * NCT * kLh], zTl[16 * NCT * kLh];      // dV'^T, then Z^T
   float kgs[kChunk], xs[kChunk];
 };
 
@@ -152,6 +153,7 @@ struct DhRegs {
   float qgs, kgs, xs;
 };
 
+template <int NCT>
 __device__ __forceinline__ void dh_fetch(const BwdArgs& a, int h, int c, int v0, int tid, DhRegs& R) {
   const ChunkInfo ci = a.geo.chunk(c);
   const size_t cm = (size_t)h * a.geo.NT + c;
@@ -187,7 +189,7 @@ __device__ __forceinline__ void dh_fetch(const BwdArgs& a, int h, int c, int v0,
     const int r = tid & 63, cc = (tid >> 6) * 8;
     R.o = z8;
     R.qgs = 0.0f;
-    if (r < ci.len) {
+    if (r < ci.len && tid < 128 * NCT) {
       R.o = *reinterpret_cast<const u16x8*>(a.dout + ((size_t)(ci.tok0 + r) * a.H + h) * kDim + v0 + cc);
       R.qgs = vec[3 * kChunk + r];
     }
@@ -200,7 +202,8 @@ __device__ __forceinline__ void dh_fetch(const BwdArgs& a, int h, int c, int v0,
   }
 }
 
-__device__ __forceinline__ void dh_put(DhSmem& sm, const DhRegs& R, int tid) {
+template <int NCT>
+__device__ __forceinline__ void dh_put(DhSmem<NCT>& sm, const DhRegs& R, int tid) {
   {
     const int r0 = 4 * (tid & 15), cc = 8 * (tid >> 4);
 #pragma unroll
@@ -221,7 +224,7 @@ __device__ __forceinline__ void dh_put(DhSmem& sm, const DhRegs& R, int tid) {
       *reinterpret_cast<uint32_t*>(sm.tTl + off) = (uint32_t)R.tl[0][e] | ((uint32_t)R.tl[1][e] << 16);
     }
   }
-  {
+  if (tid < 128 * NCT) {
     const int r = tid & 63, cc = (tid >> 6) * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -255,22 +258,24 @@ __device__ __forceinline__ void put_split4(uint16_t* dh, uint16_t* dl, int off, 
   *reinterpret_cast<u16x4*>(dl + off) = l4;
 }
 
+template <int NCT>
 __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
+  constexpr int VB = 8 / NCT;  // value blocks of 16 NCT columns
   int n, h, vb;
-  if (!state_unit(a.geo, a.H, 4, n, h, vb)) return;
-  __shared__ DhSmem sm;
+  if (!state_unit(a.geo, a.H, VB, n, h, vb)) return;
+  __shared__ DhSmem<NCT> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l = lane & 15, g = lane >> 4;
-  const int v0 = 32 * vb;
+  const int v0 = 16 * NCT * vb;
   const int H = a.H;
   const SeqInfo si = a.geo.seq(n);
   const size_t unit = (size_t)n * H + h;
 
-  f32x4 ds[2][2];
+  f32x4 ds[2][NCT];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 32 * w + 16 * rt + 4 * g + e, col = v0 + 16 * ct + l;
@@ -278,7 +283,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
       }
 
   DhRegs R;
-  dh_fetch(a, h, si.c0 + si.nch - 1, v0, tid, R);
+  dh_fetch<NCT>(a, h, si.c0 + si.nch - 1, v0, tid, R);
   for (int jc = si.nch - 1; jc >= 0; --jc) {
     const int c = si.c0 + jc;
     const size_t cm = (size_t)h * a.geo.NT + c;
@@ -287,7 +292,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
+      for (int ct = 0; ct < NCT; ++ct) {
         const int row0 = 32 * w + 16 * rt + 4 * g, col = 16 * ct + l;
 #pragma unroll
         for (int e = 0; e < 4; ++e) a.dhn[cm * (kDim * kDim) + (row0 + e) * kDim + v0 + col] = ds[rt][ct][e];
@@ -295,11 +300,11 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
       }
     const float eL = a.vec[cm * kVecStride + 7 * kChunk];
     __syncthreads();
-    if (jc > 0) dh_fetch(a, h, c - 1, v0, tid, R);
+    if (jc > 0) dh_fetch<NCT>(a, h, c - 1, v0, tid, R);
 
     // dV' = diag(rk e^(G_L - G)) k dS + Aqk^T dO   (rows 16w .. 16w+15)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < NCT; ++ct) {
       f32x4 acc = zero4();
       const uint16_t* ap = sm.k + (16 * w + l) * kLb + 8 * g;
       const int bo = (16 * ct + l) * kLb + 8 * g;
@@ -322,9 +327,9 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
     }
     __syncthreads();
     // Z = diag(b rk e^G) T^T dV'
-    f32x4 zz[2];
+    f32x4 zz[NCT];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < NCT; ++ct) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -340,13 +345,13 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
     }
     __syncthreads();
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) put_split4(sm.zTh, sm.zTl, (16 * ct + l) * kLh + 16 * w + 4 * g, zz[ct]);
+    for (int ct = 0; ct < NCT; ++ct) put_split4(sm.zTh, sm.zTl, (16 * ct + l) * kLh + 16 * w + 4 * g, zz[ct]);
     __syncthreads();
     // dS = e^(G_L) dS + q^T diag(scale rq e^G) dO - k^T Z   (W^T dV' = k^T Z)
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
+      for (int ct = 0; ct < NCT; ++ct) {
         const int ar = (32 * w + 16 * rt + l) * kLh + 8 * g, bc = (16 * ct + l) * kLh + 8 * g;
         f32x4 acc = ds[rt][ct] * eL;
         f32x4 t = zero4();
@@ -366,7 +371,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = 32 * w + 16 * rt + 4 * g + e, col = v0 + 16 * ct + l;
@@ -968,8 +973,14 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
 
 hipError_t launch_gdn_bwd(const BwdArgs& a, int stage, hipStream_t stream) {
   const unsigned cms = (unsigned)((size_t)a.H * a.geo.NT);
-  if (stage == 0)
-    hipLaunchKernelGGL(gdn_bwd_dh_kernel, dim3(state_grid(a.geo.N, a.H, 4)), dim3(256), 0, stream, a);
+  if (stage == 0) {
+    // 32-column value blocks, or 16-column ones when that is still less than
+    // one workgroup per compute unit of the device
+    if ((long)a.geo.N * a.H * 8 <= a.cus)
+      hipLaunchKernelGGL(gdn_bwd_dh_kernel<1>, dim3(state_grid(a.geo.N, a.H, 8)), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(gdn_bwd_dh_kernel<2>, dim3(state_grid(a.geo.N, a.H, 4)), dim3(256), 0, stream, a);
+  }
   else if (stage == 1)
     hipLaunchKernelGGL(gdn_bwd_sprod_kernel, dim3(cms), dim3(512), 0, stream, a);
   else
