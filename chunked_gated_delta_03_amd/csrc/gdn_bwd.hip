@@ -386,14 +386,52 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
 // D = V' dS_next^T (64 x 128 each) and <dS_next, S>. Wave w computes rows
 // 16 (w % 4) .. +15, columns 64 (w / 4) .. +63. Both operands of every
 // product are contiguous along the contraction (S is [kk][v], contracted
-// over v).
+// over v), so all run on v_mfma_f32_16x16x32_bf16: dO is exact in bf16, the
+// fp32 operands (S, dS_next, dV', V') sit in LDS as bf16 hi | lo pairs.
 // ===========================================================================
 struct alignas(16) SpSmem {
-  float s[kDim * kL128];     // S, then dS_next
-  float x[kChunk * kL128];   // dO, then V'
-  float y[kChunk * kL128];   // dV'
+  uint16_t sh[kDim * kLb], sl[kDim * kLb];      // S, then dS_next [kk][v]
+  uint16_t dO[kChunk * kLb];                    // dO [i][v]
+  uint16_t yh[kChunk * kLb], yl[kChunk * kLb];  // dV', then V' [i][v]
   float red[8];
 };
+
+// n rows of 128 fp32 into a bf16 hi | lo pair (stride kLb), 512 threads;
+// optionally the dot product with the pair already there (before it is
+// overwritten)
+template <int ROWS, bool DOT>
+__device__ __forceinline__ float load_split_512(uint16_t* dh, uint16_t* dl, const float* src, int tid) {
+  constexpr int M = ROWS * 32 / 512;
+  float4 v[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
+    v[m] = *reinterpret_cast<const float4*>(src + r * kDim + cc);
+  }
+  float dot = 0.0f;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
+    const int off = r * kLb + cc;
+    if constexpr (DOT) {
+      const u16x4 oh = *reinterpret_cast<const u16x4*>(dh + off), ol = *reinterpret_cast<const u16x4*>(dl + off);
+      dot += (bf2f(oh[0]) + bf2f(ol[0])) * v[m].x + (bf2f(oh[1]) + bf2f(ol[1])) * v[m].y +
+             (bf2f(oh[2]) + bf2f(ol[2])) * v[m].z + (bf2f(oh[3]) + bf2f(ol[3])) * v[m].w;
+    }
+    u16x4 h4, l4;
+    const float x[4] = {v[m].x, v[m].y, v[m].z, v[m].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint16_t hi, lo;
+      split_bf(x[e], hi, lo);
+      h4[e] = hi;
+      l4[e] = lo;
+    }
+    *reinterpret_cast<u16x4*>(dh + off) = h4;
+    *reinterpret_cast<u16x4*>(dl + off) = l4;
+  }
+  return dot;
+}
 
 __global__ __launch_bounds__(512, 1) void gdn_bwd_sprod_kernel(BwdArgs a) {
   __shared__ SpSmem sm;
@@ -407,58 +445,38 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_sprod_kernel(BwdArgs a) {
   const int H = a.H;
   const size_t plane = (size_t)a.H * NT * kChunk * kDim;
 
-  const float* S = a.h + cm * (kDim * kDim);
-  const float* dvn = a.dvn + cm * (kChunk * kDim);
-  {
-    float4 sv[8], yv[4];
-    u16x8 dv[2];
+  load_split_512<kDim, false>(sm.sh, sm.sl, a.h + cm * (kDim * kDim), tid);
+  load_split_512<kChunk, false>(sm.yh, sm.yl, a.dvn + cm * (kChunk * kDim), tid);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
-      sv[m] = *reinterpret_cast<const float4*>(S + r * kDim + cc);
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
-      yv[m] = *reinterpret_cast<const float4*>(dvn + r * kDim + cc);
-    }
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int idx = tid + 512 * m, r = idx >> 4, cc = (idx & 15) * 8;
-      dv[m] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (r < ci.len) dv[m] = *reinterpret_cast<const u16x8*>(a.dout + ((size_t)(ci.tok0 + r) * H + h) * kDim + cc);
-    }
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
-      *reinterpret_cast<float4*>(sm.s + r * kL128 + cc) = sv[m];
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
-      *reinterpret_cast<float4*>(sm.y + r * kL128 + cc) = yv[m];
-    }
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int idx = tid + 512 * m, r = idx >> 4, cc = (idx & 15) * 8;
-      float4 lo, hi;
-      lo.x = bf2f(dv[m][0]); lo.y = bf2f(dv[m][1]); lo.z = bf2f(dv[m][2]); lo.w = bf2f(dv[m][3]);
-      hi.x = bf2f(dv[m][4]); hi.y = bf2f(dv[m][5]); hi.z = bf2f(dv[m][6]); hi.w = bf2f(dv[m][7]);
-      *reinterpret_cast<float4*>(sm.x + r * kL128 + cc) = lo;
-      *reinterpret_cast<float4*>(sm.x + r * kL128 + cc + 4) = hi;
-    }
+  for (int m = 0; m < 2; ++m) {
+    const int idx = tid + 512 * m, r = idx >> 4, cc = (idx & 15) * 8;
+    u16x8 dv = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (r < ci.len) dv = *reinterpret_cast<const u16x8*>(a.dout + ((size_t)(ci.tok0 + r) * H + h) * kDim + cc);
+    *reinterpret_cast<u16x8*>(sm.dO + r * kLb + cc) = dv;
   }
   __syncthreads();
 
   float* E = a.efd + cm * (kChunk * kDim);
   float* F = E + plane;
   float* D = F + plane;
+  const int ao = (16 * rt + l) * kLb + 8 * g;
 #pragma unroll 2
   for (int j = 0; j < 4; ++j) {
     const int ct = 4 * ch + j;
-    // B(v, kk) = S[kk][v]
-    const f32x4 e4 = tile_mm<kL128, 1, 1, kL128>(sm.x, sm.s, 16 * rt, 16 * ct, kDim, lane, zero4());
-    const f32x4 f4 = tile_mm<kL128, 1, 1, kL128>(sm.y, sm.s, 16 * rt, 16 * ct, kDim, lane, zero4());
+    const int bo = (16 * ct + l) * kLb + 8 * g;  // B(v, kk) = S[kk][v]
+    f32x4 e4 = zero4(), f4 = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int k0 = 32 * ks;
+      const u16x8 bh = ld8(sm.sh + bo + k0), bl = ld8(sm.sl + bo + k0);
+      const u16x8 ad = ld8(sm.dO + ao + k0);
+      e4 = mfma16(ad, bh, e4);
+      e4 = mfma16(ad, bl, e4);
+      const u16x8 ah = ld8(sm.yh + ao + k0);
+      f4 = mfma16(ah, bh, f4);
+      f4 = mfma16(ah, bl, f4);
+      f4 = mfma16(ld8(sm.yl + ao + k0), bh, f4);
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 16 * rt + 4 * g + e, col = 16 * ct + l;
@@ -468,35 +486,8 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_sprod_kernel(BwdArgs a) {
   }
   __syncthreads();
 
-  const float* dSn = a.dhn + cm * (kDim * kDim);
-  const float* vn = a.vnew + cm * (kChunk * kDim);
-  float part = 0.0f;
-  {
-    float4 nv[8], xv[4];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
-      nv[m] = *reinterpret_cast<const float4*>(dSn + r * kDim + cc);
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
-      xv[m] = *reinterpret_cast<const float4*>(vn + r * kDim + cc);
-    }
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
-      float4* dst = reinterpret_cast<float4*>(sm.s + r * kL128 + cc);
-      const float4 ov = *dst;
-      part += ov.x * nv[m].x + ov.y * nv[m].y + ov.z * nv[m].z + ov.w * nv[m].w;
-      *dst = nv[m];
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int idx = tid + 512 * m, r = idx >> 5, cc = (idx & 31) * 4;
-      *reinterpret_cast<float4*>(sm.x + r * kL128 + cc) = xv[m];
-    }
-  }
+  float part = load_split_512<kDim, true>(sm.sh, sm.sl, a.dhn + cm * (kDim * kDim), tid);
+  load_split_512<kChunk, false>(sm.yh, sm.yl, a.vnew + cm * (kChunk * kDim), tid);
   part += __shfl_xor(part, 16);
   part += __shfl_xor(part, 32);
   part = sum16(part);
@@ -508,7 +499,16 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_sprod_kernel(BwdArgs a) {
 #pragma unroll 2
   for (int j = 0; j < 4; ++j) {
     const int ct = 4 * ch + j;
-    const f32x4 d4 = tile_mm<kL128, 1, 1, kL128>(sm.x, sm.s, 16 * rt, 16 * ct, kDim, lane, zero4());
+    const int bo = (16 * ct + l) * kLb + 8 * g;
+    f32x4 d4 = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int k0 = 32 * ks;
+      const u16x8 bh = ld8(sm.sh + bo + k0), ah = ld8(sm.yh + ao + k0);
+      d4 = mfma16(ah, bh, d4);
+      d4 = mfma16(ah, ld8(sm.sl + bo + k0), d4);
+      d4 = mfma16(ld8(sm.yl + ao + k0), bh, d4);
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) D[(16 * rt + 4 * g + e) * kDim + 16 * ct + l] = d4[e];
   }
