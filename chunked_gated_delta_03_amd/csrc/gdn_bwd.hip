@@ -113,9 +113,10 @@ __device__ __forceinline__ float sum16(float x) {
 }
 
 // ===========================================================================
-// Kernel 1: reverse state pass. One workgroup per (sequence, head, 32 value
-// columns); the state gradient block (128 x 32) lives in registers, wave w
-// holding rows 32w .. 32w+31. Products on v_mfma_f32_16x16x32_bf16: the
+// Kernel 1: reverse state pass. One workgroup of 8 waves per (sequence,
+// head, block of 32 or 16 value columns); the state gradient block lives in
+// registers, wave w holding rows 16w .. 16w+15. Products on
+// v_mfma_f32_16x16x32_bf16: the
 // inputs k, q, dO and the stored Aqk are exact in bf16; T comes as the
 // prepare kernel's bf16 hi + lo pair; fp32 operands (dS, dV', Z, dO scaled
 // by scale rq e^G) are split into hi + lo in LDS and both halves multiplied
@@ -141,13 +142,13 @@ struct alignas(16) DhSmem {
   float kgs[kChunk], xs[kChunk];
 };
 
-// one chunk's inputs in flight, per thread. k and q: rows 4j .. 4j+3 at
-// columns 8c .. 8c+7 (j = tid % 16, c = tid / 16), so that the transposed
-// copies take one 8-byte store per column. Aqk and T: rows 2j, 2j+1 at
-// positions 8c .. 8c+7 (j = tid % 32, c = tid / 32). dO: row tid % 64, value
-// columns 8 (tid / 64) .. +7.
+// one chunk's inputs in flight, per thread (512 threads). k and q: rows 2j,
+// 2j+1 at columns 8c .. 8c+7 (j = tid % 32, c = tid / 32), so that the
+// transposed copies take one 4-byte store per column. Threads 0..255: Aqk and
+// T, rows 2j, 2j+1 at positions 8c .. 8c+7 (j = tid % 32, c = tid / 32).
+// Threads 256..: dO, row t % 64, value columns 8 (t / 64) .. +7 (t = tid - 256).
 struct DhRegs {
-  u16x8 k[4], q[4];
+  u16x8 k[2], q[2];
   u16x8 a[2], th[2], tl[2];
   u16x8 o;
   float qgs, kgs, xs;
@@ -160,9 +161,9 @@ __device__ __forceinline__ void dh_fetch(const BwdArgs& a, int h, int c, int v0,
   const float* vec = a.vec + cm * kVecStride;
   const u16x8 z8 = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
   {
-    const int r0 = 4 * (tid & 15), cc = 8 * (tid >> 4);
+    const int r0 = 2 * (tid & 31), cc = 8 * (tid >> 5);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < 2; ++m) {
       const int r = r0 + m;
       R.k[m] = z8;
       R.q[m] = z8;
@@ -173,9 +174,9 @@ __device__ __forceinline__ void dh_fetch(const BwdArgs& a, int h, int c, int v0,
       }
     }
   }
-  const uint16_t* aq = a.aqk + cm * 4096;
-  const uint16_t* tm = a.tmat + cm * (kChunk * 128);
-  {
+  if (tid < 256) {
+    const uint16_t* aq = a.aqk + cm * 4096;
+    const uint16_t* tm = a.tmat + cm * (kChunk * 128);
     const int r0 = 2 * (tid & 31), p8 = 8 * (tid >> 5);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -184,12 +185,11 @@ __device__ __forceinline__ void dh_fetch(const BwdArgs& a, int h, int c, int v0,
       R.th[m] = *reinterpret_cast<const u16x8*>(tm + r * 128 + p8);
       R.tl[m] = *reinterpret_cast<const u16x8*>(tm + r * 128 + 64 + p8);
     }
-  }
-  {
-    const int r = tid & 63, cc = (tid >> 6) * 8;
+  } else {
+    const int t = tid - 256, r = t & 63, cc = (t >> 6) * 8;
     R.o = z8;
     R.qgs = 0.0f;
-    if (r < ci.len && tid < 128 * NCT) {
+    if (r < ci.len && t < 128 * NCT) {
       R.o = *reinterpret_cast<const u16x8*>(a.dout + ((size_t)(ci.tok0 + r) * a.H + h) * kDim + v0 + cc);
       R.qgs = vec[3 * kChunk + r];
     }
@@ -205,16 +205,16 @@ __device__ __forceinline__ void dh_fetch(const BwdArgs& a, int h, int c, int v0,
 template <int NCT>
 __device__ __forceinline__ void dh_put(DhSmem<NCT>& sm, const DhRegs& R, int tid) {
   {
-    const int r0 = 4 * (tid & 15), cc = 8 * (tid >> 4);
+    const int r0 = 2 * (tid & 31), cc = 8 * (tid >> 5);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) *reinterpret_cast<u16x8*>(sm.k + (r0 + m) * kLb + cc) = R.k[m];
+    for (int m = 0; m < 2; ++m) *reinterpret_cast<u16x8*>(sm.k + (r0 + m) * kLb + cc) = R.k[m];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      *reinterpret_cast<u16x4*>(sm.kT + (cc + e) * kLh + r0) = u16x4{R.k[0][e], R.k[1][e], R.k[2][e], R.k[3][e]};
-      *reinterpret_cast<u16x4*>(sm.qT + (cc + e) * kLh + r0) = u16x4{R.q[0][e], R.q[1][e], R.q[2][e], R.q[3][e]};
+      *reinterpret_cast<uint32_t*>(sm.kT + (cc + e) * kLh + r0) = (uint32_t)R.k[0][e] | ((uint32_t)R.k[1][e] << 16);
+      *reinterpret_cast<uint32_t*>(sm.qT + (cc + e) * kLh + r0) = (uint32_t)R.q[0][e] | ((uint32_t)R.q[1][e] << 16);
     }
   }
-  {
+  if (tid < 256) {
     const int r0 = 2 * (tid & 31), p8 = 8 * (tid >> 5);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -223,9 +223,8 @@ __device__ __forceinline__ void dh_put(DhSmem<NCT>& sm, const DhRegs& R, int tid
       *reinterpret_cast<uint32_t*>(sm.tTh + off) = (uint32_t)R.th[0][e] | ((uint32_t)R.th[1][e] << 16);
       *reinterpret_cast<uint32_t*>(sm.tTl + off) = (uint32_t)R.tl[0][e] | ((uint32_t)R.tl[1][e] << 16);
     }
-  }
-  if (tid < 128 * NCT) {
-    const int r = tid & 63, cc = (tid >> 6) * 8;
+  } else if (tid - 256 < 128 * NCT) {
+    const int t = tid - 256, r = t & 63, cc = (t >> 6) * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       sm.dOT[(cc + e) * kLh + r] = R.o[e];
@@ -258,8 +257,12 @@ __device__ __forceinline__ void put_split4(uint16_t* dh, uint16_t* dl, int off, 
   *reinterpret_cast<u16x4*>(dl + off) = l4;
 }
 
+// 8 waves. dV' and Z (64 x 16 NCT): wave w takes the tile of row block w % 4
+// and column block w / 4 (with one column block, waves 4..7 sit out). dS
+// (128 x 16 NCT): wave w holds rows 16w .. 16w+15, all column blocks, in
+// registers.
 template <int NCT>
-__global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
   constexpr int VB = 8 / NCT;  // value blocks of 16 NCT columns
   int n, h, vb;
   if (!state_unit(a.geo, a.H, VB, n, h, vb)) return;
@@ -270,44 +273,41 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
   const int H = a.H;
   const SeqInfo si = a.geo.seq(n);
   const size_t unit = (size_t)n * H + h;
+  const int vrt = w & 3, vct = w >> 2;      // dV' / Z tile of this wave
+  const bool vact = vct < NCT;
 
-  f32x4 ds[2][NCT];
+  f32x4 ds[NCT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 32 * w + 16 * rt + 4 * g + e, col = v0 + 16 * ct + l;
-        ds[rt][ct][e] = a.dsfinal ? a.dsfinal[(unit * kDim + row) * kDim + col] : 0.0f;
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * w + 4 * g + e, col = v0 + 16 * ct + l;
+      ds[ct][e] = a.dsfinal ? a.dsfinal[(unit * kDim + row) * kDim + col] : 0.0f;
+    }
 
   DhRegs R;
   dh_fetch<NCT>(a, h, si.c0 + si.nch - 1, v0, tid, R);
   for (int jc = si.nch - 1; jc >= 0; --jc) {
     const int c = si.c0 + jc;
     const size_t cm = (size_t)h * a.geo.NT + c;
-    dh_put(sm, R, tid);
+    dh_put<NCT>(sm, R, tid);
     // gradient w.r.t. the state leaving chunk c: to memory, and to LDS as dS^T
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int row0 = 16 * w + 4 * g, col = 16 * ct + l;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const int row0 = 32 * w + 16 * rt + 4 * g, col = 16 * ct + l;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) a.dhn[cm * (kDim * kDim) + (row0 + e) * kDim + v0 + col] = ds[rt][ct][e];
-        put_split4(sm.dSTh, sm.dSTl, col * kLb + row0, ds[rt][ct]);
-      }
+      for (int e = 0; e < 4; ++e) a.dhn[cm * (kDim * kDim) + (row0 + e) * kDim + v0 + col] = ds[ct][e];
+      put_split4(sm.dSTh, sm.dSTl, col * kLb + row0, ds[ct]);
+    }
     const float eL = a.vec[cm * kVecStride + 7 * kChunk];
     __syncthreads();
     if (jc > 0) dh_fetch<NCT>(a, h, c - 1, v0, tid, R);
 
-    // dV' = diag(rk e^(G_L - G)) k dS + Aqk^T dO   (rows 16w .. 16w+15)
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
+    // dV' = diag(rk e^(G_L - G)) k dS + Aqk^T dO   (tile (vrt, vct))
+    if (vact) {
       f32x4 acc = zero4();
-      const uint16_t* ap = sm.k + (16 * w + l) * kLb + 8 * g;
-      const int bo = (16 * ct + l) * kLb + 8 * g;
+      const uint16_t* ap = sm.k + (16 * vrt + l) * kLb + 8 * g;
+      const int bo = (16 * vct + l) * kLb + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const u16x8 av = ld8(ap + 32 * ks);
@@ -315,68 +315,60 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_dh_kernel(BwdArgs a) {
         acc = mfma16(av, ld8(sm.dSTl + bo + 32 * ks), acc);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] *= sm.kgs[16 * w + 4 * g + e];
+      for (int e = 0; e < 4; ++e) acc[e] *= sm.kgs[16 * vrt + 4 * g + e];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        acc = mfma16(ld8(sm.aqkT + (16 * w + l) * kLh + 32 * ks + 8 * g),
-                     ld8(sm.dOT + (16 * ct + l) * kLh + 32 * ks + 8 * g), acc);
-      const int row0 = 16 * w + 4 * g, col = 16 * ct + l;
+        acc = mfma16(ld8(sm.aqkT + (16 * vrt + l) * kLh + 32 * ks + 8 * g),
+                     ld8(sm.dOT + (16 * vct + l) * kLh + 32 * ks + 8 * g), acc);
+      const int row0 = 16 * vrt + 4 * g, col = 16 * vct + l;
 #pragma unroll
       for (int e = 0; e < 4; ++e) a.dvn[cm * (kChunk * kDim) + (row0 + e) * kDim + v0 + col] = acc[e];
       put_split4(sm.zTh, sm.zTl, col * kLh + row0, acc);
     }
     __syncthreads();
     // Z = diag(b rk e^G) T^T dV'
-    f32x4 zz[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      f32x4 acc = zero4();
+    f32x4 zz = zero4();
+    if (vact) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int ao = (16 * w + l) * kLh + 32 * ks + 8 * g, bo = (16 * ct + l) * kLh + 32 * ks + 8 * g;
+        const int ao = (16 * vrt + l) * kLh + 32 * ks + 8 * g, bo = (16 * vct + l) * kLh + 32 * ks + 8 * g;
         const u16x8 ah = ld8(sm.tTh + ao), bh = ld8(sm.zTh + bo);
-        acc = mfma16(ah, bh, acc);
-        acc = mfma16(ah, ld8(sm.zTl + bo), acc);
-        acc = mfma16(ld8(sm.tTl + ao), bh, acc);
+        zz = mfma16(ah, bh, zz);
+        zz = mfma16(ah, ld8(sm.zTl + bo), zz);
+        zz = mfma16(ld8(sm.tTl + ao), bh, zz);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] *= sm.xs[16 * w + 4 * g + e];
-      zz[ct] = acc;
+      for (int e = 0; e < 4; ++e) zz[e] *= sm.xs[16 * vrt + 4 * g + e];
     }
     __syncthreads();
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) put_split4(sm.zTh, sm.zTl, (16 * ct + l) * kLh + 16 * w + 4 * g, zz[ct]);
+    if (vact) put_split4(sm.zTh, sm.zTl, (16 * vct + l) * kLh + 16 * vrt + 4 * g, zz);
     __syncthreads();
     // dS = e^(G_L) dS + q^T diag(scale rq e^G) dO - k^T Z   (W^T dV' = k^T Z)
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int ar = (16 * w + l) * kLh + 8 * g, bc = (16 * ct + l) * kLh + 8 * g;
+      f32x4 acc = ds[ct] * eL;
+      f32x4 t = zero4();
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const int ar = (32 * w + 16 * rt + l) * kLh + 8 * g, bc = (16 * ct + l) * kLh + 8 * g;
-        f32x4 acc = ds[rt][ct] * eL;
-        f32x4 t = zero4();
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const u16x8 aq = ld8(sm.qT + ar + 32 * ks), ak = ld8(sm.kT + ar + 32 * ks);
-          acc = mfma16(aq, ld8(sm.dOsTh + bc + 32 * ks), acc);
-          acc = mfma16(aq, ld8(sm.dOsTl + bc + 32 * ks), acc);
-          t = mfma16(ak, ld8(sm.zTh + bc + 32 * ks), t);
-          t = mfma16(ak, ld8(sm.zTl + bc + 32 * ks), t);
-        }
-        ds[rt][ct] = acc - t;
+      for (int ks = 0; ks < 2; ++ks) {
+        const u16x8 aq = ld8(sm.qT + ar + 32 * ks), ak = ld8(sm.kT + ar + 32 * ks);
+        acc = mfma16(aq, ld8(sm.dOsTh + bc + 32 * ks), acc);
+        acc = mfma16(aq, ld8(sm.dOsTl + bc + 32 * ks), acc);
+        t = mfma16(ak, ld8(sm.zTh + bc + 32 * ks), t);
+        t = mfma16(ak, ld8(sm.zTl + bc + 32 * ks), t);
       }
+      ds[ct] = acc - t;
+    }
     __syncthreads();
   }
   if (a.ds0) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 32 * w + 16 * rt + 4 * g + e, col = v0 + 16 * ct + l;
-          a.ds0[(unit * kDim + row) * kDim + col] = ds[rt][ct][e];
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * w + 4 * g + e, col = v0 + 16 * ct + l;
+        a.ds0[(unit * kDim + row) * kDim + col] = ds[ct][e];
+      }
   }
 }
 
@@ -977,9 +969,9 @@ hipError_t launch_gdn_bwd(const BwdArgs& a, int stage, hipStream_t stream) {
     // 32-column value blocks, or 16-column ones when that is still less than
     // one workgroup per compute unit of the device
     if ((long)a.geo.N * a.H * 8 <= a.cus)
-      hipLaunchKernelGGL(gdn_bwd_dh_kernel<1>, dim3(state_grid(a.geo.N, a.H, 8)), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(gdn_bwd_dh_kernel<1>, dim3(state_grid(a.geo.N, a.H, 8)), dim3(512), 0, stream, a);
     else
-      hipLaunchKernelGGL(gdn_bwd_dh_kernel<2>, dim3(state_grid(a.geo.N, a.H, 4)), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(gdn_bwd_dh_kernel<2>, dim3(state_grid(a.geo.N, a.H, 4)), dim3(512), 0, stream, a);
   }
   else if (stage == 1)
     hipLaunchKernelGGL(gdn_bwd_sprod_kernel, dim3(cms), dim3(512), 0, stream, a);
