@@ -18,7 +18,9 @@ Besides these, :func:`state_summary` / :func:`apply_state_summary` (the
 affine summary of a sequence) and :func:`short_conv` (module ``oracle.conv``,
 the causal depthwise Conv1d + SiLU that forms q, k, v) and module
 ``oracle.grad`` (gradients of the recurrence by fp64 reverse-mode
-differentiation, pinned by ``tests/test_grad_pins.py``).
+differentiation, pinned by ``tests/test_grad_pins.py``) and module
+``oracle.gate`` (the in-kernel gate's formula, pinned by
+``tests/test_gate_pins.py``).
 
 Every function is pinned by ``tests/test_oracle_pins.py`` (and
 ``tests/test_conv_pins.py``) against facts fixed by the mathematics (closed forms, invariants, hand-derived fixtures); see the
