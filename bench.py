@@ -94,6 +94,8 @@ def parse():
                     help="fwd: the forward pass (default); summary: the affine state summary and its apply step; "
                          "conv: the causal depthwise Conv1d + SiLU forming q, k, v (D = 3*H*128, W = 4); "
                          "bwd: the GDN backward pass")
+    ap.add_argument("--gate-in-kernel", action="store_true",
+                    help="fwd: call the gated entry (raw gate, A_log, dt_bias; the gate formed in the kernel)")
     ap.add_argument("--scrub-mib", type=int, default=1024, help="MiB read between timed calls (0: none)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run plain device-to-device copies of this many MiB (counter calibration)")
@@ -341,10 +343,21 @@ def main():
         bench_bwd(args, gdn, gi, inp, q, k, v, g, beta, dev)
         return
     stream = torch.cuda.current_stream(dev)
-    fn = gdn.lib.kda_chunk_fwd if inp.kda else gdn.lib.gdn_chunk_fwd
     P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
-    call_args = (P(q), P(k), P(v), P(g), P(beta), P(s0), cu_p, N, B, T, H, K, V, float(inp.scale), int(inp.flags),
-                 P(o), P(fs), P(ws), ws_bytes, ctypes.c_void_p(stream.cuda_stream))
+    if args.gate_in_kernel:
+        if inp.gate_raw is None:
+            raise SystemExit("--gate-in-kernel: the %s workload has no raw gate" % args.workload)
+        g_raw = torch.from_numpy(inp.gate_raw).to(dev)
+        a_log = torch.from_numpy(inp.A_log).to(dev)
+        dt_bias = torch.from_numpy(inp.dt_bias).to(dev)
+        fn = gdn.lib.kda_chunk_fwd_gated if inp.kda else gdn.lib.gdn_chunk_fwd_gated
+        call_args = (P(q), P(k), P(v), P(g_raw), P(a_log), P(dt_bias), P(beta), P(s0), cu_p, N, B, T, H, K, V,
+                     float(inp.scale), int(inp.flags), P(o), P(fs), P(ws), ws_bytes,
+                     ctypes.c_void_p(stream.cuda_stream))
+    else:
+        fn = gdn.lib.kda_chunk_fwd if inp.kda else gdn.lib.gdn_chunk_fwd
+        call_args = (P(q), P(k), P(v), P(g), P(beta), P(s0), cu_p, N, B, T, H, K, V, float(inp.scale),
+                     int(inp.flags), P(o), P(fs), P(ws), ws_bytes, ctypes.c_void_p(stream.cuda_stream))
 
     def step():
         rc = fn(*call_args)
@@ -430,7 +443,7 @@ def main():
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": recorded_traffic(args.workload, dom["symbol"]),
+        "traffic": None if args.gate_in_kernel else recorded_traffic(args.workload, dom["symbol"]),
     }
     path_gbps = path_bytes / (ms_per_step * 1e-3) / 1e9
     mfma_frac = th * ALG_FLOPS_PER_TH / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
@@ -475,6 +488,8 @@ def main():
         "kda": "KDA B=2 T=8192 H=32 K=V=128 per-channel log2 gate",
         "tiny": "GDN B=1 T=256 H=2",
     }[args.workload]
+    if args.gate_in_kernel:
+        wl += ", gate -exp(A_log) softplus(x + dt_bias) formed in the kernel"
     line = {
         "metric": METRIC,
         "value": round(value, 1),

@@ -37,7 +37,7 @@ EXPORTED = (
     "gdn_timing_enable", "gdn_timing_read", "gdn_state_summary", "kda_state_summary",
     "gdn_state_summary_workspace_bytes", "gdn_state_summary_apply", "gdn_short_conv",
     "gdn_short_conv_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes",
-    "gdn_bwd_timing_read",
+    "gdn_bwd_timing_read", "gdn_chunk_fwd_gated", "kda_chunk_fwd_gated",
 )
 
 
@@ -67,6 +67,10 @@ def _load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p, p, sz, p]
+    for name in ("gdn_chunk_fwd_gated", "kda_chunk_fwd_gated"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p, p, sz, p]
     lib.gdn_timing_enable.restype = ctypes.c_int
     lib.gdn_timing_enable.argtypes = [i32]
     lib.gdn_timing_read.restype = ctypes.c_int
@@ -184,10 +188,23 @@ def _check_inputs(q, k, v, g, beta, kda: bool, initial_state, cu):
     return B, T, H, K, V, N
 
 
+def _check_gate_params(kda, q, A_log, dt_bias, H, K):
+    for name, t, shape in (("A_log", A_log, (H,)), ("dt_bias", dt_bias, (H, K) if kda else (H,))):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch tensor" % name)
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("%s must be a contiguous fp32 tensor on %s" % (name, q.device))
+        if tuple(t.shape) != shape:
+            raise ValueError("%s must have shape %s (got %s)" % (name, shape, tuple(t.shape)))
+
+
 def _chunk_fwd(kda, q, k, v, g, beta, scale, initial_state, cu_seqlens, l2norm_qk, beta_sigmoid,
-               output_final_state, workspace, stream):
+               output_final_state, workspace, stream, A_log=None, dt_bias=None):
     cu = _cu_array(cu_seqlens)
     B, T, H, K, V, N = _check_inputs(q, k, v, g, beta, kda, initial_state, cu)
+    gated = A_log is not None or dt_bias is not None
+    if gated:
+        _check_gate_params(kda, q, A_log, dt_bias, H, K)
     scale = K ** -0.5 if scale is None else float(scale)
     flags = _flags(l2norm_qk, beta_sigmoid, output_final_state)
     o = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=q.device)
@@ -200,11 +217,17 @@ def _chunk_fwd(kda, q, k, v, g, beta, scale, initial_state, cu_seqlens, l2norm_q
         workspace = torch.empty(int(need), dtype=torch.uint8, device=q.device)
     elif workspace.numel() * workspace.element_size() < need:
         raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel() * workspace.element_size(), need))
-    fn = lib.kda_chunk_fwd if kda else lib.gdn_chunk_fwd
-    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _cu_ptr(cu), N,
-              B, T, H, K, V, scale, flags, _ptr(o), _ptr(fs), _ptr(workspace),
-              0 if workspace is None else workspace.numel() * workspace.element_size(),
-              _stream_ptr(q.device, stream)))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if gated:
+        fn = lib.kda_chunk_fwd_gated if kda else lib.gdn_chunk_fwd_gated
+        _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(A_log), _ptr(dt_bias), _ptr(beta), _ptr(initial_state),
+                  _cu_ptr(cu), N, B, T, H, K, V, scale, flags, _ptr(o), _ptr(fs), _ptr(workspace), ws_bytes,
+                  _stream_ptr(q.device, stream)))
+    else:
+        fn = lib.kda_chunk_fwd if kda else lib.gdn_chunk_fwd
+        _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _cu_ptr(cu), N,
+                  B, T, H, K, V, scale, flags, _ptr(o), _ptr(fs), _ptr(workspace), ws_bytes,
+                  _stream_ptr(q.device, stream)))
     return o, fs
 
 
@@ -223,6 +246,27 @@ def kda_chunk_fwd(q, k, v, g, beta, scale: Optional[float] = None, initial_state
     """KDA forward: as :func:`gdn_chunk_fwd` with g fp32 [B,T,H,128] in log2 units."""
     return _chunk_fwd(True, q, k, v, g, beta, scale, initial_state, cu_seqlens, l2norm_qk, beta_sigmoid,
                       output_final_state, workspace, stream)
+
+
+def gdn_chunk_fwd_gated(q, k, v, g_raw, A_log, dt_bias, beta, scale: Optional[float] = None, initial_state=None,
+                        cu_seqlens=None, l2norm_qk: bool = False, beta_sigmoid: bool = False,
+                        output_final_state: bool = True, workspace: Optional[torch.Tensor] = None, stream=None):
+    """GDN forward with the gate formed in the kernel:
+    g = -exp(A_log[h]) * softplus(g_raw + dt_bias[h]). g_raw fp32 [B,T,H],
+    A_log, dt_bias fp32 [H]. Otherwise as :func:`gdn_chunk_fwd`."""
+    return _chunk_fwd(False, q, k, v, g_raw, beta, scale, initial_state, cu_seqlens, l2norm_qk, beta_sigmoid,
+                      output_final_state, workspace, stream, A_log, dt_bias)
+
+
+def kda_chunk_fwd_gated(q, k, v, g_raw, A_log, dt_bias, beta, scale: Optional[float] = None, initial_state=None,
+                        cu_seqlens=None, l2norm_qk: bool = False, beta_sigmoid: bool = False,
+                        output_final_state: bool = True, workspace: Optional[torch.Tensor] = None, stream=None):
+    """KDA forward with the gate formed in the kernel, in log2 units:
+    g = -exp(A_log[h]) * softplus(g_raw + dt_bias[h, :]) / ln 2. g_raw fp32
+    [B,T,H,128], A_log fp32 [H], dt_bias fp32 [H,128]. Otherwise as
+    :func:`kda_chunk_fwd`."""
+    return _chunk_fwd(True, q, k, v, g_raw, beta, scale, initial_state, cu_seqlens, l2norm_qk, beta_sigmoid,
+                      output_final_state, workspace, stream, A_log, dt_bias)
 
 
 def gdn_chunk_bwd(q, k, v, g, beta, do, scale: Optional[float] = None, initial_state=None, d_final_state=None,

@@ -363,7 +363,8 @@ int check_common(const void* q, const void* k, const void* v, const float* g, co
 int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float* g, const void* beta,
               const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
               int32_t H, int32_t K, int32_t V, float scale, uint32_t flags, void* o, float* final_state,
-              void* workspace, size_t workspace_bytes, void* stream_ptr) {
+              void* workspace, size_t workspace_bytes, void* stream_ptr, bool gated = false,
+              const float* a_log = nullptr, const float* dt_bias = nullptr) {
   g_last_error.clear();
   Problem p;
   p.kda = kda;
@@ -371,6 +372,11 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
   if (rc) return rc;
   rc = check_common(q, k, v, g, beta, scale, flags);
   if (rc) return rc;
+  if (gated) {
+    if (!a_log || !dt_bias) return fail(GDN_ERR_INVALID_ARGUMENT, "A_log and dt_bias must be non-NULL");
+    if (kda && (!aligned16(dt_bias) || !aligned16(g)))
+      return fail(GDN_ERR_INVALID_ARGUMENT, "KDA gate logits and dt_bias must be 16-byte aligned");
+  }
   if (!o) return fail(GDN_ERR_INVALID_ARGUMENT, "o must be non-NULL");
   if (!aligned16(o)) return fail(GDN_ERR_INVALID_ARGUMENT, "o must be 16-byte aligned");
   if ((flags & GDN_OUTPUT_FINAL_STATE) && !final_state)
@@ -401,6 +407,8 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
   pa.vec = reinterpret_cast<float*>(W.base + L.vec);
   pa.gk = nullptr;
   pa.kdec = kda ? reinterpret_cast<uint16_t*>(W.base + L.kdec) : nullptr;
+  pa.a_log = gated ? a_log : nullptr;
+  pa.dt_bias = gated ? dt_bias : nullptr;
   pa.geo = geo;
   pa.H = H;
   pa.scale = scale;
@@ -709,6 +717,24 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   void* workspace, size_t workspace_bytes, void* stream) {
   return chunk_fwd(true, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, scale, flags, o,
                    final_state, workspace, workspace_bytes, stream);
+}
+
+int gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, const float* g_raw, const float* A_log,
+                        const float* dt_bias, const void* beta, const float* initial_state,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+                        int32_t V, float scale, uint32_t flags, void* o, float* final_state, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return chunk_fwd(false, q, k, v, g_raw, beta, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, scale, flags,
+                   o, final_state, workspace, workspace_bytes, stream, true, A_log, dt_bias);
+}
+
+int kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const float* g_raw, const float* A_log,
+                        const float* dt_bias, const void* beta, const float* initial_state,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+                        int32_t V, float scale, uint32_t flags, void* o, float* final_state, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return chunk_fwd(true, q, k, v, g_raw, beta, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, scale, flags,
+                   o, final_state, workspace, workspace_bytes, stream, true, A_log, dt_bias);
 }
 
 size_t gdn_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,

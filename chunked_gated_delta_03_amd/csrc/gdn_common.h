@@ -32,6 +32,34 @@ __device__ __forceinline__ void split_bf(float x, uint16_t& hi, uint16_t& lo) {
   lo = f2bf(x - bf2f(hi));
 }
 
+// ---- in-kernel gate --------------------------------------------------------
+// softplus(y) / ln 2 = log2(1 + e^y) = max(y, 0) log2(e) + log2(1 + u) with
+// u = e^-|y| in (0, 1]. log2(1 + u) by Goldberg's correction of the rounded
+// sum ("What every computer scientist should know about floating-point
+// arithmetic", Theorem 4): w = 1 + u, log2(1 + u) = log2(w) u / (w - 1), or
+// u log2(e) when w rounds to 1 (w - 1 is exact). v_exp_f32, v_log_f32 and
+// v_rcp_f32 directly: w is in [1, 2], so no denormal handling is needed, and
+// a u that underflows gives l = 0. Relative error below 4e-6 for y > -80
+// (most of it from rounding |y| log2(e) ahead of the exponential when |y|
+// is large, where softplus(y) is below e^-10), a few ulp near y = 0.
+__device__ __forceinline__ float softplus_log2(float y) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float u = __builtin_amdgcn_exp2f(-fabsf(y) * kLog2e);
+  const float w = 1.0f + u;
+  const float d = w - 1.0f;
+  const float l = (d == 0.0f) ? u * kLog2e : __builtin_amdgcn_logf(w) * (u * __builtin_amdgcn_rcpf(d));
+  return fmaxf(y, 0.0f) * kLog2e + l;
+}
+// Gate from the raw per-token value x and the head's parameters:
+// -exp(A_log) softplus(x + dt_bias), in log2 units (KDA) ...
+__device__ __forceinline__ float gate_log2(float x, float exp_a_log, float dt_bias) {
+  return -exp_a_log * softplus_log2(x + dt_bias);
+}
+// ... or in natural-log units (GDN).
+__device__ __forceinline__ float gate_ln(float x, float exp_a_log, float dt_bias) {
+  return -exp_a_log * 0.6931471805599453f * softplus_log2(x + dt_bias);
+}
+
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;

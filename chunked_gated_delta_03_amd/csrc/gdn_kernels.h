@@ -18,6 +18,11 @@ struct PrepareArgs {
   float* vec;      // [H,NT,8,64]
   float* gk;       // [H,NT,64,128], KDA stage entry only
   uint16_t* kdec;  // [H,NT] blocks of kKdecElems, KDA whole pass only (see kda_kdec_*)
+  // In-kernel gate: when a_log != nullptr, g holds the raw gate values x and
+  // the gate is -exp(a_log[h]) softplus(x + dt_bias) (dt_bias [H] GDN,
+  // [H,K] KDA), natural log for GDN, log2 for KDA.
+  const float* a_log;
+  const float* dt_bias;
   Geometry geo;
   int H;
   float scale;

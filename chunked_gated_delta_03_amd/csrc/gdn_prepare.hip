@@ -282,7 +282,7 @@ __device__ __forceinline__ void gdn_prepare_wave(const PrepareArgs& a, PrepSmem&
 
   // own rows of the item in flight, with the gate and beta (wave 0)
   u16x8 kw[4], qw[4];
-  float graw = 0.f;
+  float graw = 0.f, ga = 0.f, gb = 0.f;
   uint16_t braw = 0;
   auto fetch = [&](int it) {
     const int c = it / a.H, h = it - (it / a.H) * a.H;
@@ -293,6 +293,10 @@ __device__ __forceinline__ void gdn_prepare_wave(const PrepareArgs& a, PrepSmem&
       const size_t off = (size_t)(ci.tok0 + min(lane, ci.len - 1)) * a.H + h;
       graw = a.g[off];
       braw = a.beta[off];
+      if (a.a_log) {
+        ga = a.a_log[h];
+        gb = a.dt_bias[h];
+      }
     }
   };
   auto kblk = [&](int J, u16x8 (&x)[4]) {
@@ -338,7 +342,8 @@ __device__ __forceinline__ void gdn_prepare_wave(const PrepareArgs& a, PrepSmem&
     }
     if constexpr (W == 0) {
       const bool valid = lane < ci.len;
-      sm.G[lane] = wave_inclusive_sum(valid ? graw : 0.0f);
+      const float gt = a.a_log ? gate_ln(graw, expf(ga), gb) : graw;
+      sm.G[lane] = wave_inclusive_sum(valid ? gt : 0.0f);
       const float b = valid ? bf2f(braw) : 0.0f;
       sm.beta[lane] = ((a.flags & 2u) && valid) ? 1.0f / (1.0f + expf(-b)) : b;
     }
@@ -635,7 +640,26 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
                           : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (wave == 0) load_beta(a, ci, h, lane, sBeta);
+    float ea = 0.f;
+    float4 db = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.a_log) {
+      ea = a.a_log[h];
+      db = *reinterpret_cast<const float4*>(a.dt_bias + (size_t)h * kDim + 4 * cq);
+    }
     put_qk_norms(a, ci, tid, x, sk, sq, sRk, sRq);
+    // in-kernel gate, after the q, k work so that the gate loads have landed
+    if (a.a_log) {
+      ea = expf(ea);
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        if (8 * sg + rr < ci.len) {
+          gv[rr].x = gate_log2(gv[rr].x, ea, db.x);
+          gv[rr].y = gate_log2(gv[rr].y, ea, db.y);
+          gv[rr].z = gate_log2(gv[rr].z, ea, db.z);
+          gv[rr].w = gate_log2(gv[rr].w, ea, db.w);
+        }
+      }
+    }
   }
 
   // per-channel cumulative gate: each thread scans its 8 rows in registers;

@@ -105,6 +105,11 @@ class GdnInputs:
     beta: np.ndarray
     initial_state: Optional[np.ndarray]
     cu_seqlens: Optional[np.ndarray]
+    # the draws g was made from (gdn, varlen, long, kda recipes): the raw gate
+    # (a [B,T,H] or x [B,T,H,K]), A_log [H] and dt_bias [H] or [H,K], fp32
+    gate_raw: Optional[np.ndarray] = None
+    A_log: Optional[np.ndarray] = None
+    dt_bias: Optional[np.ndarray] = None
 
     @property
     def num_seqs(self) -> int:
@@ -169,6 +174,7 @@ def make_inputs(
     v = rng.standard_normal((*shape_tok, V), dtype=np.float32)
     beta_logit = rng.standard_normal(shape_tok, dtype=np.float32)
 
+    gate_raw = A_log = dt_bias = None
     if name == "tiny":
         q /= np.sqrt((q.astype(np.float64) ** 2).sum(-1, keepdims=True)).astype(np.float32)
         k /= np.sqrt((k.astype(np.float64) ** 2).sum(-1, keepdims=True)).astype(np.float32)
@@ -180,12 +186,14 @@ def make_inputs(
         dt_bias = (rng.standard_normal((H, K), dtype=np.float32) * np.float32(0.1)).astype(np.float32)
         x = rng.standard_normal((*shape_tok, K), dtype=np.float32)
         g = (-_softplus(x + dt_bias[None, None]) * np.exp(A_log)[None, None, :, None] / np.float32(math.log(2.0))).astype(np.float32)
+        gate_raw = x
     else:
         beta = beta_logit
         A_log = rng.uniform(0.0, math.log(16.0), size=(H,)).astype(np.float32)
         dt_bias = (rng.standard_normal((H,), dtype=np.float32) * np.float32(0.1)).astype(np.float32)
         a = rng.standard_normal(shape_tok, dtype=np.float32)
         g = (-np.exp(A_log)[None, None, :] * _softplus(a + dt_bias[None, None, :])).astype(np.float32)
+        gate_raw = a
 
     s0 = None
     if name == "varlen":
@@ -195,7 +203,7 @@ def make_inputs(
         name=name, B=B, T=T, H=H, K=K, V=V, kda=kda, flags=flags, scale=scale,
         q=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k), v=f32_to_bf16_bits(v),
         g=np.ascontiguousarray(g, dtype=np.float32), beta=f32_to_bf16_bits(beta),
-        initial_state=s0, cu_seqlens=cu,
+        initial_state=s0, cu_seqlens=cu, gate_raw=gate_raw, A_log=A_log, dt_bias=dt_bias,
     )
 
 

@@ -111,6 +111,32 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, float scale, uint32_t flags,
                   void* o, float* final_state, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Whole forward pass with the gate formed in the kernel (use_gate_in_kernel
+ * of the native forward contract on the 2026-11-06 "Diff Coverage" page; the
+ * A_log / dt_bias gate parameters of _prepare_kda on the
+ * kimi_delta_attention_ascendc.py coverage page). The pages name the inputs
+ * but print no formula; the one taken is the gate of the GDN and KDA layers:
+ *   GDN: g[b,t,h]   = -exp(A_log[h]) * softplus(g_raw[b,t,h] + dt_bias[h])
+ *        (natural log), g_raw fp32 [B,T,H], A_log fp32 [H], dt_bias fp32 [H];
+ *   KDA: g[b,t,h,d] = -exp(A_log[h]) * softplus(g_raw[b,t,h,d] + dt_bias[h,d])
+ *        / ln 2 (log2), g_raw fp32 [B,T,H,K], A_log fp32 [H], dt_bias fp32
+ *        [H,K]; g_raw and dt_bias 16-byte aligned;
+ * softplus(y) = log(1 + e^y), evaluated in fp32. A_log and dt_bias are
+ * device pointers and must be non-NULL (GDN_ERR_INVALID_ARGUMENT). The
+ * result equals gdn_chunk_fwd / kda_chunk_fwd given that g; every other
+ * argument, the workspace size and the error behaviour are theirs. The
+ * lower-bounded "safe gate" variant is not provided (no formula is given). */
+int gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, const float* g_raw, const float* A_log,
+                        const float* dt_bias, const void* beta, const float* initial_state,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+                        int32_t V, float scale, uint32_t flags, void* o, float* final_state, void* workspace,
+                        size_t workspace_bytes, void* stream);
+int kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const float* g_raw, const float* A_log,
+                        const float* dt_bias, const void* beta, const float* initial_state,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+                        int32_t V, float scale, uint32_t flags, void* o, float* final_state, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 /* Per-kernel timing of gdn_chunk_fwd / kda_chunk_fwd, for benchmarks. While
  * enabled (per calling thread), every whole-pass call records three HIP
  * events on its stream: before the prepare kernel, between the prepare and

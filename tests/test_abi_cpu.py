@@ -29,7 +29,7 @@ def test_header_declares_expected_entry_points():
                  "gdn_stage_prepare", "gdn_stage_fwd_h", "gdn_stage_finalize", "gdn_num_chunks",
                  "gdn_state_summary", "kda_state_summary", "gdn_state_summary_workspace_bytes",
                  "gdn_state_summary_apply", "gdn_short_conv", "gdn_short_conv_workspace_bytes",
-                 "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes"):
+                 "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_chunk_fwd_gated", "kda_chunk_fwd_gated"):
         assert must in names
 
 
@@ -79,6 +79,33 @@ def test_invalid_arguments_rejected(gdn, kw, code, msg, kda):
     rc = _call_fwd(gdn, kda=kda, **kw)
     assert rc == code
     assert msg in gdn.last_error()
+
+
+def _call_fwd_gated(gdn, kda=False, a_log=FAKE, dt_bias=FAKE, g=FAKE, B=1, T=64, H=2, K=128, scale=0.1, flags=4):
+    fn = gdn.lib.kda_chunk_fwd_gated if kda else gdn.lib.gdn_chunk_fwd_gated
+    return fn(FAKE, FAKE, FAKE, g, a_log, dt_bias, FAKE, None, None, B, B, T, H, K, 128, scale, flags,
+              FAKE, FAKE, None, 0, None)
+
+
+@pytest.mark.parametrize("kda", [False, True])
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(a_log=None), 1, "A_log and dt_bias"),
+    (dict(dt_bias=None), 1, "A_log and dt_bias"),
+    (dict(g=None), 1, "non-NULL"),
+    (dict(K=64), 2, "K = V = 128"),
+    (dict(scale=0.0), 1, "scale"),
+])
+def test_gated_entries_validate_before_device(gdn, kw, code, msg, kda):
+    rc = _call_fwd_gated(gdn, kda=kda, **kw)
+    assert rc == code
+    assert msg in gdn.last_error()
+
+
+def test_kda_gated_requires_aligned_gate_operands(gdn):
+    rc = _call_fwd_gated(gdn, kda=True, dt_bias=ctypes.c_void_p(0x100004))
+    assert rc == 1 and "16-byte aligned" in gdn.last_error()
+    rc = _call_fwd_gated(gdn, kda=True, g=ctypes.c_void_p(0x100008))
+    assert rc == 1 and "16-byte aligned" in gdn.last_error()
 
 
 def test_num_chunks(gdn):
