@@ -131,3 +131,21 @@ def loss_value(inp, do: np.ndarray, ds_final: Optional[np.ndarray], flags: Optio
             if ds_final is not None:
                 total += float((f64(ds_final)[n] * S).sum())
     return total
+
+
+def gate_grads(kda: bool, x: np.ndarray, a_log: np.ndarray, dt_bias: np.ndarray, dg: np.ndarray) -> dict:
+    """Chain rule through the in-kernel gate of ``oracle.gate`` (fp64 autograd):
+    for the gradient dg of the loss with respect to g = -exp(A_log) softplus(x
+    + dt_bias) (divided by ln 2 for KDA), returns the gradients with respect to
+    x (shape of x), A_log [H] and dt_bias ([H] GDN, [H,K] KDA)."""
+    f64 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    xt, at, bt = f64(x), f64(a_log), f64(dt_bias)
+    for t in (xt, at, bt):
+        t.requires_grad_(True)
+    zero = torch.zeros((), dtype=torch.float64)
+    if kda:
+        g = -torch.exp(at)[:, None] * torch.logaddexp(zero, xt + bt) / float(np.log(2.0))
+    else:
+        g = -torch.exp(at) * torch.logaddexp(zero, xt + bt)
+    (g * f64(dg)).sum().backward()
+    return dict(dx=xt.grad.numpy(), da_log=at.grad.numpy(), ddt_bias=bt.grad.numpy())

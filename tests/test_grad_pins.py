@@ -122,3 +122,31 @@ def test_beta_zero_closed_form():
     assert np.abs(r["ds0"][0] - ref).max() <= 1e-12 * np.abs(ref).max()
     assert np.abs(r["dv"]).max() == 0.0
     assert np.abs(r["dk"]).max() == 0.0
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_gate_chain_rule_matches_finite_differences(kda):
+    """Loss as a function of the raw gate x and the gate parameters (A_log,
+    dt_bias), through oracle.gate: central differences along random directions
+    equal <grad, D> for the gradients of grads() chained by gate_grads()."""
+    from oracle import gate as ogate
+    rng = np.random.default_rng(21 + kda)
+    inp = gi.random_problem(rng, 1, 70, 2, 128, 128, kda=kda, with_initial_state=True)
+    H, K = inp.H, inp.K
+    x = rng.standard_normal(inp.g.shape)
+    a_log = rng.uniform(0, np.log(16), H)
+    dt = rng.standard_normal((H, K) if kda else (H,)) * 0.1
+    gate = ogate.kda_gate if kda else ogate.gdn_gate
+    inp = gi.GdnInputs(**{**inp.__dict__, "g": gate(x, a_log, dt)})
+    do, ds = _cot(inp, 22)
+    r = og.grads(inp, do, ds)
+    gg = og.gate_grads(kda, x, a_log, dt, r["dg"])
+    eps = 1e-6
+    for key, val, grad in (("x", x, gg["dx"]), ("a_log", a_log, gg["da_log"]), ("dt", dt, gg["ddt_bias"])):
+        d = rng.standard_normal(val.shape)
+        args = lambda s: {"x": x, "a_log": a_log, "dt": dt, key: val + s * eps * d}
+        lp = og.loss_value(inp, do, ds, overrides={"g": gate(*args(1).values())})
+        lm = og.loss_value(inp, do, ds, overrides={"g": gate(*args(-1).values())})
+        fd = (lp - lm) / (2 * eps)
+        an = float((grad * d).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (key, fd, an)
