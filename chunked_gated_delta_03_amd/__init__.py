@@ -37,7 +37,7 @@ EXPORTED = (
     "gdn_timing_enable", "gdn_timing_read", "gdn_state_summary", "kda_state_summary",
     "gdn_state_summary_workspace_bytes", "gdn_state_summary_apply", "gdn_short_conv",
     "gdn_short_conv_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes",
-    "gdn_bwd_timing_read", "gdn_chunk_fwd_gated", "kda_chunk_fwd_gated",
+    "gdn_bwd_timing_read", "gdn_chunk_fwd_gated", "kda_chunk_fwd_gated", "gdn_chunk_bwd_gated",
 )
 
 
@@ -95,6 +95,9 @@ def _load() -> ctypes.CDLL:
     lib.gdn_chunk_bwd.restype = ctypes.c_int
     lib.gdn_chunk_bwd.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p,
                                   p, p, p, p, p, p, p, sz, p]
+    lib.gdn_chunk_bwd_gated.restype = ctypes.c_int
+    lib.gdn_chunk_bwd_gated.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p,
+                                        p, p, p, p, p, p, p, p, p, sz, p]
     lib.gdn_stage_prepare.restype = ctypes.c_int
     lib.gdn_stage_prepare.argtypes = [i32, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p, p, p, p]
     lib.gdn_stage_fwd_h.restype = ctypes.c_int
@@ -271,14 +274,21 @@ def kda_chunk_fwd_gated(q, k, v, g_raw, A_log, dt_bias, beta, scale: Optional[fl
 
 def gdn_chunk_bwd(q, k, v, g, beta, do, scale: Optional[float] = None, initial_state=None, d_final_state=None,
                   cu_seqlens=None, l2norm_qk: bool = False, beta_sigmoid: bool = False,
-                  workspace: Optional[torch.Tensor] = None, stream=None):
+                  workspace: Optional[torch.Tensor] = None, stream=None, A_log=None, dt_bias=None):
     """GDN backward: gradients of <do, o> + <d_final_state, final_state> for the
     forward of :func:`gdn_chunk_fwd` with the same arguments. do bf16
     [B,T,H,128]; d_final_state fp32 [N,H,128,128] or None (zero).
     Returns fp32 (dq, dk, dv [B,T,H,128], dg [B,T,H] w.r.t. the raw gate,
-    dbeta [B,T,H] w.r.t. beta as passed, d_initial_state [N,H,128,128])."""
+    dbeta [B,T,H] w.r.t. beta as passed, d_initial_state [N,H,128,128]).
+
+    With A_log and dt_bias (fp32 [H]) this is the backward of
+    :func:`gdn_chunk_fwd_gated`: g holds the raw gate values, dg is the
+    gradient w.r.t. them, and (dA_log [H], ddt_bias [H]) are appended."""
     cu = _cu_array(cu_seqlens)
     B, T, H, K, V, N = _check_inputs(q, k, v, g, beta, False, initial_state, cu)
+    gated = A_log is not None or dt_bias is not None
+    if gated:
+        _check_gate_params(False, q, A_log, dt_bias, H, K)
     if (not isinstance(do, torch.Tensor) or do.dtype != torch.bfloat16 or not do.is_contiguous()
             or tuple(do.shape) != (B, T, H, V) or do.device != q.device):
         raise ValueError("do must be a contiguous bf16 [B,T,H,V] tensor on %s" % q.device)
@@ -299,10 +309,18 @@ def gdn_chunk_bwd(q, k, v, g, beta, do, scale: Optional[float] = None, initial_s
         workspace = torch.empty(int(need), dtype=torch.uint8, device=q.device)
     elif workspace.numel() * workspace.element_size() < need:
         raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel() * workspace.element_size(), need))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if gated:
+        da, ddt = torch.empty((H,), **f32), torch.empty((H,), **f32)
+        _check(lib.gdn_chunk_bwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(A_log), _ptr(dt_bias), _ptr(beta),
+                                       _ptr(initial_state), _cu_ptr(cu), N, B, T, H, K, V, scale, flags, _ptr(do),
+                                       _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(da),
+                                       _ptr(ddt), _ptr(dbeta), _ptr(ds0), _ptr(workspace), ws_bytes,
+                                       _stream_ptr(q.device, stream)))
+        return dq, dk, dv, dg, dbeta, ds0, da, ddt
     _check(lib.gdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _cu_ptr(cu), N,
                              B, T, H, K, V, scale, flags, _ptr(do), _ptr(d_final_state), _ptr(dq), _ptr(dk),
-                             _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(ds0), _ptr(workspace),
-                             0 if workspace is None else workspace.numel() * workspace.element_size(),
+                             _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(ds0), _ptr(workspace), ws_bytes,
                              _stream_ptr(q.device, stream)))
     return dq, dk, dv, dg, dbeta, ds0
 

@@ -510,7 +510,8 @@ int state_summary(bool kda, const void* q, const void* k, const void* v, const f
 // dv_new | E, F, D | <dS_next, S>, each 256-byte aligned.
 struct BwdLayout {
   Layout fwd;
-  size_t h = 0, vnew = 0, dhn = 0, dvn = 0, efd = 0, sdot = 0, total = 0;
+  size_t h = 0, vnew = 0, dhn = 0, dvn = 0, efd = 0, sdot = 0, gpart = 0, total = 0;
+  int gate_blocks = 0;  // token blocks of the gate backward
 };
 
 BwdLayout bwd_layout_for(const Problem& p) {
@@ -532,6 +533,9 @@ BwdLayout bwd_layout_for(const Problem& p) {
   off += align256(3 * rows);
   L.sdot = off;
   off += align256(cmH * sizeof(float));
+  L.gate_blocks = (int)(((long)p.B * p.T + gdn::kGateBwdTok - 1) / gdn::kGateBwdTok);
+  L.gpart = off;
+  off += align256((size_t)2 * p.H * L.gate_blocks * sizeof(float));
   L.total = off;
   return L;
 }
@@ -542,7 +546,9 @@ int chunk_bwd(const void* q, const void* k, const void* v, const float* g, const
               const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
               int32_t H, int32_t K, int32_t V, float scale, uint32_t flags, const void* d_o,
               const float* d_final_state, float* dq, float* dk, float* dv, float* dg, float* dbeta,
-              float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream_ptr) {
+              float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream_ptr,
+              bool gated = false, const float* a_log = nullptr, const float* dt_bias = nullptr,
+              float* da_log = nullptr, float* ddt_bias = nullptr) {
   g_last_error.clear();
   Problem p;
   p.kda = false;
@@ -552,6 +558,8 @@ int chunk_bwd(const void* q, const void* k, const void* v, const float* g, const
   if (rc) return rc;
   if (!d_o || !dq || !dk || !dv || !dg || !dbeta)
     return fail(GDN_ERR_INVALID_ARGUMENT, "d_o, dq, dk, dv, dg and dbeta must be non-NULL");
+  if (gated && (!a_log || !dt_bias || !da_log || !ddt_bias))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "A_log, dt_bias, dA_log and ddt_bias must be non-NULL");
   if (!aligned16(d_o) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return fail(GDN_ERR_INVALID_ARGUMENT, "d_o, dq, dk and dv must be 16-byte aligned");
   int cus = 0;
@@ -583,6 +591,8 @@ int chunk_bwd(const void* q, const void* k, const void* v, const float* g, const
   pa.scale = scale;
   pa.flags = flags & ~(uint32_t)GDN_OUTPUT_FINAL_STATE;
   pa.cus = cus;
+  pa.a_log = gated ? a_log : nullptr;
+  pa.dt_bias = gated ? dt_bias : nullptr;
   hipError_t e = gdn::launch_prepare(false, pa, stream);
   if (e != hipSuccess) return hip_fail(e, "prepare launch");
 
@@ -633,6 +643,21 @@ int chunk_bwd(const void* q, const void* k, const void* v, const float* g, const
     e = gdn::launch_gdn_bwd(ba, stage, stream);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     if (g_timing && (rc = bwd_timing_mark(3 + stage, stream))) return rc;
+  }
+  if (gated) {
+    gdn::GateBwdArgs ga{};
+    ga.x = g;
+    ga.a_log = a_log;
+    ga.dt_bias = dt_bias;
+    ga.dg = dg;
+    ga.part = reinterpret_cast<float*>(W.base + L.gpart);
+    ga.da_log = da_log;
+    ga.ddt_bias = ddt_bias;
+    ga.ntok = (long)B * T;
+    ga.H = H;
+    ga.nblk = L.gate_blocks;
+    e = gdn::launch_gate_bwd(ga, stream);
+    if (e != hipSuccess) return hip_fail(e, "gate backward launch");
   }
   return GDN_OK;
 }
@@ -756,6 +781,18 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
                   float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream) {
   return chunk_bwd(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, scale, flags, d_o,
                    d_final_state, dq, dk, dv, dg, dbeta, d_initial_state, workspace, workspace_bytes, stream);
+}
+
+int gdn_chunk_bwd_gated(const void* q, const void* k, const void* v, const float* g_raw, const float* A_log,
+                        const float* dt_bias, const void* beta, const float* initial_state,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+                        int32_t V, float scale, uint32_t flags, const void* d_o, const float* d_final_state,
+                        float* dq, float* dk, float* dv, float* dg_raw, float* dA_log, float* ddt_bias,
+                        float* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return chunk_bwd(q, k, v, g_raw, beta, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, scale, flags, d_o,
+                   d_final_state, dq, dk, dv, dg_raw, dbeta, d_initial_state, workspace, workspace_bytes, stream,
+                   true, A_log, dt_bias, dA_log, ddt_bias);
 }
 
 int gdn_state_summary(const void* q, const void* k, const void* v, const float* g, const void* beta,

@@ -36,4 +36,24 @@ struct BwdArgs {
 // stage 0: reverse state pass, 1: state products, 2: per-chunk gradients
 hipError_t launch_gdn_bwd(const BwdArgs& a, int stage, hipStream_t stream);
 
+// Backward of the in-kernel gate g = -exp(A_log[h]) softplus(x + dt_bias[h])
+// (GDN, natural log): dg (w.r.t. g) becomes dx = -exp(A_log) sigmoid(x +
+// dt_bias) dg in place, and per head dA_log = sum dg g, ddt_bias = sum dx,
+// summed in a fixed order (partial sums per block of kGateBwdTok tokens,
+// then one pass over the blocks).
+constexpr int kGateBwdTok = 2048;
+struct GateBwdArgs {
+  const float* x;        // [ntok,H] raw gate values
+  const float* a_log;    // [H]
+  const float* dt_bias;  // [H]
+  float* dg;             // [ntok,H] in: w.r.t. g, out: w.r.t. x
+  float* part;           // [2][H][nblk] workspace
+  float* da_log;         // [H]
+  float* ddt_bias;       // [H]
+  long ntok;
+  int H;
+  int nblk;              // ceil(ntok / kGateBwdTok)
+};
+hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t stream);
+
 }  // namespace gdn

@@ -980,4 +980,80 @@ hipError_t launch_gdn_bwd(const BwdArgs& a, int stage, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Backward of the in-kernel gate. Block (b, h) takes tokens
+// b*kGateBwdTok .. +kGateBwdTok of head h, thread t the tokens t + 256 j,
+// all eight loads of a thread issued before use. The sums are reduced in a
+// fixed order (per thread in j, across the wave by xor shuffles, across the
+// four waves in wave order), so results are bitwise reproducible.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum_fixed(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+__global__ __launch_bounds__(256) void gate_bwd_partial_kernel(GateBwdArgs a) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  constexpr float kLn2 = 0.6931471805599453f;
+  const int h = blockIdx.y, tid = threadIdx.x;
+  const long t0 = (long)blockIdx.x * kGateBwdTok;
+  const float ea = expf(a.a_log[h]), db = a.dt_bias[h];
+  float xv[8], dv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const long t = t0 + tid + 256 * j;
+    const bool in = t < a.ntok;
+    xv[j] = in ? a.x[t * a.H + h] : 0.f;
+    dv[j] = in ? a.dg[t * a.H + h] : 0.f;
+  }
+  float sa = 0.f, sb = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const long t = t0 + tid + 256 * j;
+    const float y = xv[j] + db;
+    const float g = -ea * kLn2 * softplus_log2(y);
+    const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-y * kLog2e));
+    const float dx = -ea * sig * dv[j];
+    if (t < a.ntok) {
+      a.dg[t * a.H + h] = dx;
+      sa += dv[j] * g;
+      sb += dx;
+    }
+  }
+  __shared__ float red[2][4];
+  sa = wave_sum_fixed(sa);
+  sb = wave_sum_fixed(sb);
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = sa;
+    red[1][tid >> 6] = sb;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    a.part[(size_t)h * a.nblk + blockIdx.x] = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
+    a.part[((size_t)a.H + h) * a.nblk + blockIdx.x] = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
+  }
+}
+
+__global__ __launch_bounds__(64) void gate_bwd_final_kernel(GateBwdArgs a) {
+  const int h = blockIdx.x, lane = threadIdx.x;
+  float sa = 0.f, sb = 0.f;
+  for (int b = lane; b < a.nblk; b += 64) {
+    sa += a.part[(size_t)h * a.nblk + b];
+    sb += a.part[((size_t)a.H + h) * a.nblk + b];
+  }
+  sa = wave_sum_fixed(sa);
+  sb = wave_sum_fixed(sb);
+  if (lane == 0) {
+    a.da_log[h] = sa;
+    a.ddt_bias[h] = sb;
+  }
+}
+
+hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(gate_bwd_partial_kernel, dim3(a.nblk, a.H), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(gate_bwd_final_kernel, dim3(a.H), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace gdn

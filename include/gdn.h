@@ -231,7 +231,8 @@ int gdn_stage_finalize(int32_t kda, const void* q, const void* aqk, const float*
  * then runs the reverse state pass and the per-chunk gradient kernels, all
  * on `stream`. workspace: as gdn_chunk_fwd, sized by
  * gdn_chunk_bwd_workspace_bytes (0 on a contract error; the forward's
- * plus NT*H*288 KiB). Errors as gdn_chunk_fwd; nothing is launched on
+ * plus NT*H*288 KiB and a few KiB for the gated variant's per-head sums).
+ * Errors as gdn_chunk_fwd; nothing is launched on
  * error.
  */
 size_t gdn_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
@@ -241,6 +242,25 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
                   int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, float scale, uint32_t flags,
                   const void* d_o, const float* d_final_state, float* dq, float* dk, float* dv, float* dg,
                   float* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of gdn_chunk_fwd_gated (the gate -exp(A_log[h]) softplus(g_raw +
+ * dt_bias[h]) formed in the kernel): the arguments of gdn_chunk_bwd with
+ * g_raw, A_log and dt_bias as gdn_chunk_fwd_gated takes them, and
+ *   dg_raw   [B,T,H] fp32, the gradient w.r.t. g_raw
+ *            (= -exp(A_log) sigmoid(g_raw + dt_bias) times the gate's);
+ *   dA_log   [H] fp32, sum over tokens of (gradient w.r.t. the gate) * gate;
+ *   ddt_bias [H] fp32, sum over tokens of dg_raw;
+ * all device pointers, required (GDN_ERR_INVALID_ARGUMENT if NULL). The
+ * per-head sums are taken in a fixed order (bitwise reproducible). Same
+ * workspace size as gdn_chunk_bwd; errors and stream behaviour as there. The
+ * pages print no gate formula: the one taken is that of gdn_chunk_fwd_gated. */
+int gdn_chunk_bwd_gated(const void* q, const void* k, const void* v, const float* g_raw, const float* A_log,
+                        const float* dt_bias, const void* beta, const float* initial_state,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+                        int32_t V, float scale, uint32_t flags, const void* d_o, const float* d_final_state,
+                        float* dq, float* dk, float* dv, float* dg_raw, float* dA_log, float* ddt_bias,
+                        float* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /*
  * Affine state summary (_compute_gdn_state_summary_from_prepared and

@@ -29,7 +29,8 @@ def test_header_declares_expected_entry_points():
                  "gdn_stage_prepare", "gdn_stage_fwd_h", "gdn_stage_finalize", "gdn_num_chunks",
                  "gdn_state_summary", "kda_state_summary", "gdn_state_summary_workspace_bytes",
                  "gdn_state_summary_apply", "gdn_short_conv", "gdn_short_conv_workspace_bytes",
-                 "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_chunk_fwd_gated", "kda_chunk_fwd_gated"):
+                 "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_chunk_fwd_gated", "kda_chunk_fwd_gated",
+                 "gdn_chunk_bwd_gated"):
         assert must in names
 
 
@@ -106,6 +107,16 @@ def test_kda_gated_requires_aligned_gate_operands(gdn):
     assert rc == 1 and "16-byte aligned" in gdn.last_error()
     rc = _call_fwd_gated(gdn, kda=True, g=ctypes.c_void_p(0x100008))
     assert rc == 1 and "16-byte aligned" in gdn.last_error()
+
+
+@pytest.mark.parametrize("missing", ["a_log", "dt_bias", "da_log", "ddt_bias"])
+def test_gated_bwd_validates_before_device(gdn, missing):
+    ptr = {n: (None if n == missing else FAKE) for n in ("a_log", "dt_bias", "da_log", "ddt_bias")}
+    rc = gdn.lib.gdn_chunk_bwd_gated(FAKE, FAKE, FAKE, FAKE, ptr["a_log"], ptr["dt_bias"], FAKE, None, None, 1, 1, 64,
+                                     2, 128, 128, 0.1, 0, FAKE, None, FAKE, FAKE, FAKE, FAKE, ptr["da_log"],
+                                     ptr["ddt_bias"], FAKE, None, None, 0, None)
+    assert rc == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert "dA_log" in gdn.last_error()
 
 
 def test_num_chunks(gdn):

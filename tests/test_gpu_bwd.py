@@ -192,3 +192,52 @@ def test_gdn_bwd_deterministic_with_caller_workspace(gdn):
     torch.cuda.synchronize()
     for name, t in zip(NAMES, out):
         assert np.array_equal(t.cpu().numpy().astype(np.float64), first[name]), name
+
+
+# ---------------------------------------------------------------------------
+# Backward of the in-kernel gate (gdn_chunk_bwd_gated): the oracle's gradient
+# w.r.t. the gate, chained through the gate by oracle.grad.gate_grads.
+# ---------------------------------------------------------------------------
+def _gated_cases():
+    import dataclasses
+    big = gi.make_inputs("gdn", B=1, T=5000, H=2)   # three token blocks of the gate reduction, ragged
+    docs = gi.make_inputs("varlen", H=2, doc_lengths=[1, 17, 64, 65, 130])
+    docs = dataclasses.replace(docs, gate_raw=(np.random.default_rng(5).standard_normal((1, docs.T, 2))
+                                               .astype(np.float32)),
+                               A_log=np.array([0.3, 2.0], np.float32), dt_bias=np.array([0.05, -0.1], np.float32))
+    return [("gdn_B2_T300_H3", gi.make_inputs("gdn", B=2, T=300, H=3)), ("gdn_T5000_H2", big),
+            ("varlen_docs", docs)]
+
+
+GATED = _gated_cases()
+
+
+def _run_bwd_gated(gdn, inp, do_bits, dsf):
+    d = to_device(inp)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    do = torch.from_numpy(np.ascontiguousarray(do_bits)).view(torch.bfloat16).cuda()
+    dsf_t = None if dsf is None else torch.from_numpy(dsf).cuda()
+    out = gdn.gdn_chunk_bwd(d["q"], d["k"], d["v"], t(inp.gate_raw), d["beta"], do, scale=inp.scale,
+                            initial_state=d["initial_state"], d_final_state=dsf_t, cu_seqlens=inp.cu_seqlens,
+                            l2norm_qk=bool(inp.flags & 1), beta_sigmoid=bool(inp.flags & 2),
+                            A_log=t(inp.A_log), dt_bias=t(inp.dt_bias))
+    torch.cuda.synchronize()
+    return {n: x.cpu().numpy().astype(np.float64) for n, x in zip(NAMES + ("da_log", "ddt_bias"), out)}
+
+
+@pytest.mark.parametrize("name,inp", GATED, ids=[c[0] for c in GATED])
+def test_gdn_bwd_gated_parity(gdn, name, inp):
+    import dataclasses
+    from oracle import gate as ogate
+    _say("gated bwd case", name, "B,T,H =", inp.B, inp.T, inp.H)
+    do_bits, dsf = _cotangents(inp, 9)
+    got = _run_bwd_gated(gdn, inp, do_bits, dsf)
+    g64 = ogate.gdn_gate(inp.gate_raw, inp.A_log, inp.dt_bias)
+    ref = og.grads(dataclasses.replace(inp, g=g64), gi.bf16_bits_to_f32(do_bits).astype(np.float64),
+                   dsf.astype(np.float64))
+    gg = og.gate_grads(False, inp.gate_raw, inp.A_log, inp.dt_bias, ref["dg"])
+    ref = {**ref, "dg": gg["dx"], "da_log": gg["da_log"], "ddt_bias": gg["ddt_bias"]}
+    _compare(got, ref, NAMES + ("da_log", "ddt_bias"))
+    again = _run_bwd_gated(gdn, inp, do_bits, dsf)
+    for n in ("dg", "da_log", "ddt_bias"):
+        assert np.array_equal(again[n], got[n]), n
