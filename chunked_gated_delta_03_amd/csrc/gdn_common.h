@@ -32,6 +32,13 @@ __device__ __forceinline__ void split_bf(float x, uint16_t& hi, uint16_t& lo) {
   lo = f2bf(x - bf2f(hi));
 }
 
+// 2^x on v_exp_f32 alone. The library exp2f adds a range reduction and an
+// ldexp (about seven instructions) to keep results below 2^-126 as
+// denormals; the decays here only scale bf16 operands and states, where a
+// factor below 2^-126 and zero are the same for every result. Results for
+// normal outputs agree with exp2f to about one ulp.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ---- in-kernel gate --------------------------------------------------------
 // softplus(y) / ln 2 = log2(1 + e^y) = max(y, 0) log2(e) + log2(1 + u) with
 // u = e^-|y| in (0, 1]. log2(1 + u) by Goldberg's correction of the rounded

@@ -708,8 +708,8 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
       for (int e = 0; e < 4; ++e) {
         const float k0 = __uint_as_float(kw[e] << 16), k1 = __uint_as_float(kw[e] & 0xFFFF0000u);
         const float q0 = __uint_as_float(qw[e] << 16), q1 = __uint_as_float(qw[e] & 0xFFFF0000u);
-        const float f0 = exp2f(ga[2 * e]), f1 = exp2f(ga[2 * e + 1]);
-        const float d0 = exp2f(la[2 * e] - ga[2 * e]), d1 = exp2f(la[2 * e + 1] - ga[2 * e + 1]);
+        const float f0 = exp2_hw(ga[2 * e]), f1 = exp2_hw(ga[2 * e + 1]);
+        const float d0 = exp2_hw(la[2 * e] - ga[2 * e]), d1 = exp2_hw(la[2 * e + 1] - ga[2 * e + 1]);
         split2(k0 * f0, k1 * f1, dh[e], dl[e]);
         split2(k0 * d0, k1 * d1, gh[e], gl[e]);
         qq[e] = pack2(q0 * f0, q1 * f1);
@@ -724,7 +724,7 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
     if (tid < 32) {
       const float4 l = *reinterpret_cast<const float4*>(sG + 63 * kLdG + 4 * tid);
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(kd + kKdecDec) + 4 * tid) =
-          make_float4(exp2f(l.x), exp2f(l.y), exp2f(l.z), exp2f(l.w));
+          make_float4(exp2_hw(l.x), exp2_hw(l.y), exp2_hw(l.z), exp2_hw(l.w));
     }
   }
 
@@ -778,8 +778,8 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
       g8(j, d0, gj);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        fi[e] = exp2f(gi[e] - gr[e]);
-        fj[e] = exp2f(gr[e] - gj[e]);
+        fi[e] = exp2_hw(gi[e] - gr[e]);
+        fj[e] = exp2_hw(gr[e] - gj[e]);
       }
       u16x8 ah, al, bh, bl;
       scale_split(row8(sk, i, d0), fi, ah, al);
@@ -810,7 +810,7 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
       g8(i, d0, gi);
       g8(t0 + 4 * psub, d0, gp);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) fa[e] = exp2f(gi[e] - gp[e]);
+      for (int e = 0; e < 8; ++e) fa[e] = exp2_hw(gi[e] - gp[e]);
       const u16x8 ki = row8(sk, i, d0), qi = row8(sq, i, d0);
       u16x8 ah, al;
       scale_split(ki, fa, ah, al);
@@ -821,7 +821,7 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
         float gr[8], fb[8];
         g8(t0 + 4 * P, d0, gr);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) fb[e] = exp2f(psub < P ? gr[e] - gi[e] : -1000.0f);
+        for (int e = 0; e < 8; ++e) fb[e] = exp2_hw(psub < P ? gr[e] - gi[e] : -1000.0f);
         u16x8 bh, bl;
         scale_split(ki, fb, bh, bl);
         const bool rowP = psub == P;
@@ -849,8 +849,8 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
       const u16x4 ki = *reinterpret_cast<const u16x4*>(sk + ei * kLdRow + d);
       const u16x4 kj = *reinterpret_cast<const u16x4*>(sk + ej * kLdRow + d);
       const u16x4 qi = *reinterpret_cast<const u16x4*>(sq + ei * kLdRow + d);
-      const float w0 = bf2f(kj[0]) * exp2f(gi.x - gj.x), w1 = bf2f(kj[1]) * exp2f(gi.y - gj.y);
-      const float w2 = bf2f(kj[2]) * exp2f(gi.z - gj.z), w3 = bf2f(kj[3]) * exp2f(gi.w - gj.w);
+      const float w0 = bf2f(kj[0]) * exp2_hw(gi.x - gj.x), w1 = bf2f(kj[1]) * exp2_hw(gi.y - gj.y);
+      const float w2 = bf2f(kj[2]) * exp2_hw(gi.z - gj.z), w3 = bf2f(kj[3]) * exp2_hw(gi.w - gj.w);
       ekk = fmaf(bf2f(ki[0]), w0, ekk); ekk = fmaf(bf2f(ki[1]), w1, ekk);
       ekk = fmaf(bf2f(ki[2]), w2, ekk); ekk = fmaf(bf2f(ki[3]), w3, ekk);
       eqk = fmaf(bf2f(qi[0]), w0, eqk); eqk = fmaf(bf2f(qi[1]), w1, eqk);

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void kda_finalize_kernel(FinArgs a) {
     const int r = idx >> 7, d = idx & 127;
     float qv = 0.f;
     if (r < ci.len) qv = bf2f(a.q[((size_t)(ci.tok0 + r) * H + h) * kDim + d]);
-    sq[r * kLdRow + d] = f2bf(qv * exp2f(a.gk[cm * (kChunk * kDim) + idx]));
+    sq[r * kLdRow + d] = f2bf(qv * exp2_hw(a.gk[cm * (kChunk * kDim) + idx]));
   }
   for (int idx = tid; idx < 64 * 64; idx += 256) {
     const int r = idx >> 6, cc = idx & 63;

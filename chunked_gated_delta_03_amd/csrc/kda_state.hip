@@ -248,8 +248,8 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
         for (int e = 0; e < 4; ++e) {
           const float k0 = __uint_as_float(kw[e] << 16), k1 = __uint_as_float(kw[e] & 0xFFFF0000u);
           const float q0 = __uint_as_float(qw[e] << 16), q1 = __uint_as_float(qw[e] & 0xFFFF0000u);
-          const float f0 = exp2f(ga[2 * e]), f1 = exp2f(ga[2 * e + 1]);
-          const float d0 = exp2f(gla[2 * e] - ga[2 * e]), d1 = exp2f(gla[2 * e + 1] - ga[2 * e + 1]);
+          const float f0 = exp2_hw(ga[2 * e]), f1 = exp2_hw(ga[2 * e + 1]);
+          const float d0 = exp2_hw(gla[2 * e] - ga[2 * e]), d1 = exp2_hw(gla[2 * e + 1] - ga[2 * e + 1]);
           uint32_t xh, xl;
           split2(k0 * f0, k1 * f1, xh, xl);
           dh[e] = xh;
@@ -266,8 +266,8 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
         kgl[p] = ll;
       }
       if (ltid < 16) {
-        dec0 = make_float4(exp2f(gl0.x), exp2f(gl0.y), exp2f(gl0.z), exp2f(gl0.w));
-        dec1 = make_float4(exp2f(gl1.x), exp2f(gl1.y), exp2f(gl1.z), exp2f(gl1.w));
+        dec0 = make_float4(exp2_hw(gl0.x), exp2_hw(gl0.y), exp2_hw(gl0.z), exp2_hw(gl0.w));
+        dec1 = make_float4(exp2_hw(gl1.x), exp2_hw(gl1.y), exp2_hw(gl1.z), exp2_hw(gl1.w));
       }
     };
 
