@@ -143,6 +143,34 @@ def test_deterministic(gdn):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def test_concurrent_streams_match_sequential(gdn):
+    """Calls enqueued on two streams at once (packed inputs, whose chunk
+    tables go through the library's pinned staging ring, and dense KDA
+    inputs, stream-ordered workspaces) give the same bits as one at a time."""
+    probs = [gi.make_inputs("varlen", H=3, doc_lengths=[70, 1, 200, 64]),
+             gi.make_inputs("kda", B=1, T=150, H=2),
+             gi.make_inputs("varlen", H=2, doc_lengths=[5, 130]),
+             gi.make_inputs("gdn", B=2, T=100, H=2)]
+    ref = [run_gpu(p) for p in probs]
+    devs = [to_device(p) for p in probs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(3):
+        for i, (p, d) in enumerate(zip(probs, devs)):
+            fn = gdn.kda_chunk_fwd if p.kda else gdn.gdn_chunk_fwd
+            s = streams[i % 2]
+            with torch.cuda.stream(s):
+                outs.append((i, fn(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=p.scale,
+                                   initial_state=d["initial_state"], cu_seqlens=p.cu_seqlens,
+                                   l2norm_qk=bool(p.flags & 1), beta_sigmoid=bool(p.flags & 2),
+                                   output_final_state=True, stream=s)))
+    torch.cuda.synchronize()
+    for i, (o, fs) in outs:
+        assert np.array_equal(o.float().cpu().numpy().astype(np.float64), ref[i][0]), i
+        assert np.array_equal(fs.cpu().numpy().astype(np.float64), ref[i][1]), i
+
+
 def test_no_final_state_flag(gdn):
     inp = gi.make_inputs("gdn", B=1, T=130, H=2)
     inp.flags &= ~gi.FLAG_OUTPUT_FINAL_STATE
