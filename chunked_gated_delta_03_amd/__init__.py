@@ -38,6 +38,7 @@ EXPORTED = (
     "gdn_state_summary_workspace_bytes", "gdn_state_summary_apply", "gdn_short_conv",
     "gdn_short_conv_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes",
     "gdn_bwd_timing_read", "gdn_chunk_fwd_gated", "kda_chunk_fwd_gated", "gdn_chunk_bwd_gated",
+    "gdn_state_summary_gated",
 )
 
 
@@ -76,6 +77,9 @@ def _load() -> ctypes.CDLL:
     lib.gdn_timing_read.restype = ctypes.c_int
     lib.gdn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_int64)]
+    lib.gdn_state_summary_gated.restype = ctypes.c_int
+    lib.gdn_state_summary_gated.argtypes = [i32, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, u32, p, p,
+                                            p, sz, p]
     for name in ("gdn_state_summary", "kda_state_summary"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
@@ -327,12 +331,17 @@ def gdn_chunk_bwd(q, k, v, g, beta, do, scale: Optional[float] = None, initial_s
 
 def state_summary(k, v, g, beta, q=None, cu_seqlens=None, kda: bool = False, l2norm_qk: bool = False,
                   beta_sigmoid: bool = False, workspace: Optional[torch.Tensor] = None,
-                  stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                  stream=None, A_log=None, dt_bias=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Affine state summary of every (sequence, head): final = M @ initial + S.
-    Inputs as :func:`gdn_chunk_fwd` / :func:`kda_chunk_fwd` (q optional, unused).
+    Inputs as :func:`gdn_chunk_fwd` / :func:`kda_chunk_fwd` (q optional, unused);
+    with A_log and dt_bias, g holds the raw gate values as for
+    :func:`gdn_chunk_fwd_gated` / :func:`kda_chunk_fwd_gated`.
     Returns (M fp32 [N,H,128,128], S fp32 [N,H,128,128])."""
     cu = _cu_array(cu_seqlens)
     B, T, H, K, V, N = _check_inputs(k if q is None else q, k, v, g, beta, kda, None, cu)
+    gated = A_log is not None or dt_bias is not None
+    if gated:
+        _check_gate_params(kda, k, A_log, dt_bias, H, K)
     flags = _flags(l2norm_qk, beta_sigmoid, False)
     M = torch.empty((N, H, K, K), dtype=torch.float32, device=k.device)
     S = torch.empty((N, H, K, V), dtype=torch.float32, device=k.device)
@@ -343,10 +352,15 @@ def state_summary(k, v, g, beta, q=None, cu_seqlens=None, kda: bool = False, l2n
         workspace = torch.empty(int(need), dtype=torch.uint8, device=k.device)
     elif workspace.numel() * workspace.element_size() < need:
         raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel() * workspace.element_size(), need))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if gated:
+        _check(lib.gdn_state_summary_gated(int(kda), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(A_log), _ptr(dt_bias),
+                                           _ptr(beta), _cu_ptr(cu), N, B, T, H, K, V, flags, _ptr(M), _ptr(S),
+                                           _ptr(workspace), ws_bytes, _stream_ptr(k.device, stream)))
+        return M, S
     fn = lib.kda_state_summary if kda else lib.gdn_state_summary
     _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _cu_ptr(cu), N, B, T, H, K, V, flags,
-              _ptr(M), _ptr(S), _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
-              _stream_ptr(k.device, stream)))
+              _ptr(M), _ptr(S), _ptr(workspace), ws_bytes, _stream_ptr(k.device, stream)))
     return M, S
 
 

@@ -443,7 +443,8 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
 int state_summary(bool kda, const void* q, const void* k, const void* v, const float* g, const void* beta,
                   const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
                   int32_t V, uint32_t flags, float* transition, float* state_ext, void* workspace,
-                  size_t workspace_bytes, void* stream_ptr) {
+                  size_t workspace_bytes, void* stream_ptr, bool gated = false, const float* a_log = nullptr,
+                  const float* dt_bias = nullptr) {
   g_last_error.clear();
   Problem p;
   p.kda = kda;
@@ -452,6 +453,11 @@ int state_summary(bool kda, const void* q, const void* k, const void* v, const f
   rc = check_common(q ? q : k, k, v, g, beta, 1.0f, flags);
   if (rc) return rc;
   if (!transition || !state_ext) return fail(GDN_ERR_INVALID_ARGUMENT, "transition and state_ext must be non-NULL");
+  if (gated) {
+    if (!a_log || !dt_bias) return fail(GDN_ERR_INVALID_ARGUMENT, "A_log and dt_bias must be non-NULL");
+    if (kda && (!aligned16(dt_bias) || !aligned16(g)))
+      return fail(GDN_ERR_INVALID_ARGUMENT, "KDA gate logits and dt_bias must be 16-byte aligned");
+  }
   int cus = 0;
   rc = check_device(&cus);
   if (rc) return rc;
@@ -477,6 +483,8 @@ int state_summary(bool kda, const void* q, const void* k, const void* v, const f
   pa.vec = reinterpret_cast<float*>(W.base + L.vec);
   pa.gk = kda ? reinterpret_cast<float*>(W.base + L.kdec) : nullptr;
   pa.kdec = nullptr;
+  pa.a_log = gated ? a_log : nullptr;
+  pa.dt_bias = gated ? dt_bias : nullptr;
   pa.geo = geo;
   pa.H = H;
   pa.scale = 1.0f;
@@ -809,6 +817,15 @@ int kda_state_summary(const void* q, const void* k, const void* v, const float* 
                       size_t workspace_bytes, void* stream) {
   return state_summary(true, q, k, v, g, beta, cu_seqlens, num_seqs, B, T, H, K, V, flags, transition, state_ext,
                        workspace, workspace_bytes, stream);
+}
+
+int gdn_state_summary_gated(int32_t kda, const void* q, const void* k, const void* v, const float* g_raw,
+                            const float* A_log, const float* dt_bias, const void* beta, const int32_t* cu_seqlens,
+                            int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                            uint32_t flags, float* transition, float* state_ext, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return state_summary(kda != 0, q, k, v, g_raw, beta, cu_seqlens, num_seqs, B, T, H, K, V, flags, transition,
+                       state_ext, workspace, workspace_bytes, stream, true, A_log, dt_bias);
 }
 
 size_t gdn_state_summary_workspace_bytes(int32_t kda, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,

@@ -298,6 +298,14 @@ int kda_state_summary(const void* q, const void* k, const void* v, const float* 
                       const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
                       int32_t V, uint32_t flags, float* transition, float* state_ext, void* workspace,
                       size_t workspace_bytes, void* stream);
+/* The summary with the gate formed in the kernel: kda selects the gate kind
+ * (0: GDN, 1: KDA); g_raw, A_log and dt_bias as gdn_chunk_fwd_gated /
+ * kda_chunk_fwd_gated take them; everything else as the summaries above. */
+int gdn_state_summary_gated(int32_t kda, const void* q, const void* k, const void* v, const float* g_raw,
+                            const float* A_log, const float* dt_bias, const void* beta, const int32_t* cu_seqlens,
+                            int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                            uint32_t flags, float* transition, float* state_ext, void* workspace,
+                            size_t workspace_bytes, void* stream);
 size_t gdn_state_summary_workspace_bytes(int32_t kda, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
                                          int32_t num_seqs, const int32_t* cu_seqlens);
 int gdn_state_summary_apply(const float* transition, const float* state_ext, const float* state_in,

@@ -30,7 +30,7 @@ def test_header_declares_expected_entry_points():
                  "gdn_state_summary", "kda_state_summary", "gdn_state_summary_workspace_bytes",
                  "gdn_state_summary_apply", "gdn_short_conv", "gdn_short_conv_workspace_bytes",
                  "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_chunk_fwd_gated", "kda_chunk_fwd_gated",
-                 "gdn_chunk_bwd_gated"):
+                 "gdn_chunk_bwd_gated", "gdn_state_summary_gated"):
         assert must in names
 
 
@@ -117,6 +117,15 @@ def test_gated_bwd_validates_before_device(gdn, missing):
                                      ptr["ddt_bias"], FAKE, None, None, 0, None)
     assert rc == gdn.GDN_ERR_INVALID_ARGUMENT
     assert "dA_log" in gdn.last_error()
+
+
+def test_gated_summary_validates_before_device(gdn):
+    rc = gdn.lib.gdn_state_summary_gated(0, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 1, 1, 64, 2, 128, 128, 0,
+                                         FAKE, FAKE, None, 0, None)
+    assert rc == gdn.GDN_ERR_INVALID_ARGUMENT and "A_log" in gdn.last_error()
+    rc = gdn.lib.gdn_state_summary_gated(1, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x100004), FAKE, None, 1, 1,
+                                         64, 2, 128, 128, 0, FAKE, FAKE, None, 0, None)
+    assert rc == gdn.GDN_ERR_INVALID_ARGUMENT and "16-byte aligned" in gdn.last_error()
 
 
 def test_num_chunks(gdn):

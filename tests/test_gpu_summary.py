@@ -121,3 +121,28 @@ def test_summary_composes_two_segments(gdn, kda):
     e = s_err(out.cpu().numpy(), s_ref)
     _say("  two-segment composition rel err %.3e" % e)
     assert e <= S_RTOL
+
+
+@pytest.mark.parametrize("name", ["gdn", "varlen", "kda"])
+def test_state_summary_gated(gdn, name):
+    """gdn_state_summary_gated: the gate formed in the kernel from the raw
+    values, against the oracle's summary on the oracle's gate."""
+    import dataclasses
+    from oracle import gate as ogate
+    inp = {"gdn": lambda: gi.make_inputs("gdn", B=2, T=200, H=2),
+           "varlen": lambda: gi.make_inputs("varlen", H=2, doc_lengths=[1, 64, 130]),
+           "kda": lambda: gi.make_inputs("kda", B=1, T=150, H=2)}[name]()
+    fn = ogate.kda_gate if inp.kda else ogate.gdn_gate
+    ref_inp = dataclasses.replace(inp, g=fn(inp.gate_raw, inp.A_log, inp.dt_bias).astype(np.float32))
+    M_ref, S_ref = oracle.state_summary(ref_inp)
+    d = to_device(inp)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    M, S = gdn.state_summary(d["k"], d["v"], t(inp.gate_raw), d["beta"], q=d["q"], cu_seqlens=inp.cu_seqlens,
+                             kda=inp.kda, l2norm_qk=bool(inp.flags & 1), beta_sigmoid=bool(inp.flags & 2),
+                             A_log=t(inp.A_log), dt_bias=t(inp.dt_bias))
+    torch.cuda.synchronize()
+    M, S = M.cpu().numpy(), S.cpu().numpy()
+    em = float(np.abs(M - M_ref).max() / max(np.abs(M_ref).max(), 0.1))
+    es = s_err(S, S_ref)
+    _say("  gated summary %s: transition err %.3e   state rel err %.3e" % (name, em, es))
+    assert em <= S_RTOL and es <= S_RTOL
