@@ -28,7 +28,7 @@
  * Contract shared by every entry point
  * ------------------------------------
  *   Sizes: K == V == 128, chunk size 64 (GDN_ERR_UNSUPPORTED otherwise).
- *   B >= 1, T >= 1, H >= 1, scale finite and > 0.
+ *   B >= 1, T >= 1, 1 <= H <= 65535, B*T < 2^30, scale finite and > 0.
  *   q, k   bf16 [B,T,H,K], v bf16 [B,T,H,V], beta bf16 [B,T,H], o bf16
  *          [B,T,H,V]: contiguous, token-major; device pointers.
  *   g      fp32 device pointer, [B,T,H] (GDN) or [B,T,H,K] (KDA).

@@ -58,6 +58,7 @@ def _call_fwd(gdn, B=1, T=64, H=2, K=128, V=128, cu=None, num_seqs=None, scale=0
     (dict(B=0), 1, "B, T and H"),
     (dict(T=0), 1, "B, T and H"),
     (dict(H=0), 1, "B, T and H"),
+    (dict(H=70000), 1, "at most 65535 heads"),
     (dict(K=64), 2, "K = V = 128"),
     (dict(V=256), 2, "K = V = 128"),
     (dict(scale=0.0), 1, "scale"),
