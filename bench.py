@@ -15,7 +15,9 @@ the headline pass, whose calls they would lengthen). Two more passes are
 reported beside the headline: the K calls with the 1 GiB buffer written
 instead of read before each (the caches then hold dirty lines of other data,
 whose write-back the call pays for), and the K calls back to back with no
-scrub ("warm").
+scrub ("warm"). The host side of a call (argument checks, the packed
+input's chunk table build and upload, the launches) is timed on its own with
+the GPU drained before each call ("host_call_us").
 
     python bench.py [--steps K] [--warmup W] [--workload gdn|varlen|long|kda|tiny]
                     [--no-cpu-baseline]
@@ -418,6 +420,16 @@ def main():
     warm_ms_per_step = ev0.elapsed_time(ev1) / args.steps
     wall_ms_per_step = (t1 - t0) * 1e3 / args.steps
 
+    # host side of one call (argument checks, for packed input the chunk
+    # table build and its upload, the launches), the GPU drained before each
+    host_us = []
+    for _ in range(args.steps):
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        step()
+        host_us.append((time.perf_counter() - h0) * 1e6)
+    torch.cuda.synchronize()
+
     ms_per_step = float(np.median(per_call))
     tokens = B * T
     value = tokens / (ms_per_step * 1e-3)
@@ -515,7 +527,8 @@ def main():
                    "p90_ms": round(float(np.percentile(per_call, 90)), 5),
                    "written_scrub_ms": round(float(np.median(per_call_dirty)), 5),
                    "warm_ms_per_step": round(warm_ms_per_step, 5),
-                   "warm_tokens_per_s": round(tokens / (warm_ms_per_step * 1e-3), 1)},
+                   "warm_tokens_per_s": round(tokens / (warm_ms_per_step * 1e-3), 1),
+                   "host_call_us": round(float(np.median(host_us)), 1)},
         "wall_ms_per_step": round(wall_ms_per_step, 5),
     }
     print(json.dumps(line), flush=True)
