@@ -431,8 +431,10 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_sprod_kernel(BwdArgs a) {
   const int l = lane & 15, g = lane >> 4;
   const int rt = w & 3, ch = w >> 2;
   const int NT = a.geo.NT;
-  const size_t cm = blockIdx.x;
-  const int h = (int)(cm / NT), c = (int)(cm % NT);
+  // heads fastest in dispatch order: neighbouring workgroups read the
+  // neighbouring head rows of the same tokens
+  const int c = (int)(blockIdx.x / a.H), h = (int)(blockIdx.x % a.H);
+  const size_t cm = (size_t)h * NT + c;
   const ChunkInfo ci = a.geo.chunk(c);
   const int H = a.H;
   const size_t plane = (size_t)a.H * NT * kChunk * kDim;
@@ -621,8 +623,10 @@ __global__ __launch_bounds__(512, 1) void gdn_bwd_intra_kernel(BwdArgs a) {
   const int l = lane & 15, g = lane >> 4;
   const int rt = w & 3, hf = w >> 2;  // row tile, column half
   const int NT = a.geo.NT;
-  const size_t cm = blockIdx.x;
-  const int h = (int)(cm / NT), c = (int)(cm % NT);
+  // heads fastest in dispatch order: neighbouring workgroups read the
+  // neighbouring head rows of the same tokens
+  const int c = (int)(blockIdx.x / a.H), h = (int)(blockIdx.x % a.H);
+  const size_t cm = (size_t)h * NT + c;
   const ChunkInfo ci = a.geo.chunk(c);
   const int L = ci.len;
   const int H = a.H;
