@@ -150,3 +150,52 @@ def test_gate_chain_rule_matches_finite_differences(kda):
         fd = (lp - lm) / (2 * eps)
         an = float((grad * d).sum())
         assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (key, fd, an)
+
+
+def _host_normalised(rng, T, H, kda):
+    """No in-kernel flags: q, k of unit norm and beta in (0, 1) given directly."""
+    base = gi.random_problem(rng, 1, T, H, 128, 128, kda=kda, gate_scale=0.3, with_initial_state=True,
+                             flags=gi.FLAG_OUTPUT_FINAL_STATE)
+    out = {}
+    for name in ("q", "k"):
+        x = decode_bf16(getattr(base, name))
+        out[name] = gi.f32_to_bf16_bits((x / np.linalg.norm(x, axis=-1, keepdims=True)).astype(np.float32))
+    b = 1.0 / (1.0 + np.exp(-decode_bf16(base.beta)))
+    out["beta"] = gi.f32_to_bf16_bits(b.astype(np.float32))
+    return gi.GdnInputs(**{**base.__dict__, **out})
+
+
+def _chunk_form_cases():
+    rng = np.random.default_rng(131)
+    return {
+        "gdn_dense": PROBLEMS["gdn_dense"],
+        "gdn_packed": PROBLEMS["gdn_packed"],
+        "kda_dense": PROBLEMS["kda_dense"],
+        "kda_packed": gi.random_problem(rng, 1, 90, 2, 128, 128, kda=True, gate_scale=0.3, with_initial_state=True,
+                                        cu_seqlens=np.array([0, 1, 66, 90])),
+        "kda_host_normalised": _host_normalised(rng, 70, 2, True),
+        "kda_reset": (lambda p: gi.GdnInputs(**{**p.__dict__, "g": np.where(
+            np.arange(p.T)[None, :, None, None] == 37, -1000.0, p.g).astype(np.float32)}))(
+            gi.random_problem(rng, 1, 80, 1, 128, 128, kda=True, gate_scale=0.3, with_initial_state=True)),
+    }
+
+
+CHUNK_FORM = _chunk_form_cases()
+
+
+@pytest.mark.parametrize("chunk", [4, 16, 64])
+@pytest.mark.parametrize("name", list(CHUNK_FORM))
+def test_chunk_form_gradients_equal_autograd(name, chunk):
+    """oracle.grad_chunk (the chunked reverse pass, step by step) equals the
+    reverse-mode derivative of the token recurrence: every input gradient, the
+    gradient of the state entering every chunk, and the forward it runs."""
+    from oracle import grad_chunk as gc
+    inp = CHUNK_FORM[name]
+    do, ds = _cot(inp, 132)
+    ref = og.grads(inp, do, ds, chunk_size=chunk)
+    got = gc.grads_chunk(inp, do, ds, chunk_size=chunk)
+    for key in ("dq", "dk", "dv", "dbeta", "dg", "ds0", "o", "s_final"):
+        err = np.abs(got[key] - ref[key]).max() / max(np.abs(ref[key]).max(), 1e-30)
+        assert err <= 1e-9, (key, err)
+    for a, b in zip(got["dh"], ref["dh"]):
+        assert np.abs(a - b).max() <= 1e-9 * max(np.abs(b).max(), 1e-30)
