@@ -57,7 +57,8 @@ ALG_FLOPS_PER_TH = 140629             # conservative (triangle-exploiting) count
 
 
 KERNEL_SOURCES = ("gdn_common.h", "gdn_kernels.h", "gdn_prepare.hip", "gdn_fwd.hip", "gdn_state.hip",
-                  "gdn_state_common.h", "kda_fwd.hip", "kda_state.hip", "gdn_bwd.h", "gdn_bwd.hip", "short_conv.hip")
+                  "gdn_state_common.h", "kda_fwd.hip", "kda_state.hip", "gdn_bwd.h", "gdn_bwd.hip", "short_conv.hip",
+                  "kda_bwd.hip")
 
 
 def kernel_source_hash() -> str:
@@ -181,7 +182,7 @@ def bench_bwd(args, gdn, gi, inp, q, k, v, g, beta, dev):
     0.1 N(0,1) (dS_final)."""
     import torch
     if inp.kda:
-        raise SystemExit("the backward pass is built for the GDN (scalar) gate only")
+        return bench_kda_bwd(args, gdn, gi, inp, q, k, g, beta, dev)
     B, T, H, K, V = inp.B, inp.T, inp.H, inp.K, inp.V
     N = inp.num_seqs
     gen = torch.Generator(device=dev).manual_seed(7)
@@ -258,6 +259,93 @@ def bench_bwd(args, gdn, gi, inp, q, k, v, g, beta, dev):
         "timing": {"per_call": "median of %d calls, %d MiB read before each" % (args.steps, args.scrub_mib),
                    "p10_ms": round(float(np.percentile(ts, 10)), 5),
                    "p90_ms": round(float(np.percentile(ts, 90)), 5)},
+    }
+    print(json.dumps(line), flush=True)
+
+
+# Reverse state pass of the KDA backward, flops per (chunk, head): dV' = KG dS
+# (64x128x128) + Aqk^T dO (lower triangle, 2080 x 128), Y = T^T dV' (2080 x
+# 128), dS update QD^T dO + KDB^T Y (2 x 128x64x128) and the decay.
+KDA_DH_FLOPS = 2 * (64 * 128 * 128 + 2080 * 128 + 2080 * 128 + 2 * 128 * 64 * 128) + 128 * 128
+VALU_FP32_PEAK_TFLOPS = 157.3
+
+
+def bench_kda_bwd(args, gdn, gi, inp, q, k, g, beta, dev):
+    """Times kda_bwd_state_pass (the KDA prepare, then the reverse state pass),
+    each call after a 1 GiB read, and the prepare alone (stage entry); the
+    reverse pass is the difference. Prints one JSON line."""
+    import torch
+    B, T, H, K, V = inp.B, inp.T, inp.H, inp.K, inp.V
+    N = inp.num_seqs
+    gen = torch.Generator(device=dev).manual_seed(7)
+    do = torch.randn((B, T, H, V), device=dev, generator=gen).to(torch.bfloat16)
+    dsf = torch.randn((N, H, K, V), device=dev, generator=gen) * 0.1
+    cu = None if inp.cu_seqlens is None else np.ascontiguousarray(inp.cu_seqlens, dtype=np.int32)
+    cu_p = None if cu is None else cu.ctypes.data_as(ctypes.c_void_p)
+    flags = inp.flags & 3
+    need = gdn.lib.kda_bwd_state_pass_workspace_bytes(B, T, H, K, V, N, cu_p, flags)
+    ws = torch.empty(int(need), dtype=torch.uint8, device=dev)
+    NT = gdn.num_chunks(B, T, inp.cu_seqlens)
+    dh = torch.empty((H, NT, K, V), dtype=torch.float32, device=dev)
+    dvn = torch.empty((H, NT, 64, V), dtype=torch.float32, device=dev)
+    ds0 = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    tm = torch.empty((H, NT, 64, 128), dtype=torch.bfloat16, device=dev)
+    aq = torch.empty((H, NT, 64, 64), dtype=torch.bfloat16, device=dev)
+    vec = torch.empty((H, NT, 8, 64), dtype=torch.float32, device=dev)
+    gk = torch.empty((H, NT, 64, 128), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def whole():
+        rc = gdn.lib.kda_bwd_state_pass(P(q), P(k), P(g), P(beta), cu_p, N, B, T, H, K, V, float(inp.scale), flags,
+                                        P(do), P(dsf), P(dh), P(dvn), P(ds0), P(ws), int(need), sp)
+        if rc != 0:
+            raise RuntimeError(gdn.last_error())
+
+    def prepare():
+        rc = gdn.lib.gdn_stage_prepare(1, P(q), P(k), P(g), P(beta), cu_p, N, B, T, H, K, V, float(inp.scale), flags,
+                                       P(tm), P(aq), P(vec), P(gk), sp)
+        if rc != 0:
+            raise RuntimeError(gdn.last_error())
+
+    scrub = torch.full((max(args.scrub_mib, 1) * (1 << 20) // 4,), 1.0, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(args.steps):
+            if args.scrub_mib:
+                scrub.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    ms = timed(whole)
+    prep_ms = timed(prepare)
+    dh_ms = ms - prep_ms
+    flops = NT * H * KDA_DH_FLOPS
+    achieved = flops / (dh_ms * 1e-3) / 1e12
+    tokens = B * T
+    line = {
+        "metric": "KDA backward reverse state pass tokens/s", "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": "KDA backward reverse state pass (prepare + reverse pass) B=%d T=%d H=%d, %d sequences"
+                               % (B, T, H, N), "global_batch": B, "seq_len": T, "heads": H, "head_dim": K,
+                   "parallelism": "single-gpu"},
+        "roofline": {"kernel": "kda_bwd_dh", "bound": "alu", "achieved": round(achieved, 2),
+                     "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4), "traffic": None},
+        "kernels_us": {"prepare": round(prep_ms * 1e3, 2), "reverse_state_pass": round(dh_ms * 1e3, 2)},
+        "timing": {"per_call": "median of %d calls, %d MiB read before each; reverse pass = whole - prepare alone"
+                               % (args.steps, args.scrub_mib)},
     }
     print(json.dumps(line), flush=True)
 

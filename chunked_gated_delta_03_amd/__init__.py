@@ -38,7 +38,7 @@ EXPORTED = (
     "gdn_state_summary_workspace_bytes", "gdn_state_summary_apply", "gdn_short_conv",
     "gdn_short_conv_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes",
     "gdn_bwd_timing_read", "gdn_chunk_fwd_gated", "kda_chunk_fwd_gated", "gdn_chunk_bwd_gated",
-    "gdn_state_summary_gated",
+    "gdn_state_summary_gated", "kda_bwd_state_pass", "kda_bwd_state_pass_workspace_bytes",
 )
 
 
@@ -102,6 +102,11 @@ def _load() -> ctypes.CDLL:
     lib.gdn_chunk_bwd_gated.restype = ctypes.c_int
     lib.gdn_chunk_bwd_gated.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p,
                                         p, p, p, p, p, p, p, p, p, sz, p]
+    lib.kda_bwd_state_pass_workspace_bytes.restype = sz
+    lib.kda_bwd_state_pass_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, p, u32]
+    lib.kda_bwd_state_pass.restype = ctypes.c_int
+    lib.kda_bwd_state_pass.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p, p, p, p, p, sz,
+                                       p]
     lib.gdn_stage_prepare.restype = ctypes.c_int
     lib.gdn_stage_prepare.argtypes = [i32, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p, p, p, p]
     lib.gdn_stage_fwd_h.restype = ctypes.c_int
@@ -327,6 +332,44 @@ def gdn_chunk_bwd(q, k, v, g, beta, do, scale: Optional[float] = None, initial_s
                              _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(ds0), _ptr(workspace), ws_bytes,
                              _stream_ptr(q.device, stream)))
     return dq, dk, dv, dg, dbeta, ds0
+
+
+def kda_bwd_state_pass(q, k, g, beta, do, scale: Optional[float] = None, d_final_state=None, cu_seqlens=None,
+                       l2norm_qk: bool = False, beta_sigmoid: bool = False, workspace: Optional[torch.Tensor] = None,
+                       stream=None):
+    """KDA backward, reverse state pass: for the forward of :func:`kda_chunk_fwd`
+    with these q, k, g, beta and the loss <do, o> + <d_final_state, final_state>,
+    returns fp32 (dh_next [H,NT,128,128]: the gradient w.r.t. the state leaving
+    each chunk, dv_new [H,NT,64,128]: w.r.t. each chunk's v_new,
+    d_initial_state [N,H,128,128])."""
+    cu = _cu_array(cu_seqlens)
+    B, T, H, K, V, N = _check_inputs(q, k, k, g, beta, True, None, cu)
+    if (not isinstance(do, torch.Tensor) or do.dtype != torch.bfloat16 or not do.is_contiguous()
+            or tuple(do.shape) != (B, T, H, V) or do.device != q.device):
+        raise ValueError("do must be a contiguous bf16 [B,T,H,V] tensor on %s" % q.device)
+    if d_final_state is not None and (d_final_state.dtype != torch.float32 or not d_final_state.is_contiguous()
+                                      or tuple(d_final_state.shape) != (N, H, K, V)
+                                      or d_final_state.device != q.device):
+        raise ValueError("d_final_state must be a contiguous fp32 [N,H,K,V] tensor on %s" % q.device)
+    scale = K ** -0.5 if scale is None else float(scale)
+    flags = _flags(l2norm_qk, beta_sigmoid, False)
+    NT = num_chunks(B, T, cu_seqlens)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dh = torch.empty((H, NT, K, V), **f32)
+    dvn = torch.empty((H, NT, CHUNK, V), **f32)
+    ds0 = torch.empty((N, H, K, V), **f32)
+    need = lib.kda_bwd_state_pass_workspace_bytes(B, T, H, K, V, N, _cu_ptr(cu), flags)
+    if need == 0:
+        workspace = None
+    elif workspace is None:
+        workspace = torch.empty(int(need), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel() * workspace.element_size(), need))
+    _check(lib.kda_bwd_state_pass(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), _cu_ptr(cu), N, B, T, H, K, V, scale, flags,
+                                  _ptr(do), _ptr(d_final_state), _ptr(dh), _ptr(dvn), _ptr(ds0), _ptr(workspace),
+                                  0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                  _stream_ptr(q.device, stream)))
+    return dh, dvn, ds0
 
 
 def state_summary(k, v, g, beta, q=None, cu_seqlens=None, kda: bool = False, l2norm_qk: bool = False,

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdn.so")
 SOURCES = ["gdn_api.cpp", "gdn_prepare.hip", "gdn_fwd.hip", "gdn_state.hip", "kda_fwd.hip", "kda_state.hip",
-           "short_conv.hip", "gdn_bwd.hip"]
+           "short_conv.hip", "gdn_bwd.hip", "kda_bwd.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

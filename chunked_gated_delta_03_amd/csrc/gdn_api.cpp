@@ -992,6 +992,85 @@ int gdn_stage_prepare(int32_t kda, const void* q, const void* k, const float* g,
   return GDN_OK;
 }
 
+size_t kda_bwd_state_pass_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                          const int32_t* cu_seqlens, uint32_t flags) {
+  g_last_error.clear();
+  Problem p;
+  p.kda = true;
+  if (check_shape(B, T, H, K, V, num_seqs, cu_seqlens, p)) return 0;
+  if (flags & ~kKnownFlags) {
+    fail(GDN_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags & ~kKnownFlags);
+    return 0;
+  }
+  return layout_for(p, true, true).total;
+}
+
+int kda_bwd_state_pass(const void* q, const void* k, const float* g, const void* beta, const int32_t* cu_seqlens,
+                       int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, float scale,
+                       uint32_t flags, const void* d_o, const float* d_final_state, float* dh_next, float* dv_new,
+                       float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  g_last_error.clear();
+  Problem p;
+  p.kda = true;
+  int rc = check_shape(B, T, H, K, V, num_seqs, cu_seqlens, p);
+  if (rc) return rc;
+  rc = check_common(q, k, k, g, beta, scale, flags);
+  if (rc) return rc;
+  if (!d_o || !dh_next || !dv_new)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "d_o, dh_next and dv_new must be non-NULL");
+  if (!aligned16(dv_new)) return fail(GDN_ERR_INVALID_ARGUMENT, "dv_new must be 16-byte aligned");
+  int cus = 0;
+  rc = check_device(&cus);
+  if (rc) return rc;
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const Layout L = layout_for(p, true, true);
+  Workspace W;
+  rc = acquire_workspace(workspace, workspace_bytes, L.total, stream, W);
+  if (rc) return rc;
+  if (p.packed) {
+    rc = upload_tables(p, W.base + L.tab, stream);
+    if (rc) return rc;
+  }
+  const gdn::Geometry geo = make_geometry(p, W.base + L.tab);
+
+  gdn::PrepareArgs pa{};
+  pa.q = static_cast<const uint16_t*>(q);
+  pa.k = static_cast<const uint16_t*>(k);
+  pa.g = g;
+  pa.beta = static_cast<const uint16_t*>(beta);
+  pa.tmat = reinterpret_cast<uint16_t*>(W.base + L.tmat);
+  pa.aqk = reinterpret_cast<uint16_t*>(W.base + L.aqk);
+  pa.vec = reinterpret_cast<float*>(W.base + L.vec);
+  pa.gk = reinterpret_cast<float*>(W.base + L.kdec);
+  pa.kdec = nullptr;
+  pa.geo = geo;
+  pa.H = H;
+  pa.scale = scale;
+  pa.flags = flags & ~(uint32_t)GDN_OUTPUT_FINAL_STATE;
+  pa.cus = cus;
+  hipError_t e = gdn::launch_prepare(true, pa, stream);
+  if (e != hipSuccess) return hip_fail(e, "prepare launch");
+
+  gdn::KdaBwdArgs ka{};
+  ka.q = pa.q;
+  ka.k = pa.k;
+  ka.dout = static_cast<const uint16_t*>(d_o);
+  ka.gk = pa.gk;
+  ka.vec = pa.vec;
+  ka.tmat = pa.tmat;
+  ka.aqk = pa.aqk;
+  ka.dsfinal = d_final_state;
+  ka.dhn = dh_next;
+  ka.dvn = dv_new;
+  ka.ds0 = d_initial_state;
+  ka.geo = geo;
+  ka.H = H;
+  e = gdn::launch_kda_bwd_dh(ka, stream);
+  if (e != hipSuccess) return hip_fail(e, "reverse state pass launch");
+  return GDN_OK;
+}
+
 int gdn_stage_fwd_h(int32_t kda, const void* k, const void* v, const void* tmat, const float* vec, const float* gk,
                     const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
                     int32_t H, int32_t K, int32_t V, uint32_t flags, float* h, float* v_new, float* final_state,

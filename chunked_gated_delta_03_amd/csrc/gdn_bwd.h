@@ -36,6 +36,24 @@ struct BwdArgs {
 // stage 0: reverse state pass, 1: state products, 2: per-chunk gradients
 hipError_t launch_gdn_bwd(const BwdArgs& a, int stage, hipStream_t stream);
 
+// Reverse state pass of the KDA backward (kda_bwd.hip).
+struct KdaBwdArgs {
+  const uint16_t* q;         // [B*T,H,K] bf16
+  const uint16_t* k;
+  const uint16_t* dout;      // [B*T,H,V] bf16
+  const float* gk;           // [H,NT,64,K] cumulative log2 gate (prepare, stage mode)
+  const float* vec;          // [H,NT,8,64] prepare row vectors
+  const uint16_t* tmat;      // [H,NT,64,128] T, bf16 hi | lo, permuted columns
+  const uint16_t* aqk;       // [H,NT,64,64] bf16, permuted columns
+  const float* dsfinal;      // [N,H,K,V] or nullptr (zero)
+  float* dhn;                // [H,NT,K,V] gradient w.r.t. the state leaving each chunk
+  float* dvn;                // [H,NT,64,V] gradient w.r.t. v_new
+  float* ds0;                // [N,H,K,V] or nullptr
+  Geometry geo;
+  int H;
+};
+hipError_t launch_kda_bwd_dh(const KdaBwdArgs& a, hipStream_t stream);
+
 // Backward of the in-kernel gate g = -exp(A_log[h]) softplus(x + dt_bias[h])
 // (GDN, natural log): dg (w.r.t. g) becomes dx = -exp(A_log) sigmoid(x +
 // dt_bias) dg in place, and per head dA_log = sum dg g, ddt_bias = sum dx,

@@ -312,6 +312,34 @@ int gdn_state_summary_apply(const float* transition, const float* state_ext, con
                             float* state_out, int32_t N, int32_t H, int32_t K, int32_t V, void* stream);
 
 /*
+ * KDA backward, reverse state pass (the stage of the backward that carries the
+ * state gradient across chunks; bwd_state_saved of the backward on the
+ * 2026-09-10 "Diff Coverage" page, with the per-channel decays of the KDA
+ * stages). For the forward of kda_chunk_fwd with the same q, k, g, beta,
+ * scale, flags and cu_seqlens, and the loss <d_o, o> + <d_final_state,
+ * final_state>, it writes per chunk, from the last to the first:
+ *   dh_next [H,NT,K,V] fp32  the gradient w.r.t. the state leaving the chunk;
+ *   dv_new  [H,NT,64,V] fp32 the gradient w.r.t. the chunk's
+ *                            v_new = U - W S (rows past a document's end 0;
+ *                            16-byte aligned);
+ *   d_initial_state [N,H,K,V] fp32 or NULL  the gradient w.r.t. the initial
+ *                            state.
+ * NT = gdn_num_chunks(...), chunks numbered as the forward's chunk table
+ * (head-major: element [h, c]). The gradient is linear in d_o and
+ * d_final_state and does not depend on v or the initial state, which are not
+ * arguments. d_o bf16 [B,T,H,V] (required); d_final_state fp32 [N,H,K,V] or
+ * NULL (zero). Workspace sized by kda_bwd_state_pass_workspace_bytes; other
+ * arguments, errors and stream behaviour as kda_chunk_fwd. The remaining KDA
+ * backward stages (the per-chunk input gradients) are not provided.
+ */
+size_t kda_bwd_state_pass_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                          const int32_t* cu_seqlens, uint32_t flags);
+int kda_bwd_state_pass(const void* q, const void* k, const float* g, const void* beta, const int32_t* cu_seqlens,
+                       int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, float scale,
+                       uint32_t flags, const void* d_o, const float* d_final_state, float* dh_next, float* dv_new,
+                       float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Causal depthwise Conv1d + SiLU (the ShortConv forming q, k, v from the
  * projections; _causal_conv1d_with_cp_halo on the 2026-09-10 "Diff Coverage"
  * page): per channel c and token t,

@@ -104,7 +104,9 @@ def grads_chunk(inp, do: np.ndarray, ds_final: Optional[np.ndarray], chunk_size:
                 flags: Optional[int] = None) -> dict:
     """Gradients of L = <dO, o> + <dS_T, S_T> for a :class:`gdn_inputs.GdnInputs`
     problem by the chunk-form reverse pass; same outputs as ``oracle.grad.grads``
-    (dq, dk, dv, dbeta, dg, ds0, dh, o, s_final), fp64."""
+    (dq, dk, dv, dbeta, dg, ds0, dh, o, s_final), fp64, and per sequence the
+    gradient w.r.t. each chunk's v_new, dvn [NC,H,C,V] (rows past a partial
+    chunk's end zero)."""
     flags = inp.flags if flags is None else flags
     C = chunk_size
     q_all, k_all, v_all = decode_bf16(inp.q), decode_bf16(inp.k), decode_bf16(inp.v)
@@ -115,7 +117,7 @@ def grads_chunk(inp, do: np.ndarray, ds_final: Optional[np.ndarray], chunk_size:
     o_all = np.zeros((inp.B, inp.T, H, V))
     ds0 = np.zeros((N, H, K, V))
     s_fin = np.zeros((N, H, K, V))
-    dh = []
+    dh, dvn_all = [], []
     if inp.cu_seqlens is None:
         spans = [(n, n, 0, inp.T) for n in range(inp.B)]
     else:
@@ -123,6 +125,7 @@ def grads_chunk(inp, do: np.ndarray, ds_final: Optional[np.ndarray], chunk_size:
         spans = [(n, 0, cu[n], cu[n + 1]) for n in range(N)]
     for n, row, a, e in spans:
         dh_n = np.zeros(((e - a + C - 1) // C, H, K, V))
+        dvn_n = np.zeros(((e - a + C - 1) // C, H, C, V))
         for h in range(H):
             q, k, v = q_all[row, a:e, h], k_all[row, a:e, h], v_all[row, a:e, h]
             if flags & 1:
@@ -154,6 +157,7 @@ def grads_chunk(inp, do: np.ndarray, ds_final: Optional[np.ndarray], chunk_size:
                                inp.scale)
                 dS = r["dS"]
                 dh_n[ci, h] = dS
+                dvn_n[ci, h, :sl.stop - sl.start] = r["dvn"]
                 dqn[sl], dkn[sl], dv[sl], db[sl] = r["dqn"], r["dkn"], r["dv"], r["db"]
                 # G is the cumulative sum of the chunk's gates: reverse cumulative sum
                 dgn[sl] = np.cumsum(r["dG"][::-1], axis=0)[::-1]
@@ -167,4 +171,5 @@ def grads_chunk(inp, do: np.ndarray, ds_final: Optional[np.ndarray], chunk_size:
             out["dbeta"][row, a:e, h] = db * b * (1.0 - b) if flags & 2 else db
             out["dg"][row, a:e, h] = dgn * np.log(2.0) if inp.kda else dgn.sum(1)
         dh.append(dh_n)
-    return dict(**out, ds0=ds0, dh=dh, o=o_all, s_final=s_fin)
+        dvn_all.append(dvn_n)
+    return dict(**out, ds0=ds0, dh=dh, dvn=dvn_all, o=o_all, s_final=s_fin)

@@ -30,7 +30,7 @@ def test_header_declares_expected_entry_points():
                  "gdn_state_summary", "kda_state_summary", "gdn_state_summary_workspace_bytes",
                  "gdn_state_summary_apply", "gdn_short_conv", "gdn_short_conv_workspace_bytes",
                  "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_chunk_fwd_gated", "kda_chunk_fwd_gated",
-                 "gdn_chunk_bwd_gated", "gdn_state_summary_gated"):
+                 "gdn_chunk_bwd_gated", "gdn_state_summary_gated", "kda_bwd_state_pass"):
         assert must in names
 
 
@@ -127,6 +127,17 @@ def test_gated_summary_validates_before_device(gdn):
     rc = gdn.lib.gdn_state_summary_gated(1, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x100004), FAKE, None, 1, 1,
                                          64, 2, 128, 128, 0, FAKE, FAKE, None, 0, None)
     assert rc == gdn.GDN_ERR_INVALID_ARGUMENT and "16-byte aligned" in gdn.last_error()
+
+
+def test_kda_bwd_state_pass_validates_before_device(gdn):
+    call = lambda **kw: gdn.lib.kda_bwd_state_pass(
+        FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 2, kw.get("K", 128), 128, 0.1, 0, kw.get("do", FAKE), None,
+        FAKE, kw.get("dvn", FAKE), None, None, 0, None)
+    assert call(do=None) == gdn.GDN_ERR_INVALID_ARGUMENT and "non-NULL" in gdn.last_error()
+    assert call(dvn=ctypes.c_void_p(0x100004)) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert "16-byte aligned" in gdn.last_error()
+    assert call(K=64) == gdn.GDN_ERR_UNSUPPORTED
+    assert gdn.lib.kda_bwd_state_pass_workspace_bytes(1, 64, 2, 128, 128, 1, None, 0) > 0
 
 
 def test_num_chunks(gdn):
