@@ -39,6 +39,7 @@ EXPORTED = (
     "gdn_short_conv_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes",
     "gdn_bwd_timing_read", "gdn_chunk_fwd_gated", "kda_chunk_fwd_gated", "gdn_chunk_bwd_gated",
     "gdn_state_summary_gated", "kda_bwd_state_pass", "kda_bwd_state_pass_workspace_bytes",
+    "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
 )
 
 
@@ -102,6 +103,11 @@ def _load() -> ctypes.CDLL:
     lib.gdn_chunk_bwd_gated.restype = ctypes.c_int
     lib.gdn_chunk_bwd_gated.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p,
                                         p, p, p, p, p, p, p, p, p, sz, p]
+    lib.kda_chunk_bwd_workspace_bytes.restype = sz
+    lib.kda_chunk_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, p, u32]
+    lib.kda_chunk_bwd.restype = ctypes.c_int
+    lib.kda_chunk_bwd.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p,
+                                  p, p, p, p, p, p, p, sz, p]
     lib.kda_bwd_state_pass_workspace_bytes.restype = sz
     lib.kda_bwd_state_pass_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, p, u32]
     lib.kda_bwd_state_pass.restype = ctypes.c_int
@@ -330,6 +336,41 @@ def gdn_chunk_bwd(q, k, v, g, beta, do, scale: Optional[float] = None, initial_s
     _check(lib.gdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _cu_ptr(cu), N,
                              B, T, H, K, V, scale, flags, _ptr(do), _ptr(d_final_state), _ptr(dq), _ptr(dk),
                              _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(ds0), _ptr(workspace), ws_bytes,
+                             _stream_ptr(q.device, stream)))
+    return dq, dk, dv, dg, dbeta, ds0
+
+
+def kda_chunk_bwd(q, k, v, g, beta, do, scale: Optional[float] = None, initial_state=None, d_final_state=None,
+                  cu_seqlens=None, l2norm_qk: bool = False, beta_sigmoid: bool = False,
+                  workspace: Optional[torch.Tensor] = None, stream=None):
+    """KDA backward: as :func:`gdn_chunk_bwd` for the forward of :func:`kda_chunk_fwd`;
+    dg is fp32 [B,T,H,128] w.r.t. the raw log2 gate."""
+    cu = _cu_array(cu_seqlens)
+    B, T, H, K, V, N = _check_inputs(q, k, v, g, beta, True, initial_state, cu)
+    if (not isinstance(do, torch.Tensor) or do.dtype != torch.bfloat16 or not do.is_contiguous()
+            or tuple(do.shape) != (B, T, H, V) or do.device != q.device):
+        raise ValueError("do must be a contiguous bf16 [B,T,H,V] tensor on %s" % q.device)
+    if d_final_state is not None and (d_final_state.dtype != torch.float32 or not d_final_state.is_contiguous()
+                                      or tuple(d_final_state.shape) != (N, H, K, V)
+                                      or d_final_state.device != q.device):
+        raise ValueError("d_final_state must be a contiguous fp32 [N,H,K,V] tensor on %s" % q.device)
+    scale = K ** -0.5 if scale is None else float(scale)
+    flags = _flags(l2norm_qk, beta_sigmoid, False)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq, dk, dv, dg = (torch.empty((B, T, H, K), **f32) for _ in range(4))
+    dbeta = torch.empty((B, T, H), **f32)
+    ds0 = torch.empty((N, H, K, V), **f32)
+    need = lib.kda_chunk_bwd_workspace_bytes(B, T, H, K, V, N, _cu_ptr(cu), flags)
+    if need == 0:
+        workspace = None
+    elif workspace is None:
+        workspace = torch.empty(int(need), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel() * workspace.element_size(), need))
+    _check(lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _cu_ptr(cu), N,
+                             B, T, H, K, V, scale, flags, _ptr(do), _ptr(d_final_state), _ptr(dq), _ptr(dk),
+                             _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(ds0), _ptr(workspace),
+                             0 if workspace is None else workspace.numel() * workspace.element_size(),
                              _stream_ptr(q.device, stream)))
     return dq, dk, dv, dg, dbeta, ds0
 

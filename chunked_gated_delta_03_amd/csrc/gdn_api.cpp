@@ -992,6 +992,162 @@ int gdn_stage_prepare(int32_t kda, const void* q, const void* k, const float* g,
   return GDN_OK;
 }
 
+// KDA backward workspace: the GDN backward's sections (the KDA decayed-operand
+// area holds the cumulative gate) plus dP, dA (64 x 64), dKD (64 x 128) and
+// the T-term part of dbeta per chunk-head.
+struct KdaBwdLayout {
+  BwdLayout b;
+  size_t dp = 0, da = 0, dkd = 0, db1 = 0, total = 0;
+};
+
+KdaBwdLayout kda_bwd_layout_for(const Problem& p) {
+  KdaBwdLayout L;
+  L.b = bwd_layout_for(p);
+  size_t off = L.b.total;
+  const size_t cmH = (size_t)p.NT * p.H;
+  L.dp = off;
+  off += align256(cmH * GDN_CHUNK * GDN_CHUNK * sizeof(float));
+  L.da = off;
+  off += align256(cmH * GDN_CHUNK * GDN_CHUNK * sizeof(float));
+  L.dkd = off;
+  off += align256(cmH * GDN_CHUNK * GDN_HEAD_DIM * sizeof(float));
+  L.db1 = off;
+  off += align256(cmH * GDN_CHUNK * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+size_t kda_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                     const int32_t* cu_seqlens, uint32_t flags) {
+  g_last_error.clear();
+  Problem p;
+  p.kda = true;
+  if (check_shape(B, T, H, K, V, num_seqs, cu_seqlens, p)) return 0;
+  if (flags & ~kKnownFlags) {
+    fail(GDN_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags & ~kKnownFlags);
+    return 0;
+  }
+  return kda_bwd_layout_for(p).total;
+}
+
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                  int32_t H, int32_t K, int32_t V, float scale, uint32_t flags, const void* d_o,
+                  const float* d_final_state, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                  float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  g_last_error.clear();
+  Problem p;
+  p.kda = true;
+  int rc = check_shape(B, T, H, K, V, num_seqs, cu_seqlens, p);
+  if (rc) return rc;
+  rc = check_common(q, k, v, g, beta, scale, flags);
+  if (rc) return rc;
+  if (!d_o || !dq || !dk || !dv || !dg || !dbeta)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "d_o, dq, dk, dv, dg and dbeta must be non-NULL");
+  if (!aligned16(d_o) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dg) || !aligned16(g))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "g, d_o, dq, dk, dv and dg must be 16-byte aligned");
+  int cus = 0;
+  rc = check_device(&cus);
+  if (rc) return rc;
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const KdaBwdLayout L = kda_bwd_layout_for(p);
+  Workspace W;
+  rc = acquire_workspace(workspace, workspace_bytes, L.total, stream, W);
+  if (rc) return rc;
+  if (p.packed) {
+    rc = upload_tables(p, W.base + L.b.fwd.tab, stream);
+    if (rc) return rc;
+  }
+  const gdn::Geometry geo = make_geometry(p, W.base + L.b.fwd.tab);
+  auto ws = [&](size_t off) { return reinterpret_cast<float*>(W.base + off); };
+
+  // forward recompute: T, Aqk, row vectors, cumulative gate; states and v_new
+  gdn::PrepareArgs pa{};
+  pa.q = static_cast<const uint16_t*>(q);
+  pa.k = static_cast<const uint16_t*>(k);
+  pa.g = g;
+  pa.beta = static_cast<const uint16_t*>(beta);
+  pa.tmat = reinterpret_cast<uint16_t*>(W.base + L.b.fwd.tmat);
+  pa.aqk = reinterpret_cast<uint16_t*>(W.base + L.b.fwd.aqk);
+  pa.vec = ws(L.b.fwd.vec);
+  pa.gk = ws(L.b.fwd.kdec);
+  pa.kdec = nullptr;
+  pa.geo = geo;
+  pa.H = H;
+  pa.scale = scale;
+  pa.flags = flags & ~(uint32_t)GDN_OUTPUT_FINAL_STATE;
+  pa.cus = cus;
+  hipError_t e = gdn::launch_prepare(true, pa, stream);
+  if (e != hipSuccess) return hip_fail(e, "prepare launch");
+  gdn::FwdArgs fa{};
+  fa.k = pa.k;
+  fa.v = static_cast<const uint16_t*>(v);
+  fa.tmat = pa.tmat;
+  fa.aqk = pa.aqk;
+  fa.vec = pa.vec;
+  fa.gk = pa.gk;
+  fa.s0 = initial_state;
+  fa.h_out = ws(L.b.h);
+  fa.vnew_out = ws(L.b.vnew);
+  fa.geo = geo;
+  fa.H = H;
+  e = gdn::launch_fwd(true, true, false, fa, stream);
+  if (e != hipSuccess) return hip_fail(e, "forward recompute launch");
+
+  // reverse state pass
+  gdn::KdaBwdArgs ka{};
+  ka.q = pa.q;
+  ka.k = pa.k;
+  ka.v = fa.v;
+  ka.dout = static_cast<const uint16_t*>(d_o);
+  ka.gk = pa.gk;
+  ka.vec = pa.vec;
+  ka.tmat = pa.tmat;
+  ka.aqk = pa.aqk;
+  ka.dsfinal = d_final_state;
+  ka.dhn = ws(L.b.dhn);
+  ka.dvn = ws(L.b.dvn);
+  ka.ds0 = d_initial_state;
+  ka.h = fa.h_out;
+  ka.vnew = fa.vnew_out;
+  ka.efd = ws(L.b.efd);
+  ka.dp = ws(L.dp);
+  ka.da = ws(L.da);
+  ka.dkd = ws(L.dkd);
+  ka.db1 = ws(L.db1);
+  ka.dq = dq;
+  ka.dk = dk;
+  ka.dv = dv;
+  ka.dg = dg;
+  ka.dbeta = dbeta;
+  ka.scale = scale;
+  ka.flags = flags;
+  ka.geo = geo;
+  ka.H = H;
+  e = gdn::launch_kda_bwd_dh(ka, stream);
+  if (e != hipSuccess) return hip_fail(e, "reverse state pass launch");
+
+  // products with the saved states (the gate does not enter them)
+  gdn::BwdArgs ba{};
+  ba.dout = ka.dout;
+  ba.h = fa.h_out;
+  ba.vnew = fa.vnew_out;
+  ba.dhn = ka.dhn;
+  ba.dvn = ka.dvn;
+  ba.efd = ws(L.b.efd);
+  ba.sdot = ws(L.b.sdot);
+  ba.geo = geo;
+  ba.H = H;
+  ba.cus = cus;
+  e = gdn::launch_gdn_bwd(ba, 1, stream);
+  if (e != hipSuccess) return hip_fail(e, "state products launch");
+
+  e = gdn::launch_kda_bwd_chunks(ka, stream);
+  if (e != hipSuccess) return hip_fail(e, "per-chunk gradients launch");
+  return GDN_OK;
+}
+
 size_t kda_bwd_state_pass_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
                                           const int32_t* cu_seqlens, uint32_t flags) {
   g_last_error.clear();

@@ -49,10 +49,28 @@ struct KdaBwdArgs {
   float* dhn;                // [H,NT,K,V] gradient w.r.t. the state leaving each chunk
   float* dvn;                // [H,NT,64,V] gradient w.r.t. v_new
   float* ds0;                // [N,H,K,V] or nullptr
+  // per-chunk gradients (whole backward only)
+  const uint16_t* v;         // [B*T,H,V] bf16
+  const float* h;            // [H,NT,K,V] state entering each chunk
+  const float* vnew;         // [H,NT,64,V] v_new
+  const float* efd;          // [3][H,NT,64,K]: dO S^T, dV' S^T, V' dS_next^T
+  float* dp;                 // [H,NT,64,64] workspace: dP
+  float* da;                 // [H,NT,64,64] workspace: dA
+  float* dkd;                // [H,NT,64,K] workspace: dKD
+  float* db1;                // [H,NT,64] workspace: the T-term part of dbeta
+  float* dq;                 // [B*T,H,K] fp32 outputs
+  float* dk;
+  float* dv;
+  float* dg;                 // [B*T,H,K] w.r.t. the raw log2 gate
+  float* dbeta;              // [B*T,H]
+  float scale;
+  uint32_t flags;
   Geometry geo;
   int H;
 };
 hipError_t launch_kda_bwd_dh(const KdaBwdArgs& a, hipStream_t stream);
+// per-chunk gradients: the mats kernel, then the gram kernel
+hipError_t launch_kda_bwd_chunks(const KdaBwdArgs& a, hipStream_t stream);
 
 // Backward of the in-kernel gate g = -exp(A_log[h]) softplus(x + dt_bias[h])
 // (GDN, natural log): dg (w.r.t. g) becomes dx = -exp(A_log) sigmoid(x +

@@ -222,6 +222,477 @@ __global__ __launch_bounds__(256) void kda_bwd_dh_kernel(KdaBwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Per-chunk gradients of the KDA backward, the chunk-form reverse pass of
+// one (chunk, head) given the state products E = dO S^T, F = dV' S^T,
+// D = V' dS_next^T (the state-products kernel), dV' and dS_next (the reverse
+// pass), the saved S and V' (the forward recompute):
+//   mats: dP = scale (dO V'^T) on i >= j, dT = dV' (b v)^T - F (b KD)^T,
+//         tU = T^T dV', tW = -T^T F, dv = b tU, db1 = rowsum(tU v + tW KD),
+//         dKD = b tW, dA = (T^T dT T^T) on i > j;
+//   gram: the terms of A and P with their per-channel decays, the chains
+//         through KD = k^ 2^G, QD = q^ 2^G, KG = k^ 2^(G_last - G) and
+//         2^G_last, the reverse cumulative sum of the gate gradient inside
+//         the chunk, the L2-norm and sigmoid derivatives.
+// k^ = k rk and q^ = q rq are the normalised rows; G the cumulative log2
+// gate. Every exponent 2^(G_i - G_j) is taken with i >= j, so it is <= 0.
+// fp32 arithmetic on the vector units; one workgroup per (chunk, head),
+// heads fastest in dispatch order.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kLdR = kDim + 4;    // fp32 row stride of 64 x 128 arrays in LDS
+constexpr int kLdB = kDim + 8;    // bf16 row stride
+
+struct alignas(16) MatsSmem {
+  union {
+    struct {
+      float dO[kChunk * kLdR];
+      float vp[kChunk * kLdR];
+    } p1;
+    struct {
+      float dv[kChunk * kLdR];
+      float f[kChunk * kLdR];    // F, then X = T^T dT
+      float kd[kChunk * kLdR];
+      uint16_t v[kChunk * kLdB];
+    } p2;
+  } u;
+  float t[kChunk * kLdM];
+  float dt[kChunk * kLdM];
+  float b[kChunk];
+};
+
+__device__ __forceinline__ void chunk_of(const Geometry& geo, int bx, int H, int& c, int& h, ChunkInfo& ci) {
+  c = bx / H;
+  h = bx - (bx / H) * H;
+  ci = geo.chunk(c);
+}
+
+// 64 x 128 fp32 rows (global, row stride 128) into LDS (row stride kLdR)
+__device__ __forceinline__ void rows_f32(float* dst, const float* src, int tid) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int idx = tid + 256 * e, r = idx >> 5, c4 = (idx & 31) * 4;
+    *reinterpret_cast<float4*>(dst + r * kLdR + c4) = *reinterpret_cast<const float4*>(src + r * kDim + c4);
+  }
+}
+
+// T = hi + lo from its stored permuted columns into LDS (row stride kLdM)
+__device__ __forceinline__ void load_t(float* dst, const uint16_t* tm, int tid) {
+  const int r = tid >> 2, qq = tid & 3;
+  const uint16_t* row = tm + r * (2 * kChunk) + 16 * qq;
+  const uint4 h0 = reinterpret_cast<const uint4*>(row)[0], h1 = reinterpret_cast<const uint4*>(row)[1];
+  const uint4 l0 = reinterpret_cast<const uint4*>(row + kChunk)[0];
+  const uint4 l1 = reinterpret_cast<const uint4*>(row + kChunk)[1];
+  const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+  const uint32_t lw[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float hv = __uint_as_float((e & 1) ? (hw[e >> 1] & 0xFFFF0000u) : (hw[e >> 1] << 16));
+    const float lv = __uint_as_float((e & 1) ? (lw[e >> 1] & 0xFFFF0000u) : (lw[e >> 1] << 16));
+    dst[r * kLdM + unperm_col(16 * qq + e)] = hv + lv;
+  }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void kda_bwd_mats_kernel(KdaBwdArgs a) {
+  __shared__ MatsSmem sm;
+  const int tid = threadIdx.x;
+  int c, h;
+  ChunkInfo ci;
+  chunk_of(a.geo, blockIdx.x, a.H, c, h, ci);
+  const int L = ci.len, H = a.H, NT = a.geo.NT;
+  const size_t cm = (size_t)h * NT + c;
+  const size_t plane = (size_t)H * NT * kChunk * kDim;
+  const float* vec = a.vec + cm * (kVecRows * kChunk);
+  const int i = tid >> 2, q4 = tid & 3;   // row i; 16 columns from 16 q4 (64-wide) or 32 from 32 q4
+
+  // ---- dP = scale (dO V'^T), i >= j
+  {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid + 256 * e, r = idx >> 5, c4 = (idx & 31) * 4;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (r < L) {
+        const uint2 w = *reinterpret_cast<const uint2*>(a.dout + ((size_t)(ci.tok0 + r) * H + h) * kDim + c4);
+        x = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                        __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+      }
+      *reinterpret_cast<float4*>(sm.u.p1.dO + r * kLdR + c4) = x;
+    }
+    rows_f32(sm.u.p1.vp, a.vnew + cm * (kChunk * kDim), tid);
+    load_t(sm.t, a.tmat + cm * (kChunk * 2 * kChunk), tid);
+    if (tid < kChunk) sm.b[tid] = vec[tid];
+    __syncthreads();
+    float acc[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int v4 = 0; v4 < kDim; v4 += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(sm.u.p1.dO + i * kLdR + v4);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float4 y = *reinterpret_cast<const float4*>(sm.u.p1.vp + (16 * q4 + e) * kLdR + v4);
+        acc[e] = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, acc[e]))));
+      }
+    }
+    float* dP = a.dp + cm * (kChunk * kChunk);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int j = 16 * q4 + e;
+      dP[i * kChunk + j] = i >= j ? a.scale * acc[e] : 0.0f;
+    }
+    __syncthreads();
+  }
+
+  // ---- dT = dV' (b v)^T - F (b KD)^T
+  {
+    rows_f32(sm.u.p2.dv, a.dvn + cm * (kChunk * kDim), tid);
+    rows_f32(sm.u.p2.f, a.efd + plane + cm * (kChunk * kDim), tid);
+    const float* gk = a.gk + cm * (kChunk * kDim);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid + 256 * e, r = idx >> 5, c4 = (idx & 31) * 4;
+      const float rk = vec[2 * kChunk + r];
+      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f);
+      uint2 vv = make_uint2(0, 0);
+      if (r < L) {
+        const size_t off = ((size_t)(ci.tok0 + r) * H + h) * kDim + c4;
+        const uint2 w = *reinterpret_cast<const uint2*>(a.k + off);
+        vv = *reinterpret_cast<const uint2*>(a.v + off);
+        kv = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                         __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+      }
+      const float4 g = *reinterpret_cast<const float4*>(gk + r * kDim + c4);
+      *reinterpret_cast<float4*>(sm.u.p2.kd + r * kLdR + c4) =
+          make_float4(kv.x * rk * exp2_hw(g.x), kv.y * rk * exp2_hw(g.y), kv.z * rk * exp2_hw(g.z),
+                      kv.w * rk * exp2_hw(g.w));
+      *reinterpret_cast<uint2*>(sm.u.p2.v + r * kLdB + c4) = vv;
+    }
+    __syncthreads();
+    float acc[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int c4 = 0; c4 < kDim; c4 += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(sm.u.p2.dv + i * kLdR + c4);
+      const float4 f = *reinterpret_cast<const float4*>(sm.u.p2.f + i * kLdR + c4);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = 16 * q4 + e;
+        const uint2 w = *reinterpret_cast<const uint2*>(sm.u.p2.v + j * kLdB + c4);
+        const float4 kd = *reinterpret_cast<const float4*>(sm.u.p2.kd + j * kLdR + c4);
+        float s = acc[e];
+        s = fmaf(x.x, __uint_as_float(w.x << 16), s);
+        s = fmaf(x.y, __uint_as_float(w.x & 0xFFFF0000u), s);
+        s = fmaf(x.z, __uint_as_float(w.y << 16), s);
+        s = fmaf(x.w, __uint_as_float(w.y & 0xFFFF0000u), s);
+        s = fmaf(-f.x, kd.x, fmaf(-f.y, kd.y, fmaf(-f.z, kd.z, fmaf(-f.w, kd.w, s))));
+        acc[e] = s;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sm.dt[i * kLdM + 16 * q4 + e] = sm.b[16 * q4 + e] * acc[e];
+  }
+
+  // ---- tU = T^T dV', tW = -T^T F: dv = b tU, db1 = rowsum(tU v + tW KD), dKD = b tW
+  {
+    float tu[32], tw[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) { tu[e] = 0.f; tw[e] = 0.f; }
+    const int c0 = 32 * q4;
+    for (int r = i; r < kChunk; ++r) {
+      const float tv = sm.t[r * kLdM + i];
+#pragma unroll
+      for (int e4 = 0; e4 < 8; ++e4) {
+        const float4 x = *reinterpret_cast<const float4*>(sm.u.p2.dv + r * kLdR + c0 + 4 * e4);
+        const float4 f = *reinterpret_cast<const float4*>(sm.u.p2.f + r * kLdR + c0 + 4 * e4);
+        tu[4 * e4 + 0] = fmaf(tv, x.x, tu[4 * e4 + 0]); tu[4 * e4 + 1] = fmaf(tv, x.y, tu[4 * e4 + 1]);
+        tu[4 * e4 + 2] = fmaf(tv, x.z, tu[4 * e4 + 2]); tu[4 * e4 + 3] = fmaf(tv, x.w, tu[4 * e4 + 3]);
+        tw[4 * e4 + 0] = fmaf(-tv, f.x, tw[4 * e4 + 0]); tw[4 * e4 + 1] = fmaf(-tv, f.y, tw[4 * e4 + 1]);
+        tw[4 * e4 + 2] = fmaf(-tv, f.z, tw[4 * e4 + 2]); tw[4 * e4 + 3] = fmaf(-tv, f.w, tw[4 * e4 + 3]);
+      }
+    }
+    const float bi = sm.b[i];
+    float dbp = 0.f;
+    float* dkd = a.dkd + cm * (kChunk * kDim) + i * kDim + c0;
+#pragma unroll
+    for (int e4 = 0; e4 < 8; ++e4) {
+      const uint2 w = *reinterpret_cast<const uint2*>(sm.u.p2.v + i * kLdB + c0 + 4 * e4);
+      const float4 kd = *reinterpret_cast<const float4*>(sm.u.p2.kd + i * kLdR + c0 + 4 * e4);
+      const float vv[4] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                           __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+      const float kk[4] = {kd.x, kd.y, kd.z, kd.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dbp = fmaf(tu[4 * e4 + e], vv[e], fmaf(tw[4 * e4 + e], kk[e], dbp));
+      *reinterpret_cast<float4*>(dkd + 4 * e4) =
+          make_float4(bi * tw[4 * e4], bi * tw[4 * e4 + 1], bi * tw[4 * e4 + 2], bi * tw[4 * e4 + 3]);
+    }
+    if (i < L) {
+      float* dvo = a.dv + ((size_t)(ci.tok0 + i) * H + h) * kDim + c0;
+#pragma unroll
+      for (int e4 = 0; e4 < 8; ++e4)
+        *reinterpret_cast<float4*>(dvo + 4 * e4) =
+            make_float4(bi * tu[4 * e4], bi * tu[4 * e4 + 1], bi * tu[4 * e4 + 2], bi * tu[4 * e4 + 3]);
+    }
+    dbp += __shfl_xor(dbp, 1);
+    dbp += __shfl_xor(dbp, 2);
+    if (q4 == 0) a.db1[cm * kChunk + i] = dbp;
+  }
+  __syncthreads();
+
+  // ---- dA = (T^T dT T^T) on i > j: X = T^T dT (into the F area), then X T^T
+  {
+    float acc[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int r = i; r < kChunk; ++r) {
+      const float tv = sm.t[r * kLdM + i];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = fmaf(tv, sm.dt[r * kLdM + 16 * q4 + e], acc[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sm.u.p2.f[i * kLdR + 16 * q4 + e] = acc[e];
+  }
+  __syncthreads();
+  {
+    float* dA = a.da + cm * (kChunk * kChunk);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int j = 16 * q4 + e;
+      float s = 0.f;
+      if (i > j)
+        for (int k2 = 0; k2 <= j; ++k2) s = fmaf(sm.u.p2.f[i * kLdR + k2], sm.t[j * kLdM + k2], s);
+      dA[i * kChunk + j] = s;
+    }
+  }
+}
+
+namespace {
+
+struct alignas(16) GramSmem {
+  float g[kChunk * kLdR];     // G, then the gate gradient
+  float kn[kChunk * kLdR];    // k^, then dKG * KG
+  float qn[kChunk * kLdR];
+  float da[kChunk * kLdM];
+  float dp[kChunk * kLdM];
+  float b[kChunk];
+  float dgl[kDim];
+};
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void kda_bwd_gram_kernel(KdaBwdArgs a) {
+  __shared__ GramSmem sm;
+  const int tid = threadIdx.x;
+  int c, h;
+  ChunkInfo ci;
+  chunk_of(a.geo, blockIdx.x, a.H, c, h, ci);
+  const int L = ci.len, H = a.H, NT = a.geo.NT;
+  const size_t cm = (size_t)h * NT + c;
+  const float* vec = a.vec + cm * (kVecRows * kChunk);
+  const int r = tid >> 2, q4 = tid & 3, d0 = 32 * q4;
+
+  // G, k^, q^ rows; dA, dP; beta
+  {
+    const float* gk = a.gk + cm * (kChunk * kDim);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid + 256 * e, rr = idx >> 5, c4 = (idx & 31) * 4;
+      *reinterpret_cast<float4*>(sm.g + rr * kLdR + c4) = *reinterpret_cast<const float4*>(gk + rr * kDim + c4);
+      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
+      if (rr < L) {
+        const size_t off = ((size_t)(ci.tok0 + rr) * H + h) * kDim + c4;
+        const uint2 kw = *reinterpret_cast<const uint2*>(a.k + off);
+        const uint2 qw = *reinterpret_cast<const uint2*>(a.q + off);
+        const float rk = vec[6 * kChunk + rr], rq = vec[5 * kChunk + rr];
+        kv = make_float4(rk * __uint_as_float(kw.x << 16), rk * __uint_as_float(kw.x & 0xFFFF0000u),
+                         rk * __uint_as_float(kw.y << 16), rk * __uint_as_float(kw.y & 0xFFFF0000u));
+        qv = make_float4(rq * __uint_as_float(qw.x << 16), rq * __uint_as_float(qw.x & 0xFFFF0000u),
+                         rq * __uint_as_float(qw.y << 16), rq * __uint_as_float(qw.y & 0xFFFF0000u));
+      }
+      *reinterpret_cast<float4*>(sm.kn + rr * kLdR + c4) = kv;
+      *reinterpret_cast<float4*>(sm.qn + rr * kLdR + c4) = qv;
+    }
+    const float* dA = a.da + cm * (kChunk * kChunk);
+    const float* dP = a.dp + cm * (kChunk * kChunk);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int idx = tid + 256 * e, rr = idx >> 6, cc = idx & 63;
+      sm.da[rr * kLdM + cc] = dA[idx];
+      sm.dp[rr * kLdM + cc] = dP[idx];
+    }
+    if (tid < kChunk) sm.b[tid] = vec[tid];
+  }
+  __syncthreads();
+
+  float knr[32], qnr[32], gr[32], dkn[32], dqn[32], dG[32];
+#pragma unroll
+  for (int e4 = 0; e4 < 8; ++e4) {
+    const float4 k4 = *reinterpret_cast<const float4*>(sm.kn + r * kLdR + d0 + 4 * e4);
+    const float4 q4v = *reinterpret_cast<const float4*>(sm.qn + r * kLdR + d0 + 4 * e4);
+    const float4 g4 = *reinterpret_cast<const float4*>(sm.g + r * kLdR + d0 + 4 * e4);
+    knr[4 * e4] = k4.x; knr[4 * e4 + 1] = k4.y; knr[4 * e4 + 2] = k4.z; knr[4 * e4 + 3] = k4.w;
+    qnr[4 * e4] = q4v.x; qnr[4 * e4 + 1] = q4v.y; qnr[4 * e4 + 2] = q4v.z; qnr[4 * e4 + 3] = q4v.w;
+    gr[4 * e4] = g4.x; gr[4 * e4 + 1] = g4.y; gr[4 * e4 + 2] = g4.z; gr[4 * e4 + 3] = g4.w;
+  }
+#pragma unroll
+  for (int e = 0; e < 32; ++e) { dkn[e] = 0.f; dqn[e] = 0.f; dG[e] = 0.f; }
+  float dbp = 0.f;   // sum_j dA[r,j] sum_d k^_rd k^_jd 2^(G_rd - G_jd) over this thread's channels
+
+  // row r as the later row i: j <= r
+  const float br = sm.b[r];
+  for (int j = 0; j <= r; ++j) {
+    const float dAr = j < r ? sm.da[r * kLdM + j] : 0.0f;
+    const float wa = -br * dAr, dp = sm.dp[r * kLdM + j];
+#pragma unroll
+    for (int e4 = 0; e4 < 8; ++e4) {
+      const float4 kj = *reinterpret_cast<const float4*>(sm.kn + j * kLdR + d0 + 4 * e4);
+      const float4 gj = *reinterpret_cast<const float4*>(sm.g + j * kLdR + d0 + 4 * e4);
+      const float kja[4] = {kj.x, kj.y, kj.z, kj.w}, gja[4] = {gj.x, gj.y, gj.z, gj.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 4 * e4 + e;
+        const float ke = kja[e] * exp2_hw(gr[d] - gja[e]);
+        const float t1 = wa * ke, t2 = dp * ke;
+        dkn[d] += t1;
+        dqn[d] += t2;
+        dG[d] = fmaf(t1, knr[d], fmaf(t2, qnr[d], dG[d]));
+        dbp = fmaf(dAr * knr[d], ke, dbp);
+      }
+    }
+  }
+  // row r as the earlier row j: i >= r
+  for (int i2 = r; i2 < kChunk; ++i2) {
+    const float wa = i2 > r ? -sm.b[i2] * sm.da[i2 * kLdM + r] : 0.0f;
+    const float dp = sm.dp[i2 * kLdM + r];
+#pragma unroll
+    for (int e4 = 0; e4 < 8; ++e4) {
+      const float4 ki = *reinterpret_cast<const float4*>(sm.kn + i2 * kLdR + d0 + 4 * e4);
+      const float4 qi = *reinterpret_cast<const float4*>(sm.qn + i2 * kLdR + d0 + 4 * e4);
+      const float4 gi = *reinterpret_cast<const float4*>(sm.g + i2 * kLdR + d0 + 4 * e4);
+      const float kia[4] = {ki.x, ki.y, ki.z, ki.w}, qia[4] = {qi.x, qi.y, qi.z, qi.w};
+      const float gia[4] = {gi.x, gi.y, gi.z, gi.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 4 * e4 + e;
+        const float ex = exp2_hw(gia[e] - gr[d]);
+        const float s = (wa * kia[e] + dp * qia[e]) * ex;
+        dkn[d] += s;
+        dG[d] = fmaf(-s, knr[d], dG[d]);
+      }
+    }
+  }
+
+  // chains through KD, QD, KG and 2^G_last
+  const size_t plane = (size_t)H * NT * kChunk * kDim;
+  const float* Eo = a.efd + cm * (kChunk * kDim) + r * kDim + d0;
+  const float* Do = a.efd + 2 * plane + cm * (kChunk * kDim) + r * kDim + d0;
+  const float* dKD = a.dkd + cm * (kChunk * kDim) + r * kDim + d0;
+  float wkg[32];
+#pragma unroll
+  for (int e4 = 0; e4 < 8; ++e4) {
+    const float4 eo = *reinterpret_cast<const float4*>(Eo + 4 * e4);
+    const float4 dd = *reinterpret_cast<const float4*>(Do + 4 * e4);
+    const float4 dk4 = *reinterpret_cast<const float4*>(dKD + 4 * e4);
+    const float4 gl = *reinterpret_cast<const float4*>(sm.g + (kChunk - 1) * kLdR + d0 + 4 * e4);
+    const float eoa[4] = {eo.x, eo.y, eo.z, eo.w}, dda[4] = {dd.x, dd.y, dd.z, dd.w};
+    const float dka[4] = {dk4.x, dk4.y, dk4.z, dk4.w}, gla[4] = {gl.x, gl.y, gl.z, gl.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d = 4 * e4 + e;
+      const float eg = exp2_hw(gr[d]), el = exp2_hw(gla[e] - gr[d]);
+      const float dqd = a.scale * eoa[e];
+      const float kg = knr[d] * el;
+      dkn[d] = fmaf(dka[e], eg, fmaf(dda[e], el, dkn[d]));
+      dqn[d] = fmaf(dqd, eg, dqn[d]);
+      dG[d] += dka[e] * knr[d] * eg + dqd * qnr[d] * eg - dda[e] * kg;
+      wkg[d] = dda[e] * kg;
+    }
+  }
+  __syncthreads();  // every thread is done with G, k^, q^ in LDS
+#pragma unroll
+  for (int e4 = 0; e4 < 8; ++e4) {
+    *reinterpret_cast<float4*>(sm.g + r * kLdR + d0 + 4 * e4) =
+        make_float4(dG[4 * e4], dG[4 * e4 + 1], dG[4 * e4 + 2], dG[4 * e4 + 3]);
+    *reinterpret_cast<float4*>(sm.kn + r * kLdR + d0 + 4 * e4) =
+        make_float4(wkg[4 * e4], wkg[4 * e4 + 1], wkg[4 * e4 + 2], wkg[4 * e4 + 3]);
+  }
+  // gradient of G_last per channel: 2^G_last rowsum(S * dS_next) + sum_i dKG KG
+  if (tid < kDim) {
+    const int d = tid;
+    const float* S = a.h + cm * (kDim * kDim) + (size_t)d * kDim;
+    const float* dSn = a.dhn + cm * (kDim * kDim) + (size_t)d * kDim;
+    float s = 0.f;
+    for (int v4 = 0; v4 < kDim; v4 += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(S + v4), y = *reinterpret_cast<const float4*>(dSn + v4);
+      s = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, s))));
+    }
+    sm.dgl[d] = exp2_hw(a.gk[cm * (kChunk * kDim) + (kChunk - 1) * kDim + d]) * s;
+  }
+  __syncthreads();
+  // reverse cumulative sum of the gate gradient inside the chunk (channel d
+  // per thread), G_last's gradient entering at the last row
+  if (tid < kDim) {
+    const int d = tid;
+    float w = 0.f;
+    for (int i2 = 0; i2 < kChunk; ++i2) w += sm.kn[i2 * kLdR + d];
+    float run = sm.dgl[d] + w;
+    for (int i2 = kChunk - 1; i2 >= 0; --i2) {
+      run += sm.g[i2 * kLdR + d];
+      sm.g[i2 * kLdR + d] = run;
+    }
+  }
+  __syncthreads();
+
+  // outputs of row r: L2-norm and sigmoid derivatives
+  float qdot = 0.f, kdot = 0.f;
+#pragma unroll
+  for (int d = 0; d < 32; ++d) {
+    qdot = fmaf(qnr[d], dqn[d], qdot);
+    kdot = fmaf(knr[d], dkn[d], kdot);
+  }
+  qdot += __shfl_xor(qdot, 1);
+  qdot += __shfl_xor(qdot, 2);
+  kdot += __shfl_xor(kdot, 1);
+  kdot += __shfl_xor(kdot, 2);
+  dbp += __shfl_xor(dbp, 1);
+  dbp += __shfl_xor(dbp, 2);
+  if (r < L) {
+    const bool l2 = (a.flags & 1u) != 0;
+    const float rq = vec[5 * kChunk + r], rk = vec[6 * kChunk + r];
+    const size_t off = ((size_t)(ci.tok0 + r) * H + h) * kDim + d0;
+    constexpr float kLn2 = 0.6931471805599453f;
+#pragma unroll
+    for (int e4 = 0; e4 < 8; ++e4) {
+      float4 oq, ok, og;
+      float* pq = &oq.x;
+      float* pk = &ok.x;
+      float* pg = &og.x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 4 * e4 + e;
+        pq[e] = l2 ? rq * (dqn[d] - qnr[d] * qdot) : dqn[d];
+        pk[e] = l2 ? rk * (dkn[d] - knr[d] * kdot) : dkn[d];
+        pg[e] = kLn2 * sm.g[r * kLdR + d0 + d];
+      }
+      *reinterpret_cast<float4*>(a.dq + off + 4 * e4) = oq;
+      *reinterpret_cast<float4*>(a.dk + off + 4 * e4) = ok;
+      *reinterpret_cast<float4*>(a.dg + off + 4 * e4) = og;
+    }
+    if (q4 == 0) {
+      const float db = a.db1[cm * kChunk + r] - dbp;
+      a.dbeta[(size_t)(ci.tok0 + r) * H + h] = (a.flags & 2u) ? db * br * (1.0f - br) : db;
+    }
+  }
+}
+
+hipError_t launch_kda_bwd_chunks(const KdaBwdArgs& a, hipStream_t stream) {
+  const unsigned grid = (unsigned)((size_t)a.geo.NT * a.H);
+  hipLaunchKernelGGL(kda_bwd_mats_kernel, dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(kda_bwd_gram_kernel, dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_kda_bwd_dh(const KdaBwdArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)((size_t)a.geo.N * a.H * (kDim / kCols));
   hipLaunchKernelGGL(kda_bwd_dh_kernel, dim3(grid), dim3(256), 0, stream, a);

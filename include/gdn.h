@@ -312,6 +312,29 @@ int gdn_state_summary_apply(const float* transition, const float* state_ext, con
                             float* state_out, int32_t N, int32_t H, int32_t K, int32_t V, void* stream);
 
 /*
+ * Backward pass, KDA (per-key-channel log2 gate): the arguments and outputs
+ * of gdn_chunk_bwd for the forward of kda_chunk_fwd, with g [B,T,H,K] and
+ *   dg [B,T,H,K] fp32, the gradient w.r.t. the raw log2 gate;
+ * g, d_o, dq, dk, dv and dg 16-byte aligned. The call recomputes the forward
+ * intermediates (the KDA prepare kernel writing the cumulative gate; the
+ * state pass storing the state entering every chunk and v_new), runs the
+ * reverse state pass below, the products with the saved states, and the
+ * per-chunk gradients (the terms of the intra-chunk matrices with their
+ * per-channel decays, the gate's reverse cumulative sum, the L2-norm and
+ * sigmoid derivatives). Workspace sized by kda_chunk_bwd_workspace_bytes.
+ * The pages print no backward formula; the steps are the derivatives of the
+ * forward's chunk form, in the order of bwd_prepare_saved, bwd_state_saved
+ * and bwd_finish_saved on the 2026-09-10 "Diff Coverage" page.
+ */
+size_t kda_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                     const int32_t* cu_seqlens, uint32_t flags);
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                  int32_t H, int32_t K, int32_t V, float scale, uint32_t flags, const void* d_o,
+                  const float* d_final_state, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                  float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * KDA backward, reverse state pass (the stage of the backward that carries the
  * state gradient across chunks; bwd_state_saved of the backward on the
  * 2026-09-10 "Diff Coverage" page, with the per-channel decays of the KDA
@@ -329,8 +352,8 @@ int gdn_state_summary_apply(const float* transition, const float* state_ext, con
  * d_final_state and does not depend on v or the initial state, which are not
  * arguments. d_o bf16 [B,T,H,V] (required); d_final_state fp32 [N,H,K,V] or
  * NULL (zero). Workspace sized by kda_bwd_state_pass_workspace_bytes; other
- * arguments, errors and stream behaviour as kda_chunk_fwd. The remaining KDA
- * backward stages (the per-chunk input gradients) are not provided.
+ * arguments, errors and stream behaviour as kda_chunk_fwd. It is the second
+ * stage of kda_chunk_bwd, exposed for stage checks.
  */
 size_t kda_bwd_state_pass_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
                                           const int32_t* cu_seqlens, uint32_t flags);

@@ -115,3 +115,54 @@ def test_kda_reverse_state_pass_full_size_sampled(gdn):
     _say("  " + "  ".join("%s %.2e" % kv for kv in errs.items()))
     for key, e in errs.items():
         assert e <= RTOL, (key, e)
+
+
+# ---------------------------------------------------------------------------
+# Whole KDA backward (kda_chunk_bwd) against the fp64 autograd oracle.
+# ---------------------------------------------------------------------------
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "ds0")
+
+
+def _whole_cases():
+    rng = np.random.default_rng(221)
+    return [
+        ("kda_B2_T150_H2", gi.make_inputs("kda", B=2, T=150, H=2)),
+        # with an initial state: from a zero one the gate's gradient at T = 1 is exactly zero
+        ("kda_T1_init", gi.random_problem(rng, 2, 1, 2, 128, 128, kda=True, with_initial_state=True)),
+        ("kda_T64", gi.make_inputs("kda", B=1, T=64, H=3)),
+        ("kda_mild_init", gi.random_problem(rng, 1, 200, 2, 128, 128, kda=True, gate_scale=0.05,
+                                            with_initial_state=True)),
+        ("kda_packed", gi.random_problem(rng, 1, 277, 2, 128, 128, kda=True, gate_scale=0.3, with_initial_state=True,
+                                         cu_seqlens=np.array([0, 1, 18, 82, 147, 277]))),
+        ("kda_l2norm_only", gi.random_problem(rng, 1, 100, 2, 128, 128, kda=True, gate_scale=0.3,
+                                              with_initial_state=True,
+                                              flags=gi.FLAG_L2NORM_QK | gi.FLAG_OUTPUT_FINAL_STATE)),
+    ]
+
+
+WHOLE = _whole_cases()
+
+
+@pytest.mark.parametrize("name,inp", WHOLE, ids=[c[0] for c in WHOLE])
+def test_kda_chunk_bwd_parity(gdn, name, inp):
+    from oracle import grad as og
+    _say("kda bwd", name, inp.B, inp.T, inp.H, "flags", inp.flags)
+    rng = np.random.default_rng(8)
+    do_bits = gi.f32_to_bf16_bits(rng.standard_normal((inp.B, inp.T, inp.H, inp.V), dtype=np.float32))
+    dsf = (rng.standard_normal((inp.num_seqs, inp.H, inp.K, inp.V)) * 0.1).astype(np.float32)
+    d = to_device(inp)
+    out = gdn.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                            torch.from_numpy(do_bits).view(torch.bfloat16).cuda(), scale=inp.scale,
+                            initial_state=d["initial_state"], d_final_state=torch.from_numpy(dsf).cuda(),
+                            cu_seqlens=inp.cu_seqlens, l2norm_qk=bool(inp.flags & 1),
+                            beta_sigmoid=bool(inp.flags & 2))
+    torch.cuda.synchronize()
+    ref = og.grads(inp, gi.bf16_bits_to_f32(do_bits).astype(np.float64), dsf.astype(np.float64))
+    errs = {}
+    for key, t in zip(NAMES, out):
+        x = t.cpu().numpy().astype(np.float64)
+        assert np.isfinite(x).all(), key
+        errs[key] = float(np.abs(x - ref[key]).max() / max(np.abs(ref[key]).max(), 1e-30))
+    _say("  " + "  ".join("%s %.2e" % kv for kv in errs.items()))
+    for key, e in errs.items():
+        assert e <= RTOL, (key, e)
