@@ -166,3 +166,32 @@ def test_kda_chunk_bwd_parity(gdn, name, inp):
     _say("  " + "  ".join("%s %.2e" % kv for kv in errs.items()))
     for key, e in errs.items():
         assert e <= RTOL, (key, e)
+
+
+def test_kda_chunk_bwd_full_size_sampled(gdn):
+    """The benchmark shape (B=2, T=8192, H=32): the whole backward on the GPU,
+    then one (sequence, head) against the autograd oracle run on that slice."""
+    from oracle import grad as og
+    inp = gi.make_inputs("kda")
+    _say("kda bwd full size B,T,H =", inp.B, inp.T, inp.H)
+    rng = np.random.default_rng(9)
+    do_bits = gi.f32_to_bf16_bits(rng.standard_normal((inp.B, inp.T, inp.H, inp.V), dtype=np.float32))
+    dsf = (rng.standard_normal((inp.num_seqs, inp.H, inp.K, inp.V)) * 0.1).astype(np.float32)
+    d = to_device(inp)
+    out = gdn.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                            torch.from_numpy(do_bits).view(torch.bfloat16).cuda(), scale=inp.scale,
+                            d_final_state=torch.from_numpy(dsf).cuda(), l2norm_qk=True, beta_sigmoid=True)
+    torch.cuda.synchronize()
+    b, h = 0, 17
+    sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
+    one = gi.GdnInputs(**{**inp.__dict__, "B": 1, "H": 1, "q": sl(inp.q), "k": sl(inp.k), "v": sl(inp.v),
+                          "g": sl(inp.g), "beta": sl(inp.beta), "initial_state": None})
+    ref = og.grads(one, gi.bf16_bits_to_f32(sl(do_bits)).astype(np.float64), dsf[b:b + 1, h:h + 1].astype(np.float64))
+    errs = {}
+    for key, t in zip(NAMES, out):
+        x = t.cpu().numpy().astype(np.float64)
+        x = x[b:b + 1, h:h + 1] if key == "ds0" else x[b:b + 1, :, h:h + 1]
+        errs[key] = float(np.abs(x - ref[key]).max() / max(np.abs(ref[key]).max(), 1e-30))
+    _say("  " + "  ".join("%s %.2e" % kv for kv in errs.items()))
+    for key, e in errs.items():
+        assert e <= RTOL, (key, e)
