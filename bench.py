@@ -56,16 +56,28 @@ STATE_BYTES_PER_UNIT = 128 * 128 * 4  # one fp32 state per (sequence, head), eac
 ALG_FLOPS_PER_TH = 140629             # conservative (triangle-exploiting) count
 
 
-KERNEL_SOURCES = ("gdn_common.h", "gdn_kernels.h", "gdn_prepare.hip", "gdn_fwd.hip", "gdn_state.hip",
-                  "gdn_state_common.h", "kda_fwd.hip", "kda_state.hip", "gdn_bwd.h", "gdn_bwd.hip", "short_conv.hip",
-                  "kda_bwd.hip")
+FWD_SOURCES = ("gdn_common.h", "gdn_kernels.h", "gdn_prepare.hip", "gdn_fwd.hip", "gdn_state.hip",
+               "gdn_state_common.h", "kda_fwd.hip", "kda_state.hip")
+KERNEL_SOURCES = FWD_SOURCES + ("gdn_bwd.h", "gdn_bwd.hip", "short_conv.hip", "kda_bwd.hip")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources; HBM counters recorded for other sources are stale."""
+def sources_for(workload: str):
+    """The kernel sources a workload's counter summary depends on."""
+    if workload == "bwd_kda":
+        return FWD_SOURCES + ("gdn_bwd.h", "gdn_bwd.hip", "kda_bwd.hip")
+    if workload.startswith("bwd"):
+        return FWD_SOURCES + ("gdn_bwd.h", "gdn_bwd.hip")
+    if workload == "conv":
+        return ("gdn_common.h", "gdn_kernels.h", "short_conv.hip")
+    return FWD_SOURCES
+
+
+def kernel_source_hash(workload=None) -> str:
+    """Hash of the kernel sources (of one workload's kernels, or all); HBM
+    counters recorded for other sources are stale."""
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in (KERNEL_SOURCES if workload is None else sources_for(workload)):
         with open(os.path.join(ROOT, "chunked_gated_delta_03_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -78,7 +90,7 @@ def recorded_traffic(workload: str, kernel_name_part: str):
     for path in glob.glob(os.path.join(ROOT, "profiles", "*_hbm_counters.json")):
         with open(path) as f:
             d = json.load(f)
-        if d.get("workload") != workload or d.get("kernel_source_hash") != kernel_source_hash():
+        if d.get("workload") != workload or d.get("kernel_source_hash") != kernel_source_hash(workload):
             continue
         for name, rec in d["kernels"].items():
             if kernel_name_part in name:

@@ -17,7 +17,8 @@
 // WY inverse and Aqk the intra-chunk output matrix (scale rq rk included),
 // all from the KDA prepare kernel. Every exponent is <= 0.
 //
-// One workgroup per (sequence, head, 16 value columns), fp32 arithmetic on
+// One workgroup per (sequence, head, 16 value columns), the eight of a
+// (sequence, head) dispatched to one XCD, fp32 arithmetic on
 // the vector units: the operands of a chunk are formed in LDS, the 128 x 16
 // block of dS is held in registers (thread t: column t % 16, rows 8 (t / 16)
 // .. + 7). It stores, per chunk, dS before the update (the gradient w.r.t. the
@@ -50,9 +51,10 @@ struct alignas(16) KdaDhSmem {
 __global__ __launch_bounds__(256) void kda_bwd_dh_kernel(KdaBwdArgs a) {
   __shared__ KdaDhSmem sm;
   const int tid = threadIdx.x;
-  const int vb = blockIdx.x % (kDim / kCols);
-  const int unit = blockIdx.x / (kDim / kCols);
-  const int n = unit / a.H, h = unit - (unit / a.H) * a.H;
+  // the value-column blocks of one (sequence, head) on one XCD, where they
+  // share the L2 copy of the chunk operands; longest sequences first
+  int n, h, vb;
+  if (!state_unit(a.geo, a.H, kDim / kCols, n, h, vb)) return;
   const SeqInfo si = a.geo.seq(n);
   const int NT = a.geo.NT;
   const int col0 = vb * kCols;
@@ -694,8 +696,7 @@ hipError_t launch_kda_bwd_chunks(const KdaBwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_kda_bwd_dh(const KdaBwdArgs& a, hipStream_t stream) {
-  const unsigned grid = (unsigned)((size_t)a.geo.N * a.H * (kDim / kCols));
-  hipLaunchKernelGGL(kda_bwd_dh_kernel, dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(kda_bwd_dh_kernel, dim3(state_grid(a.geo.N, a.H, kDim / kCols)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

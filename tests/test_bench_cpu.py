@@ -18,6 +18,13 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr
 
 
+def test_counter_hash_follows_the_workloads_sources():
+    assert "kda_bwd.hip" not in bench.sources_for("gdn")
+    assert "kda_bwd.hip" in bench.sources_for("bwd_kda")
+    assert "gdn_bwd.hip" in bench.sources_for("bwd_gdn")
+    assert bench.sources_for("conv") == ("gdn_common.h", "gdn_kernels.h", "short_conv.hip")
+
+
 def test_algorithmic_bytes_per_token_head():
     # q, k, v bf16 (768) + gate (GDN 4 / KDA 512) + beta (2) + o bf16 (256)
     assert bench.GDN_PREP_BYTES + bench.STATE_BYTES == 1030
@@ -28,12 +35,12 @@ def test_recorded_traffic_requires_matching_sources(tmp_path, monkeypatch):
     """A counter summary counts only for the kernel sources it was taken on."""
     prof = tmp_path / "profiles"
     prof.mkdir()
-    rec = {"workload": "gdn", "kernel_source_hash": bench.kernel_source_hash(),
+    rec = {"workload": "gdn", "kernel_source_hash": bench.kernel_source_hash("gdn"),
            "kernels": {"void gdn::gdn_state_kernel<2, false, true>(gdn::FwdArgs)": {"hbm_bytes_scaled": 123.0}}}
     (prof / "x_hbm_counters.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: rec["kernel_source_hash"])
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda w=None: rec["kernel_source_hash"])
     assert bench.recorded_traffic("gdn", "gdn_state_kernel") == 123.0
     assert bench.recorded_traffic("kda", "gdn_state_kernel") is None
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "other")
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda w=None: "other")
     assert bench.recorded_traffic("gdn", "gdn_state_kernel") is None
