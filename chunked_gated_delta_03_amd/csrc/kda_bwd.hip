@@ -243,7 +243,8 @@ __global__ __launch_bounds__(512) void kda_bwd_dh_kernel(KdaBwdArgs a) {
 //         the chunk, the L2-norm and sigmoid derivatives.
 // k^ = k rk and q^ = q rq are the normalised rows; G the cumulative log2
 // gate. Every exponent 2^(G_i - G_j) is taken with i >= j, so it is <= 0.
-// fp32 arithmetic on the vector units; one workgroup per (chunk, head),
+// fp32 arithmetic on the vector units; one workgroup per (chunk, head) (the
+// gram kernel with 512 threads: row r, 16 channels each),
 // heads fastest in dispatch order.
 // ---------------------------------------------------------------------------
 namespace {
@@ -488,7 +489,7 @@ struct alignas(16) GramSmem {
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void kda_bwd_gram_kernel(KdaBwdArgs a) {
+__global__ __launch_bounds__(512) void kda_bwd_gram_kernel(KdaBwdArgs a) {
   __shared__ GramSmem sm;
   const int tid = threadIdx.x;
   int c, h;
@@ -497,14 +498,14 @@ __global__ __launch_bounds__(256) void kda_bwd_gram_kernel(KdaBwdArgs a) {
   const int L = ci.len, H = a.H, NT = a.geo.NT;
   const size_t cm = (size_t)h * NT + c;
   const float* vec = a.vec + cm * (kVecRows * kChunk);
-  const int r = tid >> 2, q4 = tid & 3, d0 = 32 * q4;
+  const int r = tid >> 3, q8 = tid & 7, d0 = 16 * q8;
 
   // G, k^, q^ rows; dA, dP; beta
   {
     const float* gk = a.gk + cm * (kChunk * kDim);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int idx = tid + 256 * e, rr = idx >> 5, c4 = (idx & 31) * 4;
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + 512 * e, rr = idx >> 5, c4 = (idx & 31) * 4;
       *reinterpret_cast<float4*>(sm.g + rr * kLdR + c4) = *reinterpret_cast<const float4*>(gk + rr * kDim + c4);
       float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
       if (rr < L) {
@@ -523,8 +524,8 @@ __global__ __launch_bounds__(256) void kda_bwd_gram_kernel(KdaBwdArgs a) {
     const float* dA = a.da + cm * (kChunk * kChunk);
     const float* dP = a.dp + cm * (kChunk * kChunk);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int idx = tid + 256 * e, rr = idx >> 6, cc = idx & 63;
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid + 512 * e, rr = idx >> 6, cc = idx & 63;
       sm.da[rr * kLdM + cc] = dA[idx];
       sm.dp[rr * kLdM + cc] = dP[idx];
     }
@@ -532,9 +533,9 @@ __global__ __launch_bounds__(256) void kda_bwd_gram_kernel(KdaBwdArgs a) {
   }
   __syncthreads();
 
-  float knr[32], qnr[32], gr[32], dkn[32], dqn[32], dG[32];
+  float knr[16], qnr[16], gr[16], dkn[16], dqn[16], dG[16];
 #pragma unroll
-  for (int e4 = 0; e4 < 8; ++e4) {
+  for (int e4 = 0; e4 < 4; ++e4) {
     const float4 k4 = *reinterpret_cast<const float4*>(sm.kn + r * kLdR + d0 + 4 * e4);
     const float4 q4v = *reinterpret_cast<const float4*>(sm.qn + r * kLdR + d0 + 4 * e4);
     const float4 g4 = *reinterpret_cast<const float4*>(sm.g + r * kLdR + d0 + 4 * e4);
@@ -543,7 +544,7 @@ __global__ __launch_bounds__(256) void kda_bwd_gram_kernel(KdaBwdArgs a) {
     gr[4 * e4] = g4.x; gr[4 * e4 + 1] = g4.y; gr[4 * e4 + 2] = g4.z; gr[4 * e4 + 3] = g4.w;
   }
 #pragma unroll
-  for (int e = 0; e < 32; ++e) { dkn[e] = 0.f; dqn[e] = 0.f; dG[e] = 0.f; }
+  for (int e = 0; e < 16; ++e) { dkn[e] = 0.f; dqn[e] = 0.f; dG[e] = 0.f; }
   float dbp = 0.f;   // sum_j dA[r,j] sum_d k^_rd k^_jd 2^(G_rd - G_jd) over this thread's channels
 
   // row r as the later row i: j <= r
@@ -552,7 +553,7 @@ __global__ __launch_bounds__(256) void kda_bwd_gram_kernel(KdaBwdArgs a) {
     const float dAr = j < r ? sm.da[r * kLdM + j] : 0.0f;
     const float wa = -br * dAr, dp = sm.dp[r * kLdM + j];
 #pragma unroll
-    for (int e4 = 0; e4 < 8; ++e4) {
+    for (int e4 = 0; e4 < 4; ++e4) {
       const float4 kj = *reinterpret_cast<const float4*>(sm.kn + j * kLdR + d0 + 4 * e4);
       const float4 gj = *reinterpret_cast<const float4*>(sm.g + j * kLdR + d0 + 4 * e4);
       const float kja[4] = {kj.x, kj.y, kj.z, kj.w}, gja[4] = {gj.x, gj.y, gj.z, gj.w};
@@ -573,7 +574,7 @@ __global__ __launch_bounds__(256) void kda_bwd_gram_kernel(KdaBwdArgs a) {
     const float wa = i2 > r ? -sm.b[i2] * sm.da[i2 * kLdM + r] : 0.0f;
     const float dp = sm.dp[i2 * kLdM + r];
 #pragma unroll
-    for (int e4 = 0; e4 < 8; ++e4) {
+    for (int e4 = 0; e4 < 4; ++e4) {
       const float4 ki = *reinterpret_cast<const float4*>(sm.kn + i2 * kLdR + d0 + 4 * e4);
       const float4 qi = *reinterpret_cast<const float4*>(sm.qn + i2 * kLdR + d0 + 4 * e4);
       const float4 gi = *reinterpret_cast<const float4*>(sm.g + i2 * kLdR + d0 + 4 * e4);
@@ -595,9 +596,9 @@ __global__ __launch_bounds__(256) void kda_bwd_gram_kernel(KdaBwdArgs a) {
   const float* Eo = a.efd + cm * (kChunk * kDim) + r * kDim + d0;
   const float* Do = a.efd + 2 * plane + cm * (kChunk * kDim) + r * kDim + d0;
   const float* dKD = a.dkd + cm * (kChunk * kDim) + r * kDim + d0;
-  float wkg[32];
+  float wkg[16];
 #pragma unroll
-  for (int e4 = 0; e4 < 8; ++e4) {
+  for (int e4 = 0; e4 < 4; ++e4) {
     const float4 eo = *reinterpret_cast<const float4*>(Eo + 4 * e4);
     const float4 dd = *reinterpret_cast<const float4*>(Do + 4 * e4);
     const float4 dk4 = *reinterpret_cast<const float4*>(dKD + 4 * e4);
@@ -618,7 +619,7 @@ __global__ __launch_bounds__(256) void kda_bwd_gram_kernel(KdaBwdArgs a) {
   }
   __syncthreads();  // every thread is done with G, k^, q^ in LDS
 #pragma unroll
-  for (int e4 = 0; e4 < 8; ++e4) {
+  for (int e4 = 0; e4 < 4; ++e4) {
     *reinterpret_cast<float4*>(sm.g + r * kLdR + d0 + 4 * e4) =
         make_float4(dG[4 * e4], dG[4 * e4 + 1], dG[4 * e4 + 2], dG[4 * e4 + 3]);
     *reinterpret_cast<float4*>(sm.kn + r * kLdR + d0 + 4 * e4) =
@@ -654,23 +655,23 @@ __global__ __launch_bounds__(256) void kda_bwd_gram_kernel(KdaBwdArgs a) {
   // outputs of row r: L2-norm and sigmoid derivatives
   float qdot = 0.f, kdot = 0.f;
 #pragma unroll
-  for (int d = 0; d < 32; ++d) {
+  for (int d = 0; d < 16; ++d) {
     qdot = fmaf(qnr[d], dqn[d], qdot);
     kdot = fmaf(knr[d], dkn[d], kdot);
   }
-  qdot += __shfl_xor(qdot, 1);
-  qdot += __shfl_xor(qdot, 2);
-  kdot += __shfl_xor(kdot, 1);
-  kdot += __shfl_xor(kdot, 2);
-  dbp += __shfl_xor(dbp, 1);
-  dbp += __shfl_xor(dbp, 2);
+#pragma unroll
+  for (int m = 1; m <= 4; m <<= 1) {
+    qdot += __shfl_xor(qdot, m);
+    kdot += __shfl_xor(kdot, m);
+    dbp += __shfl_xor(dbp, m);
+  }
   if (r < L) {
     const bool l2 = (a.flags & 1u) != 0;
     const float rq = vec[5 * kChunk + r], rk = vec[6 * kChunk + r];
     const size_t off = ((size_t)(ci.tok0 + r) * H + h) * kDim + d0;
     constexpr float kLn2 = 0.6931471805599453f;
 #pragma unroll
-    for (int e4 = 0; e4 < 8; ++e4) {
+    for (int e4 = 0; e4 < 4; ++e4) {
       float4 oq, ok, og;
       float* pq = &oq.x;
       float* pk = &ok.x;
@@ -686,7 +687,7 @@ __global__ __launch_bounds__(256) void kda_bwd_gram_kernel(KdaBwdArgs a) {
       *reinterpret_cast<float4*>(a.dk + off + 4 * e4) = ok;
       *reinterpret_cast<float4*>(a.dg + off + 4 * e4) = og;
     }
-    if (q4 == 0) {
+    if (q8 == 0) {
       const float db = a.db1[cm * kChunk + r] - dbp;
       a.dbeta[(size_t)(ci.tok0 + r) * H + h] = (a.flags & 2u) ? db * br * (1.0f - br) : db;
     }
@@ -696,7 +697,7 @@ __global__ __launch_bounds__(256) void kda_bwd_gram_kernel(KdaBwdArgs a) {
 hipError_t launch_kda_bwd_chunks(const KdaBwdArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)((size_t)a.geo.NT * a.H);
   hipLaunchKernelGGL(kda_bwd_mats_kernel, dim3(grid), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(kda_bwd_gram_kernel, dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(kda_bwd_gram_kernel, dim3(grid), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
