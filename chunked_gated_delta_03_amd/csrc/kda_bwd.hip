@@ -244,7 +244,7 @@ __global__ __launch_bounds__(512) void kda_bwd_dh_kernel(KdaBwdArgs a) {
 // k^ = k rk and q^ = q rq are the normalised rows; G the cumulative log2
 // gate. Every exponent 2^(G_i - G_j) is taken with i >= j, so it is <= 0.
 // fp32 arithmetic on the vector units; one workgroup per (chunk, head) (the
-// gram kernel with 512 threads: row r, 16 channels each),
+// kernels with 512 threads; the gram kernel's thread: row r, 16 channels),
 // heads fastest in dispatch order.
 // ---------------------------------------------------------------------------
 namespace {
@@ -276,35 +276,34 @@ __device__ __forceinline__ void chunk_of(const Geometry& geo, int bx, int H, int
   ci = geo.chunk(c);
 }
 
-// 64 x 128 fp32 rows (global, row stride 128) into LDS (row stride kLdR)
+// 64 x 128 fp32 rows (global, row stride 128) into LDS (row stride kLdR), 512 threads
 __device__ __forceinline__ void rows_f32(float* dst, const float* src, int tid) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int idx = tid + 256 * e, r = idx >> 5, c4 = (idx & 31) * 4;
+  for (int e = 0; e < 4; ++e) {
+    const int idx = tid + 512 * e, r = idx >> 5, c4 = (idx & 31) * 4;
     *reinterpret_cast<float4*>(dst + r * kLdR + c4) = *reinterpret_cast<const float4*>(src + r * kDim + c4);
   }
 }
 
-// T = hi + lo from its stored permuted columns into LDS (row stride kLdM)
+// T = hi + lo from its stored permuted columns into LDS (row stride kLdM), 512 threads
 __device__ __forceinline__ void load_t(float* dst, const uint16_t* tm, int tid) {
-  const int r = tid >> 2, qq = tid & 3;
-  const uint16_t* row = tm + r * (2 * kChunk) + 16 * qq;
-  const uint4 h0 = reinterpret_cast<const uint4*>(row)[0], h1 = reinterpret_cast<const uint4*>(row)[1];
-  const uint4 l0 = reinterpret_cast<const uint4*>(row + kChunk)[0];
-  const uint4 l1 = reinterpret_cast<const uint4*>(row + kChunk)[1];
-  const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-  const uint32_t lw[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+  const int r = tid >> 3, qq = tid & 7;
+  const uint16_t* row = tm + r * (2 * kChunk) + 8 * qq;
+  const uint4 h0 = *reinterpret_cast<const uint4*>(row);
+  const uint4 l0 = *reinterpret_cast<const uint4*>(row + kChunk);
+  const uint32_t hw[4] = {h0.x, h0.y, h0.z, h0.w};
+  const uint32_t lw[4] = {l0.x, l0.y, l0.z, l0.w};
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < 8; ++e) {
     const float hv = __uint_as_float((e & 1) ? (hw[e >> 1] & 0xFFFF0000u) : (hw[e >> 1] << 16));
     const float lv = __uint_as_float((e & 1) ? (lw[e >> 1] & 0xFFFF0000u) : (lw[e >> 1] << 16));
-    dst[r * kLdM + unperm_col(16 * qq + e)] = hv + lv;
+    dst[r * kLdM + unperm_col(8 * qq + e)] = hv + lv;
   }
 }
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void kda_bwd_mats_kernel(KdaBwdArgs a) {
+__global__ __launch_bounds__(512) void kda_bwd_mats_kernel(KdaBwdArgs a) {
   __shared__ MatsSmem sm;
   const int tid = threadIdx.x;
   int c, h;
@@ -314,13 +313,13 @@ __global__ __launch_bounds__(256) void kda_bwd_mats_kernel(KdaBwdArgs a) {
   const size_t cm = (size_t)h * NT + c;
   const size_t plane = (size_t)H * NT * kChunk * kDim;
   const float* vec = a.vec + cm * (kVecRows * kChunk);
-  const int i = tid >> 2, q4 = tid & 3;   // row i; 16 columns from 16 q4 (64-wide) or 32 from 32 q4
+  const int i = tid >> 3, q8 = tid & 7;   // row i; 8 columns from 8 q8 (64-wide) or 16 from 16 q8
 
   // ---- dP = scale (dO V'^T), i >= j
   {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int idx = tid + 256 * e, r = idx >> 5, c4 = (idx & 31) * 4;
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + 512 * e, r = idx >> 5, c4 = (idx & 31) * 4;
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
       if (r < L) {
         const uint2 w = *reinterpret_cast<const uint2*>(a.dout + ((size_t)(ci.tok0 + r) * H + h) * kDim + c4);
@@ -333,21 +332,21 @@ __global__ __launch_bounds__(256) void kda_bwd_mats_kernel(KdaBwdArgs a) {
     load_t(sm.t, a.tmat + cm * (kChunk * 2 * kChunk), tid);
     if (tid < kChunk) sm.b[tid] = vec[tid];
     __syncthreads();
-    float acc[16];
+    float acc[8];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     for (int v4 = 0; v4 < kDim; v4 += 4) {
       const float4 x = *reinterpret_cast<const float4*>(sm.u.p1.dO + i * kLdR + v4);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float4 y = *reinterpret_cast<const float4*>(sm.u.p1.vp + (16 * q4 + e) * kLdR + v4);
+      for (int e = 0; e < 8; ++e) {
+        const float4 y = *reinterpret_cast<const float4*>(sm.u.p1.vp + (8 * q8 + e) * kLdR + v4);
         acc[e] = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, acc[e]))));
       }
     }
     float* dP = a.dp + cm * (kChunk * kChunk);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int j = 16 * q4 + e;
+    for (int e = 0; e < 8; ++e) {
+      const int j = 8 * q8 + e;
       dP[i * kChunk + j] = i >= j ? a.scale * acc[e] : 0.0f;
     }
     __syncthreads();
@@ -359,8 +358,8 @@ __global__ __launch_bounds__(256) void kda_bwd_mats_kernel(KdaBwdArgs a) {
     rows_f32(sm.u.p2.f, a.efd + plane + cm * (kChunk * kDim), tid);
     const float* gk = a.gk + cm * (kChunk * kDim);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int idx = tid + 256 * e, r = idx >> 5, c4 = (idx & 31) * 4;
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + 512 * e, r = idx >> 5, c4 = (idx & 31) * 4;
       const float rk = vec[2 * kChunk + r];
       float4 kv = make_float4(0.f, 0.f, 0.f, 0.f);
       uint2 vv = make_uint2(0, 0);
@@ -378,15 +377,15 @@ __global__ __launch_bounds__(256) void kda_bwd_mats_kernel(KdaBwdArgs a) {
       *reinterpret_cast<uint2*>(sm.u.p2.v + r * kLdB + c4) = vv;
     }
     __syncthreads();
-    float acc[16];
+    float acc[8];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     for (int c4 = 0; c4 < kDim; c4 += 4) {
       const float4 x = *reinterpret_cast<const float4*>(sm.u.p2.dv + i * kLdR + c4);
       const float4 f = *reinterpret_cast<const float4*>(sm.u.p2.f + i * kLdR + c4);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = 16 * q4 + e;
+      for (int e = 0; e < 8; ++e) {
+        const int j = 8 * q8 + e;
         const uint2 w = *reinterpret_cast<const uint2*>(sm.u.p2.v + j * kLdB + c4);
         const float4 kd = *reinterpret_cast<const float4*>(sm.u.p2.kd + j * kLdR + c4);
         float s = acc[e];
@@ -399,19 +398,19 @@ __global__ __launch_bounds__(256) void kda_bwd_mats_kernel(KdaBwdArgs a) {
       }
     }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sm.dt[i * kLdM + 16 * q4 + e] = sm.b[16 * q4 + e] * acc[e];
+    for (int e = 0; e < 8; ++e) sm.dt[i * kLdM + 8 * q8 + e] = sm.b[8 * q8 + e] * acc[e];
   }
 
   // ---- tU = T^T dV', tW = -T^T F: dv = b tU, db1 = rowsum(tU v + tW KD), dKD = b tW
   {
-    float tu[32], tw[32];
+    float tu[16], tw[16];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) { tu[e] = 0.f; tw[e] = 0.f; }
-    const int c0 = 32 * q4;
+    for (int e = 0; e < 16; ++e) { tu[e] = 0.f; tw[e] = 0.f; }
+    const int c0 = 16 * q8;
     for (int r = i; r < kChunk; ++r) {
       const float tv = sm.t[r * kLdM + i];
 #pragma unroll
-      for (int e4 = 0; e4 < 8; ++e4) {
+      for (int e4 = 0; e4 < 4; ++e4) {
         const float4 x = *reinterpret_cast<const float4*>(sm.u.p2.dv + r * kLdR + c0 + 4 * e4);
         const float4 f = *reinterpret_cast<const float4*>(sm.u.p2.f + r * kLdR + c0 + 4 * e4);
         tu[4 * e4 + 0] = fmaf(tv, x.x, tu[4 * e4 + 0]); tu[4 * e4 + 1] = fmaf(tv, x.y, tu[4 * e4 + 1]);
@@ -424,7 +423,7 @@ __global__ __launch_bounds__(256) void kda_bwd_mats_kernel(KdaBwdArgs a) {
     float dbp = 0.f;
     float* dkd = a.dkd + cm * (kChunk * kDim) + i * kDim + c0;
 #pragma unroll
-    for (int e4 = 0; e4 < 8; ++e4) {
+    for (int e4 = 0; e4 < 4; ++e4) {
       const uint2 w = *reinterpret_cast<const uint2*>(sm.u.p2.v + i * kLdB + c0 + 4 * e4);
       const float4 kd = *reinterpret_cast<const float4*>(sm.u.p2.kd + i * kLdR + c0 + 4 * e4);
       const float vv[4] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
@@ -438,35 +437,36 @@ __global__ __launch_bounds__(256) void kda_bwd_mats_kernel(KdaBwdArgs a) {
     if (i < L) {
       float* dvo = a.dv + ((size_t)(ci.tok0 + i) * H + h) * kDim + c0;
 #pragma unroll
-      for (int e4 = 0; e4 < 8; ++e4)
+      for (int e4 = 0; e4 < 4; ++e4)
         *reinterpret_cast<float4*>(dvo + 4 * e4) =
             make_float4(bi * tu[4 * e4], bi * tu[4 * e4 + 1], bi * tu[4 * e4 + 2], bi * tu[4 * e4 + 3]);
     }
     dbp += __shfl_xor(dbp, 1);
     dbp += __shfl_xor(dbp, 2);
-    if (q4 == 0) a.db1[cm * kChunk + i] = dbp;
+    dbp += __shfl_xor(dbp, 4);
+    if (q8 == 0) a.db1[cm * kChunk + i] = dbp;
   }
   __syncthreads();
 
   // ---- dA = (T^T dT T^T) on i > j: X = T^T dT (into the F area), then X T^T
   {
-    float acc[16];
+    float acc[8];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     for (int r = i; r < kChunk; ++r) {
       const float tv = sm.t[r * kLdM + i];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = fmaf(tv, sm.dt[r * kLdM + 16 * q4 + e], acc[e]);
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(tv, sm.dt[r * kLdM + 8 * q8 + e], acc[e]);
     }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sm.u.p2.f[i * kLdR + 16 * q4 + e] = acc[e];
+    for (int e = 0; e < 8; ++e) sm.u.p2.f[i * kLdR + 8 * q8 + e] = acc[e];
   }
   __syncthreads();
   {
     float* dA = a.da + cm * (kChunk * kChunk);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int j = 16 * q4 + e;
+    for (int e = 0; e < 8; ++e) {
+      const int j = 8 * q8 + e;
       float s = 0.f;
       if (i > j)
         for (int k2 = 0; k2 <= j; ++k2) s = fmaf(sm.u.p2.f[i * kLdR + k2], sm.t[j * kLdM + k2], s);
@@ -696,7 +696,7 @@ __global__ __launch_bounds__(512) void kda_bwd_gram_kernel(KdaBwdArgs a) {
 
 hipError_t launch_kda_bwd_chunks(const KdaBwdArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)((size_t)a.geo.NT * a.H);
-  hipLaunchKernelGGL(kda_bwd_mats_kernel, dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(kda_bwd_mats_kernel, dim3(grid), dim3(512), 0, stream, a);
   hipLaunchKernelGGL(kda_bwd_gram_kernel, dim3(grid), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
