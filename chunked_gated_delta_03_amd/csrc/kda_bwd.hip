@@ -67,49 +67,56 @@ __global__ __launch_bounds__(512) void kda_bwd_dh_kernel(KdaBwdArgs a) {
   for (int e = 0; e < 4; ++e)
     dS[e] = a.dsfinal ? a.dsfinal[sbase + (size_t)(4 * rg + e) * kDim + col0 + cc] : 0.0f;
 
-  for (int jc = si.nch - 1; jc >= 0; --jc) {
-    const int c = si.c0 + jc;
-    const size_t cm = (size_t)h * NT + c;
+  // one chunk's global operands, loaded into registers a chunk ahead:
+  // thread (row fi, channels fd0 .. fd0 + 15; stored T / Aqk positions
+  // 8 fq .. 8 fq + 7); rows past the end are zero
+  const int fi = tid >> 3, fd0 = (tid & 7) * 16, fq = tid & 7;
+  uint4 kr[2], qr[2], th, tl, av;
+  float4 gr[4], gl[4], decv;
+  float rkb, rk, srq, dov[2];
+  auto fetch = [&](int jc) {
+    const size_t cm = (size_t)h * NT + si.c0 + jc;
     const int tok0 = si.tok0 + jc * kChunk;
     const int rem = si.len - jc * kChunk;
     const int len = rem < kChunk ? rem : kChunk;
     const float* gk = a.gk + cm * (kChunk * kDim);
     const float* vec = a.vec + cm * (kVecRows * kChunk);
+    const bool valid = fi < len;
+    rkb = vec[1 * kChunk + fi];
+    rk = vec[2 * kChunk + fi];
+    srq = vec[3 * kChunk + fi];
+    const size_t roff = ((size_t)(tok0 + (valid ? fi : 0)) * a.H + h) * kDim + fd0;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      kr[p] = valid ? reinterpret_cast<const uint4*>(a.k + roff)[p] : make_uint4(0, 0, 0, 0);
+      qr[p] = valid ? reinterpret_cast<const uint4*>(a.q + roff)[p] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      gr[p] = reinterpret_cast<const float4*>(gk + fi * kDim + fd0)[p];
+      gl[p] = reinterpret_cast<const float4*>(gk + (kChunk - 1) * kDim + fd0)[p];
+    }
+    if (tid < kDim / 4) decv = reinterpret_cast<const float4*>(gk + (kChunk - 1) * kDim)[tid];
+    const uint16_t* tm = a.tmat + cm * (kChunk * 2 * kChunk) + fi * (2 * kChunk) + 8 * fq;
+    th = *reinterpret_cast<const uint4*>(tm);
+    tl = *reinterpret_cast<const uint4*>(tm + kChunk);
+    av = *reinterpret_cast<const uint4*>(a.aqk + cm * (kChunk * kChunk) + fi * kChunk + 8 * fq);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int idx = tid + 512 * e, ri = idx >> 4, cj = idx & 15;
+      dov[e] = ri < len ? bf2f(a.dout[((size_t)(tok0 + ri) * a.H + h) * kDim + col0 + cj]) : 0.0f;
+    }
+  };
+  if (si.nch > 0) fetch(si.nch - 1);
 
-    // operands: thread (row i, 16 channels from d0), all loads issued
-    // together as 16-byte pieces; rows past the end are zero
+  for (int jc = si.nch - 1; jc >= 0; --jc) {
+    const int c = si.c0 + jc;
+    const size_t cm = (size_t)h * NT + c;
+
+    // this chunk's operands from the registers into LDS, then the next
+    // chunk's loads go out
     {
-      const int i = tid >> 3, d0 = (tid & 7) * 16;
-      const bool valid = i < len;
-      const float rkb = vec[1 * kChunk + i], rk = vec[2 * kChunk + i], srq = vec[3 * kChunk + i];
-      const size_t roff = ((size_t)(tok0 + (valid ? i : 0)) * a.H + h) * kDim + d0;
-      uint4 kr[2], qr[2];
-      float4 gr[4], gl[4];
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        kr[p] = valid ? reinterpret_cast<const uint4*>(a.k + roff)[p] : make_uint4(0, 0, 0, 0);
-        qr[p] = valid ? reinterpret_cast<const uint4*>(a.q + roff)[p] : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        gr[p] = reinterpret_cast<const float4*>(gk + i * kDim + d0)[p];
-        gl[p] = reinterpret_cast<const float4*>(gk + (kChunk - 1) * kDim + d0)[p];
-      }
-      // T (hi + lo) and Aqk rows: thread (row r, stored positions 8 qq ..
-      // 8 qq + 7), scattered to their columns
-      const int r = tid >> 3, qq = tid & 7;
-      const uint16_t* tm = a.tmat + cm * (kChunk * 2 * kChunk) + r * (2 * kChunk) + 8 * qq;
-      const uint16_t* aq = a.aqk + cm * (kChunk * kChunk) + r * kChunk + 8 * qq;
-      const uint4 th = *reinterpret_cast<const uint4*>(tm);
-      const uint4 tl = *reinterpret_cast<const uint4*>(tm + kChunk);
-      const uint4 av = *reinterpret_cast<const uint4*>(aq);
-      float dov[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int idx = tid + 512 * e, ri = idx >> 4, cj = idx & 15;
-        dov[e] = ri < len ? bf2f(a.dout[((size_t)(tok0 + ri) * a.H + h) * kDim + col0 + cj]) : 0.0f;
-      }
-
+      const int i = fi, d0 = fd0;
       const uint32_t kw[8] = {kr[0].x, kr[0].y, kr[0].z, kr[0].w, kr[1].x, kr[1].y, kr[1].z, kr[1].w};
       const uint32_t qw[8] = {qr[0].x, qr[0].y, qr[0].z, qr[0].w, qr[1].x, qr[1].y, qr[1].z, qr[1].w};
 #pragma unroll
@@ -134,27 +141,27 @@ __global__ __launch_bounds__(512) void kda_bwd_dh_kernel(KdaBwdArgs a) {
         *reinterpret_cast<float4*>(sm.kdb + i * kLdO + d) = make_float4(kb4[0], kb4[1], kb4[2], kb4[3]);
       }
       if (tid < kDim / 4) {
-        const float4 l = reinterpret_cast<const float4*>(gk + (kChunk - 1) * kDim)[tid];
-        sm.dec[4 * tid + 0] = exp2_hw(l.x);
-        sm.dec[4 * tid + 1] = exp2_hw(l.y);
-        sm.dec[4 * tid + 2] = exp2_hw(l.z);
-        sm.dec[4 * tid + 3] = exp2_hw(l.w);
+        sm.dec[4 * tid + 0] = exp2_hw(decv.x);
+        sm.dec[4 * tid + 1] = exp2_hw(decv.y);
+        sm.dec[4 * tid + 2] = exp2_hw(decv.z);
+        sm.dec[4 * tid + 3] = exp2_hw(decv.w);
       }
       const uint32_t thw[4] = {th.x, th.y, th.z, th.w};
       const uint32_t tlw[4] = {tl.x, tl.y, tl.z, tl.w};
       const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int col = unperm_col(8 * qq + e);
+        const int col = unperm_col(8 * fq + e);
         const uint32_t hw = thw[e >> 1], lw = tlw[e >> 1], pw = aw[e >> 1];
         const float hv = __uint_as_float((e & 1) ? (hw & 0xFFFF0000u) : (hw << 16));
         const float lv = __uint_as_float((e & 1) ? (lw & 0xFFFF0000u) : (lw << 16));
-        sm.t[r * kLdM + col] = hv + lv;
-        sm.p[r * kLdM + col] = __uint_as_float((e & 1) ? (pw & 0xFFFF0000u) : (pw << 16));
+        sm.t[i * kLdM + col] = hv + lv;
+        sm.p[i * kLdM + col] = __uint_as_float((e & 1) ? (pw & 0xFFFF0000u) : (pw << 16));
       }
 #pragma unroll
       for (int e = 0; e < 2; ++e) sm.dO[tid + 512 * e] = dov[e];
     }
+    if (jc > 0) fetch(jc - 1);
     // dS before the update: the gradient w.r.t. the state leaving the chunk
     float* dhn = a.dhn + cm * (kDim * kDim);
 #pragma unroll
