@@ -17,12 +17,15 @@
 // WY inverse and Aqk the intra-chunk output matrix (scale rq rk included),
 // all from the KDA prepare kernel. Every exponent is <= 0.
 //
-// One workgroup per (sequence, head, 16 value columns), the eight of a
-// (sequence, head) dispatched to one XCD, fp32 arithmetic on
-// the vector units, 512 threads: the operands of a chunk are formed in LDS,
-// the 128 x 16 block of dS is held in registers (thread t: column t % 16,
-// rows 4 (t / 16) .. + 3). It stores, per chunk, dS before the update (the gradient w.r.t. the
-// state leaving the chunk) and dV', and the gradient w.r.t. the initial state.
+// One workgroup per (sequence, head, 32 value columns), the four of a
+// (sequence, head) dispatched to one XCD, fp32 arithmetic on the vector
+// units, 512 threads: the operands of a chunk are formed in LDS, the
+// 128 x 32 block of dS is held in registers (thread t: column t % 32, rows
+// 8 (t / 32) .. + 7). With 32 columns the grid is one workgroup per compute
+// unit for 64 (sequence, head) units, and the per-chunk operands are formed
+// by four workgroups per unit rather than eight. It stores, per chunk, dS
+// before the update (the gradient w.r.t. the state leaving the chunk) and
+// dV', and the gradient w.r.t. the initial state.
 #include "gdn_bwd.h"
 
 namespace gdn {
@@ -30,19 +33,21 @@ namespace gdn {
 namespace {
 
 constexpr int kLdO = kDim + 4;     // fp32 row stride of the 64 x 128 operands (16-byte rows)
-constexpr int kLdM = kChunk + 1;   // fp32 row stride of T and Aqk
-constexpr int kCols = 16;          // value columns per workgroup
+constexpr int kLdM = kChunk + 1;   // row stride of T (fp32) and Aqk (bf16)
+constexpr int kCols = 32;          // value columns per workgroup
 
 struct alignas(16) KdaDhSmem {
   float kg[kChunk * kLdO];
   float qd[kChunk * kLdO];
   float kdb[kChunk * kLdO];
   float t[kChunk * kLdM];
-  float p[kChunk * kLdM];
+  uint16_t p[kChunk * kLdM];         // Aqk, exact in bf16
   float dO[kChunk * kCols];
-  float ds[kDim * kCols];
+  union {
+    float ds[kDim * kCols];          // dS, read by the dV' products
+    float y[kChunk * kCols];         // then T^T dV'
+  } u;
   float dv[kChunk * kCols];
-  float y[kChunk * kCols];
   float dec[kDim];
 };
 
@@ -59,13 +64,13 @@ __global__ __launch_bounds__(512) void kda_bwd_dh_kernel(KdaBwdArgs a) {
   const int NT = a.geo.NT;
   const int col0 = vb * kCols;
 
-  // dS block: column cc, rows 4 rg .. 4 rg + 3
-  const int cc = tid & 15, rg = tid >> 4;
-  float dS[4];
+  // dS block: column cc, rows 8 rg .. 8 rg + 7
+  const int cc = tid & 31, rg = tid >> 5;
+  float dS[8];
   const size_t sbase = ((size_t)n * a.H + h) * kDim * kDim;
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    dS[e] = a.dsfinal ? a.dsfinal[sbase + (size_t)(4 * rg + e) * kDim + col0 + cc] : 0.0f;
+  for (int e = 0; e < 8; ++e)
+    dS[e] = a.dsfinal ? a.dsfinal[sbase + (size_t)(8 * rg + e) * kDim + col0 + cc] : 0.0f;
 
   // one chunk's global operands, loaded into registers a chunk ahead:
   // thread (row fi, channels fd0 .. fd0 + 15; stored T / Aqk positions
@@ -73,7 +78,7 @@ __global__ __launch_bounds__(512) void kda_bwd_dh_kernel(KdaBwdArgs a) {
   const int fi = tid >> 3, fd0 = (tid & 7) * 16, fq = tid & 7;
   uint4 kr[2], qr[2], th, tl, av;
   float4 gr[4], gl[4], decv;
-  float rkb, rk, srq, dov[2];
+  float rkb, rk, srq, dov[4];
   auto fetch = [&](int jc) {
     const size_t cm = (size_t)h * NT + si.c0 + jc;
     const int tok0 = si.tok0 + jc * kChunk;
@@ -102,8 +107,8 @@ __global__ __launch_bounds__(512) void kda_bwd_dh_kernel(KdaBwdArgs a) {
     tl = *reinterpret_cast<const uint4*>(tm + kChunk);
     av = *reinterpret_cast<const uint4*>(a.aqk + cm * (kChunk * kChunk) + fi * kChunk + 8 * fq);
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int idx = tid + 512 * e, ri = idx >> 4, cj = idx & 15;
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + 512 * e, ri = idx >> 5, cj = idx & 31;
       dov[e] = ri < len ? bf2f(a.dout[((size_t)(tok0 + ri) * a.H + h) * kDim + col0 + cj]) : 0.0f;
     }
   };
@@ -156,83 +161,93 @@ __global__ __launch_bounds__(512) void kda_bwd_dh_kernel(KdaBwdArgs a) {
         const float hv = __uint_as_float((e & 1) ? (hw & 0xFFFF0000u) : (hw << 16));
         const float lv = __uint_as_float((e & 1) ? (lw & 0xFFFF0000u) : (lw << 16));
         sm.t[i * kLdM + col] = hv + lv;
-        sm.p[i * kLdM + col] = __uint_as_float((e & 1) ? (pw & 0xFFFF0000u) : (pw << 16));
+        sm.p[i * kLdM + col] = (uint16_t)((e & 1) ? (pw >> 16) : (pw & 0xFFFFu));
       }
 #pragma unroll
-      for (int e = 0; e < 2; ++e) sm.dO[tid + 512 * e] = dov[e];
+      for (int e = 0; e < 4; ++e) sm.dO[tid + 512 * e] = dov[e];
     }
     if (jc > 0) fetch(jc - 1);
     // dS before the update: the gradient w.r.t. the state leaving the chunk
     float* dhn = a.dhn + cm * (kDim * kDim);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sm.ds[(4 * rg + e) * kCols + cc] = dS[e];
-      dhn[(size_t)(4 * rg + e) * kDim + col0 + cc] = dS[e];
+    for (int e = 0; e < 8; ++e) {
+      sm.u.ds[(8 * rg + e) * kCols + cc] = dS[e];
+      dhn[(size_t)(8 * rg + e) * kDim + col0 + cc] = dS[e];
     }
     __syncthreads();
 
-    // dV' = KG dS + Aqk^T dO: thread (row i, columns c2, c2 + 1)
+    // dV' = KG dS + Aqk^T dO: thread (row i, columns c4 .. c4 + 3)
     {
-      const int i = tid >> 3, c2 = (tid & 7) * 2;
-      float2 acc = make_float2(0.f, 0.f);
+      const int i = tid >> 3, c4 = (tid & 7) * 4;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int d = 0; d < kDim; d += 4) {
         const float4 kg4 = *reinterpret_cast<const float4*>(sm.kg + i * kLdO + d);
         const float kga[4] = {kg4.x, kg4.y, kg4.z, kg4.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float2 x = *reinterpret_cast<const float2*>(sm.ds + (d + q) * kCols + c2);
+          const float4 x = *reinterpret_cast<const float4*>(sm.u.ds + (d + q) * kCols + c4);
           acc.x = fmaf(kga[q], x.x, acc.x);
           acc.y = fmaf(kga[q], x.y, acc.y);
+          acc.z = fmaf(kga[q], x.z, acc.z);
+          acc.w = fmaf(kga[q], x.w, acc.w);
         }
       }
       for (int r = i; r < kChunk; ++r) {  // Aqk is lower triangular (with its diagonal)
-        const float pv = sm.p[r * kLdM + i];
-        const float2 x = *reinterpret_cast<const float2*>(sm.dO + r * kCols + c2);
+        const float pv = bf2f(sm.p[r * kLdM + i]);
+        const float4 x = *reinterpret_cast<const float4*>(sm.dO + r * kCols + c4);
         acc.x = fmaf(pv, x.x, acc.x);
         acc.y = fmaf(pv, x.y, acc.y);
+        acc.z = fmaf(pv, x.z, acc.z);
+        acc.w = fmaf(pv, x.w, acc.w);
       }
-      *reinterpret_cast<float2*>(sm.dv + i * kCols + c2) = acc;
-      *reinterpret_cast<float2*>(a.dvn + cm * (kChunk * kDim) + (size_t)i * kDim + col0 + c2) = acc;
+      *reinterpret_cast<float4*>(sm.dv + i * kCols + c4) = acc;
+      *reinterpret_cast<float4*>(a.dvn + cm * (kChunk * kDim) + (size_t)i * kDim + col0 + c4) = acc;
     }
     __syncthreads();
 
-    // Y = T^T dV' (T lower triangular): thread (row j, columns c2, c2 + 1)
+    // Y = T^T dV' (T lower triangular): thread (row j, columns c4 .. c4 + 3);
+    // Y takes the place of dS, whose readers are done
     {
-      const int j = tid >> 3, c2 = (tid & 7) * 2;
-      float2 acc = make_float2(0.f, 0.f);
+      const int j = tid >> 3, c4 = (tid & 7) * 4;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int i = j; i < kChunk; ++i) {
         const float tv = sm.t[i * kLdM + j];
-        const float2 x = *reinterpret_cast<const float2*>(sm.dv + i * kCols + c2);
+        const float4 x = *reinterpret_cast<const float4*>(sm.dv + i * kCols + c4);
         acc.x = fmaf(tv, x.x, acc.x);
         acc.y = fmaf(tv, x.y, acc.y);
+        acc.z = fmaf(tv, x.z, acc.z);
+        acc.w = fmaf(tv, x.w, acc.w);
       }
-      *reinterpret_cast<float2*>(sm.y + j * kCols + c2) = acc;
+      *reinterpret_cast<float4*>(sm.u.y + j * kCols + c4) = acc;
     }
     __syncthreads();
 
-    // dS <- diag(2^G_last) dS + QD^T dO - KDB^T Y (this thread's 4 rows)
+    // dS <- diag(2^G_last) dS + QD^T dO - KDB^T Y (this thread's 8 rows)
     {
-      float acc[4];
+      float acc[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = sm.dec[4 * rg + e] * dS[e];
+      for (int e = 0; e < 8; ++e) acc[e] = sm.dec[8 * rg + e] * dS[e];
 #pragma unroll 4
       for (int i = 0; i < kChunk; ++i) {
-        const float dov = sm.dO[i * kCols + cc], yv = sm.y[i * kCols + cc];
-        const float4 q0 = *reinterpret_cast<const float4*>(sm.qd + i * kLdO + 4 * rg);
-        const float4 k0 = *reinterpret_cast<const float4*>(sm.kdb + i * kLdO + 4 * rg);
-        acc[0] = fmaf(q0.x, dov, fmaf(-k0.x, yv, acc[0]));
-        acc[1] = fmaf(q0.y, dov, fmaf(-k0.y, yv, acc[1]));
-        acc[2] = fmaf(q0.z, dov, fmaf(-k0.z, yv, acc[2]));
-        acc[3] = fmaf(q0.w, dov, fmaf(-k0.w, yv, acc[3]));
+        const float dov = sm.dO[i * kCols + cc], yv = sm.u.y[i * kCols + cc];
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq) {
+          const float4 q0 = *reinterpret_cast<const float4*>(sm.qd + i * kLdO + 8 * rg + 4 * hq);
+          const float4 k0 = *reinterpret_cast<const float4*>(sm.kdb + i * kLdO + 8 * rg + 4 * hq);
+          acc[4 * hq + 0] = fmaf(q0.x, dov, fmaf(-k0.x, yv, acc[4 * hq + 0]));
+          acc[4 * hq + 1] = fmaf(q0.y, dov, fmaf(-k0.y, yv, acc[4 * hq + 1]));
+          acc[4 * hq + 2] = fmaf(q0.z, dov, fmaf(-k0.z, yv, acc[4 * hq + 2]));
+          acc[4 * hq + 3] = fmaf(q0.w, dov, fmaf(-k0.w, yv, acc[4 * hq + 3]));
+        }
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dS[e] = acc[e];
+      for (int e = 0; e < 8; ++e) dS[e] = acc[e];
     }
     __syncthreads();  // the next chunk rewrites the operands
   }
   if (a.ds0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) a.ds0[sbase + (size_t)(4 * rg + e) * kDim + col0 + cc] = dS[e];
+    for (int e = 0; e < 8; ++e) a.ds0[sbase + (size_t)(8 * rg + e) * kDim + col0 + cc] = dS[e];
   }
 }
 
