@@ -323,6 +323,23 @@ __device__ __forceinline__ void load_t(float* dst, const uint16_t* tm, int tid) 
   }
 }
 
+// acc += the 16 x 16 tile (rows r0.., columns c0..) of A B^T over a
+// contraction of 16 indices from k0, on v_mfma_f32_16x16x4f32 (exact fp32
+// products, fp32 accumulation): A and B are fp32 rows in LDS (row stride
+// kLdR, contraction index contiguous). Lane (g, l) takes contraction slots
+// k0 + 4g .. k0 + 4g + 3, one per MFMA step, so each operand is one 16-byte
+// read; it ends with C[r0 + 4g + e][c0 + l] in acc[e].
+__device__ __forceinline__ f32x4 mma_rows(const float* A, const float* B, int r0, int c0, int k0, int l, int g,
+                                          f32x4 acc) {
+  const float4 x = *reinterpret_cast<const float4*>(A + (r0 + l) * kLdR + k0 + 4 * g);
+  const float4 y = *reinterpret_cast<const float4*>(B + (c0 + l) * kLdR + k0 + 4 * g);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.x, y.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.y, y.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.z, y.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.w, y.w, acc, 0, 0, 0);
+  return acc;
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(512) void kda_bwd_mats_kernel(KdaBwdArgs a) {
@@ -336,6 +353,10 @@ __global__ __launch_bounds__(512) void kda_bwd_mats_kernel(KdaBwdArgs a) {
   const size_t plane = (size_t)H * NT * kChunk * kDim;
   const float* vec = a.vec + cm * (kVecRows * kChunk);
   const int i = tid >> 3, q8 = tid & 7;   // row i; 8 columns from 8 q8 (64-wide) or 16 from 16 q8
+  // the 64 x 64 products on the matrix unit: wave w takes the 16 x 16 tiles
+  // (row block w % 4, column blocks 2 (w / 4) and 2 (w / 4) + 1)
+  const int lane = tid & 63, ml = lane & 15, mg = lane >> 4;
+  const int mrt = (tid >> 6) & 3, mct = 2 * (tid >> 8);
 
   // ---- dP = scale (dO V'^T), i >= j
   {
@@ -354,23 +375,21 @@ __global__ __launch_bounds__(512) void kda_bwd_mats_kernel(KdaBwdArgs a) {
     load_t(sm.t, a.tmat + cm * (kChunk * 2 * kChunk), tid);
     if (tid < kChunk) sm.b[tid] = vec[tid];
     __syncthreads();
-    float acc[8];
+    // tiles above the diagonal are zero (a wave-uniform skip)
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int k0 = 0; k0 < kDim; k0 += 16) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int v4 = 0; v4 < kDim; v4 += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(sm.u.p1.dO + i * kLdR + v4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float4 y = *reinterpret_cast<const float4*>(sm.u.p1.vp + (8 * q8 + e) * kLdR + v4);
-        acc[e] = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, acc[e]))));
-      }
+      for (int t = 0; t < 2; ++t)
+        if (mct + t <= mrt) acc[t] = mma_rows(sm.u.p1.dO, sm.u.p1.vp, 16 * mrt, 16 * (mct + t), k0, ml, mg, acc[t]);
     }
     float* dP = a.dp + cm * (kChunk * kChunk);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = 8 * q8 + e;
-      dP[i * kChunk + j] = i >= j ? a.scale * acc[e] : 0.0f;
-    }
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ii = 16 * mrt + 4 * mg + e, j = 16 * (mct + t) + ml;
+        dP[ii * kChunk + j] = ii >= j ? a.scale * acc[t][e] : 0.0f;
+      }
     __syncthreads();
   }
 
@@ -399,28 +418,28 @@ __global__ __launch_bounds__(512) void kda_bwd_mats_kernel(KdaBwdArgs a) {
       *reinterpret_cast<uint2*>(sm.u.p2.v + r * kLdB + c4) = vv;
     }
     __syncthreads();
-    float acc[8];
+    // dV' v^T and F KD^T, tile by tile; v is exact in bf16
+    f32x4 au[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 aw[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int k0 = 0; k0 < kDim; k0 += 16) {
+      const float4 x = *reinterpret_cast<const float4*>(sm.u.p2.dv + (16 * mrt + ml) * kLdR + k0 + 4 * mg);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int c4 = 0; c4 < kDim; c4 += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(sm.u.p2.dv + i * kLdR + c4);
-      const float4 f = *reinterpret_cast<const float4*>(sm.u.p2.f + i * kLdR + c4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 8 * q8 + e;
-        const uint2 w = *reinterpret_cast<const uint2*>(sm.u.p2.v + j * kLdB + c4);
-        const float4 kd = *reinterpret_cast<const float4*>(sm.u.p2.kd + j * kLdR + c4);
-        float s = acc[e];
-        s = fmaf(x.x, __uint_as_float(w.x << 16), s);
-        s = fmaf(x.y, __uint_as_float(w.x & 0xFFFF0000u), s);
-        s = fmaf(x.z, __uint_as_float(w.y << 16), s);
-        s = fmaf(x.w, __uint_as_float(w.y & 0xFFFF0000u), s);
-        s = fmaf(-f.x, kd.x, fmaf(-f.y, kd.y, fmaf(-f.z, kd.z, fmaf(-f.w, kd.w, s))));
-        acc[e] = s;
+      for (int t = 0; t < 2; ++t) {
+        const uint2 wv = *reinterpret_cast<const uint2*>(sm.u.p2.v + (16 * (mct + t) + ml) * kLdB + k0 + 4 * mg);
+        au[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.x, __uint_as_float(wv.x << 16), au[t], 0, 0, 0);
+        au[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.y, __uint_as_float(wv.x & 0xFFFF0000u), au[t], 0, 0, 0);
+        au[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.z, __uint_as_float(wv.y << 16), au[t], 0, 0, 0);
+        au[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.w, __uint_as_float(wv.y & 0xFFFF0000u), au[t], 0, 0, 0);
+        aw[t] = mma_rows(sm.u.p2.f, sm.u.p2.kd, 16 * mrt, 16 * (mct + t), k0, ml, mg, aw[t]);
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sm.dt[i * kLdM + 8 * q8 + e] = sm.b[8 * q8 + e] * acc[e];
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ii = 16 * mrt + 4 * mg + e, j = 16 * (mct + t) + ml;
+        sm.dt[ii * kLdM + j] = sm.b[j] * (au[t][e] - aw[t][e]);
+      }
   }
 
   // ---- tU = T^T dV', tW = -T^T F: dv = b tU, db1 = rowsum(tU v + tW KD), dKD = b tW
