@@ -290,6 +290,7 @@ struct alignas(16) MatsSmem {
   float t[kChunk * kLdM];
   float dt[kChunk * kLdM];
   float b[kChunk];
+  float red[8][kChunk];          // per-wave partial row sums of d beta
 };
 
 __device__ __forceinline__ void chunk_of(const Geometry& geo, int bx, int H, int& c, int& h, ChunkInfo& ci) {
@@ -442,52 +443,65 @@ __global__ __launch_bounds__(512) void kda_bwd_mats_kernel(KdaBwdArgs a) {
       }
   }
 
-  // ---- tU = T^T dV', tW = -T^T F: dv = b tU, db1 = rowsum(tU v + tW KD), dKD = b tW
+  // ---- tU = T^T dV', tW = -T^T F: dv = b tU, db1 = rowsum(tU v + tW KD), dKD = b tW.
+  // On the matrix unit: wave w takes value columns 16 w .. 16 w + 15 and
+  // every row block; T is lower triangular, so row block rt takes the
+  // contraction blocks kb >= rt, masked (r >= i) inside the diagonal block.
   {
-    float tu[16], tw[16];
+    const int mw = tid >> 6, cc = 16 * mw + ml;
+    f32x4 tu[4], tw[4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) { tu[e] = 0.f; tw[e] = 0.f; }
-    const int c0 = 16 * q8;
-    for (int r = i; r < kChunk; ++r) {
-      const float tv = sm.t[r * kLdM + i];
+    for (int rt = 0; rt < 4; ++rt) {
+      tu[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      tw[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const float4 x = *reinterpret_cast<const float4*>(sm.u.p2.dv + r * kLdR + c0 + 4 * e4);
-        const float4 f = *reinterpret_cast<const float4*>(sm.u.p2.f + r * kLdR + c0 + 4 * e4);
-        tu[4 * e4 + 0] = fmaf(tv, x.x, tu[4 * e4 + 0]); tu[4 * e4 + 1] = fmaf(tv, x.y, tu[4 * e4 + 1]);
-        tu[4 * e4 + 2] = fmaf(tv, x.z, tu[4 * e4 + 2]); tu[4 * e4 + 3] = fmaf(tv, x.w, tu[4 * e4 + 3]);
-        tw[4 * e4 + 0] = fmaf(-tv, f.x, tw[4 * e4 + 0]); tw[4 * e4 + 1] = fmaf(-tv, f.y, tw[4 * e4 + 1]);
-        tw[4 * e4 + 2] = fmaf(-tv, f.z, tw[4 * e4 + 2]); tw[4 * e4 + 3] = fmaf(-tv, f.w, tw[4 * e4 + 3]);
+    for (int kb = 0; kb < 4; ++kb) {
+      float bu[4], bw[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int r = 16 * kb + 4 * mg + ks;
+        bu[ks] = sm.u.p2.dv[r * kLdR + cc];
+        bw[ks] = sm.u.p2.f[r * kLdR + cc];
+      }
+#pragma unroll
+      for (int rt = 0; rt <= kb; ++rt) {
+        const int ii = 16 * rt + ml;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int r = 16 * kb + 4 * mg + ks;
+          float tv = sm.t[r * kLdM + ii];
+          if (rt == kb) tv = r >= ii ? tv : 0.0f;
+          tu[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(tv, bu[ks], tu[rt], 0, 0, 0);
+          tw[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(-tv, bw[ks], tw[rt], 0, 0, 0);
+        }
       }
     }
-    const float bi = sm.b[i];
-    float dbp = 0.f;
-    float* dkd = a.dkd + cm * (kChunk * kDim) + i * kDim + c0;
+    float* dkd = a.dkd + cm * (kChunk * kDim);
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const uint2 w = *reinterpret_cast<const uint2*>(sm.u.p2.v + i * kLdB + c0 + 4 * e4);
-      const float4 kd = *reinterpret_cast<const float4*>(sm.u.p2.kd + i * kLdR + c0 + 4 * e4);
-      const float vv[4] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
-                           __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
-      const float kk[4] = {kd.x, kd.y, kd.z, kd.w};
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dbp = fmaf(tu[4 * e4 + e], vv[e], fmaf(tw[4 * e4 + e], kk[e], dbp));
-      *reinterpret_cast<float4*>(dkd + 4 * e4) =
-          make_float4(bi * tw[4 * e4], bi * tw[4 * e4 + 1], bi * tw[4 * e4 + 2], bi * tw[4 * e4 + 3]);
-    }
-    if (i < L) {
-      float* dvo = a.dv + ((size_t)(ci.tok0 + i) * H + h) * kDim + c0;
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4)
-        *reinterpret_cast<float4*>(dvo + 4 * e4) =
-            make_float4(bi * tu[4 * e4], bi * tu[4 * e4 + 1], bi * tu[4 * e4 + 2], bi * tu[4 * e4 + 3]);
-    }
-    dbp += __shfl_xor(dbp, 1);
-    dbp += __shfl_xor(dbp, 2);
-    dbp += __shfl_xor(dbp, 4);
-    if (q8 == 0) a.db1[cm * kChunk + i] = dbp;
+      for (int e = 0; e < 4; ++e) {
+        const int ii = 16 * rt + 4 * mg + e;
+        const float bi = sm.b[ii];
+        const float vv = bf2f(sm.u.p2.v[ii * kLdB + cc]);
+        float part = fmaf(tu[rt][e], vv, tw[rt][e] * sm.u.p2.kd[ii * kLdR + cc]);
+        part += __shfl_xor(part, 1);
+        part += __shfl_xor(part, 2);
+        part += __shfl_xor(part, 4);
+        part += __shfl_xor(part, 8);
+        if (ml == 0) sm.red[mw][ii] = part;
+        dkd[ii * kDim + cc] = bi * tw[rt][e];
+        if (ii < L) a.dv[((size_t)(ci.tok0 + ii) * H + h) * kDim + cc] = bi * tu[rt][e];
+      }
   }
   __syncthreads();
+  if (tid < kChunk) {
+    float s = 0.f;
+#pragma unroll
+    for (int w8 = 0; w8 < 8; ++w8) s += sm.red[w8][tid];
+    a.db1[cm * kChunk + tid] = s;
+  }
 
   // ---- dA = (T^T dT T^T) on i > j: X = T^T dT (into the F area), then X T^T
   {
