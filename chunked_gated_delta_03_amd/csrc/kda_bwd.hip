@@ -503,29 +503,75 @@ __global__ __launch_bounds__(512) void kda_bwd_mats_kernel(KdaBwdArgs a) {
     a.db1[cm * kChunk + tid] = s;
   }
 
-  // ---- dA = (T^T dT T^T) on i > j: X = T^T dT (into the F area), then X T^T
+  // ---- dA = (T^T dT T^T) on i > j: X = T^T dT (into the F area), then
+  // X T^T, both on the matrix unit. X: wave w takes column block w % 4 and
+  // row blocks {0, 3} or {1, 2} (equal contraction lengths, T lower
+  // triangular, masked r >= i inside the diagonal block).
   {
-    float acc[8];
+    const int xct = (tid >> 6) & 3, xsel = tid >> 8;
+    f32x4 xa[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int r = i; r < kChunk; ++r) {
-      const float tv = sm.t[r * kLdM + i];
+    for (int kb = 0; kb < 4; ++kb) {
+      float bx[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(tv, sm.dt[r * kLdM + 8 * q8 + e], acc[e]);
+      for (int ks = 0; ks < 4; ++ks) bx[ks] = sm.dt[(16 * kb + 4 * mg + ks) * kLdM + 16 * xct + ml];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int rt = q == 0 ? xsel : 3 - xsel;
+        if (kb < rt) continue;
+        const int ii = 16 * rt + ml;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int r = 16 * kb + 4 * mg + ks;
+          float tv = sm.t[r * kLdM + ii];
+          if (kb == rt) tv = r >= ii ? tv : 0.0f;
+          xa[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(tv, bx[ks], xa[q], 0, 0, 0);
+        }
+      }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sm.u.p2.f[i * kLdR + 8 * q8 + e] = acc[e];
+    for (int q = 0; q < 2; ++q) {
+      const int rt = q == 0 ? xsel : 3 - xsel;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.u.p2.f[(16 * rt + 4 * mg + e) * kLdR + 16 * xct + ml] = xa[q][e];
+    }
   }
   __syncthreads();
   {
+    // dA tile (rt, ct) = X T^T over k2 <= j, i.e. contraction blocks
+    // kb <= ct, masked inside the diagonal one; tiles above the diagonal are
+    // zero. Tiles per wave (row block, column block; -1: none), balanced at
+    // four contraction blocks per computing wave.
+    constexpr signed char kTr[8][3] = {{3, -1, -1}, {2, 0, -1}, {3, 1, -1}, {1, 2, -1},
+                                       {3, 2, 3},   {0, 0, -1}, {0, 1, -1}, {1, 2, -1}};
+    constexpr signed char kTc[8][3] = {{3, -1, -1}, {2, 0, -1}, {2, 0, -1}, {1, 1, -1},
+                                       {1, 0, 0},   {1, 2, -1}, {3, 2, -1}, {3, 3, -1}};
+    const int mw = __builtin_amdgcn_readfirstlane(tid >> 6);
     float* dA = a.da + cm * (kChunk * kChunk);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = 8 * q8 + e;
-      float s = 0.f;
-      if (i > j)
-        for (int k2 = 0; k2 <= j; ++k2) s = fmaf(sm.u.p2.f[i * kLdR + k2], sm.t[j * kLdM + k2], s);
-      dA[i * kChunk + j] = s;
+    for (int sl = 0; sl < 3; ++sl) {
+      const int rt = kTr[mw][sl], ct = kTc[mw][sl];
+      if (rt < 0) continue;
+      const int jj = 16 * ct + ml;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (rt >= ct) {
+        for (int kb = 0; kb <= ct; ++kb) {
+          const float4 xv = *reinterpret_cast<const float4*>(sm.u.p2.f + (16 * rt + ml) * kLdR + 16 * kb + 4 * mg);
+          const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const int k2 = 16 * kb + 4 * mg + ks;
+            float tb = sm.t[jj * kLdM + k2];
+            if (kb == ct) tb = k2 <= jj ? tb : 0.0f;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xs[ks], tb, acc, 0, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ii = 16 * rt + 4 * mg + e;
+        dA[ii * kChunk + jj] = ii > jj ? acc[e] : 0.0f;
+      }
     }
   }
 }
