@@ -18,10 +18,12 @@
 // all from the KDA prepare kernel. Every exponent is <= 0.
 //
 // One workgroup per (sequence, head, 32 value columns), the four of a
-// (sequence, head) dispatched to one XCD, fp32 arithmetic on the vector
-// units, 512 threads: the operands of a chunk are formed in LDS, the
-// 128 x 32 block of dS is held in registers (thread t: column t % 32, rows
-// 8 (t / 32) .. + 7). With 32 columns the grid is one workgroup per compute
+// (sequence, head) dispatched to one XCD, 512 threads: the operands of a
+// chunk are formed in LDS (fp32), the products run on v_mfma_f32_16x16x4f32
+// (exact fp32 operands, fp32 accumulation) in 16 x 16 tiles, and the
+// 128 x 32 block of dS is held in registers in that instruction's
+// accumulator layout (wave w: rows 16 w .. 16 w + 15; lane (g, l): rows
+// 16 w + 4 g + e, columns l and 16 + l). With 32 columns the grid is one workgroup per compute
 // unit for 64 (sequence, head) units, and the per-chunk operands are formed
 // by four workgroups per unit rather than eight. It stores, per chunk, dS
 // before the update (the gradient w.r.t. the state leaving the chunk) and
@@ -35,6 +37,8 @@ namespace {
 constexpr int kLdO = kDim + 4;     // fp32 row stride of the 64 x 128 operands (16-byte rows)
 constexpr int kLdM = kChunk + 1;   // row stride of T (fp32) and Aqk (bf16)
 constexpr int kCols = 32;          // value columns per workgroup
+constexpr int kLdC = kCols + 4;    // fp32 row stride of the 32-column arrays: rows 4 apart
+                                   // (the four lane groups of an MFMA operand) on distinct banks
 
 struct alignas(16) KdaDhSmem {
   float kg[kChunk * kLdO];
@@ -42,12 +46,12 @@ struct alignas(16) KdaDhSmem {
   float kdb[kChunk * kLdO];
   float t[kChunk * kLdM];
   uint16_t p[kChunk * kLdM];         // Aqk, exact in bf16
-  float dO[kChunk * kCols];
+  float dO[kChunk * kLdC];
   union {
-    float ds[kDim * kCols];          // dS, read by the dV' products
-    float y[kChunk * kCols];         // then T^T dV'
+    float ds[kDim * kLdC];           // dS, read by the dV' products
+    float y[kChunk * kLdC];          // then T^T dV'
   } u;
-  float dv[kChunk * kCols];
+  float dv[kChunk * kLdC];
   float dec[kDim];
 };
 
@@ -64,13 +68,17 @@ __global__ __launch_bounds__(512) void kda_bwd_dh_kernel(KdaBwdArgs a) {
   const int NT = a.geo.NT;
   const int col0 = vb * kCols;
 
-  // dS block: column cc, rows 8 rg .. 8 rg + 7
-  const int cc = tid & 31, rg = tid >> 5;
-  float dS[8];
+  // dS block in the accumulator layout: dS[ct][e] is row 16 w + 4 g + e,
+  // column 16 ct + l of the block
+  const int lane = tid & 63, l = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  f32x4 dS[2];
   const size_t sbase = ((size_t)n * a.H + h) * kDim * kDim;
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    dS[e] = a.dsfinal ? a.dsfinal[sbase + (size_t)(8 * rg + e) * kDim + col0 + cc] : 0.0f;
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dS[ct][e] = a.dsfinal ? a.dsfinal[sbase + (size_t)(16 * w + 4 * g + e) * kDim + col0 + 16 * ct + l] : 0.0f;
 
   // one chunk's global operands, loaded into registers a chunk ahead:
   // thread (row fi, channels fd0 .. fd0 + 15; stored T / Aqk positions
@@ -164,90 +172,109 @@ __global__ __launch_bounds__(512) void kda_bwd_dh_kernel(KdaBwdArgs a) {
         sm.p[i * kLdM + col] = (uint16_t)((e & 1) ? (pw >> 16) : (pw & 0xFFFFu));
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.dO[tid + 512 * e] = dov[e];
+      for (int e = 0; e < 4; ++e) {
+        const int idx = tid + 512 * e;
+        sm.dO[(idx >> 5) * kLdC + (idx & 31)] = dov[e];
+      }
     }
     if (jc > 0) fetch(jc - 1);
     // dS before the update: the gradient w.r.t. the state leaving the chunk
     float* dhn = a.dhn + cm * (kDim * kDim);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sm.u.ds[(8 * rg + e) * kCols + cc] = dS[e];
-      dhn[(size_t)(8 * rg + e) * kDim + col0 + cc] = dS[e];
-    }
-    __syncthreads();
-
-    // dV' = KG dS + Aqk^T dO: thread (row i, columns c4 .. c4 + 3)
-    {
-      const int i = tid >> 3, c4 = (tid & 7) * 4;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int d = 0; d < kDim; d += 4) {
-        const float4 kg4 = *reinterpret_cast<const float4*>(sm.kg + i * kLdO + d);
-        const float kga[4] = {kg4.x, kg4.y, kg4.z, kg4.w};
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 x = *reinterpret_cast<const float4*>(sm.u.ds + (d + q) * kCols + c4);
-          acc.x = fmaf(kga[q], x.x, acc.x);
-          acc.y = fmaf(kga[q], x.y, acc.y);
-          acc.z = fmaf(kga[q], x.z, acc.z);
-          acc.w = fmaf(kga[q], x.w, acc.w);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * w + 4 * g + e, col = 16 * ct + l;
+        sm.u.ds[row * kLdC + col] = dS[ct][e];
+        dhn[(size_t)row * kDim + col0 + col] = dS[ct][e];
       }
-      for (int r = i; r < kChunk; ++r) {  // Aqk is lower triangular (with its diagonal)
-        const float pv = bf2f(sm.p[r * kLdM + i]);
-        const float4 x = *reinterpret_cast<const float4*>(sm.dO + r * kCols + c4);
-        acc.x = fmaf(pv, x.x, acc.x);
-        acc.y = fmaf(pv, x.y, acc.y);
-        acc.z = fmaf(pv, x.z, acc.z);
-        acc.w = fmaf(pv, x.w, acc.w);
-      }
-      *reinterpret_cast<float4*>(sm.dv + i * kCols + c4) = acc;
-      *reinterpret_cast<float4*>(a.dvn + cm * (kChunk * kDim) + (size_t)i * kDim + col0 + c4) = acc;
-    }
     __syncthreads();
 
-    // Y = T^T dV' (T lower triangular): thread (row j, columns c4 .. c4 + 3);
-    // Y takes the place of dS, whose readers are done
-    {
-      const int j = tid >> 3, c4 = (tid & 7) * 4;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int i = j; i < kChunk; ++i) {
-        const float tv = sm.t[i * kLdM + j];
-        const float4 x = *reinterpret_cast<const float4*>(sm.dv + i * kCols + c4);
-        acc.x = fmaf(tv, x.x, acc.x);
-        acc.y = fmaf(tv, x.y, acc.y);
-        acc.z = fmaf(tv, x.z, acc.z);
-        acc.w = fmaf(tv, x.w, acc.w);
-      }
-      *reinterpret_cast<float4*>(sm.u.y + j * kCols + c4) = acc;
-    }
-    __syncthreads();
+    // Wave w's 16 x 16 tile of the 64 x 32 results below: row block w % 4,
+    // column block w / 4. Lane (g, l) supplies contraction slots
+    // k0 + 4 g + ks (one per MFMA step) of its operand row or column.
+    const int rt = w & 3, ctl = w >> 2;
+    const int ia = 16 * rt + l, cb = 16 * ctl + l;
 
-    // dS <- diag(2^G_last) dS + QD^T dO - KDB^T Y (this thread's 8 rows)
+    // dV' = KG dS + Aqk^T dO (Aqk lower triangular with its diagonal:
+    // contraction blocks kb >= rt, masked r >= i in the diagonal one)
     {
-      float acc[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = sm.dec[8 * rg + e] * dS[e];
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-      for (int i = 0; i < kChunk; ++i) {
-        const float dov = sm.dO[i * kCols + cc], yv = sm.u.y[i * kCols + cc];
+      for (int k0 = 0; k0 < kDim; k0 += 16) {
+        const float4 av = *reinterpret_cast<const float4*>(sm.kg + ia * kLdO + k0 + 4 * g);
+        const float ava[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
-        for (int hq = 0; hq < 2; ++hq) {
-          const float4 q0 = *reinterpret_cast<const float4*>(sm.qd + i * kLdO + 8 * rg + 4 * hq);
-          const float4 k0 = *reinterpret_cast<const float4*>(sm.kdb + i * kLdO + 8 * rg + 4 * hq);
-          acc[4 * hq + 0] = fmaf(q0.x, dov, fmaf(-k0.x, yv, acc[4 * hq + 0]));
-          acc[4 * hq + 1] = fmaf(q0.y, dov, fmaf(-k0.y, yv, acc[4 * hq + 1]));
-          acc[4 * hq + 2] = fmaf(q0.z, dov, fmaf(-k0.z, yv, acc[4 * hq + 2]));
-          acc[4 * hq + 3] = fmaf(q0.w, dov, fmaf(-k0.w, yv, acc[4 * hq + 3]));
+        for (int ks = 0; ks < 4; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ava[ks], sm.u.ds[(k0 + 4 * g + ks) * kLdC + cb], acc, 0, 0, 0);
+      }
+      for (int kb = rt; kb < 4; ++kb) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int r = 16 * kb + 4 * g + ks;
+          float pv = bf2f(sm.p[r * kLdM + ia]);
+          if (kb == rt) pv = r >= ia ? pv : 0.0f;
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, sm.dO[r * kLdC + cb], acc, 0, 0, 0);
         }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dS[e] = acc[e];
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * rt + 4 * g + e;
+        sm.dv[row * kLdC + cb] = acc[e];
+        a.dvn[cm * (kChunk * kDim) + (size_t)row * kDim + col0 + cb] = acc[e];
+      }
+    }
+    __syncthreads();
+
+    // Y = T^T dV' (T lower triangular: blocks kb >= rt, masked i >= j in the
+    // diagonal one); Y takes the place of dS, whose readers are done
+    {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = rt; kb < 4; ++kb) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int i = 16 * kb + 4 * g + ks;
+          float tv = sm.t[i * kLdM + ia];
+          if (kb == rt) tv = i >= ia ? tv : 0.0f;
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tv, sm.dv[i * kLdC + cb], acc, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.u.y[(16 * rt + 4 * g + e) * kLdC + cb] = acc[e];
+    }
+    __syncthreads();
+
+    // dS <- diag(2^G_last) dS + QD^T dO - KDB^T Y (wave w: rows 16 w ..)
+    {
+      f32x4 acc[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[ct][e] = sm.dec[16 * w + 4 * g + e] * dS[ct][e];
+      const int d = 16 * w + l;
+#pragma unroll 2
+      for (int k0 = 0; k0 < kChunk; k0 += 16) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int i = k0 + 4 * g + ks;
+          const float qa = sm.qd[i * kLdO + d], ka = -sm.kdb[i * kLdO + d];
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa, sm.dO[i * kLdC + 16 * ct + l], acc[ct], 0, 0, 0);
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, sm.u.y[i * kLdC + 16 * ct + l], acc[ct], 0, 0, 0);
+          }
+        }
+      }
+      dS[0] = acc[0];
+      dS[1] = acc[1];
     }
     __syncthreads();  // the next chunk rewrites the operands
   }
   if (a.ds0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a.ds0[sbase + (size_t)(8 * rg + e) * kDim + col0 + cc] = dS[e];
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a.ds0[sbase + (size_t)(16 * w + 4 * g + e) * kDim + col0 + 16 * ct + l] = dS[ct][e];
   }
 }
 
