@@ -614,6 +614,7 @@ struct alignas(16) GramSmem {
   float dp[kChunk * kLdM];
   float b[kChunk];
   float dgl[kDim];
+  float stg[3][16 * kLdR];    // one row block's R1, R2, C1 (pairs across row blocks)
 };
 
 }  // namespace
@@ -676,9 +677,10 @@ __global__ __launch_bounds__(512) void kda_bwd_gram_kernel(KdaBwdArgs a) {
   for (int e = 0; e < 16; ++e) { dkn[e] = 0.f; dqn[e] = 0.f; dG[e] = 0.f; }
   float dbp = 0.f;   // sum_j dA[r,j] sum_d k^_rd k^_jd 2^(G_rd - G_jd) over this thread's channels
 
-  // row r as the later row i: j <= r
+  // Pairs inside row r's 16-row block here; pairs across blocks on the
+  // matrix unit below. Row r as the later row i: j <= r
   const float br = sm.b[r];
-  for (int j = 0; j <= r; ++j) {
+  for (int j = r & ~15; j <= r; ++j) {
     const float dAr = j < r ? sm.da[r * kLdM + j] : 0.0f;
     const float wa = -br * dAr, dp = sm.dp[r * kLdM + j];
 #pragma unroll
@@ -699,7 +701,7 @@ __global__ __launch_bounds__(512) void kda_bwd_gram_kernel(KdaBwdArgs a) {
     }
   }
   // row r as the earlier row j: i >= r
-  for (int i2 = r; i2 < kChunk; ++i2) {
+  for (int i2 = r; i2 <= (r | 15); ++i2) {
     const float wa = i2 > r ? -sm.b[i2] * sm.da[i2 * kLdM + r] : 0.0f;
     const float dp = sm.dp[i2 * kLdM + r];
 #pragma unroll
@@ -717,6 +719,91 @@ __global__ __launch_bounds__(512) void kda_bwd_gram_kernel(KdaBwdArgs a) {
         dkn[d] += s;
         dG[d] = fmaf(-s, knr[d], dG[d]);
       }
+    }
+  }
+
+  // Pairs (i, j) in different 16-row blocks, on v_mfma_f32_16x16x4f32, one
+  // row block per round (wave w: channels 16 w .. 16 w + 15). Each decay is
+  // split at a reference row between the two blocks, both factors <= 1:
+  //   row side of block I (j < 16 I <= i): 2^(G_i - G_j) =
+  //     2^(G_i - G_16I) 2^(G_16I - G_j), giving
+  //     R1[i] = sum_j dA[i,j] k^_j 2^(..),  R2[i] = sum_j dP[i,j] k^_j 2^(..);
+  //   column side of block J (j < rho = 16 (J + 1) <= i): 2^(G_i - G_j) =
+  //     2^(G_i - G_rho) 2^(G_rho - G_j), giving
+  //     C1[j] = sum_i (wA[i,j] k^_i + dP[i,j] q^_i) 2^(..), wA = -b_i dA[i,j].
+  // The rows of the round's block then add them to their sums as the
+  // in-block loops above do per pair.
+  {
+    const int lane = tid & 63, ml = lane & 15, mg = lane >> 4;
+    const int dch = 16 * (tid >> 6) + ml;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      f32x4 r1 = f32x4{0.f, 0.f, 0.f, 0.f}, r2 = r1, c1 = r1;
+      if (I >= 1) {
+        const float gref = sm.g[16 * I * kLdR + dch];
+        const int i = 16 * I + ml;
+        for (int k0 = 0; k0 < 16 * I; k0 += 16) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const int j = k0 + 4 * mg + ks;
+            const float bv = sm.kn[j * kLdR + dch] * exp2_hw(gref - sm.g[j * kLdR + dch]);
+            r1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.da[i * kLdM + j], bv, r1, 0, 0, 0);
+            r2 = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.dp[i * kLdM + j], bv, r2, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float as = exp2_hw(sm.g[(16 * I + 4 * mg + e) * kLdR + dch] - gref);
+          r1[e] *= as;
+          r2[e] *= as;
+        }
+      }
+      if (I <= 2) {
+        const int rho = 16 * (I + 1);
+        const float gref = sm.g[rho * kLdR + dch];
+        const int j = 16 * I + ml;
+        for (int k0 = rho; k0 < kChunk; k0 += 16) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const int i = k0 + 4 * mg + ks;
+            const float ex = exp2_hw(sm.g[i * kLdR + dch] - gref);
+            const float wa = -sm.b[i] * sm.da[i * kLdM + j];
+            c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wa, sm.kn[i * kLdR + dch] * ex, c1, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.dp[i * kLdM + j], sm.qn[i * kLdR + dch] * ex, c1, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c1[e] *= exp2_hw(gref - sm.g[(16 * I + 4 * mg + e) * kLdR + dch]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int o = (4 * mg + e) * kLdR + dch;
+        sm.stg[0][o] = r1[e];
+        sm.stg[1][o] = r2[e];
+        sm.stg[2][o] = c1[e];
+      }
+      __syncthreads();
+      if ((r >> 4) == I) {
+        const int o = (r & 15) * kLdR + d0;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const float4 x1 = *reinterpret_cast<const float4*>(&sm.stg[0][o + 4 * e4]);
+          const float4 x2 = *reinterpret_cast<const float4*>(&sm.stg[1][o + 4 * e4]);
+          const float4 x3 = *reinterpret_cast<const float4*>(&sm.stg[2][o + 4 * e4]);
+          const float a1[4] = {x1.x, x1.y, x1.z, x1.w}, a2[4] = {x2.x, x2.y, x2.z, x2.w};
+          const float a3[4] = {x3.x, x3.y, x3.z, x3.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int d = 4 * e4 + e;
+            const float dkr = -br * a1[e];
+            dkn[d] += dkr + a3[e];
+            dqn[d] += a2[e];
+            dG[d] = fmaf(dkr - a3[e], knr[d], fmaf(a2[e], qnr[d], dG[d]));
+            dbp = fmaf(a1[e], knr[d], dbp);
+          }
+        }
+      }
+      __syncthreads();
     }
   }
 
