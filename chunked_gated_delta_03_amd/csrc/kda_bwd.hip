@@ -293,9 +293,11 @@ __global__ __launch_bounds__(512) void kda_bwd_dh_kernel(KdaBwdArgs a) {
 // k^ = k rk and q^ = q rq are the normalised rows; G the cumulative log2
 // gate. Every exponent 2^(G_i - G_j) is taken with i >= j, so it is <= 0.
 // fp32 throughout: the mats kernel's products on v_mfma_f32_16x16x4f32
-// (exact fp32 operands), the gram kernel on the vector units; one workgroup
-// per (chunk, head) (the kernels with 512 threads; the gram kernel's thread:
-// row r, 16 channels), heads fastest in dispatch order.
+// (exact fp32 operands); the gram kernel's pairs of rows in different 16-row
+// blocks on the same instruction (decays split at a reference row), its
+// pairs inside a block on the vector units. One workgroup per (chunk, head)
+// (the kernels with 512 threads; the gram kernel's thread: row r, 16
+// channels), heads fastest in dispatch order.
 // ---------------------------------------------------------------------------
 namespace {
 
