@@ -39,7 +39,7 @@ EXPORTED = (
     "gdn_short_conv_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes",
     "gdn_bwd_timing_read", "gdn_chunk_fwd_gated", "kda_chunk_fwd_gated", "gdn_chunk_bwd_gated",
     "gdn_state_summary_gated", "kda_bwd_state_pass", "kda_bwd_state_pass_workspace_bytes",
-    "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
+    "kda_chunk_bwd", "kda_chunk_bwd_gated", "kda_chunk_bwd_workspace_bytes",
 )
 
 
@@ -108,6 +108,9 @@ def _load() -> ctypes.CDLL:
     lib.kda_chunk_bwd.restype = ctypes.c_int
     lib.kda_chunk_bwd.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p,
                                   p, p, p, p, p, p, p, sz, p]
+    lib.kda_chunk_bwd_gated.restype = ctypes.c_int
+    lib.kda_chunk_bwd_gated.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p,
+                                        p, p, p, p, p, p, p, p, p, sz, p]
     lib.kda_bwd_state_pass_workspace_bytes.restype = sz
     lib.kda_bwd_state_pass_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, p, u32]
     lib.kda_bwd_state_pass.restype = ctypes.c_int
@@ -342,11 +345,18 @@ def gdn_chunk_bwd(q, k, v, g, beta, do, scale: Optional[float] = None, initial_s
 
 def kda_chunk_bwd(q, k, v, g, beta, do, scale: Optional[float] = None, initial_state=None, d_final_state=None,
                   cu_seqlens=None, l2norm_qk: bool = False, beta_sigmoid: bool = False,
-                  workspace: Optional[torch.Tensor] = None, stream=None):
+                  workspace: Optional[torch.Tensor] = None, stream=None, A_log=None, dt_bias=None):
     """KDA backward: as :func:`gdn_chunk_bwd` for the forward of :func:`kda_chunk_fwd`;
-    dg is fp32 [B,T,H,128] w.r.t. the raw log2 gate."""
+    dg is fp32 [B,T,H,128] w.r.t. the raw log2 gate.
+
+    With A_log (fp32 [H]) and dt_bias (fp32 [H,128]) this is the backward of
+    :func:`kda_chunk_fwd_gated`: g holds the raw gate values, dg is the
+    gradient w.r.t. them, and (dA_log [H], ddt_bias [H,128]) are appended."""
     cu = _cu_array(cu_seqlens)
     B, T, H, K, V, N = _check_inputs(q, k, v, g, beta, True, initial_state, cu)
+    gated = A_log is not None or dt_bias is not None
+    if gated:
+        _check_gate_params(True, q, A_log, dt_bias, H, K)
     if (not isinstance(do, torch.Tensor) or do.dtype != torch.bfloat16 or not do.is_contiguous()
             or tuple(do.shape) != (B, T, H, V) or do.device != q.device):
         raise ValueError("do must be a contiguous bf16 [B,T,H,V] tensor on %s" % q.device)
@@ -367,10 +377,18 @@ def kda_chunk_bwd(q, k, v, g, beta, do, scale: Optional[float] = None, initial_s
         workspace = torch.empty(int(need), dtype=torch.uint8, device=q.device)
     elif workspace.numel() * workspace.element_size() < need:
         raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel() * workspace.element_size(), need))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if gated:
+        da, ddt = torch.empty((H,), **f32), torch.empty((H, K), **f32)
+        _check(lib.kda_chunk_bwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(A_log), _ptr(dt_bias), _ptr(beta),
+                                       _ptr(initial_state), _cu_ptr(cu), N, B, T, H, K, V, scale, flags, _ptr(do),
+                                       _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(da),
+                                       _ptr(ddt), _ptr(dbeta), _ptr(ds0), _ptr(workspace), ws_bytes,
+                                       _stream_ptr(q.device, stream)))
+        return dq, dk, dv, dg, dbeta, ds0, da, ddt
     _check(lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _cu_ptr(cu), N,
                              B, T, H, K, V, scale, flags, _ptr(do), _ptr(d_final_state), _ptr(dq), _ptr(dk),
-                             _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(ds0), _ptr(workspace),
-                             0 if workspace is None else workspace.numel() * workspace.element_size(),
+                             _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(ds0), _ptr(workspace), ws_bytes,
                              _stream_ptr(q.device, stream)))
     return dq, dk, dv, dg, dbeta, ds0
 

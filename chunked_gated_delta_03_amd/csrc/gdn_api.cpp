@@ -994,10 +994,12 @@ int gdn_stage_prepare(int32_t kda, const void* q, const void* k, const float* g,
 
 // KDA backward workspace: the GDN backward's sections (the KDA decayed-operand
 // area holds the cumulative gate) plus dP, dA (64 x 64), dKD (64 x 128) and
-// the T-term part of dbeta per chunk-head.
+// the T-term part of dbeta per chunk-head, and the partial sums of the
+// in-kernel gate's backward.
 struct KdaBwdLayout {
   BwdLayout b;
-  size_t dp = 0, da = 0, dkd = 0, db1 = 0, total = 0;
+  size_t dp = 0, da = 0, dkd = 0, db1 = 0, kgpart = 0, total = 0;
+  int kgate_blocks = 0;
 };
 
 KdaBwdLayout kda_bwd_layout_for(const Problem& p) {
@@ -1013,6 +1015,9 @@ KdaBwdLayout kda_bwd_layout_for(const Problem& p) {
   off += align256(cmH * GDN_CHUNK * GDN_HEAD_DIM * sizeof(float));
   L.db1 = off;
   off += align256(cmH * GDN_CHUNK * sizeof(float));
+  L.kgate_blocks = (int)(((long)p.B * p.T + gdn::kKdaGateTok - 1) / gdn::kKdaGateTok);
+  L.kgpart = off;
+  off += align256((size_t)p.H * (1 + GDN_HEAD_DIM) * L.kgate_blocks * sizeof(float));
   L.total = off;
   return L;
 }
@@ -1030,11 +1035,12 @@ size_t kda_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K,
   return kda_bwd_layout_for(p).total;
 }
 
-int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
-                  const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
-                  int32_t H, int32_t K, int32_t V, float scale, uint32_t flags, const void* d_o,
-                  const float* d_final_state, float* dq, float* dk, float* dv, float* dg, float* dbeta,
-                  float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream_ptr) {
+static int kda_bwd_impl(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                        const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                        int32_t T, int32_t H, int32_t K, int32_t V, float scale, uint32_t flags, const void* d_o,
+                        const float* d_final_state, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                        float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream_ptr,
+                        bool gated, const float* a_log, const float* dt_bias, float* da_log, float* ddt_bias) {
   g_last_error.clear();
   Problem p;
   p.kda = true;
@@ -1046,6 +1052,11 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
     return fail(GDN_ERR_INVALID_ARGUMENT, "d_o, dq, dk, dv, dg and dbeta must be non-NULL");
   if (!aligned16(d_o) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dg) || !aligned16(g))
     return fail(GDN_ERR_INVALID_ARGUMENT, "g, d_o, dq, dk, dv and dg must be 16-byte aligned");
+  if (gated) {
+    if (!a_log || !dt_bias || !da_log || !ddt_bias)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "A_log, dt_bias, dA_log and ddt_bias must be non-NULL");
+    if (!aligned16(dt_bias)) return fail(GDN_ERR_INVALID_ARGUMENT, "dt_bias must be 16-byte aligned");
+  }
   int cus = 0;
   rc = check_device(&cus);
   if (rc) return rc;
@@ -1073,6 +1084,8 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
   pa.vec = ws(L.b.fwd.vec);
   pa.gk = ws(L.b.fwd.kdec);
   pa.kdec = nullptr;
+  pa.a_log = gated ? a_log : nullptr;
+  pa.dt_bias = gated ? dt_bias : nullptr;
   pa.geo = geo;
   pa.H = H;
   pa.scale = scale;
@@ -1145,7 +1158,44 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
 
   e = gdn::launch_kda_bwd_chunks(ka, stream);
   if (e != hipSuccess) return hip_fail(e, "per-chunk gradients launch");
+  if (gated) {
+    gdn::KdaGateBwdArgs ga{};
+    ga.x = g;
+    ga.a_log = a_log;
+    ga.dt_bias = dt_bias;
+    ga.dg = dg;
+    ga.part = ws(L.kgpart);
+    ga.da_log = da_log;
+    ga.ddt_bias = ddt_bias;
+    ga.ntok = (long)B * T;
+    ga.H = H;
+    ga.nblk = L.kgate_blocks;
+    e = gdn::launch_kda_gate_bwd(ga, stream);
+    if (e != hipSuccess) return hip_fail(e, "gate backward launch");
+  }
   return GDN_OK;
+}
+
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                  int32_t H, int32_t K, int32_t V, float scale, uint32_t flags, const void* d_o,
+                  const float* d_final_state, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                  float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  return kda_bwd_impl(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, scale, flags, d_o,
+                      d_final_state, dq, dk, dv, dg, dbeta, d_initial_state, workspace, workspace_bytes, stream_ptr,
+                      false, nullptr, nullptr, nullptr, nullptr);
+}
+
+int kda_chunk_bwd_gated(const void* q, const void* k, const void* v, const float* g_raw, const float* A_log,
+                        const float* dt_bias, const void* beta, const float* initial_state,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+                        int32_t V, float scale, uint32_t flags, const void* d_o, const float* d_final_state,
+                        float* dq, float* dk, float* dv, float* dg_raw, float* dA_log, float* ddt_bias,
+                        float* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return kda_bwd_impl(q, k, v, g_raw, beta, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, scale, flags, d_o,
+                      d_final_state, dq, dk, dv, dg_raw, dbeta, d_initial_state, workspace, workspace_bytes, stream,
+                      true, A_log, dt_bias, dA_log, ddt_bias);
 }
 
 size_t kda_bwd_state_pass_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,

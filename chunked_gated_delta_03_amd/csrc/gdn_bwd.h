@@ -92,4 +92,23 @@ struct GateBwdArgs {
 };
 hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t stream);
 
+// Backward of the KDA in-kernel gate, per key channel:
+// g = -exp(A_log[h]) softplus(x + dt_bias[h,d]) / ln 2 (log2 units), so
+// dx = dg (-exp(A_log) / ln 2) sigmoid(x + dt_bias), dA_log[h] = sum dg g
+// over tokens and channels, ddt_bias[h,d] = sum of dx over tokens.
+constexpr int kKdaGateTok = 256;  // tokens per block of the partial sums
+struct KdaGateBwdArgs {
+  const float* x;        // [ntok,H,128] raw gate values
+  const float* a_log;    // [H]
+  const float* dt_bias;  // [H,128]
+  float* dg;             // [ntok,H,128] in: w.r.t. g, out: w.r.t. x
+  float* part;           // [H][nblk] then [H][128][nblk] workspace
+  float* da_log;         // [H]
+  float* ddt_bias;       // [H,128]
+  long ntok;
+  int H;
+  int nblk;              // ceil(ntok / kKdaGateTok)
+};
+hipError_t launch_kda_gate_bwd(const KdaGateBwdArgs& a, hipStream_t stream);
+
 }  // namespace gdn

@@ -1060,4 +1060,60 @@ hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// KDA gate backward, per key channel. Partial sums per block of
+// kKdaGateTok tokens and head: thread (channel d = tid % 128, token parity
+// tid / 128) walks its tokens in order; dA_log's partial is reduced over the
+// block in a fixed order (xor shuffles, then the four waves in order),
+// dt_bias's per channel as (even tokens) + (odd tokens). The final kernel
+// sums the blocks in order, so results are bitwise reproducible.
+__global__ __launch_bounds__(256) void kda_gate_bwd_partial_kernel(KdaGateBwdArgs a) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int h = blockIdx.y, tid = threadIdx.x, d = tid & 127, par = tid >> 7;
+  const long t0 = (long)blockIdx.x * kKdaGateTok;
+  const float ea = expf(a.a_log[h]), db = a.dt_bias[(size_t)h * kDim + d];
+  const float c = -ea * kLog2e;
+  float sa = 0.f, sb = 0.f;
+  for (int j = 0; j < kKdaGateTok / 2; ++j) {
+    const long t = t0 + par + 2 * j;
+    if (t >= a.ntok) break;
+    const size_t idx = ((size_t)t * a.H + h) * kDim + d;
+    const float y = a.x[idx] + db;
+    const float dgv = a.dg[idx];
+    const float g = -ea * softplus_log2(y);
+    const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-y * kLog2e));
+    const float dx = dgv * c * sig;
+    a.dg[idx] = dx;
+    sa = fmaf(dgv, g, sa);
+    sb += dx;
+  }
+  __shared__ float red[4];
+  __shared__ float odd[kDim];
+  sa = wave_sum_fixed(sa);
+  if ((tid & 63) == 0) red[tid >> 6] = sa;
+  if (par == 1) odd[d] = sb;
+  __syncthreads();
+  if (par == 0) a.part[(size_t)a.H * a.nblk + ((size_t)h * kDim + d) * a.nblk + blockIdx.x] = sb + odd[d];
+  if (tid == 0) a.part[(size_t)h * a.nblk + blockIdx.x] = ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+__global__ __launch_bounds__(128) void kda_gate_bwd_final_kernel(KdaGateBwdArgs a) {
+  const int h = blockIdx.x, d = threadIdx.x;
+  const float* pb = a.part + (size_t)a.H * a.nblk + ((size_t)h * kDim + d) * a.nblk;
+  float sb = 0.f;
+  for (int b = 0; b < a.nblk; ++b) sb += pb[b];
+  a.ddt_bias[(size_t)h * kDim + d] = sb;
+  if (d < 64) {
+    float sa = 0.f;
+    for (int b = d; b < a.nblk; b += 64) sa += a.part[(size_t)h * a.nblk + b];
+    sa = wave_sum_fixed(sa);
+    if (d == 0) a.da_log[h] = sa;
+  }
+}
+
+hipError_t launch_kda_gate_bwd(const KdaGateBwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(kda_gate_bwd_partial_kernel, dim3(a.nblk, a.H), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(kda_gate_bwd_final_kernel, dim3(a.H), dim3(128), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace gdn

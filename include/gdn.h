@@ -334,6 +334,28 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
                   const float* d_final_state, float* dq, float* dk, float* dv, float* dg, float* dbeta,
                   float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward of kda_chunk_fwd_gated (the per-channel gate
+ * -exp(A_log[h]) softplus(g_raw + dt_bias[h,d]) / ln 2 formed in the
+ * kernel): the arguments of kda_chunk_bwd with g_raw [B,T,H,K], A_log [H] and
+ * dt_bias [H,K] as kda_chunk_fwd_gated takes them, and
+ *   dg_raw   [B,T,H,K] fp32, the gradient w.r.t. g_raw
+ *            (= -exp(A_log) sigmoid(g_raw + dt_bias) / ln 2 times the gate's);
+ *   dA_log   [H] fp32, sum over tokens and channels of (gradient w.r.t. the
+ *            gate) * gate;
+ *   ddt_bias [H,K] fp32, sum over tokens of dg_raw;
+ * all device pointers, required (GDN_ERR_INVALID_ARGUMENT if NULL), dt_bias
+ * 16-byte aligned. The sums are taken in a fixed order (bitwise
+ * reproducible). Same workspace size as kda_chunk_bwd; errors and stream
+ * behaviour as there. The pages print no gate formula: the one taken is that
+ * of kda_chunk_fwd_gated. */
+int kda_chunk_bwd_gated(const void* q, const void* k, const void* v, const float* g_raw, const float* A_log,
+                        const float* dt_bias, const void* beta, const float* initial_state,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+                        int32_t V, float scale, uint32_t flags, const void* d_o, const float* d_final_state,
+                        float* dq, float* dk, float* dv, float* dg_raw, float* dA_log, float* ddt_bias,
+                        float* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 /*
  * KDA backward, reverse state pass (the stage of the backward that carries the
  * state gradient across chunks; bwd_state_saved of the backward on the

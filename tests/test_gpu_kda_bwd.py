@@ -195,3 +195,61 @@ def test_kda_chunk_bwd_full_size_sampled(gdn):
     _say("  " + "  ".join("%s %.2e" % kv for kv in errs.items()))
     for key, e in errs.items():
         assert e <= RTOL, (key, e)
+
+
+# ---------------------------------------------------------------------------
+# Backward of the in-kernel KDA gate (kda_chunk_bwd_gated): the oracle's
+# gradient w.r.t. the per-channel gate, chained through the gate by
+# oracle.grad.gate_grads; the gate's sums are bitwise reproducible.
+# ---------------------------------------------------------------------------
+def _gated_cases():
+    import dataclasses
+    packed = gi.make_inputs("kda", B=1, T=277, H=2)
+    packed = dataclasses.replace(packed, cu_seqlens=np.array([0, 1, 18, 82, 147, 277], np.int32))
+    return [("kda_gated_B1_T600_H2", gi.make_inputs("kda", B=1, T=600, H=2)),  # three gate blocks, ragged
+            ("kda_gated_B2_T150_H3", gi.make_inputs("kda", B=2, T=150, H=3)),
+            ("kda_gated_packed", packed)]
+
+
+GATED = _gated_cases()
+
+
+def _run_kda_bwd_gated(gdn, inp, do_bits, dsf):
+    d = to_device(inp)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    out = gdn.kda_chunk_bwd(d["q"], d["k"], d["v"], t(inp.gate_raw), d["beta"],
+                            torch.from_numpy(do_bits).view(torch.bfloat16).cuda(), scale=inp.scale,
+                            initial_state=d["initial_state"], d_final_state=torch.from_numpy(dsf).cuda(),
+                            cu_seqlens=inp.cu_seqlens, l2norm_qk=bool(inp.flags & 1),
+                            beta_sigmoid=bool(inp.flags & 2), A_log=t(inp.A_log), dt_bias=t(inp.dt_bias))
+    torch.cuda.synchronize()
+    return {n: x.cpu().numpy().astype(np.float64) for n, x in zip(NAMES + ("da_log", "ddt_bias"), out)}
+
+
+@pytest.mark.parametrize("name,inp", GATED, ids=[c[0] for c in GATED])
+def test_kda_chunk_bwd_gated_parity(gdn, name, inp):
+    import dataclasses
+    from oracle import gate as ogate
+    from oracle import grad as og
+    _say("kda gated bwd", name, inp.B, inp.T, inp.H, "seqs", inp.num_seqs)
+    rng = np.random.default_rng(12)
+    do_bits = gi.f32_to_bf16_bits(rng.standard_normal((inp.B, inp.T, inp.H, inp.V), dtype=np.float32))
+    dsf = (rng.standard_normal((inp.num_seqs, inp.H, inp.K, inp.V)) * 0.1).astype(np.float32)
+    got = _run_kda_bwd_gated(gdn, inp, do_bits, dsf)
+    g64 = ogate.kda_gate(inp.gate_raw, inp.A_log, inp.dt_bias)
+    ref = og.grads(dataclasses.replace(inp, g=g64), gi.bf16_bits_to_f32(do_bits).astype(np.float64),
+                   dsf.astype(np.float64))
+    gg = og.gate_grads(True, inp.gate_raw, inp.A_log, inp.dt_bias, ref["dg"])
+    ref = {**ref, "dg": gg["dx"], "da_log": gg["da_log"], "ddt_bias": gg["ddt_bias"]}
+    errs = {}
+    for key in NAMES + ("da_log", "ddt_bias"):
+        x = got[key]
+        assert np.isfinite(x).all(), key
+        assert x.shape == ref[key].shape, (key, x.shape, ref[key].shape)
+        errs[key] = float(np.abs(x - ref[key]).max() / max(np.abs(ref[key]).max(), 1e-30))
+    _say("  " + "  ".join("%s %.2e" % kv for kv in errs.items()))
+    for key, e in errs.items():
+        assert e <= RTOL, (key, e)
+    again = _run_kda_bwd_gated(gdn, inp, do_bits, dsf)
+    for n in ("dg", "da_log", "ddt_bias"):
+        assert np.array_equal(again[n], got[n]), n
