@@ -39,7 +39,7 @@ EXPORTED = (
     "gdn_short_conv_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes",
     "gdn_bwd_timing_read", "gdn_chunk_fwd_gated", "kda_chunk_fwd_gated", "gdn_chunk_bwd_gated",
     "gdn_state_summary_gated", "kda_bwd_state_pass", "kda_bwd_state_pass_workspace_bytes",
-    "kda_chunk_bwd", "kda_chunk_bwd_gated", "kda_chunk_bwd_workspace_bytes",
+    "kda_chunk_bwd", "kda_chunk_bwd_gated", "kda_chunk_bwd_workspace_bytes", "gdn_chunk_fwd_noalloc",
 )
 
 
@@ -69,6 +69,8 @@ def _load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p, p, sz, p]
+    lib.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_noalloc.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, u32, p, p, p]
     for name in ("gdn_chunk_fwd_gated", "kda_chunk_fwd_gated"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
@@ -259,6 +261,37 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale: Optional[float] = None, initial_state
     beta bf16 [B,T,H]. Returns (o bf16 [B,T,H,128], final_state fp32 [N,H,128,128] or None)."""
     return _chunk_fwd(False, q, k, v, g, beta, scale, initial_state, cu_seqlens, l2norm_qk, beta_sigmoid,
                       output_final_state, workspace, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, scale: Optional[float] = None, initial_state=None,
+                          l2norm_qk: bool = False, beta_sigmoid: bool = False, output_final_state: bool = True,
+                          stream=None, out: Optional[Tuple[torch.Tensor, Optional[torch.Tensor]]] = None):
+    """GDN forward through the entry that allocates nothing (dense input only;
+    intermediates in the library's fixed device scratch of
+    NOALLOC_SCRATCH_BYTES). ``out`` = (o, final_state) preallocated by the
+    caller (final_state may be None without output_final_state); else this
+    binding allocates them with torch. Returns (o, final_state)."""
+    B, T, H, K, V, N = _check_inputs(q, k, v, g, beta, False, initial_state, None)
+    scale = K ** -0.5 if scale is None else float(scale)
+    flags = _flags(l2norm_qk, beta_sigmoid, output_final_state)
+    if out is None:
+        o = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=q.device)
+        fs = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device) if output_final_state else None
+    else:
+        o, fs = out
+        if (o.dtype != torch.bfloat16 or not o.is_contiguous() or tuple(o.shape) != (B, T, H, V)
+                or o.device != q.device):
+            raise ValueError("o must be a contiguous bf16 [B,T,H,V] tensor on %s" % q.device)
+        if output_final_state and (fs is None or fs.dtype != torch.float32 or not fs.is_contiguous()
+                                   or tuple(fs.shape) != (N, H, K, V) or fs.device != q.device):
+            raise ValueError("final_state must be a contiguous fp32 [N,H,K,V] tensor on %s" % q.device)
+    _check(lib.gdn_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), None, N,
+                                     B, T, H, K, V, scale, flags, _ptr(o), _ptr(fs) if output_final_state else None,
+                                     _stream_ptr(q.device, stream)))
+    return o, (fs if output_final_state else None)
 
 
 def kda_chunk_fwd(q, k, v, g, beta, scale: Optional[float] = None, initial_state=None, cu_seqlens=None,

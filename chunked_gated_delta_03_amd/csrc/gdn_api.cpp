@@ -366,7 +366,7 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
               const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
               int32_t H, int32_t K, int32_t V, float scale, uint32_t flags, void* o, float* final_state,
               void* workspace, size_t workspace_bytes, void* stream_ptr, bool gated = false,
-              const float* a_log = nullptr, const float* dt_bias = nullptr) {
+              const float* a_log = nullptr, const float* dt_bias = nullptr, bool timed = true) {
   g_last_error.clear();
   Problem p;
   p.kda = kda;
@@ -397,7 +397,8 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
     if (rc) return rc;
   }
   const gdn::Geometry geo = make_geometry(p, W.base + L.tab);
-  if (g_timing && (rc = timing_mark(g_timing_recs, 0, stream))) return rc;
+  const bool timing = g_timing && timed;
+  if (timing && (rc = timing_mark(g_timing_recs, 0, stream))) return rc;
 
   gdn::PrepareArgs pa{};
   pa.q = static_cast<const uint16_t*>(q);
@@ -418,7 +419,7 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
   pa.cus = cus;
   hipError_t e = gdn::launch_prepare(kda, pa, stream);
   if (e != hipSuccess) return hip_fail(e, "prepare launch");
-  if (g_timing && (rc = timing_mark(g_timing_recs, 1, stream))) return rc;
+  if (timing && (rc = timing_mark(g_timing_recs, 1, stream))) return rc;
 
   gdn::FwdArgs fa{};
   fa.q = pa.q;
@@ -436,7 +437,36 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
   fa.H = H;
   e = gdn::launch_fwd(kda, false, true, fa, stream);
   if (e != hipSuccess) return hip_fail(e, "state/output launch");
-  if (g_timing && (rc = timing_mark(g_timing_recs, 2, stream))) return rc;
+  if (timing && (rc = timing_mark(g_timing_recs, 2, stream))) return rc;
+  return GDN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The fixed scratch of gdn_chunk_fwd_noalloc: a file-scope device array in
+// place of a workspace, so that a call allocates nothing. Every device the
+// library runs on holds its own copy until the process ends. In host code
+// the array's name is only a host-side stand-in: kernels get the device
+// address that hipGetSymbolAddress returns for the current device, resolved
+// once per device on the first call there and kept.
+static __device__ __align__(256) unsigned char noalloc_scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+int noalloc_scratch_address(void** out) {
+  static std::mutex mu;
+  static std::vector<void*> addr;  // per device id
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(noalloc_scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(noalloc scratch)");
+    if (!ptr || (reinterpret_cast<uintptr_t>(ptr) & 255u) != 0)
+      return fail(GDN_ERR_HIP, "the no-allocation scratch has no usable device address");
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
   return GDN_OK;
 }
 
@@ -744,6 +774,39 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   void* workspace, size_t workspace_bytes, void* stream) {
   return chunk_fwd(false, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, scale, flags, o,
                    final_state, workspace, workspace_bytes, stream);
+}
+
+int gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                          const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                          int32_t T, int32_t H, int32_t K, int32_t V, float scale, uint32_t flags, void* o,
+                          float* final_state, void* stream) {
+  g_last_error.clear();
+  if (cu_seqlens)
+    return fail(GDN_ERR_UNSUPPORTED,
+                "gdn_chunk_fwd_noalloc takes dense input only (the packed chunk table is staged through "
+                "pinned host memory, which this entry does not allocate)");
+  Problem p;
+  int rc = check_shape(B, T, H, K, V, num_seqs, nullptr, p);
+  if (rc) return rc;
+  const size_t need = layout_for(p, true).total;
+  if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
+    return fail(GDN_ERR_INVALID_ARGUMENT,
+                "problem needs %zu bytes of scratch, above the fixed %zu bytes of gdn_chunk_fwd_noalloc "
+                "(B*ceil(T/64)*H = %lld chunk-heads; use gdn_chunk_fwd with a workspace)",
+                need, (size_t)GDN_NOALLOC_SCRATCH_BYTES, (long long)(p.NT * p.H));
+  rc = check_common(q, k, v, g, beta, scale, flags);
+  if (rc) return rc;
+  if (!o) return fail(GDN_ERR_INVALID_ARGUMENT, "o must be non-NULL");
+  if ((flags & GDN_OUTPUT_FINAL_STATE) && !final_state)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "GDN_OUTPUT_FINAL_STATE set but final_state is NULL");
+  rc = check_device(nullptr);
+  if (rc) return rc;
+  void* scratch = nullptr;
+  rc = noalloc_scratch_address(&scratch);
+  if (rc) return rc;
+  return chunk_fwd(false, q, k, v, g, beta, initial_state, nullptr, num_seqs, B, T, H, K, V, scale, flags, o,
+                   final_state, scratch, (size_t)GDN_NOALLOC_SCRATCH_BYTES, stream, false, nullptr, nullptr,
+                   /*timed=*/false);
 }
 
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const void* beta,

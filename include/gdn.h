@@ -103,6 +103,35 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, float scale, uint32_t flags,
                   void* o, float* final_state, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Whole forward pass, GDN, for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and results as gdn_chunk_fwd with dense input, but the
+ * intermediates (the per-chunk T, output matrix and row vectors) go to a
+ * fixed device array of GDN_NOALLOC_SCRATCH_BYTES inside the library instead
+ * of a workspace, and the call allocates nothing (no hipMalloc, hipFree,
+ * pinned host memory or events). The caller still passes every input and
+ * output. Limits and behaviour:
+ *   - dense input only: cu_seqlens must be NULL (GDN_ERR_UNSUPPORTED
+ *     otherwise) and num_seqs == B;
+ *   - the intermediates must fit: gdn_chunk_fwd_workspace_bytes() of the
+ *     same problem <= GDN_NOALLOC_SCRATCH_BYTES (B=4, T=4096, H=16 fits);
+ *     larger problems get GDN_ERR_INVALID_ARGUMENT and nothing is
+ *     launched;
+ *   - the array is per device and shared by every call on that device: two
+ *     calls that overlap in time on one device (other streams or threads)
+ *     race on it and their results are undefined. Each call overwrites every
+ *     scratch byte it reads before reading it, so nothing needs clearing
+ *     between calls;
+ *   - the device address of the array is resolved on the first call on each
+ *     device and kept; the array lives until the process ends;
+ *   - per-kernel timing (gdn_timing_enable) does not apply to this entry.
+ * Every other argument, and the error behaviour, as gdn_chunk_fwd. */
+#define GDN_NOALLOC_SCRATCH_BYTES (128u << 20)
+int gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                          const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                          int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, float scale, uint32_t flags,
+                          void* o, float* final_state, void* stream);
+
 /* Whole forward pass, KDA (per-key-channel log2 gate g [B,T,H,K]; the
  * chunk-local cumulative log2 decay slot gk of the KDA prepare stage on the
  * kimi_delta_attention_ascendc.py coverage page). Same arguments otherwise. */

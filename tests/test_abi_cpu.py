@@ -292,3 +292,68 @@ def test_chunk_bwd_workspace_bytes(gdn):
     assert b >= fwd + cmh * (2 * 128 * 128 * 4 + 5 * 64 * 128 * 4 + 4) and b % 256 == 0
     assert ws(4, 4096, 16, 64, 128, 4, None, 3) == 0
     assert ws(4, 4096, 16, 128, 128, 4, None, 8) == 0
+
+
+def _header_define(name):
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    m = re.search(r"#define\s+%s\s+\((\d+)u\s*<<\s*(\d+)\)" % name, src)
+    return int(m.group(1)) << int(m.group(2))
+
+
+def _call_noalloc(gdn, B=1, T=64, H=2, K=128, V=128, cu=None, num_seqs=None, scale=0.1, flags=4, q=FAKE, o=FAKE,
+                  fs=FAKE):
+    cu_arr = None if cu is None else np.asarray(cu, dtype=np.int32)
+    n = (B if cu is None else len(cu) - 1) if num_seqs is None else num_seqs
+    return gdn.lib.gdn_chunk_fwd_noalloc(q, FAKE, FAKE, FAKE, FAKE, None,
+                                         None if cu_arr is None else cu_arr.ctypes.data_as(ctypes.c_void_p),
+                                         n, B, T, H, K, V, scale, flags, o, fs, None)
+
+
+def test_noalloc_scratch_size_matches_binding(gdn):
+    assert _header_define("GDN_NOALLOC_SCRATCH_BYTES") == gdn.NOALLOC_SCRATCH_BYTES == 128 << 20
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(T=10, cu=[0, 4, 10]), 2, "dense input only"),
+    (dict(B=0), 1, "B, T and H"),
+    (dict(K=64), 2, "K = V = 128"),
+    (dict(scale=0.0), 1, "scale"),
+    (dict(q=None), 1, "non-NULL"),
+    (dict(o=None), 1, "o must be non-NULL"),
+    (dict(fs=None), 1, "final_state is NULL"),
+    (dict(B=2, num_seqs=3), 1, "num_seqs == B"),
+])
+def test_noalloc_invalid_arguments_rejected(gdn, kw, code, msg):
+    rc = _call_noalloc(gdn, **kw)
+    assert rc == code
+    assert msg in gdn.last_error()
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch(gdn):
+    limit = gdn.NOALLOC_SCRATCH_BYTES
+    # the largest dense H that fits at B=4, T=4096 by the library's own workspace count, then one more head
+    per_head = gdn.lib.gdn_chunk_fwd_workspace_bytes(4, 4096, 1, 128, 128, 4, None, 7)
+    assert per_head > 0
+    h_fit = limit // per_head
+    assert gdn.lib.gdn_chunk_fwd_workspace_bytes(4, 4096, h_fit, 128, 128, 4, None, 7) <= limit
+    rc = _call_noalloc(gdn, B=4, T=4096, H=h_fit + 1)
+    assert rc == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert "scratch" in gdn.last_error()
+    # the benchmark shape fits
+    assert gdn.lib.gdn_chunk_fwd_workspace_bytes(4, 4096, 16, 128, 128, 4, None, 7) <= limit
+
+
+def test_documented_size_limits_are_the_enforced_ones(gdn):
+    """The header allows B*T < 2^30 and 1 <= H <= 65535; both edges are checked
+    before any device call."""
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    assert "1 <= H <= 65535, B*T < 2^30" in src
+    assert _call_fwd(gdn, H=65536) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert _call_fwd(gdn, B=1, T=1 << 30) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert _call_fwd(gdn, B=2, T=1 << 29) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert "exceeds the supported range" in gdn.last_error()
+    # sizes at the edges pass the shape checks: the workspace count (pure host
+    # arithmetic) accepts them
+    assert gdn.lib.gdn_chunk_fwd_workspace_bytes(1, (1 << 30) - 1, 1, 128, 128, 1, None, 0) > 0
+    assert gdn.lib.gdn_chunk_fwd_workspace_bytes(1, 64, 65535, 128, 128, 1, None, 0) > 0
+    assert gdn.lib.kda_chunk_fwd_workspace_bytes(1, (1 << 30) - 1, 1, 128, 128, 1, None, 0) > 0
