@@ -236,10 +236,12 @@ __device__ __forceinline__ f32x4 gram_tile(const u16x8 (&x)[4], const u16x8 (&y)
   return acc;
 }
 
-// T (stride kLdP) and Aqk of one item to HBM, as store_t_aqk.
+// T (stride kLdP) and Aqk of one item to HBM, as store_t_aqk; with
+// a.t_ld == 64 only the hi part bf16(T) is stored (the whole-pass layout).
 __device__ __forceinline__ void store_t_aqk_p(const PrepareArgs& a, size_t cm, int tid, const float* sT,
                                               const uint16_t* sAqk) {
-  uint16_t* tdst = a.tmat + cm * (kChunk * 2 * kChunk);
+  const int tld = a.t_ld;
+  uint16_t* tdst = a.tmat + cm * (kChunk * (size_t)tld);
   uint16_t* qdst = a.aqk + cm * (kChunk * kChunk);
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
@@ -256,8 +258,9 @@ __device__ __forceinline__ void store_t_aqk_p(const PrepareArgs& a, size_t cm, i
     split2(x0.z, x0.w, hi[1], lo[1]);
     split2(x1.x, x1.y, hi[2], lo[2]);
     split2(x1.z, x1.w, hi[3], lo[3]);
-    *reinterpret_cast<uint4*>(tdst + r * (2 * kChunk) + 8 * m) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    *reinterpret_cast<uint4*>(tdst + r * (2 * kChunk) + kChunk + 8 * m) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<uint4*>(tdst + r * tld + 8 * m) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    if (tld == 2 * kChunk)
+      *reinterpret_cast<uint4*>(tdst + r * tld + kChunk + 8 * m) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     const u16x4 q0 = up0 ? u16x4{0, 0, 0, 0} : *reinterpret_cast<const u16x4*>(sAqk + r * kLdQ + c0);
     const u16x4 q1 = up1 ? u16x4{0, 0, 0, 0} : *reinterpret_cast<const u16x4*>(sAqk + r * kLdQ + c0 + 16);
     *reinterpret_cast<u16x8*>(qdst + r * kChunk + 8 * m) = cat4(q0, q1);
