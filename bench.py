@@ -98,6 +98,23 @@ def recorded_traffic(workload: str, kernel_name_part: str):
     return None
 
 
+def recorded_mfma(workload: str, kernel_name_part: str):
+    """MFMA counters of a kernel from the committed summary of this workload
+    (``profiles/*_mfma_counters.json``): the fraction of the SIMDs' cycles
+    their matrix units were busy during the kernel, or None if absent or
+    taken on other sources."""
+    import glob
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*_mfma_counters.json")):
+        with open(path) as f:
+            d = json.load(f)
+        if d.get("workload") != workload or d.get("kernel_source_hash") != kernel_source_hash(workload):
+            continue
+        for name, rec in d["kernels"].items():
+            if kernel_name_part in name:
+                return rec["mfma_busy_frac"]
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -565,7 +582,12 @@ def main():
     }
     dom_name = max(kernels, key=lambda n: kernels[n]["avg_us"])
     dom = kernels[dom_name]
-    achieved = dom["alg_bytes"] / (dom["avg_us"] * 1e-6) / 1e9
+    # achieved: the call's algorithmic bytes (1,030 B per token-head, 1,538 for
+    # KDA, plus 64 KiB per state read or written) over the dominant kernel's
+    # average duration; the same kernel's share of those bytes by first touch
+    # is reported beside it
+    achieved = path_bytes / (dom["avg_us"] * 1e-6) / 1e9
+    achieved_ft = dom["alg_bytes"] / (dom["avg_us"] * 1e-6) / 1e9
     roofline = {
         "kernel": dom_name,
         "bound": "hbm",
@@ -574,6 +596,10 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
         "traffic": None if args.gate_in_kernel else recorded_traffic(args.workload, dom["symbol"]),
+        "alg_bytes": int(path_bytes),
+        "mfma_busy": None if args.gate_in_kernel else recorded_mfma(args.workload, dom["symbol"]),
+        "first_touch": {"alg_bytes": int(dom["alg_bytes"]), "achieved": round(achieved_ft, 1),
+                        "frac": round(achieved_ft / HBM_PEAK_GBPS, 4)},
     }
     path_gbps = path_bytes / (ms_per_step * 1e-3) / 1e9
     mfma_frac = th * ALG_FLOPS_PER_TH / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)

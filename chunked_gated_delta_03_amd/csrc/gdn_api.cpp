@@ -57,7 +57,7 @@ int check_shape(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t n
     return fail(GDN_ERR_INVALID_ARGUMENT, "B, T and H must be >= 1 (got B=%d T=%d H=%d)", B, T, H);
   if (K != GDN_HEAD_DIM || V != GDN_HEAD_DIM)
     return fail(GDN_ERR_UNSUPPORTED, "only K = V = %d is supported (got K=%d V=%d)", GDN_HEAD_DIM, K, V);
-  if (H > 65535)  // a grid dimension of the per-(chunk, head) launches
+  if (H > 65535)  // grid y of the stage finalize and gate-backward launches
     return fail(GDN_ERR_INVALID_ARGUMENT, "H = %d exceeds the supported range (at most 65535 heads)", H);
   if ((int64_t)B * T > INT32_MAX / 2)
     return fail(GDN_ERR_INVALID_ARGUMENT, "B*T = %lld tokens exceeds the supported range",

@@ -600,10 +600,11 @@ __device__ __forceinline__ void invert_unit_lower(const float* sA, float* sT, in
 // KDA: per-key-channel log2 gate per (token, head, channel)
 // ===========================================================================
 __global__ __launch_bounds__(256) void kda_prepare_kernel(PrepareArgs a) {
-  // grid (H, NT): workgroups are dispatched head-fastest, so neighbouring
-  // ones read the neighbouring head rows of the same tokens
-  const int c = blockIdx.y;
-  const int h = blockIdx.x;
+  // 1-D grid over the (chunk, head) items, heads fastest in dispatch order
+  // (neighbouring workgroups read the neighbouring head rows of the same
+  // tokens)
+  const int c = blockIdx.x / a.H;
+  const int h = blockIdx.x - c * a.H;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -925,7 +926,7 @@ hipError_t launch_prepare(bool kda, const PrepareArgs& a, hipStream_t stream) {
   const long items = (long)a.geo.NT * a.H;
   const int cus = a.cus > 0 ? a.cus : 256;
   if (kda) {
-    hipLaunchKernelGGL(kda_prepare_kernel, dim3(a.H, a.geo.NT), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(kda_prepare_kernel, dim3((unsigned)((size_t)a.geo.NT * a.H)), dim3(256), 0, stream, a);
   } else {
     // three workgroups fit a compute unit (43.5 KiB of LDS each)
     const long slots = 3L * cus;

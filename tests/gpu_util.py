@@ -41,6 +41,25 @@ def s_err(s_gpu, s_ref):
     return float(np.abs(s_gpu - s_ref).max() / max(np.abs(s_ref).max(), 1e-30))
 
 
+def check_all_units(o, fs, o_ref, s_ref, say=print):
+    """Every element of o (max-abs <= O_ATOL) and the final state of every
+    (sequence, head) unit (max |S - S_ref| / max |S_ref| of the unit <=
+    S_RTOL, which implies the whole-tensor bar). Returns (o error, worst unit
+    relative state error)."""
+    N, H = fs.shape[:2]
+    assert np.isfinite(o).all() and np.isfinite(fs).all()
+    eo = o_err(o, o_ref)
+    diff = np.abs(fs - s_ref).reshape(N, H, -1).max(-1)
+    ref = np.maximum(np.abs(s_ref).reshape(N, H, -1).max(-1), 1e-30)
+    rel = diff / ref
+    worst = np.unravel_index(int(np.argmax(rel)), rel.shape)
+    say("  all %d x %d units: o max-abs err %.3e; final state: worst unit %s rel err %.3e, whole tensor %.3e"
+        % (N, H, eo, tuple(int(x) for x in worst), float(rel.max()), s_err(fs, s_ref)))
+    assert eo <= O_ATOL
+    assert float(rel.max()) <= S_RTOL
+    return eo, float(rel.max())
+
+
 def hm_chunks(arr_list, dense: bool):
     """Oracle per-batch/per-document [B,H,NC,...] intermediates -> GPU layout [H,NT,...]."""
     parts = []

@@ -13,7 +13,8 @@ import pytest
 
 import gdn_inputs as gi
 import oracle
-from gpu_util import O_ATOL, S_RTOL, decode_aqk, decode_tmat, hm_chunks, o_err, run_gpu, s_err, to_device
+from gpu_util import (O_ATOL, S_RTOL, check_all_units, decode_aqk, decode_tmat, hm_chunks, o_err, run_gpu,
+                      s_err, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -73,9 +74,14 @@ def test_end_to_end_reduced(gdn, name, inp):
 
 def test_stage_parity(gdn):
     """Each stage against the chunk-form intermediates of the oracle."""
+    # gdn_B4_T1024_H16 has 1,024 (chunk, head) items, more than the prepare
+    # kernel's persistent grid (three workgroups per compute unit), so each
+    # workgroup takes several items and the next item's loads overlap the
+    # previous item's deferred stores
     for name, inp in [("tiny", gi.make_inputs("tiny")),
                       ("gdn_B2_T200_H2", gi.make_inputs("gdn", B=2, T=200, H=2)),
-                      ("varlen", gi.make_inputs("varlen", H=2, doc_lengths=[17, 64, 100]))]:
+                      ("varlen", gi.make_inputs("varlen", H=2, doc_lengths=[17, 64, 100])),
+                      ("gdn_B4_T1024_H16", gi.make_inputs("gdn", B=4, T=1024, H=16))]:
         _say("stage case", name)
         d = to_device(inp)
         l2, sig = bool(inp.flags & 1), bool(inp.flags & 2)
@@ -268,65 +274,35 @@ def test_kda_stage_parity(gdn):
         assert o_err(o.float().cpu().numpy().astype(np.float64), o_ref) <= O_ATOL
 
 
-def test_full_size_kda_sampled(gdn):
-    """B=2 T=8192 H=32 per-channel gate; 4 sampled (sequence, head) units."""
-    inp = gi.make_inputs("kda")
-    _say("full-size kda: inputs ready")
+def _full_size(name):
+    inp = gi.make_inputs(name)
+    _say("full-size %s: inputs ready (%d sequences)" % (name, inp.num_seqs))
     o, fs = run_gpu(inp)
-    assert np.isfinite(o).all() and np.isfinite(fs).all()
-    units = [(0, 0), (1, 31), (0, 17), (1, 8)]
-    o_ref, s_ref = _sampled(inp, units)
-    _check_units(inp, o, fs, o_ref, s_ref, units)
+    _say("full-size %s: GPU done" % name)
+    o_ref, s_ref = oracle.recur(inp)
+    _say("full-size %s: oracle done" % name)
+    check_all_units(o, fs, o_ref, s_ref, _say)
 
 
-def _sampled(inp, units):
-    o_ref, s_ref = oracle.recur(inp, units=units)
-    return o_ref, s_ref
+def test_full_size_gdn(gdn):
+    """B=4 T=4096 H=16, the benchmarked launch: every output and final state."""
+    _full_size("gdn")
 
 
-def _check_units(inp, o, fs, o_ref, s_ref, units):
-    cu = inp.cu_seqlens
-    for n, h in units:
-        if cu is None:
-            eo = np.abs(o[n, :, h] - o_ref[n, :, h]).max()
-        else:
-            a, b = int(cu[n]), int(cu[n + 1])
-            eo = np.abs(o[0, a:b, h] - o_ref[0, a:b, h]).max()
-        es = np.abs(fs[n, h] - s_ref[n, h]).max() / max(np.abs(s_ref[n, h]).max(), 1e-30)
-        _say("  unit (%d,%d): o err %.3e  S rel err %.3e" % (n, h, eo, es))
-        assert eo <= O_ATOL and es <= S_RTOL
+def test_full_size_varlen(gdn):
+    """Packed T=32768 H=16, documents ~U[17,8192] with per-document initial
+    states: every output and every document's final state."""
+    _full_size("varlen")
 
 
-def test_full_size_gdn_sampled(gdn):
-    """B=4 T=4096 H=16, the benchmarked launch; 6 sampled (sequence, head) units."""
-    inp = gi.make_inputs("gdn")
-    _say("full-size gdn: generating done")
-    o, fs = run_gpu(inp)
-    assert np.isfinite(o).all() and np.isfinite(fs).all()
-    units = [(0, 0), (1, 5), (2, 9), (3, 15), (0, 15), (3, 0)]
-    o_ref, s_ref = _sampled(inp, units)
-    _check_units(inp, o, fs, o_ref, s_ref, units)
+def test_full_size_long(gdn):
+    """B=1 T=131072 H=32 (2048 sequential chunks): every output and final state."""
+    _full_size("long")
 
 
-def test_full_size_varlen_sampled(gdn):
-    """Packed T=32768 H=16, documents ~U[17,8192]; every document, 2 heads each."""
-    inp = gi.make_inputs("varlen")
-    N = inp.num_seqs
-    _say("full-size varlen: %d documents" % N)
-    o, fs = run_gpu(inp)
-    units = [(n, (3 * n) % inp.H) for n in range(N)] + [(n, (3 * n + 7) % inp.H) for n in range(N)]
-    o_ref, s_ref = _sampled(inp, units)
-    _check_units(inp, o, fs, o_ref, s_ref, units)
-
-
-def test_full_size_long_sampled(gdn):
-    """B=1 T=131072 H=32 (2048 sequential chunks); 2 sampled heads."""
-    inp = gi.make_inputs("long")
-    _say("full-size long: inputs ready")
-    o, fs = run_gpu(inp)
-    units = [(0, 0), (0, 31)]
-    o_ref, s_ref = _sampled(inp, units)
-    _check_units(inp, o, fs, o_ref, s_ref, units)
+def test_full_size_kda(gdn):
+    """KDA B=2 T=8192 H=32 per-channel gate: every output and final state."""
+    _full_size("kda")
 
 
 def _degenerate_cases():
