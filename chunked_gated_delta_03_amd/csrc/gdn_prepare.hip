@@ -206,7 +206,6 @@ struct PrepSmem {
     u16x8 kst[4][4][64];      // the k blocks in operand order, [block][step][lane]
   } u;
   float T[kChunk * kLdP];     // lower blocks of T
-  uint16_t aqk[kChunk * kLdQ];
   float G[kChunk], beta[kChunk], rq[kChunk], rk[kChunk];
 };
 
@@ -236,13 +235,11 @@ __device__ __forceinline__ f32x4 gram_tile(const u16x8 (&x)[4], const u16x8 (&y)
   return acc;
 }
 
-// T (stride kLdP) and Aqk of one item to HBM, as store_t_aqk; with
+// T (stride kLdP) of one item to HBM in the layout of store_t_aqk; with
 // a.t_ld == 64 only the hi part bf16(T) is stored (the whole-pass layout).
-__device__ __forceinline__ void store_t_aqk_p(const PrepareArgs& a, size_t cm, int tid, const float* sT,
-                                              const uint16_t* sAqk) {
+__device__ __forceinline__ void store_t_p(const PrepareArgs& a, size_t cm, int tid, const float* sT) {
   const int tld = a.t_ld;
   uint16_t* tdst = a.tmat + cm * (kChunk * (size_t)tld);
-  uint16_t* qdst = a.aqk + cm * (kChunk * kChunk);
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int idx = pass * 256 + tid;
@@ -261,9 +258,6 @@ __device__ __forceinline__ void store_t_aqk_p(const PrepareArgs& a, size_t cm, i
     *reinterpret_cast<uint4*>(tdst + r * tld + 8 * m) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
     if (tld == 2 * kChunk)
       *reinterpret_cast<uint4*>(tdst + r * tld + kChunk + 8 * m) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    const u16x4 q0 = up0 ? u16x4{0, 0, 0, 0} : *reinterpret_cast<const u16x4*>(sAqk + r * kLdQ + c0);
-    const u16x4 q1 = up1 ? u16x4{0, 0, 0, 0} : *reinterpret_cast<const u16x4*>(sAqk + r * kLdQ + c0 + 16);
-    *reinterpret_cast<u16x8*>(qdst + r * kChunk + 8 * m) = cat4(q0, q1);
   }
 }
 
@@ -312,7 +306,7 @@ __device__ __forceinline__ void gdn_prepare_wave(const PrepareArgs& a, PrepSmem&
   auto store_prev = [&]() {
     const int c = prev / a.H, h = prev - (prev / a.H) * a.H;
     const size_t cm = (size_t)h * a.geo.NT + c;
-    store_t_aqk_p(a, cm, tid, sm.T, sm.aqk);
+    store_t_p(a, cm, tid, sm.T);
     float* vd = a.vec + cm * (kVecRows * kChunk);
     vd[W * 64 + lane] = vrow0;
     vd[(W + 4) * 64 + lane] = vrow1;
@@ -320,7 +314,7 @@ __device__ __forceinline__ void gdn_prepare_wave(const PrepareArgs& a, PrepSmem&
 
   if ((int)blockIdx.x < n_items) fetch(blockIdx.x);
   for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
-    const int c = it / a.H;
+    const int c = it / a.H, hh = it - c * a.H;
     const ChunkInfo ci = a.geo.chunk(c);
 
     // own k block to LDS (the A area is free since the previous item's last
@@ -328,7 +322,7 @@ __device__ __forceinline__ void gdn_prepare_wave(const PrepareArgs& a, PrepSmem&
 #pragma unroll
     for (int s = 0; s < 4; ++s) sm.u.kst[W][s][lane] = kw[s];
     const f32x4 kkD = gram_tile(kw, kw);
-    const f32x4 qkD = gram_tile(qw, kw);
+    const f32x4 qkD = gram_tile(kw, qw);  // transposed: lane (g, l) holds row l
     // norms of this wave's 16 rows; lanes l, l+16, l+32, l+48 share a row
     {
       float sk = sumsq_blk(kw), sq = sumsq_blk(qw);
@@ -366,17 +360,17 @@ __device__ __forceinline__ void gdn_prepare_wave(const PrepareArgs& a, PrepSmem&
         kblk(0, b0); kblk(2, b1);
         kk0 = gram_tile(kw, b0);  // (1,0)
         kk1 = gram_tile(b1, kw);  // (2,1)
-        qk0 = gram_tile(qw, b0);  // q (1,0)
+        qk0 = gram_tile(b0, qw);  // q (1,0), transposed
       } else if constexpr (W == 2) {
         kblk(0, b0); kblk(1, b1); kblk(3, b2);
         kk0 = gram_tile(b2, kw);  // (3,2)
-        qk0 = gram_tile(qw, b0);  // q (2,0)
-        qk1 = gram_tile(qw, b1);  // q (2,1)
+        qk0 = gram_tile(b0, qw);  // q (2,0)
+        qk1 = gram_tile(b1, qw);  // q (2,1)
       } else {
         kblk(0, b0); kblk(1, b1); kblk(2, b2);
-        qk0 = gram_tile(qw, b0);  // q (3,0)
-        qk1 = gram_tile(qw, b1);  // q (3,1)
-        qk2 = gram_tile(qw, b2);  // q (3,2)
+        qk0 = gram_tile(b0, qw);  // q (3,0)
+        qk1 = gram_tile(b1, qw);  // q (3,1)
+        qk2 = gram_tile(b2, qw);  // q (3,2)
       }
     }
     const int next = min(it + (int)gridDim.x, n_items - 1);
@@ -399,20 +393,41 @@ __device__ __forceinline__ void gdn_prepare_wave(const PrepareArgs& a, PrepSmem&
 #pragma unroll
       for (int e = 0; e < 4; ++e) sm.u.A[(i0 + e) * kLdP + j] = -bia[e] * kia[e] * rj * __expf(gia[e] - gj) * kk[e];
     };
-    auto put_qk = [&](int J, const f32x4& qk) {  // block row W
-      const int i0 = 16 * W + 4 * g, j = 16 * J + l;
-      const float4 gi = *reinterpret_cast<const float4*>(sm.G + i0);
-      const float4 qi = *reinterpret_cast<const float4*>(sm.rq + i0);
-      const float gj = sm.G[j], rj = sm.rk[j] * a.scale;
-      const float gia[4] = {gi.x, gi.y, gi.z, gi.w}, qia[4] = {qi.x, qi.y, qi.z, qi.w};
+    // Aqk_ij = scale rq_i rk_j e^(G_i - G_j) (q_i . k_j), i >= j, for row
+    // i = 16 W + l and columns 16 J + 4 g + e of the transposed tile, as four
+    // bf16; the stored position 8 p of a row holds columns 4p..4p+3 and
+    // 16+4p..16+4p+3 of its 32-column half (perm_col), so a lane's tiles
+    // J = 0, 1 and J = 2, 3 make its two 16-byte pieces of the row
+    auto aqk4 = [&](int J, const f32x4& qkt) {
+      const int i = 16 * W + l, j0 = 16 * J + 4 * g;
+      const float gi = sm.G[i], qi = sm.rq[i];
+      const float4 gj = *reinterpret_cast<const float4*>(sm.G + j0);
+      const float4 kj = *reinterpret_cast<const float4*>(sm.rk + j0);
+      const float gja[4] = {gj.x, gj.y, gj.z, gj.w}, kja[4] = {kj.x, kj.y, kj.z, kj.w};
+      float x[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float m = (J < W || 4 * g + e >= l) ? 1.0f : 0.0f;
-        sm.aqk[(i0 + e) * kLdQ + j] =
-            __builtin_bit_cast(uint16_t, (__bf16)(m * qia[e] * rj * __expf((gia[e] - gj) * m) * qk[e]));
+        const float m = (J < W || l >= 4 * g + e) ? 1.0f : 0.0f;
+        x[e] = m * qi * (kja[e] * a.scale) * __expf((gi - gja[e]) * m) * qkt[e];
       }
+      return uint2{pack2(x[0], x[1]), pack2(x[2], x[3])};
     };
-    put_qk(W, qkD);
+    {
+      const uint2 zz = {0u, 0u};
+      uint2 t0 = zz, t1 = zz, t2 = zz, t3 = zz;
+      if constexpr (W == 0) {
+        t0 = aqk4(0, qkD);
+      } else if constexpr (W == 1) {
+        t0 = aqk4(0, qk0); t1 = aqk4(1, qkD);
+      } else if constexpr (W == 2) {
+        t0 = aqk4(0, qk0); t1 = aqk4(1, qk1); t2 = aqk4(2, qkD);
+      } else {
+        t0 = aqk4(0, qk0); t1 = aqk4(1, qk1); t2 = aqk4(2, qk2); t3 = aqk4(3, qkD);
+      }
+      uint16_t* qrow = a.aqk + ((size_t)hh * a.geo.NT + c) * (kChunk * kChunk) + (16 * W + l) * kChunk;
+      *reinterpret_cast<uint4*>(qrow + 8 * g) = make_uint4(t0.x, t0.y, t1.x, t1.y);
+      *reinterpret_cast<uint4*>(qrow + 8 * (4 + g)) = make_uint4(t2.x, t2.y, t3.x, t3.y);
+    }
     if constexpr (W == 0) {
       put_kk(2, 0, kk0);
       put_kk(3, 0, kk1);
@@ -420,15 +435,8 @@ __device__ __forceinline__ void gdn_prepare_wave(const PrepareArgs& a, PrepSmem&
     } else if constexpr (W == 1) {
       put_kk(1, 0, kk0);
       put_kk(2, 1, kk1);
-      put_qk(0, qk0);
     } else if constexpr (W == 2) {
       put_kk(3, 2, kk0);
-      put_qk(0, qk0);
-      put_qk(1, qk1);
-    } else {
-      put_qk(0, qk0);
-      put_qk(1, qk1);
-      put_qk(2, qk2);
     }
 
     // diagonal block W: N (strictly lower part of A's block) and N^T in the

@@ -64,13 +64,15 @@ struct alignas(16) Smem {
   static constexpr int NCW = 2 * NCB;    // compute waves
   struct alignas(16) Buf {
     uint16_t k[kChunk * kDim];           // swizzled 16-byte pieces
-    uint16_t q[kChunk * kDim];
     uint16_t t[kChunk * kChunk];         // bf16(T), swizzled pieces (8 per row)
     uint16_t aqk[kChunk * kChunk];       // swizzled pieces (8 per row)
     uint16_t v[kChunk * BV];             // v rows of this V-block
     float vec[kVecRows * kChunk];
   };
   Buf buf[2];
+  // q is read only before the pair barrier, and the loaders write the next
+  // chunk's q after it: one buffer
+  uint16_t q[kChunk * kDim];
   // per wave: its partial k S (4 tiles) and the partner's two tiles of its
   // partial q S; lane-major 16-byte slots
   f32x4 xch[NCW][6][64];
@@ -141,7 +143,7 @@ __global__ __launch_bounds__((2 * NCB + kLoaders) * 64) void gdn_state_kernel(Fw
         const int slot = 8 * ((idx & 15) ^ (r & 15));
         if (part == 0) {
           *reinterpret_cast<u32x4*>(B.k + r * kDim + slot) = kr[p];
-          if constexpr (COMPUTE_O) *reinterpret_cast<u32x4*>(B.q + r * kDim + slot) = qr[p];
+          if constexpr (COMPUTE_O) *reinterpret_cast<u32x4*>(sm.q + r * kDim + slot) = qr[p];
         }
       }
       if (part == 0) return;
@@ -254,7 +256,7 @@ __global__ __launch_bounds__((2 * NCB + kLoaders) * 64) void gdn_state_kernel(Fw
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
           fk[it] = *reinterpret_cast<const u16x8*>(B.k + (16 * it + l16) * kDim + slot);
-          if constexpr (COMPUTE_O) fq[it] = *reinterpret_cast<const u16x8*>(B.q + (16 * it + l16) * kDim + slot);
+          if constexpr (COMPUTE_O) fq[it] = *reinterpret_cast<const u16x8*>(sm.q + (16 * it + l16) * kDim + slot);
         }
 #pragma unroll
         for (int it = 0; it < 4; ++it) X[it] = mfma16(fk[it], Shi[sp], X[it]);
