@@ -8,11 +8,11 @@ Two independent fp64 definitions of the same result:
 
 * :func:`recur` -- the token-by-token recurrence, in plain C (``recur.c``),
   OpenMP over (sequence, head) units. This is the reference result.
-* :func:`chunk` (module ``oracle.chunk``) -- the chunked rewrite as the
-  hyper-parallel "Diff Coverage" page of 2026-09-10 writes it out in numpy
-  fp64 (``torch_chunk_gated_delta_rule`` / ``_prepare_gdn_chunks_for_summary``
-  / ``_run_prepared_gdn_chunks``), exporting its intermediates for stage
-  parity.
+* :func:`chunk` (module ``oracle.chunk``) -- the chunk form of the same
+  recurrence in numpy fp64, derived in that module's header from the token
+  recurrence (the method of the hyper-parallel "Diff Coverage" page of
+  2026-09-10, ``torch_chunk_gated_delta_rule``), exporting its per-chunk
+  intermediates (T, U, W, the output matrix, h, v_new) for stage parity.
 
 Besides these, :func:`state_summary` / :func:`apply_state_summary` (the
 affine summary of a sequence) and :func:`short_conv` (module ``oracle.conv``,

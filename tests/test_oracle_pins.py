@@ -2,7 +2,7 @@
 
 Each test names the part of the oracle it pins and the plausible mistake it
 would catch. Both oracle functions are covered: ``oracle.recur`` (C token
-recurrence) and ``oracle.chunk`` (numpy chunked rewrite).
+recurrence) and ``oracle.chunk`` (numpy chunk form derived from it).
 """
 import glob
 import json
@@ -72,10 +72,10 @@ CASES = [
 
 @pytest.mark.parametrize("T,C,K,kda,flags,init", CASES)
 def test_chunk_form_equals_recurrence(oracle_lib, T, C, K, kda, flags, init):
-    """The chunked rewrite (pages' algorithm) and the token recurrence are two
-    independent codes; they must agree to rounding. Catches a dropped term in
-    the WY terms, a wrong mask (diagonal in A or missing in the QK term), a
-    wrong decay exponent, the forward substitution, partial-chunk padding."""
+    """The chunk form and the token recurrence are two independent codes;
+    they must agree to rounding. Catches a dropped term in the WY terms, a
+    wrong mask (diagonal in A or missing in the QK term), a wrong decay
+    exponent, a wrong triangular system for T, partial-chunk padding."""
     rng = np.random.default_rng(T * 1000 + C + K + kda)
     inp = gi.random_problem(rng, 2, T, 3, K, K, kda=kda, with_initial_state=init, flags=flags)
     o1, s1 = oracle.recur(inp)
