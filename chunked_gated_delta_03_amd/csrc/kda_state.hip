@@ -83,8 +83,8 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
 
   // ------------------------------------------------------------- loaders
   if constexpr (COMPUTE_O) {
-    if (w >= NCW) {
-      // Whole pass: the decayed operands come from the prepare kernel; the
+    if (w >= NCW && a.kdec) {
+      // Whole pass with a.kdec: the decayed operands come from the prepare kernel; the
       // loaders copy them (16-byte pieces, loaded one chunk ahead) into the
       // same windows as below.
       constexpr int NL = 64 * kLoadersK;
@@ -202,7 +202,9 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
     u32x4 kgh[1024 / NL], kgl[1024 / NL];
     float4 dec0, dec1;
 
-    auto fetch = [&](int jc) {
+    // k, q and the cumulative gate of chunk jc (for its build); T, Aqk, v
+    // and the row vectors of chunk jc (for its late window)
+    auto fetch_kqg = [&](int jc) {
       const int tok0 = si.tok0 + jc * kChunk;
       const int rem = si.len - jc * kChunk;
       const int len = rem < kChunk ? rem : kChunk;
@@ -216,10 +218,17 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
         if constexpr (COMPUTE_O) qr[p] = r < len ? *reinterpret_cast<const u32x4*>(a.q + off) : u32x4{0, 0, 0, 0};
         g0[p] = *reinterpret_cast<const float4*>(gk + r * kDim + 8 * pc);
         g1[p] = *reinterpret_cast<const float4*>(gk + r * kDim + 8 * pc + 4);
-        tr[p] = reinterpret_cast<const u32x4*>(a.tmat + cm * (kChunk * 2 * kChunk))[idx];
       }
       gl0 = *reinterpret_cast<const float4*>(gk + 63 * kDim + 8 * pc);
       gl1 = *reinterpret_cast<const float4*>(gk + 63 * kDim + 8 * pc + 4);
+    };
+    auto fetch_tav = [&](int jc) {
+      const int tok0 = si.tok0 + jc * kChunk;
+      const int rem = si.len - jc * kChunk;
+      const int len = rem < kChunk ? rem : kChunk;
+      const size_t cm = (size_t)h * a.geo.NT + si.c0 + jc;
+#pragma unroll
+      for (int p = 0; p < 1024 / NL; ++p) tr[p] = reinterpret_cast<const u32x4*>(a.tmat + cm * (kChunk * 2 * kChunk))[p * NL + ltid];
       if constexpr (COMPUTE_O) {
 #pragma unroll
         for (int p = 0; p < 512 / NL; ++p) ar[p] = reinterpret_cast<const u32x4*>(a.aqk + cm * (kChunk * kChunk))[p * NL + ltid];
@@ -297,19 +306,24 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
     };
 
     // Same barrier sequence as the compute waves: one before the loop, two
-    // per chunk. Chunk jc's late arrays go in before its pair barrier; the
-    // next chunk is loaded meanwhile and, after the pair barrier, its kd and
-    // qd are written (past the end the last chunk is repeated, harmlessly).
+    // per chunk. Chunk jc's late arrays go in before its pair barrier and
+    // chunk jc+1's T, Aqk, v and row vectors are loaded; after the pair
+    // barrier, chunk jc+1's decayed operands are built from the k, q and gate
+    // loaded a chunk earlier, and chunk jc+2's are loaded (past the end the
+    // last chunk is repeated, harmlessly). Every load has a chunk to arrive.
     if (si.nch > 0) {
-      fetch(0);
+      fetch_kqg(0);
+      fetch_tav(0);
       build();
+      fetch_kqg(min(1, last));
     }
     __syncthreads();
     for (int jc = 0; jc < si.nch; ++jc) {
       put_late();
-      fetch(min(jc + 1, last));
+      fetch_tav(min(jc + 1, last));
       __syncthreads();
       build();
+      fetch_kqg(min(jc + 2, last));
       __syncthreads();
     }
     return;
@@ -351,7 +365,7 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
     for (int jc = 0; jc < si.nch; ++jc) {
       const int c = si.c0 + jc;
       const size_t cm = (size_t)h * a.geo.NT + c;
-      const int tb = COMPUTE_O ? (jc & 1) : 0;  // buffer of T, row vectors, decays
+      const int tb = (COMPUTE_O && a.kdec) ? (jc & 1) : 0;  // buffer of T, row vectors, decays
 
       if constexpr (COMPUTE_O) {
         if (jc >= 1) store_o(jc - 1);
