@@ -136,9 +136,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // kda_gate: a KDA pass whose state kernel forms the decayed operands from the
 // cumulative gate (state summary) instead of reading them from prepare.
-// t_ld: row length of the stored T, 128 (bf16 hi | lo: the stage entries, the
-// backward and KDA) or 64 (bf16 hi only: the GDN whole pass and summary).
-Layout layout_for(const Problem& p, bool with_intermediates, bool kda_gate = false, int t_ld = 128) {
+Layout layout_for(const Problem& p, bool with_intermediates, bool kda_gate = false) {
   Layout L;
   size_t off = 0;
   L.tab = off;
@@ -146,7 +144,7 @@ Layout layout_for(const Problem& p, bool with_intermediates, bool kda_gate = fal
   if (with_intermediates) {
     const size_t cmH = (size_t)p.NT * p.H;
     L.tmat = off;
-    off += align256(cmH * GDN_CHUNK * (size_t)t_ld * sizeof(uint16_t));  // T, bf16 hi (| lo)
+    off += align256(cmH * GDN_CHUNK * 2 * GDN_CHUNK * sizeof(uint16_t));  // T, bf16 hi | lo
     L.aqk = off;
     off += align256(cmH * GDN_CHUNK * GDN_CHUNK * sizeof(uint16_t));
     L.vec = off;
@@ -161,9 +159,6 @@ Layout layout_for(const Problem& p, bool with_intermediates, bool kda_gate = fal
   return L;
 }
 
-// Row length of T in the whole-pass and summary workspaces: the GDN state
-// kernel reads only bf16(T), the KDA one the hi | lo pair.
-int whole_pass_t_ld(bool kda) { return kda ? 128 : 64; }
 
 // Pinned host staging for chunk tables: a small ring per process; a slot is
 // reused only after the copy that last read it has completed.
@@ -394,8 +389,7 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
   if (rc) return rc;
 
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  const int t_ld = whole_pass_t_ld(kda);
-  const Layout L = layout_for(p, true, false, t_ld);
+  const Layout L = layout_for(p, true);
   Workspace W;
   rc = acquire_workspace(workspace, workspace_bytes, L.total, stream, W);
   if (rc) return rc;
@@ -408,7 +402,6 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
   if (timing && (rc = timing_mark(g_timing_recs, 0, stream))) return rc;
 
   gdn::PrepareArgs pa{};
-  pa.t_ld = t_ld;
   pa.q = static_cast<const uint16_t*>(q);
   pa.k = static_cast<const uint16_t*>(k);
   pa.g = g;
@@ -430,7 +423,6 @@ int chunk_fwd(bool kda, const void* q, const void* k, const void* v, const float
   if (timing && (rc = timing_mark(g_timing_recs, 1, stream))) return rc;
 
   gdn::FwdArgs fa{};
-  fa.t_ld = t_ld;
   fa.q = pa.q;
   fa.k = pa.k;
   fa.v = static_cast<const uint16_t*>(v);
@@ -504,8 +496,7 @@ int state_summary(bool kda, const void* q, const void* k, const void* v, const f
   if (rc) return rc;
 
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  const int t_ld = whole_pass_t_ld(kda);
-  const Layout L = layout_for(p, true, true, t_ld);
+  const Layout L = layout_for(p, true, true);
   Workspace W;
   rc = acquire_workspace(workspace, workspace_bytes, L.total, stream, W);
   if (rc) return rc;
@@ -516,7 +507,6 @@ int state_summary(bool kda, const void* q, const void* k, const void* v, const f
   const gdn::Geometry geo = make_geometry(p, W.base + L.tab);
 
   gdn::PrepareArgs pa{};
-  pa.t_ld = t_ld;
   pa.q = static_cast<const uint16_t*>(q ? q : k);  // only the unused Aqk depends on q
   pa.k = static_cast<const uint16_t*>(k);
   pa.g = g;
@@ -537,7 +527,6 @@ int state_summary(bool kda, const void* q, const void* k, const void* v, const f
   if (e != hipSuccess) return hip_fail(e, "prepare launch");
 
   gdn::FwdArgs fa{};
-  fa.t_ld = t_ld;
   fa.k = pa.k;
   fa.v = static_cast<const uint16_t*>(v);
   fa.tmat = pa.tmat;
@@ -631,7 +620,6 @@ int chunk_bwd(const void* q, const void* k, const void* v, const float* g, const
   if (g_timing && (rc = bwd_timing_mark(0, stream))) return rc;
 
   gdn::PrepareArgs pa{};
-  pa.t_ld = 128;  // T as bf16 hi | lo
   pa.q = static_cast<const uint16_t*>(q);
   pa.k = static_cast<const uint16_t*>(k);
   pa.g = g;
@@ -650,7 +638,6 @@ int chunk_bwd(const void* q, const void* k, const void* v, const float* g, const
   if (e != hipSuccess) return hip_fail(e, "prepare launch");
 
   gdn::FwdArgs fa{};
-  fa.t_ld = 128;  // T as bf16 hi | lo
   fa.k = pa.k;
   fa.v = static_cast<const uint16_t*>(v);
   fa.tmat = pa.tmat;
@@ -769,7 +756,7 @@ static size_t workspace_bytes(bool kda, int32_t B, int32_t T, int32_t H, int32_t
     fail(GDN_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags & ~kKnownFlags);
     return 0;
   }
-  return layout_for(p, true, false, whole_pass_t_ld(kda)).total;
+  return layout_for(p, true).total;
 }
 
 size_t gdn_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
@@ -802,7 +789,7 @@ int gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const flo
   Problem p;
   int rc = check_shape(B, T, H, K, V, num_seqs, nullptr, p);
   if (rc) return rc;
-  const size_t need = layout_for(p, true, false, whole_pass_t_ld(false)).total;
+  const size_t need = layout_for(p, true).total;
   if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
     return fail(GDN_ERR_INVALID_ARGUMENT,
                 "problem needs %zu bytes of scratch, above the fixed %zu bytes of gdn_chunk_fwd_noalloc "
@@ -913,7 +900,7 @@ size_t gdn_state_summary_workspace_bytes(int32_t kda, int32_t B, int32_t T, int3
   Problem p;
   p.kda = kda != 0;
   if (check_shape(B, T, H, K, V, num_seqs, cu_seqlens, p)) return 0;
-  return layout_for(p, true, true, whole_pass_t_ld(p.kda)).total;
+  return layout_for(p, true, true).total;
 }
 
 int gdn_state_summary_apply(const float* transition, const float* state_ext, const float* state_in,
@@ -1051,7 +1038,6 @@ int gdn_stage_prepare(int32_t kda, const void* q, const void* k, const float* g,
   rc = stage_begin(kda, cu_seqlens, num_seqs, B, T, H, K, V, stream, ctx);
   if (rc) return rc;
   gdn::PrepareArgs pa{};
-  pa.t_ld = 128;  // T as bf16 hi | lo
   pa.q = static_cast<const uint16_t*>(q);
   pa.k = static_cast<const uint16_t*>(k);
   pa.g = g;
@@ -1153,7 +1139,6 @@ static int kda_bwd_impl(const void* q, const void* k, const void* v, const float
 
   // forward recompute: T, Aqk, row vectors, cumulative gate; states and v_new
   gdn::PrepareArgs pa{};
-  pa.t_ld = 128;  // T as bf16 hi | lo
   pa.q = static_cast<const uint16_t*>(q);
   pa.k = static_cast<const uint16_t*>(k);
   pa.g = g;
@@ -1173,7 +1158,6 @@ static int kda_bwd_impl(const void* q, const void* k, const void* v, const float
   hipError_t e = gdn::launch_prepare(true, pa, stream);
   if (e != hipSuccess) return hip_fail(e, "prepare launch");
   gdn::FwdArgs fa{};
-  fa.t_ld = 128;  // T as bf16 hi | lo
   fa.k = pa.k;
   fa.v = static_cast<const uint16_t*>(v);
   fa.tmat = pa.tmat;
@@ -1321,7 +1305,6 @@ int kda_bwd_state_pass(const void* q, const void* k, const float* g, const void*
   const gdn::Geometry geo = make_geometry(p, W.base + L.tab);
 
   gdn::PrepareArgs pa{};
-  pa.t_ld = 128;  // T as bf16 hi | lo
   pa.q = static_cast<const uint16_t*>(q);
   pa.k = static_cast<const uint16_t*>(k);
   pa.g = g;
@@ -1374,7 +1357,6 @@ int gdn_stage_fwd_h(int32_t kda, const void* k, const void* v, const void* tmat,
   int rc = stage_begin(kda, cu_seqlens, num_seqs, B, T, H, K, V, stream, ctx);
   if (rc) return rc;
   gdn::FwdArgs fa{};
-  fa.t_ld = 128;  // T as bf16 hi | lo
   fa.k = static_cast<const uint16_t*>(k);
   fa.v = static_cast<const uint16_t*>(v);
   fa.tmat = static_cast<const uint16_t*>(tmat);

@@ -13,7 +13,7 @@ struct PrepareArgs {
   const uint16_t* k;
   const float* g;
   const uint16_t* beta;
-  uint16_t* tmat;  // [H,NT,64,t_ld] bf16 hi (| lo), permuted columns
+  uint16_t* tmat;  // [H,NT,64,128] bf16 hi | lo, permuted columns
   uint16_t* aqk;   // [H,NT,64,64] bf16, permuted columns
   float* vec;      // [H,NT,8,64]
   float* gk;       // [H,NT,64,128], KDA stage entry only
@@ -28,7 +28,6 @@ struct PrepareArgs {
   float scale;
   uint32_t flags;
   int cus;         // compute units of the device (grid size of persistent launches)
-  int t_ld;        // row length of tmat: 128 (hi | lo) or 64 (hi only; GDN prepare only)
 };
 
 // KDA whole pass: the decayed operands of one (chunk, head), written by the
@@ -46,7 +45,7 @@ struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  const uint16_t* tmat;  // [H,NT,64,t_ld] bf16 hi (| lo), permuted columns
+  const uint16_t* tmat;  // [H,NT,64,128] bf16 hi | lo, permuted columns
   const uint16_t* aqk;   // [H,NT,64,64] bf16, permuted columns
   const float* vec;
   const float* gk;       // KDA stage entry only
@@ -59,7 +58,6 @@ struct FwdArgs {
   Geometry geo;
   int H;
   int s_identity;        // state summary transition: S0 = I and v taken as 0 (s0 ignored)
-  int t_ld;              // row length of tmat (the GDN state kernel reads its first 64 columns)
 };
 
 struct FinArgs {

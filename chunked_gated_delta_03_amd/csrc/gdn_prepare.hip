@@ -235,11 +235,10 @@ __device__ __forceinline__ f32x4 gram_tile(const u16x8 (&x)[4], const u16x8 (&y)
   return acc;
 }
 
-// T (stride kLdP) of one item to HBM in the layout of store_t_aqk; with
-// a.t_ld == 64 only the hi part bf16(T) is stored (the whole-pass layout).
+// T (stride kLdP) of one item to HBM in the layout of store_t_aqk: row r
+// holds 64 bf16 hi values, then the 64 lo values.
 __device__ __forceinline__ void store_t_p(const PrepareArgs& a, size_t cm, int tid, const float* sT) {
-  const int tld = a.t_ld;
-  uint16_t* tdst = a.tmat + cm * (kChunk * (size_t)tld);
+  uint16_t* tdst = a.tmat + cm * (kChunk * 2 * kChunk);
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int idx = pass * 256 + tid;
@@ -255,9 +254,8 @@ __device__ __forceinline__ void store_t_p(const PrepareArgs& a, size_t cm, int t
     split2(x0.z, x0.w, hi[1], lo[1]);
     split2(x1.x, x1.y, hi[2], lo[2]);
     split2(x1.z, x1.w, hi[3], lo[3]);
-    *reinterpret_cast<uint4*>(tdst + r * tld + 8 * m) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    if (tld == 2 * kChunk)
-      *reinterpret_cast<uint4*>(tdst + r * tld + kChunk + 8 * m) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<uint4*>(tdst + r * (2 * kChunk) + 8 * m) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *reinterpret_cast<uint4*>(tdst + r * (2 * kChunk) + kChunk + 8 * m) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
   }
 }
 

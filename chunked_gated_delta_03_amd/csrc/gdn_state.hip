@@ -21,27 +21,25 @@
 // summed through LDS. Both waves then form the whole v_new (T times the
 // right-hand side), update their own K half of S, and finish 32 of the 64
 // output rows. k, q and v enter the MFMAs as the exact bf16 inputs.
-// Precision: the two operands that carry new values into the state, the
-// right-hand side beta v - c (k S) of T(...) and d * v_new of the update, are
-// bf16 hi + lo pairs (about 16 significant bits) with fp32 accumulation; S in
-// k S and q S, and T, enter as single bf16. A rounding of S in k S or of T
-// perturbs only the removal of the state's old value along the chunk's keys,
-// which the delta rule takes out again whenever those keys recur, so it does
-// not build up in the state: in an fp32 simulation of this scheme against the
-// fp64 recurrence the final state stays within about 3e-5 (GDN workload
-// shapes) to 3e-4 (slowly decaying, unit-norm keys) of max |S|, while
-// rounding either of the two new-value operands to bf16 gives 1e-3 to 4e-3.
+// Precision: the operands that carry the state are bf16 hi + lo pairs
+// (about 16 significant bits) with fp32 accumulation: S in k S, T and the
+// right-hand side beta v - c (k S) in T(...), and d * v_new in the update.
+// Only q S (output side, which does not feed the state) uses bf16(S). In an
+// fp32 simulation against the fp64 recurrence this keeps the final state
+// within about 1e-5 of max |S| for every gate tested, including no decay at
+// all over 8192 tokens; rounding S in k S or T to a single bf16 instead gives
+// up to 1.7e-3 there (the errors it writes into the state persist when the
+// gate barely decays), above the 1e-3 bar.
 //
 // Layouts. Row i of state tile t (16 K rows) holds K index perm_col(16 t + i):
 // then the B operand of contraction step s built from tiles 2s, 2s+1 covers
 // K indices 32s + 8g .. 32s + 8g + 7 in lane group g, which an A-operand
 // fragment of a k or q row reads as one 16-byte piece in natural column
-// order. k and q rows (256 bytes) are stored as 16-byte pieces with piece p
-// of row r at slot p ^ (r & 15), T and Aqk rows (128 bytes) with p ^ (r & 7),
-// so that the rows of a fragment read fall on distinct banks; bf16(T) (the
-// first 64 columns of each stored row) and Aqk come from the prepare kernel
-// with permuted columns. k^T for the update and the v columns are read with
-// the transposing LDS read (ds_read_b64_tr_b16).
+// order. k, q and T rows (256 bytes) are stored as 16-byte pieces with piece p
+// of row r at slot p ^ (r & 15), Aqk rows (128 bytes) with p ^ (r & 7), so
+// that the 16 rows of a fragment read fall on distinct banks; T (hi | lo) and
+// Aqk come from the prepare kernel with permuted columns. k^T for the update
+// and the v columns are read with the transposing LDS read (ds_read_b64_tr_b16).
 //
 // Register arrays are indexed with compile-time indices only (the compute
 // loop is specialised per K half): an index that depends on the wave becomes
@@ -64,7 +62,7 @@ struct alignas(16) Smem {
   static constexpr int NCW = 2 * NCB;    // compute waves
   struct alignas(16) Buf {
     uint16_t k[kChunk * kDim];           // swizzled 16-byte pieces
-    uint16_t t[kChunk * kChunk];         // bf16(T), swizzled pieces (8 per row)
+    uint16_t t[kChunk * 2 * kChunk];     // hi | lo, swizzled pieces
     uint16_t aqk[kChunk * kChunk];       // swizzled pieces (8 per row)
     uint16_t v[kChunk * BV];             // v rows of this V-block
     float vec[kVecRows * kChunk];
@@ -107,7 +105,7 @@ __global__ __launch_bounds__((2 * NCB + kLoaders) * 64) void gdn_state_kernel(Fw
     constexpr int NL = 64 * kLoaders;
     constexpr int PPR = BV / 8;              // v pieces per row
     const int ltid = tid - NCW * 64;
-    u32x4 kr[1024 / NL], qr[1024 / NL], tr[512 / NL], ar[512 / NL], vr, er;
+    u32x4 kr[1024 / NL], qr[1024 / NL], tr[1024 / NL], ar[512 / NL], vr, er;
     auto fetch = [&](int jc) {
       const int tok0 = si.tok0 + jc * kChunk;
       const int rem = si.len - jc * kChunk;
@@ -119,13 +117,11 @@ __global__ __launch_bounds__((2 * NCB + kLoaders) * 64) void gdn_state_kernel(Fw
         const size_t off = ((size_t)(tok0 + r) * H + h) * kDim + 8 * (idx & 15);
         kr[p] = r < len ? *reinterpret_cast<const u32x4*>(a.k + off) : u32x4{0, 0, 0, 0};
         if constexpr (COMPUTE_O) qr[p] = r < len ? *reinterpret_cast<const u32x4*>(a.q + off) : u32x4{0, 0, 0, 0};
+        tr[p] = reinterpret_cast<const u32x4*>(a.tmat + cm * (kChunk * 2 * kChunk))[idx];
       }
-      const uint16_t* tsrc = a.tmat + cm * (kChunk * (size_t)a.t_ld);
+      if constexpr (COMPUTE_O) {
 #pragma unroll
-      for (int p = 0; p < 512 / NL; ++p) {
-        const int idx = p * NL + ltid, r = idx >> 3;
-        tr[p] = *reinterpret_cast<const u32x4*>(tsrc + r * a.t_ld + 8 * (idx & 7));
-        if constexpr (COMPUTE_O) ar[p] = reinterpret_cast<const u32x4*>(a.aqk + cm * (kChunk * kChunk))[idx];
+        for (int p = 0; p < 512 / NL; ++p) ar[p] = reinterpret_cast<const u32x4*>(a.aqk + cm * (kChunk * kChunk))[p * NL + ltid];
       }
       if (ltid < 64 * PPR) {
         const int r = ltid / PPR;
@@ -144,15 +140,17 @@ __global__ __launch_bounds__((2 * NCB + kLoaders) * 64) void gdn_state_kernel(Fw
         if (part == 0) {
           *reinterpret_cast<u32x4*>(B.k + r * kDim + slot) = kr[p];
           if constexpr (COMPUTE_O) *reinterpret_cast<u32x4*>(sm.q + r * kDim + slot) = qr[p];
+        } else {
+          *reinterpret_cast<u32x4*>(B.t + r * (2 * kChunk) + slot) = tr[p];
         }
       }
       if (part == 0) return;
+      if constexpr (COMPUTE_O) {
 #pragma unroll
-      for (int p = 0; p < 512 / NL; ++p) {
-        const int idx = p * NL + ltid, r = idx >> 3;
-        const int slot = 8 * ((idx & 7) ^ (r & 7));
-        *reinterpret_cast<u32x4*>(B.t + r * kChunk + slot) = tr[p];
-        if constexpr (COMPUTE_O) *reinterpret_cast<u32x4*>(B.aqk + r * kChunk + slot) = ar[p];
+        for (int p = 0; p < 512 / NL; ++p) {
+          const int idx = p * NL + ltid, r = idx >> 3;
+          *reinterpret_cast<u32x4*>(B.aqk + r * kChunk + 8 * ((idx & 7) ^ (r & 7))) = ar[p];
+        }
       }
       if (ltid < 64 * PPR) *reinterpret_cast<u32x4*>(B.v + 8 * ltid) = vr;
       if (ltid < kVecRows * kChunk / 4) *reinterpret_cast<u32x4*>(B.vec + 4 * ltid) = er;
@@ -237,11 +235,11 @@ __global__ __launch_bounds__((2 * NCB + kLoaders) * 64) void gdn_state_kernel(Fw
           for (int e = 0; e < 4; ++e) hd[(size_t)srow(t, e) * kDim + colw + l16] = S[t][e];
       }
 
-      // partial X = k S_hi and o_inter = q S_hi over this wave's K half
+      // partial X = k S and o_inter = q S_hi over this wave's K half
       // (contraction steps 2 kh, 2 kh + 1)
-      u16x8 Shi[2];
-      Shi[0] = pack_tiles(S[0], S[1]);
-      Shi[1] = pack_tiles(S[2], S[3]);
+      u16x8 Shi[2], Slo[2];
+      split_tiles(S[0], S[1], Shi[0], Slo[0]);
+      split_tiles(S[2], S[3], Shi[1], Slo[1]);
       f32x4 X[4], OI[4];
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
@@ -264,6 +262,8 @@ __global__ __launch_bounds__((2 * NCB + kLoaders) * 64) void gdn_state_kernel(Fw
 #pragma unroll
           for (int it = 0; it < 4; ++it) OI[it] = mfma16(fq[it], Shi[sp], OI[it]);
         }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) X[it] = mfma16(fk[it], Slo[sp], X[it]);
       }
 
       // post the partial sums, then add the partner's
@@ -301,16 +301,20 @@ __global__ __launch_bounds__((2 * NCB + kLoaders) * 64) void gdn_state_kernel(Fw
         split_tiles(y2[0], y2[1], yhi, ylo);
       };
 
-      // v_new = bf16(T) (Y_hi + Y_lo) (all 64 rows), four accumulators. T is
-      // lower triangular: rows 0..31 have no terms in contraction step 1.
+      // v_new = T Y (all 64 rows), three split products, four accumulators.
+      // T is lower triangular: rows 0..31 have no terms in contraction step 1.
       f32x4 VN[4];
       {
-        u16x8 th[4][2];
+        u16x8 th[4][2], tl[4][2];
 #pragma unroll
         for (int io = 0; io < 4; ++io) {
-          const uint16_t* row = B.t + (16 * io + l16) * kChunk;
-          th[io][0] = *reinterpret_cast<const u16x8*>(row + 8 * (g4 ^ (l16 & 7)));
-          if (io >= 2) th[io][1] = *reinterpret_cast<const u16x8*>(row + 8 * ((4 + g4) ^ (l16 & 7)));
+          const uint16_t* row = B.t + (16 * io + l16) * (2 * kChunk);
+          th[io][0] = *reinterpret_cast<const u16x8*>(row + 8 * (g4 ^ l16));
+          tl[io][0] = *reinterpret_cast<const u16x8*>(row + 8 * ((8 + g4) ^ l16));
+          if (io >= 2) {
+            th[io][1] = *reinterpret_cast<const u16x8*>(row + 8 * ((4 + g4) ^ l16));
+            tl[io][1] = *reinterpret_cast<const u16x8*>(row + 8 * ((12 + g4) ^ l16));
+          }
           VN[io] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         u16x8 Yhi[2], Ylo[2];
@@ -321,9 +325,13 @@ __global__ __launch_bounds__((2 * NCB + kLoaders) * 64) void gdn_state_kernel(Fw
 #pragma unroll
         for (int io = 0; io < 4; ++io) VN[io] = mfma16(th[io][0], Ylo[0], VN[io]);
 #pragma unroll
+        for (int io = 0; io < 4; ++io) VN[io] = mfma16(tl[io][0], Yhi[0], VN[io]);
+#pragma unroll
         for (int io = 2; io < 4; ++io) VN[io] = mfma16(th[io][1], Yhi[1], VN[io]);
 #pragma unroll
         for (int io = 2; io < 4; ++io) VN[io] = mfma16(th[io][1], Ylo[1], VN[io]);
+#pragma unroll
+        for (int io = 2; io < 4; ++io) VN[io] = mfma16(tl[io][1], Yhi[1], VN[io]);
       }
       if constexpr (STORE_H) {
         float* vd = a.vnew_out + cm * (kChunk * kDim);

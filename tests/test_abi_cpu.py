@@ -150,10 +150,10 @@ def test_num_chunks(gdn):
 
 
 def test_workspace_bytes(gdn):
-    # per (chunk, head): T (GDN: bf16; KDA: bf16 hi | lo), Aqk bf16, 8 fp32 row vectors
+    # per (chunk, head): T bf16 hi | lo, Aqk bf16, 8 fp32 row vectors
     a = gdn.workspace_bytes(4, 4096, 16)
     nt = 4 * 64
-    per = 64 * 64 * 2 + 64 * 64 * 2 + 8 * 64 * 4
+    per = 64 * 64 * 4 + 64 * 64 * 2 + 8 * 64 * 4
     assert a >= 16 * nt * per
     assert a % 256 == 0
     b = gdn.workspace_bytes(1, 150, 16, cu_seqlens=[0, 1, 18, 82, 150])
@@ -223,7 +223,7 @@ def test_state_summary_workspace_and_apply_validation(gdn):
     ws = gdn.lib.gdn_state_summary_workspace_bytes
     a = ws(0, 1, 8192, 32, 128, 128, 1, None)
     k = ws(1, 1, 8192, 32, 128, 128, 1, None)
-    per = 64 * 64 * 2 + 64 * 64 * 2 + 8 * 64 * 4        # GDN: T bf16
+    per = 64 * 64 * 4 + 64 * 64 * 2 + 8 * 64 * 4        # GDN: T hi | lo
     assert a >= 32 * 128 * per and a % 256 == 0
     per_kda = 64 * 64 * 4 + 64 * 64 * 2 + 8 * 64 * 4    # KDA: T hi | lo, plus the cumulative gate
     assert k >= 32 * 128 * (per_kda + 64 * 128 * 4)

@@ -52,6 +52,13 @@ def _problems_reduced():
         # 64+ (sequence, head) units: the state kernel's four-compute-wave form
         ("wide_B4_T200_H16", gi.make_inputs("gdn", B=4, T=200, H=16)),
         ("wide_varlen_H16", gi.make_inputs("varlen", H=16, doc_lengths=[1, 64, 65, 130, 7])),
+        # gates that barely decay (or not at all) over 64 chunks: rounding errors
+        # written into the state persist, so the state operands must keep
+        # about 16 significant bits (single bf16 there gives 1.4e-3 .. 1.7e-3)
+        ("slow_gate_T4096_H2", gi.random_problem(rng, 1, 4096, 2, 128, 128, gate_scale=0.001)),
+        ("no_decay_T4096_H2", gi.random_problem(rng, 1, 4096, 2, 128, 128, gate_scale=0.0)),
+        ("kda_slow_gate_T4096_H2", gi.random_problem(rng, 1, 4096, 2, 128, 128, kda=True, gate_scale=0.001,
+                                                     with_initial_state=True)),
     ]
     return out
 
