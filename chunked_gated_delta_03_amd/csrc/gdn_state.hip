@@ -5,7 +5,8 @@
 //     held by a pair of waves, one per half of the K rows (64 x 16 each, in
 //     MFMA accumulators), so a wave carries half of every K-contraction. A
 //     compute wave also stores its output rows of chunk c-1 during chunk c;
-//   - kLoaders loader waves that write chunk c+1 (loaded into registers
+//   - loader waves (8 in the whole pass, 4 in the other forms; see
+//     loaders()) that write chunk c+1 (loaded into registers
 //     during chunk c-1) into the other LDS buffer at the start of chunk c
 //     and issue the loads of chunk c+2.
 // Two workgroup barriers per chunk: one after the pairs have posted their
@@ -54,7 +55,13 @@ namespace gdn {
 namespace {
 using namespace st;
 
-constexpr int kLoaders = 4;              // loader waves per workgroup
+// Loader waves per workgroup. The loaders' stores into LDS end close to the
+// compute waves' end barrier (they are nearly on the chunk's critical path),
+// so the whole pass splits them over 8 waves (state kernel 145 -> 137 us on
+// the B=4 T=4096 H=16 workload). The other forms (storing h and v_new, or
+// state only) keep 4: at 12 waves per workgroup (3 per SIMD, at most 168
+// registers each) their larger register sets would spill.
+__host__ __device__ constexpr int loaders(bool store_h, bool compute_o) { return (compute_o && !store_h) ? 8 : 4; }
 
 template <int NCB>
 struct alignas(16) Smem {
@@ -81,7 +88,7 @@ struct alignas(16) Smem {
 }  // namespace
 
 template <int NCB, bool STORE_H, bool COMPUTE_O>
-__global__ __launch_bounds__((2 * NCB + kLoaders) * 64) void gdn_state_kernel(FwdArgs a) {
+__global__ __launch_bounds__((2 * NCB + loaders(STORE_H, COMPUTE_O)) * 64) void gdn_state_kernel(FwdArgs a) {
   using SM = Smem<NCB>;
   constexpr int BV = SM::BV;
   constexpr int NCW = SM::NCW;
@@ -102,7 +109,7 @@ __global__ __launch_bounds__((2 * NCB + kLoaders) * 64) void gdn_state_kernel(Fw
     // ltid + NL*p of each array, loads them into registers one chunk ahead
     // and writes them to their (swizzled) LDS slots. Rows of k, q, v past the
     // end of the sequence are zero.
-    constexpr int NL = 64 * kLoaders;
+    constexpr int NL = 64 * loaders(STORE_H, COMPUTE_O);
     constexpr int PPR = BV / 8;              // v pieces per row
     const int ltid = tid - NCW * 64;
     u32x4 kr[1024 / NL], qr[1024 / NL], tr[1024 / NL], ar[512 / NL], vr, er;
@@ -430,7 +437,8 @@ hipError_t launch_gdn_state(bool store_h, bool compute_o, const FwdArgs& a, hipS
   const long units = (long)a.geo.N * a.H;
   const bool narrow = units * (kDim / 32) < 256;
   const dim3 grid1(state_grid(a.geo.N, a.H, kDim / 16)), grid2(state_grid(a.geo.N, a.H, kDim / 32));
-  const dim3 block1(64 * (2 + kLoaders)), block2(64 * (4 + kLoaders));
+  const int nl = loaders(store_h, compute_o);
+  const dim3 block1(64 * (2 + nl)), block2(64 * (4 + nl));
   if (store_h && !compute_o) {
     if (narrow) hipLaunchKernelGGL((gdn_state_kernel<1, true, false>), grid1, block1, 0, stream, a);
     else hipLaunchKernelGGL((gdn_state_kernel<2, true, false>), grid2, block2, 0, stream, a);
