@@ -5,9 +5,10 @@
 //     held by a pair of waves, one per half of the K rows (64 x 16 each, in
 //     MFMA accumulators); the pair exchanges its partial K-contractions
 //     through LDS, as in the GDN state kernel;
-//   - kLoaders loader waves that stage the chunk's decayed operands: in the
-//     whole pass they copy them from the prepare kernel's output; in the
-//     stage entry they form them from k, q and the cumulative gate.
+//   - loader waves (8 in the whole pass, else 4) that stage the chunk's
+//     decayed operands: in the whole pass they copy them from the prepare
+//     kernel's output; in the stage entry they form them from k, q and the
+//     cumulative gate.
 //
 // Per chunk, with S (K x V) the state entering it, G the chunk-local
 // cumulative log2 gate per channel (written by the prepare kernel) and
@@ -40,7 +41,11 @@ namespace gdn {
 namespace {
 using namespace st;
 
-constexpr int kLoadersK = 4;
+// Loader waves per workgroup: 8 in the whole pass (its loaders' LDS stores
+// sit nearly on the chunk's critical path; state kernel 375 -> 342 us on the
+// B=2 T=8192 H=32 workload), 4 in the other forms, whose larger register sets
+// would spill at 12 waves per workgroup.
+__host__ __device__ constexpr int loaders_k(bool store_h, bool compute_o) { return (compute_o && !store_h) ? 8 : 4; }
 
 template <int NCB>
 struct alignas(16) KSmem {
@@ -66,7 +71,7 @@ struct alignas(16) KSmem {
 }  // namespace
 
 template <int NCB, bool STORE_H, bool COMPUTE_O>
-__global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(FwdArgs a) {
+__global__ __launch_bounds__((2 * NCB + loaders_k(STORE_H, COMPUTE_O)) * 64) void kda_state_kernel(FwdArgs a) {
   using SM = KSmem<NCB>;
   constexpr int BV = SM::BV;
   constexpr int NCW = SM::NCW;
@@ -87,7 +92,7 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
       // Whole pass with a.kdec: the decayed operands come from the prepare kernel; the
       // loaders copy them (16-byte pieces, loaded one chunk ahead) into the
       // same windows as below.
-      constexpr int NL = 64 * kLoadersK;
+      constexpr int NL = 64 * loaders_k(STORE_H, COMPUTE_O);
       constexpr int PPR = BV / 8;
       const int ltid = tid - NCW * 64;
       const int pc = ltid & 15;
@@ -191,7 +196,7 @@ __global__ __launch_bounds__((2 * NCB + kLoadersK) * 64) void kda_state_kernel(F
   if (w >= NCW) {
     // Stage entry: the loaders form the decayed operands from k, q and the
     // cumulative gate.
-    constexpr int NL = 64 * kLoadersK;
+    constexpr int NL = 64 * loaders_k(STORE_H, COMPUTE_O);
     constexpr int PPR = BV / 8;              // v pieces per row
     const int ltid = tid - NCW * 64;
     const int pc = ltid & 15;                // this lane's 8-channel piece of every row
@@ -573,7 +578,8 @@ hipError_t launch_kda_fwd(bool store_h, bool compute_o, const FwdArgs& a, hipStr
   const long units = (long)a.geo.N * a.H;
   const bool narrow = units * (kDim / 32) < 256;
   const dim3 grid1(state_grid(a.geo.N, a.H, kDim / 16)), grid2(state_grid(a.geo.N, a.H, kDim / 32));
-  const dim3 block1(64 * (2 + kLoadersK)), block2(64 * (4 + kLoadersK));
+  const int nl = loaders_k(store_h, compute_o);
+  const dim3 block1(64 * (2 + nl)), block2(64 * (4 + nl));
   if (store_h && !compute_o) {
     if (narrow) hipLaunchKernelGGL((kda_state_kernel<1, true, false>), grid1, block1, 0, stream, a);
     else hipLaunchKernelGGL((kda_state_kernel<2, true, false>), grid2, block2, 0, stream, a);
