@@ -36,9 +36,10 @@
 // then the B operand of contraction step s built from tiles 2s, 2s+1 covers
 // K indices 32s + 8g .. 32s + 8g + 7 in lane group g, which an A-operand
 // fragment of a k or q row reads as one 16-byte piece in natural column
-// order. k, q and T rows (256 bytes) are stored as 16-byte pieces with piece p
-// of row r at slot p ^ (r & 15), Aqk rows (128 bytes) with p ^ (r & 7), so
-// that the 16 rows of a fragment read fall on distinct banks; T (hi | lo) and
+// order. k, q and T rows (256 bytes) are stored as 16-byte pieces: piece p of
+// row r of T at slot p ^ (r & 15), of k and q at slot p ^ kswz(r) (see
+// there), Aqk rows (128 bytes) at p ^ (r & 7), so that the 16 rows of a
+// fragment read fall on distinct banks; T (hi | lo) and
 // Aqk come from the prepare kernel with permuted columns. k^T for the update
 // and the v columns are read with the transposing LDS read (ds_read_b64_tr_b16).
 //
@@ -143,12 +144,12 @@ __global__ __launch_bounds__((2 * NCB + loaders(STORE_H, COMPUTE_O)) * 64) void 
 #pragma unroll
       for (int p = 0; p < 1024 / NL; ++p) {
         const int idx = p * NL + ltid, r = idx >> 4;
-        const int slot = 8 * ((idx & 15) ^ (r & 15));
         if (part == 0) {
+          const int slot = 8 * ((idx & 15) ^ kswz(r));
           *reinterpret_cast<u32x4*>(B.k + r * kDim + slot) = kr[p];
           if constexpr (COMPUTE_O) *reinterpret_cast<u32x4*>(sm.q + r * kDim + slot) = qr[p];
         } else {
-          *reinterpret_cast<u32x4*>(B.t + r * (2 * kChunk) + slot) = tr[p];
+          *reinterpret_cast<u32x4*>(B.t + r * (2 * kChunk) + 8 * ((idx & 15) ^ (r & 15))) = tr[p];
         }
       }
       if (part == 0) return;
@@ -256,7 +257,7 @@ __global__ __launch_bounds__((2 * NCB + loaders(STORE_H, COMPUTE_O)) * 64) void 
 #pragma unroll
       for (int sp = 0; sp < 2; ++sp) {
         const int s = 2 * kh + sp;
-        const int slot = 8 * ((4 * s + g4) ^ l16);
+        const int slot = 8 * ((4 * s + g4) ^ kswz(l16));
         u16x8 fk[4], fq[4];
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
@@ -376,8 +377,8 @@ __global__ __launch_bounds__((2 * NCB + loaders(STORE_H, COMPUTE_O)) * 64) void 
           for (int t = 0; t < 4; ++t) {
             const int c0 = perm_col(64 * kh + 16 * t + 4 * trQ);
             const int r0 = 32 * s + 4 * trG + trJ, r1 = r0 + 16;
-            const u16x4 x0 = tr_read(B.k + r0 * kDim + 8 * ((c0 >> 3) ^ (r0 & 15)) + (c0 & 7));
-            const u16x4 x1 = tr_read(B.k + r1 * kDim + 8 * ((c0 >> 3) ^ (r1 & 15)) + (c0 & 7));
+            const u16x4 x0 = tr_read(B.k + r0 * kDim + 8 * ((c0 >> 3) ^ kswz(r0)) + (c0 & 7));
+            const u16x4 x1 = tr_read(B.k + r1 * kDim + 8 * ((c0 >> 3) ^ kswz(r1)) + (c0 & 7));
             ak[s][t] = cat4(x0, x1);
           }
         const float dec = B.vec[7 * kChunk];

@@ -16,6 +16,15 @@ __device__ __forceinline__ u16x4 tr_read(const uint16_t* p) {
 }
 
 
+// Slot swizzle of the k (and q) rows: piece p of row r sits at slot
+// p ^ kswz(r). Besides the 16-row fragment reads (any bijection of r & 15
+// keeps those on distinct banks), the k rows are read transposed for the
+// update: 16 lanes read the first 8 bytes of pieces P + j of rows x + i
+// (i, j = 0..3, P and x multiples of 4). With p ^ (r & 15) those land in
+// only 4 distinct slots (4 lanes per bank); folding the row's low bits into
+// the slot's high bits spreads them over 16.
+__device__ __forceinline__ int kswz(int r) { return (r & 15) ^ ((r & 3) << 2); }
+
 __device__ __forceinline__ uint16_t bfr(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
 // B operand (8 contraction slots) from two accumulator tiles: slots 0..3 are

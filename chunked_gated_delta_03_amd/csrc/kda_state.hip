@@ -30,8 +30,9 @@
 // and the channel decays (read after the pair barrier) have two buffers in
 // the whole pass and are written after the pair barrier with kd and qd: LDS
 // writes before that barrier compete with the compute waves' reads there. Layouts and the state-row permutation are those of the GDN state
-// kernel: 16-byte pieces of 256-byte rows at slot p ^ (r & 15) (Aqk rows:
-// p ^ (r & 7)), row i of state tile t is K index perm_col(16 t + i).
+// kernel: 16-byte pieces of 256-byte rows at slot p ^ (r & 15), the
+// transposed-read kg rows at p ^ kswz(r) (Aqk rows: p ^ (r & 7)), row i of
+// state tile t is K index perm_col(16 t + i).
 #include <type_traits>
 
 #include "gdn_state_common.h"
@@ -159,7 +160,7 @@ __global__ __launch_bounds__((2 * NCB + loaders_k(STORE_H, COMPUTE_O)) * 64) voi
 #pragma unroll
         for (int p = 0; p < 1024 / NL; ++p) {
           const int idx = p * NL + ltid, r = idx >> 4;
-          const int slot = 8 * (pc ^ (r & 15));
+          const int slot = 8 * (pc ^ kswz(r));
           *reinterpret_cast<u32x4*>(sm.kgh + r * kDim + slot) = gh[p];
           *reinterpret_cast<u32x4*>(sm.kgl + r * kDim + slot) = gl[p];
         }
@@ -290,10 +291,10 @@ __global__ __launch_bounds__((2 * NCB + loaders_k(STORE_H, COMPUTE_O)) * 64) voi
 #pragma unroll
       for (int p = 0; p < 1024 / NL; ++p) {
         const int idx = p * NL + ltid, r = idx >> 4;
-        const int slot = 8 * (pc ^ (r & 15));
+        const int slot = 8 * (pc ^ kswz(r));
         *reinterpret_cast<u32x4*>(sm.kgh + r * kDim + slot) = kgh[p];
         *reinterpret_cast<u32x4*>(sm.kgl + r * kDim + slot) = kgl[p];
-        *reinterpret_cast<u32x4*>(sm.t[0] + r * (2 * kChunk) + slot) = tr[p];
+        *reinterpret_cast<u32x4*>(sm.t[0] + r * (2 * kChunk) + 8 * (pc ^ (r & 15))) = tr[p];
       }
       if constexpr (COMPUTE_O) {
 #pragma unroll
@@ -511,8 +512,8 @@ __global__ __launch_bounds__((2 * NCB + loaders_k(STORE_H, COMPUTE_O)) * 64) voi
           for (int t = 0; t < 4; ++t) {
             const int c0 = perm_col(64 * kh + 16 * t + 4 * trQ);
             const int r0 = 32 * s + 4 * trG + trJ, r1 = r0 + 16;
-            const int o0 = r0 * kDim + 8 * ((c0 >> 3) ^ (r0 & 15)) + (c0 & 7);
-            const int o1 = r1 * kDim + 8 * ((c0 >> 3) ^ (r1 & 15)) + (c0 & 7);
+            const int o0 = r0 * kDim + 8 * ((c0 >> 3) ^ kswz(r0)) + (c0 & 7);
+            const int o1 = r1 * kDim + 8 * ((c0 >> 3) ^ kswz(r1)) + (c0 & 7);
             gh[s][t] = cat4(tr_read(sm.kgh + o0), tr_read(sm.kgh + o1));
             gl[s][t] = cat4(tr_read(sm.kgl + o0), tr_read(sm.kgl + o1));
           }
