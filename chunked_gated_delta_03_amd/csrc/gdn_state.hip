@@ -38,10 +38,12 @@
 // fragment of a k or q row reads as one 16-byte piece in natural column
 // order. k, q and T rows (256 bytes) are stored as 16-byte pieces: piece p of
 // row r of T at slot p ^ (r & 15), of k and q at slot p ^ kswz(r) (see
-// there), Aqk rows (128 bytes) at p ^ (r & 7), so that the 16 rows of a
-// fragment read fall on distinct banks; T (hi | lo) and
-// Aqk come from the prepare kernel with permuted columns. k^T for the update
-// and the v columns are read with the transposing LDS read (ds_read_b64_tr_b16).
+// there), Aqk rows (128 bytes) at p ^ ((r >> 1) & 7) (the two rows that
+// share a 256-byte bank line take the same slot in different halves), so that
+// the 16 rows of a fragment read fall on distinct banks; T (hi | lo) and Aqk
+// come from the prepare kernel with permuted columns. k^T for the update and
+// the v columns are read with the transposing LDS read (ds_read_b64_tr_b16);
+// the v rows of a 32-column block use the slot swizzle vswz.
 //
 // Register arrays are indexed with compile-time indices only (the compute
 // loop is specialised per K half): an index that depends on the wave becomes
@@ -157,10 +159,13 @@ __global__ __launch_bounds__((2 * NCB + loaders(STORE_H, COMPUTE_O)) * 64) void 
 #pragma unroll
         for (int p = 0; p < 512 / NL; ++p) {
           const int idx = p * NL + ltid, r = idx >> 3;
-          *reinterpret_cast<u32x4*>(B.aqk + r * kChunk + 8 * ((idx & 7) ^ (r & 7))) = ar[p];
+          *reinterpret_cast<u32x4*>(B.aqk + r * kChunk + 8 * ((idx & 7) ^ ((r >> 1) & 7))) = ar[p];
         }
       }
-      if (ltid < 64 * PPR) *reinterpret_cast<u32x4*>(B.v + 8 * ltid) = vr;
+      if (ltid < 64 * PPR) {
+        const int vrow = ltid / PPR;
+        *reinterpret_cast<u32x4*>(B.v + vrow * BV + 8 * ((ltid % PPR) ^ vswz<BV>(vrow))) = vr;
+      }
       if (ltid < kVecRows * kChunk / 4) *reinterpret_cast<u32x4*>(B.vec + 4 * ltid) = er;
     };
     // Same barrier sequence as the compute waves: one before the loop, two
@@ -298,7 +303,7 @@ __global__ __launch_bounds__((2 * NCB + loaders(STORE_H, COMPUTE_O)) * 64) void 
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
           const int it = 2 * hh + k2;
-          const u16x4 vv = tr_read(B.v + (16 * it + 4 * g4 + trJ) * BV + 16 * cb + 4 * trQ);
+          const u16x4 vv = tr_read(B.v + (16 * it + 4 * g4 + trJ) * BV + 8 * ((2 * cb + (trQ >> 1)) ^ vswz<BV>(16 * it + 4 * g4 + trJ)) + 4 * (trQ & 1));
           const float4 bt = *reinterpret_cast<const float4*>(B.vec + 16 * it + 4 * g4);
           const float4 cc = *reinterpret_cast<const float4*>(B.vec + kChunk + 16 * it + 4 * g4);
           y2[k2][0] = bt.x * bf2f(vv[0]) - cc.x * X[it][0];
@@ -406,9 +411,9 @@ __global__ __launch_bounds__((2 * NCB + loaders(STORE_H, COMPUTE_O)) * 64) void 
           const int r = 16 * it + l16;
           const float4 rr = *reinterpret_cast<const float4*>(B.vec + 3 * kChunk + 16 * it + 4 * g4);
           O[i][0] *= rr.x; O[i][1] *= rr.y; O[i][2] *= rr.z; O[i][3] *= rr.w;
-          O[i] = mfma16(*reinterpret_cast<const u16x8*>(B.aqk + r * kChunk + 8 * (g4 ^ (r & 7))), VNb0, O[i]);
+          O[i] = mfma16(*reinterpret_cast<const u16x8*>(B.aqk + r * kChunk + 8 * (g4 ^ ((r >> 1) & 7))), VNb0, O[i]);
           if (kh == 1)  // Aqk is lower triangular
-            O[i] = mfma16(*reinterpret_cast<const u16x8*>(B.aqk + r * kChunk + 8 * ((4 + g4) ^ (r & 7))), VNb1, O[i]);
+            O[i] = mfma16(*reinterpret_cast<const u16x8*>(B.aqk + r * kChunk + 8 * ((4 + g4) ^ ((r >> 1) & 7))), VNb1, O[i]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) ostage[(16 * i + 4 * g4 + e) * 16 + l16] = bfr(O[i][e]);
         }

@@ -25,6 +25,12 @@ __device__ __forceinline__ u16x4 tr_read(const uint16_t* p) {
 // the slot's high bits spreads them over 16.
 __device__ __forceinline__ int kswz(int r) { return (r & 15) ^ ((r & 3) << 2); }
 
+// Slot swizzle of 32-column v rows (64 bytes, four 16-byte pieces): rows
+// 4..7 of each group of 8 swap their halves, so that the transposing reads of
+// lane groups 0 and 1 (rows 4 g4 + j) fall on different banks.
+template <int BV>
+__device__ __forceinline__ int vswz(int r) { return BV == 32 ? ((r >> 2) & 1) << 1 : 0; }
+
 __device__ __forceinline__ uint16_t bfr(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
 // B operand (8 contraction slots) from two accumulator tiles: slots 0..3 are

@@ -31,8 +31,8 @@
 // the whole pass and are written after the pair barrier with kd and qd: LDS
 // writes before that barrier compete with the compute waves' reads there. Layouts and the state-row permutation are those of the GDN state
 // kernel: 16-byte pieces of 256-byte rows at slot p ^ (r & 15), the
-// transposed-read kg rows at p ^ kswz(r) (Aqk rows: p ^ (r & 7)), row i of
-// state tile t is K index perm_col(16 t + i).
+// transposed-read kg rows at p ^ kswz(r) (Aqk rows: p ^ ((r >> 1) & 7), v
+// rows: p ^ vswz(r)), row i of state tile t is K index perm_col(16 t + i).
 #include <type_traits>
 
 #include "gdn_state_common.h"
@@ -167,9 +167,12 @@ __global__ __launch_bounds__((2 * NCB + loaders_k(STORE_H, COMPUTE_O)) * 64) voi
 #pragma unroll
         for (int p = 0; p < 512 / NL; ++p) {
           const int idx = p * NL + ltid, r = idx >> 3;
-          *reinterpret_cast<u32x4*>(sm.aqk + r * kChunk + 8 * ((idx & 7) ^ (r & 7))) = ar[p];
+          *reinterpret_cast<u32x4*>(sm.aqk + r * kChunk + 8 * ((idx & 7) ^ ((r >> 1) & 7))) = ar[p];
         }
-        if (ltid < 64 * PPR) *reinterpret_cast<u32x4*>(sm.v + 8 * ltid) = vr;
+        if (ltid < 64 * PPR) {
+        const int vrow = ltid / PPR;
+        *reinterpret_cast<u32x4*>(sm.v + vrow * BV + 8 * ((ltid % PPR) ^ vswz<BV>(vrow))) = vr;
+      }
       };
       // same barrier sequence as the stage loaders below. During chunk jc:
       // before the pair barrier, chunk jc's kg, Aqk, v go in and chunk
@@ -300,10 +303,13 @@ __global__ __launch_bounds__((2 * NCB + loaders_k(STORE_H, COMPUTE_O)) * 64) voi
 #pragma unroll
         for (int p = 0; p < 512 / NL; ++p) {
           const int idx = p * NL + ltid, r = idx >> 3;
-          *reinterpret_cast<u32x4*>(sm.aqk + r * kChunk + 8 * ((idx & 7) ^ (r & 7))) = ar[p];
+          *reinterpret_cast<u32x4*>(sm.aqk + r * kChunk + 8 * ((idx & 7) ^ ((r >> 1) & 7))) = ar[p];
         }
       }
-      if (ltid < 64 * PPR) *reinterpret_cast<u32x4*>(sm.v + 8 * ltid) = vr;
+      if (ltid < 64 * PPR) {
+        const int vrow = ltid / PPR;
+        *reinterpret_cast<u32x4*>(sm.v + vrow * BV + 8 * ((ltid % PPR) ^ vswz<BV>(vrow))) = vr;
+      }
       if (ltid < kVecRows * kChunk / 4) *reinterpret_cast<u32x4*>(sm.vec[0] + 4 * ltid) = er;
       if (ltid < 16) {
         *reinterpret_cast<float4*>(sm.dec[0] + 8 * ltid) = dec0;
@@ -440,7 +446,7 @@ __global__ __launch_bounds__((2 * NCB + loaders_k(STORE_H, COMPUTE_O)) * 64) voi
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
           const int it = 2 * hh + k2;
-          const u16x4 vv = tr_read(sm.v + (16 * it + 4 * g4 + trJ) * BV + 16 * cb + 4 * trQ);
+          const u16x4 vv = tr_read(sm.v + (16 * it + 4 * g4 + trJ) * BV + 8 * ((2 * cb + (trQ >> 1)) ^ vswz<BV>(16 * it + 4 * g4 + trJ)) + 4 * (trQ & 1));
           const float4 bt = *reinterpret_cast<const float4*>(sm.vec[tb] + 16 * it + 4 * g4);
           const float4 cc = *reinterpret_cast<const float4*>(sm.vec[tb] + kChunk + 16 * it + 4 * g4);
           y2[k2][0] = bt.x * bf2f(vv[0]) - cc.x * X[it][0];
@@ -547,9 +553,9 @@ __global__ __launch_bounds__((2 * NCB + loaders_k(STORE_H, COMPUTE_O)) * 64) voi
           const int r = 16 * it + l16;
           const float4 rr = *reinterpret_cast<const float4*>(sm.vec[tb] + 3 * kChunk + 16 * it + 4 * g4);
           O[i][0] *= rr.x; O[i][1] *= rr.y; O[i][2] *= rr.z; O[i][3] *= rr.w;
-          O[i] = mfma16(*reinterpret_cast<const u16x8*>(sm.aqk + r * kChunk + 8 * (g4 ^ (r & 7))), VNb0, O[i]);
+          O[i] = mfma16(*reinterpret_cast<const u16x8*>(sm.aqk + r * kChunk + 8 * (g4 ^ ((r >> 1) & 7))), VNb0, O[i]);
           if (kh == 1)  // Aqk is lower triangular
-            O[i] = mfma16(*reinterpret_cast<const u16x8*>(sm.aqk + r * kChunk + 8 * ((4 + g4) ^ (r & 7))), VNb1, O[i]);
+            O[i] = mfma16(*reinterpret_cast<const u16x8*>(sm.aqk + r * kChunk + 8 * ((4 + g4) ^ ((r >> 1) & 7))), VNb1, O[i]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) ostage[(16 * i + 4 * g4 + e) * 16 + l16] = bfr(O[i][e]);
         }
