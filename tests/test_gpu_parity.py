@@ -52,6 +52,9 @@ def _problems_reduced():
         # 64+ (sequence, head) units: the state kernel's four-compute-wave form
         ("wide_B4_T200_H16", gi.make_inputs("gdn", B=4, T=200, H=16)),
         ("wide_varlen_H16", gi.make_inputs("varlen", H=16, doc_lengths=[1, 64, 65, 130, 7])),
+        # 65 units: the four-compute-wave form with padding workgroups (the
+        # grid rounds the units up to groups of 8), ragged last chunk
+        ("wide_pad_B5_T130_H13", gi.make_inputs("gdn", B=5, T=130, H=13)),
         # gates that barely decay (or not at all) over 64 chunks: rounding errors
         # written into the state persist, so the state operands must keep
         # about 16 significant bits (single bf16 there gives 1.4e-3 .. 1.7e-3)
@@ -224,6 +227,7 @@ def _kda_problems():
                                          cu_seqlens=[0, 1, 18, 82, 147, 317])),
         # 64+ (sequence, head) units: the four-compute-wave form of the state kernel
         ("kda_wide_B2_T130_H32", gi.make_inputs("kda", B=2, T=130, H=32)),
+        ("kda_wide_pad_B5_T70_H13", gi.make_inputs("kda", B=5, T=70, H=13)),
     ]
 
 
